@@ -1,0 +1,193 @@
+/*
+ * oracle.c -- plain CPU reference for the gradient of a 2-D convolution with
+ * respect to its input, and a separately written forward convolution.
+ *
+ * TEST INFRASTRUCTURE.  This file is the checker, not the product: only the
+ * tests, the smoke check and the CPU-baseline leg of the benchmark load it.  It
+ * shares no source, header, table or helper with the GPU library.
+ *
+ * Everything is accumulated in IEEE double, in one fixed order per output
+ * element, with no fast-math, so a result does not depend on the thread count.
+ *
+ * Definitions followed
+ * --------------------
+ * grad_input (doppler conv2d_backward_input.wgsl, the direct kernel and its
+ * header comment; meganeura conv2d_grad_input_gemm.wgsl, the general-stride
+ * branch of the B-tile gather).  Each input pixel (n, ci, ih, iw) collects
+ * every output-gradient value it fed in the forward pass:
+ *
+ *   grad_input[n,ci,ih,iw] = sum over co < Co, kh < kH, kw < kW of
+ *                            grad_out[n,co,oh,ow] * weight[co,ci,kh,kw]
+ *   where a = ih + pad_h - kh and b = iw + pad_w - kw must both be >= 0,
+ *   divisible by the stride, and give oh = a/stride < oH, ow = b/stride < oW.
+ *   Terms that fail a condition are absent; an element with none is 0.
+ *
+ * The doppler kernel has one batch item and one pad; meganeura carries the
+ * batch on the grid and separate pad_h / pad_w.  Both are merged here: N
+ * independent batch items, per-dimension symmetric zero padding, one stride
+ * for both dimensions.  The sign test comes before the divisibility test, as
+ * in both pages, so C's sign-following remainder never sees a negative value.
+ *
+ * abs_sum[n,ci,ih,iw] = the same sum of |grad_out * weight| (used to scale the
+ * floating-point tolerance of a GPU result).
+ *
+ * Forward convolution (the forward mapping stated in the doppler direct
+ * kernel's comment: an output pixel oy reads input row oy*stride - pad + ky):
+ *
+ *   y[n,co,oh,ow] = sum over ci, kh, kw of
+ *                   x[n,ci,oh*stride-pad_h+kh, ow*stride-pad_w+kw] * w[co,ci,kh,kw]
+ *   with x taken as 0 outside [0,H) x [0,W).
+ *
+ * It is written from the forward side on purpose (a loop over output pixels),
+ * so the adjoint identity <conv(x,w), g> = <x, grad_input(g,w)> checks the two
+ * against each other rather than against a shared index formula.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+typedef struct {
+    int64_t N, Ci, H, W, Co, kH, kW, stride, pad_h, pad_w, oH, oW;
+} shape_t;
+
+static shape_t make_shape(int N, int Ci, int H, int W, int Co, int kH, int kW,
+                          int stride, int pad_h, int pad_w, int oH, int oW)
+{
+    shape_t s = {N, Ci, H, W, Co, kH, kW, stride, pad_h, pad_w, oH, oW};
+    return s;
+}
+
+/* One grad_input element, straight from the definition above. */
+static void grad_input_element(const double *grad_out, const double *weight,
+                               const shape_t *s, int64_t n, int64_t ci,
+                               int64_t ih, int64_t iw, double *value,
+                               double *abs_value)
+{
+    double acc = 0.0, acc_abs = 0.0;
+    for (int64_t co = 0; co < s->Co; ++co) {
+        for (int64_t kh = 0; kh < s->kH; ++kh) {
+            int64_t a = ih + s->pad_h - kh;
+            if (a < 0) continue;
+            if (a % s->stride != 0) continue;
+            int64_t oh = a / s->stride;
+            if (oh >= s->oH) continue;
+            for (int64_t kw = 0; kw < s->kW; ++kw) {
+                int64_t b = iw + s->pad_w - kw;
+                if (b < 0) continue;
+                if (b % s->stride != 0) continue;
+                int64_t ow = b / s->stride;
+                if (ow >= s->oW) continue;
+                double g = grad_out[((n * s->Co + co) * s->oH + oh) * s->oW + ow];
+                double w = weight[((co * s->Ci + ci) * s->kH + kh) * s->kW + kw];
+                double t = g * w;
+                acc += t;
+                acc_abs += fabs(t);
+            }
+        }
+    }
+    *value = acc;
+    *abs_value = acc_abs;
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/*
+ * Full grad_input.  grad_out [N,Co,oH,oW], weight [Co,Ci,kH,kW], out and
+ * abs_sum [N,Ci,H,W]; all contiguous doubles.  abs_sum may be NULL.
+ */
+void oracle_grad_input_f64(const double *grad_out, const double *weight,
+                           double *out, double *abs_sum, int N, int Ci, int H,
+                           int W, int Co, int kH, int kW, int stride,
+                           int pad_h, int pad_w, int oH, int oW)
+{
+    shape_t s = make_shape(N, Ci, H, W, Co, kH, kW, stride, pad_h, pad_w, oH, oW);
+    int64_t rows = s.N * s.Ci * s.H;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t row = 0; row < rows; ++row) {
+        int64_t ih = row % s.H;
+        int64_t ci = (row / s.H) % s.Ci;
+        int64_t n = row / (s.H * s.Ci);
+        for (int64_t iw = 0; iw < s.W; ++iw) {
+            double v, va;
+            grad_input_element(grad_out, weight, &s, n, ci, ih, iw, &v, &va);
+            out[row * s.W + iw] = v;
+            if (abs_sum) abs_sum[row * s.W + iw] = va;
+        }
+    }
+}
+
+/*
+ * The same result at chosen elements only: flat_idx[i] indexes the
+ * [N,Ci,H,W] tensor.  Used where the full tensor would take the CPU too long.
+ * Indices outside the tensor give NaN.
+ */
+void oracle_grad_input_at_f64(const double *grad_out, const double *weight,
+                              const int64_t *flat_idx, int64_t count,
+                              double *out, double *abs_sum, int N, int Ci,
+                              int H, int W, int Co, int kH, int kW, int stride,
+                              int pad_h, int pad_w, int oH, int oW)
+{
+    shape_t s = make_shape(N, Ci, H, W, Co, kH, kW, stride, pad_h, pad_w, oH, oW);
+    int64_t total = s.N * s.Ci * s.H * s.W;
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t i = 0; i < count; ++i) {
+        int64_t f = flat_idx[i];
+        if (f < 0 || f >= total) {
+            out[i] = NAN;
+            if (abs_sum) abs_sum[i] = NAN;
+            continue;
+        }
+        int64_t iw = f % s.W;
+        int64_t ih = (f / s.W) % s.H;
+        int64_t ci = (f / (s.W * s.H)) % s.Ci;
+        int64_t n = f / (s.W * s.H * s.Ci);
+        double v, va;
+        grad_input_element(grad_out, weight, &s, n, ci, ih, iw, &v, &va);
+        out[i] = v;
+        if (abs_sum) abs_sum[i] = va;
+    }
+}
+
+/*
+ * Forward cross-correlation, written from the output side.  x [N,Ci,H,W],
+ * w [Co,Ci,kH,kW], y [N,Co,oH,oW]; all contiguous doubles.
+ */
+void oracle_conv2d_fwd_f64(const double *x, const double *w, double *y, int N,
+                           int Ci, int H, int W, int Co, int kH, int kW,
+                           int stride, int pad_h, int pad_w, int oH, int oW)
+{
+    int64_t planes = (int64_t)N * Co;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t plane = 0; plane < planes; ++plane) {
+        int64_t n = plane / Co, co = plane % Co;
+        for (int64_t oh = 0; oh < oH; ++oh) {
+            for (int64_t ow = 0; ow < oW; ++ow) {
+                double acc = 0.0;
+                for (int64_t ci = 0; ci < Ci; ++ci) {
+                    const double *xp = x + (n * Ci + ci) * H * W;
+                    const double *wp = w + (co * Ci + ci) * kH * kW;
+                    for (int64_t kh = 0; kh < kH; ++kh) {
+                        int64_t ih = oh * stride - pad_h + kh;
+                        if (ih < 0 || ih >= H) continue;
+                        for (int64_t kw = 0; kw < kW; ++kw) {
+                            int64_t iw = ow * stride - pad_w + kw;
+                            if (iw < 0 || iw >= W) continue;
+                            acc += xp[ih * W + iw] * wp[kh * kW + kw];
+                        }
+                    }
+                }
+                y[(plane * oH + oh) * oW + ow] = acc;
+            }
+        }
+    }
+}
