@@ -1,0 +1,186 @@
+#!/usr/bin/env python3
+"""Benchmark of conv2d grad_input on one MI355X: effective TFLOP/s and the
+fraction of the matrix-core roofline, with the CPU oracle timed beside it.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                    [--no-others]
+
+A step is one grad_input call (weight reorder + every GEMM launch) over one
+batch of synthetic inputs already resident in HBM.  W untimed steps, then K
+steps bracketed by a device synchronize on both sides; rank 0 prints ONE JSON
+line.  Effective work per call is 2*N*Co*oH*oW*Ci*kH*kW flops.
+
+The GEMM kernels' own duration is measured live with HIP events that the
+library records on the launch stream around its GEMM launches (the
+``roofline.achieved`` figure); the whole-call time gives ``value``.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import workloads  # noqa: E402
+
+METRIC = "effective TFLOP/s of conv2d grad_input per config; % of MFMA peak (1 GPU)"
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6}   # MI355X dense matrix-core peaks
+HBM_PEAK_GBS = 8000.0
+DEFAULT_WORKLOAD = "resnet_stage_3x3"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(workloads.BY_NAME))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the short timing of the other workloads")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle baseline sample")
+    return ap.parse_args()
+
+
+def device_inputs(wl, torch, dev):
+    g, w = workloads.make_inputs(wl)
+    if wl.dtype == "bf16":
+        tg = torch.from_numpy(g.view(np.int16)).to(dev).view(torch.bfloat16)
+        tw = torch.from_numpy(w.view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        tg = torch.from_numpy(g).to(dev)
+        tw = torch.from_numpy(w).to(dev)
+    out = torch.empty(wl.shape.dst_shape, dtype=torch.float32, device=dev)
+    return (g, w), tg, tw, out
+
+
+def time_workload(wl, steps, warmup, torch, gi, dev):
+    """Returns dict with whole-call ms, GEMM-kernel ms (HIP events), flops."""
+    s = wl.shape
+    _, tg, tw, out = device_inputs(wl, torch, dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def call():
+        gi.grad_input(tg, tw, stride=s.stride, padding=(s.pad_h, s.pad_w),
+                      input_hw=(s.H, s.W), out=out, stream=stream)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    kb = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ke = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for i in range(steps):
+        gi.set_profile_events(kb[i], ke[i])
+        call()
+    t1.record(stream)
+    gi.set_profile_events(None, None)
+    torch.cuda.synchronize()
+    wall1 = time.perf_counter()
+    total_ms = t0.elapsed_time(t1)
+    kern_ms = [kb[i].elapsed_time(ke[i]) for i in range(steps)]
+    return dict(ms_per_step=total_ms / steps, kernel_ms=float(np.mean(kern_ms)),
+                kernel_ms_min=float(np.min(kern_ms)), wall_ms=(wall1 - wall0) * 1e3 / steps,
+                flops=s.eff_flops)
+
+
+def cpu_baseline(wl, target_s):
+    """The oracle, untuned, on a bounded sample: the first n batch items of the
+    same workload (n chosen from a one-item probe to take about target_s)."""
+    import oracle
+    s = wl.shape
+    g, w = workloads.make_inputs(wl)
+    if wl.dtype == "bf16":
+        g, w = workloads.bf16_to_f32(g), workloads.bf16_to_f32(w)
+    t = time.perf_counter()
+    oracle.grad_input(g[:1], w, s.stride, (s.pad_h, s.pad_w), (s.H, s.W), with_abs=False)
+    one = max(time.perf_counter() - t, 1e-4)
+    n = int(max(1, min(s.N, round(target_s / one))))
+    t = time.perf_counter()
+    oracle.grad_input(g[:n], w, s.stride, (s.pad_h, s.pad_w), (s.H, s.W), with_abs=False)
+    dt = time.perf_counter() - t
+    flops = s.eff_flops * n / s.N
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "first %d of %d batch items of %s (fp64 direct loop, %.2f s, %s)"
+                      % (n, s.N, wl.name, dt, platform.processor() or platform.machine())}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(grad_input shards over the batch with no exchange); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import conv2d_backward_amd as gi
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    gi.load_library()
+    dev = torch.device("cuda:0")
+    wl = workloads.BY_NAME[args.workload]
+    s = wl.shape
+
+    r = time_workload(wl, args.steps, args.warmup, torch, gi, dev)
+    value = r["flops"] / (r["ms_per_step"] * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[wl.dtype]
+    achieved = r["flops"] / (r["kernel_ms"] * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded PCG64: grad_out N(0,1), weight Kaiming-normal)",
+        "config": {"workload": wl.name, "N": s.N, "Ci": s.Ci, "Co": s.Co, "H": s.H, "W": s.W,
+                   "kH": s.kH, "kW": s.kW, "stride": s.stride, "pad_h": s.pad_h,
+                   "pad_w": s.pad_w, "oH": s.oH, "oW": s.oW, "eff_gflop": s.eff_flops / 1e9,
+                   "plan": gi.plan(gi.make_params(*s.as_tuple()[:10]), wl.dtype == "bf16")},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "kernel": "gi_generic_%s" % wl.dtype,
+                     "kernel_ms": round(r["kernel_ms"], 5),
+                     "per_unit": "2*Ci*kH*kW*Co flops per output pixel (n,oh,ow)",
+                     "units_per_launch": s.N * s.oH * s.oW},
+        "frac_of_peak_whole_call": round(value / peak, 4),
+    }
+    if not args.no_others:
+        others = {}
+        for o in workloads.WORKLOADS:
+            if o.name == wl.name:
+                continue
+            ro = time_workload(o, 20, 3, torch, gi, dev)
+            v = ro["flops"] / (ro["ms_per_step"] * 1e-3) / 1e12
+            others[o.name] = {"dtype": o.dtype, "tflops": round(v, 3),
+                              "ms_per_call": round(ro["ms_per_step"], 5),
+                              "kernel_ms": round(ro["kernel_ms"], 5),
+                              "frac_of_peak": round(v / PEAK_TFLOPS[o.dtype], 4)}
+        line["other_workloads"] = others
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,188 @@
+"""conv2d grad_input for MI355X (gfx950): Python binding of ``libconv2d_gi.so``.
+
+The binding only marshals arguments: every step of the computation runs in the
+library's HIP kernels.  PyTorch provides device memory and the current stream.
+If the library has not been built, importing works but every call raises
+``LibraryNotBuilt`` -- there is no CPU fallback.
+
+    from conv2d_backward_amd import grad_input
+    dx = grad_input(dy, w, stride=2, padding=(1, 1), input_hw=(56, 56))
+
+The C entry points mirror these names (see include/conv2d_grad_input.h).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "grad_input", "Conv2dGiParams", "Conv2dGiError", "LibraryNotBuilt", "load_library",
+    "make_params", "validate", "plan", "set_variant", "set_profile_events", "library_path", "exported_names",
+    "OK", "EINVAL", "EUNSUPPORTED", "EHIP", "VARIANT_AUTO", "VARIANT_GENERIC",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_PKG, "libconv2d_gi.so")
+
+OK, EINVAL, EUNSUPPORTED, EHIP = 0, 1, 2, 3
+VARIANT_AUTO, VARIANT_GENERIC = 0, 1
+
+_FIELDS = ("N", "Ci", "H", "W", "Co", "kH", "kW", "stride", "pad_h", "pad_w", "oH", "oW")
+
+
+class Conv2dGiParams(ctypes.Structure):
+    """Mirror of ``conv2d_gi_params`` (twelve int32 fields)."""
+    _fields_ = [(f, ctypes.c_int32) for f in _FIELDS]
+
+    def __repr__(self):
+        return "Conv2dGiParams(%s)" % ", ".join("%s=%d" % (f, getattr(self, f)) for f in _FIELDS)
+
+
+class Conv2dGiError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__("conv2d_grad_input failed (%d): %s" % (code, msg))
+        self.code = code
+
+
+class LibraryNotBuilt(ImportError):
+    pass
+
+
+_lib = None
+
+
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load the in-tree HIP library (built by ``conv2d_backward_amd.build``)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or library_path
+    if not os.path.exists(p):
+        raise LibraryNotBuilt(
+            "%s is missing: build it with `python -m conv2d_backward_amd.build`" % p)
+    lib = ctypes.CDLL(p)
+    P = ctypes.c_void_p
+    PP = ctypes.POINTER(Conv2dGiParams)
+    lib.conv2d_grad_input.argtypes = [P, P, P, PP, P]
+    lib.conv2d_grad_input.restype = ctypes.c_int
+    lib.conv2d_grad_input_bf16.argtypes = [P, P, P, PP, P]
+    lib.conv2d_grad_input_bf16.restype = ctypes.c_int
+    lib.conv2d_gi_validate.argtypes = [PP]
+    lib.conv2d_gi_validate.restype = ctypes.c_int
+    lib.conv2d_gi_strerror.argtypes = [ctypes.c_int]
+    lib.conv2d_gi_strerror.restype = ctypes.c_char_p
+    lib.conv2d_gi_last_hip_error.argtypes = []
+    lib.conv2d_gi_last_hip_error.restype = ctypes.c_char_p
+    lib.conv2d_gi_set_variant.argtypes = [ctypes.c_int]
+    lib.conv2d_gi_set_variant.restype = ctypes.c_int
+    lib.conv2d_gi_plan.argtypes = [PP, ctypes.c_int, ctypes.c_char_p, ctypes.c_size_t]
+    lib.conv2d_gi_plan.restype = ctypes.c_int
+    lib.conv2d_gi_set_profile_events.argtypes = [P, P]
+    lib.conv2d_gi_set_profile_events.restype = None
+    lib.conv2d_gi_version.argtypes = []
+    lib.conv2d_gi_version.restype = ctypes.c_char_p
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def exported_names():
+    """Names of the C entry points the binding wraps."""
+    return ["conv2d_grad_input", "conv2d_grad_input_bf16", "conv2d_gi_validate",
+            "conv2d_gi_strerror", "conv2d_gi_last_hip_error", "conv2d_gi_set_variant",
+            "conv2d_gi_plan", "conv2d_gi_set_profile_events", "conv2d_gi_version"]
+
+
+def make_params(N, Ci, H, W, Co, kH, kW, stride, pad_h, pad_w, oH=None, oW=None):
+    """Build a params struct; oH/oW default to the forward-conv formula."""
+    if oH is None:
+        oH = (H + 2 * pad_h - kH) // stride + 1
+    if oW is None:
+        oW = (W + 2 * pad_w - kW) // stride + 1
+    return Conv2dGiParams(N, Ci, H, W, Co, kH, kW, stride, pad_h, pad_w, oH, oW)
+
+
+def _check(code: int):
+    if code != OK:
+        lib = load_library()
+        msg = lib.conv2d_gi_strerror(code).decode()
+        if code == EHIP:
+            msg += ": " + lib.conv2d_gi_last_hip_error().decode()
+        raise Conv2dGiError(code, msg)
+
+
+def validate(p: Conv2dGiParams) -> int:
+    """Host-only shape check; returns the status code (no HIP call)."""
+    return load_library().conv2d_gi_validate(ctypes.byref(p))
+
+
+def plan(p: Conv2dGiParams, bf16: bool = False) -> str:
+    """Host-only: the plan the library would run for this shape."""
+    buf = ctypes.create_string_buffer(8192)
+    _check(load_library().conv2d_gi_plan(ctypes.byref(p), int(bool(bf16)), buf, len(buf)))
+    return buf.value.decode()
+
+
+def set_variant(variant: int) -> int:
+    """Force a kernel variant (VARIANT_AUTO restores the planner); returns the old one."""
+    old = load_library().conv2d_gi_set_variant(int(variant))
+    if old < 0:
+        raise ValueError("unknown variant %r" % (variant,))
+    return old
+
+
+def set_profile_events(begin, end):
+    """Record torch.cuda.Event ``begin``/``end`` around the GEMM launches of later
+    calls from this thread (None, None switches it off)."""
+    if begin is None or end is None:
+        load_library().conv2d_gi_set_profile_events(None, None)
+        return
+    load_library().conv2d_gi_set_profile_events(ctypes.c_void_p(begin.cuda_event),
+                                                ctypes.c_void_p(end.cuda_event))
+
+
+def grad_input(grad_out, weight, *, stride: int, padding, input_hw, out=None, stream=None):
+    """grad_input [N, Ci, H, W] (fp32) of a conv2d, computed on the GPU.
+
+    grad_out [N, Co, oH, oW] and weight [Co, Ci, kH, kW]: both float32 or both
+    bfloat16, contiguous, on the same ROCm device.  padding: int or (pad_h, pad_w).
+    input_hw: (H, W) of the forward input.  out: optional float32 [N, Ci, H, W]
+    tensor to write (every element is overwritten).  stream: a torch stream
+    (default: the device's current stream).  The call is asynchronous on that stream.
+    """
+    import torch
+
+    if isinstance(padding, int):
+        padding = (padding, padding)
+    pad_h, pad_w = (int(v) for v in padding)
+    H, W = (int(v) for v in input_hw)
+    if grad_out.dim() != 4 or weight.dim() != 4:
+        raise ValueError("grad_out and weight must be 4-D (NCHW and [Co,Ci,kH,kW])")
+    if not (grad_out.is_cuda and weight.is_cuda) or grad_out.device != weight.device:
+        raise ValueError("grad_out and weight must be on the same GPU device")
+    if grad_out.dtype != weight.dtype or grad_out.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("grad_out and weight must both be float32 or both bfloat16")
+    if not (grad_out.is_contiguous() and weight.is_contiguous()):
+        raise ValueError("grad_out and weight must be contiguous")
+    N, Co, oH, oW = (int(v) for v in grad_out.shape)
+    Co_w, Ci, kH, kW = (int(v) for v in weight.shape)
+    if Co_w != Co:
+        raise ValueError("weight has %d output channels, grad_out %d" % (Co_w, Co))
+    p = Conv2dGiParams(N, Ci, H, W, Co, kH, kW, int(stride), pad_h, pad_w, oH, oW)
+    lib = load_library()
+    _check(lib.conv2d_gi_validate(ctypes.byref(p)))
+    dev = grad_out.device
+    if out is None:
+        out = torch.empty((N, Ci, H, W), dtype=torch.float32, device=dev)
+    else:
+        if (out.dtype != torch.float32 or out.device != dev or not out.is_contiguous()
+                or tuple(out.shape) != (N, Ci, H, W)):
+            raise ValueError("out must be a contiguous float32 [N,Ci,H,W] tensor on %s" % dev)
+    with torch.cuda.device(dev):
+        s = stream if stream is not None else torch.cuda.current_stream(dev)
+        fn = lib.conv2d_grad_input_bf16 if grad_out.dtype == torch.bfloat16 else lib.conv2d_grad_input
+        code = fn(ctypes.c_void_p(grad_out.data_ptr()), ctypes.c_void_p(weight.data_ptr()),
+                  ctypes.c_void_p(out.data_ptr()), ctypes.byref(p),
+                  ctypes.c_void_p(s.cuda_stream))
+    _check(code)
+    return out

@@ -1,0 +1,44 @@
+// gi_common.h -- structures shared by the planner (host) and the kernels.
+//
+// Phase split.  With stride s, input pixel (ih, iw) only meets taps kh with
+// ih + pad_h - kh divisible by s (meganeura conv2d_grad_input_gemm.wgsl,
+// general-stride branch of the B gather; doppler conv2d_backward_input.wgsl,
+// the divisibility guards).  Group input rows by their residue rho = ih mod s:
+// writing ih = rho + s*a, the contributing taps are kh = r + s*j with
+// r = (rho + pad_h) mod s and j = 0, 1, ..., and the output row they read is
+//     oh = (ih + pad_h - kh) / s = a + q - j,   q = (rho + pad_h) div s.
+// The same holds along w.  Each residue pair (rho_h, rho_w) is therefore a
+// dense stride-1 sub-problem over its own pixels (a, b) and its own taps
+// (j, jw), with K = Co * J_h * J_w.  Stride 1 is the single phase rho = r = 0,
+// q = pad.  A phase with no taps (J = 0, when the kernel is shorter than the
+// stride) still owns its pixels and writes zeros there.
+#pragma once
+
+#include <stdint.h>
+
+namespace gi {
+
+constexpr int kMaxPhasesPerLaunch = 16;
+
+struct Phase {
+    int32_t rho_h, rho_w;   // input-pixel residues mod stride
+    int32_t q_h, q_w;       // (rho + pad) div stride
+    int32_t r_h, r_w;       // first tap of the phase: (rho + pad) mod stride
+    int32_t J_h, J_w;       // taps of the phase per dimension
+    int32_t Ha, Wb;         // pixels of the phase per image: rows, columns
+    int32_t tile_begin;     // first pixel tile of the phase within its launch
+    int32_t pad_;           // keeps the struct 48 bytes
+};
+
+// Kernel arguments of one launch of a phase-split GEMM kernel.
+struct GemmArgs {
+    const void *grad_out;   // [N, Co, oH, oW], fp32 or bf16
+    const void *wt;         // weight in kernel order (see prologue), fp32 or bf16
+    float *dst;             // [N, Ci, H, W] fp32
+    int32_t N, Ci, H, W, Co, kH, kW, stride, oH, oW;
+    int32_t nphases;
+    int32_t ci_tiles;
+    Phase ph[kMaxPhasesPerLaunch];
+};
+
+}  // namespace gi

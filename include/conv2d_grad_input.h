@@ -1,0 +1,161 @@
+/*
+ * conv2d_grad_input.h -- C ABI of the MI355X (gfx950) conv2d grad_input library.
+ *
+ * The operation
+ * -------------
+ * The gradient of a 2-D convolution (cross-correlation, no dilation, one group)
+ * with respect to its input.  For every batch item n, input channel ci and
+ * input pixel (ih, iw):
+ *
+ *   dst[n,ci,ih,iw] = sum over co < Co, kh < kH, kw < kW of
+ *                     grad_out[n,co,oh,ow] * weight[co,ci,kh,kw]
+ *
+ * where a = ih + pad_h - kh and b = iw + pad_w - kw are both >= 0 and
+ * divisible by the stride, and oh = a / stride < oH, ow = b / stride < oW.
+ * Terms that fail a condition are absent; a pixel with none gets 0.
+ *
+ * This is the direct kernel of doppler conv2d_backward_input.wgsl (an input
+ * pixel sums the output gradients it fed in the forward pass, the transposed
+ * convolution of its header comment), batched and with per-dimension padding,
+ * and the general-stride branch of the B-tile gather of meganeura
+ * conv2d_grad_input_gemm.wgsl.  The library computes it as the implicit GEMM
+ * of that shader's header comment, C[Ci, H*W] = A[Ci, Co*kH*kW] x
+ * B[Co*kH*kW, H*W] per batch item with A the weight read as [Ci, Co*kH*kW]
+ * and B the on-the-fly im2col of grad_out, after splitting a strided problem
+ * into stride*stride dense sub-problems (one per input-pixel residue), so
+ * that taps that would land between output pixels are never multiplied.
+ *
+ * Layouts and ownership
+ * ---------------------
+ * All tensors are dense, row-major, on the device the call runs on:
+ *   grad_out [N, Co, oH, oW]   read only
+ *   weight   [Co, Ci, kH, kW]  read only
+ *   dst      [N, Ci, H, W]     fp32, written (every element, never accumulated)
+ * The caller allocates and owns all three; the library never frees them.  dst
+ * must not overlap either input.  The library allocates a small scratch
+ * buffer (the weight in kernel order, Co*Ci*kH*kW elements) stream-ordered on
+ * `stream` (hipMallocAsync / hipFreeAsync), so calls on different streams
+ * share no state.  Both convolution stride dimensions take `stride`; padding
+ * is symmetric per dimension (pad_h top and bottom, pad_w left and right).
+ *
+ * Asynchrony and errors
+ * ---------------------
+ * Calls enqueue work on `stream` (0 = the device's null stream) and return
+ * without waiting; dst is valid once the stream has reached that point.  The
+ * current HIP device must own the buffers.  All arguments are checked on the
+ * host before anything is enqueued: on CONV2D_GI_EINVAL or
+ * CONV2D_GI_EUNSUPPORTED nothing is launched and dst is untouched.
+ * CONV2D_GI_EHIP reports a HIP runtime error from an allocation or launch
+ * (the error string of the last one is kept for conv2d_gi_last_hip_error).
+ */
+#ifndef CONV2D_GRAD_INPUT_H
+#define CONV2D_GRAD_INPUT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define CONV2D_GI_API __attribute__((visibility("default")))
+#else
+#define CONV2D_GI_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * Problem shape.  Field names follow the Params block of meganeura
+ * conv2d_grad_input_gemm.wgsl (batch, in_channels, in_h, in_w, out_channels,
+ * kernel_h, kernel_w, stride, padding_h, padding_w, out_h, out_w).  H and W
+ * are given, not derived, because with stride > 1 several input sizes give the
+ * same oH and oW.
+ */
+typedef struct conv2d_gi_params {
+    int32_t N;        /* batch items; 0 is allowed (nothing is done)          */
+    int32_t Ci;       /* input channels = channels of dst; 0 allowed          */
+    int32_t H, W;     /* input (dst) spatial size, >= 1                       */
+    int32_t Co;       /* output channels; 0 allowed (dst is zero-filled)      */
+    int32_t kH, kW;   /* kernel size, >= 1                                    */
+    int32_t stride;   /* one stride for both dimensions, >= 1                 */
+    int32_t pad_h;    /* zero padding above and below, >= 0                   */
+    int32_t pad_w;    /* zero padding left and right, >= 0                    */
+    int32_t oH, oW;   /* grad_out spatial size; must equal
+                         (H + 2*pad_h - kH)/stride + 1 and
+                         (W + 2*pad_w - kW)/stride + 1 (floor division), >= 1 */
+} conv2d_gi_params;
+
+/* Status codes returned by every entry point. */
+enum {
+    CONV2D_GI_OK = 0,
+    CONV2D_GI_EINVAL = 1,       /* bad pointer or shape; nothing launched      */
+    CONV2D_GI_EUNSUPPORTED = 2, /* valid but beyond the library's index width  */
+    CONV2D_GI_EHIP = 3          /* HIP runtime error from allocation or launch */
+};
+
+/* Kernel variants, for conv2d_gi_set_variant and conv2d_gi_plan. */
+enum {
+    CONV2D_GI_VARIANT_AUTO = 0,    /* the planner chooses                      */
+    CONV2D_GI_VARIANT_GENERIC = 1  /* any shape: phase split, gathered B tile  */
+};
+
+/*
+ * fp32 grad_input.  grad_out and weight fp32, dst fp32 (layouts above).
+ * Contraction on the fp32 matrix cores, fp32 accumulation.
+ * Pointers may be NULL only when the tensor they point to has no elements.
+ */
+CONV2D_GI_API int conv2d_grad_input(const float *grad_out, const float *weight, float *dst,
+                      const conv2d_gi_params *p, hipStream_t stream);
+
+/*
+ * bf16-input grad_input.  grad_out and weight hold bf16 bit patterns (the top
+ * 16 bits of an IEEE float32); dst is fp32.  Products of two bf16 values are
+ * exact in fp32; accumulation is fp32 on the bf16 matrix cores.
+ */
+CONV2D_GI_API int conv2d_grad_input_bf16(const uint16_t *grad_out, const uint16_t *weight,
+                           float *dst, const conv2d_gi_params *p,
+                           hipStream_t stream);
+
+/* Host-only check of a shape, as done by the entry points (no HIP call). */
+CONV2D_GI_API int conv2d_gi_validate(const conv2d_gi_params *p);
+
+/* Static text for a status code. */
+CONV2D_GI_API const char *conv2d_gi_strerror(int code);
+
+/* Text of the last HIP error seen by this thread's calls ("" if none). */
+CONV2D_GI_API const char *conv2d_gi_last_hip_error(void);
+
+/*
+ * Test and diagnostic hook: force a kernel variant for later calls in this
+ * process (CONV2D_GI_VARIANT_AUTO restores the planner).  Returns the
+ * previous setting, or -1 for an unknown variant (setting unchanged).
+ */
+CONV2D_GI_API int conv2d_gi_set_variant(int variant);
+
+/*
+ * Host-only: describe the plan the entry point would run for this shape
+ * (dtype_bf16 = 0 for fp32 inputs, 1 for bf16), as text written into buf
+ * (NUL-terminated, truncated to len).  Returns a status code.
+ */
+CONV2D_GI_API int conv2d_gi_plan(const conv2d_gi_params *p, int dtype_bf16, char *buf,
+                   size_t len);
+
+/*
+ * Measurement hook: when both events are non-NULL, later calls from this
+ * thread record `begin` on their stream just before the first GEMM kernel
+ * launch and `end` just after the last one, so the caller can time the
+ * contraction kernels apart from the weight reorder that precedes them.
+ * NULL, NULL switches it off.  The events (hipEvent_t) stay the caller's.
+ */
+CONV2D_GI_API void conv2d_gi_set_profile_events(hipEvent_t begin, hipEvent_t end);
+
+/* Library version as "major.minor.patch". */
+CONV2D_GI_API const char *conv2d_gi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CONV2D_GRAD_INPUT_H */

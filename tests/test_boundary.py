@@ -1,0 +1,171 @@
+"""Host-side tests of the C-ABI library: it loads, exports every entry point
+that include/*.h declares, and rejects bad arguments before any HIP call.
+
+No test here launches a kernel, so they run without a GPU.
+"""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import conv2d_backward_amd as gi
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gi.library_path):
+        from conv2d_backward_amd import build
+        build.build()
+    return gi.load_library()
+
+
+def declared_functions():
+    names = []
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        names += re.findall(r"^CONV2D_GI_API\s+[\w\s\*]*?\b(\w+)\s*\(", text, re.M)
+    return names
+
+
+def test_header_declares_entry_points():
+    names = declared_functions()
+    assert "conv2d_grad_input" in names and "conv2d_grad_input_bf16" in names
+    assert len(names) == len(set(names))
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(gi.exported_names()) <= set(declared_functions())
+
+
+def test_version(lib):
+    assert re.fullmatch(r"\d+\.\d+\.\d+", lib.conv2d_gi_version().decode())
+
+
+def test_strerror(lib):
+    for code in (gi.OK, gi.EINVAL, gi.EUNSUPPORTED, gi.EHIP):
+        assert lib.conv2d_gi_strerror(code)
+    assert b"unknown" in lib.conv2d_gi_strerror(99)
+
+
+def test_validate_accepts_workloads(lib):
+    for wl in workloads.WORKLOADS:
+        s = wl.shape
+        assert gi.validate(gi.make_params(*s.as_tuple()[:10])) == gi.OK, wl.name
+    for s in workloads.sweep_shapes():
+        assert gi.validate(gi.make_params(*s.as_tuple()[:10])) == gi.OK, s
+
+
+BAD = [
+    dict(H=0), dict(W=-1), dict(kH=0), dict(kW=0), dict(stride=0), dict(stride=-2),
+    dict(pad_h=-1), dict(pad_w=-1), dict(N=-1), dict(Ci=-1), dict(Co=-1),
+    dict(oH=57), dict(oW=55), dict(oH=0),
+    dict(kH=61, pad_h=1, oH=1),   # H + 2*pad < kH: empty forward output
+]
+
+
+@pytest.mark.parametrize("change", BAD, ids=lambda d: ",".join("%s=%s" % kv for kv in d.items()))
+def test_validate_rejects(lib, change):
+    base = dict(N=2, Ci=3, H=56, W=56, Co=4, kH=3, kW=3, stride=1, pad_h=1, pad_w=1, oH=56, oW=56)
+    base.update(change)
+    p = gi.Conv2dGiParams(*[base[f] for f in gi._FIELDS])
+    assert gi.validate(p) == gi.EINVAL
+
+
+def test_validate_index_width(lib):
+    p = gi.make_params(1, 70000, 200, 200, 1, 1, 1, 1, 0, 0)  # Ci*H*W > 2^31
+    assert gi.validate(p) == gi.EUNSUPPORTED
+    p = gi.make_params(70000, 1, 200, 200, 1, 1, 1, 1, 0, 0)  # N*H*W > 2^31
+    assert gi.validate(p) == gi.EUNSUPPORTED
+
+
+def test_validate_null(lib):
+    assert lib.conv2d_gi_validate(None) == gi.EINVAL
+
+
+def _call(lib, fn, g, w, d, p):
+    return getattr(lib, fn)(ctypes.c_void_p(g), ctypes.c_void_p(w), ctypes.c_void_p(d),
+                            ctypes.byref(p) if p is not None else None, None)
+
+
+@pytest.mark.parametrize("fn", ["conv2d_grad_input", "conv2d_grad_input_bf16"])
+def test_entry_rejects_before_any_hip_call(lib, fn):
+    """Invalid calls return EINVAL without touching the (fake) pointers."""
+    good = gi.make_params(2, 3, 8, 8, 4, 3, 3, 1, 1, 1)
+    fake = 0x1000
+    assert _call(lib, fn, fake, fake, fake, None) == gi.EINVAL
+    bad = gi.make_params(2, 3, 8, 8, 4, 3, 3, 1, 1, 1, oH=9)
+    assert _call(lib, fn, fake, fake, fake, bad) == gi.EINVAL
+    assert _call(lib, fn, 0, fake, fake, good) == gi.EINVAL
+    assert _call(lib, fn, fake, 0, fake, good) == gi.EINVAL
+    assert _call(lib, fn, fake, fake, 0, good) == gi.EINVAL
+    big = gi.make_params(1, 70000, 200, 200, 1, 1, 1, 1, 0, 0)
+    assert _call(lib, fn, fake, fake, fake, big) == gi.EUNSUPPORTED
+
+
+@pytest.mark.parametrize("fn", ["conv2d_grad_input", "conv2d_grad_input_bf16"])
+def test_empty_outputs_do_nothing(lib, fn):
+    """N = 0 or Ci = 0: dst has no elements, the call succeeds with no work.
+    Null is accepted exactly for the tensors that have no elements (a fake
+    pointer stands for the non-empty one, which is never read)."""
+    fake = 0x1000
+    # N = 0: grad_out and dst are empty, the weight is not
+    assert _call(lib, fn, 0, fake, 0, gi.make_params(0, 3, 8, 8, 4, 3, 3, 1, 1, 1)) == gi.OK
+    assert _call(lib, fn, 0, 0, 0, gi.make_params(0, 3, 8, 8, 4, 3, 3, 1, 1, 1)) == gi.EINVAL
+    # Ci = 0: weight and dst are empty, grad_out is not
+    assert _call(lib, fn, fake, 0, 0, gi.make_params(2, 0, 8, 8, 4, 3, 3, 1, 1, 1)) == gi.OK
+
+
+def test_set_variant(lib):
+    old = gi.set_variant(gi.VARIANT_GENERIC)
+    try:
+        assert gi.set_variant(gi.VARIANT_AUTO) == gi.VARIANT_GENERIC
+        assert lib.conv2d_gi_set_variant(12345) == -1
+    finally:
+        gi.set_variant(old)
+
+
+def test_plan_phases(lib):
+    """The planner splits a stride-s problem into s*s residue classes with the
+    tap counts of the phase split (e.g. 3x3, stride 2, pad 1: 1x1, 1x2, 2x1, 2x2)."""
+    s = workloads.BY_NAME["strided_downsample"].shape
+    txt = gi.plan(gi.make_params(*s.as_tuple()[:10]))
+    phases = re.findall(r"phase\((\d+),(\d+)\) taps=(\d+)x(\d+) px=(\d+)x(\d+)", txt)
+    assert len(phases) == 4
+    taps = {(int(a), int(b)): (int(c), int(d)) for a, b, c, d, _, _ in phases}
+    # rho = 0: (0 + 1) mod 2 = 1 -> taps kh in {1}; rho = 1: (1 + 1) mod 2 = 0 -> kh in {0, 2}
+    assert taps == {(0, 0): (1, 1), (0, 1): (1, 2), (1, 0): (2, 1), (1, 1): (2, 2)}
+    assert all((int(e), int(f)) == (28, 28) for *_, e, f in phases)
+    # every tap of the kernel is in exactly one phase per dimension
+    s1 = workloads.BY_NAME["stem_7x7_s2"].shape
+    txt = gi.plan(gi.make_params(*s1.as_tuple()[:10]))
+    ph = re.findall(r"phase\((\d+),(\d+)\) taps=(\d+)x(\d+)", txt)
+    assert sum(int(c) for a, b, c, d in ph if b == "0") == 7
+    # kernel shorter than the stride: some phases get no taps but keep their pixels
+    txt = gi.plan(gi.make_params(1, 2, 9, 9, 3, 2, 2, 3, 0, 0))
+    ph = re.findall(r"phase\((\d+),(\d+)\) taps=(\d+)x(\d+) px=(\d+)x(\d+)", txt)
+    assert len(ph) == 9
+    assert sum(1 for p in ph if p[2] == "0" or p[3] == "0") == 5
+    assert sum(int(p[4]) * int(p[5]) for p in ph) == 81
+
+
+def test_binding_rejects_cpu_tensors(lib):
+    torch = pytest.importorskip("torch")
+    g = torch.zeros(1, 2, 4, 4)
+    w = torch.zeros(2, 3, 3, 3)
+    with pytest.raises(ValueError):
+        gi.grad_input(g, w, stride=1, padding=1, input_hw=(4, 4))
+
+
+def test_product_path_does_not_import_oracle():
+    """The library package and its binding never reach the CPU oracle."""
+    for path in glob.glob(os.path.join(ROOT, "conv2d_backward_amd", "**", "*"), recursive=True):
+        if os.path.isfile(path) and path.endswith((".py", ".cpp", ".hip", ".h")):
+            text = open(path).read()
+            assert "oracle" not in text.lower(), path

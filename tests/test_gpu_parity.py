@@ -1,0 +1,220 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Criteria (element by element, S = sum |grad_out * weight| over the element's terms):
+  fp32 inputs:  |gpu - oracle| <= 1e-5 * S + 1e-6
+  bf16 inputs:  ||gpu - oracle||_2 <= 1e-2 * ||oracle||_2  and
+                |gpu - oracle| <= 1e-2 * S + 1e-6        (oracle on the same bf16 values)
+dst is pre-filled with NaN (an unwritten element fails) and framed by guard
+bands that must stay untouched (an out-of-bounds write fails).
+"""
+import os
+import sys
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import conv2d_backward_amd as gi  # noqa: E402
+
+F32_REL, F32_ABS = 1e-5, 1e-6
+BF16_REL, BF16_ABS = 1e-2, 1e-6
+GUARD = 4096
+SENTINEL = 12345.0
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gi.load_library()
+    return torch.device("cuda:0")
+
+
+def run_gpu(g_np, w_np, shape, dtype, variant=gi.VARIANT_AUTO, stream=None):
+    """Run the library on numpy inputs; returns (dst numpy float64, guard ok)."""
+    dev = torch.device("cuda:0")
+    if dtype == "bf16":
+        g = torch.from_numpy(g_np.view(np.int16)).to(dev).view(torch.bfloat16)
+        w = torch.from_numpy(w_np.view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        g = torch.from_numpy(np.ascontiguousarray(g_np, dtype=np.float32)).to(dev)
+        w = torch.from_numpy(np.ascontiguousarray(w_np, dtype=np.float32)).to(dev)
+    n_dst = int(np.prod(shape.dst_shape))
+    buf = torch.full((n_dst + 2 * GUARD,), SENTINEL, dtype=torch.float32, device=dev)
+    buf[GUARD:GUARD + n_dst] = float("nan")
+    out = buf[GUARD:GUARD + n_dst].view(shape.dst_shape)
+    old = gi.set_variant(variant)
+    try:
+        gi.grad_input(g, w, stride=shape.stride, padding=(shape.pad_h, shape.pad_w),
+                      input_hw=(shape.H, shape.W), out=out, stream=stream)
+        torch.cuda.synchronize()
+    finally:
+        gi.set_variant(old)
+    host = buf.cpu().numpy()
+    guard_ok = bool(np.all(host[:GUARD] == SENTINEL) and np.all(host[GUARD + n_dst:] == SENTINEL))
+    return host[GUARD:GUARD + n_dst].astype(np.float64).reshape(shape.dst_shape), guard_ok
+
+
+def oracle_inputs(g_np, w_np, dtype):
+    if dtype == "bf16":
+        return workloads.bf16_to_f32(g_np), workloads.bf16_to_f32(w_np)
+    return g_np, w_np
+
+
+def check(got, ref, S, dtype, what):
+    assert not np.isnan(got).any(), "%s: unwritten (NaN) elements" % what
+    err = np.abs(got - ref)
+    if dtype == "bf16":
+        bound = BF16_REL * S + BF16_ABS
+        nrm = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300)
+        assert nrm <= BF16_REL, "%s: normwise rel err %.3g" % (what, nrm)
+    else:
+        bound = F32_REL * S + F32_ABS
+    bad = err > bound
+    if bad.any():
+        i = int(np.argmax(err - bound))
+        raise AssertionError("%s: %d elements out of tolerance; worst flat %d got %r want %r S %r"
+                             % (what, int(bad.sum()), i, got.ravel()[i], ref.ravel()[i],
+                                S.ravel()[i]))
+    return float(np.max(err / (bound)))
+
+
+def full_parity(shape, seed, dtype, variant=gi.VARIANT_AUTO, dist="uniform"):
+    g, w = workloads.make_case(shape, seed, dist)
+    if dtype == "bf16":
+        g, w = workloads.bf16_bits(g), workloads.bf16_bits(w)
+    say("case %s dtype=%s variant=%d seed=%d" % (shape, dtype, variant, seed))
+    got, guard_ok = run_gpu(g, w, shape, dtype, variant)
+    assert guard_ok, "write outside dst"
+    go, wo = oracle_inputs(g, w, dtype)
+    ref, S = oracle.grad_input(go, wo, shape.stride, (shape.pad_h, shape.pad_w),
+                               (shape.H, shape.W))
+    return check(got, ref, S, dtype, str(shape))
+
+
+SWEEP = workloads.sweep_shapes()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("idx", range(len(SWEEP)))
+def test_sweep(idx, dtype):
+    full_parity(SWEEP[idx], 100 + idx, dtype)
+
+
+# Mid-size shapes: several tiles in every direction plus ragged tails.
+MID = [
+    workloads.Shape(2, 130, 20, 21, 96, 3, 3, 1, 1, 1),
+    workloads.Shape(3, 64, 17, 17, 80, 1, 7, 1, 0, 3),
+    workloads.Shape(2, 100, 23, 22, 72, 3, 3, 2, 1, 1),
+    workloads.Shape(2, 3, 45, 44, 64, 7, 7, 2, 3, 3),
+    workloads.Shape(1, 200, 9, 9, 300, 3, 3, 1, 1, 1),
+    workloads.Shape(2, 48, 30, 30, 40, 5, 5, 3, 2, 2),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("idx", range(len(MID)))
+def test_mid(idx, dtype):
+    full_parity(MID[idx], 500 + idx, dtype, dist="normal")
+
+
+@pytest.mark.parametrize("variant", [gi.VARIANT_GENERIC])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_forced_variant(variant, dtype):
+    for i, s in enumerate([SWEEP[4], SWEEP[9], MID[0], MID[2]]):
+        full_parity(s, 900 + i, dtype, variant)
+
+
+def test_tiny_workload_full():
+    wl = workloads.BY_NAME["tiny"]
+    s = wl.shape
+    g, w = workloads.make_inputs(wl)
+    got, ok = run_gpu(g, w, s, "f32")
+    assert ok
+    ref, S = oracle.grad_input(g, w, s.stride, (s.pad_h, s.pad_w), (s.H, s.W))
+    check(got, ref, S, "f32", "tiny")
+
+
+def sample_indices(shape, rng, count=6000):
+    """Random flat indices plus structured ones: every corner/edge pixel of the
+    first and last image on the first and last channels, and channel tile edges."""
+    N, Ci, H, W = shape.dst_shape
+    idx = list(rng.integers(0, N * Ci * H * W, size=count))
+    for n in {0, N - 1}:
+        for ci in sorted({0, 31, 32, 63, 64, Ci - 1} & set(range(Ci))):
+            for ih in {0, 1, H // 2, H - 2, H - 1} & set(range(H)):
+                for iw in {0, 1, W // 2, W - 2, W - 1} & set(range(W)):
+                    idx.append(((n * Ci + ci) * H + ih) * W + iw)
+    return np.array(idx, dtype=np.int64)
+
+
+@pytest.mark.parametrize("name", [w.name for w in workloads.WORKLOADS if w.name != "tiny"])
+def test_workload_sampled(name):
+    """Full-size workloads, launched as the benchmark launches them; checked on
+    sampled elements against the oracle, and every element for NaN (unwritten)."""
+    wl = workloads.BY_NAME[name]
+    s = wl.shape
+    g, w = workloads.make_inputs(wl)
+    say("workload %s" % name)
+    got, ok = run_gpu(g, w, s, wl.dtype)
+    assert ok, "write outside dst"
+    assert not np.isnan(got).any()
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    idx = sample_indices(s, rng)
+    go, wo = oracle_inputs(g, w, wl.dtype)
+    ref, S = oracle.grad_input_at(go, wo, s.stride, (s.pad_h, s.pad_w), (s.H, s.W), idx)
+    check(got.ravel()[idx], ref, S, wl.dtype, name)
+
+
+def test_deterministic():
+    s = MID[0]
+    g, w = workloads.make_case(s, 77, "normal")
+    a, _ = run_gpu(g, w, s, "f32")
+    b, _ = run_gpu(g, w, s, "f32")
+    assert np.array_equal(a, b)
+
+
+def test_zero_output_channels_zero_fill():
+    """Co = 0: every sum is empty, so dst must be all zeros (not left as is)."""
+    s = workloads.Shape(2, 5, 6, 6, 0, 3, 3, 1, 1, 1)
+    g = np.zeros(s.grad_out_shape, np.float32)
+    w = np.zeros(s.weight_shape, np.float32)
+    got, ok = run_gpu(g, w, s, "f32")
+    assert ok and np.array_equal(got, np.zeros(s.dst_shape))
+
+
+def test_side_stream():
+    s = SWEEP[6]
+    g, w = workloads.make_case(s, 5, "uniform")
+    side = torch.cuda.Stream()
+    got, ok = run_gpu(g, w, s, "f32", stream=side)
+    ref, S = oracle.grad_input(g, w, s.stride, (s.pad_h, s.pad_w), (s.H, s.W))
+    assert ok
+    check(got, ref, S, "f32", "side stream")
+
+
+def test_invalid_leaves_dst_untouched():
+    """H = 9 with pad 1 and a 3x3 kernel gives oH = 9, but grad_out has oH = 8:
+    the call fails with EINVAL and launches nothing."""
+    dev = torch.device("cuda:0")
+    g = torch.randn(1, 4, 8, 8, device=dev)
+    w = torch.randn(4, 3, 3, 3, device=dev)
+    out = torch.full((1, 3, 9, 8), 7.0, device=dev)
+    with pytest.raises(gi.Conv2dGiError) as e:
+        gi.grad_input(g, w, stride=1, padding=1, input_hw=(9, 8), out=out)
+    assert e.value.code == gi.EINVAL
+    with pytest.raises(ValueError):
+        gi.grad_input(g, w.to(torch.bfloat16), stride=1, padding=1, input_hw=(8, 8))
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)
