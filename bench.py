@@ -63,6 +63,38 @@ def device_inputs(wl, torch, dev):
     return (g, w), tg, tw, out
 
 
+class HipEvents:
+    """Raw HIP events (libamdhip64 via ctypes): the library records them itself
+    on its launch stream, which torch.cuda.Event (created lazily) cannot see."""
+
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        ev = self.ct.c_void_p()
+        rc = self.hip.hipEventCreate(self.ct.byref(ev))
+        if rc != 0:
+            raise RuntimeError("hipEventCreate failed: %d" % rc)
+        return ev
+
+    def elapsed_ms(self, a, b):
+        ms = self.ct.c_float()
+        rc = self.hip.hipEventElapsedTime(self.ct.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError("hipEventElapsedTime failed: %d" % rc)
+        return float(ms.value)
+
+    def destroy(self, ev):
+        self.hip.hipEventDestroy(ev)
+
+
 def time_workload(wl, steps, warmup, torch, gi, dev):
     """Returns dict with whole-call ms, GEMM-kernel ms (HIP events), flops."""
     s = wl.shape
@@ -76,22 +108,25 @@ def time_workload(wl, steps, warmup, torch, gi, dev):
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
-    kb = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ke = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
+    hev = HipEvents()
+    kb = [hev.create() for _ in range(steps)]
+    ke = [hev.create() for _ in range(steps)]
+    t0, t1 = hev.create(), hev.create()
+    sp = stream.cuda_stream
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    t0.record(stream)
+    hev.hip.hipEventRecord(t0, sp)
     for i in range(steps):
         gi.set_profile_events(kb[i], ke[i])
         call()
-    t1.record(stream)
+    hev.hip.hipEventRecord(t1, sp)
     gi.set_profile_events(None, None)
     torch.cuda.synchronize()
     wall1 = time.perf_counter()
-    total_ms = t0.elapsed_time(t1)
-    kern_ms = [kb[i].elapsed_time(ke[i]) for i in range(steps)]
+    total_ms = hev.elapsed_ms(t0, t1)
+    kern_ms = [hev.elapsed_ms(kb[i], ke[i]) for i in range(steps)]
+    for ev in kb + ke + [t0, t1]:
+        hev.destroy(ev)
     return dict(ms_per_step=total_ms / steps, kernel_ms=float(np.mean(kern_ms)),
                 kernel_ms_min=float(np.min(kern_ms)), wall_ms=(wall1 - wall0) * 1e3 / steps,
                 flops=s.eff_flops)

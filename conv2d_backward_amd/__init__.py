@@ -132,13 +132,12 @@ def set_variant(variant: int) -> int:
 
 
 def set_profile_events(begin, end):
-    """Record torch.cuda.Event ``begin``/``end`` around the GEMM launches of later
-    calls from this thread (None, None switches it off)."""
+    """Record the hipEvent_t handles ``begin``/``end`` (ints or ctypes pointers)
+    around the GEMM launches of later calls from this thread; None switches it off."""
     if begin is None or end is None:
         load_library().conv2d_gi_set_profile_events(None, None)
         return
-    load_library().conv2d_gi_set_profile_events(ctypes.c_void_p(begin.cuda_event),
-                                                ctypes.c_void_p(end.cuda_event))
+    load_library().conv2d_gi_set_profile_events(begin, end)
 
 
 def grad_input(grad_out, weight, *, stride: int, padding, input_hw, out=None, stream=None):
