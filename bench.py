@@ -174,6 +174,8 @@ def main():
     r = time_workload(wl, args.steps, args.warmup, torch, gi, dev)
     value = r["flops"] / (r["ms_per_step"] * 1e-3) / 1e12
     peak = PEAK_TFLOPS[wl.dtype]
+    plan_desc = gi.plan(gi.make_params(*s.as_tuple()[:10]), wl.dtype == "bf16")
+    variant = plan_desc.split()[0].split("=")[1]
     achieved = r["flops"] / (r["kernel_ms"] * 1e-3) / 1e12
     line = {
         "metric": METRIC,
@@ -191,10 +193,10 @@ def main():
         "config": {"workload": wl.name, "N": s.N, "Ci": s.Ci, "Co": s.Co, "H": s.H, "W": s.W,
                    "kH": s.kH, "kW": s.kW, "stride": s.stride, "pad_h": s.pad_h,
                    "pad_w": s.pad_w, "oH": s.oH, "oW": s.oW, "eff_gflop": s.eff_flops / 1e9,
-                   "plan": gi.plan(gi.make_params(*s.as_tuple()[:10]), wl.dtype == "bf16")},
+                   "plan": plan_desc},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
-                     "kernel": "gi_generic_%s" % wl.dtype,
+                     "kernel": "gi_%s_%s" % (variant, wl.dtype),
                      "kernel_ms": round(r["kernel_ms"], 5),
                      "per_unit": "2*Ci*kH*kW*Co flops per output pixel (n,oh,ow)",
                      "units_per_launch": s.N * s.oH * s.oW},

@@ -17,15 +17,15 @@ import os
 
 __all__ = [
     "grad_input", "Conv2dGiParams", "Conv2dGiError", "LibraryNotBuilt", "load_library",
-    "make_params", "validate", "plan", "set_variant", "set_profile_events", "library_path", "exported_names",
-    "OK", "EINVAL", "EUNSUPPORTED", "EHIP", "VARIANT_AUTO", "VARIANT_GENERIC",
+    "make_params", "validate", "plan", "set_variant", "set_halo_tile", "set_profile_events", "library_path", "exported_names",
+    "OK", "EINVAL", "EUNSUPPORTED", "EHIP", "VARIANT_AUTO", "VARIANT_GENERIC", "VARIANT_HALO",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_PKG, "libconv2d_gi.so")
 
 OK, EINVAL, EUNSUPPORTED, EHIP = 0, 1, 2, 3
-VARIANT_AUTO, VARIANT_GENERIC = 0, 1
+VARIANT_AUTO, VARIANT_GENERIC, VARIANT_HALO = 0, 1, 2
 
 _FIELDS = ("N", "Ci", "H", "W", "Co", "kH", "kW", "stride", "pad_h", "pad_w", "oH", "oW")
 
@@ -77,6 +77,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.conv2d_gi_set_variant.restype = ctypes.c_int
     lib.conv2d_gi_plan.argtypes = [PP, ctypes.c_int, ctypes.c_char_p, ctypes.c_size_t]
     lib.conv2d_gi_plan.restype = ctypes.c_int
+    lib.conv2d_gi_set_halo_tile.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    lib.conv2d_gi_set_halo_tile.restype = ctypes.c_int
     lib.conv2d_gi_set_profile_events.argtypes = [P, P]
     lib.conv2d_gi_set_profile_events.restype = None
     lib.conv2d_gi_version.argtypes = []
@@ -90,7 +92,8 @@ def exported_names():
     """Names of the C entry points the binding wraps."""
     return ["conv2d_grad_input", "conv2d_grad_input_bf16", "conv2d_gi_validate",
             "conv2d_gi_strerror", "conv2d_gi_last_hip_error", "conv2d_gi_set_variant",
-            "conv2d_gi_plan", "conv2d_gi_set_profile_events", "conv2d_gi_version"]
+            "conv2d_gi_plan", "conv2d_gi_set_halo_tile", "conv2d_gi_set_profile_events",
+            "conv2d_gi_version"]
 
 
 def make_params(N, Ci, H, W, Co, kH, kW, stride, pad_h, pad_w, oH=None, oW=None):
@@ -129,6 +132,11 @@ def set_variant(variant: int) -> int:
     if old < 0:
         raise ValueError("unknown variant %r" % (variant,))
     return old
+
+
+def set_halo_tile(nb: int = 0, tile_rows: int = 0, tile_cols: int = 0):
+    """Force the HALO variant's pixel tile (test hook); set_halo_tile() restores the planner."""
+    _check(load_library().conv2d_gi_set_halo_tile(int(nb), int(tile_rows), int(tile_cols)))
 
 
 def set_profile_events(begin, end):

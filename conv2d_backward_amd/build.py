@@ -24,9 +24,11 @@ ARCH = "gfx950"
 SOURCES = [
     "api.cpp",
     "kernels_generic.hip",
+    "kernels_halo_f32.hip",
 ]
 
-COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", "-Werror", "-I", INCLUDE, "-I", CSRC]
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", "-Werror",
+          "--offload-arch=" + ARCH, "-I", INCLUDE, "-I", CSRC]
 # Device code: gfx950 only; packed fp32 instructions are switched off.
 DEVICE = ["-x", "hip", "--offload-arch=" + ARCH,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -5,6 +5,7 @@
 // and the options of doppler conv2d_backward.d.ts (Conv2DBackwardOptions).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdio>
 #include <cstring>
@@ -21,6 +22,8 @@ using gi::GemmArgs;
 using gi::Phase;
 
 std::atomic<int> g_variant{CONV2D_GI_VARIANT_AUTO};
+// Forced halo tile (test hook): NB pixel blocks, TR x TC phase-grid pixels; 0 = planner.
+std::atomic<int> g_tile_nb{0}, g_tile_tr{0}, g_tile_tc{0};
 thread_local char g_last_hip[256] = "";
 thread_local hipEvent_t g_prof_begin = nullptr, g_prof_end = nullptr;
 
@@ -82,19 +85,165 @@ struct Launch {
     int tiles_x;
 };
 
+// A halo-kernel plan (fp32): one launch over every phase.
+struct HaloPlan {
+    gi::HaloArgs args{};
+    int nb = 0, cfg = -1, bl = 0, tiles = 0, ci_tiles = 0;
+    size_t lds = 0;
+    double cost = 0.0;
+    int64_t ws_floats = 0;  // weight image
+};
+
 struct Plan {
     int variant = CONV2D_GI_VARIANT_GENERIC;
     bool bf16 = false;
     size_t ws_bytes = 0;  // reordered weight
-    std::vector<Launch> launches;
+    std::vector<Launch> launches;  // generic
+    HaloPlan halo;                 // halo
 };
 
-Plan make_plan(const conv2d_gi_params &p, bool bf16) {
-    Plan plan;
-    plan.bf16 = bf16;
-    plan.variant = CONV2D_GI_VARIANT_GENERIC;  // the only variant so far
-    plan.ws_bytes = (size_t)p.Co * p.Ci * p.kH * p.kW * (bf16 ? 2 : 4);
-    std::vector<Phase> phases = make_phases(p);
+constexpr int kCUs = 256;               // MI355X compute units
+constexpr size_t kLdsBytes = 160 * 1024;
+
+
+// Smallest p >= v with p % m == r (0 <= r < m).
+int round_to_residue(int v, int m, int r) {
+    int p = v + ((r - v % m) % m + m) % m;
+    return p;
+}
+
+// Halo plan for fp32: choose the pixel tile (TR x TC of the phase grid, at
+// most NB*16 pixels) that minimises the work of the busiest compute unit,
+// ceil(work-groups / CUs) x (MFMA cycles of one work-group + staging + a
+// fixed per-work-group cost), among the instantiated kernels that fit.
+bool plan_halo(const conv2d_gi_params &p, const std::vector<Phase> &phases, HaloPlan &out) {
+    if (phases.empty() || (int)phases.size() > gi::kMaxPhasesPerLaunch) return false;
+    // Buffer offsets inside the kernel are 32-bit byte offsets.
+    const int64_t lim = 0x7fff0000LL;
+    if ((int64_t)p.N * p.Co * p.oH * p.oW * 4 > lim) return false;
+    if ((int64_t)p.N * p.Ci * p.H * p.W * 4 > lim) return false;
+    int maxT = 0, maxJh = 0, maxJw = 0, maxHa = 0, maxWb = 0;
+    bool fold = true;
+    const int nchunks = (p.Co + gi::kHaloBC - 1) / gi::kHaloBC;
+    int64_t kall = 0;  // sum over phases of padded Co x taps
+    int64_t w_ci_stride = 0;
+    unsigned tmask = 0;
+    for (const Phase &ph : phases) {
+        const int T = ph.J_h * ph.J_w;
+        if (T > 0) tmask |= gi::halo_f32_tbit(T);
+        maxT = std::max(maxT, T);
+        maxJh = std::max(maxJh, ph.J_h);
+        maxJw = std::max(maxJw, ph.J_w);
+        maxHa = std::max(maxHa, ph.Ha);
+        maxWb = std::max(maxWb, ph.Wb);
+        if (ph.J_h > 1) fold = false;
+        kall += (int64_t)nchunks * gi::kHaloBC * T;
+        w_ci_stride += (int64_t)nchunks * T * 512;
+    }
+    const int ci_tiles = (p.Ci + gi::kHaloCT - 1) / gi::kHaloCT;
+    if (w_ci_stride * ci_tiles * 4 > lim || maxT == 0) return false;
+    static const int kNB[] = {4, 8, 13};
+    const int f_nb = g_tile_nb.load(), f_tr = g_tile_tr.load(), f_tc = g_tile_tc.load();
+    const bool forced = f_nb > 0;
+    bool found = false;
+    for (int nb : kNB) {
+        if (forced && nb != f_nb) continue;
+        const int maxpx = nb * 16;
+        for (int cdiv = 1; cdiv <= (forced ? 1 : 8); ++cdiv) {
+            const int TC = forced ? f_tc : (maxWb + cdiv - 1) / cdiv;
+            if (!forced && cdiv > 1 && TC == (maxWb + cdiv - 2) / (cdiv - 1)) continue;
+            if (TC > maxpx) continue;
+            const int rows_total = fold ? p.N * maxHa : maxHa;
+            for (int TR = forced ? f_tr : std::min(maxpx / TC, rows_total); TR >= 1; --TR) {
+                if (forced && (TR != f_tr || TR * TC > maxpx)) break;
+                if (!forced && nb > 4 && TR * TC <= (nb == 8 ? 4 : 8) * 16) break;
+                const int HR = TR + maxJh - 1, HC = TC + maxJw - 1;
+                // Halo positions are staged in groups of 32, the groups dealt
+                // round-robin to the 4 waves; the pitch sits 16 float2 off a
+                // multiple of 32 so the co-pair rows of a fragment read fall
+                // on disjoint banks.
+                const int groups = (HR * HC + 31) / 32;
+                const int bl = (groups + 3) / 4;
+                const int cfg = gi::halo_f32_config(nb, tmask, bl);
+                if (cfg < 0) continue;
+                const int HPc = round_to_residue(groups * 32, 32, 16);
+                const size_t lds = gi::halo_f32_lds_bytes(maxT, HPc);
+                if (lds > kLdsBytes) continue;
+                const int64_t row_tiles = (rows_total + TR - 1) / TR;
+                const int64_t col_tiles = (maxWb + TC - 1) / TC;
+                const int64_t tiles = row_tiles * col_tiles * (fold ? 1 : p.N);
+                if (tiles > INT32_MAX) continue;
+                const int64_t wgs = tiles * ci_tiles;
+                const double rounds = (double)((wgs + kCUs - 1) / kCUs);
+                // 16x16x4 MFMA: 32 cycles per 16 pixels x 4 k; plus halo staging.
+                const double per_wg = 8.0 * nb * kall +
+                                      (double)nchunks * phases.size() * HR * HC * 2.0 + 4000.0;
+                // Among equal critical paths, fewer work-groups do less total work.
+                const double cost = rounds * per_wg + 0.05 * (double)wgs * per_wg / kCUs;
+                if (!found || cost < out.cost) {
+                    found = true;
+                    out = HaloPlan{};
+                    out.cost = cost;
+                    out.nb = nb;
+                    out.cfg = cfg;
+                    out.bl = bl;
+                    out.tiles = (int)tiles;
+                    out.ci_tiles = ci_tiles;
+                    out.lds = lds;
+                    gi::HaloArgs &a = out.args;
+                    a.TR = TR;
+                    a.TC = TC;
+                    a.row_tiles = (int)row_tiles;
+                    a.col_tiles = (int)col_tiles;
+                    a.HPc = HPc;
+                }
+            }
+        }
+    }
+    if (!found) return false;
+    gi::HaloArgs &a = out.args;
+    a.g_bytes = (uint32_t)((int64_t)p.N * p.Co * p.oH * p.oW * 4);
+    a.d_bytes = (uint32_t)((int64_t)p.N * p.Ci * p.H * p.W * 4);
+    a.w_bytes = (uint32_t)(w_ci_stride * ci_tiles * 4);
+    a.N = p.N;
+    a.Ci = p.Ci;
+    a.H = p.H;
+    a.W = p.W;
+    a.Co = p.Co;
+    a.oH = p.oH;
+    a.oW = p.oW;
+    a.stride = p.stride;
+    a.fold = fold ? 1 : 0;
+    a.nchunks = nchunks;
+    a.maxT = maxT;
+    a.w_ci_stride = (int)w_ci_stride;
+    a.nphases = (int)phases.size();
+    int64_t woff = 0;
+    for (size_t i = 0; i < phases.size(); ++i) {
+        const Phase &ph = phases[i];
+        gi::HaloPhase &h = a.ph[i];
+        h.rho_h = ph.rho_h;
+        h.rho_w = ph.rho_w;
+        h.q_h = ph.q_h;
+        h.q_w = ph.q_w;
+        h.r_h = ph.r_h;
+        h.r_w = ph.r_w;
+        h.J_h = ph.J_h;
+        h.J_w = ph.J_w;
+        h.Ha = ph.Ha;
+        h.Wb = ph.Wb;
+        h.woff = (int)woff;
+        woff += (int64_t)nchunks * ph.J_h * ph.J_w * 512;
+    }
+    out.ws_floats = w_ci_stride * ci_tiles;
+    return true;
+}
+
+// Generic plan: phase-split gathered GEMM, launches of at most
+// kMaxPhasesPerLaunch phases.
+void plan_generic(const conv2d_gi_params &p, const std::vector<Phase> &phases, Plan &plan) {
+    plan.variant = CONV2D_GI_VARIANT_GENERIC;
+    plan.ws_bytes = (size_t)p.Co * p.Ci * p.kH * p.kW * (plan.bf16 ? 2 : 4);
     GemmArgs base{};
     base.N = p.N;
     base.Ci = p.Ci;
@@ -123,6 +272,21 @@ Plan make_plan(const conv2d_gi_params &p, bool bf16) {
         L.tiles_x = tiles;
         plan.launches.push_back(L);
     }
+}
+
+Plan make_plan(const conv2d_gi_params &p, bool bf16) {
+    Plan plan;
+    plan.bf16 = bf16;
+    std::vector<Phase> phases = make_phases(p);
+    const int forced = g_variant.load();
+    bool want_halo = !bf16 && p.Ci >= 16 &&
+                     (forced == CONV2D_GI_VARIANT_HALO || forced == CONV2D_GI_VARIANT_AUTO);
+    if (want_halo && plan_halo(p, phases, plan.halo)) {
+        plan.variant = CONV2D_GI_VARIANT_HALO;
+        plan.ws_bytes = (size_t)plan.halo.ws_floats * sizeof(float);
+        return plan;
+    }
+    plan_generic(p, phases, plan);
     return plan;
 }
 
@@ -148,7 +312,11 @@ int run(const T *grad_out, const T *weight, float *dst, const conv2d_gi_params *
         e = hipMallocAsync(&ws, plan.ws_bytes, stream);
         if (e != hipSuccess) return fail_hip(e);
         const int kHW = p->kH * p->kW;
-        if (bf16)
+        if (plan.variant == CONV2D_GI_VARIANT_HALO)
+            e = gi::launch_weight_image_f32((const float *)weight, (float *)ws, plan.halo.args,
+                                            p->kH, p->kW, plan.halo.ci_tiles,
+                                            plan.halo.ws_floats, stream);
+        else if (bf16)
             e = gi::launch_weight_tap_ci_co_bf16((const uint16_t *)weight, (uint16_t *)ws, p->Co,
                                                  p->Ci, kHW, stream);
         else
@@ -161,13 +329,23 @@ int run(const T *grad_out, const T *weight, float *dst, const conv2d_gi_params *
     }
     e = hipSuccess;
     if (g_prof_begin && g_prof_end) e = hipEventRecord(g_prof_begin, stream);
-    for (Launch &L : plan.launches) {
-        if (e != hipSuccess) break;
-        L.args.grad_out = grad_out;
-        L.args.wt = ws;
-        L.args.dst = dst;
-        e = bf16 ? gi::launch_generic_bf16(L.args, L.tiles_x, stream)
-                 : gi::launch_generic_f32(L.args, L.tiles_x, stream);
+    if (plan.variant == CONV2D_GI_VARIANT_HALO) {
+        if (e == hipSuccess) {
+            HaloPlan &h = plan.halo;
+            h.args.grad_out = (const float *)grad_out;
+            h.args.wk = (const float *)ws;
+            h.args.dst = dst;
+            e = gi::launch_halo_f32(h.args, h.cfg, h.tiles, h.ci_tiles, h.lds, stream);
+        }
+    } else {
+        for (Launch &L : plan.launches) {
+            if (e != hipSuccess) break;
+            L.args.grad_out = grad_out;
+            L.args.wt = ws;
+            L.args.dst = dst;
+            e = bf16 ? gi::launch_generic_bf16(L.args, L.tiles_x, stream)
+                     : gi::launch_generic_f32(L.args, L.tiles_x, stream);
+        }
     }
     if (e == hipSuccess && g_prof_begin && g_prof_end) e = hipEventRecord(g_prof_end, stream);
     if (ws) {
@@ -176,6 +354,43 @@ int run(const T *grad_out, const T *weight, float *dst, const conv2d_gi_params *
     }
     if (e != hipSuccess) return fail_hip(e);
     return CONV2D_GI_OK;
+}
+
+std::string describe(const Plan &plan, bool bf16) {
+    std::string s = "variant=";
+    s += plan.variant == CONV2D_GI_VARIANT_HALO ? "halo" : "generic";
+    s += " dtype=";
+    s += bf16 ? "bf16" : "f32";
+    s += " ws_bytes=" + std::to_string(plan.ws_bytes);
+    if (plan.variant == CONV2D_GI_VARIANT_HALO) {
+        const HaloPlan &h = plan.halo;
+        const gi::HaloArgs &a = h.args;
+        s += " launches=1 [nb=" + std::to_string(h.nb) + " cfg=" + std::to_string(h.cfg) +
+             " bl=" + std::to_string(h.bl) + " tile=" + std::to_string(a.TR) + "x" +
+             std::to_string(a.TC) + (a.fold ? " fold" : "") + " wgs=" + std::to_string(h.tiles) +
+             "x" + std::to_string(h.ci_tiles) + " lds=" + std::to_string(h.lds) +
+             " HPc=" + std::to_string(a.HPc);
+        for (int i = 0; i < a.nphases; ++i) {
+            const gi::HaloPhase &ph = a.ph[i];
+            s += " phase(" + std::to_string(ph.rho_h) + "," + std::to_string(ph.rho_w) +
+                 ") taps=" + std::to_string(ph.J_h) + "x" + std::to_string(ph.J_w) +
+                 " px=" + std::to_string(ph.Ha) + "x" + std::to_string(ph.Wb);
+        }
+        s += "]";
+        return s;
+    }
+    s += " launches=" + std::to_string(plan.launches.size());
+    for (const Launch &L : plan.launches) {
+        s += " [tiles=" + std::to_string(L.tiles_x) + "x" + std::to_string(L.args.ci_tiles);
+        for (int i = 0; i < L.args.nphases; ++i) {
+            const Phase &ph = L.args.ph[i];
+            s += " phase(" + std::to_string(ph.rho_h) + "," + std::to_string(ph.rho_w) +
+                 ") taps=" + std::to_string(ph.J_h) + "x" + std::to_string(ph.J_w) +
+                 " px=" + std::to_string(ph.Ha) + "x" + std::to_string(ph.Wb);
+        }
+        s += "]";
+    }
+    return s;
 }
 
 }  // namespace
@@ -207,7 +422,9 @@ const char *conv2d_gi_strerror(int code) {
 const char *conv2d_gi_last_hip_error(void) { return g_last_hip; }
 
 int conv2d_gi_set_variant(int variant) {
-    if (variant != CONV2D_GI_VARIANT_AUTO && variant != CONV2D_GI_VARIANT_GENERIC) return -1;
+    if (variant != CONV2D_GI_VARIANT_AUTO && variant != CONV2D_GI_VARIANT_GENERIC &&
+        variant != CONV2D_GI_VARIANT_HALO)
+        return -1;
     return g_variant.exchange(variant);
 }
 
@@ -216,21 +433,23 @@ int conv2d_gi_plan(const conv2d_gi_params *p, int dtype_bf16, char *buf, size_t 
     if (rc != CONV2D_GI_OK) return rc;
     if (!buf || len == 0) return CONV2D_GI_EINVAL;
     Plan plan = make_plan(*p, dtype_bf16 != 0);
-    std::string s = "variant=generic dtype=";
-    s += dtype_bf16 ? "bf16" : "f32";
-    s += " ws_bytes=" + std::to_string(plan.ws_bytes);
-    s += " launches=" + std::to_string(plan.launches.size());
-    for (const Launch &L : plan.launches) {
-        s += " [tiles=" + std::to_string(L.tiles_x) + "x" + std::to_string(L.args.ci_tiles);
-        for (int i = 0; i < L.args.nphases; ++i) {
-            const Phase &ph = L.args.ph[i];
-            s += " phase(" + std::to_string(ph.rho_h) + "," + std::to_string(ph.rho_w) +
-                 ") taps=" + std::to_string(ph.J_h) + "x" + std::to_string(ph.J_w) +
-                 " px=" + std::to_string(ph.Ha) + "x" + std::to_string(ph.Wb);
-        }
-        s += "]";
+    std::snprintf(buf, len, "%s", describe(plan, dtype_bf16 != 0).c_str());
+    return CONV2D_GI_OK;
+}
+
+int conv2d_gi_set_halo_tile(int nb, int tile_rows, int tile_cols) {
+    if (nb == 0) {
+        g_tile_nb = 0;
+        g_tile_tr = 0;
+        g_tile_tc = 0;
+        return CONV2D_GI_OK;
     }
-    std::snprintf(buf, len, "%s", s.c_str());
+    if ((nb != 4 && nb != 8 && nb != 13) || tile_rows < 1 || tile_cols < 1 ||
+        tile_rows * tile_cols > nb * 16)
+        return CONV2D_GI_EINVAL;
+    g_tile_tr = tile_rows;
+    g_tile_tc = tile_cols;
+    g_tile_nb = nb;
     return CONV2D_GI_OK;
 }
 

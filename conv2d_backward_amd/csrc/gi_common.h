@@ -42,3 +42,47 @@ struct GemmArgs {
 };
 
 }  // namespace gi
+
+namespace gi {
+
+// One residue class of the stride for the halo kernel.
+struct HaloPhase {
+    int32_t rho_h, rho_w;   // input-pixel residues mod stride
+    int32_t q_h, q_w;       // (rho + pad) div stride
+    int32_t r_h, r_w;       // first tap of the phase: (rho + pad) mod stride
+    int32_t J_h, J_w;       // taps of the phase per dimension
+    int32_t Ha, Wb;         // pixels of the phase per image: rows, columns
+    int32_t woff;           // first float of the phase's weight blocks in a ci tile
+    int32_t pad_;
+};
+
+// Arguments of one launch of the fp32 halo kernel.  A work-group owns a tile
+// of TR x TC pixels of the phase grid (the same tile in every phase) and 64
+// input channels, and walks the phases one after another.
+//
+// Weight image (written by the prologue, zero-padded in ci and co):
+//   wk[ci_tile][phase][chunk of 8 co][tap][co pair cp][ci of 64][2]
+// so one chunk of one phase is a contiguous block of taps * 512 floats; a
+// ci tile spans w_ci_stride floats.
+struct HaloArgs {
+    const float *grad_out;  // [N, Co, oH, oW]
+    const float *wk;        // weight image (above)
+    float *dst;             // [N, Ci, H, W]
+    uint32_t g_bytes;       // size of grad_out in bytes (< 2^31)
+    uint32_t w_bytes;       // size of the weight image in bytes (< 2^31)
+    uint32_t d_bytes;       // size of dst in bytes (< 2^31)
+    int32_t N, Ci, H, W, Co, oH, oW, stride;
+    int32_t nphases;
+    int32_t TR, TC;         // tile rows / columns in phase-grid pixels
+    int32_t row_tiles, col_tiles;
+    int32_t fold;           // 1: tile rows run across images (every phase has J_h <= 1)
+    int32_t nchunks;        // ceil(Co / 8)
+    int32_t HPc;            // LDS pitch of one co pair's halo, in float2
+    int32_t pad1_;
+    int32_t maxT;           // most taps of any phase
+    int32_t w_ci_stride;    // floats of the weight image per ci tile
+    int32_t pad_;
+    HaloPhase ph[kMaxPhasesPerLaunch];
+};
+
+}  // namespace gi

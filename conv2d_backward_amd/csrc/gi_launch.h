@@ -24,4 +24,23 @@ constexpr int kGenericBN = 128;
 hipError_t launch_generic_f32(const GemmArgs &a, int tiles_x, hipStream_t s);
 hipError_t launch_generic_bf16(const GemmArgs &a, int tiles_x, hipStream_t s);
 
+// Halo-tile fp32 kernel (kernels_halo_f32.hip).  Instantiations are indexed
+// by (NB pixel blocks of 16 per work-group, HG halo groups of 32 positions
+// per wave, the set of per-phase tap counts served as a bit mask of
+// halo_f32_tbit(T));
+// halo_f32_config returns the first instantiation that covers the request, or
+// -1 when none does.
+constexpr int kHaloBC = 8;     // output channels per LDS stage (chunk)
+constexpr int kHaloCT = 64;    // input channels per work-group
+unsigned halo_f32_tbit(int T);
+int halo_f32_config(int nb, unsigned tmask, int hg);
+hipError_t launch_halo_f32(const HaloArgs &a, int cfg, int tiles, int ci_tiles, size_t lds,
+                           hipStream_t s);
+// LDS bytes of the halo kernel: most taps of a phase, halo pitch (float2).
+size_t halo_f32_lds_bytes(int maxT, int HPc);
+
+// Weight image of the halo kernel (layout in gi_common.h); `total` floats.
+hipError_t launch_weight_image_f32(const float *w, float *wk, const HaloArgs &a, int kH, int kW,
+                                   int ci_tiles, int64_t total, hipStream_t s);
+
 }  // namespace gi

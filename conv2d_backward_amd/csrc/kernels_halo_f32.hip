@@ -1,0 +1,407 @@
+// kernels_halo_f32.hip -- fp32 halo-tile implicit-GEMM kernel for gfx950.
+//
+// The contraction is the implicit GEMM of meganeura conv2d_grad_input_gemm.wgsl
+// (header comment: C[Ci, pixels] = A[Ci, K] x B[K, pixels], A the weight read
+// as [Ci, Co*kH*kW], B the im2col of grad_out), restricted to the taps of one
+// residue class of the stride at a time (see gi_common.h).  B is never
+// gathered per tap: for each chunk of 8 output channels a work-group stages in
+// LDS
+//   * the grad_out "halo" of its pixel tile, i.e. the (TR + J_h - 1) x
+//     (TC + J_w - 1) output rows/columns its TR x TC pixels read, zero outside
+//     the image (this zero border is the transposed padding kH-1-pad of the
+//     shader's header comment), and
+//   * the weights of the chunk for its 64 input channels and every tap of the
+//     phase, copied from a weight image laid out by the prologue below,
+// and every tap (j, jw) reads its B fragment as the halo shifted by
+// (J_h-1-j, J_w-1-jw) positions: one LDS read per fragment, the shift a
+// uniform offset.
+//
+// Matrix cores: V_MFMA_F32_16X16X4_F32, rows = 16 input channels, columns = 16
+// pixels, k = 4 output channels of one tap.  Lane l = 16*g + i supplies
+// A[i][k=g], B[k=g][i] and receives D[4g + r][i], r = 0..3.  The K axis is
+// permuted so that MFMA step s (0, 1) of a tap uses output channel 2g + s for
+// lane group g: a lane then reads both of its k values with one 8-byte LDS
+// read.  Each of the 4 waves owns 16 input channels and all NB pixel blocks of
+// the tile; the next tap's fragments are read from LDS while the current
+// tap's 2*NB MFMAs run.  Chunks are double-buffered in LDS and staged with
+// direct global -> LDS loads, the next chunk's in flight during the current
+// chunk's MFMAs.
+//
+// Out-of-range elements (halo outside the image, output channels past Co,
+// pixels past the tile's edge, input channels past Ci) are handled with raw
+// buffer loads and stores whose offset is pushed past the end of the buffer:
+// the hardware returns 0 for such loads and drops such stores, so the loops
+// carry no branches.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gi_common.h"
+#include "gi_launch.h"
+
+namespace gi {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+
+namespace {
+
+static_assert(kHaloCT == 64, "four waves of 16 input channels");
+static_assert(kHaloBC == 8, "four co pairs per chunk");
+
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9)
+constexpr int kOOB = 0x7ffffff0;         // byte offset past the end of every buffer
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (long)bytes, kRsrcWord3);
+}
+
+// Phase-grid pixel px (row-major in the TR x TC tile at origin (a0, b0)):
+// image and coordinates, false outside the phase grid.
+__device__ __forceinline__ bool tile_pixel(const HaloArgs &A, const HaloPhase &P, int px,
+                                           int a0, int b0, int n_img, int &img, int &a,
+                                           int &b) {
+    const int r = px / A.TC, c = px - r * A.TC;
+    img = 0;
+    a = 0;
+    b = b0 + c;
+    if (px >= A.TR * A.TC || b >= P.Wb) return false;
+    if (A.fold) {
+        const int R = a0 + r;
+        if (R >= A.N * P.Ha) return false;
+        img = R / P.Ha;
+        a = R - img * P.Ha;
+        return true;
+    }
+    if (a0 + r >= P.Ha) return false;
+    img = n_img;
+    a = a0 + r;
+    return true;
+}
+
+// Bit of tap count T in a kernel's TMASK.
+constexpr unsigned tbit(int T) { return 1u << T; }
+
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+
+// Direct global -> LDS loads (no registers): lane i of the wave writes its
+// `bytes` at LDS address dst + i * bytes; an out-of-range offset writes 0.
+// dst must be the same for the whole wave.
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, void *dst, int voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)dst, 4, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void *dst, int voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)dst, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// All chunks of one phase with T = J_h * J_w taps (compile time) for this
+// work-group's tile; accumulates into acc.  Every thread of the work-group
+// calls it (it contains barriers).  HG = halo position groups of 32 staged
+// per wave.
+//
+// LDS stage (float2 units): weights [maxT][4 co pairs][64 ci], then halo
+// [4 co pairs][HPc positions]; both written by direct loads:
+//   * weights: the chunk's block of the weight image is T * 2 KB, copied in
+//     1 KB pieces (16 bytes per lane);
+//   * halo: for co pair cp and a group of 32 positions, even lanes load
+//     output channel 2cp and odd lanes 2cp+1 of position base + lane/2, which
+//     lands exactly on the float2 layout.
+template <int T, int NB, int HG>
+__device__ __forceinline__ void run_phase(const HaloArgs &A, const HaloPhase &P, v2f *smem2,
+                                          const int (&pbase)[NB], v4f (&acc)[NB], int a0,
+                                          int b0, int n_img, int ci_tile,
+                                          __amdgpu_buffer_rsrc_t grs,
+                                          __amdgpu_buffer_rsrc_t wrs) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const int as_f2 = A.maxT * 4 * 64;
+    const int stage_f2 = as_f2 + 4 * A.HPc;
+    const int HC = A.TC + P.J_w - 1;
+    const int HR = A.TR + P.J_h - 1;
+    const int hpos = HR * HC;
+    const int groups = (hpos + 31) / 32;
+    const int oHW = A.oH * A.oW;
+
+    // Halo shift of every tap (j, jw): (J_h-1-j) rows and (J_w-1-jw) columns.
+    int shift[T];
+    {
+        int j = 0, jw = 0;
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            shift[t] = (P.J_h - 1 - j) * HC + (P.J_w - 1 - jw);
+            if (++jw == P.J_w) {
+                jw = 0;
+                ++j;
+            }
+        }
+    }
+
+    // Halo position of this lane in each of its wave's groups: grad_out byte
+    // offset of output channel 0 (kOOB outside the image or the halo).
+    int hoff[HG];
+#pragma unroll
+    for (int k = 0; k < HG; ++k) {
+        const int pos = (wave + 4 * k) * 32 + (lane >> 1);
+        const int hr = pos / HC, hc = pos - (pos / HC) * HC;
+        const int ow = b0 + P.q_w - (P.J_w - 1) + hc;
+        bool v = pos < hpos && ow >= 0 && ow < A.oW;
+        int img, oh;
+        if (A.fold) {
+            const int R = a0 + hr;
+            img = R / P.Ha;
+            oh = (R - img * P.Ha) + P.q_h;
+            v = v && R < A.N * P.Ha;
+        } else {
+            img = n_img;
+            oh = a0 + P.q_h - (P.J_h - 1) + hr;
+        }
+        v = v && oh >= 0 && oh < A.oH;
+        hoff[k] = v ? ((img * A.Co) * oHW + oh * A.oW + ow) * 4 : kOOB;
+    }
+    const int wbyte0 = (ci_tile * A.w_ci_stride + P.woff) * 4;
+    const int co_lane = lane & 1;
+
+    auto issue = [&](int chunk, int buf) {
+        v2f *st = smem2 + buf * stage_f2;
+        const int wb = wbyte0 + chunk * (T * 2048) + lane * 16;
+        for (int m = wave; m < 2 * T; m += 4) dma16(wrs, st + m * 128, wb + m * 1024);
+        v2f *hs = st + as_f2;
+#pragma unroll
+        for (int k = 0; k < HG; ++k) {
+            const int g = wave + 4 * k;
+            if (g < groups) {
+#pragma unroll
+                for (int cp = 0; cp < 4; ++cp) {
+                    const int co = chunk * kHaloBC + 2 * cp + co_lane;
+                    const int off =
+                        (hoff[k] != kOOB && co < A.Co) ? hoff[k] + co * oHW * 4 : kOOB;
+                    dma4(grs, hs + cp * A.HPc + g * 32, off);
+                }
+            }
+        }
+    };
+
+    issue(0, 0);
+    wait_dma();
+    __syncthreads();
+    for (int chunk = 0; chunk < A.nchunks; ++chunk) {
+        const int cur = chunk & 1;
+        if (chunk + 1 < A.nchunks) issue(chunk + 1, cur ^ 1);
+        const v2f *as = smem2 + cur * stage_f2 + g4 * 64 + wave * 16 + l16;
+        const v2f *hs = smem2 + cur * stage_f2 + as_f2 + g4 * A.HPc;
+        // Two fragment slots: tap t+1 is read from LDS while tap t's MFMAs
+        // run; the schedule interleaves one read with every two MFMAs.
+        v2f fa[2], fb[2][NB];
+        auto fetch = [&](int t, int slot) {
+            fa[slot] = as[t * 4 * 64];
+#pragma unroll
+            for (int blk = 0; blk < NB; ++blk) fb[slot][blk] = hs[pbase[blk] + shift[t]];
+        };
+        fetch(0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            const int slot = t & 1;
+            if (t + 1 < T) fetch(t + 1, slot ^ 1);
+#pragma unroll
+            for (int blk = 0; blk < NB; ++blk)
+                acc[blk] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[slot].x, fb[slot][blk].x,
+                                                                acc[blk], 0, 0, 0);
+#pragma unroll
+            for (int blk = 0; blk < NB; ++blk)
+                acc[blk] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[slot].y, fb[slot][blk].y,
+                                                                acc[blk], 0, 0, 0);
+            // Keep taps in order: nothing moves across a tap boundary.
+            __builtin_amdgcn_sched_barrier(0);
+        }
+
+        wait_dma();
+        __syncthreads();
+    }
+}
+
+template <int NB, int HG, unsigned TMASK>
+__global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void gi_halo_f32(
+    const HaloArgs A) {
+    extern __shared__ __attribute__((aligned(16))) v2f smem2[];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, g4 = lane >> 4;
+
+    int t = blockIdx.x;
+    const int ct = t % A.col_tiles;
+    t /= A.col_tiles;
+    int rt, n_img = 0;
+    if (A.fold) {
+        rt = t;
+    } else {
+        rt = t % A.row_tiles;
+        n_img = t / A.row_tiles;
+    }
+    const int ci_tile = blockIdx.y;
+    const int ci0 = ci_tile * kHaloCT;
+    const int a0 = rt * A.TR, b0 = ct * A.TC;
+    const int plane = A.H * A.W;
+    const __amdgpu_buffer_rsrc_t grs = make_rsrc(A.grad_out, A.g_bytes);
+    const __amdgpu_buffer_rsrc_t wrs = make_rsrc(A.wk, A.w_bytes);
+    const __amdgpu_buffer_rsrc_t drs = make_rsrc(A.dst, A.d_bytes);
+
+    for (int p = 0; p < A.nphases; ++p) {
+        const HaloPhase P = A.ph[p];
+        const int T = P.J_h * P.J_w;
+        const int HC = A.TC + P.J_w - 1;
+
+        // Halo position of this lane's pixel in each block (0 for a pixel
+        // outside the phase grid: it reads a valid position, its column is
+        // never stored).
+        int pbase[NB];
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) {
+            int img, a, b;
+            const int px = blk * 16 + l16;
+            pbase[blk] = tile_pixel(A, P, px, a0, b0, n_img, img, a, b)
+                             ? (px / A.TC) * HC + (px - (px / A.TC) * A.TC)
+                             : 0;
+        }
+
+        v4f acc[NB];
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) acc[blk] = v4f{0.f, 0.f, 0.f, 0.f};
+
+#define GI_HALO_CASE(TT)                                                                     \
+    case TT:                                                                                 \
+        if constexpr ((TMASK & tbit(TT)) != 0)                                               \
+            run_phase<TT, NB, HG>(A, P, smem2, pbase, acc, a0, b0, n_img, ci_tile, grs, wrs); \
+        break;
+        switch (T) {
+            GI_HALO_CASE(1)
+            GI_HALO_CASE(2)
+            GI_HALO_CASE(3)
+            GI_HALO_CASE(4)
+            GI_HALO_CASE(6)
+            GI_HALO_CASE(7)
+            GI_HALO_CASE(9)
+            default: break;  // T = 0: no taps, the phase's pixels are zero
+        }
+#undef GI_HALO_CASE
+
+        // Epilogue: D[4*g4 + r][l16] of each block, NCHW.
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) {
+            int img, a, b;
+            const bool pv = tile_pixel(A, P, blk * 16 + l16, a0, b0, n_img, img, a, b);
+            const int pix = (P.rho_h + A.stride * a) * A.W + P.rho_w + A.stride * b;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int ci = ci0 + wave * 16 + 4 * g4 + r;
+                const int off = (pv && ci < A.Ci) ? ((img * A.Ci + ci) * plane + pix) * 4 : kOOB;
+                // Copy the element to a scalar first: a bit-cast taken directly
+                // of a vector element reads element 0 with this compiler.
+                const float v = acc[blk][r];
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), drs, off, 0, 0);
+            }
+        }
+    }
+}
+
+constexpr unsigned kT9 = tbit(9);
+constexpr unsigned kT7 = tbit(7);
+constexpr unsigned kTs2 = tbit(1) | tbit(2) | tbit(4);
+constexpr unsigned kTall = tbit(1) | tbit(2) | tbit(3) | tbit(4) | tbit(6) | tbit(7) | tbit(9);
+
+template <int NB, int HG, unsigned TMASK>
+hipError_t launch_one(const HaloArgs &a, int tiles, int ci_tiles, size_t lds, hipStream_t s) {
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute((const void *)gi_halo_f32<NB, HG, TMASK>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((gi_halo_f32<NB, HG, TMASK>), dim3(tiles, ci_tiles), dim3(256), lds, s,
+                       a);
+    return hipGetLastError();
+}
+
+// Instantiations: pixel blocks, halo groups of 32 positions per wave, tap
+// counts served.
+struct HaloCfg {
+    int nb, hg;
+    unsigned tmask;
+};
+constexpr HaloCfg kCfg[] = {
+    {13, 2, kT9},   {13, 2, kTs2}, {8, 2, kT7},  {13, 4, kTall},
+    {8, 4, kTall},  {4, 4, kTall},
+};
+
+}  // namespace
+
+unsigned halo_f32_tbit(int T) { return T >= 0 && T < 32 ? tbit(T) : 0u; }
+
+int halo_f32_config(int nb, unsigned tmask, int hg) {
+    for (int i = 0; i < (int)(sizeof(kCfg) / sizeof(kCfg[0])); ++i)
+        if (kCfg[i].nb == nb && kCfg[i].hg >= hg && (kCfg[i].tmask & tmask) == tmask) return i;
+    return -1;
+}
+
+size_t halo_f32_lds_bytes(int maxT, int HPc) {
+    return (size_t)2 * (maxT * 4 * 64 + 4 * HPc) * sizeof(v2f);
+}
+
+hipError_t launch_halo_f32(const HaloArgs &a, int cfg, int tiles, int ci_tiles, size_t lds,
+                           hipStream_t s) {
+    switch (cfg) {
+        case 0: return launch_one<13, 2, kT9>(a, tiles, ci_tiles, lds, s);
+        case 1: return launch_one<13, 2, kTs2>(a, tiles, ci_tiles, lds, s);
+        case 2: return launch_one<8, 2, kT7>(a, tiles, ci_tiles, lds, s);
+        case 3: return launch_one<13, 4, kTall>(a, tiles, ci_tiles, lds, s);
+        case 4: return launch_one<8, 4, kTall>(a, tiles, ci_tiles, lds, s);
+        case 5: return launch_one<4, 4, kTall>(a, tiles, ci_tiles, lds, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+// Weight image: one thread per float of wk, in order
+// [ci_tile][phase][chunk][tap][cp][ci][2], zero where ci >= Ci or co >= Co.
+__global__ __launch_bounds__(256) void weight_image_f32(const float *__restrict__ w,
+                                                        float *__restrict__ wk, const HaloArgs A,
+                                                        int kH, int kW, int64_t total) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * 256) {
+        const int ct = (int)(i / A.w_ci_stride);
+        const int e = (int)(i - (int64_t)ct * A.w_ci_stride);
+        int p = 0;
+        for (int k = 1; k < A.nphases; ++k)
+            if (e >= A.ph[k].woff) p = k;
+        const HaloPhase &P = A.ph[p];
+        const int T = P.J_h * P.J_w;
+        int r = e - P.woff;
+        const int chunk = r / (T * 512);
+        r -= chunk * T * 512;
+        const int tap = r / 512;
+        r -= tap * 512;
+        const int cp = r / 128;
+        r -= cp * 128;
+        const int ci = ct * kHaloCT + r / 2;
+        const int co = chunk * kHaloBC + 2 * cp + (r & 1);
+        float v = 0.f;
+        if (ci < A.Ci && co < A.Co) {
+            const int j = tap / P.J_w, jw = tap - (tap / P.J_w) * P.J_w;
+            const int kh = P.r_h + A.stride * j, kw = P.r_w + A.stride * jw;
+            v = w[(((int64_t)co * A.Ci + ci) * kH + kh) * kW + kw];
+        }
+        wk[i] = v;
+    }
+}
+
+hipError_t launch_weight_image_f32(const float *w, float *wk, const HaloArgs &a, int kH, int kW,
+                                   int ci_tiles, int64_t total, hipStream_t s) {
+    (void)ci_tiles;
+    int64_t b = (total + 255) / 256;
+    const int blocks = (int)(b < 8192 ? (b > 0 ? b : 1) : 8192);
+    hipLaunchKernelGGL(weight_image_f32, dim3(blocks), dim3(256), 0, s, w, wk, a, kH, kW, total);
+    return hipGetLastError();
+}
+
+}  // namespace gi

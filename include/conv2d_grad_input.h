@@ -98,7 +98,10 @@ enum {
 /* Kernel variants, for conv2d_gi_set_variant and conv2d_gi_plan. */
 enum {
     CONV2D_GI_VARIANT_AUTO = 0,    /* the planner chooses                      */
-    CONV2D_GI_VARIANT_GENERIC = 1  /* any shape: phase split, gathered B tile  */
+    CONV2D_GI_VARIANT_GENERIC = 1, /* any shape: phase split, gathered B tile  */
+    CONV2D_GI_VARIANT_HALO = 2     /* fp32, Ci >= 16: grad_out halo tile in LDS,
+                                      every tap a shifted view of it; shapes it
+                                      cannot hold in LDS fall back to GENERIC  */
 };
 
 /*
@@ -133,6 +136,16 @@ CONV2D_GI_API const char *conv2d_gi_last_hip_error(void);
  * previous setting, or -1 for an unknown variant (setting unchanged).
  */
 CONV2D_GI_API int conv2d_gi_set_variant(int variant);
+
+/*
+ * Test and diagnostic hook: force the pixel tile of the HALO variant for later
+ * calls in this process: nb pixel blocks of 16 per work-group (4, 8 or 13)
+ * and a tile of tile_rows x tile_cols pixels of the stride-phase grid
+ * (at most nb*16 pixels).  A shape the forced tile does not fit (LDS, halo
+ * size) is planned with GENERIC instead.  nb = 0 restores the planner.
+ * Returns CONV2D_GI_OK, or CONV2D_GI_EINVAL for values out of range.
+ */
+CONV2D_GI_API int conv2d_gi_set_halo_tile(int nb, int tile_rows, int tile_cols);
 
 /*
  * Host-only: describe the plan the entry point would run for this shape

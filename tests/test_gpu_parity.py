@@ -129,11 +129,62 @@ def test_mid(idx, dtype):
     full_parity(MID[idx], 500 + idx, dtype, dist="normal")
 
 
-@pytest.mark.parametrize("variant", [gi.VARIANT_GENERIC])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_forced_variant(variant, dtype):
+def test_forced_generic(dtype):
     for i, s in enumerate([SWEEP[4], SWEEP[9], MID[0], MID[2]]):
-        full_parity(s, 900 + i, dtype, variant)
+        full_parity(s, 900 + i, dtype, gi.VARIANT_GENERIC)
+
+
+HALO_SHAPES = [s for s in SWEEP + MID if s.Ci >= 16] + [
+    workloads.Shape(2, 16, 9, 9, 5, 3, 3, 1, 1, 1),      # Co below one channel chunk
+    workloads.Shape(1, 20, 33, 70, 9, 3, 3, 1, 1, 1),     # wide rows: several column tiles
+    workloads.Shape(3, 24, 11, 13, 12, 5, 5, 2, 2, 2),    # stride 2, 5x5
+    workloads.Shape(2, 17, 10, 9, 6, 2, 3, 3, 0, 1),      # stride 3: phases with different taps
+    workloads.Shape(4, 32, 7, 7, 40, 1, 3, 1, 0, 1),      # 1xk: tile rows fold across images
+    workloads.Shape(1, 64, 6, 6, 8, 2, 3, 1, 0, 0),       # even kernel, no padding
+]
+
+
+@pytest.mark.parametrize("idx", range(len(HALO_SHAPES)))
+def test_forced_halo(idx):
+    s = HALO_SHAPES[idx]
+    gi.set_variant(gi.VARIANT_HALO)
+    desc = gi.plan(gi.make_params(*s.as_tuple()[:10]), False)
+    gi.set_variant(gi.VARIANT_AUTO)
+    assert "variant=halo" in desc, desc
+    full_parity(s, 1300 + idx, "f32", gi.VARIANT_HALO, dist="normal")
+
+
+# (shape, nb, tile_rows, tile_cols): tiles with ragged row and column tails,
+# tiles wider than the image, rows folded across images, strided phases.
+FORCED_TILES = [
+    (MID[0], 8, 3, 11),
+    (MID[0], 13, 6, 29),
+    (MID[0], 13, 8, 25),
+    (MID[0], 4, 1, 50),
+    (workloads.Shape(4, 32, 7, 7, 40, 1, 3, 1, 0, 1), 8, 5, 7),
+    (workloads.Shape(4, 32, 7, 7, 40, 1, 3, 1, 0, 1), 13, 9, 3),
+    (MID[2], 8, 4, 5),
+    (MID[2], 13, 12, 12),
+    (MID[5], 13, 6, 7),
+    (workloads.Shape(3, 70, 31, 33, 20, 3, 3, 2, 1, 1), 4, 3, 17),
+    (workloads.Shape(2, 64, 14, 14, 24, 3, 3, 1, 1, 1), 13, 14, 14),   # the deep-stage tile
+    (workloads.Shape(2, 70, 28, 28, 40, 3, 3, 2, 1, 1), 13, 14, 14),   # the downsample tile
+]
+
+
+@pytest.mark.parametrize("idx", range(len(FORCED_TILES)))
+def test_forced_halo_tile(idx):
+    s, nb, tr, tc = FORCED_TILES[idx]
+    gi.set_halo_tile(nb, tr, tc)
+    try:
+        gi.set_variant(gi.VARIANT_HALO)
+        desc = gi.plan(gi.make_params(*s.as_tuple()[:10]), False)
+        gi.set_variant(gi.VARIANT_AUTO)
+        assert "variant=halo" in desc and ("tile=%dx%d" % (tr, tc)) in desc, desc
+        full_parity(s, 1700 + idx, "f32", gi.VARIANT_HALO, dist="normal")
+    finally:
+        gi.set_halo_tile()
 
 
 def test_tiny_workload_full():
