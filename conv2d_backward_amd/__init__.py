@@ -17,7 +17,7 @@ import os
 
 __all__ = [
     "grad_input", "Conv2dGiParams", "Conv2dGiError", "LibraryNotBuilt", "load_library",
-    "make_params", "validate", "plan", "set_variant", "set_halo_tile", "set_profile_events", "library_path", "exported_names",
+    "make_params", "validate", "plan", "set_variant", "set_halo_tile", "release_workspaces", "set_profile_events", "library_path", "exported_names",
     "OK", "EINVAL", "EUNSUPPORTED", "EHIP", "VARIANT_AUTO", "VARIANT_GENERIC", "VARIANT_HALO",
 ]
 
@@ -81,6 +81,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.conv2d_gi_set_halo_tile.restype = ctypes.c_int
     lib.conv2d_gi_set_profile_events.argtypes = [P, P]
     lib.conv2d_gi_set_profile_events.restype = None
+    lib.conv2d_gi_release_workspaces.argtypes = []
+    lib.conv2d_gi_release_workspaces.restype = ctypes.c_int
     lib.conv2d_gi_version.argtypes = []
     lib.conv2d_gi_version.restype = ctypes.c_char_p
     if path is None:
@@ -93,7 +95,7 @@ def exported_names():
     return ["conv2d_grad_input", "conv2d_grad_input_bf16", "conv2d_gi_validate",
             "conv2d_gi_strerror", "conv2d_gi_last_hip_error", "conv2d_gi_set_variant",
             "conv2d_gi_plan", "conv2d_gi_set_halo_tile", "conv2d_gi_set_profile_events",
-            "conv2d_gi_version"]
+            "conv2d_gi_release_workspaces", "conv2d_gi_version"]
 
 
 def make_params(N, Ci, H, W, Co, kH, kW, stride, pad_h, pad_w, oH=None, oW=None):
@@ -137,6 +139,11 @@ def set_variant(variant: int) -> int:
 def set_halo_tile(nb: int = 0, tile_rows: int = 0, tile_cols: int = 0):
     """Force the HALO variant's pixel tile (test hook); set_halo_tile() restores the planner."""
     _check(load_library().conv2d_gi_set_halo_tile(int(nb), int(tile_rows), int(tile_cols)))
+
+
+def release_workspaces():
+    """Free the library's cached per-stream scratch buffers."""
+    _check(load_library().conv2d_gi_release_workspaces())
 
 
 def set_profile_events(begin, end):

@@ -9,7 +9,10 @@
 #include <atomic>
 #include <cstdio>
 #include <cstring>
+#include <map>
+#include <mutex>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "conv2d_grad_input.h"
@@ -26,6 +29,37 @@ std::atomic<int> g_variant{CONV2D_GI_VARIANT_AUTO};
 std::atomic<int> g_tile_nb{0}, g_tile_tr{0}, g_tile_tc{0};
 thread_local char g_last_hip[256] = "";
 thread_local hipEvent_t g_prof_begin = nullptr, g_prof_end = nullptr;
+
+// Scratch (the reordered weight) cached per (device, stream): allocated
+// stream-ordered on first use, grown when a call needs more, reused by later
+// calls on the same stream (stream order keeps them apart), released by
+// conv2d_gi_release_workspaces.  The lock is held while a call enqueues.
+struct Workspace {
+    void *ptr = nullptr;
+    size_t bytes = 0;
+};
+std::mutex g_ws_mu;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+hipError_t workspace_for(int dev, hipStream_t s, size_t bytes, void **out) {
+    Workspace &w = g_ws[{dev, s}];
+    if (w.bytes < bytes) {
+        if (w.ptr) {
+            hipError_t e = hipFreeAsync(w.ptr, s);
+            w.ptr = nullptr;
+            w.bytes = 0;
+            if (e != hipSuccess) return e;
+        }
+        hipError_t e = hipMallocAsync(&w.ptr, bytes, s);
+        if (e != hipSuccess) {
+            w.ptr = nullptr;
+            return e;
+        }
+        w.bytes = bytes;
+    }
+    *out = w.ptr;
+    return hipSuccess;
+}
 
 int fail_hip(hipError_t e) {
     std::snprintf(g_last_hip, sizeof(g_last_hip), "%s: %s", hipGetErrorName(e),
@@ -308,8 +342,12 @@ int run(const T *grad_out, const T *weight, float *dst, const conv2d_gi_params *
     Plan plan = make_plan(*p, bf16);
     void *ws = nullptr;
     hipError_t e;
+    int dev = 0;
+    e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail_hip(e);
+    std::lock_guard<std::mutex> lock(g_ws_mu);
     if (plan.ws_bytes > 0) {
-        e = hipMallocAsync(&ws, plan.ws_bytes, stream);
+        e = workspace_for(dev, stream, plan.ws_bytes, &ws);
         if (e != hipSuccess) return fail_hip(e);
         const int kHW = p->kH * p->kW;
         if (plan.variant == CONV2D_GI_VARIANT_HALO)
@@ -322,10 +360,7 @@ int run(const T *grad_out, const T *weight, float *dst, const conv2d_gi_params *
         else
             e = gi::launch_weight_tap_co_ci_f32((const float *)weight, (float *)ws, p->Co, p->Ci,
                                                 kHW, stream);
-        if (e != hipSuccess) {
-            (void)hipFreeAsync(ws, stream);
-            return fail_hip(e);
-        }
+        if (e != hipSuccess) return fail_hip(e);
     }
     e = hipSuccess;
     if (g_prof_begin && g_prof_end) e = hipEventRecord(g_prof_begin, stream);
@@ -348,10 +383,6 @@ int run(const T *grad_out, const T *weight, float *dst, const conv2d_gi_params *
         }
     }
     if (e == hipSuccess && g_prof_begin && g_prof_end) e = hipEventRecord(g_prof_end, stream);
-    if (ws) {
-        hipError_t e2 = hipFreeAsync(ws, stream);
-        if (e == hipSuccess) e = e2;
-    }
     if (e != hipSuccess) return fail_hip(e);
     return CONV2D_GI_OK;
 }
@@ -451,6 +482,23 @@ int conv2d_gi_set_halo_tile(int nb, int tile_rows, int tile_cols) {
     g_tile_tc = tile_cols;
     g_tile_nb = nb;
     return CONV2D_GI_OK;
+}
+
+int conv2d_gi_release_workspaces(void) {
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    int prev = 0;
+    if (hipGetDevice(&prev) != hipSuccess) return fail_hip(hipErrorNoDevice);
+    hipError_t first = hipSuccess;
+    for (auto &kv : g_ws) {
+        if (!kv.second.ptr) continue;
+        hipError_t e = hipSetDevice(kv.first.first);
+        if (e == hipSuccess) e = hipFreeAsync(kv.second.ptr, kv.first.second);
+        if (e == hipSuccess) e = hipStreamSynchronize(kv.first.second);
+        if (first == hipSuccess) first = e;
+    }
+    g_ws.clear();
+    (void)hipSetDevice(prev);
+    return first == hipSuccess ? CONV2D_GI_OK : fail_hip(first);
 }
 
 void conv2d_gi_set_profile_events(hipEvent_t begin, hipEvent_t end) {

@@ -32,10 +32,14 @@
  *   weight   [Co, Ci, kH, kW]  read only
  *   dst      [N, Ci, H, W]     fp32, written (every element, never accumulated)
  * The caller allocates and owns all three; the library never frees them.  dst
- * must not overlap either input.  The library allocates a small scratch
- * buffer (the weight in kernel order, Co*Ci*kH*kW elements) stream-ordered on
- * `stream` (hipMallocAsync / hipFreeAsync), so calls on different streams
- * share no state.  Both convolution stride dimensions take `stride`; padding
+ * must not overlap either input.  The library keeps one scratch buffer (the
+ * weight in kernel order, about Co*Ci*kH*kW elements) per (device, stream):
+ * allocated stream-ordered on `stream` (hipMallocAsync) at the first call
+ * that needs it, grown when a later call needs more, and reused by later
+ * calls on that stream, which stream order keeps apart.  Calls on different
+ * streams share no state.  conv2d_gi_release_workspaces frees the buffers
+ * (call it before destroying a stream the library ran on, since a new stream
+ * could receive the same handle).  Both convolution stride dimensions take `stride`; padding
  * is symmetric per dimension (pad_h top and bottom, pad_w left and right).
  *
  * Asynchrony and errors
@@ -163,6 +167,12 @@ CONV2D_GI_API int conv2d_gi_plan(const conv2d_gi_params *p, int dtype_bf16, char
  * NULL, NULL switches it off.  The events (hipEvent_t) stay the caller's.
  */
 CONV2D_GI_API void conv2d_gi_set_profile_events(hipEvent_t begin, hipEvent_t end);
+
+/*
+ * Free every cached scratch buffer (each after the work queued on its stream
+ * has finished).  Returns a status code.  Later calls allocate again.
+ */
+CONV2D_GI_API int conv2d_gi_release_workspaces(void);
 
 /* Library version as "major.minor.patch". */
 CONV2D_GI_API const char *conv2d_gi_version(void);
