@@ -25,6 +25,7 @@ SOURCES = [
     "api.cpp",
     "kernels_generic.hip",
     "kernels_halo_f32.hip",
+    "kernels_halo_bf16.hip",
 ]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", "-Werror",

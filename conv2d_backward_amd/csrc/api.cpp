@@ -128,12 +128,22 @@ struct HaloPlan {
     int64_t ws_floats = 0;  // weight image
 };
 
+// A bf16 halo-kernel plan (stride 1): two prologues and one launch.
+struct HaloBf16Plan {
+    gi::HaloBf16Args args{};
+    int cfg = -1, tiles = 0, ci_tiles = 0;
+    size_t lds = 0;
+    size_t gp_bytes = 0, wk_bytes = 0;  // workspace: padded grad_out, then weight fragments
+    double cost = 0.0;
+};
+
 struct Plan {
     int variant = CONV2D_GI_VARIANT_GENERIC;
     bool bf16 = false;
     size_t ws_bytes = 0;  // reordered weight
     std::vector<Launch> launches;  // generic
-    HaloPlan halo;                 // halo
+    HaloPlan halo;                 // halo, fp32
+    HaloBf16Plan hb;               // halo, bf16
 };
 
 constexpr int kCUs = 256;               // MI355X compute units
@@ -273,6 +283,82 @@ bool plan_halo(const conv2d_gi_params &p, const std::vector<Phase> &phases, Halo
     return true;
 }
 
+// bf16 halo plan (stride 1, tap counts the kernel is built for): choose the
+// TR x TC pixel tile (at most 2*NBW*16 pixels, halo at most 256 positions)
+// that minimises ceil(work-groups / CUs) x per-work-group MFMA cycles.
+bool plan_halo_bf16(const conv2d_gi_params &p, HaloBf16Plan &out) {
+    if (p.stride != 1 || p.Ci < 16) return false;
+    const int T = p.kH * p.kW;
+    const int nchunks = (p.Co + 31) / 32;
+    const int Cop = nchunks * 32;
+    const int YP = p.H + p.kH - 1, XP = p.W + p.kW - 1;
+    const int ci_tiles = (p.Ci + 63) / 64;
+    const int64_t lim = 0x7fff0000LL;
+    const int64_t gp_bytes = (int64_t)p.N * YP * XP * Cop * 2;
+    const int64_t wk_bytes = (int64_t)ci_tiles * 64 * Cop * T * 2;
+    if (gp_bytes > lim || wk_bytes > lim || (int64_t)p.N * p.Ci * p.H * p.W * 4 > lim)
+        return false;
+    static const int kNBW[] = {4, 7};
+    bool found = false;
+    for (int nbw : kNBW) {
+        const int cfg = gi::halo_bf16_config(nbw, T);
+        if (cfg < 0) continue;
+        const int maxpx = 2 * nbw * 16;
+        for (int cdiv = 1; cdiv <= 8; ++cdiv) {
+            const int TC = (p.W + cdiv - 1) / cdiv;
+            if (cdiv > 1 && TC == (p.W + cdiv - 2) / (cdiv - 1)) continue;
+            if (TC > maxpx) continue;
+            for (int TR = std::min(maxpx / TC, p.H); TR >= 1; --TR) {
+                const int HR = TR + p.kH - 1, HC = TC + p.kW - 1;
+                if (HR * HC > 256) continue;
+                const int64_t tiles = (int64_t)((p.H + TR - 1) / TR) * ((p.W + TC - 1) / TC) * p.N;
+                if (tiles > INT32_MAX) continue;
+                const int64_t wgs = tiles * ci_tiles;
+                const double rounds = (double)((wgs + kCUs - 1) / kCUs);
+                // 16x16x32 MFMA, 16 cycles: 2 ci blocks x nbw pixel blocks per wave per k step.
+                const double per_wg = 16.0 * 2 * nbw * (double)nchunks * T + 3000.0;
+                const double cost = rounds * per_wg + 0.05 * (double)wgs * per_wg / kCUs;
+                if (!found || cost < out.cost) {
+                    found = true;
+                    out = HaloBf16Plan{};
+                    out.cost = cost;
+                    out.cfg = cfg;
+                    out.tiles = (int)tiles;
+                    out.ci_tiles = ci_tiles;
+                    gi::HaloBf16Args &a = out.args;
+                    a.TR = TR;
+                    a.TC = TC;
+                    a.HR = HR;
+                    a.HC = HC;
+                    a.row_tiles = (p.H + TR - 1) / TR;
+                    a.col_tiles = (p.W + TC - 1) / TC;
+                    a.nq = (HR * HC + 15) / 16;
+                }
+            }
+        }
+    }
+    if (!found) return false;
+    gi::HaloBf16Args &a = out.args;
+    a.N = p.N;
+    a.Ci = p.Ci;
+    a.H = p.H;
+    a.W = p.W;
+    a.Co = p.Co;
+    a.kH = p.kH;
+    a.kW = p.kW;
+    a.YP = YP;
+    a.XP = XP;
+    a.Cop = Cop;
+    a.nchunks = nchunks;
+    a.gp_bytes = (uint32_t)gp_bytes;
+    a.wk_bytes = (uint32_t)wk_bytes;
+    a.d_bytes = (uint32_t)((int64_t)p.N * p.Ci * p.H * p.W * 4);
+    out.lds = (size_t)2 * a.nq * 16 * 64;
+    out.gp_bytes = (size_t)(gp_bytes + 255) / 256 * 256;
+    out.wk_bytes = (size_t)wk_bytes;
+    return true;
+}
+
 // Generic plan: phase-split gathered GEMM, launches of at most
 // kMaxPhasesPerLaunch phases.
 void plan_generic(const conv2d_gi_params &p, const std::vector<Phase> &phases, Plan &plan) {
@@ -320,6 +406,12 @@ Plan make_plan(const conv2d_gi_params &p, bool bf16) {
         plan.ws_bytes = (size_t)plan.halo.ws_floats * sizeof(float);
         return plan;
     }
+    if (bf16 && (forced == CONV2D_GI_VARIANT_HALO || forced == CONV2D_GI_VARIANT_AUTO) &&
+        plan_halo_bf16(p, plan.hb)) {
+        plan.variant = CONV2D_GI_VARIANT_HALO;
+        plan.ws_bytes = plan.hb.gp_bytes + plan.hb.wk_bytes;
+        return plan;
+    }
     plan_generic(p, phases, plan);
     return plan;
 }
@@ -350,7 +442,16 @@ int run(const T *grad_out, const T *weight, float *dst, const conv2d_gi_params *
         e = workspace_for(dev, stream, plan.ws_bytes, &ws);
         if (e != hipSuccess) return fail_hip(e);
         const int kHW = p->kH * p->kW;
-        if (plan.variant == CONV2D_GI_VARIANT_HALO)
+        if (plan.variant == CONV2D_GI_VARIANT_HALO && bf16) {
+            HaloBf16Plan &h = plan.hb;
+            uint16_t *gp = (uint16_t *)ws;
+            uint16_t *wk = (uint16_t *)((char *)ws + h.gp_bytes);
+            e = gi::launch_pad_nhwc_bf16((const uint16_t *)grad_out, gp, h.args, p->oH, p->oW,
+                                         p->pad_h, p->pad_w, stream);
+            if (e == hipSuccess)
+                e = gi::launch_weight_frag_bf16((const uint16_t *)weight, wk, h.args, h.ci_tiles,
+                                                stream);
+        } else if (plan.variant == CONV2D_GI_VARIANT_HALO)
             e = gi::launch_weight_image_f32((const float *)weight, (float *)ws, plan.halo.args,
                                             p->kH, p->kW, plan.halo.ci_tiles,
                                             plan.halo.ws_floats, stream);
@@ -364,7 +465,15 @@ int run(const T *grad_out, const T *weight, float *dst, const conv2d_gi_params *
     }
     e = hipSuccess;
     if (g_prof_begin && g_prof_end) e = hipEventRecord(g_prof_begin, stream);
-    if (plan.variant == CONV2D_GI_VARIANT_HALO) {
+    if (plan.variant == CONV2D_GI_VARIANT_HALO && bf16) {
+        if (e == hipSuccess) {
+            HaloBf16Plan &h = plan.hb;
+            h.args.gp = (const uint16_t *)ws;
+            h.args.wk = (const uint16_t *)((char *)ws + h.gp_bytes);
+            h.args.dst = dst;
+            e = gi::launch_halo_bf16(h.args, h.cfg, h.tiles, h.ci_tiles, h.lds, stream);
+        }
+    } else if (plan.variant == CONV2D_GI_VARIANT_HALO) {
         if (e == hipSuccess) {
             HaloPlan &h = plan.halo;
             h.args.grad_out = (const float *)grad_out;
@@ -393,6 +502,16 @@ std::string describe(const Plan &plan, bool bf16) {
     s += " dtype=";
     s += bf16 ? "bf16" : "f32";
     s += " ws_bytes=" + std::to_string(plan.ws_bytes);
+    if (plan.variant == CONV2D_GI_VARIANT_HALO && bf16) {
+        const HaloBf16Plan &h = plan.hb;
+        const gi::HaloBf16Args &a = h.args;
+        s += " launches=3 [cfg=" + std::to_string(h.cfg) + " tile=" + std::to_string(a.TR) + "x" +
+             std::to_string(a.TC) + " wgs=" + std::to_string(h.tiles) + "x" +
+             std::to_string(h.ci_tiles) + " lds=" + std::to_string(h.lds) +
+             " halo=" + std::to_string(a.HR) + "x" + std::to_string(a.HC) +
+             " chunks=" + std::to_string(a.nchunks) + "]";
+        return s;
+    }
     if (plan.variant == CONV2D_GI_VARIANT_HALO) {
         const HaloPlan &h = plan.halo;
         const gi::HaloArgs &a = h.args;

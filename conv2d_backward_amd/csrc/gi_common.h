@@ -86,3 +86,32 @@ struct HaloArgs {
 };
 
 }  // namespace gi
+
+namespace gi {
+
+// Arguments of the bf16 halo kernel (stride 1).
+//
+// gp: grad_out as zero-padded NHWC bf16, gp[N][YP][XP][Cop] with
+//     YP = H + kH - 1, XP = W + kW - 1, Cop = nchunks * 32: element (y, x)
+//     holds grad_out[oh = y - (kH-1-pad_h)][ow = x - (kW-1-pad_w)] (zero
+//     outside the image), so tap (kh, kw) of input pixel (ih, iw) reads
+//     gp[ih + kH-1-kh][iw + kW-1-kw].
+// wk: weights in the lane order of the MFMA A fragments,
+//     wk[ci tile][chunk][tap][ci block of 16][lane][8]: lane l holds the 8
+//     output channels chunk*32 + 8*(l/16) + e of input channel
+//     tile*64 + block*16 + l%16 (zero past Ci or Co).
+struct HaloBf16Args {
+    const uint16_t *gp;
+    const uint16_t *wk;
+    float *dst;             // [N, Ci, H, W] fp32
+    uint32_t gp_bytes, wk_bytes, d_bytes;
+    int32_t N, Ci, H, W, Co, kH, kW;
+    int32_t YP, XP, Cop, nchunks;
+    int32_t TR, TC, row_tiles, col_tiles;
+    int32_t HR, HC;         // halo rows / columns: TR + kH - 1, TC + kW - 1
+    int32_t nq;             // halo DMA groups of 16 positions per stage
+    int32_t pad_;
+};
+
+}  // namespace gi
+

@@ -1,0 +1,334 @@
+// kernels_halo_bf16.hip -- bf16-input halo-tile implicit-GEMM kernel for
+// gfx950 (stride 1), fp32 accumulation and output.
+//
+// The contraction is the implicit GEMM of meganeura conv2d_grad_input_gemm.wgsl
+// (header comment: C[Ci, pixels] = A[Ci, K] x B[K, pixels], K = Co*kH*kW),
+// with K ordered (chunk of 32 output channels, tap, channel).  The bf16 matrix
+// cores take 8 consecutive k per lane from both operands, so both operands are
+// laid out output-channel-minor by two prologues:
+//   * grad_out -> zero-padded NHWC copy (the zero border is the transposed
+//     padding kH-1-pad of the shader's header comment), so a halo position's
+//     32 channels of a chunk are one 64-byte run;
+//   * weight   -> the exact lane order of the MFMA A fragments.
+//
+// Work-group: 256 threads = 2 x 2 waves over 64 input channels x a TR x TC
+// pixel tile of one image.  Wave (wm, wn) owns input-channel blocks 2wm, 2wm+1
+// (16 each) and pixel blocks wn*NBW .. wn*NBW + NBW - 1 (16 pixels each).
+// Per chunk the tile's halo, (TR+kH-1) x (TC+kW-1) positions x 32 channels,
+// is copied into LDS by direct global -> LDS loads (double-buffered), and tap
+// (kh, kw) reads its B fragments as the halo shifted by (kH-1-kh, kW-1-kw).
+// A fragments are loaded from the weight image straight into registers, two
+// taps ahead.  LDS holds a position's four 16-byte channel groups in slots
+// permuted by (position / 4) mod 4 so that 16 lanes reading 16 consecutive
+// positions hit 16 different bank groups.
+//
+// V_MFMA_F32_16X16X32_BF16: lane l = 16*g + i supplies A[i][k = 8g .. 8g+7]
+// and B[k = 8g .. 8g+7][i] and receives D[4g + r][i], r = 0..3.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gi_common.h"
+#include "gi_launch.h"
+
+namespace gi {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+namespace {
+
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9)
+constexpr int kOOB = 0x7ffffff0;         // byte offset past the end of every buffer
+constexpr int kQW = 4;                   // halo DMA groups per wave (<= 256 positions)
+
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (long)bytes, kRsrcWord3);
+}
+
+template <int NBW, int T>
+__global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void gi_halo_bf16(
+    const HaloBf16Args A) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j16 = lane & 15, g = lane >> 4;
+    const int wm = wave & 1, wn = wave >> 1;
+
+    int t = blockIdx.x;
+    const int ct = t % A.col_tiles;
+    t /= A.col_tiles;
+    const int rt = t % A.row_tiles;
+    const int n = t / A.row_tiles;
+    const int ci_tile = blockIdx.y;
+    const int a0 = rt * A.TR, b0 = ct * A.TC;
+    const int hpos = A.HR * A.HC;
+    const int stage = A.nq * 16 * 64;  // bytes per LDS stage
+
+    const __amdgpu_buffer_rsrc_t grs = make_rsrc(A.gp, A.gp_bytes);
+    const __amdgpu_buffer_rsrc_t wrs = make_rsrc(A.wk, A.wk_bytes);
+    const __amdgpu_buffer_rsrc_t drs = make_rsrc(A.dst, A.d_bytes);
+
+    // This lane's pixel in each of its blocks: halo position (0 outside the
+    // tile or image: a valid position whose column is never stored).
+    int ppos[NBW];
+#pragma unroll
+    for (int b = 0; b < NBW; ++b) {
+        const int p = (wn * NBW + b) * 16 + j16;
+        const int r = p / A.TC, c = p - (p / A.TC) * A.TC;
+        const bool v = p < A.TR * A.TC && a0 + r < A.H && b0 + c < A.W;
+        ppos[b] = v ? r * A.HC + c : 0;
+    }
+
+    // Halo DMA: group q covers positions 16q .. 16q+15; lane -> (position
+    // 16q + lane/4, slot lane%4) loads channel group slot ^ ((pos/4) & 3).
+    int goff[kQW];
+#pragma unroll
+    for (int i = 0; i < kQW; ++i) {
+        const int q = wave + 4 * i;
+        const int pos = q * 16 + (lane >> 2);
+        const int slot = lane & 3;
+        const int kg = slot ^ ((pos >> 2) & 3);
+        const int hr = pos / A.HC, hc = pos - (pos / A.HC) * A.HC;
+        const int y = a0 + hr, x = b0 + hc;
+        const bool v = q < A.nq && pos < hpos && y < A.YP && x < A.XP;
+        goff[i] = v ? (((n * A.YP + y) * A.XP + x) * A.Cop + 8 * kg) * 2 : kOOB;
+    }
+    auto issue = [&](int chunk, int buf) {
+#pragma unroll
+        for (int i = 0; i < kQW; ++i) {
+            const int q = wave + 4 * i;
+            if (q < A.nq) {
+                const int off = goff[i] == kOOB ? kOOB : goff[i] + chunk * 64;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    grs, (lds_ptr_t)(smem + buf * stage + q * 1024), 16, off, 0, 0, 0);
+            }
+        }
+    };
+
+    // A fragments: weight image offset of (chunk, tap, block 2wm + cb).
+    const int wlane = (ci_tile * A.nchunks * T * 4 + 2 * wm) * 1024 + lane * 16;
+    auto aload = [&](int chunk, int tap, int cb) {
+        const int off = wlane + ((chunk * T + tap) * 4 + cb) * 1024;
+        return __builtin_bit_cast(v8bf, __builtin_amdgcn_raw_buffer_load_b128(wrs, off, 0, 0));
+    };
+
+    v4f acc[2][NBW];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int b = 0; b < NBW; ++b) acc[cb][b] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    // Tap shifts in halo positions.
+    int shift[T];
+#pragma unroll
+    for (int tp = 0; tp < T; ++tp) {
+        const int kh = tp / A.kW, kw = tp - (tp / A.kW) * A.kW;
+        shift[tp] = (A.kH - 1 - kh) * A.HC + (A.kW - 1 - kw);
+    }
+
+    // A ring of three tap slots: step s = chunk*T + tap uses slot s % 3, and
+    // step s + 2 is loaded while step s computes (T is a multiple of 3).
+    static_assert(T % 3 == 0, "tap count must be a multiple of 3");
+    v8bf fa[3][2];
+    fa[0][0] = aload(0, 0, 0);
+    fa[0][1] = aload(0, 0, 1);
+    if (T > 1 || A.nchunks > 1) {
+        const int c1 = T > 1 ? 0 : 1, t1 = T > 1 ? 1 : 0;
+        fa[1][0] = aload(c1, t1, 0);
+        fa[1][1] = aload(c1, t1, 1);
+    }
+
+    issue(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int chunk = 0; chunk < A.nchunks; ++chunk) {
+        const int cur = chunk & 1;
+        if (chunk + 1 < A.nchunks) issue(chunk + 1, cur ^ 1);
+        const unsigned char *hs = smem + cur * stage;
+        // Per-lane positions, opaque to the optimiser so the tap x block
+        // addresses are formed inside the chunk instead of being hoisted out of
+        // the loop and held in registers.
+        int pp[NBW];
+#pragma unroll
+        for (int b = 0; b < NBW; ++b) {
+            pp[b] = ppos[b];
+            asm volatile("" : "+v"(pp[b]));
+        }
+        v8bf fb[2][NBW];
+        auto bfetch = [&](int tp, int sl) {
+#pragma unroll
+            for (int b = 0; b < NBW; ++b) {
+                const int pos = pp[b] + shift[tp];
+                const int slot = g ^ ((pos >> 2) & 3);
+                fb[sl][b] = *(const v8bf *)(hs + (pos * 4 + slot) * 16);
+            }
+        };
+        bfetch(0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int tp = 0; tp < T; ++tp) {
+            const int sl = tp & 1;
+            const int as = tp % 3;
+            // Prefetch: A of step + 2, B of the next tap.
+            {
+                const int t2 = tp + 2;
+                const int c2 = t2 < T ? chunk : chunk + 1;
+                if (c2 < A.nchunks) {
+                    const int t2m = t2 < T ? t2 : t2 - T;
+                    fa[(tp + 2) % 3][0] = aload(c2, t2m, 0);
+                    fa[(tp + 2) % 3][1] = aload(c2, t2m, 1);
+                }
+            }
+            if (tp + 1 < T) bfetch(tp + 1, sl ^ 1);
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+                for (int b = 0; b < NBW; ++b)
+                    acc[cb][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[as][cb], fb[sl][b],
+                                                                         acc[cb][b], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    }
+
+    // Epilogue: D[4g + r][j16] of each block, NCHW fp32.
+    const int plane = A.H * A.W;
+#pragma unroll
+    for (int b = 0; b < NBW; ++b) {
+        const int p = (wn * NBW + b) * 16 + j16;
+        const int r = p / A.TC, c = p - (p / A.TC) * A.TC;
+        const bool pv = p < A.TR * A.TC && a0 + r < A.H && b0 + c < A.W;
+        const int pix = (a0 + r) * A.W + b0 + c;
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int ci = ci_tile * 64 + (2 * wm + cb) * 16 + 4 * g + rr;
+                const int off = (pv && ci < A.Ci) ? ((n * A.Ci + ci) * plane + pix) * 4 : kOOB;
+                const float v = acc[cb][b][rr];
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), drs, off, 0, 0);
+            }
+        }
+    }
+}
+
+template <int NBW, int T>
+hipError_t launch_one(const HaloBf16Args &a, int tiles, int ci_tiles, size_t lds, hipStream_t s) {
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute((const void *)gi_halo_bf16<NBW, T>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((gi_halo_bf16<NBW, T>), dim3(tiles, ci_tiles), dim3(256), lds, s, a);
+    return hipGetLastError();
+}
+
+constexpr int kCfg[][2] = {{7, 9}, {4, 9}, {7, 3}, {4, 3}};
+
+// grad_out NCHW bf16 -> zero-padded NHWC bf16.  One work-group per (row y,
+// image n); channels in blocks of 64 staged through LDS (transposed), written
+// as channel pairs.
+__global__ __launch_bounds__(256) void pad_nhwc_bf16(const uint16_t *__restrict__ g,
+                                                     uint16_t *__restrict__ gp,
+                                                     const HaloBf16Args A, int oH, int oW,
+                                                     int pad_h, int pad_w) {
+    extern __shared__ uint16_t tile[];  // [oW][66]
+    const int y = blockIdx.x, n = blockIdx.y;
+    const int oh = y - (A.kH - 1 - pad_h);
+    const bool row_in = oh >= 0 && oh < oH;
+    const int xoff = A.kW - 1 - pad_w;  // ow = x - xoff
+    uint32_t *out = (uint32_t *)(gp + ((int64_t)n * A.YP + y) * A.XP * A.Cop);
+    for (int co0 = 0; co0 < A.Cop; co0 += 64) {
+        if (row_in) {
+            for (int e = threadIdx.x; e < 64 * oW; e += 256) {
+                const int c = e / oW, ow = e - (e / oW) * oW;
+                const int co = co0 + c;
+                tile[ow * 66 + c] =
+                    co < A.Co ? g[(((int64_t)n * A.Co + co) * oH + oh) * oW + ow] : (uint16_t)0;
+            }
+        }
+        __syncthreads();
+        for (int e = threadIdx.x; e < A.XP * 32; e += 256) {
+            const int x = e >> 5, cp = e & 31;
+            if (co0 + 2 * cp >= A.Cop) continue;
+            const int ow = x - xoff;
+            uint32_t v = 0;
+            if (row_in && ow >= 0 && ow < oW)
+                v = (uint32_t)tile[ow * 66 + 2 * cp] | ((uint32_t)tile[ow * 66 + 2 * cp + 1] << 16);
+            out[((int64_t)x * A.Cop + co0) / 2 + cp] = v;
+        }
+        __syncthreads();
+    }
+}
+
+// Weights [Co][Ci][kH][kW] bf16 -> A-fragment lane order (gi_common.h).
+__global__ __launch_bounds__(256) void weight_frag_bf16(const uint16_t *__restrict__ w,
+                                                        uint16_t *__restrict__ wk,
+                                                        const HaloBf16Args A, int64_t total) {
+    const int T = A.kH * A.kW;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * 256) {
+        const int e = (int)(i & 7);
+        int64_t r = i >> 3;
+        const int l = (int)(r & 63);
+        r >>= 6;
+        const int cb = (int)(r & 3);
+        r >>= 2;
+        const int tap = (int)(r % T);
+        r /= T;
+        const int chunk = (int)(r % A.nchunks);
+        const int ct = (int)(r / A.nchunks);
+        const int ci = ct * 64 + cb * 16 + (l & 15);
+        const int co = chunk * 32 + 8 * (l >> 4) + e;
+        uint16_t v = 0;
+        if (ci < A.Ci && co < A.Co) v = w[((int64_t)co * A.Ci + ci) * T + tap];
+        wk[i] = v;
+    }
+}
+
+}  // namespace
+
+int halo_bf16_config(int nbw, int taps) {
+    for (int i = 0; i < (int)(sizeof(kCfg) / sizeof(kCfg[0])); ++i)
+        if (kCfg[i][0] == nbw && kCfg[i][1] == taps) return i;
+    return -1;
+}
+
+hipError_t launch_halo_bf16(const HaloBf16Args &a, int cfg, int tiles, int ci_tiles, size_t lds,
+                            hipStream_t s) {
+    switch (cfg) {
+        case 0: return launch_one<7, 9>(a, tiles, ci_tiles, lds, s);
+        case 1: return launch_one<4, 9>(a, tiles, ci_tiles, lds, s);
+        case 2: return launch_one<7, 3>(a, tiles, ci_tiles, lds, s);
+        case 3: return launch_one<4, 3>(a, tiles, ci_tiles, lds, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_pad_nhwc_bf16(const uint16_t *g, uint16_t *gp, const HaloBf16Args &a, int oH,
+                                int oW, int pad_h, int pad_w, hipStream_t s) {
+    const size_t lds = (size_t)oW * 66 * sizeof(uint16_t);
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute((const void *)pad_nhwc_bf16,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(pad_nhwc_bf16, dim3(a.YP, a.N), dim3(256), lds, s, g, gp, a, oH, oW, pad_h,
+                       pad_w);
+    return hipGetLastError();
+}
+
+hipError_t launch_weight_frag_bf16(const uint16_t *w, uint16_t *wk, const HaloBf16Args &a,
+                                   int ci_tiles, hipStream_t s) {
+    const int64_t total = (int64_t)ci_tiles * a.nchunks * a.kH * a.kW * 4 * 64 * 8;
+    int64_t b = (total + 255) / 256;
+    const int blocks = (int)(b < 8192 ? (b > 0 ? b : 1) : 8192);
+    hipLaunchKernelGGL(weight_frag_bf16, dim3(blocks), dim3(256), 0, s, w, wk, a, total);
+    return hipGetLastError();
+}
+
+}  // namespace gi

@@ -155,6 +155,29 @@ def test_forced_halo(idx):
     full_parity(s, 1300 + idx, "f32", gi.VARIANT_HALO, dist="normal")
 
 
+HALO_BF16_SHAPES = [
+    MID[0],                                                # ragged Ci tiles, 3 chunks
+    MID[4],                                                # Co = 300: partial last chunk
+    workloads.Shape(2, 16, 9, 9, 5, 3, 3, 1, 1, 1),       # Co below one chunk
+    workloads.Shape(3, 40, 17, 17, 50, 1, 3, 1, 0, 1),    # 1x3
+    workloads.Shape(2, 24, 11, 13, 12, 3, 1, 1, 1, 0),    # 3x1
+    workloads.Shape(1, 64, 6, 6, 8, 3, 3, 1, 0, 0),       # pad 0
+    workloads.Shape(1, 32, 6, 6, 16, 3, 3, 1, 3, 3),      # pad beyond kernel - 1
+    workloads.Shape(2, 64, 14, 14, 64, 3, 3, 1, 1, 1),    # the deep-stage tile
+    workloads.Shape(1, 70, 31, 40, 33, 3, 3, 1, 1, 1),    # several tiles per image
+]
+
+
+@pytest.mark.parametrize("idx", range(len(HALO_BF16_SHAPES)))
+def test_forced_halo_bf16(idx):
+    s = HALO_BF16_SHAPES[idx]
+    gi.set_variant(gi.VARIANT_HALO)
+    desc = gi.plan(gi.make_params(*s.as_tuple()[:10]), True)
+    gi.set_variant(gi.VARIANT_AUTO)
+    assert "variant=halo" in desc, desc
+    full_parity(s, 1500 + idx, "bf16", gi.VARIANT_HALO, dist="normal")
+
+
 # (shape, nb, tile_rows, tile_cols): tiles with ragged row and column tails,
 # tiles wider than the image, rows folded across images, strided phases.
 FORCED_TILES = [
