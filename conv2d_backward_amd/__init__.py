@@ -18,14 +18,14 @@ import os
 __all__ = [
     "grad_input", "Conv2dGiParams", "Conv2dGiError", "LibraryNotBuilt", "load_library",
     "make_params", "validate", "plan", "set_variant", "set_halo_tile", "release_workspaces", "set_profile_events", "library_path", "exported_names",
-    "OK", "EINVAL", "EUNSUPPORTED", "EHIP", "VARIANT_AUTO", "VARIANT_GENERIC", "VARIANT_HALO",
+    "OK", "EINVAL", "EUNSUPPORTED", "EHIP", "VARIANT_AUTO", "VARIANT_GENERIC", "VARIANT_HALO", "VARIANT_STEM",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_PKG, "libconv2d_gi.so")
 
 OK, EINVAL, EUNSUPPORTED, EHIP = 0, 1, 2, 3
-VARIANT_AUTO, VARIANT_GENERIC, VARIANT_HALO = 0, 1, 2
+VARIANT_AUTO, VARIANT_GENERIC, VARIANT_HALO, VARIANT_STEM = 0, 1, 2, 3
 
 _FIELDS = ("N", "Ci", "H", "W", "Co", "kH", "kW", "stride", "pad_h", "pad_w", "oH", "oW")
 

@@ -137,6 +137,12 @@ struct HaloBf16Plan {
     double cost = 0.0;
 };
 
+// A small-Ci plan (fp32, Ci <= 4): one prologue and one launch.
+struct StemPlan {
+    gi::StemArgs args{};
+    size_t ws_bytes = 0;
+};
+
 struct Plan {
     int variant = CONV2D_GI_VARIANT_GENERIC;
     bool bf16 = false;
@@ -144,6 +150,7 @@ struct Plan {
     std::vector<Launch> launches;  // generic
     HaloPlan halo;                 // halo, fp32
     HaloBf16Plan hb;               // halo, bf16
+    StemPlan stem;                 // small Ci, fp32
 };
 
 constexpr int kCUs = 256;               // MI355X compute units
@@ -186,6 +193,7 @@ bool plan_halo(const conv2d_gi_params &p, const std::vector<Phase> &phases, Halo
     }
     const int ci_tiles = (p.Ci + gi::kHaloCT - 1) / gi::kHaloCT;
     if (w_ci_stride * ci_tiles * 4 > lim || maxT == 0) return false;
+    if (gi::weight_image_f32_lds(p.kH, p.kW) > kLdsBytes) return false;
     static const int kNB[] = {4, 8, 13};
     const int f_nb = g_tile_nb.load(), f_tr = g_tile_tr.load(), f_tc = g_tile_tc.load();
     const bool forced = f_nb > 0;
@@ -359,6 +367,64 @@ bool plan_halo_bf16(const conv2d_gi_params &p, HaloBf16Plan &out) {
     return true;
 }
 
+// Small-Ci plan (fp32, Ci <= 4): 16 x 16 phase-grid tiles, one work-group
+// per (image, tile, phase); every phase's tap count must be one the kernel
+// is built for and its halo must fit the kernel's staging.
+bool plan_stem(const conv2d_gi_params &p, const std::vector<Phase> &phases, StemPlan &out) {
+    if (p.Ci > 4 || phases.empty() || (int)phases.size() > gi::kMaxPhasesPerLaunch) return false;
+    const int64_t lim = 0x7fff0000LL;
+    if ((int64_t)p.N * p.Co * p.oH * p.oW * 4 > lim) return false;
+    if ((int64_t)p.N * p.Ci * p.H * p.W * 4 > lim) return false;
+    gi::StemArgs &a = out.args;
+    a = gi::StemArgs{};
+    const int nchunks = (p.Co + 3) / 4;
+    int maxHa = 0, maxWb = 0, hpmax = 16;
+    int64_t groups = 0;
+    for (size_t i = 0; i < phases.size(); ++i) {
+        const Phase &ph = phases[i];
+        const int T = ph.J_h * ph.J_w;
+        if (!gi::stem_f32_taps_ok(T)) return false;
+        const int hpos = (16 + ph.J_h - 1) * (16 + ph.J_w - 1);
+        if (hpos > 512) return false;
+        hpmax = std::max(hpmax, (hpos + 15) / 16 * 16);
+        maxHa = std::max(maxHa, ph.Ha);
+        maxWb = std::max(maxWb, ph.Wb);
+        gi::StemPhase &s = a.ph[i];
+        s.rho_h = ph.rho_h;
+        s.rho_w = ph.rho_w;
+        s.q_h = ph.q_h;
+        s.q_w = ph.q_w;
+        s.r_h = ph.r_h;
+        s.r_w = ph.r_w;
+        s.J_h = ph.J_h;
+        s.J_w = ph.J_w;
+        s.Ha = ph.Ha;
+        s.Wb = ph.Wb;
+        s.woff = (int)groups;
+        groups += (int64_t)nchunks * T;
+    }
+    if (groups * 64 > lim) return false;
+    a.N = p.N;
+    a.Ci = p.Ci;
+    a.H = p.H;
+    a.W = p.W;
+    a.Co = p.Co;
+    a.oH = p.oH;
+    a.oW = p.oW;
+    a.stride = p.stride;
+    a.nphases = (int)phases.size();
+    a.nchunks = nchunks;
+    a.tiles_r = (maxHa + 15) / 16;
+    a.tiles_c = (maxWb + 15) / 16;
+    a.HPmax = hpmax;
+    a.g_bytes = (uint32_t)((int64_t)p.N * p.Co * p.oH * p.oW * 4);
+    a.d_bytes = (uint32_t)((int64_t)p.N * p.Ci * p.H * p.W * 4);
+    a.w_bytes = (uint32_t)(groups * 64);
+    if ((int64_t)p.N * a.tiles_r * a.tiles_c * a.nphases > INT32_MAX) return false;
+    out.ws_bytes = (size_t)std::max<int64_t>(groups * 64, 64);
+    return true;
+}
+
 // Generic plan: phase-split gathered GEMM, launches of at most
 // kMaxPhasesPerLaunch phases.
 void plan_generic(const conv2d_gi_params &p, const std::vector<Phase> &phases, Plan &plan) {
@@ -406,6 +472,12 @@ Plan make_plan(const conv2d_gi_params &p, bool bf16) {
         plan.ws_bytes = (size_t)plan.halo.ws_floats * sizeof(float);
         return plan;
     }
+    if (!bf16 && (forced == CONV2D_GI_VARIANT_STEM || forced == CONV2D_GI_VARIANT_AUTO) &&
+        plan_stem(p, phases, plan.stem)) {
+        plan.variant = CONV2D_GI_VARIANT_STEM;
+        plan.ws_bytes = plan.stem.ws_bytes;
+        return plan;
+    }
     if (bf16 && (forced == CONV2D_GI_VARIANT_HALO || forced == CONV2D_GI_VARIANT_AUTO) &&
         plan_halo_bf16(p, plan.hb)) {
         plan.variant = CONV2D_GI_VARIANT_HALO;
@@ -442,7 +514,10 @@ int run(const T *grad_out, const T *weight, float *dst, const conv2d_gi_params *
         e = workspace_for(dev, stream, plan.ws_bytes, &ws);
         if (e != hipSuccess) return fail_hip(e);
         const int kHW = p->kH * p->kW;
-        if (plan.variant == CONV2D_GI_VARIANT_HALO && bf16) {
+        if (plan.variant == CONV2D_GI_VARIANT_STEM) {
+            e = gi::launch_weight_stem_f32((const float *)weight, (float *)ws, plan.stem.args,
+                                           p->kH, p->kW, stream);
+        } else if (plan.variant == CONV2D_GI_VARIANT_HALO && bf16) {
             HaloBf16Plan &h = plan.hb;
             uint16_t *gp = (uint16_t *)ws;
             uint16_t *wk = (uint16_t *)((char *)ws + h.gp_bytes);
@@ -465,7 +540,15 @@ int run(const T *grad_out, const T *weight, float *dst, const conv2d_gi_params *
     }
     e = hipSuccess;
     if (g_prof_begin && g_prof_end) e = hipEventRecord(g_prof_begin, stream);
-    if (plan.variant == CONV2D_GI_VARIANT_HALO && bf16) {
+    if (plan.variant == CONV2D_GI_VARIANT_STEM) {
+        if (e == hipSuccess) {
+            gi::StemArgs &a = plan.stem.args;
+            a.grad_out = (const float *)grad_out;
+            a.wk = (const float *)ws;
+            a.dst = dst;
+            e = gi::launch_stem_f32(a, stream);
+        }
+    } else if (plan.variant == CONV2D_GI_VARIANT_HALO && bf16) {
         if (e == hipSuccess) {
             HaloBf16Plan &h = plan.hb;
             h.args.gp = (const uint16_t *)ws;
@@ -498,10 +581,26 @@ int run(const T *grad_out, const T *weight, float *dst, const conv2d_gi_params *
 
 std::string describe(const Plan &plan, bool bf16) {
     std::string s = "variant=";
-    s += plan.variant == CONV2D_GI_VARIANT_HALO ? "halo" : "generic";
+    s += plan.variant == CONV2D_GI_VARIANT_HALO   ? "halo"
+         : plan.variant == CONV2D_GI_VARIANT_STEM ? "stem"
+                                                  : "generic";
     s += " dtype=";
     s += bf16 ? "bf16" : "f32";
     s += " ws_bytes=" + std::to_string(plan.ws_bytes);
+    if (plan.variant == CONV2D_GI_VARIANT_STEM) {
+        const gi::StemArgs &a = plan.stem.args;
+        s += " launches=1 [tiles=" + std::to_string(a.N) + "x" + std::to_string(a.tiles_r) + "x" +
+             std::to_string(a.tiles_c) + "x" + std::to_string(a.nphases) +
+             " chunks=" + std::to_string(a.nchunks);
+        for (int i = 0; i < a.nphases; ++i) {
+            const gi::StemPhase &ph = a.ph[i];
+            s += " phase(" + std::to_string(ph.rho_h) + "," + std::to_string(ph.rho_w) +
+                 ") taps=" + std::to_string(ph.J_h) + "x" + std::to_string(ph.J_w) +
+                 " px=" + std::to_string(ph.Ha) + "x" + std::to_string(ph.Wb);
+        }
+        s += "]";
+        return s;
+    }
     if (plan.variant == CONV2D_GI_VARIANT_HALO && bf16) {
         const HaloBf16Plan &h = plan.hb;
         const gi::HaloBf16Args &a = h.args;
@@ -573,7 +672,7 @@ const char *conv2d_gi_last_hip_error(void) { return g_last_hip; }
 
 int conv2d_gi_set_variant(int variant) {
     if (variant != CONV2D_GI_VARIANT_AUTO && variant != CONV2D_GI_VARIANT_GENERIC &&
-        variant != CONV2D_GI_VARIANT_HALO)
+        variant != CONV2D_GI_VARIANT_HALO && variant != CONV2D_GI_VARIANT_STEM)
         return -1;
     return g_variant.exchange(variant);
 }

@@ -115,3 +115,38 @@ struct HaloBf16Args {
 
 }  // namespace gi
 
+namespace gi {
+
+// One stride phase of the small-Ci ("stem") kernel.
+struct StemPhase {
+    int32_t rho_h, rho_w;   // input-pixel residues mod stride
+    int32_t q_h, q_w;       // (rho + pad) div stride
+    int32_t r_h, r_w;       // first tap of the phase: (rho + pad) mod stride
+    int32_t J_h, J_w;       // taps of the phase per dimension
+    int32_t Ha, Wb;         // pixels of the phase per image
+    int32_t woff;           // first (chunk, tap) group of the phase in the weight image
+    int32_t pad_;
+};
+
+// Arguments of the fp32 small-Ci kernel (Ci <= 4).  Work-groups are
+// (image, tile row, tile column, phase) with the phase fastest; a tile is
+// 16 x 16 pixels of the phase grid.
+//
+// Weight image (float4 units): wk[phase][chunk of 4 co][tap][ci of 4] holds
+// the four output channels chunk*4 .. +3 of one (ci, tap), zero past Ci / Co;
+// float4 index = (woff + chunk * taps + tap) * 4 + ci.
+struct StemArgs {
+    const float *grad_out;  // [N, Co, oH, oW]
+    const float *wk;
+    float *dst;             // [N, Ci, H, W]
+    uint32_t g_bytes, w_bytes, d_bytes;
+    int32_t N, Ci, H, W, Co, oH, oW, stride;
+    int32_t nphases, nchunks;
+    int32_t tiles_r, tiles_c;
+    int32_t HPmax;          // halo positions of the largest phase, rounded up to 16
+    int32_t pad_;
+    StemPhase ph[kMaxPhasesPerLaunch];
+};
+
+}  // namespace gi
+

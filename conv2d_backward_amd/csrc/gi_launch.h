@@ -40,6 +40,8 @@ hipError_t launch_halo_f32(const HaloArgs &a, int cfg, int tiles, int ci_tiles, 
 size_t halo_f32_lds_bytes(int maxT, int HPc);
 
 // Weight image of the halo kernel (layout in gi_common.h); `total` floats.
+// Needs weight_image_f32_lds(kH, kW) bytes of LDS per work-group.
+size_t weight_image_f32_lds(int kH, int kW);
 hipError_t launch_weight_image_f32(const float *w, float *wk, const HaloArgs &a, int kH, int kW,
                                    int ci_tiles, int64_t total, hipStream_t s);
 
@@ -53,5 +55,12 @@ hipError_t launch_pad_nhwc_bf16(const uint16_t *g, uint16_t *gp, const HaloBf16A
                                 int oW, int pad_h, int pad_w, hipStream_t s);
 hipError_t launch_weight_frag_bf16(const uint16_t *w, uint16_t *wk, const HaloBf16Args &a,
                                    int ci_tiles, hipStream_t s);
+
+// Small-Ci fp32 kernel (kernels_stem_f32.hip): Ci <= 4, any stride whose
+// phases have a tap count in the served set (stem_f32_taps_ok).
+bool stem_f32_taps_ok(int taps);
+hipError_t launch_stem_f32(const StemArgs &a, hipStream_t s);
+hipError_t launch_weight_stem_f32(const float *w, float *wk, const StemArgs &a, int kH, int kW,
+                                  hipStream_t s);
 
 }  // namespace gi

@@ -229,64 +229,107 @@ hipError_t launch_one(const HaloBf16Args &a, int tiles, int ci_tiles, size_t lds
 
 constexpr int kCfg[][2] = {{7, 9}, {4, 9}, {7, 3}, {4, 3}};
 
-// grad_out NCHW bf16 -> zero-padded NHWC bf16.  One work-group per (row y,
-// image n); channels in blocks of 64 staged through LDS (transposed), written
-// as channel pairs.
+// grad_out NCHW bf16 -> zero-padded NHWC bf16.  One work-group per (image n,
+// block of 64 channels, band of RB rows of gp): the band is read along ow
+// (coalesced), packed into channel pairs in LDS, and written as 16-byte runs
+// of 8 channels per position.
 __global__ __launch_bounds__(256) void pad_nhwc_bf16(const uint16_t *__restrict__ g,
                                                      uint16_t *__restrict__ gp,
                                                      const HaloBf16Args A, int oH, int oW,
-                                                     int pad_h, int pad_w) {
-    extern __shared__ uint16_t tile[];  // [oW][66]
-    const int y = blockIdx.x, n = blockIdx.y;
-    const int oh = y - (A.kH - 1 - pad_h);
-    const bool row_in = oh >= 0 && oh < oH;
+                                                     int pad_h, int pad_w, int RB) {
+    extern __shared__ uint32_t band[];  // [RB][oW][33] channel pairs
+    const int n = blockIdx.x, co0 = blockIdx.y * 64, y0 = blockIdx.z * RB;
+    const int yoff = A.kH - 1 - pad_h;  // oh = y - yoff
     const int xoff = A.kW - 1 - pad_w;  // ow = x - xoff
-    uint32_t *out = (uint32_t *)(gp + ((int64_t)n * A.YP + y) * A.XP * A.Cop);
-    for (int co0 = 0; co0 < A.Cop; co0 += 64) {
-        if (row_in) {
-            for (int e = threadIdx.x; e < 64 * oW; e += 256) {
-                const int c = e / oW, ow = e - (e / oW) * oW;
-                const int co = co0 + c;
-                tile[ow * 66 + c] =
-                    co < A.Co ? g[(((int64_t)n * A.Co + co) * oH + oh) * oW + ow] : (uint16_t)0;
+    const int per_pair = RB * oW;
+    const int nload = 32 * per_pair;
+    for (int e0 = 0; e0 < nload; e0 += 256 * 8) {
+        uint32_t v[8];
+        int at[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int e = e0 + u * 256 + threadIdx.x;
+            at[u] = -1;
+            v[u] = 0;
+            if (e < nload) {
+                const int cp = e / per_pair, rem = e - (e / per_pair) * per_pair;
+                const int ry = rem / oW, ow = rem - (rem / oW) * oW;
+                const int oh = y0 + ry - yoff;
+                const int co = co0 + 2 * cp;
+                at[u] = (ry * oW + ow) * 33 + cp;
+                if (y0 + ry < A.YP && oh >= 0 && oh < oH) {
+                    const int64_t base = (((int64_t)n * A.Co + co) * oH + oh) * oW + ow;
+                    const uint32_t lo = co < A.Co ? g[base] : 0u;
+                    const uint32_t hi = co + 1 < A.Co ? g[base + (int64_t)oH * oW] : 0u;
+                    v[u] = lo | (hi << 16);
+                }
             }
         }
-        __syncthreads();
-        for (int e = threadIdx.x; e < A.XP * 32; e += 256) {
-            const int x = e >> 5, cp = e & 31;
-            if (co0 + 2 * cp >= A.Cop) continue;
-            const int ow = x - xoff;
-            uint32_t v = 0;
-            if (row_in && ow >= 0 && ow < oW)
-                v = (uint32_t)tile[ow * 66 + 2 * cp] | ((uint32_t)tile[ow * 66 + 2 * cp + 1] << 16);
-            out[((int64_t)x * A.Cop + co0) / 2 + cp] = v;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (at[u] >= 0) band[at[u]] = v[u];
+    }
+    __syncthreads();
+    const int groups = min(8, (A.Cop - co0) / 8);  // 16-byte groups of 8 channels
+    const int nstore = RB * A.XP * 8;
+    for (int e = threadIdx.x; e < nstore; e += 256) {
+        const int q = e & 7, pos = e >> 3;
+        const int ry = pos / A.XP, x = pos - (pos / A.XP) * A.XP;
+        const int y = y0 + ry;
+        if (q >= groups || y >= A.YP) continue;
+        const int ow = x - xoff;
+        uint4 v = {0u, 0u, 0u, 0u};
+        if (ow >= 0 && ow < oW) {
+            const uint32_t *src = band + (ry * oW + ow) * 33 + 4 * q;
+            v = uint4{src[0], src[1], src[2], src[3]};
         }
-        __syncthreads();
+        *(uint4 *)(gp + (((int64_t)n * A.YP + y) * A.XP + x) * A.Cop + co0 + 8 * q) = v;
     }
 }
 
-// Weights [Co][Ci][kH][kW] bf16 -> A-fragment lane order (gi_common.h).
+// Weights [Co][Ci][kH][kW] bf16 -> A-fragment lane order (gi_common.h).  One
+// work-group per (chunk of 32 output channels, ci tile, lane group g): it
+// reads the 8 output channels 8g .. 8g+7 of the chunk for the tile's input
+// channels and every tap (one contiguous run per channel) into LDS, and each
+// thread then writes one lane's 16 bytes.
 __global__ __launch_bounds__(256) void weight_frag_bf16(const uint16_t *__restrict__ w,
                                                         uint16_t *__restrict__ wk,
-                                                        const HaloBf16Args A, int64_t total) {
+                                                        const HaloBf16Args A) {
+    extern __shared__ uint16_t slab[];  // [8 co][64 ci * T]
+    const int chunk = blockIdx.x, ct = blockIdx.y, g = blockIdx.z;
     const int T = A.kH * A.kW;
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
-         i += (int64_t)gridDim.x * 256) {
-        const int e = (int)(i & 7);
-        int64_t r = i >> 3;
-        const int l = (int)(r & 63);
-        r >>= 6;
-        const int cb = (int)(r & 3);
-        r >>= 2;
-        const int tap = (int)(r % T);
-        r /= T;
-        const int chunk = (int)(r % A.nchunks);
-        const int ct = (int)(r / A.nchunks);
-        const int ci = ct * 64 + cb * 16 + (l & 15);
-        const int co = chunk * 32 + 8 * (l >> 4) + e;
-        uint16_t v = 0;
-        if (ci < A.Ci && co < A.Co) v = w[((int64_t)co * A.Ci + ci) * T + tap];
-        wk[i] = v;
+    const int run = 64 * T;
+    const int ci_rows = min(64, A.Ci - ct * 64);
+    const int nload = 8 * run;
+    for (int e0 = 0; e0 < nload; e0 += 256 * 16) {
+        uint16_t v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int e = e0 + u * 256 + threadIdx.x;
+            const int c = e / run, r = e - (e / run) * run;
+            const int co = chunk * 32 + 8 * g + c;
+            v[u] = (e < nload && co < A.Co && r < ci_rows * T)
+                       ? w[((int64_t)co * A.Ci + (int64_t)ct * 64) * T + r]
+                       : (uint16_t)0;
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int e = e0 + u * 256 + threadIdx.x;
+            if (e < nload) slab[e] = v[u];
+        }
+    }
+    __syncthreads();
+    // Lanes 16g .. 16g+15 of every (tap, ci block) of this (ci tile, chunk).
+    uint4 *out = (uint4 *)(wk + ((int64_t)ct * A.nchunks + chunk) * T * 2048);
+    for (int f = threadIdx.x; f < T * 64; f += 256) {
+        const int tap = f >> 6, cb = (f >> 4) & 3, l16 = f & 15;
+        const int ci = cb * 16 + l16;
+        uint32_t h[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            h[q] = (uint32_t)slab[(2 * q) * run + ci * T + tap] |
+                   ((uint32_t)slab[(2 * q + 1) * run + ci * T + tap] << 16);
+        out[(tap * 4 + cb) * 64 + 16 * g + l16] = uint4{h[0], h[1], h[2], h[3]};
     }
 }
 
@@ -311,23 +354,34 @@ hipError_t launch_halo_bf16(const HaloBf16Args &a, int cfg, int tiles, int ci_ti
 
 hipError_t launch_pad_nhwc_bf16(const uint16_t *g, uint16_t *gp, const HaloBf16Args &a, int oH,
                                 int oW, int pad_h, int pad_w, hipStream_t s) {
-    const size_t lds = (size_t)oW * 66 * sizeof(uint16_t);
+    // Rows per work-group: at most what fits 16 KB of LDS, and few enough that
+    // the grid has some 2048 work-groups to keep loads in flight.
+    int RB = (int)(16384 / ((size_t)oW * 33 * sizeof(uint32_t)));
+    const int64_t others = (int64_t)a.N * ((a.Cop + 63) / 64);
+    const int want = (int)((a.YP * others + 2047) / 2048);
+    if (want < RB) RB = want;
+    RB = RB < 1 ? 1 : (RB > a.YP ? a.YP : RB);
+    const size_t lds = (size_t)RB * oW * 33 * sizeof(uint32_t);
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void *)pad_nhwc_bf16,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(pad_nhwc_bf16, dim3(a.YP, a.N), dim3(256), lds, s, g, gp, a, oH, oW, pad_h,
-                       pad_w);
+    hipLaunchKernelGGL(pad_nhwc_bf16, dim3(a.N, (a.Cop + 63) / 64, (a.YP + RB - 1) / RB),
+                       dim3(256), lds, s, g, gp, a, oH, oW, pad_h, pad_w, RB);
     return hipGetLastError();
 }
 
 hipError_t launch_weight_frag_bf16(const uint16_t *w, uint16_t *wk, const HaloBf16Args &a,
                                    int ci_tiles, hipStream_t s) {
-    const int64_t total = (int64_t)ci_tiles * a.nchunks * a.kH * a.kW * 4 * 64 * 8;
-    int64_t b = (total + 255) / 256;
-    const int blocks = (int)(b < 8192 ? (b > 0 ? b : 1) : 8192);
-    hipLaunchKernelGGL(weight_frag_bf16, dim3(blocks), dim3(256), 0, s, w, wk, a, total);
+    const size_t lds = (size_t)8 * 64 * a.kH * a.kW * sizeof(uint16_t);
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute((const void *)weight_frag_bf16,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(weight_frag_bf16, dim3(a.nchunks, ci_tiles, 4), dim3(256), lds, s, w, wk,
+                       a);
     return hipGetLastError();
 }
 

@@ -47,6 +47,7 @@ namespace {
 
 static_assert(kHaloCT == 64, "four waves of 16 input channels");
 static_assert(kHaloBC == 8, "four co pairs per chunk");
+constexpr int kHalo64 = 64;              // input channels of a weight-image row
 
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9)
 constexpr int kOOB = 0x7ffffff0;         // byte offset past the end of every buffer
@@ -362,45 +363,68 @@ hipError_t launch_halo_f32(const HaloArgs &a, int cfg, int tiles, int ci_tiles, 
     }
 }
 
-// Weight image: one thread per float of wk, in order
-// [ci_tile][phase][chunk][tap][cp][ci][2], zero where ci >= Ci or co >= Co.
+// Weight image [ci_tile][phase][chunk][tap][cp][ci][2], zero where ci >= Ci
+// or co >= Co.  One work-group per (chunk, ci tile): it stages the slab
+// weight[chunk*8 .. +8][ci tile][kH][kW] in LDS with coalesced reads (for a
+// fixed output channel the (ci, kh, kw) run is contiguous) and writes every
+// phase's block of that chunk contiguously.
 __global__ __launch_bounds__(256) void weight_image_f32(const float *__restrict__ w,
                                                         float *__restrict__ wk, const HaloArgs A,
-                                                        int kH, int kW, int64_t total) {
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
-         i += (int64_t)gridDim.x * 256) {
-        const int ct = (int)(i / A.w_ci_stride);
-        const int e = (int)(i - (int64_t)ct * A.w_ci_stride);
-        int p = 0;
-        for (int k = 1; k < A.nphases; ++k)
-            if (e >= A.ph[k].woff) p = k;
+                                                        int kH, int kW) {
+    extern __shared__ float slab[];  // [8 co][64 ci][kH*kW]
+    const int chunk = blockIdx.x, ct = blockIdx.y;
+    const int kHW = kH * kW;
+    const int run = kHalo64 * kHW;
+    const int ci_rows = min(kHaloCT, A.Ci - ct * kHaloCT);
+    const int nload = kHaloBC * run;
+    for (int e0 = 0; e0 < nload; e0 += 256 * 16) {
+        float v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int e = e0 + u * 256 + threadIdx.x;
+            const int c = e / run, r = e - (e / run) * run;
+            const int co = chunk * kHaloBC + c;
+            v[u] = (e < nload && co < A.Co && r < ci_rows * kHW)
+                       ? w[((int64_t)co * A.Ci + (int64_t)ct * kHaloCT) * kHW + r]
+                       : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int e = e0 + u * 256 + threadIdx.x;
+            if (e < nload) slab[e] = v[u];
+        }
+    }
+    __syncthreads();
+    for (int p = 0; p < A.nphases; ++p) {
         const HaloPhase &P = A.ph[p];
         const int T = P.J_h * P.J_w;
-        int r = e - P.woff;
-        const int chunk = r / (T * 512);
-        r -= chunk * T * 512;
-        const int tap = r / 512;
-        r -= tap * 512;
-        const int cp = r / 128;
-        r -= cp * 128;
-        const int ci = ct * kHaloCT + r / 2;
-        const int co = chunk * kHaloBC + 2 * cp + (r & 1);
-        float v = 0.f;
-        if (ci < A.Ci && co < A.Co) {
+        // float4 f4 -> (tap, co pair cp, ci pair): ci 2q and 2q+1, channels 2cp, 2cp+1.
+        v4f *out = (v4f *)(wk + (int64_t)ct * A.w_ci_stride + P.woff + (int64_t)chunk * T * 512);
+        for (int f4 = threadIdx.x; f4 < T * 128; f4 += 256) {
+            const int tap = f4 >> 7, cp = (f4 >> 5) & 3, q = f4 & 31;
             const int j = tap / P.J_w, jw = tap - (tap / P.J_w) * P.J_w;
-            const int kh = P.r_h + A.stride * j, kw = P.r_w + A.stride * jw;
-            v = w[(((int64_t)co * A.Ci + ci) * kH + kh) * kW + kw];
+            const int t = (P.r_h + A.stride * j) * kW + P.r_w + A.stride * jw;
+            const float *s0 = slab + (2 * cp) * run + (2 * q) * kHW + t;
+            out[f4] = v4f{s0[0], s0[run], s0[kHW], s0[run + kHW]};
         }
-        wk[i] = v;
     }
+}
+
+size_t weight_image_f32_lds(int kH, int kW) {
+    return (size_t)kHaloBC * kHalo64 * kH * kW * sizeof(float);
 }
 
 hipError_t launch_weight_image_f32(const float *w, float *wk, const HaloArgs &a, int kH, int kW,
                                    int ci_tiles, int64_t total, hipStream_t s) {
-    (void)ci_tiles;
-    int64_t b = (total + 255) / 256;
-    const int blocks = (int)(b < 8192 ? (b > 0 ? b : 1) : 8192);
-    hipLaunchKernelGGL(weight_image_f32, dim3(blocks), dim3(256), 0, s, w, wk, a, kH, kW, total);
+    (void)total;
+    const size_t lds = weight_image_f32_lds(kH, kW);
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute((const void *)weight_image_f32,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(weight_image_f32, dim3(a.nchunks, ci_tiles), dim3(256), lds, s, w, wk, a,
+                       kH, kW);
     return hipGetLastError();
 }
 

@@ -1,0 +1,273 @@
+// kernels_stem_f32.hip -- fp32 implicit-GEMM kernel for few input channels
+// (Ci <= 4, e.g. an RGB stem) on gfx950.
+//
+// The contraction is the implicit GEMM of meganeura conv2d_grad_input_gemm.wgsl
+// (header comment: C[Ci, pixels] = A[Ci, K] x B[K, pixels], K = Co*kH*kW),
+// taken one residue class of the stride at a time (see gi_common.h).  With
+// Ci <= 4 the wide matrix-core shapes would be mostly padding, so the kernel
+// uses V_MFMA_F32_4X4X1_16B_F32: 16 independent 4x4x1 blocks per instruction.
+// Block b of an instruction has rows = the 4 input channels (A, the weights)
+// and columns = 4 pixels (B, grad_out); lane l supplies A[b][l%4] and B[b][l%4]
+// with b = l/4, and receives D[b][r][l%4] in register r.  So lane l's column
+// is pixel l of the wave's 64-pixel block, and after the contraction lane l
+// holds input channels 0..3 of its own pixel.
+//
+// Work-group: 128 threads = 2 waves over a 16 x 16 tile of one phase grid;
+// wave w owns tile rows 8w .. 8w+7 as two 4 x 16 pixel blocks.  Output
+// channels are streamed 4 at a time: the tile's grad_out halo for the 4
+// channels is copied into LDS by direct global -> LDS loads (a position's 4
+// channels are one 16-byte word, so one LDS read serves 4 MFMAs), double-
+// buffered; the A fragments of every tap of the chunk come straight from a
+// weight image into registers, the next chunk's loaded while this one runs.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gi_common.h"
+#include "gi_launch.h"
+
+namespace gi {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+namespace {
+
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9)
+constexpr int kOOB = 0x7ffffff0;         // byte offset past the end of every buffer
+constexpr int kStemTile = 16;            // tile side in phase-grid pixels
+constexpr int kStemGroups = 16;          // halo groups of 16 positions per wave (<= 512)
+
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (long)bytes, kRsrcWord3);
+}
+
+// One phase with T taps (compile time) for this work-group's tile.
+template <int T>
+__device__ __forceinline__ void stem_phase(const StemArgs &A, const StemPhase &P, v4f *sm4,
+                                           v4f (&acc)[2], int n, int a0, int b0,
+                                           __amdgpu_buffer_rsrc_t grs,
+                                           __amdgpu_buffer_rsrc_t wrs) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int HC = kStemTile + P.J_w - 1;
+    const int HR = kStemTile + P.J_h - 1;
+    const int hpos = HR * HC;
+    const int groups = (hpos + 15) / 16;
+    const int oHW = A.oH * A.oW;
+
+    // Halo DMA: group q = wave + 2k covers positions 16q .. 16q+15; lane ->
+    // (position 16q + lane/4, channel lane%4).
+    int goff[kStemGroups];
+#pragma unroll
+    for (int k = 0; k < kStemGroups; ++k) {
+        const int q = wave + 2 * k;
+        const int pos = q * 16 + (lane >> 2);
+        const int hr = pos / HC, hc = pos - (pos / HC) * HC;
+        const int oh = a0 + P.q_h - (P.J_h - 1) + hr;
+        const int ow = b0 + P.q_w - (P.J_w - 1) + hc;
+        const bool v = q < groups && pos < hpos && oh >= 0 && oh < A.oH && ow >= 0 && ow < A.oW;
+        goff[k] = v ? ((n * A.Co) * oHW + oh * A.oW + ow) * 4 : kOOB;
+    }
+    const int co_l = lane & 3;
+    auto issue = [&](int chunk, int buf) {
+#pragma unroll
+        for (int k = 0; k < kStemGroups; ++k) {
+            const int q = wave + 2 * k;
+            if (q < groups) {
+                const int co = chunk * 4 + co_l;
+                const int off = (goff[k] != kOOB && co < A.Co) ? goff[k] + co * oHW * 4 : kOOB;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    grs, (lds_ptr_t)(sm4 + buf * A.HPmax + q * 16), 4, off, 0, 0, 0);
+            }
+        }
+    };
+    // A fragment of (chunk, tap): the 4 output channels of input channel lane%4.
+    const int wl = (P.woff * 4 + (lane & 3)) * 16;
+    auto aload = [&](int chunk, int t) {
+        const int off = wl + ((chunk * T + t) * 4) * 16;
+        return __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(wrs, off, 0, 0));
+    };
+
+    // Halo position of this lane's pixel in each block, and tap shifts.
+    const int r = lane >> 4, c = lane & 15;
+    int pb[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) pb[blk] = (8 * wave + 4 * blk + r) * HC + c;
+    int shift[T];
+    {
+        int j = 0, jw = 0;
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            shift[t] = (P.J_h - 1 - j) * HC + (P.J_w - 1 - jw);
+            if (++jw == P.J_w) {
+                jw = 0;
+                ++j;
+            }
+        }
+    }
+
+    v4f af[2][T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) af[0][t] = aload(0, t);
+    issue(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+
+    auto body = [&](int chunk, v4f(&cur_a)[T], v4f(&next_a)[T]) {
+        const int cur = chunk & 1;
+        if (chunk + 1 < A.nchunks) {
+            issue(chunk + 1, cur ^ 1);
+#pragma unroll
+            for (int t = 0; t < T; ++t) next_a[t] = aload(chunk + 1, t);
+        }
+        const v4f *hs = sm4 + cur * A.HPmax;
+        int pp[2];
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            pp[blk] = pb[blk];
+            asm volatile("" : "+v"(pp[blk]));
+        }
+        // B fragments two taps ahead (three slots).
+        v4f fb[3][2];
+        auto bfetch = [&](int t, int sl) {
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk) fb[sl][blk] = hs[pp[blk] + shift[t]];
+        };
+        bfetch(0, 0);
+        if (T > 1) bfetch(1, 1);
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            if (t + 2 < T) bfetch(t + 2, (t + 2) % 3);
+            const int sl = t % 3;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int blk = 0; blk < 2; ++blk)
+                    acc[blk] = __builtin_amdgcn_mfma_f32_4x4x1f32(cur_a[t][e], fb[sl][blk][e],
+                                                                  acc[blk], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    };
+    for (int chunk = 0; chunk < A.nchunks; chunk += 2) {
+        body(chunk, af[0], af[1]);
+        if (chunk + 1 < A.nchunks) body(chunk + 1, af[1], af[0]);
+    }
+}
+
+__global__ __launch_bounds__(128, 2) void gi_stem_f32(const StemArgs A) {
+    extern __shared__ __attribute__((aligned(16))) v4f sm4[];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    int bid = blockIdx.x;
+    const int p = bid % A.nphases;
+    bid /= A.nphases;
+    const int tc = bid % A.tiles_c;
+    bid /= A.tiles_c;
+    const int tr = bid % A.tiles_r;
+    const int n = bid / A.tiles_r;
+    const StemPhase P = A.ph[p];
+    const int T = P.J_h * P.J_w;
+    const int a0 = tr * kStemTile, b0 = tc * kStemTile;
+    const __amdgpu_buffer_rsrc_t grs = make_rsrc(A.grad_out, A.g_bytes);
+    const __amdgpu_buffer_rsrc_t wrs = make_rsrc(A.wk, A.w_bytes);
+    const __amdgpu_buffer_rsrc_t drs = make_rsrc(A.dst, A.d_bytes);
+
+    v4f acc[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+#define GI_STEM_CASE(TT)                                                        \
+    case TT:                                                                    \
+        stem_phase<TT>(A, P, sm4, acc, n, a0, b0, grs, wrs);                    \
+        break;
+    switch (T) {
+        GI_STEM_CASE(1)
+        GI_STEM_CASE(2)
+        GI_STEM_CASE(3)
+        GI_STEM_CASE(4)
+        GI_STEM_CASE(6)
+        GI_STEM_CASE(8)
+        GI_STEM_CASE(9)
+        GI_STEM_CASE(12)
+        GI_STEM_CASE(16)
+        default: break;  // no taps: the phase's pixels are zero
+    }
+#undef GI_STEM_CASE
+
+    // Epilogue: lane l holds input channels 0..3 of pixel l of each block.
+    const int plane = A.H * A.W;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+        const int a = a0 + 8 * wave + 4 * blk + (lane >> 4);
+        const int b = b0 + (lane & 15);
+        const bool pv = a < P.Ha && b < P.Wb;
+        const int pix = (P.rho_h + A.stride * a) * A.W + P.rho_w + A.stride * b;
+#pragma unroll
+        for (int ci = 0; ci < 4; ++ci) {
+            const int off = (pv && ci < A.Ci) ? ((n * A.Ci + ci) * plane + pix) * 4 : kOOB;
+            const float v = acc[blk][ci];
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), drs, off, 0, 0);
+        }
+    }
+}
+
+// Weight image: one thread per float4 wk[phase][chunk][tap][ci] holding the
+// 4 output channels chunk*4 .. +3 (zero past Ci or Co).
+__global__ __launch_bounds__(256) void weight_stem_f32(const float *__restrict__ w,
+                                                       float *__restrict__ wk,
+                                                       const StemArgs A, int kH, int kW,
+                                                       int total4) {
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < total4; i += gridDim.x * 256) {
+        int p = 0;
+        for (int k = 1; k < A.nphases; ++k)
+            if (i >= A.ph[k].woff * 4) p = k;
+        const StemPhase &P = A.ph[p];
+        const int T = P.J_h * P.J_w;
+        int r = i - P.woff * 4;
+        const int ci = r & 3;
+        r >>= 2;
+        const int t = r % T;
+        const int chunk = r / T;
+        const int j = t / P.J_w, jw = t - (t / P.J_w) * P.J_w;
+        const int kh = P.r_h + A.stride * j, kw = P.r_w + A.stride * jw;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int co = chunk * 4 + e;
+            v[e] = (ci < A.Ci && co < A.Co) ? w[(((int64_t)co * A.Ci + ci) * kH + kh) * kW + kw]
+                                            : 0.f;
+        }
+        ((v4f *)wk)[i] = v4f{v[0], v[1], v[2], v[3]};
+    }
+}
+
+}  // namespace
+
+bool stem_f32_taps_ok(int taps) {
+    switch (taps) {
+        case 0: case 1: case 2: case 3: case 4: case 6: case 8: case 9: case 12: case 16:
+            return true;
+        default:
+            return false;
+    }
+}
+
+hipError_t launch_stem_f32(const StemArgs &a, hipStream_t s) {
+    const size_t lds = (size_t)2 * a.HPmax * sizeof(v4f);
+    const int64_t wgs = (int64_t)a.N * a.tiles_r * a.tiles_c * a.nphases;
+    hipLaunchKernelGGL(gi_stem_f32, dim3((unsigned)wgs), dim3(128), lds, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_weight_stem_f32(const float *w, float *wk, const StemArgs &a, int kH, int kW,
+                                  hipStream_t s) {
+    int total4 = 0;
+    for (int p = 0; p < a.nphases; ++p)
+        total4 += a.nchunks * a.ph[p].J_h * a.ph[p].J_w * 4;
+    const int blocks = total4 > 0 ? (total4 + 255) / 256 : 1;
+    hipLaunchKernelGGL(weight_stem_f32, dim3(blocks < 4096 ? blocks : 4096), dim3(256), 0, s, w,
+                       wk, a, kH, kW, total4);
+    return hipGetLastError();
+}
+
+}  // namespace gi

@@ -103,9 +103,12 @@ enum {
 enum {
     CONV2D_GI_VARIANT_AUTO = 0,    /* the planner chooses                      */
     CONV2D_GI_VARIANT_GENERIC = 1, /* any shape: phase split, gathered B tile  */
-    CONV2D_GI_VARIANT_HALO = 2     /* fp32, Ci >= 16: grad_out halo tile in LDS,
-                                      every tap a shifted view of it; shapes it
-                                      cannot hold in LDS fall back to GENERIC  */
+    CONV2D_GI_VARIANT_HALO = 2,    /* Ci >= 16 (bf16: stride 1): grad_out halo
+                                      tile in LDS, every tap a shifted view of
+                                      it; other shapes fall back to GENERIC    */
+    CONV2D_GI_VARIANT_STEM = 3     /* fp32, Ci <= 4: 4x4 matrix-core blocks with
+                                      the input channels on one side; other
+                                      shapes fall back to GENERIC              */
 };
 
 /*

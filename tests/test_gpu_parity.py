@@ -178,6 +178,29 @@ def test_forced_halo_bf16(idx):
     full_parity(s, 1500 + idx, "bf16", gi.VARIANT_HALO, dist="normal")
 
 
+STEM_SHAPES = [
+    workloads.Shape(2, 3, 45, 44, 64, 7, 7, 2, 3, 3),      # stem-like, ragged tiles
+    workloads.Shape(1, 4, 20, 19, 7, 3, 3, 1, 1, 1),       # Ci = 4, Co not a multiple of 4
+    workloads.Shape(3, 1, 17, 33, 9, 4, 4, 1, 1, 2),       # 4x4 stride 1 (16 taps), Ci = 1
+    workloads.Shape(1, 2, 12, 18, 5, 2, 4, 1, 0, 1),       # 2x4 (8 taps)
+    workloads.Shape(2, 3, 9, 40, 6, 1, 3, 1, 0, 1),        # 1x3
+    workloads.Shape(1, 3, 23, 21, 10, 3, 3, 2, 1, 1),      # stride 2, odd sizes
+    workloads.Shape(1, 3, 30, 30, 13, 5, 5, 2, 2, 2),      # 5x5 stride 2: 9, 6, 6, 4 taps
+    workloads.Shape(2, 2, 11, 10, 3, 2, 2, 3, 0, 0),       # kernel < stride: empty phases
+    workloads.Shape(1, 3, 40, 36, 64, 7, 7, 2, 3, 3),      # several tiles per phase
+]
+
+
+@pytest.mark.parametrize("idx", range(len(STEM_SHAPES)))
+def test_forced_stem(idx):
+    s = STEM_SHAPES[idx]
+    gi.set_variant(gi.VARIANT_STEM)
+    desc = gi.plan(gi.make_params(*s.as_tuple()[:10]), False)
+    gi.set_variant(gi.VARIANT_AUTO)
+    assert "variant=stem" in desc, desc
+    full_parity(s, 1900 + idx, "f32", gi.VARIANT_STEM, dist="normal")
+
+
 # (shape, nb, tile_rows, tile_cols): tiles with ragged row and column tails,
 # tiles wider than the image, rows folded across images, strided phases.
 FORCED_TILES = [
