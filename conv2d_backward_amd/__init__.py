@@ -77,7 +77,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.conv2d_gi_set_variant.restype = ctypes.c_int
     lib.conv2d_gi_plan.argtypes = [PP, ctypes.c_int, ctypes.c_char_p, ctypes.c_size_t]
     lib.conv2d_gi_plan.restype = ctypes.c_int
-    lib.conv2d_gi_set_halo_tile.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    lib.conv2d_gi_set_halo_tile.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]
     lib.conv2d_gi_set_halo_tile.restype = ctypes.c_int
     lib.conv2d_gi_set_profile_events.argtypes = [P, P]
     lib.conv2d_gi_set_profile_events.restype = None
@@ -136,9 +136,11 @@ def set_variant(variant: int) -> int:
     return old
 
 
-def set_halo_tile(nb: int = 0, tile_rows: int = 0, tile_cols: int = 0):
-    """Force the HALO variant's pixel tile (test hook); set_halo_tile() restores the planner."""
-    _check(load_library().conv2d_gi_set_halo_tile(int(nb), int(tile_rows), int(tile_cols)))
+def set_halo_tile(nb: int = 0, tile_rows: int = 0, tile_cols: int = 0, stages: int = 0):
+    """Force the fp32 HALO variant's pixel tile and pipeline depth (test hook);
+    set_halo_tile() restores the planner."""
+    _check(load_library().conv2d_gi_set_halo_tile(int(nb), int(tile_rows), int(tile_cols),
+                                                  int(stages)))
 
 
 def release_workspaces():

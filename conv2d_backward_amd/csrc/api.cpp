@@ -26,7 +26,7 @@ using gi::Phase;
 
 std::atomic<int> g_variant{CONV2D_GI_VARIANT_AUTO};
 // Forced halo tile (test hook): NB pixel blocks, TR x TC phase-grid pixels; 0 = planner.
-std::atomic<int> g_tile_nb{0}, g_tile_tr{0}, g_tile_tc{0};
+std::atomic<int> g_tile_nb{0}, g_tile_tr{0}, g_tile_tc{0}, g_tile_stages{0};
 thread_local char g_last_hip[256] = "";
 thread_local hipEvent_t g_prof_begin = nullptr, g_prof_end = nullptr;
 
@@ -219,19 +219,43 @@ bool plan_halo(const conv2d_gi_params &p, const std::vector<Phase> &phases, Halo
                 const int cfg = gi::halo_f32_config(nb, tmask, bl);
                 if (cfg < 0) continue;
                 const int HPc = round_to_residue(groups * 32, 32, 16);
-                const size_t lds = gi::halo_f32_lds_bytes(maxT, HPc);
+                const int cps = gi::halo_f32_cps(cfg);
+                // Three pipeline stages when two work-groups still fit a CU, or
+                // when one work-group per CU is all that fits anyway.
+                int stages = 3;
+                size_t lds = gi::halo_f32_lds_bytes(maxT, HPc, 3, cps);
+                if (lds > kLdsBytes / 2) {
+                    stages = 2;
+                    lds = gi::halo_f32_lds_bytes(maxT, HPc, 2, cps);
+                    if (lds > kLdsBytes / 2 &&
+                        gi::halo_f32_lds_bytes(maxT, HPc, 3, cps) <= kLdsBytes) {
+                        stages = 3;
+                        lds = gi::halo_f32_lds_bytes(maxT, HPc, 3, cps);
+                    }
+                }
+                if (forced && g_tile_stages.load() > 0) {
+                    stages = g_tile_stages.load();
+                    lds = gi::halo_f32_lds_bytes(maxT, HPc, stages, cps);
+                }
                 if (lds > kLdsBytes) continue;
                 const int64_t row_tiles = (rows_total + TR - 1) / TR;
                 const int64_t col_tiles = (maxWb + TC - 1) / TC;
                 const int64_t tiles = row_tiles * col_tiles * (fold ? 1 : p.N);
                 if (tiles > INT32_MAX) continue;
                 const int64_t wgs = tiles * ci_tiles;
-                const double rounds = (double)((wgs + kCUs - 1) / kCUs);
+                // Busiest CU: ceil(work-groups / CUs) work-groups.  Measured
+                // efficiency of the instantiations: more pixel blocks per wave
+                // amortise more per-tap and per-chunk overhead, and a lone
+                // work-group per CU hides less latency.
+                const int64_t per_cu = (wgs + kCUs - 1) / kCUs;
+                const double eff_nb = nb >= 13 ? 1.0 : nb >= 8 ? 0.85 : 0.75;
+                const double eff_occ = per_cu >= 2 ? 1.0 : 0.9;
                 // 16x16x4 MFMA: 32 cycles per 16 pixels x 4 k; plus halo staging.
                 const double per_wg = 8.0 * nb * kall +
                                       (double)nchunks * phases.size() * HR * HC * 2.0 + 4000.0;
                 // Among equal critical paths, fewer work-groups do less total work.
-                const double cost = rounds * per_wg + 0.05 * (double)wgs * per_wg / kCUs;
+                const double cost = (double)per_cu * per_wg / (eff_nb * eff_occ) +
+                                    0.05 * (double)wgs * per_wg / kCUs;
                 if (!found || cost < out.cost) {
                     found = true;
                     out = HaloPlan{};
@@ -248,6 +272,7 @@ bool plan_halo(const conv2d_gi_params &p, const std::vector<Phase> &phases, Halo
                     a.row_tiles = (int)row_tiles;
                     a.col_tiles = (int)col_tiles;
                     a.HPc = HPc;
+                    a.stages = stages;
                 }
             }
         }
@@ -618,7 +643,7 @@ std::string describe(const Plan &plan, bool bf16) {
              " bl=" + std::to_string(h.bl) + " tile=" + std::to_string(a.TR) + "x" +
              std::to_string(a.TC) + (a.fold ? " fold" : "") + " wgs=" + std::to_string(h.tiles) +
              "x" + std::to_string(h.ci_tiles) + " lds=" + std::to_string(h.lds) +
-             " HPc=" + std::to_string(a.HPc);
+             " HPc=" + std::to_string(a.HPc) + " stages=" + std::to_string(a.stages);
         for (int i = 0; i < a.nphases; ++i) {
             const gi::HaloPhase &ph = a.ph[i];
             s += " phase(" + std::to_string(ph.rho_h) + "," + std::to_string(ph.rho_w) +
@@ -686,18 +711,20 @@ int conv2d_gi_plan(const conv2d_gi_params *p, int dtype_bf16, char *buf, size_t 
     return CONV2D_GI_OK;
 }
 
-int conv2d_gi_set_halo_tile(int nb, int tile_rows, int tile_cols) {
+int conv2d_gi_set_halo_tile(int nb, int tile_rows, int tile_cols, int stages) {
     if (nb == 0) {
         g_tile_nb = 0;
         g_tile_tr = 0;
         g_tile_tc = 0;
+        g_tile_stages = 0;
         return CONV2D_GI_OK;
     }
     if ((nb != 4 && nb != 8 && nb != 13) || tile_rows < 1 || tile_cols < 1 ||
-        tile_rows * tile_cols > nb * 16)
+        tile_rows * tile_cols > nb * 16 || stages < 0 || stages == 1 || stages > 3)
         return CONV2D_GI_EINVAL;
     g_tile_tr = tile_rows;
     g_tile_tc = tile_cols;
+    g_tile_stages = stages;
     g_tile_nb = nb;
     return CONV2D_GI_OK;
 }

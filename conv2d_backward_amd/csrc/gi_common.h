@@ -78,7 +78,7 @@ struct HaloArgs {
     int32_t fold;           // 1: tile rows run across images (every phase has J_h <= 1)
     int32_t nchunks;        // ceil(Co / 8)
     int32_t HPc;            // LDS pitch of one co pair's halo, in float2
-    int32_t pad1_;
+    int32_t stages;         // LDS stages of the chunk pipeline (2 or 3)
     int32_t maxT;           // most taps of any phase
     int32_t w_ci_stride;    // floats of the weight image per ci tile
     int32_t pad_;

@@ -36,8 +36,11 @@ unsigned halo_f32_tbit(int T);
 int halo_f32_config(int nb, unsigned tmask, int hg);
 hipError_t launch_halo_f32(const HaloArgs &a, int cfg, int tiles, int ci_tiles, size_t lds,
                            hipStream_t s);
-// LDS bytes of the halo kernel: most taps of a phase, halo pitch (float2).
-size_t halo_f32_lds_bytes(int maxT, int HPc);
+// Chunks of 8 output channels per LDS stage of instantiation cfg, and the LDS
+// bytes of the halo kernel: most taps of a phase, halo pitch (float2),
+// pipeline stages, chunks per stage.
+int halo_f32_cps(int cfg);
+size_t halo_f32_lds_bytes(int maxT, int HPc, int stages, int cps);
 
 // Weight image of the halo kernel (layout in gi_common.h); `total` floats.
 // Needs weight_image_f32_lds(kH, kW) bytes of LDS per work-group.

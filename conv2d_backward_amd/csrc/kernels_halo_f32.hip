@@ -93,21 +93,27 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, void *dst, int vo
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void *dst, int voff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)dst, 16, voff, 0, 0, 0);
 }
-__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N direct loads of this wave are outstanding (loads
+// complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_dma() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 // All chunks of one phase with T = J_h * J_w taps (compile time) for this
 // work-group's tile; accumulates into acc.  Every thread of the work-group
-// calls it (it contains barriers).  HG = halo position groups of 32 staged
-// per wave.
+// calls it (it contains barriers).  HG = halo groups of 32 positions staged
+// per wave; CPS = chunks of 8 output channels per LDS stage (several for
+// phases with few taps, so a barrier covers enough work).
 //
-// LDS stage (float2 units): weights [maxT][4 co pairs][64 ci], then halo
-// [4 co pairs][HPc positions]; both written by direct loads:
-//   * weights: the chunk's block of the weight image is T * 2 KB, copied in
-//     1 KB pieces (16 bytes per lane);
+// LDS stage (float2 units): weights [CPS][maxT][4 co pairs][64 ci], then
+// halos [CPS][4 co pairs][HPc positions]; both written by direct loads:
+//   * weights: the stage's chunks are consecutive blocks of the weight image,
+//     T * 2 KB each, copied in 1 KB pieces (16 bytes per lane);
 //   * halo: for co pair cp and a group of 32 positions, even lanes load
 //     output channel 2cp and odd lanes 2cp+1 of position base + lane/2, which
 //     lands exactly on the float2 layout.
-template <int T, int NB, int HG>
+template <int T, int NB, int HG, int CPS>
 __device__ __forceinline__ void run_phase(const HaloArgs &A, const HaloPhase &P, v2f *smem2,
                                           const int (&pbase)[NB], v4f (&acc)[NB], int a0,
                                           int b0, int n_img, int ci_tile,
@@ -117,13 +123,14 @@ __device__ __forceinline__ void run_phase(const HaloArgs &A, const HaloPhase &P,
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, g4 = lane >> 4;
-    const int as_f2 = A.maxT * 4 * 64;
-    const int stage_f2 = as_f2 + 4 * A.HPc;
+    const int wreg = CPS * A.maxT * 256;
+    const int stage_f2 = wreg + CPS * 4 * A.HPc;
     const int HC = A.TC + P.J_w - 1;
     const int HR = A.TR + P.J_h - 1;
     const int hpos = HR * HC;
     const int groups = (hpos + 31) / 32;
     const int oHW = A.oH * A.oW;
+    const int nstages = (A.nchunks + CPS - 1) / CPS;
 
     // Halo shift of every tap (j, jw): (J_h-1-j) rows and (J_w-1-jw) columns.
     int shift[T];
@@ -164,67 +171,110 @@ __device__ __forceinline__ void run_phase(const HaloArgs &A, const HaloPhase &P,
     const int wbyte0 = (ci_tile * A.w_ci_stride + P.woff) * 4;
     const int co_lane = lane & 1;
 
-    auto issue = [&](int chunk, int buf) {
+    // Every wave issues the same fixed number of direct loads per stage (the
+    // surplus ones read past the end of their buffer, i.e. zeros, into a
+    // scratch kilobyte of LDS nobody reads), so "this stage's loads are done"
+    // is a wait on a compile-time count.
+    constexpr int WPW = (2 * T * CPS + 3) / 4;  // 1 KB weight pieces per wave
+    constexpr int NDMA = WPW + 4 * HG * CPS;     // direct loads per wave per stage
+    static_assert(NDMA <= 63, "vmcnt holds at most 63");
+    v2f *const dummy = smem2 + A.stages * stage_f2;
+    auto issue = [&](int stg, int buf) {
         v2f *st = smem2 + buf * stage_f2;
-        const int wb = wbyte0 + chunk * (T * 2048) + lane * 16;
-        for (int m = wave; m < 2 * T; m += 4) dma16(wrs, st + m * 128, wb + m * 1024);
-        v2f *hs = st + as_f2;
+        const int wb = wbyte0 + stg * (CPS * T * 2048) + lane * 16;
+#pragma unroll
+        for (int i = 0; i < WPW; ++i) {
+            const int m = wave + 4 * i;
+            const bool real = m < 2 * T * CPS && stg * CPS + m / (2 * T) < A.nchunks;
+            dma16(wrs, real ? st + m * 128 : dummy, real ? wb + m * 1024 : kOOB);
+        }
+        v2f *hs = st + wreg;
+        // Opaque copies: the offsets below are formed at each issue (a few
+        // VALU ops per load) rather than strength-reduced into one register
+        // per load held across the whole loop.
+        int ho[HG];
 #pragma unroll
         for (int k = 0; k < HG; ++k) {
-            const int g = wave + 4 * k;
-            if (g < groups) {
+            ho[k] = hoff[k];
+            asm volatile("" : "+v"(ho[k]));
+        }
+#pragma unroll
+        for (int o = 0; o < CPS; ++o) {
+#pragma unroll
+            for (int k = 0; k < HG; ++k) {
+                const int g = wave + 4 * k;
+                const bool real = g < groups;
 #pragma unroll
                 for (int cp = 0; cp < 4; ++cp) {
-                    const int co = chunk * kHaloBC + 2 * cp + co_lane;
+                    const int co = (stg * CPS + o) * kHaloBC + 2 * cp + co_lane;
                     const int off =
-                        (hoff[k] != kOOB && co < A.Co) ? hoff[k] + co * oHW * 4 : kOOB;
-                    dma4(grs, hs + cp * A.HPc + g * 32, off);
+                        (real && ho[k] != kOOB && co < A.Co) ? ho[k] + co * oHW * 4 : kOOB;
+                    dma4(grs, real ? hs + (o * 4 + cp) * A.HPc + g * 32 : dummy, off);
                 }
             }
         }
     };
 
+    // Stage pipeline: with 3 LDS stages, stage s+2 is in flight while stage s
+    // is multiplied (with 2, stage s+1).
+    const int D = A.stages - 1;
+    wait_dma<0>();  // the previous phase's stores count too: drain them first
     issue(0, 0);
-    wait_dma();
+    if (D == 2 && nstages > 1) {
+        issue(1, 1);
+        wait_dma<NDMA>();
+    } else {
+        wait_dma<0>();
+    }
     __syncthreads();
-    for (int chunk = 0; chunk < A.nchunks; ++chunk) {
-        const int cur = chunk & 1;
-        if (chunk + 1 < A.nchunks) issue(chunk + 1, cur ^ 1);
-        const v2f *as = smem2 + cur * stage_f2 + g4 * 64 + wave * 16 + l16;
-        const v2f *hs = smem2 + cur * stage_f2 + as_f2 + g4 * A.HPc;
-        // Two fragment slots: tap t+1 is read from LDS while tap t's MFMAs
-        // run; the schedule interleaves one read with every two MFMAs.
-        v2f fa[2], fb[2][NB];
-        auto fetch = [&](int t, int slot) {
-            fa[slot] = as[t * 4 * 64];
+    for (int stg = 0; stg < nstages; ++stg) {
+        const int cur = stg % A.stages;
+        const bool ahead = stg + D < nstages;
+        if (ahead) issue(stg + D, (stg + D) % A.stages);
 #pragma unroll
-            for (int blk = 0; blk < NB; ++blk) fb[slot][blk] = hs[pbase[blk] + shift[t]];
-        };
-        fetch(0, 0);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int o = 0; o < CPS; ++o) {
+            if (CPS > 1 && stg * CPS + o >= A.nchunks) break;
+            const v2f *as =
+                smem2 + cur * stage_f2 + o * T * 256 + g4 * 64 + wave * 16 + l16;
+            const v2f *hs = smem2 + cur * stage_f2 + wreg + (o * 4 + g4) * A.HPc;
+            // Two fragment slots: tap t+1 is read from LDS while tap t's MFMAs
+            // run.
+            v2f fa[2], fb[2][NB];
+            auto fetch = [&](int t, int slot) {
+                fa[slot] = as[t * 4 * 64];
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
-            const int slot = t & 1;
-            if (t + 1 < T) fetch(t + 1, slot ^ 1);
-#pragma unroll
-            for (int blk = 0; blk < NB; ++blk)
-                acc[blk] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[slot].x, fb[slot][blk].x,
-                                                                acc[blk], 0, 0, 0);
-#pragma unroll
-            for (int blk = 0; blk < NB; ++blk)
-                acc[blk] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[slot].y, fb[slot][blk].y,
-                                                                acc[blk], 0, 0, 0);
-            // Keep taps in order: nothing moves across a tap boundary.
+                for (int blk = 0; blk < NB; ++blk) fb[slot][blk] = hs[pbase[blk] + shift[t]];
+            };
+            fetch(0, 0);
             __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                const int slot = t & 1;
+                if (t + 1 < T) fetch(t + 1, slot ^ 1);
+#pragma unroll
+                for (int blk = 0; blk < NB; ++blk)
+                    acc[blk] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[slot].x, fb[slot][blk].x,
+                                                                    acc[blk], 0, 0, 0);
+#pragma unroll
+                for (int blk = 0; blk < NB; ++blk)
+                    acc[blk] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[slot].y, fb[slot][blk].y,
+                                                                    acc[blk], 0, 0, 0);
+                // Keep taps in order: nothing moves across a tap boundary.
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
-
-        wait_dma();
+        // Stage s+1 must have landed: with 3 stages the loads of stage s+2
+        // (issued this iteration) may still be in flight.
+        if (D == 2 && ahead)
+            wait_dma<NDMA>();
+        else
+            wait_dma<0>();
         __syncthreads();
     }
 }
 
-template <int NB, int HG, unsigned TMASK>
-__global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void gi_halo_f32(
+template <int NB, int HG, unsigned TMASK, int CPS, int OCC>
+__global__ __launch_bounds__(256, OCC) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void gi_halo_f32(
     const HaloArgs A) {
     extern __shared__ __attribute__((aligned(16))) v2f smem2[];
 
@@ -275,7 +325,7 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 #define GI_HALO_CASE(TT)                                                                     \
     case TT:                                                                                 \
         if constexpr ((TMASK & tbit(TT)) != 0)                                               \
-            run_phase<TT, NB, HG>(A, P, smem2, pbase, acc, a0, b0, n_img, ci_tile, grs, wrs); \
+            run_phase<TT, NB, HG, CPS>(A, P, smem2, pbase, acc, a0, b0, n_img, ci_tile, grs, wrs); \
         break;
         switch (T) {
             GI_HALO_CASE(1)
@@ -313,27 +363,30 @@ constexpr unsigned kT7 = tbit(7);
 constexpr unsigned kTs2 = tbit(1) | tbit(2) | tbit(4);
 constexpr unsigned kTall = tbit(1) | tbit(2) | tbit(3) | tbit(4) | tbit(6) | tbit(7) | tbit(9);
 
-template <int NB, int HG, unsigned TMASK>
+template <int NB, int HG, unsigned TMASK, int CPS, int OCC>
 hipError_t launch_one(const HaloArgs &a, int tiles, int ci_tiles, size_t lds, hipStream_t s) {
     if (lds > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute((const void *)gi_halo_f32<NB, HG, TMASK>,
+        hipError_t e = hipFuncSetAttribute((const void *)gi_halo_f32<NB, HG, TMASK, CPS, OCC>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((gi_halo_f32<NB, HG, TMASK>), dim3(tiles, ci_tiles), dim3(256), lds, s,
-                       a);
+    hipLaunchKernelGGL((gi_halo_f32<NB, HG, TMASK, CPS, OCC>), dim3(tiles, ci_tiles), dim3(256),
+                       lds, s, a);
     return hipGetLastError();
 }
 
 // Instantiations: pixel blocks, halo groups of 32 positions per wave, tap
-// counts served.
+// counts served, chunks of 8 output channels per LDS stage (the 4-chunk
+// kernel holds one work-group per CU by LDS, so it is compiled for one wave
+// per SIMD and the whole register file).
 struct HaloCfg {
     int nb, hg;
     unsigned tmask;
+    int cps;
 };
 constexpr HaloCfg kCfg[] = {
-    {13, 2, kT9},   {13, 2, kTs2}, {8, 2, kT7},  {13, 4, kTall},
-    {8, 4, kTall},  {4, 4, kTall},
+    {13, 2, kT9, 1},   {13, 2, kTs2, 4}, {8, 2, kT7, 1},
+    {13, 4, kTall, 1}, {8, 4, kTall, 1}, {4, 4, kTall, 1},
 };
 
 }  // namespace
@@ -346,19 +399,23 @@ int halo_f32_config(int nb, unsigned tmask, int hg) {
     return -1;
 }
 
-size_t halo_f32_lds_bytes(int maxT, int HPc) {
-    return (size_t)2 * (maxT * 4 * 64 + 4 * HPc) * sizeof(v2f);
+int halo_f32_cps(int cfg) { return kCfg[cfg].cps; }
+
+size_t halo_f32_lds_bytes(int maxT, int HPc, int stages, int cps) {
+    // stages x (weights + halos of cps chunks), plus the kilobyte the
+    // surplus loads write.
+    return ((size_t)stages * cps * (maxT * 4 * 64 + 4 * HPc) + 128) * sizeof(v2f);
 }
 
 hipError_t launch_halo_f32(const HaloArgs &a, int cfg, int tiles, int ci_tiles, size_t lds,
                            hipStream_t s) {
     switch (cfg) {
-        case 0: return launch_one<13, 2, kT9>(a, tiles, ci_tiles, lds, s);
-        case 1: return launch_one<13, 2, kTs2>(a, tiles, ci_tiles, lds, s);
-        case 2: return launch_one<8, 2, kT7>(a, tiles, ci_tiles, lds, s);
-        case 3: return launch_one<13, 4, kTall>(a, tiles, ci_tiles, lds, s);
-        case 4: return launch_one<8, 4, kTall>(a, tiles, ci_tiles, lds, s);
-        case 5: return launch_one<4, 4, kTall>(a, tiles, ci_tiles, lds, s);
+        case 0: return launch_one<13, 2, kT9, 1, 2>(a, tiles, ci_tiles, lds, s);
+        case 1: return launch_one<13, 2, kTs2, 4, 1>(a, tiles, ci_tiles, lds, s);
+        case 2: return launch_one<8, 2, kT7, 1, 2>(a, tiles, ci_tiles, lds, s);
+        case 3: return launch_one<13, 4, kTall, 1, 2>(a, tiles, ci_tiles, lds, s);
+        case 4: return launch_one<8, 4, kTall, 1, 2>(a, tiles, ci_tiles, lds, s);
+        case 5: return launch_one<4, 4, kTall, 1, 2>(a, tiles, ci_tiles, lds, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -222,7 +222,7 @@ FORCED_TILES = [
 @pytest.mark.parametrize("idx", range(len(FORCED_TILES)))
 def test_forced_halo_tile(idx):
     s, nb, tr, tc = FORCED_TILES[idx]
-    gi.set_halo_tile(nb, tr, tc)
+    gi.set_halo_tile(nb, tr, tc, 0)
     try:
         gi.set_variant(gi.VARIANT_HALO)
         desc = gi.plan(gi.make_params(*s.as_tuple()[:10]), False)
