@@ -129,16 +129,16 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         shift[tp] = (A.kH - 1 - kh) * A.HC + (A.kW - 1 - kw);
     }
 
-    // A ring of three tap slots: step s = chunk*T + tap uses slot s % 3, and
-    // step s + 2 is loaded while step s computes (T is a multiple of 3).
-    static_assert(T % 3 == 0, "tap count must be a multiple of 3");
-    v8bf fa[3][2];
-    fa[0][0] = aload(0, 0, 0);
-    fa[0][1] = aload(0, 0, 1);
-    if (T > 1 || A.nchunks > 1) {
-        const int c1 = T > 1 ? 0 : 1, t1 = T > 1 ? 1 : 0;
-        fa[1][0] = aload(c1, t1, 0);
-        fa[1][1] = aload(c1, t1, 1);
+    // A ring of T slots indexed by tap: step s = chunk*T + tap uses slot
+    // s % T = tap (a compile-time index), and step s + AD is loaded while step
+    // s computes (A comes from L2, so it is fetched several taps ahead).
+    constexpr int AD = T >= 9 ? 4 : T - 1;
+    static_assert(AD >= 1 && AD < T, "prefetch distance");
+    v8bf fa[T][2];
+#pragma unroll
+    for (int s0 = 0; s0 < AD; ++s0) {
+        fa[s0][0] = aload(0, s0, 0);
+        fa[s0][1] = aload(0, s0, 1);
     }
 
     issue(0, 0);
@@ -171,15 +171,15 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 #pragma unroll
         for (int tp = 0; tp < T; ++tp) {
             const int sl = tp & 1;
-            const int as = tp % 3;
-            // Prefetch: A of step + 2, B of the next tap.
+            const int as = tp;
+            // Prefetch: A of step + AD, B of the next tap.
             {
-                const int t2 = tp + 2;
+                const int t2 = tp + AD;
                 const int c2 = t2 < T ? chunk : chunk + 1;
+                const int t2m = t2 < T ? t2 : t2 - T;
                 if (c2 < A.nchunks) {
-                    const int t2m = t2 < T ? t2 : t2 - T;
-                    fa[(tp + 2) % 3][0] = aload(c2, t2m, 0);
-                    fa[(tp + 2) % 3][1] = aload(c2, t2m, 1);
+                    fa[t2m][0] = aload(c2, t2m, 0);
+                    fa[t2m][1] = aload(c2, t2m, 1);
                 }
             }
             if (tp + 1 < T) bfetch(tp + 1, sl ^ 1);
@@ -241,33 +241,38 @@ __global__ __launch_bounds__(256) void pad_nhwc_bf16(const uint16_t *__restrict_
     const int n = blockIdx.x, co0 = blockIdx.y * 64, y0 = blockIdx.z * RB;
     const int yoff = A.kH - 1 - pad_h;  // oh = y - yoff
     const int xoff = A.kW - 1 - pad_w;  // ow = x - xoff
-    const int per_pair = RB * oW;
-    const int nload = 32 * per_pair;
-    for (int e0 = 0; e0 < nload; e0 += 256 * 8) {
-        uint32_t v[8];
-        int at[8];
+    // Thread -> one position of the band (fixed), looping over channel pairs:
+    // no division per element.
+    const int PB = RB * oW;
+    const int PBc = PB < 256 ? PB : 256;
+    const int cstep = 256 / PBc;
+    const int64_t plane = (int64_t)oH * oW;
+    for (int p0 = 0; p0 < PB; p0 += PBc) {
+        const int pos = p0 + threadIdx.x % PBc;
+        const int cp0 = threadIdx.x / PBc;
+        if (cp0 >= cstep || pos >= PB) continue;
+        const int ry = pos / oW, ow = pos - (pos / oW) * oW;
+        const int oh = y0 + ry - yoff;
+        const bool row_ok = y0 + ry < A.YP && oh >= 0 && oh < oH;
+        const int64_t base = ((int64_t)n * A.Co * oH + oh) * oW + ow;
+        uint32_t *dstb = band + pos * 33;
+        for (int cp = cp0; cp < 32; cp += 4 * cstep) {
+            uint32_t v[4];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int e = e0 + u * 256 + threadIdx.x;
-            at[u] = -1;
-            v[u] = 0;
-            if (e < nload) {
-                const int cp = e / per_pair, rem = e - (e / per_pair) * per_pair;
-                const int ry = rem / oW, ow = rem - (rem / oW) * oW;
-                const int oh = y0 + ry - yoff;
-                const int co = co0 + 2 * cp;
-                at[u] = (ry * oW + ow) * 33 + cp;
-                if (y0 + ry < A.YP && oh >= 0 && oh < oH) {
-                    const int64_t base = (((int64_t)n * A.Co + co) * oH + oh) * oW + ow;
-                    const uint32_t lo = co < A.Co ? g[base] : 0u;
-                    const uint32_t hi = co + 1 < A.Co ? g[base + (int64_t)oH * oW] : 0u;
-                    v[u] = lo | (hi << 16);
+            for (int u = 0; u < 4; ++u) {
+                const int c2 = cp + u * cstep;
+                const int co = co0 + 2 * c2;
+                uint32_t lo = 0, hi = 0;
+                if (row_ok && c2 < 32) {
+                    if (co < A.Co) lo = g[base + co * plane];
+                    if (co + 1 < A.Co) hi = g[base + (co + 1) * plane];
                 }
+                v[u] = lo | (hi << 16);
             }
-        }
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-            if (at[u] >= 0) band[at[u]] = v[u];
+            for (int u = 0; u < 4; ++u)
+                if (cp + u * cstep < 32) dstb[cp + u * cstep] = v[u];
+        }
     }
     __syncthreads();
     const int groups = min(8, (A.Cop - co0) / 8);  // 16-byte groups of 8 channels
@@ -300,22 +305,27 @@ __global__ __launch_bounds__(256) void weight_frag_bf16(const uint16_t *__restri
     const int T = A.kH * A.kW;
     const int run = 64 * T;
     const int ci_rows = min(64, A.Ci - ct * 64);
-    const int nload = 8 * run;
-    for (int e0 = 0; e0 < nload; e0 += 256 * 16) {
-        uint16_t v[16];
+    // Thread -> offsets r, r + 256, ... of each channel's run (no division).
+    for (int r0 = 0; r0 < run; r0 += 256 * 2) {
+        uint16_t v[2][8];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            const int e = e0 + u * 256 + threadIdx.x;
-            const int c = e / run, r = e - (e / run) * run;
-            const int co = chunk * 32 + 8 * g + c;
-            v[u] = (e < nload && co < A.Co && r < ci_rows * T)
-                       ? w[((int64_t)co * A.Ci + (int64_t)ct * 64) * T + r]
-                       : (uint16_t)0;
+        for (int u = 0; u < 2; ++u) {
+            const int r = r0 + u * 256 + threadIdx.x;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const int co = chunk * 32 + 8 * g + c;
+                v[u][c] = (r < ci_rows * T && co < A.Co)
+                              ? w[((int64_t)co * A.Ci + (int64_t)ct * 64) * T + r]
+                              : (uint16_t)0;
+            }
         }
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            const int e = e0 + u * 256 + threadIdx.x;
-            if (e < nload) slab[e] = v[u];
+        for (int u = 0; u < 2; ++u) {
+            const int r = r0 + u * 256 + threadIdx.x;
+            if (r < run) {
+#pragma unroll
+                for (int c = 0; c < 8; ++c) slab[c * run + r] = v[u][c];
+            }
         }
     }
     __syncthreads();

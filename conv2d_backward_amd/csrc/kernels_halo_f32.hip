@@ -433,22 +433,27 @@ __global__ __launch_bounds__(256) void weight_image_f32(const float *__restrict_
     const int kHW = kH * kW;
     const int run = kHalo64 * kHW;
     const int ci_rows = min(kHaloCT, A.Ci - ct * kHaloCT);
-    const int nload = kHaloBC * run;
-    for (int e0 = 0; e0 < nload; e0 += 256 * 16) {
-        float v[16];
+    // Thread -> offsets r, r + 256, ... of each channel's run (no division).
+    for (int r0 = 0; r0 < run; r0 += 256 * 2) {
+        float v[2][kHaloBC];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            const int e = e0 + u * 256 + threadIdx.x;
-            const int c = e / run, r = e - (e / run) * run;
-            const int co = chunk * kHaloBC + c;
-            v[u] = (e < nload && co < A.Co && r < ci_rows * kHW)
-                       ? w[((int64_t)co * A.Ci + (int64_t)ct * kHaloCT) * kHW + r]
-                       : 0.f;
+        for (int u = 0; u < 2; ++u) {
+            const int r = r0 + u * 256 + threadIdx.x;
+#pragma unroll
+            for (int c = 0; c < kHaloBC; ++c) {
+                const int co = chunk * kHaloBC + c;
+                v[u][c] = (r < ci_rows * kHW && co < A.Co)
+                              ? w[((int64_t)co * A.Ci + (int64_t)ct * kHaloCT) * kHW + r]
+                              : 0.f;
+            }
         }
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            const int e = e0 + u * 256 + threadIdx.x;
-            if (e < nload) slab[e] = v[u];
+        for (int u = 0; u < 2; ++u) {
+            const int r = r0 + u * 256 + threadIdx.x;
+            if (r < run) {
+#pragma unroll
+                for (int c = 0; c < kHaloBC; ++c) slab[c * run + r] = v[u][c];
+            }
         }
     }
     __syncthreads();
