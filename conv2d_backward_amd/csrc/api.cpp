@@ -343,7 +343,11 @@ bool plan_halo_bf16(const conv2d_gi_params &p, HaloBf16Plan &out) {
             if (TC > maxpx) continue;
             for (int TR = std::min(maxpx / TC, p.H); TR >= 1; --TR) {
                 const int HR = TR + p.kH - 1, HC = TC + p.kW - 1;
-                if (HR * HC > 256) continue;
+                const int QR = (HC + 15) / 16;
+                if (HR * QR > 32) continue;
+                // Row pitch: room for QR loads of 16 positions, and = TC mod 16.
+                const int HP = round_to_residue(QR * 16, 16, TC % 16);
+                if ((size_t)2 * HR * HP * 64 > kLdsBytes / 2) continue;
                 const int64_t tiles = (int64_t)((p.H + TR - 1) / TR) * ((p.W + TC - 1) / TC) * p.N;
                 if (tiles > INT32_MAX) continue;
                 const int64_t wgs = tiles * ci_tiles;
@@ -365,7 +369,8 @@ bool plan_halo_bf16(const conv2d_gi_params &p, HaloBf16Plan &out) {
                     a.HC = HC;
                     a.row_tiles = (p.H + TR - 1) / TR;
                     a.col_tiles = (p.W + TC - 1) / TC;
-                    a.nq = (HR * HC + 15) / 16;
+                    a.HP = HP;
+                    a.QR = QR;
                 }
             }
         }
@@ -386,7 +391,7 @@ bool plan_halo_bf16(const conv2d_gi_params &p, HaloBf16Plan &out) {
     a.gp_bytes = (uint32_t)gp_bytes;
     a.wk_bytes = (uint32_t)wk_bytes;
     a.d_bytes = (uint32_t)((int64_t)p.N * p.Ci * p.H * p.W * 4);
-    out.lds = (size_t)2 * a.nq * 16 * 64;
+    out.lds = (size_t)2 * a.HR * a.HP * 64;
     out.gp_bytes = (size_t)(gp_bytes + 255) / 256 * 256;
     out.wk_bytes = (size_t)wk_bytes;
     return true;

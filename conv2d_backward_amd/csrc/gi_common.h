@@ -109,8 +109,9 @@ struct HaloBf16Args {
     int32_t YP, XP, Cop, nchunks;
     int32_t TR, TC, row_tiles, col_tiles;
     int32_t HR, HC;         // halo rows / columns: TR + kH - 1, TC + kW - 1
-    int32_t nq;             // halo DMA groups of 16 positions per stage
-    int32_t pad_;
+    int32_t HP;             // LDS pitch of a halo row in positions: a multiple of 16
+                            // holding HC, congruent to TC mod 16 (see the kernel)
+    int32_t QR;             // direct loads of 16 positions per halo row: ceil(HC / 16)
 };
 
 }  // namespace gi

@@ -19,8 +19,10 @@
 // (kh, kw) reads its B fragments as the halo shifted by (kH-1-kh, kW-1-kw).
 // A fragments are loaded from the weight image straight into registers, two
 // taps ahead.  LDS holds a position's four 16-byte channel groups in slots
-// permuted by (position / 4) mod 4 so that 16 lanes reading 16 consecutive
-// positions hit 16 different bank groups.
+// permuted by (position / 4) mod 4, and halo rows sit HP positions apart with
+// HP = TC (mod 16): 16 lanes reading 16 consecutive pixels of the tile (which
+// may wrap to the next tile row) then read 16 positions that are consecutive
+// mod 16, i.e. 16 different bank groups.
 //
 // V_MFMA_F32_16X16X32_BF16: lane l = 16*g + i supplies A[i][k = 8g .. 8g+7]
 // and B[k = 8g .. 8g+7][i] and receives D[4g + r][i], r = 0..3.
@@ -39,7 +41,7 @@ namespace {
 
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9)
 constexpr int kOOB = 0x7ffffff0;         // byte offset past the end of every buffer
-constexpr int kQW = 4;                   // halo DMA groups per wave (<= 256 positions)
+constexpr int kQW = 8;                   // halo direct loads per wave per chunk (<= 32 rows)
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
@@ -64,8 +66,8 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     const int n = t / A.row_tiles;
     const int ci_tile = blockIdx.y;
     const int a0 = rt * A.TR, b0 = ct * A.TC;
-    const int hpos = A.HR * A.HC;
-    const int stage = A.nq * 16 * 64;  // bytes per LDS stage
+    const int nq = A.HR * A.QR;           // direct loads per chunk (16 positions each)
+    const int stage = A.HR * A.HP * 64;  // bytes per LDS stage
 
     const __amdgpu_buffer_rsrc_t grs = make_rsrc(A.gp, A.gp_bytes);
     const __amdgpu_buffer_rsrc_t wrs = make_rsrc(A.wk, A.wk_bytes);
@@ -79,31 +81,34 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         const int p = (wn * NBW + b) * 16 + j16;
         const int r = p / A.TC, c = p - (p / A.TC) * A.TC;
         const bool v = p < A.TR * A.TC && a0 + r < A.H && b0 + c < A.W;
-        ppos[b] = v ? r * A.HC + c : 0;
+        ppos[b] = v ? r * A.HP + c : 0;
     }
 
-    // Halo DMA: group q covers positions 16q .. 16q+15; lane -> (position
-    // 16q + lane/4, slot lane%4) loads channel group slot ^ ((pos/4) & 3).
+    // Halo DMA: load q covers halo row q / QR, columns 16 (q % QR) .. +15;
+    // lane -> (column + lane/4, slot lane%4) loads channel group
+    // slot ^ ((lds position / 4) & 3).
     int goff[kQW];
 #pragma unroll
     for (int i = 0; i < kQW; ++i) {
         const int q = wave + 4 * i;
-        const int pos = q * 16 + (lane >> 2);
+        const int hr = q / A.QR, hc = (q - (q / A.QR) * A.QR) * 16 + (lane >> 2);
+        const int lpos = hr * A.HP + hc;
         const int slot = lane & 3;
-        const int kg = slot ^ ((pos >> 2) & 3);
-        const int hr = pos / A.HC, hc = pos - (pos / A.HC) * A.HC;
+        const int kg = slot ^ ((lpos >> 2) & 3);
         const int y = a0 + hr, x = b0 + hc;
-        const bool v = q < A.nq && pos < hpos && y < A.YP && x < A.XP;
+        const bool v = q < nq && hc < A.HC && y < A.YP && x < A.XP;
         goff[i] = v ? (((n * A.YP + y) * A.XP + x) * A.Cop + 8 * kg) * 2 : kOOB;
     }
     auto issue = [&](int chunk, int buf) {
 #pragma unroll
         for (int i = 0; i < kQW; ++i) {
             const int q = wave + 4 * i;
-            if (q < A.nq) {
+            if (q < nq) {
+                const int hr = q / A.QR, u = q - (q / A.QR) * A.QR;
                 const int off = goff[i] == kOOB ? kOOB : goff[i] + chunk * 64;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    grs, (lds_ptr_t)(smem + buf * stage + q * 1024), 16, off, 0, 0, 0);
+                    grs, (lds_ptr_t)(smem + buf * stage + (hr * A.HP + u * 16) * 64), 16, off, 0,
+                    0, 0);
             }
         }
     };
@@ -126,7 +131,7 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 #pragma unroll
     for (int tp = 0; tp < T; ++tp) {
         const int kh = tp / A.kW, kw = tp - (tp / A.kW) * A.kW;
-        shift[tp] = (A.kH - 1 - kh) * A.HC + (A.kW - 1 - kw);
+        shift[tp] = (A.kH - 1 - kh) * A.HP + (A.kW - 1 - kw);
     }
 
     // A ring of T slots indexed by tap: step s = chunk*T + tap uses slot
