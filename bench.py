@@ -10,9 +10,11 @@ batch of synthetic inputs already resident in HBM.  W untimed steps, then K
 steps bracketed by a device synchronize on both sides; rank 0 prints ONE JSON
 line.  Effective work per call is 2*N*Co*oH*oW*Ci*kH*kW flops.
 
-The GEMM kernels' own duration is measured live with HIP events that the
-library records on the launch stream around its GEMM launches (the
+The main kernel's own duration is measured live with HIP events that its
+launch records with the dispatch's start and end timestamps (the
 ``roofline.achieved`` figure); the whole-call time gives ``value``.
+``roofline.traffic`` is the HBM bytes per launch from the committed counter
+summary under profiles/, when its kernel sources and plan still match.
 """
 from __future__ import annotations
 
@@ -30,6 +32,7 @@ if ROOT not in sys.path:
 import numpy as np  # noqa: E402
 
 import workloads  # noqa: E402
+from conv2d_backward_amd import profiling  # noqa: E402
 
 METRIC = "effective TFLOP/s of conv2d grad_input per config; % of MFMA peak (1 GPU)"
 PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6}   # MI355X dense matrix-core peaks
@@ -48,6 +51,10 @@ def parse():
                     help="skip the short timing of the other workloads")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="end with %d plain device copies of this many MiB (the "
+                         "reference kernel for scaling HBM byte counters)"
+                         % profiling.CALIBRATION_COPIES)
     return ap.parse_args()
 
 
@@ -121,9 +128,9 @@ def time_workload(wl, steps, warmup, torch, gi, dev):
     torch.cuda.synchronize()
     wall1 = time.perf_counter()
     total_ms = hev.elapsed_ms(t0, t1)
-    # Contraction kernels alone: the library records a begin/end event pair
-    # around its GEMM launches (these records add their own gaps, so this
-    # loop is not used for the whole-call figure).
+    # Contraction kernels alone: the library's main launch records a
+    # begin/end event pair with the dispatch's own timestamps (a separate
+    # loop, so the whole-call figure above has no events inside it).
     kb = [hev.create() for _ in range(steps)]
     ke = [hev.create() for _ in range(steps)]
     for i in range(steps):
@@ -182,8 +189,11 @@ def main():
     value = r["flops"] / (r["ms_per_step"] * 1e-3) / 1e12
     peak = PEAK_TFLOPS[wl.dtype]
     plan_desc = gi.plan(gi.make_params(*s.as_tuple()[:10]), wl.dtype == "bf16")
-    variant = plan_desc.split()[0].split("=")[1]
+    variant = profiling.plan_variant(plan_desc)
+    kernel = profiling.kernel_name(variant, wl.dtype)
     achieved = r["flops"] / (r["kernel_ms"] * 1e-3) / 1e12
+    alg_bytes = s.algorithmic_bytes(2 if wl.dtype == "bf16" else 4)
+    traffic = profiling.read_traffic(kernel, wl.name, plan_desc, variant, wl.dtype)
     line = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -202,8 +212,12 @@ def main():
                    "pad_w": s.pad_w, "oH": s.oH, "oW": s.oW, "eff_gflop": s.eff_flops / 1e9,
                    "plan": plan_desc},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
-                     "kernel": "gi_%s_%s" % (variant, wl.dtype),
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": None if traffic is None else round(traffic["bytes"]),
+                     "algorithmic_bytes": alg_bytes,
+                     "hbm_gbs": None if traffic is None else
+                     round(traffic["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9, 1),
+                     "kernel": kernel,
                      "kernel_ms": round(r["kernel_ms"], 5),
                      "per_unit": "2*Ci*kH*kW*Co flops per output pixel (n,oh,ow)",
                      "units_per_launch": s.N * s.oH * s.oW},
@@ -216,13 +230,33 @@ def main():
                 continue
             ro = time_workload(o, 20, 3, torch, gi, dev)
             v = ro["flops"] / (ro["ms_per_step"] * 1e-3) / 1e12
+            so = o.shape
+            po = gi.plan(gi.make_params(*so.as_tuple()[:10]), o.dtype == "bf16")
+            vo = profiling.plan_variant(po)
+            to = profiling.read_traffic(profiling.kernel_name(vo, o.dtype), o.name, po, vo,
+                                        o.dtype)
             others[o.name] = {"dtype": o.dtype, "tflops": round(v, 3),
                               "ms_per_call": round(ro["ms_per_step"], 5),
                               "kernel_ms": round(ro["kernel_ms"], 5),
-                              "frac_of_peak": round(v / PEAK_TFLOPS[o.dtype], 4)}
+                              "frac_of_peak": round(v / PEAK_TFLOPS[o.dtype], 4),
+                              "kernel_frac_of_peak": round(
+                                  ro["flops"] / (ro["kernel_ms"] * 1e-3) / 1e12
+                                  / PEAK_TFLOPS[o.dtype], 4),
+                              "traffic": None if to is None else round(to["bytes"]),
+                              "algorithmic_bytes": so.algorithmic_bytes(
+                                  2 if o.dtype == "bf16" else 4)}
         line["other_workloads"] = others
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    if args.calibration_copy_mib > 0:
+        n = args.calibration_copy_mib * 1024 * 1024 // 4
+        src = torch.empty(n, dtype=torch.float32, device=dev).uniform_()
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(profiling.CALIBRATION_COPIES):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     print(json.dumps(line), flush=True)
 
 

@@ -294,6 +294,7 @@ bool plan_halo(const conv2d_gi_params &p, const std::vector<Phase> &phases, Halo
     a.nchunks = nchunks;
     a.maxT = maxT;
     a.w_ci_stride = (int)w_ci_stride;
+    a.ci_tiles = ci_tiles;
     a.nphases = (int)phases.size();
     int64_t woff = 0;
     for (size_t i = 0; i < phases.size(); ++i) {
@@ -388,6 +389,7 @@ bool plan_halo_bf16(const conv2d_gi_params &p, HaloBf16Plan &out) {
     a.XP = XP;
     a.Cop = Cop;
     a.nchunks = nchunks;
+    a.ci_tiles = ci_tiles;
     a.gp_bytes = (uint32_t)gp_bytes;
     a.wk_bytes = (uint32_t)wk_bytes;
     a.d_bytes = (uint32_t)((int64_t)p.N * p.Ci * p.H * p.W * 4);
@@ -569,14 +571,17 @@ int run(const T *grad_out, const T *weight, float *dst, const conv2d_gi_params *
         if (e != hipSuccess) return fail_hip(e);
     }
     e = hipSuccess;
-    if (g_prof_begin && g_prof_end) e = hipEventRecord(g_prof_begin, stream);
+    // Profiling events, when set, take the main kernel's own start and end
+    // timestamps (first and last launch when there are several).
+    gi::KernelEvents ev;
+    if (g_prof_begin && g_prof_end) ev = {g_prof_begin, g_prof_end};
     if (plan.variant == CONV2D_GI_VARIANT_STEM) {
         if (e == hipSuccess) {
             gi::StemArgs &a = plan.stem.args;
             a.grad_out = (const float *)grad_out;
             a.wk = (const float *)ws;
             a.dst = dst;
-            e = gi::launch_stem_f32(a, stream);
+            e = gi::launch_stem_f32(a, stream, ev);
         }
     } else if (plan.variant == CONV2D_GI_VARIANT_HALO && bf16) {
         if (e == hipSuccess) {
@@ -584,7 +589,7 @@ int run(const T *grad_out, const T *weight, float *dst, const conv2d_gi_params *
             h.args.gp = (const uint16_t *)ws;
             h.args.wk = (const uint16_t *)((char *)ws + h.gp_bytes);
             h.args.dst = dst;
-            e = gi::launch_halo_bf16(h.args, h.cfg, h.tiles, h.ci_tiles, h.lds, stream);
+            e = gi::launch_halo_bf16(h.args, h.cfg, h.tiles, h.ci_tiles, h.lds, stream, ev);
         }
     } else if (plan.variant == CONV2D_GI_VARIANT_HALO) {
         if (e == hipSuccess) {
@@ -592,19 +597,23 @@ int run(const T *grad_out, const T *weight, float *dst, const conv2d_gi_params *
             h.args.grad_out = (const float *)grad_out;
             h.args.wk = (const float *)ws;
             h.args.dst = dst;
-            e = gi::launch_halo_f32(h.args, h.cfg, h.tiles, h.ci_tiles, h.lds, stream);
+            e = gi::launch_halo_f32(h.args, h.cfg, h.tiles, h.ci_tiles, h.lds, stream, ev);
         }
     } else {
-        for (Launch &L : plan.launches) {
+        const size_t nl = plan.launches.size();
+        for (size_t i = 0; i < nl; ++i) {
             if (e != hipSuccess) break;
+            Launch &L = plan.launches[i];
             L.args.grad_out = grad_out;
             L.args.wt = ws;
             L.args.dst = dst;
-            e = bf16 ? gi::launch_generic_bf16(L.args, L.tiles_x, stream)
-                     : gi::launch_generic_f32(L.args, L.tiles_x, stream);
+            gi::KernelEvents li;
+            li.start = i == 0 ? ev.start : nullptr;
+            li.stop = i + 1 == nl ? ev.stop : nullptr;
+            e = bf16 ? gi::launch_generic_bf16(L.args, L.tiles_x, stream, li)
+                     : gi::launch_generic_f32(L.args, L.tiles_x, stream, li);
         }
     }
-    if (e == hipSuccess && g_prof_begin && g_prof_end) e = hipEventRecord(g_prof_end, stream);
     if (e != hipSuccess) return fail_hip(e);
     return CONV2D_GI_OK;
 }

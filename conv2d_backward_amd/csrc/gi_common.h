@@ -18,6 +18,20 @@
 
 namespace gi {
 
+// The dispatcher hands work-groups to the chip's 8 XCDs in turn by linear id,
+// and each XCD has its own L2.  xcd_order maps linear id L of a 1-D grid of G
+// work-groups to a logical index such that XCD x = L mod 8 receives the
+// contiguous logical range starting at x*(G/8) + min(x, G mod 8), in order:
+// work-groups that read the same grad_out lines (the input-channel tiles or
+// phases of one pixel tile, neighbouring tiles) then run on one L2 at about
+// the same time.  It is a bijection on [0, G) whatever the dispatch order.
+constexpr int kXcds = 8;
+__host__ __device__ inline int xcd_order(int L, int G) {
+    const int x = L % kXcds, k = L / kXcds;
+    const int q = G / kXcds, r = G % kXcds;
+    return x * q + (x < r ? x : r) + k;
+}
+
 constexpr int kMaxPhasesPerLaunch = 16;
 
 struct Phase {
@@ -81,7 +95,7 @@ struct HaloArgs {
     int32_t stages;         // LDS stages of the chunk pipeline (2 or 3)
     int32_t maxT;           // most taps of any phase
     int32_t w_ci_stride;    // floats of the weight image per ci tile
-    int32_t pad_;
+    int32_t ci_tiles;       // ceil(Ci / 64); grid = tiles * ci_tiles (1-D, xcd_order)
     HaloPhase ph[kMaxPhasesPerLaunch];
 };
 
@@ -112,6 +126,8 @@ struct HaloBf16Args {
     int32_t HP;             // LDS pitch of a halo row in positions: a multiple of 16
                             // holding HC, congruent to TC mod 16 (see the kernel)
     int32_t QR;             // direct loads of 16 positions per halo row: ceil(HC / 16)
+    int32_t ci_tiles;       // ceil(Ci / 64); grid = tiles * ci_tiles (1-D, xcd_order)
+    int32_t pad_;
 };
 
 }  // namespace gi

@@ -1,12 +1,20 @@
 // gi_launch.h -- host-side launchers of the kernels (one per kernel family).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "gi_common.h"
 
 namespace gi {
+
+// Events recorded by a main-kernel launch with the dispatch's own start and
+// end timestamps (hipExtLaunchKernelGGL); either may be null.
+struct KernelEvents {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
 
 // Weight reorder prologues.
 //   fp32: wt[(tap*Co + co)*Ci + ci] = w[((co*Ci + ci)*kH*kW) + tap]   (ci fastest)
@@ -21,8 +29,10 @@ hipError_t launch_weight_tap_ci_co_bf16(const uint16_t *w, uint16_t *wt, int Co,
 // ceil(Ci/64)).
 constexpr int kGenericBM = 64;
 constexpr int kGenericBN = 128;
-hipError_t launch_generic_f32(const GemmArgs &a, int tiles_x, hipStream_t s);
-hipError_t launch_generic_bf16(const GemmArgs &a, int tiles_x, hipStream_t s);
+hipError_t launch_generic_f32(const GemmArgs &a, int tiles_x, hipStream_t s,
+                              const KernelEvents &ev);
+hipError_t launch_generic_bf16(const GemmArgs &a, int tiles_x, hipStream_t s,
+                               const KernelEvents &ev);
 
 // Halo-tile fp32 kernel (kernels_halo_f32.hip).  Instantiations are indexed
 // by (NB pixel blocks of 16 per work-group, HG halo groups of 32 positions
@@ -35,7 +45,7 @@ constexpr int kHaloCT = 64;    // input channels per work-group
 unsigned halo_f32_tbit(int T);
 int halo_f32_config(int nb, unsigned tmask, int hg);
 hipError_t launch_halo_f32(const HaloArgs &a, int cfg, int tiles, int ci_tiles, size_t lds,
-                           hipStream_t s);
+                           hipStream_t s, const KernelEvents &ev);
 // Chunks of 8 output channels per LDS stage of instantiation cfg, and the LDS
 // bytes of the halo kernel: most taps of a phase, halo pitch (float2),
 // pipeline stages, chunks per stage.
@@ -52,7 +62,7 @@ hipError_t launch_weight_image_f32(const float *w, float *wk, const HaloArgs &a,
 // indexed by (NBW pixel blocks of 16 per wave, tap count T); -1 when none.
 int halo_bf16_config(int nbw, int taps);
 hipError_t launch_halo_bf16(const HaloBf16Args &a, int cfg, int tiles, int ci_tiles, size_t lds,
-                            hipStream_t s);
+                            hipStream_t s, const KernelEvents &ev);
 // Prologues of the bf16 halo kernel (layouts in gi_common.h).
 hipError_t launch_pad_nhwc_bf16(const uint16_t *g, uint16_t *gp, const HaloBf16Args &a, int oH,
                                 int oW, int pad_h, int pad_w, hipStream_t s);
@@ -62,7 +72,7 @@ hipError_t launch_weight_frag_bf16(const uint16_t *w, uint16_t *wk, const HaloBf
 // Small-Ci fp32 kernel (kernels_stem_f32.hip): Ci <= 4, any stride whose
 // phases have a tap count in the served set (stem_f32_taps_ok).
 bool stem_f32_taps_ok(int taps);
-hipError_t launch_stem_f32(const StemArgs &a, hipStream_t s);
+hipError_t launch_stem_f32(const StemArgs &a, hipStream_t s, const KernelEvents &ev);
 hipError_t launch_weight_stem_f32(const float *w, float *wk, const StemArgs &a, int kH, int kW,
                                   hipStream_t s);
 

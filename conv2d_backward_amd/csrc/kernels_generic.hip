@@ -300,13 +300,17 @@ __global__ __launch_bounds__(256) void gi_generic_bf16(const GemmArgs A) {
     store_block(A, P, acc1, ci0 + wm * 32, pix0 + wn * 64 + 32 + ml, npix, lane);
 }
 
-hipError_t launch_generic_f32(const GemmArgs &a, int tiles_x, hipStream_t s) {
-    hipLaunchKernelGGL(gi_generic_f32<16>, dim3(tiles_x, a.ci_tiles), dim3(256), 0, s, a);
+hipError_t launch_generic_f32(const GemmArgs &a, int tiles_x, hipStream_t s,
+                              const KernelEvents &ev) {
+    hipExtLaunchKernelGGL(gi_generic_f32<16>, dim3(tiles_x, a.ci_tiles), dim3(256), 0, s,
+                          ev.start, ev.stop, 0, a);
     return hipGetLastError();
 }
 
-hipError_t launch_generic_bf16(const GemmArgs &a, int tiles_x, hipStream_t s) {
-    hipLaunchKernelGGL(gi_generic_bf16, dim3(tiles_x, a.ci_tiles), dim3(256), 0, s, a);
+hipError_t launch_generic_bf16(const GemmArgs &a, int tiles_x, hipStream_t s,
+                               const KernelEvents &ev) {
+    hipExtLaunchKernelGGL(gi_generic_bf16, dim3(tiles_x, a.ci_tiles), dim3(256), 0, s, ev.start,
+                          ev.stop, 0, a);
     return hipGetLastError();
 }
 

@@ -17,8 +17,8 @@
 // Per chunk the tile's halo, (TR+kH-1) x (TC+kW-1) positions x 32 channels,
 // is copied into LDS by direct global -> LDS loads (double-buffered), and tap
 // (kh, kw) reads its B fragments as the halo shifted by (kH-1-kh, kW-1-kw).
-// A fragments are loaded from the weight image straight into registers, two
-// taps ahead.  LDS holds a position's four 16-byte channel groups in slots
+// A fragments are loaded from the weight image straight into registers,
+// several taps ahead.  LDS holds a position's four 16-byte channel groups in slots
 // permuted by (position / 4) mod 4, and halo rows sit HP positions apart with
 // HP = TC (mod 16): 16 lanes reading 16 consecutive pixels of the tile (which
 // may wrap to the next tile row) then read 16 positions that are consecutive
@@ -59,12 +59,14 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     const int j16 = lane & 15, g = lane >> 4;
     const int wm = wave & 1, wn = wave >> 1;
 
-    int t = blockIdx.x;
+    // Logical order: input-channel tile fastest, then column, row, image.
+    const int J = xcd_order(blockIdx.x, gridDim.x);
+    const int ci_tile = J % A.ci_tiles;
+    int t = J / A.ci_tiles;
     const int ct = t % A.col_tiles;
     t /= A.col_tiles;
     const int rt = t % A.row_tiles;
     const int n = t / A.row_tiles;
-    const int ci_tile = blockIdx.y;
     const int a0 = rt * A.TR, b0 = ct * A.TC;
     const int nq = A.HR * A.QR;           // direct loads per chunk (16 positions each)
     const int stage = A.HR * A.HP * 64;  // bytes per LDS stage
@@ -222,13 +224,16 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 }
 
 template <int NBW, int T>
-hipError_t launch_one(const HaloBf16Args &a, int tiles, int ci_tiles, size_t lds, hipStream_t s) {
+hipError_t launch_one(const HaloBf16Args &a, int tiles, int ci_tiles, size_t lds, hipStream_t s,
+                      const KernelEvents &ev) {
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void *)gi_halo_bf16<NBW, T>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((gi_halo_bf16<NBW, T>), dim3(tiles, ci_tiles), dim3(256), lds, s, a);
+    if (a.ci_tiles != ci_tiles) return hipErrorInvalidValue;
+    hipExtLaunchKernelGGL((gi_halo_bf16<NBW, T>), dim3(tiles * ci_tiles), dim3(256), (uint32_t)lds,
+                          s, ev.start, ev.stop, 0, a);
     return hipGetLastError();
 }
 
@@ -357,12 +362,12 @@ int halo_bf16_config(int nbw, int taps) {
 }
 
 hipError_t launch_halo_bf16(const HaloBf16Args &a, int cfg, int tiles, int ci_tiles, size_t lds,
-                            hipStream_t s) {
+                            hipStream_t s, const KernelEvents &ev) {
     switch (cfg) {
-        case 0: return launch_one<7, 9>(a, tiles, ci_tiles, lds, s);
-        case 1: return launch_one<4, 9>(a, tiles, ci_tiles, lds, s);
-        case 2: return launch_one<7, 3>(a, tiles, ci_tiles, lds, s);
-        case 3: return launch_one<4, 3>(a, tiles, ci_tiles, lds, s);
+        case 0: return launch_one<7, 9>(a, tiles, ci_tiles, lds, s, ev);
+        case 1: return launch_one<4, 9>(a, tiles, ci_tiles, lds, s, ev);
+        case 2: return launch_one<7, 3>(a, tiles, ci_tiles, lds, s, ev);
+        case 3: return launch_one<4, 3>(a, tiles, ci_tiles, lds, s, ev);
         default: return hipErrorInvalidValue;
     }
 }

@@ -282,7 +282,10 @@ __global__ __launch_bounds__(256, OCC) __attribute__((amdgpu_waves_per_eu(OCC, O
     const int lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, g4 = lane >> 4;
 
-    int t = blockIdx.x;
+    // Logical order: input-channel tile fastest, then column, row, image.
+    const int J = xcd_order(blockIdx.x, gridDim.x);
+    const int ci_tile = J % A.ci_tiles;
+    int t = J / A.ci_tiles;
     const int ct = t % A.col_tiles;
     t /= A.col_tiles;
     int rt, n_img = 0;
@@ -292,7 +295,6 @@ __global__ __launch_bounds__(256, OCC) __attribute__((amdgpu_waves_per_eu(OCC, O
         rt = t % A.row_tiles;
         n_img = t / A.row_tiles;
     }
-    const int ci_tile = blockIdx.y;
     const int ci0 = ci_tile * kHaloCT;
     const int a0 = rt * A.TR, b0 = ct * A.TC;
     const int plane = A.H * A.W;
@@ -364,14 +366,16 @@ constexpr unsigned kTs2 = tbit(1) | tbit(2) | tbit(4);
 constexpr unsigned kTall = tbit(1) | tbit(2) | tbit(3) | tbit(4) | tbit(6) | tbit(7) | tbit(9);
 
 template <int NB, int HG, unsigned TMASK, int CPS, int OCC>
-hipError_t launch_one(const HaloArgs &a, int tiles, int ci_tiles, size_t lds, hipStream_t s) {
+hipError_t launch_one(const HaloArgs &a, int tiles, int ci_tiles, size_t lds, hipStream_t s,
+                      const KernelEvents &ev) {
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void *)gi_halo_f32<NB, HG, TMASK, CPS, OCC>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((gi_halo_f32<NB, HG, TMASK, CPS, OCC>), dim3(tiles, ci_tiles), dim3(256),
-                       lds, s, a);
+    if (a.ci_tiles != ci_tiles) return hipErrorInvalidValue;
+    hipExtLaunchKernelGGL((gi_halo_f32<NB, HG, TMASK, CPS, OCC>), dim3(tiles * ci_tiles),
+                          dim3(256), (uint32_t)lds, s, ev.start, ev.stop, 0, a);
     return hipGetLastError();
 }
 
@@ -408,14 +412,14 @@ size_t halo_f32_lds_bytes(int maxT, int HPc, int stages, int cps) {
 }
 
 hipError_t launch_halo_f32(const HaloArgs &a, int cfg, int tiles, int ci_tiles, size_t lds,
-                           hipStream_t s) {
+                           hipStream_t s, const KernelEvents &ev) {
     switch (cfg) {
-        case 0: return launch_one<13, 2, kT9, 1, 2>(a, tiles, ci_tiles, lds, s);
-        case 1: return launch_one<13, 2, kTs2, 4, 1>(a, tiles, ci_tiles, lds, s);
-        case 2: return launch_one<8, 2, kT7, 1, 2>(a, tiles, ci_tiles, lds, s);
-        case 3: return launch_one<13, 4, kTall, 1, 2>(a, tiles, ci_tiles, lds, s);
-        case 4: return launch_one<8, 4, kTall, 1, 2>(a, tiles, ci_tiles, lds, s);
-        case 5: return launch_one<4, 4, kTall, 1, 2>(a, tiles, ci_tiles, lds, s);
+        case 0: return launch_one<13, 2, kT9, 1, 2>(a, tiles, ci_tiles, lds, s, ev);
+        case 1: return launch_one<13, 2, kTs2, 4, 1>(a, tiles, ci_tiles, lds, s, ev);
+        case 2: return launch_one<8, 2, kT7, 1, 2>(a, tiles, ci_tiles, lds, s, ev);
+        case 3: return launch_one<13, 4, kTall, 1, 2>(a, tiles, ci_tiles, lds, s, ev);
+        case 4: return launch_one<8, 4, kTall, 1, 2>(a, tiles, ci_tiles, lds, s, ev);
+        case 5: return launch_one<4, 4, kTall, 1, 2>(a, tiles, ci_tiles, lds, s, ev);
         default: return hipErrorInvalidValue;
     }
 }

@@ -161,7 +161,8 @@ __global__ __launch_bounds__(128, 2) void gi_stem_f32(const StemArgs A) {
     extern __shared__ __attribute__((aligned(16))) v4f sm4[];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    int bid = blockIdx.x;
+    // Logical order: phase fastest, then tile column, row, image.
+    int bid = xcd_order(blockIdx.x, gridDim.x);
     const int p = bid % A.nphases;
     bid /= A.nphases;
     const int tc = bid % A.tiles_c;
@@ -252,10 +253,11 @@ bool stem_f32_taps_ok(int taps) {
     }
 }
 
-hipError_t launch_stem_f32(const StemArgs &a, hipStream_t s) {
+hipError_t launch_stem_f32(const StemArgs &a, hipStream_t s, const KernelEvents &ev) {
     const size_t lds = (size_t)2 * a.HPmax * sizeof(v4f);
     const int64_t wgs = (int64_t)a.N * a.tiles_r * a.tiles_c * a.nphases;
-    hipLaunchKernelGGL(gi_stem_f32, dim3((unsigned)wgs), dim3(128), lds, s, a);
+    hipExtLaunchKernelGGL(gi_stem_f32, dim3((unsigned)wgs), dim3(128), (uint32_t)lds, s, ev.start,
+                          ev.stop, 0, a);
     return hipGetLastError();
 }
 

@@ -1,0 +1,261 @@
+"""Summaries of rocprofv3 output for the grad_input kernels (host-side text
+processing only: nothing here touches a GPU or the library).
+
+Two summaries are written under ``profiles/``, named for kernel and workload:
+
+* ``<kernel>_<workload>_stats.md`` -- the ``--kernel-trace --stats`` table of
+  one bench.py run, beside the kernel duration that bench.py measured live
+  with HIP events in the same run;
+* ``<kernel>_<workload>_traffic.txt`` -- HBM bytes per launch of the dominant
+  kernel from two ``--pmc`` runs (FETCH_SIZE, then WRITE_SIZE, both in KiB per
+  dispatch), each scaled by what the same counter reads for a plain
+  device-to-device copy of known size run at the end of the same program.
+
+The traffic file records a fingerprint of the kernel's sources and the
+planner's description of the launch; bench.py reports its figure only while
+both still match what it is about to run.
+
+    python -m conv2d_backward_amd.profiling stats --run-dir D --bench-log L \
+        --workload W --command "..." [--out-dir profiles]
+    python -m conv2d_backward_amd.profiling traffic --fetch-dir D1 --write-dir D2 \
+        --bench-log L --workload W --copy-mib M --command-fetch "..." \
+        --command-write "..." [--out-dir profiles]
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG, "csrc")
+ROOT = os.path.dirname(PKG)
+PROFILES = os.path.join(ROOT, "profiles")
+
+# Sources that define each main kernel (its launch parameters come from the
+# planner, whose result is matched separately through the plan description).
+KERNEL_SOURCES = {
+    ("halo", "f32"): ["kernels_halo_f32.hip"],
+    ("halo", "bf16"): ["kernels_halo_bf16.hip"],
+    ("stem", "f32"): ["kernels_stem_f32.hip"],
+    ("generic", "f32"): ["kernels_generic.hip"],
+    ("generic", "bf16"): ["kernels_generic.hip"],
+}
+COMMON_SOURCES = ["gi_common.h", "gi_launch.h"]
+CALIBRATION_COPIES = 3   # copies bench.py runs for --calibration-copy-mib
+
+
+def kernel_name(variant: str, dtype: str) -> str:
+    """Short name of the main kernel of a plan: gi_<variant>_<dtype>."""
+    return "gi_%s_%s" % (variant, dtype)
+
+
+def plan_variant(plan_desc: str) -> str:
+    return plan_desc.split()[0].split("=", 1)[1]
+
+
+def fingerprint(variant: str, dtype: str) -> str:
+    """sha256 (first 16 hex digits) over the kernel's source files."""
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[(variant, dtype)] + COMMON_SOURCES:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def _matches(name: str, short: str) -> bool:
+    return (short + "<") in name or (short + "(") in name
+
+
+def _bench_line(path: str) -> dict:
+    with open(path) as fh:
+        for line in reversed(fh.read().strip().splitlines()):
+            line = line.strip()
+            if line.startswith("{"):
+                return json.loads(line)
+    raise ValueError("no JSON line in %s" % path)
+
+
+def _csv(run_dir: str, suffix: str) -> str:
+    hits = sorted(glob.glob(os.path.join(run_dir, "**", "*" + suffix), recursive=True))
+    if not hits:
+        raise FileNotFoundError("no *%s under %s" % (suffix, run_dir))
+    return hits[0]
+
+
+def _unprofiled_kernel_ms(bench_log: str, workload: str):
+    """Main-kernel ms of `workload` in a bench.py run without the profiler
+    (its headline workload or one of its other_workloads), else None."""
+    line = _bench_line(bench_log)
+    if line["config"]["workload"] == workload:
+        return line["roofline"]["kernel_ms"], "bench.py --steps %d --warmup %d" % (
+            line["steps"], line["warmup"])
+    o = line.get("other_workloads", {}).get(workload)
+    if o is None:
+        return None
+    return o["kernel_ms"], "bench.py (other workloads: 20 steps, 3 warm-up)"
+
+
+def write_stats(run_dir: str, bench_log: str, workload: str, command: str,
+                out_dir: str = PROFILES, top: int = 8, plain_log: str = None) -> str:
+    line = _bench_line(bench_log)
+    plan = line["config"]["plan"]
+    short = kernel_name(plan_variant(plan), line["dtype"])
+    with open(_csv(run_dir, "kernel_stats.csv")) as fh:
+        rows = list(csv.DictReader(fh))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    main = [r for r in rows if _matches(r["Name"], short)]
+    if not main:
+        raise ValueError("kernel %s not in %s" % (short, run_dir))
+    out = os.path.join(out_dir, "%s_%s_stats.md" % (short, workload))
+    rf = line["roofline"]
+    with open(out, "w") as fh:
+        fh.write("# %s on %s: rocprofv3 kernel-trace statistics\n\n" % (short, workload))
+        fh.write("Command (from the repository root):\n\n    %s\n\n" % command)
+        fh.write("Plan: `%s`\n\n" % plan)
+        fh.write("| Kernel | Calls | Average (us) | Min (us) | Max (us) | Share |\n")
+        fh.write("|---|---|---|---|---|---|\n")
+        for r in rows[:top]:
+            fh.write("| `%s` | %s | %.2f | %.2f | %.2f | %s%% |\n" % (
+                r["Name"][:110], r["Calls"], float(r["AverageNs"]) / 1e3,
+                float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, r["Percentage"]))
+        avg_us = float(main[0]["AverageNs"]) / 1e3
+        fh.write("\nSame run, bench.py's own measurement (HIP events on the launch stream):\n\n")
+        fh.write("- main kernel `%s`: %.2f us per launch (rocprofv3 average %.2f us, "
+                 "ratio %.3f)\n" % (short, rf["kernel_ms"] * 1e3, avg_us,
+                                    rf["kernel_ms"] * 1e3 / avg_us))
+        if plain_log:
+            u = _unprofiled_kernel_ms(plain_log, workload)
+            if u is not None:
+                fh.write("- without the profiler (`python3 %s`): %.2f us per launch "
+                         "(ratio to the rocprofv3 average %.3f); the profiler's own "
+                         "per-dispatch work delays the events in the run above\n"
+                         % (u[1], u[0] * 1e3, u[0] * 1e3 / avg_us))
+        fh.write("- roofline: achieved %.3f %s of %.1f (frac %.4f)\n"
+                 % (rf["achieved"], rf["unit"], rf["peak"], rf["frac"]))
+        fh.write("- whole call: %.2f us, %.3f %s\n"
+                 % (line["ms_per_step"] * 1e3, line["value"], line["unit"]))
+    return out
+
+
+def _counter(run_dir: str, counter: str):
+    """Per-dispatch (dispatch id, kernel name, value) of one counter, with
+    the values of all hardware instances of a dispatch summed."""
+    with open(_csv(run_dir, "counter_collection.csv")) as fh:
+        rows = list(csv.DictReader(fh))
+    per = {}
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        d = int(r["Dispatch_Id"])
+        name, v = per.get(d, (r["Kernel_Name"], 0.0))
+        per[d] = (name, v + float(r["Counter_Value"]))
+    return [(d, per[d][0], per[d][1]) for d in sorted(per)]
+
+
+def _kernel_and_copy(run_dir: str, counter: str, short: str):
+    disp = _counter(run_dir, counter)
+    copies = disp[-CALIBRATION_COPIES:]
+    if len(copies) < CALIBRATION_COPIES or not all("copy" in n.lower() for _, n, _ in copies):
+        raise ValueError("the last %d dispatches in %s are not the calibration copies"
+                         % (CALIBRATION_COPIES, run_dir))
+    main = [(d, n, v) for d, n, v in disp if _matches(n, short)]
+    if not main:
+        raise ValueError("kernel %s not in %s" % (short, run_dir))
+    kib = sum(v for _, _, v in main) / len(main)
+    ckib = sum(v for _, _, v in copies) / len(copies)
+    return main[0][1], len(main), kib, copies[0][1], ckib
+
+
+def write_traffic(fetch_dir: str, write_dir: str, bench_log: str, workload: str,
+                  copy_mib: int, command_fetch: str, command_write: str,
+                  out_dir: str = PROFILES) -> str:
+    line = _bench_line(bench_log)
+    plan = line["config"]["plan"]
+    variant, dtype = plan_variant(plan), line["dtype"]
+    short = kernel_name(variant, dtype)
+    kname, nf, fkib, cname, cfkib = _kernel_and_copy(fetch_dir, "FETCH_SIZE", short)
+    _, nw, wkib, _, cwkib = _kernel_and_copy(write_dir, "WRITE_SIZE", short)
+    copy_bytes = copy_mib * 1024 * 1024
+    fscale = copy_bytes / (cfkib * 1024.0)
+    wscale = copy_bytes / (cwkib * 1024.0)
+    fbytes = fkib * 1024.0 * fscale
+    wbytes = wkib * 1024.0 * wscale
+    alg = line["roofline"].get("algorithmic_bytes")
+    out = os.path.join(out_dir, "%s_%s_traffic.txt" % (short, workload))
+    with open(out, "w") as fh:
+        fh.write("# HBM traffic per launch of %s on %s (rocprofv3 --pmc, scaled by a\n"
+                 "# plain device copy of %d MiB run at the end of the same program)\n"
+                 % (short, workload, copy_mib))
+        for k, v in [("kernel", short), ("workload", workload), ("plan", plan),
+                     ("source_fingerprint", fingerprint(variant, dtype)),
+                     ("command_fetch", command_fetch), ("command_write", command_write),
+                     ("kernel_name", kname), ("fetch_dispatches", nf), ("write_dispatches", nw),
+                     ("fetch_kib_per_dispatch", "%.3f" % fkib),
+                     ("write_kib_per_dispatch", "%.3f" % wkib),
+                     ("copy_kernel_name", cname), ("copy_bytes", copy_bytes),
+                     ("copy_fetch_kib", "%.3f" % cfkib), ("copy_write_kib", "%.3f" % cwkib),
+                     ("fetch_scale", "%.5f" % fscale), ("write_scale", "%.5f" % wscale),
+                     ("fetch_bytes", "%.0f" % fbytes), ("write_bytes", "%.0f" % wbytes),
+                     ("traffic_bytes", "%.0f" % (fbytes + wbytes)),
+                     ("algorithmic_bytes", alg if alg is not None else "n/a")]:
+            fh.write("%s: %s\n" % (k, v))
+    return out
+
+
+def read_traffic(kernel: str, workload: str, plan: str, variant: str, dtype: str):
+    """Scaled HBM bytes per launch from the committed traffic summary, or None
+    when there is none or when the kernel's sources or plan changed since."""
+    path = os.path.join(PROFILES, "%s_%s_traffic.txt" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for ln in fh:
+            if ln.startswith("#") or ":" not in ln:
+                continue
+            k, v = ln.split(":", 1)
+            kv[k.strip()] = v.strip()
+    try:
+        if kv.get("plan") != plan or kv.get("source_fingerprint") != fingerprint(variant, dtype):
+            return None
+        return {"bytes": float(kv["traffic_bytes"]), "fetch_bytes": float(kv["fetch_bytes"]),
+                "write_bytes": float(kv["write_bytes"])}
+    except (KeyError, ValueError, FileNotFoundError):
+        return None
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(prog="python -m conv2d_backward_amd.profiling")
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("--run-dir", required=True)
+    s.add_argument("--bench-log", required=True)
+    s.add_argument("--workload", required=True)
+    s.add_argument("--command", required=True)
+    s.add_argument("--out-dir", default=PROFILES)
+    s.add_argument("--plain-bench-log", default=None,
+                   help="log of a bench.py run without the profiler, for comparison")
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch-dir", required=True)
+    t.add_argument("--write-dir", required=True)
+    t.add_argument("--bench-log", required=True)
+    t.add_argument("--workload", required=True)
+    t.add_argument("--copy-mib", type=int, required=True)
+    t.add_argument("--command-fetch", required=True)
+    t.add_argument("--command-write", required=True)
+    t.add_argument("--out-dir", default=PROFILES)
+    a = ap.parse_args(argv)
+    if a.cmd == "stats":
+        print(write_stats(a.run_dir, a.bench_log, a.workload, a.command, a.out_dir,
+                          plain_log=a.plain_bench_log))
+    else:
+        print(write_traffic(a.fetch_dir, a.write_dir, a.bench_log, a.workload, a.copy_mib,
+                            a.command_fetch, a.command_write, a.out_dir))
+
+
+if __name__ == "__main__":
+    main()

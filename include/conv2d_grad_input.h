@@ -165,9 +165,10 @@ CONV2D_GI_API int conv2d_gi_plan(const conv2d_gi_params *p, int dtype_bf16, char
 
 /*
  * Measurement hook: when both events are non-NULL, later calls from this
- * thread record `begin` on their stream just before the first GEMM kernel
- * launch and `end` just after the last one, so the caller can time the
- * contraction kernels apart from the weight reorder that precedes them.
+ * thread launch their first contraction kernel so that it records `begin`
+ * with the dispatch's own start time and their last one so that it records
+ * `end` with its completion time (hipExtLaunchKernelGGL), so the caller can
+ * time the contraction kernels apart from the reorder prologues before them.
  * NULL, NULL switches it off.  The events (hipEvent_t) stay the caller's.
  */
 CONV2D_GI_API void conv2d_gi_set_profile_events(hipEvent_t begin, hipEvent_t end);

@@ -1,0 +1,87 @@
+"""Host logic of the rocprofv3 summaries (no GPU): counter parsing, the
+copy-kernel scaling, and that bench.py's traffic figure is dropped once the
+kernel's sources or plan no longer match the summary."""
+import csv
+import json
+import os
+
+import pytest
+
+from conv2d_backward_amd import profiling
+
+PLAN = "variant=halo dtype=f32 ws_bytes=1 launches=1 [tile=14x14]"
+KNAME = "void gi::(anonymous namespace)::gi_halo_f32<13, 2, 512u, 1, 2>(gi::HaloArgs)"
+COPY = "__amd_rocclr_copyBuffer"
+
+
+def _counter_csv(path, counter, rows):
+    """rows: (kernel name, per-instance values) in dispatch order."""
+    os.makedirs(path, exist_ok=True)
+    with open(os.path.join(path, "run_counter_collection.csv"), "w", newline="") as fh:
+        w = csv.writer(fh)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        for d, (name, vals) in enumerate(rows, 1):
+            for v in vals:
+                w.writerow([d, name, counter, v])
+
+
+def _bench_log(path, workload="resnet_stage_3x3"):
+    line = {"dtype": "f32", "config": {"plan": PLAN, "workload": workload},
+            "roofline": {"algorithmic_bytes": 1000, "kernel_ms": 0.08},
+            "steps": 3, "warmup": 1}
+    with open(path, "w") as fh:
+        fh.write("noise\n" + json.dumps(line) + "\n")
+
+
+def test_traffic_scaled_by_copy(tmp_path):
+    mib = 4
+    copy_b = mib * 1024 * 1024
+    # The copy reads copy_b bytes but its FETCH counter says half (in KiB);
+    # writes read exactly.  Values of several hardware instances add up.
+    fetch_rows = [("other", [7.0]), (KNAME, [100.0, 100.0]), (KNAME, [300.0, 100.0])]
+    fetch_rows += [(COPY, [copy_b / 2048 / 2, copy_b / 2048 / 2])] * 3
+    write_rows = [(KNAME, [50.0]), (KNAME, [50.0])] + [(COPY, [copy_b / 1024])] * 3
+    _counter_csv(str(tmp_path / "f"), "FETCH_SIZE", fetch_rows)
+    _counter_csv(str(tmp_path / "w"), "WRITE_SIZE", write_rows)
+    _bench_log(str(tmp_path / "b.log"))
+    out = profiling.write_traffic(str(tmp_path / "f"), str(tmp_path / "w"),
+                                  str(tmp_path / "b.log"), "wl", mib, "cf", "cw",
+                                  out_dir=str(tmp_path))
+    kv = dict(ln.split(": ", 1) for ln in open(out).read().splitlines()
+              if not ln.startswith("#"))
+    assert float(kv["fetch_kib_per_dispatch"]) == pytest.approx(300.0)
+    assert float(kv["fetch_scale"]) == pytest.approx(2.0, rel=1e-4)
+    assert float(kv["write_scale"]) == pytest.approx(1.0, rel=1e-4)
+    assert float(kv["fetch_bytes"]) == pytest.approx(300 * 1024 * 2, rel=1e-4)
+    assert float(kv["write_bytes"]) == pytest.approx(50 * 1024, rel=1e-4)
+    assert kv["fetch_dispatches"] == "2"
+
+
+def test_traffic_rejects_missing_copies(tmp_path):
+    _counter_csv(str(tmp_path / "f"), "FETCH_SIZE", [(KNAME, [1.0])] * 4)
+    _counter_csv(str(tmp_path / "w"), "WRITE_SIZE", [(KNAME, [1.0])] * 4)
+    _bench_log(str(tmp_path / "b.log"))
+    with pytest.raises(ValueError):
+        profiling.write_traffic(str(tmp_path / "f"), str(tmp_path / "w"),
+                                str(tmp_path / "b.log"), "wl", 4, "a", "b",
+                                out_dir=str(tmp_path))
+
+
+def test_read_traffic_checks_plan_and_sources(tmp_path, monkeypatch):
+    monkeypatch.setattr(profiling, "PROFILES", str(tmp_path))
+    fp = profiling.fingerprint("halo", "f32")
+    path = tmp_path / "gi_halo_f32_wl_traffic.txt"
+    path.write_text("# x\nplan: %s\nsource_fingerprint: %s\ntraffic_bytes: 123\n"
+                    "fetch_bytes: 100\nwrite_bytes: 23\n" % (PLAN, fp))
+    got = profiling.read_traffic("gi_halo_f32", "wl", PLAN, "halo", "f32")
+    assert got == {"bytes": 123.0, "fetch_bytes": 100.0, "write_bytes": 23.0}
+    # Another plan, or sources that changed since: no figure.
+    assert profiling.read_traffic("gi_halo_f32", "wl", PLAN + " ", "halo", "f32") is None
+    path.write_text(path.read_text().replace(fp, "0" * 16))
+    assert profiling.read_traffic("gi_halo_f32", "wl", PLAN, "halo", "f32") is None
+    assert profiling.read_traffic("gi_halo_f32", "none", PLAN, "halo", "f32") is None
+
+
+def test_fingerprint_covers_every_kernel():
+    seen = {profiling.fingerprint(v, d) for v, d in profiling.KERNEL_SOURCES}
+    assert len(seen) == 4   # generic f32 and bf16 share one source file
