@@ -335,8 +335,6 @@ bool plan_halo_bf16(const conv2d_gi_params &p, HaloBf16Plan &out) {
     static const int kNBW[] = {4, 7};
     bool found = false;
     for (int nbw : kNBW) {
-        const int cfg = gi::halo_bf16_config(nbw, T);
-        if (cfg < 0) continue;
         const int maxpx = 2 * nbw * 16;
         for (int cdiv = 1; cdiv <= 8; ++cdiv) {
             const int TC = (p.W + cdiv - 1) / cdiv;
@@ -344,11 +342,12 @@ bool plan_halo_bf16(const conv2d_gi_params &p, HaloBf16Plan &out) {
             if (TC > maxpx) continue;
             for (int TR = std::min(maxpx / TC, p.H); TR >= 1; --TR) {
                 const int HR = TR + p.kH - 1, HC = TC + p.kW - 1;
-                const int QR = (HC + 15) / 16;
-                if (HR * QR > 32) continue;
-                // Row pitch: room for QR loads of 16 positions, and = TC mod 16.
-                const int HP = round_to_residue(QR * 16, 16, TC % 16);
-                if ((size_t)2 * HR * HP * 64 > kLdsBytes / 2) continue;
+                // Row pitch: holds a halo row, and = TC mod 16.
+                const int HP = round_to_residue(HC, 16, TC % 16);
+                const int nql = (HR * HP + 63) / 64;
+                if (nql > gi::kHaloBf16Loads) continue;
+                const int cfg = gi::halo_bf16_config(nbw, p.kH, p.kW, HP);
+                if (cfg < 0) continue;
                 const int64_t tiles = (int64_t)((p.H + TR - 1) / TR) * ((p.W + TC - 1) / TC) * p.N;
                 if (tiles > INT32_MAX) continue;
                 const int64_t wgs = tiles * ci_tiles;
@@ -371,7 +370,8 @@ bool plan_halo_bf16(const conv2d_gi_params &p, HaloBf16Plan &out) {
                     a.row_tiles = (p.H + TR - 1) / TR;
                     a.col_tiles = (p.W + TC - 1) / TC;
                     a.HP = HP;
-                    a.QR = QR;
+                    a.nql = nql;
+                    a.PS = nql * 1024;
                 }
             }
         }
@@ -393,7 +393,7 @@ bool plan_halo_bf16(const conv2d_gi_params &p, HaloBf16Plan &out) {
     a.gp_bytes = (uint32_t)gp_bytes;
     a.wk_bytes = (uint32_t)wk_bytes;
     a.d_bytes = (uint32_t)((int64_t)p.N * p.Ci * p.H * p.W * 4);
-    out.lds = (size_t)2 * a.HR * a.HP * 64;
+    out.lds = (size_t)2 * 4 * a.PS + 1024;  // 2 stages of 4 planes + a scratch kilobyte
     out.gp_bytes = (size_t)(gp_bytes + 255) / 256 * 256;
     out.wk_bytes = (size_t)wk_bytes;
     return true;
@@ -553,8 +553,8 @@ int run(const T *grad_out, const T *weight, float *dst, const conv2d_gi_params *
             HaloBf16Plan &h = plan.hb;
             uint16_t *gp = (uint16_t *)ws;
             uint16_t *wk = (uint16_t *)((char *)ws + h.gp_bytes);
-            e = gi::launch_pad_nhwc_bf16((const uint16_t *)grad_out, gp, h.args, p->oH, p->oW,
-                                         p->pad_h, p->pad_w, stream);
+            e = gi::launch_pad_planes_bf16((const uint16_t *)grad_out, gp, h.args, p->oH, p->oW,
+                                           p->pad_h, p->pad_w, stream);
             if (e == hipSuccess)
                 e = gi::launch_weight_frag_bf16((const uint16_t *)weight, wk, h.args, h.ci_tiles,
                                                 stream);
@@ -646,7 +646,8 @@ std::string describe(const Plan &plan, bool bf16) {
         s += " launches=3 [cfg=" + std::to_string(h.cfg) + " tile=" + std::to_string(a.TR) + "x" +
              std::to_string(a.TC) + " wgs=" + std::to_string(h.tiles) + "x" +
              std::to_string(h.ci_tiles) + " lds=" + std::to_string(h.lds) +
-             " halo=" + std::to_string(a.HR) + "x" + std::to_string(a.HC) +
+             " halo=" + std::to_string(a.HR) + "x" + std::to_string(a.HC) + " pitch=" +
+             std::to_string(a.HP) +
              " chunks=" + std::to_string(a.nchunks) + "]";
         return s;
     }

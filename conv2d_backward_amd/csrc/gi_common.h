@@ -105,15 +105,17 @@ namespace gi {
 
 // Arguments of the bf16 halo kernel (stride 1).
 //
-// gp: grad_out as zero-padded NHWC bf16, gp[N][YP][XP][Cop] with
-//     YP = H + kH - 1, XP = W + kW - 1, Cop = nchunks * 32: element (y, x)
+// gp: grad_out as zero-padded planes of 8 channels, bf16,
+//     gp[N][nchunks][4][YP][XP][8] with YP = H + kH - 1, XP = W + kW - 1:
+//     plane g of chunk c holds channels 32c + 8g .. +7, and position (y, x)
 //     holds grad_out[oh = y - (kH-1-pad_h)][ow = x - (kW-1-pad_w)] (zero
-//     outside the image), so tap (kh, kw) of input pixel (ih, iw) reads
-//     gp[ih + kH-1-kh][iw + kW-1-kw].
+//     outside the image or past Co), so tap (kh, kw) of input pixel (ih, iw)
+//     reads position (ih + kH-1-kh, iw + kW-1-kw).
 // wk: weights in the lane order of the MFMA A fragments,
 //     wk[ci tile][chunk][tap][ci block of 16][lane][8]: lane l holds the 8
 //     output channels chunk*32 + 8*(l/16) + e of input channel
 //     tile*64 + block*16 + l%16 (zero past Ci or Co).
+constexpr int kHaloBf16Loads = 8;   // most 64-position halo loads per plane
 struct HaloBf16Args {
     const uint16_t *gp;
     const uint16_t *wk;
@@ -123,11 +125,11 @@ struct HaloBf16Args {
     int32_t YP, XP, Cop, nchunks;
     int32_t TR, TC, row_tiles, col_tiles;
     int32_t HR, HC;         // halo rows / columns: TR + kH - 1, TC + kW - 1
-    int32_t HP;             // LDS pitch of a halo row in positions: a multiple of 16
-                            // holding HC, congruent to TC mod 16 (see the kernel)
-    int32_t QR;             // direct loads of 16 positions per halo row: ceil(HC / 16)
+    int32_t HP;             // LDS pitch of a halo row in positions: at least HC,
+                            // congruent to TC mod 16 (see the kernel)
+    int32_t nql;            // 64-position loads per plane: ceil(HR * HP / 64) <= 8
+    int32_t PS;             // LDS bytes per plane: nql * 1024
     int32_t ci_tiles;       // ceil(Ci / 64); grid = tiles * ci_tiles (1-D, xcd_order)
-    int32_t pad_;
 };
 
 }  // namespace gi

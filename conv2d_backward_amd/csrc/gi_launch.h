@@ -59,13 +59,14 @@ hipError_t launch_weight_image_f32(const float *w, float *wk, const HaloArgs &a,
                                    int ci_tiles, int64_t total, hipStream_t s);
 
 // bf16 halo kernel (kernels_halo_bf16.hip), stride 1.  Instantiations are
-// indexed by (NBW pixel blocks of 16 per wave, tap count T); -1 when none.
-int halo_bf16_config(int nbw, int taps);
+// indexed by (NBW pixel blocks of 16 per wave, kH x kW taps, halo pitch hp):
+// some fix the kernel width and pitch at compile time; -1 when none serves.
+int halo_bf16_config(int nbw, int kH, int kW, int hp);
 hipError_t launch_halo_bf16(const HaloBf16Args &a, int cfg, int tiles, int ci_tiles, size_t lds,
                             hipStream_t s, const KernelEvents &ev);
 // Prologues of the bf16 halo kernel (layouts in gi_common.h).
-hipError_t launch_pad_nhwc_bf16(const uint16_t *g, uint16_t *gp, const HaloBf16Args &a, int oH,
-                                int oW, int pad_h, int pad_w, hipStream_t s);
+hipError_t launch_pad_planes_bf16(const uint16_t *g, uint16_t *gp, const HaloBf16Args &a, int oH,
+                                  int oW, int pad_h, int pad_w, hipStream_t s);
 hipError_t launch_weight_frag_bf16(const uint16_t *w, uint16_t *wk, const HaloBf16Args &a,
                                    int ci_tiles, hipStream_t s);
 

@@ -6,23 +6,34 @@
 // with K ordered (chunk of 32 output channels, tap, channel).  The bf16 matrix
 // cores take 8 consecutive k per lane from both operands, so both operands are
 // laid out output-channel-minor by two prologues:
-//   * grad_out -> zero-padded NHWC copy (the zero border is the transposed
-//     padding kH-1-pad of the shader's header comment), so a halo position's
-//     32 channels of a chunk are one 64-byte run;
+//   * grad_out -> zero-padded planes of 8 channels (gi_common.h): the zero
+//     border is the transposed padding kH-1-pad of the shader's header
+//     comment, and a plane row is one contiguous run of 16-byte positions;
 //   * weight   -> the exact lane order of the MFMA A fragments.
 //
 // Work-group: 256 threads = 2 x 2 waves over 64 input channels x a TR x TC
 // pixel tile of one image.  Wave (wm, wn) owns input-channel blocks 2wm, 2wm+1
 // (16 each) and pixel blocks wn*NBW .. wn*NBW + NBW - 1 (16 pixels each).
-// Per chunk the tile's halo, (TR+kH-1) x (TC+kW-1) positions x 32 channels,
-// is copied into LDS by direct global -> LDS loads (double-buffered), and tap
-// (kh, kw) reads its B fragments as the halo shifted by (kH-1-kh, kW-1-kw).
-// A fragments are loaded from the weight image straight into registers,
-// several taps ahead.  LDS holds a position's four 16-byte channel groups in slots
-// permuted by (position / 4) mod 4, and halo rows sit HP positions apart with
-// HP = TC (mod 16): 16 lanes reading 16 consecutive pixels of the tile (which
-// may wrap to the next tile row) then read 16 positions that are consecutive
-// mod 16, i.e. 16 different bank groups.
+// Per chunk of 32 output channels the tile's halo, (TR+kH-1) x (TC+kW-1)
+// positions, is copied into LDS by direct global -> LDS loads (double-
+// buffered; wave w copies channel plane w), and tap (kh, kw) reads its B
+// fragments as the halo shifted by (kH-1-kh, kW-1-kw) positions.  A fragments
+// are loaded from the weight image straight into registers, several taps
+// ahead.  The loop carries almost no vector arithmetic: a B read is a per-lane
+// base address plus the tap's shift, a compile-time immediate when the halo
+// pitch and kernel width are template parameters; the chunk parts of the
+// global offsets are scalar.
+//
+// LDS banks: a 16-byte-per-lane LDS read is served 16 lanes per cycle (64
+// banks of 4 bytes, i.e. 16 bank groups of 16 bytes).  Measured on gfx950:
+// within each half of the wave, the lanes whose index bits 2, 3 and 4 have
+// even parity form one cycle and the odd ones the other.  LDS holds each
+// channel plane separately (plane offsets a multiple of 256 bytes) with halo
+// rows HP positions apart, HP = TC (mod 16): the 16 pixels of a block (which
+// may wrap to the next tile row) sit at 16 positions that are consecutive mod
+// 16 whatever the tap shift, so every cycle's 16 lanes (8 of one channel
+// plane, 8 of the other, covering all 16 pixels) touch 16 different bank
+// groups.
 //
 // V_MFMA_F32_16X16X32_BF16: lane l = 16*g + i supplies A[i][k = 8g .. 8g+7]
 // and B[k = 8g .. 8g+7][i] and receives D[4g + r][i], r = 0..3.
@@ -41,7 +52,7 @@ namespace {
 
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9)
 constexpr int kOOB = 0x7ffffff0;         // byte offset past the end of every buffer
-constexpr int kQW = 8;                   // halo direct loads per wave per chunk (<= 32 rows)
+constexpr int kQW = kHaloBf16Loads;      // halo direct loads per wave per chunk
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
@@ -49,7 +60,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint3
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (long)bytes, kRsrcWord3);
 }
 
-template <int NBW, int T>
+// NBW pixel blocks per wave, T taps; KW > 0: kernel width and HPT halo pitch
+// known at compile time (they must equal A.kW and A.HP), else read from A.
+template <int NBW, int T, int KW, int HPT>
 __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void gi_halo_bf16(
     const HaloBf16Args A) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -58,6 +71,9 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int j16 = lane & 15, g = lane >> 4;
     const int wm = wave & 1, wn = wave >> 1;
+    const int HP = HPT > 0 ? HPT : A.HP;
+    const int kW = KW > 0 ? KW : A.kW;
+    const int kH = KW > 0 ? T / KW : A.kH;
 
     // Logical order: input-channel tile fastest, then column, row, image.
     const int J = xcd_order(blockIdx.x, gridDim.x);
@@ -68,59 +84,71 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     const int rt = t % A.row_tiles;
     const int n = t / A.row_tiles;
     const int a0 = rt * A.TR, b0 = ct * A.TC;
-    const int nq = A.HR * A.QR;           // direct loads per chunk (16 positions each)
-    const int stage = A.HR * A.HP * 64;  // bytes per LDS stage
+    const int stage = 4 * A.PS;              // bytes per LDS stage: 4 planes
+    unsigned char *const dummy = smem + 2 * stage;
 
     const __amdgpu_buffer_rsrc_t grs = make_rsrc(A.gp, A.gp_bytes);
     const __amdgpu_buffer_rsrc_t wrs = make_rsrc(A.wk, A.wk_bytes);
     const __amdgpu_buffer_rsrc_t drs = make_rsrc(A.dst, A.d_bytes);
 
-    // This lane's pixel in each of its blocks: halo position (0 outside the
-    // tile or image: a valid position whose column is never stored).
-    int ppos[NBW];
+    // Halo direct loads: wave w copies plane w (channels 8w .. 8w+7 of the
+    // chunk); its load k covers LDS positions 64k .. 64k+63 of the plane,
+    // lane -> position 64k + lane = (row, column) with pitch HP.  Positions
+    // past the halo's columns or the padded image read zeros.  The chunk part
+    // of the offset is scalar.
+    int goff[kQW];
+#pragma unroll
+    for (int k = 0; k < kQW; ++k) {
+        const int pos = 64 * k + lane;
+        const int hr = pos / HP, hc = pos - (pos / HP) * HP;
+        const int y = a0 + hr, x = b0 + hc;
+        const bool v = hr < A.HR && hc < A.HC && y < A.YP && x < A.XP;
+        goff[k] = v ? (((n * A.nchunks * 4 + wave) * A.YP + y) * A.XP + x) * 16 : kOOB;
+    }
+    const int chunk_bytes = 4 * A.YP * A.XP * 16;
+    // Every wave issues exactly kQW loads per chunk, also past the last chunk
+    // (the surplus ones read zeros into a scratch kilobyte of LDS nobody
+    // reads), so the number of loads in flight is known at compile time and
+    // the compiler's wait counts stay exact.
+    auto issue = [&](int chunk, int buf) {
+        const bool live = chunk < A.nchunks;
+        const int soff = live ? chunk * chunk_bytes : 0;
+#pragma unroll
+        for (int k = 0; k < kQW; ++k) {
+            const bool real = live && k < A.nql;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                grs, (lds_ptr_t)(real ? smem + buf * stage + wave * A.PS + k * 1024 : dummy), 16,
+                real ? goff[k] : kOOB, soff, 0, 0);
+        }
+    };
+
+    // A fragments: weight image offset of (chunk, tap, block 2wm + cb); the
+    // per-lane part is the vector offset, the rest scalar.  Past the last
+    // chunk the offset is out of range (the load returns zeros): every
+    // prefetch is issued unconditionally, so the compiler's wait counts stay
+    // exact (a conditional load it cannot count would make it wait for every
+    // later load too).
+    const int wlane = (ci_tile * A.nchunks * T * 4 + 2 * wm) * 1024 + lane * 16;
+    auto aload = [&](int chunk, int tap, int cb) {
+        const int soff = chunk < A.nchunks ? ((chunk * T + tap) * 4 + cb) * 1024 : kOOB;
+        return __builtin_bit_cast(v8bf, __builtin_amdgcn_raw_buffer_load_b128(wrs, wlane, soff, 0));
+    };
+
+    // This lane's pixel in each of its blocks: LDS byte offset of its halo
+    // position in plane g of stage 0.  Outside the tile or image the lane reads
+    // position j16 (its column is never stored; distinct positions keep the
+    // read conflict-free) when every tap's shift keeps that inside the plane,
+    // else position 0.
+    const int max_shift = (kH - 1) * HP + (kW - 1);
+    const int inv = j16 + max_shift < A.nql * 64 ? j16 : 0;
+    int bbase[NBW];
 #pragma unroll
     for (int b = 0; b < NBW; ++b) {
         const int p = (wn * NBW + b) * 16 + j16;
         const int r = p / A.TC, c = p - (p / A.TC) * A.TC;
         const bool v = p < A.TR * A.TC && a0 + r < A.H && b0 + c < A.W;
-        ppos[b] = v ? r * A.HP + c : 0;
+        bbase[b] = g * A.PS + (v ? r * HP + c : inv) * 16;
     }
-
-    // Halo DMA: load q covers halo row q / QR, columns 16 (q % QR) .. +15;
-    // lane -> (column + lane/4, slot lane%4) loads channel group
-    // slot ^ ((lds position / 4) & 3).
-    int goff[kQW];
-#pragma unroll
-    for (int i = 0; i < kQW; ++i) {
-        const int q = wave + 4 * i;
-        const int hr = q / A.QR, hc = (q - (q / A.QR) * A.QR) * 16 + (lane >> 2);
-        const int lpos = hr * A.HP + hc;
-        const int slot = lane & 3;
-        const int kg = slot ^ ((lpos >> 2) & 3);
-        const int y = a0 + hr, x = b0 + hc;
-        const bool v = q < nq && hc < A.HC && y < A.YP && x < A.XP;
-        goff[i] = v ? (((n * A.YP + y) * A.XP + x) * A.Cop + 8 * kg) * 2 : kOOB;
-    }
-    auto issue = [&](int chunk, int buf) {
-#pragma unroll
-        for (int i = 0; i < kQW; ++i) {
-            const int q = wave + 4 * i;
-            if (q < nq) {
-                const int hr = q / A.QR, u = q - (q / A.QR) * A.QR;
-                const int off = goff[i] == kOOB ? kOOB : goff[i] + chunk * 64;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    grs, (lds_ptr_t)(smem + buf * stage + (hr * A.HP + u * 16) * 64), 16, off, 0,
-                    0, 0);
-            }
-        }
-    };
-
-    // A fragments: weight image offset of (chunk, tap, block 2wm + cb).
-    const int wlane = (ci_tile * A.nchunks * T * 4 + 2 * wm) * 1024 + lane * 16;
-    auto aload = [&](int chunk, int tap, int cb) {
-        const int off = wlane + ((chunk * T + tap) * 4 + cb) * 1024;
-        return __builtin_bit_cast(v8bf, __builtin_amdgcn_raw_buffer_load_b128(wrs, off, 0, 0));
-    };
 
     v4f acc[2][NBW];
 #pragma unroll
@@ -128,13 +156,11 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 #pragma unroll
         for (int b = 0; b < NBW; ++b) acc[cb][b] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    // Tap shifts in halo positions.
-    int shift[T];
-#pragma unroll
-    for (int tp = 0; tp < T; ++tp) {
-        const int kh = tp / A.kW, kw = tp - (tp / A.kW) * A.kW;
-        shift[tp] = (A.kH - 1 - kh) * A.HP + (A.kW - 1 - kw);
-    }
+    // Byte shift of tap tp: (kH-1-kh) rows and (kW-1-kw) columns.
+    auto shift_bytes = [&](int tp) {
+        const int kh = tp / kW, kw = tp - (tp / kW) * kW;
+        return ((kH - 1 - kh) * HP + (kW - 1 - kw)) * 16;
+    };
 
     // A ring of T slots indexed by tap: step s = chunk*T + tap uses slot
     // s % T = tap (a compile-time index), and step s + AD is loaded while step
@@ -153,54 +179,54 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     __syncthreads();
     for (int chunk = 0; chunk < A.nchunks; ++chunk) {
         const int cur = chunk & 1;
-        if (chunk + 1 < A.nchunks) issue(chunk + 1, cur ^ 1);
-        const unsigned char *hs = smem + cur * stage;
-        // Per-lane positions, opaque to the optimiser so the tap x block
-        // addresses are formed inside the chunk instead of being hoisted out of
-        // the loop and held in registers.
-        int pp[NBW];
+        issue(chunk + 1, cur ^ 1);
+        // Per-lane addresses of this stage, opaque to the optimiser so the
+        // tap x block addresses are a base register plus an immediate instead
+        // of registers held across the loop.
+        int bb[NBW];
 #pragma unroll
         for (int b = 0; b < NBW; ++b) {
-            pp[b] = ppos[b];
-            asm volatile("" : "+v"(pp[b]));
+            bb[b] = bbase[b] + cur * stage;
+            asm volatile("" : "+v"(bb[b]));
         }
         v8bf fb[2][NBW];
         auto bfetch = [&](int tp, int sl) {
+            const int sh = shift_bytes(tp);
 #pragma unroll
-            for (int b = 0; b < NBW; ++b) {
-                const int pos = pp[b] + shift[tp];
-                const int slot = g ^ ((pos >> 2) & 3);
-                fb[sl][b] = *(const v8bf *)(hs + (pos * 4 + slot) * 16);
-            }
+            for (int b = 0; b < NBW; ++b) fb[sl][b] = *(const v8bf *)(smem + bb[b] + sh);
         };
         bfetch(0, 0);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int tp = 0; tp < T; ++tp) {
             const int sl = tp & 1;
-            const int as = tp;
             // Prefetch: A of step + AD, B of the next tap.
             {
                 const int t2 = tp + AD;
                 const int c2 = t2 < T ? chunk : chunk + 1;
                 const int t2m = t2 < T ? t2 : t2 - T;
-                if (c2 < A.nchunks) {
-                    fa[t2m][0] = aload(c2, t2m, 0);
-                    fa[t2m][1] = aload(c2, t2m, 1);
-                }
+                fa[t2m][0] = aload(c2, t2m, 0);
+                fa[t2m][1] = aload(c2, t2m, 1);
             }
             if (tp + 1 < T) bfetch(tp + 1, sl ^ 1);
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
                 for (int b = 0; b < NBW; ++b)
-                    acc[cb][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[as][cb], fb[sl][b],
+                    acc[cb][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[tp][cb], fb[sl][b],
                                                                          acc[cb][b], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        // The next chunk's halo must have landed before the barrier.  Loads
+        // complete in issue order and the halo loads were issued before this
+        // chunk's A prefetches, so it is enough that at most the 2*AD most
+        // recent loads (the A fragments of the next chunk's first AD taps)
+        // are still in flight: they stay in flight across the barrier.
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * AD) : "memory");
         __syncthreads();
     }
+    // Nothing may still write this work-group's LDS when it ends.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // Epilogue: D[4g + r][j16] of each block, NCHW fp32.
     const int plane = A.H * A.W;
@@ -223,30 +249,35 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     }
 }
 
-template <int NBW, int T>
+template <int NBW, int T, int KW, int HPT>
 hipError_t launch_one(const HaloBf16Args &a, int tiles, int ci_tiles, size_t lds, hipStream_t s,
                       const KernelEvents &ev) {
+    if ((KW > 0 && (a.kW != KW || a.kH * a.kW != T)) || (HPT > 0 && a.HP != HPT))
+        return hipErrorInvalidValue;
     if (lds > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute((const void *)gi_halo_bf16<NBW, T>,
+        hipError_t e = hipFuncSetAttribute((const void *)gi_halo_bf16<NBW, T, KW, HPT>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
     if (a.ci_tiles != ci_tiles) return hipErrorInvalidValue;
-    hipExtLaunchKernelGGL((gi_halo_bf16<NBW, T>), dim3(tiles * ci_tiles), dim3(256), (uint32_t)lds,
-                          s, ev.start, ev.stop, 0, a);
+    hipExtLaunchKernelGGL((gi_halo_bf16<NBW, T, KW, HPT>), dim3(tiles * ci_tiles), dim3(256),
+                          (uint32_t)lds, s, ev.start, ev.stop, 0, a);
     return hipGetLastError();
 }
 
-constexpr int kCfg[][2] = {{7, 9}, {4, 9}, {7, 3}, {4, 3}};
+// Instantiations: pixel blocks per wave, taps, and (kernel width, halo pitch)
+// when fixed at compile time (0: read at run time).  The first serves 3 x 3
+// kernels on 14-wide tiles (pitch 30).
+constexpr int kCfg[][4] = {{7, 9, 3, 30}, {7, 9, 0, 0}, {4, 9, 0, 0}, {7, 3, 0, 0}, {4, 3, 0, 0}};
 
-// grad_out NCHW bf16 -> zero-padded NHWC bf16.  One work-group per (image n,
-// block of 64 channels, band of RB rows of gp): the band is read along ow
-// (coalesced), packed into channel pairs in LDS, and written as 16-byte runs
-// of 8 channels per position.
-__global__ __launch_bounds__(256) void pad_nhwc_bf16(const uint16_t *__restrict__ g,
-                                                     uint16_t *__restrict__ gp,
-                                                     const HaloBf16Args A, int oH, int oW,
-                                                     int pad_h, int pad_w, int RB) {
+// grad_out NCHW bf16 -> zero-padded channel planes (gi_common.h).  One
+// work-group per (image n, block of 64 channels, band of RB rows of gp): the
+// band is read along ow (coalesced), packed into channel pairs in LDS, and
+// written plane by plane as 16-byte positions (coalesced along x).
+__global__ __launch_bounds__(256) void pad_planes_bf16(const uint16_t *__restrict__ g,
+                                                       uint16_t *__restrict__ gp,
+                                                       const HaloBf16Args A, int oH, int oW,
+                                                       int pad_h, int pad_w, int RB) {
     extern __shared__ uint32_t band[];  // [RB][oW][33] channel pairs
     const int n = blockIdx.x, co0 = blockIdx.y * 64, y0 = blockIdx.z * RB;
     const int yoff = A.kH - 1 - pad_h;  // oh = y - yoff
@@ -285,20 +316,23 @@ __global__ __launch_bounds__(256) void pad_nhwc_bf16(const uint16_t *__restrict_
         }
     }
     __syncthreads();
-    const int groups = min(8, (A.Cop - co0) / 8);  // 16-byte groups of 8 channels
-    const int nstore = RB * A.XP * 8;
-    for (int e = threadIdx.x; e < nstore; e += 256) {
-        const int q = e & 7, pos = e >> 3;
-        const int ry = pos / A.XP, x = pos - (pos / A.XP) * A.XP;
-        const int y = y0 + ry;
-        if (q >= groups || y >= A.YP) continue;
+    // Plane q (channels co0 + 8q .. +7) of each band row: consecutive threads
+    // take consecutive x of one row (16-byte stores, coalesced).
+    const int groups = min(8, (A.Cop - co0) / 8);  // planes in this block
+    const int rows = min(RB, A.YP - y0);
+    const int per_plane = rows * A.XP;
+    for (int e = threadIdx.x; e < groups * per_plane; e += 256) {
+        const int q = e / per_plane, rem = e - q * per_plane;
+        const int ry = rem / A.XP, x = rem - ry * A.XP;
+        const int co = co0 + 8 * q;
+        const int64_t pl = ((int64_t)n * A.nchunks + co / 32) * 4 + (co / 8) % 4;
         const int ow = x - xoff;
         uint4 v = {0u, 0u, 0u, 0u};
         if (ow >= 0 && ow < oW) {
             const uint32_t *src = band + (ry * oW + ow) * 33 + 4 * q;
             v = uint4{src[0], src[1], src[2], src[3]};
         }
-        *(uint4 *)(gp + (((int64_t)n * A.YP + y) * A.XP + x) * A.Cop + co0 + 8 * q) = v;
+        *(uint4 *)(gp + ((pl * A.YP + y0 + ry) * A.XP + x) * 8) = v;
     }
 }
 
@@ -355,25 +389,28 @@ __global__ __launch_bounds__(256) void weight_frag_bf16(const uint16_t *__restri
 
 }  // namespace
 
-int halo_bf16_config(int nbw, int taps) {
-    for (int i = 0; i < (int)(sizeof(kCfg) / sizeof(kCfg[0])); ++i)
-        if (kCfg[i][0] == nbw && kCfg[i][1] == taps) return i;
+int halo_bf16_config(int nbw, int kH, int kW, int hp) {
+    for (int i = 0; i < (int)(sizeof(kCfg) / sizeof(kCfg[0])); ++i) {
+        if (kCfg[i][0] != nbw || kCfg[i][1] != kH * kW) continue;
+        if (kCfg[i][2] == 0 || (kCfg[i][2] == kW && kCfg[i][3] == hp)) return i;
+    }
     return -1;
 }
 
 hipError_t launch_halo_bf16(const HaloBf16Args &a, int cfg, int tiles, int ci_tiles, size_t lds,
                             hipStream_t s, const KernelEvents &ev) {
     switch (cfg) {
-        case 0: return launch_one<7, 9>(a, tiles, ci_tiles, lds, s, ev);
-        case 1: return launch_one<4, 9>(a, tiles, ci_tiles, lds, s, ev);
-        case 2: return launch_one<7, 3>(a, tiles, ci_tiles, lds, s, ev);
-        case 3: return launch_one<4, 3>(a, tiles, ci_tiles, lds, s, ev);
+        case 0: return launch_one<7, 9, 3, 30>(a, tiles, ci_tiles, lds, s, ev);
+        case 1: return launch_one<7, 9, 0, 0>(a, tiles, ci_tiles, lds, s, ev);
+        case 2: return launch_one<4, 9, 0, 0>(a, tiles, ci_tiles, lds, s, ev);
+        case 3: return launch_one<7, 3, 0, 0>(a, tiles, ci_tiles, lds, s, ev);
+        case 4: return launch_one<4, 3, 0, 0>(a, tiles, ci_tiles, lds, s, ev);
         default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_pad_nhwc_bf16(const uint16_t *g, uint16_t *gp, const HaloBf16Args &a, int oH,
-                                int oW, int pad_h, int pad_w, hipStream_t s) {
+hipError_t launch_pad_planes_bf16(const uint16_t *g, uint16_t *gp, const HaloBf16Args &a, int oH,
+                                  int oW, int pad_h, int pad_w, hipStream_t s) {
     // Rows per work-group: at most what fits 16 KB of LDS, and few enough that
     // the grid has some 2048 work-groups to keep loads in flight.
     int RB = (int)(16384 / ((size_t)oW * 33 * sizeof(uint32_t)));
@@ -383,11 +420,11 @@ hipError_t launch_pad_nhwc_bf16(const uint16_t *g, uint16_t *gp, const HaloBf16A
     RB = RB < 1 ? 1 : (RB > a.YP ? a.YP : RB);
     const size_t lds = (size_t)RB * oW * 33 * sizeof(uint32_t);
     if (lds > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute((const void *)pad_nhwc_bf16,
+        hipError_t e = hipFuncSetAttribute((const void *)pad_planes_bf16,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(pad_nhwc_bf16, dim3(a.N, (a.Cop + 63) / 64, (a.YP + RB - 1) / RB),
+    hipLaunchKernelGGL(pad_planes_bf16, dim3(a.N, (a.Cop + 63) / 64, (a.YP + RB - 1) / RB),
                        dim3(256), lds, s, g, gp, a, oH, oW, pad_h, pad_w, RB);
     return hipGetLastError();
 }
