@@ -191,6 +191,13 @@ bool plan_halo(const conv2d_gi_params &p, const std::vector<Phase> &phases, Halo
         kall += (int64_t)nchunks * gi::kHaloBC * T;
         w_ci_stride += (int64_t)nchunks * T * 512;
     }
+    // The kernel-width tap count shared by every phase with taps (0 if not).
+    int jw_common = -1;
+    for (const Phase &ph : phases) {
+        if (ph.J_h * ph.J_w == 0) continue;
+        jw_common = jw_common < 0 || jw_common == ph.J_w ? ph.J_w : 0;
+    }
+    if (jw_common < 0) jw_common = 0;
     const int ci_tiles = (p.Ci + gi::kHaloCT - 1) / gi::kHaloCT;
     if (w_ci_stride * ci_tiles * 4 > lim || maxT == 0) return false;
     if (gi::weight_image_f32_lds(p.kH, p.kW) > kLdsBytes) return false;
@@ -210,13 +217,20 @@ bool plan_halo(const conv2d_gi_params &p, const std::vector<Phase> &phases, Halo
                 if (forced && (TR != f_tr || TR * TC > maxpx)) break;
                 if (!forced && nb > 4 && TR * TC <= (nb == 8 ? 4 : 8) * 16) break;
                 const int HR = TR + maxJh - 1, HC = TC + maxJw - 1;
+                // Halo row pitch: the padded one (= TC mod 16) puts the 16
+                // pixels of a block (which may wrap to the next tile row) at
+                // positions distinct mod 16, so the fragment reads of a
+                // half-wave are conflict-free; it costs LDS and staging.
+                for (int padded = 1; padded >= 0; --padded) {
+                const int HP = padded ? round_to_residue(HC, 16, TC % 16) : HC;
+                if (padded && HP == HC) continue;
                 // Halo positions are staged in groups of 32, the groups dealt
-                // round-robin to the 4 waves; the pitch sits 16 float2 off a
-                // multiple of 32 so the co-pair rows of a fragment read fall
-                // on disjoint banks.
-                const int groups = (HR * HC + 31) / 32;
+                // round-robin to the 4 waves; the co-pair pitch sits 16 float2
+                // off a multiple of 32 so the co-pair rows of a fragment read
+                // fall on disjoint banks.
+                const int groups = (HR * HP + 31) / 32;
                 const int bl = (groups + 3) / 4;
-                const int cfg = gi::halo_f32_config(nb, tmask, bl);
+                const int cfg = gi::halo_f32_config(nb, tmask, bl, HP, jw_common);
                 if (cfg < 0) continue;
                 const int HPc = round_to_residue(groups * 32, 32, 16);
                 const int cps = gi::halo_f32_cps(cfg);
@@ -245,16 +259,20 @@ bool plan_halo(const conv2d_gi_params &p, const std::vector<Phase> &phases, Halo
                 const int64_t wgs = tiles * ci_tiles;
                 // Busiest CU: ceil(work-groups / CUs) work-groups.  Measured
                 // efficiency of the instantiations: more pixel blocks per wave
-                // amortise more per-tap and per-chunk overhead, and a lone
-                // work-group per CU hides less latency.
+                // amortise more per-tap and per-chunk overhead, a lone
+                // work-group per CU hides less latency, and conflict-free
+                // fragment reads with compile-time tap offsets save time.
                 const int64_t per_cu = (wgs + kCUs - 1) / kCUs;
                 const double eff_nb = nb >= 13 ? 1.0 : nb >= 8 ? 0.85 : 0.75;
                 const double eff_occ = per_cu >= 2 ? 1.0 : 0.9;
+                const bool conflict_free = (HP - TC) % 16 == 0 || TC % 16 == 0;
+                const double eff_pitch = (gi::halo_f32_fixed_pitch(cfg) ? 1.05 : 1.0) *
+                                         (conflict_free ? 1.03 : 1.0);
                 // 16x16x4 MFMA: 32 cycles per 16 pixels x 4 k; plus halo staging.
                 const double per_wg = 8.0 * nb * kall +
-                                      (double)nchunks * phases.size() * HR * HC * 2.0 + 4000.0;
+                                      (double)nchunks * phases.size() * HR * HP * 2.0 + 4000.0;
                 // Among equal critical paths, fewer work-groups do less total work.
-                const double cost = (double)per_cu * per_wg / (eff_nb * eff_occ) +
+                const double cost = (double)per_cu * per_wg / (eff_nb * eff_occ * eff_pitch) +
                                     0.05 * (double)wgs * per_wg / kCUs;
                 if (!found || cost < out.cost) {
                     found = true;
@@ -271,8 +289,10 @@ bool plan_halo(const conv2d_gi_params &p, const std::vector<Phase> &phases, Halo
                     a.TC = TC;
                     a.row_tiles = (int)row_tiles;
                     a.col_tiles = (int)col_tiles;
+                    a.HP = HP;
                     a.HPc = HPc;
                     a.stages = stages;
+                }
                 }
             }
         }
@@ -658,7 +678,8 @@ std::string describe(const Plan &plan, bool bf16) {
              " bl=" + std::to_string(h.bl) + " tile=" + std::to_string(a.TR) + "x" +
              std::to_string(a.TC) + (a.fold ? " fold" : "") + " wgs=" + std::to_string(h.tiles) +
              "x" + std::to_string(h.ci_tiles) + " lds=" + std::to_string(h.lds) +
-             " HPc=" + std::to_string(a.HPc) + " stages=" + std::to_string(a.stages);
+             " HP=" + std::to_string(a.HP) + " HPc=" + std::to_string(a.HPc) +
+             " stages=" + std::to_string(a.stages);
         for (int i = 0; i < a.nphases; ++i) {
             const gi::HaloPhase &ph = a.ph[i];
             s += " phase(" + std::to_string(ph.rho_h) + "," + std::to_string(ph.rho_w) +

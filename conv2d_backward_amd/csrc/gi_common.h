@@ -91,6 +91,7 @@ struct HaloArgs {
     int32_t row_tiles, col_tiles;
     int32_t fold;           // 1: tile rows run across images (every phase has J_h <= 1)
     int32_t nchunks;        // ceil(Co / 8)
+    int32_t HP;             // halo row pitch in positions (>= TC + J_w - 1 of every phase)
     int32_t HPc;            // LDS pitch of one co pair's halo, in float2
     int32_t stages;         // LDS stages of the chunk pipeline (2 or 3)
     int32_t maxT;           // most taps of any phase

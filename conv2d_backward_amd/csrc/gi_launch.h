@@ -43,13 +43,17 @@ hipError_t launch_generic_bf16(const GemmArgs &a, int tiles_x, hipStream_t s,
 constexpr int kHaloBC = 8;     // output channels per LDS stage (chunk)
 constexpr int kHaloCT = 64;    // input channels per work-group
 unsigned halo_f32_tbit(int T);
-int halo_f32_config(int nb, unsigned tmask, int hg);
+// hp: halo row pitch in positions; jw: the kernel-width tap count shared by
+// every phase with taps (0 if they differ).
+int halo_f32_config(int nb, unsigned tmask, int hg, int hp, int jw);
 hipError_t launch_halo_f32(const HaloArgs &a, int cfg, int tiles, int ci_tiles, size_t lds,
                            hipStream_t s, const KernelEvents &ev);
 // Chunks of 8 output channels per LDS stage of instantiation cfg, and the LDS
 // bytes of the halo kernel: most taps of a phase, halo pitch (float2),
 // pipeline stages, chunks per stage.
 int halo_f32_cps(int cfg);
+// True when instantiation cfg has its halo pitch fixed at compile time.
+bool halo_f32_fixed_pitch(int cfg);
 size_t halo_f32_lds_bytes(int maxT, int HPc, int stages, int cps);
 
 // Weight image of the halo kernel (layout in gi_common.h); `total` floats.

@@ -113,7 +113,7 @@ __device__ __forceinline__ void wait_dma() {
 //   * halo: for co pair cp and a group of 32 positions, even lanes load
 //     output channel 2cp and odd lanes 2cp+1 of position base + lane/2, which
 //     lands exactly on the float2 layout.
-template <int T, int NB, int HG, int CPS>
+template <int T, int NB, int HG, int CPS, int PITCH, int JW>
 __device__ __forceinline__ void run_phase(const HaloArgs &A, const HaloPhase &P, v2f *smem2,
                                           const int (&pbase)[NB], v4f (&acc)[NB], int a0,
                                           int b0, int n_img, int ci_tile,
@@ -125,9 +125,15 @@ __device__ __forceinline__ void run_phase(const HaloArgs &A, const HaloPhase &P,
     const int l16 = lane & 15, g4 = lane >> 4;
     const int wreg = CPS * A.maxT * 256;
     const int stage_f2 = wreg + CPS * 4 * A.HPc;
-    const int HC = A.TC + P.J_w - 1;
-    const int HR = A.TR + P.J_h - 1;
-    const int hpos = HR * HC;
+    // Tap grid of the phase (compile time when JW is), halo extent, and the
+    // halo row pitch in LDS (compile time when PITCH is): every tap's shift
+    // is then an immediate offset of the fragment reads.
+    const int J_w = JW > 0 ? JW : P.J_w;
+    const int J_h = JW > 0 ? T / JW : P.J_h;
+    const int HP = PITCH > 0 ? PITCH : A.HP;
+    const int HC = A.TC + J_w - 1;
+    const int HR = A.TR + J_h - 1;
+    const int hpos = HR * HP;
     const int groups = (hpos + 31) / 32;
     const int oHW = A.oH * A.oW;
     const int nstages = (A.nchunks + CPS - 1) / CPS;
@@ -138,8 +144,8 @@ __device__ __forceinline__ void run_phase(const HaloArgs &A, const HaloPhase &P,
         int j = 0, jw = 0;
 #pragma unroll
         for (int t = 0; t < T; ++t) {
-            shift[t] = (P.J_h - 1 - j) * HC + (P.J_w - 1 - jw);
-            if (++jw == P.J_w) {
+            shift[t] = (J_h - 1 - j) * HP + (J_w - 1 - jw);
+            if (++jw == J_w) {
                 jw = 0;
                 ++j;
             }
@@ -152,9 +158,9 @@ __device__ __forceinline__ void run_phase(const HaloArgs &A, const HaloPhase &P,
 #pragma unroll
     for (int k = 0; k < HG; ++k) {
         const int pos = (wave + 4 * k) * 32 + (lane >> 1);
-        const int hr = pos / HC, hc = pos - (pos / HC) * HC;
-        const int ow = b0 + P.q_w - (P.J_w - 1) + hc;
-        bool v = pos < hpos && ow >= 0 && ow < A.oW;
+        const int hr = pos / HP, hc = pos - (pos / HP) * HP;
+        const int ow = b0 + P.q_w - (J_w - 1) + hc;
+        bool v = pos < hpos && hc < HC && ow >= 0 && ow < A.oW;
         int img, oh;
         if (A.fold) {
             const int R = a0 + hr;
@@ -163,7 +169,7 @@ __device__ __forceinline__ void run_phase(const HaloArgs &A, const HaloPhase &P,
             v = v && R < A.N * P.Ha;
         } else {
             img = n_img;
-            oh = a0 + P.q_h - (P.J_h - 1) + hr;
+            oh = a0 + P.q_h - (J_h - 1) + hr;
         }
         v = v && oh >= 0 && oh < A.oH;
         hoff[k] = v ? ((img * A.Co) * oHW + oh * A.oW + ow) * 4 : kOOB;
@@ -234,8 +240,11 @@ __device__ __forceinline__ void run_phase(const HaloArgs &A, const HaloPhase &P,
 #pragma unroll
         for (int o = 0; o < CPS; ++o) {
             if (CPS > 1 && stg * CPS + o >= A.nchunks) break;
-            const v2f *as =
-                smem2 + cur * stage_f2 + o * T * 256 + g4 * 64 + wave * 16 + l16;
+            // Odd co pairs hold their 64 input channels rotated by 16 (weight
+            // image layout), so the two co pairs of a half-wave fall on
+            // disjoint banks.
+            const v2f *as = smem2 + cur * stage_f2 + o * T * 256 + g4 * 64 +
+                            ((wave * 16 + l16 + 16 * (g4 & 1)) & 63);
             const v2f *hs = smem2 + cur * stage_f2 + wreg + (o * 4 + g4) * A.HPc;
             // Two fragment slots: tap t+1 is read from LDS while tap t's MFMAs
             // run.
@@ -273,7 +282,7 @@ __device__ __forceinline__ void run_phase(const HaloArgs &A, const HaloPhase &P,
     }
 }
 
-template <int NB, int HG, unsigned TMASK, int CPS, int OCC>
+template <int NB, int HG, unsigned TMASK, int CPS, int OCC, int PITCH, int JW>
 __global__ __launch_bounds__(256, OCC) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void gi_halo_f32(
     const HaloArgs A) {
     extern __shared__ __attribute__((aligned(16))) v2f smem2[];
@@ -305,19 +314,22 @@ __global__ __launch_bounds__(256, OCC) __attribute__((amdgpu_waves_per_eu(OCC, O
     for (int p = 0; p < A.nphases; ++p) {
         const HaloPhase P = A.ph[p];
         const int T = P.J_h * P.J_w;
-        const int HC = A.TC + P.J_w - 1;
+        const int HP = PITCH > 0 ? PITCH : A.HP;
 
-        // Halo position of this lane's pixel in each block (0 for a pixel
-        // outside the phase grid: it reads a valid position, its column is
-        // never stored).
+        // Halo position of this lane's pixel in each block.  A pixel outside
+        // the phase grid reads position l16 (its column is never stored;
+        // distinct positions keep the read conflict-free) when every tap's
+        // shift keeps that inside the halo plane, else position 0.
+        const int max_shift = (P.J_h - 1) * HP + (P.J_w - 1);
+        const int inv = l16 + max_shift < A.HPc ? l16 : 0;
         int pbase[NB];
 #pragma unroll
         for (int blk = 0; blk < NB; ++blk) {
             int img, a, b;
             const int px = blk * 16 + l16;
             pbase[blk] = tile_pixel(A, P, px, a0, b0, n_img, img, a, b)
-                             ? (px / A.TC) * HC + (px - (px / A.TC) * A.TC)
-                             : 0;
+                             ? (px / A.TC) * HP + (px - (px / A.TC) * A.TC)
+                             : inv;
         }
 
         v4f acc[NB];
@@ -327,7 +339,8 @@ __global__ __launch_bounds__(256, OCC) __attribute__((amdgpu_waves_per_eu(OCC, O
 #define GI_HALO_CASE(TT)                                                                     \
     case TT:                                                                                 \
         if constexpr ((TMASK & tbit(TT)) != 0)                                               \
-            run_phase<TT, NB, HG, CPS>(A, P, smem2, pbase, acc, a0, b0, n_img, ci_tile, grs, wrs); \
+            run_phase<TT, NB, HG, CPS, PITCH, JW>(A, P, smem2, pbase, acc, a0, b0, n_img, ci_tile, \
+                                                 grs, wrs);                                     \
         break;
         switch (T) {
             GI_HALO_CASE(1)
@@ -365,16 +378,20 @@ constexpr unsigned kT7 = tbit(7);
 constexpr unsigned kTs2 = tbit(1) | tbit(2) | tbit(4);
 constexpr unsigned kTall = tbit(1) | tbit(2) | tbit(3) | tbit(4) | tbit(6) | tbit(7) | tbit(9);
 
-template <int NB, int HG, unsigned TMASK, int CPS, int OCC>
+template <int NB, int HG, unsigned TMASK, int CPS, int OCC, int PITCH, int JW>
 hipError_t launch_one(const HaloArgs &a, int tiles, int ci_tiles, size_t lds, hipStream_t s,
                       const KernelEvents &ev) {
+    if (PITCH > 0 && a.HP != PITCH) return hipErrorInvalidValue;
+    for (int i = 0; JW > 0 && i < a.nphases; ++i)
+        if (a.ph[i].J_w != JW && a.ph[i].J_h * a.ph[i].J_w != 0) return hipErrorInvalidValue;
     if (lds > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute((const void *)gi_halo_f32<NB, HG, TMASK, CPS, OCC>,
+        hipError_t e = hipFuncSetAttribute(
+            (const void *)gi_halo_f32<NB, HG, TMASK, CPS, OCC, PITCH, JW>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
     if (a.ci_tiles != ci_tiles) return hipErrorInvalidValue;
-    hipExtLaunchKernelGGL((gi_halo_f32<NB, HG, TMASK, CPS, OCC>), dim3(tiles * ci_tiles),
+    hipExtLaunchKernelGGL((gi_halo_f32<NB, HG, TMASK, CPS, OCC, PITCH, JW>), dim3(tiles * ci_tiles),
                           dim3(256), (uint32_t)lds, s, ev.start, ev.stop, 0, a);
     return hipGetLastError();
 }
@@ -382,28 +399,36 @@ hipError_t launch_one(const HaloArgs &a, int tiles, int ci_tiles, size_t lds, hi
 // Instantiations: pixel blocks, halo groups of 32 positions per wave, tap
 // counts served, chunks of 8 output channels per LDS stage (the 4-chunk
 // kernel holds one work-group per CU by LDS, so it is compiled for one wave
-// per SIMD and the whole register file).
+// per SIMD and the whole register file), and the halo pitch and kernel width
+// when fixed at compile time (0: read at run time).  The first serves 3 x 3
+// stride-1 kernels on 14-wide tiles with the conflict-free pitch 30.
 struct HaloCfg {
     int nb, hg;
     unsigned tmask;
-    int cps;
+    int cps, pitch, jw;
 };
 constexpr HaloCfg kCfg[] = {
-    {13, 2, kT9, 1},   {13, 2, kTs2, 4}, {8, 2, kT7, 1},
-    {13, 4, kTall, 1}, {8, 4, kTall, 1}, {4, 4, kTall, 1},
+    {13, 4, kT9, 1, 30, 3}, {13, 2, kT9, 1, 0, 0},   {13, 2, kTs2, 4, 0, 0},
+    {8, 2, kT7, 1, 0, 0},   {13, 4, kTall, 1, 0, 0}, {8, 4, kTall, 1, 0, 0},
+    {4, 4, kTall, 1, 0, 0},
 };
 
 }  // namespace
 
 unsigned halo_f32_tbit(int T) { return T >= 0 && T < 32 ? tbit(T) : 0u; }
 
-int halo_f32_config(int nb, unsigned tmask, int hg) {
-    for (int i = 0; i < (int)(sizeof(kCfg) / sizeof(kCfg[0])); ++i)
-        if (kCfg[i].nb == nb && kCfg[i].hg >= hg && (kCfg[i].tmask & tmask) == tmask) return i;
+int halo_f32_config(int nb, unsigned tmask, int hg, int hp, int jw) {
+    for (int i = 0; i < (int)(sizeof(kCfg) / sizeof(kCfg[0])); ++i) {
+        const HaloCfg &c = kCfg[i];
+        if (c.nb != nb || c.hg < hg || (c.tmask & tmask) != tmask) continue;
+        if (c.pitch == 0 || (c.pitch == hp && c.jw == jw)) return i;
+    }
     return -1;
 }
 
 int halo_f32_cps(int cfg) { return kCfg[cfg].cps; }
+
+bool halo_f32_fixed_pitch(int cfg) { return kCfg[cfg].pitch > 0; }
 
 size_t halo_f32_lds_bytes(int maxT, int HPc, int stages, int cps) {
     // stages x (weights + halos of cps chunks), plus the kilobyte the
@@ -414,18 +439,20 @@ size_t halo_f32_lds_bytes(int maxT, int HPc, int stages, int cps) {
 hipError_t launch_halo_f32(const HaloArgs &a, int cfg, int tiles, int ci_tiles, size_t lds,
                            hipStream_t s, const KernelEvents &ev) {
     switch (cfg) {
-        case 0: return launch_one<13, 2, kT9, 1, 2>(a, tiles, ci_tiles, lds, s, ev);
-        case 1: return launch_one<13, 2, kTs2, 4, 1>(a, tiles, ci_tiles, lds, s, ev);
-        case 2: return launch_one<8, 2, kT7, 1, 2>(a, tiles, ci_tiles, lds, s, ev);
-        case 3: return launch_one<13, 4, kTall, 1, 2>(a, tiles, ci_tiles, lds, s, ev);
-        case 4: return launch_one<8, 4, kTall, 1, 2>(a, tiles, ci_tiles, lds, s, ev);
-        case 5: return launch_one<4, 4, kTall, 1, 2>(a, tiles, ci_tiles, lds, s, ev);
+        case 0: return launch_one<13, 4, kT9, 1, 2, 30, 3>(a, tiles, ci_tiles, lds, s, ev);
+        case 1: return launch_one<13, 2, kT9, 1, 2, 0, 0>(a, tiles, ci_tiles, lds, s, ev);
+        case 2: return launch_one<13, 2, kTs2, 4, 1, 0, 0>(a, tiles, ci_tiles, lds, s, ev);
+        case 3: return launch_one<8, 2, kT7, 1, 2, 0, 0>(a, tiles, ci_tiles, lds, s, ev);
+        case 4: return launch_one<13, 4, kTall, 1, 2, 0, 0>(a, tiles, ci_tiles, lds, s, ev);
+        case 5: return launch_one<8, 4, kTall, 1, 2, 0, 0>(a, tiles, ci_tiles, lds, s, ev);
+        case 6: return launch_one<4, 4, kTall, 1, 2, 0, 0>(a, tiles, ci_tiles, lds, s, ev);
         default: return hipErrorInvalidValue;
     }
 }
 
-// Weight image [ci_tile][phase][chunk][tap][cp][ci][2], zero where ci >= Ci
-// or co >= Co.  One work-group per (chunk, ci tile): it stages the slab
+// Weight image [ci_tile][phase][chunk][tap][cp][ci'][2], zero where ci >= Ci
+// or co >= Co; ci' = (ci + 16 * (cp & 1)) mod 64, a rotation that puts the
+// fragment reads of neighbouring co pairs on disjoint LDS banks.  One work-group per (chunk, ci tile): it stages the slab
 // weight[chunk*8 .. +8][ci tile][kH][kW] in LDS with coalesced reads (for a
 // fixed output channel the (ci, kh, kw) run is contiguous) and writes every
 // phase's block of that chunk contiguously.
@@ -471,7 +498,8 @@ __global__ __launch_bounds__(256) void weight_image_f32(const float *__restrict_
             const int j = tap / P.J_w, jw = tap - (tap / P.J_w) * P.J_w;
             const int t = (P.r_h + A.stride * j) * kW + P.r_w + A.stride * jw;
             const float *s0 = slab + (2 * cp) * run + (2 * q) * kHW + t;
-            out[f4] = v4f{s0[0], s0[run], s0[kHW], s0[run + kHW]};
+            out[tap * 128 + cp * 32 + ((q + 8 * (cp & 1)) & 31)] =
+                v4f{s0[0], s0[run], s0[kHW], s0[run + kHW]};
         }
     }
 }
