@@ -336,13 +336,34 @@ __global__ __launch_bounds__(256, OCC) __attribute__((amdgpu_waves_per_eu(OCC, O
 #pragma unroll
         for (int blk = 0; blk < NB; ++blk) acc[blk] = v4f{0.f, 0.f, 0.f, 0.f};
 
+        // JW < 0: each phase's tap grid is dispatched to a compile-time
+        // instance when one exists (else the run-time one below).
+        bool done = false;
+#define GI_HALO_CASE_JW(TT, JJ)                                                              \
+    case TT * 16 + JJ:                                                                       \
+        if constexpr ((TMASK & tbit(TT)) != 0) {                                             \
+            run_phase<TT, NB, HG, CPS, PITCH, JJ>(A, P, smem2, pbase, acc, a0, b0, n_img,      \
+                                                  ci_tile, grs, wrs);                        \
+            done = true;                                                                     \
+        }                                                                                    \
+        break;
+        if constexpr (JW < 0) {
+            switch (T * 16 + P.J_w) {
+                GI_HALO_CASE_JW(1, 1)
+                GI_HALO_CASE_JW(2, 1)
+                GI_HALO_CASE_JW(2, 2)
+                GI_HALO_CASE_JW(4, 2)
+                default: break;
+            }
+        }
+#undef GI_HALO_CASE_JW
 #define GI_HALO_CASE(TT)                                                                     \
     case TT:                                                                                 \
         if constexpr ((TMASK & tbit(TT)) != 0)                                               \
-            run_phase<TT, NB, HG, CPS, PITCH, JW>(A, P, smem2, pbase, acc, a0, b0, n_img, ci_tile, \
-                                                 grs, wrs);                                     \
+            run_phase<TT, NB, HG, CPS, PITCH, (JW > 0 ? JW : 0)>(A, P, smem2, pbase, acc, a0, \
+                                                                b0, n_img, ci_tile, grs, wrs); \
         break;
-        switch (T) {
+        if (!done) switch (T) {
             GI_HALO_CASE(1)
             GI_HALO_CASE(2)
             GI_HALO_CASE(3)
@@ -382,6 +403,7 @@ template <int NB, int HG, unsigned TMASK, int CPS, int OCC, int PITCH, int JW>
 hipError_t launch_one(const HaloArgs &a, int tiles, int ci_tiles, size_t lds, hipStream_t s,
                       const KernelEvents &ev) {
     if (PITCH > 0 && a.HP != PITCH) return hipErrorInvalidValue;
+    // JW > 0: every phase with taps has that kernel-width tap count.
     for (int i = 0; JW > 0 && i < a.nphases; ++i)
         if (a.ph[i].J_w != JW && a.ph[i].J_h * a.ph[i].J_w != 0) return hipErrorInvalidValue;
     if (lds > 64 * 1024) {
@@ -400,16 +422,20 @@ hipError_t launch_one(const HaloArgs &a, int tiles, int ci_tiles, size_t lds, hi
 // counts served, chunks of 8 output channels per LDS stage (the 4-chunk
 // kernel holds one work-group per CU by LDS, so it is compiled for one wave
 // per SIMD and the whole register file), and the halo pitch and kernel width
-// when fixed at compile time (0: read at run time).  The first serves 3 x 3
-// stride-1 kernels on 14-wide tiles with the conflict-free pitch 30.
+// when fixed at compile time (pitch 0: read at run time; jw -1: each phase's
+// tap grid dispatched to a compile-time instance).  Served at fixed pitch:
+// 3 x 3 stride-1 kernels on 14-wide tiles (conflict-free pitch 30) and
+// 28-wide ones (30), 1 x 7 kernels on 17-wide tiles (conflict-free 33, or
+// 23), and the four phases of 3 x 3 stride-2 kernels on 14-wide tiles (15).
 struct HaloCfg {
     int nb, hg;
     unsigned tmask;
     int cps, pitch, jw;
 };
 constexpr HaloCfg kCfg[] = {
-    {13, 4, kT9, 1, 30, 3}, {13, 2, kT9, 1, 0, 0},   {13, 2, kTs2, 4, 0, 0},
-    {8, 2, kT7, 1, 0, 0},   {13, 4, kTall, 1, 0, 0}, {8, 4, kTall, 1, 0, 0},
+    {13, 4, kT9, 1, 30, 3},   {13, 2, kT9, 1, 0, 0},   {13, 2, kTs2, 4, 15, -1},
+    {13, 2, kTs2, 4, 0, 0},   {8, 2, kT7, 1, 33, 7},   {8, 2, kT7, 1, 23, 7},
+    {8, 2, kT7, 1, 0, 0},     {13, 4, kTall, 1, 0, 0}, {8, 4, kTall, 1, 0, 0},
     {4, 4, kTall, 1, 0, 0},
 };
 
@@ -421,7 +447,7 @@ int halo_f32_config(int nb, unsigned tmask, int hg, int hp, int jw) {
     for (int i = 0; i < (int)(sizeof(kCfg) / sizeof(kCfg[0])); ++i) {
         const HaloCfg &c = kCfg[i];
         if (c.nb != nb || c.hg < hg || (c.tmask & tmask) != tmask) continue;
-        if (c.pitch == 0 || (c.pitch == hp && c.jw == jw)) return i;
+        if (c.pitch == 0 || (c.pitch == hp && (c.jw == jw || c.jw < 0))) return i;
     }
     return -1;
 }
@@ -441,11 +467,14 @@ hipError_t launch_halo_f32(const HaloArgs &a, int cfg, int tiles, int ci_tiles, 
     switch (cfg) {
         case 0: return launch_one<13, 4, kT9, 1, 2, 30, 3>(a, tiles, ci_tiles, lds, s, ev);
         case 1: return launch_one<13, 2, kT9, 1, 2, 0, 0>(a, tiles, ci_tiles, lds, s, ev);
-        case 2: return launch_one<13, 2, kTs2, 4, 1, 0, 0>(a, tiles, ci_tiles, lds, s, ev);
-        case 3: return launch_one<8, 2, kT7, 1, 2, 0, 0>(a, tiles, ci_tiles, lds, s, ev);
-        case 4: return launch_one<13, 4, kTall, 1, 2, 0, 0>(a, tiles, ci_tiles, lds, s, ev);
-        case 5: return launch_one<8, 4, kTall, 1, 2, 0, 0>(a, tiles, ci_tiles, lds, s, ev);
-        case 6: return launch_one<4, 4, kTall, 1, 2, 0, 0>(a, tiles, ci_tiles, lds, s, ev);
+        case 2: return launch_one<13, 2, kTs2, 4, 1, 15, -1>(a, tiles, ci_tiles, lds, s, ev);
+        case 3: return launch_one<13, 2, kTs2, 4, 1, 0, 0>(a, tiles, ci_tiles, lds, s, ev);
+        case 4: return launch_one<8, 2, kT7, 1, 2, 33, 7>(a, tiles, ci_tiles, lds, s, ev);
+        case 5: return launch_one<8, 2, kT7, 1, 2, 23, 7>(a, tiles, ci_tiles, lds, s, ev);
+        case 6: return launch_one<8, 2, kT7, 1, 2, 0, 0>(a, tiles, ci_tiles, lds, s, ev);
+        case 7: return launch_one<13, 4, kTall, 1, 2, 0, 0>(a, tiles, ci_tiles, lds, s, ev);
+        case 8: return launch_one<8, 4, kTall, 1, 2, 0, 0>(a, tiles, ci_tiles, lds, s, ev);
+        case 9: return launch_one<4, 4, kTall, 1, 2, 0, 0>(a, tiles, ci_tiles, lds, s, ev);
         default: return hipErrorInvalidValue;
     }
 }
