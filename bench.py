@@ -6,8 +6,9 @@ fraction of the matrix-core roofline, with the CPU oracle timed beside it.
                     [--no-others]
 
 A step is one grad_input call (weight reorder + every GEMM launch) over one
-batch of synthetic inputs already resident in HBM.  W untimed steps, then K
-steps bracketed by a device synchronize on both sides; rank 0 prints ONE JSON
+batch of synthetic inputs already resident in HBM.  W untimed steps (and
+more until 0.1 s has passed, so the clocks have settled), then K steps
+bracketed by a device synchronize on both sides; rank 0 prints ONE JSON
 line.  Effective work per call is 2*N*Co*oH*oW*Ci*kH*kW flops.
 
 The main kernel's own duration is measured live with HIP events that its
@@ -38,6 +39,7 @@ METRIC = "effective TFLOP/s of conv2d grad_input per config; % of MFMA peak (1 G
 PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6}   # MI355X dense matrix-core peaks
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "resnet_stage_3x3"
+WARMUP_SECONDS = 0.1   # untimed warm-up also lasts at least this long
 
 
 def parse():
@@ -112,11 +114,29 @@ def time_workload(wl, steps, warmup, torch, gi, dev):
         gi.grad_input(tg, tw, stride=s.stride, padding=(s.pad_h, s.pad_w),
                       input_hw=(s.H, s.W), out=out, stream=stream)
 
-    for _ in range(warmup):
+    # Warm-up: W calls, and more until 0.1 s has passed, so both timed loops
+    # below run at the clocks of a busy GPU.
+    t_w = time.perf_counter()
+    n_w = 0
+    while n_w < warmup or time.perf_counter() - t_w < WARMUP_SECONDS:
         call()
+        n_w += 1
+        if n_w % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     hev = HipEvents()
     sp = stream.cuda_stream
+    # Main kernel alone: the library's main launch records a begin/end event
+    # pair with the dispatch's own timestamps.  This loop runs first, so the
+    # whole-call loop below also starts at the clocks of a busy GPU.
+    kb = [hev.create() for _ in range(steps)]
+    ke = [hev.create() for _ in range(steps)]
+    for i in range(steps):
+        gi.set_profile_events(kb[i], ke[i])
+        call()
+    gi.set_profile_events(None, None)
+    torch.cuda.synchronize()
+    kern_ms = [hev.elapsed_ms(kb[i], ke[i]) for i in range(steps)]
     # Whole calls: K steps bracketed by two events, nothing else recorded.
     t0, t1 = hev.create(), hev.create()
     torch.cuda.synchronize()
@@ -128,17 +148,6 @@ def time_workload(wl, steps, warmup, torch, gi, dev):
     torch.cuda.synchronize()
     wall1 = time.perf_counter()
     total_ms = hev.elapsed_ms(t0, t1)
-    # Contraction kernels alone: the library's main launch records a
-    # begin/end event pair with the dispatch's own timestamps (a separate
-    # loop, so the whole-call figure above has no events inside it).
-    kb = [hev.create() for _ in range(steps)]
-    ke = [hev.create() for _ in range(steps)]
-    for i in range(steps):
-        gi.set_profile_events(kb[i], ke[i])
-        call()
-    gi.set_profile_events(None, None)
-    torch.cuda.synchronize()
-    kern_ms = [hev.elapsed_ms(kb[i], ke[i]) for i in range(steps)]
     for ev in kb + ke + [t0, t1]:
         hev.destroy(ev)
     return dict(ms_per_step=total_ms / steps, kernel_ms=float(np.mean(kern_ms)),

@@ -200,7 +200,6 @@ bool plan_halo(const conv2d_gi_params &p, const std::vector<Phase> &phases, Halo
     if (jw_common < 0) jw_common = 0;
     const int ci_tiles = (p.Ci + gi::kHaloCT - 1) / gi::kHaloCT;
     if (w_ci_stride * ci_tiles * 4 > lim || maxT == 0) return false;
-    if (gi::weight_image_f32_lds(p.kH, p.kW) > kLdsBytes) return false;
     static const int kNB[] = {4, 8, 13};
     const int f_nb = g_tile_nb.load(), f_tr = g_tile_tr.load(), f_tc = g_tile_tc.load();
     const bool forced = f_nb > 0;
@@ -430,15 +429,22 @@ bool plan_stem(const conv2d_gi_params &p, const std::vector<Phase> &phases, Stem
     gi::StemArgs &a = out.args;
     a = gi::StemArgs{};
     const int nchunks = (p.Co + 3) / 4;
-    int maxHa = 0, maxWb = 0, hpmax = 16;
+    int maxHa = 0, maxWb = 0, maxJh = 1, maxJw = 1;
     int64_t groups = 0;
+    for (const Phase &ph : phases) {
+        maxJh = std::max(maxJh, ph.J_h);
+        maxJw = std::max(maxJw, ph.J_w);
+    }
+    // One halo row pitch for every phase: the widest halo row.
+    const int pitch = 16 + maxJw - 1;
+    // Largest halo in LDS positions, in whole 16-position loads (at most 2
+    // waves x 16 loads).
+    const int hpmax = ((16 + maxJh - 1) * pitch + 15) / 16 * 16;
+    if (hpmax > 512) return false;
     for (size_t i = 0; i < phases.size(); ++i) {
         const Phase &ph = phases[i];
         const int T = ph.J_h * ph.J_w;
         if (!gi::stem_f32_taps_ok(T)) return false;
-        const int hpos = (16 + ph.J_h - 1) * (16 + ph.J_w - 1);
-        if (hpos > 512) return false;
-        hpmax = std::max(hpmax, (hpos + 15) / 16 * 16);
         maxHa = std::max(maxHa, ph.Ha);
         maxWb = std::max(maxWb, ph.Wb);
         gi::StemPhase &s = a.ph[i];
@@ -469,6 +475,7 @@ bool plan_stem(const conv2d_gi_params &p, const std::vector<Phase> &phases, Stem
     a.tiles_r = (maxHa + 15) / 16;
     a.tiles_c = (maxWb + 15) / 16;
     a.HPmax = hpmax;
+    a.pitch = pitch;
     a.g_bytes = (uint32_t)((int64_t)p.N * p.Co * p.oH * p.oW * 4);
     a.d_bytes = (uint32_t)((int64_t)p.N * p.Ci * p.H * p.W * 4);
     a.w_bytes = (uint32_t)(groups * 64);

@@ -163,8 +163,8 @@ struct StemArgs {
     int32_t N, Ci, H, W, Co, oH, oW, stride;
     int32_t nphases, nchunks;
     int32_t tiles_r, tiles_c;
-    int32_t HPmax;          // halo positions of the largest phase, rounded up to 16
-    int32_t pad_;
+    int32_t HPmax;          // LDS positions of the largest phase halo, rounded up to 16
+    int32_t pitch;          // halo row pitch in positions (>= 16 + J_w - 1 of every phase)
     StemPhase ph[kMaxPhasesPerLaunch];
 };
 

@@ -57,8 +57,6 @@ bool halo_f32_fixed_pitch(int cfg);
 size_t halo_f32_lds_bytes(int maxT, int HPc, int stages, int cps);
 
 // Weight image of the halo kernel (layout in gi_common.h); `total` floats.
-// Needs weight_image_f32_lds(kH, kW) bytes of LDS per work-group.
-size_t weight_image_f32_lds(int kH, int kW);
 hipError_t launch_weight_image_f32(const float *w, float *wk, const HaloArgs &a, int kH, int kW,
                                    int ci_tiles, int64_t total, hipStream_t s);
 
@@ -77,6 +75,10 @@ hipError_t launch_weight_frag_bf16(const uint16_t *w, uint16_t *wk, const HaloBf
 // Small-Ci fp32 kernel (kernels_stem_f32.hip): Ci <= 4, any stride whose
 // phases have a tap count in the served set (stem_f32_taps_ok).
 bool stem_f32_taps_ok(int taps);
+// The halo pitch the stem kernel has a compile-time instance for, and the LDS
+// bytes of the kernel for a largest halo of hpmax positions.
+int stem_f32_fixed_pitch();
+size_t stem_f32_lds_bytes(int hpmax);
 hipError_t launch_stem_f32(const StemArgs &a, hipStream_t s, const KernelEvents &ev);
 hipError_t launch_weight_stem_f32(const float *w, float *wk, const StemArgs &a, int kH, int kW,
                                   hipStream_t s);

@@ -35,6 +35,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "gi_common.h"
 #include "gi_launch.h"
 
@@ -481,73 +483,42 @@ hipError_t launch_halo_f32(const HaloArgs &a, int cfg, int tiles, int ci_tiles, 
 
 // Weight image [ci_tile][phase][chunk][tap][cp][ci'][2], zero where ci >= Ci
 // or co >= Co; ci' = (ci + 16 * (cp & 1)) mod 64, a rotation that puts the
-// fragment reads of neighbouring co pairs on disjoint LDS banks.  One work-group per (chunk, ci tile): it stages the slab
-// weight[chunk*8 .. +8][ci tile][kH][kW] in LDS with coalesced reads (for a
-// fixed output channel the (ci, kh, kw) run is contiguous) and writes every
-// phase's block of that chunk contiguously.
+// fragment reads of neighbouring co pairs on disjoint LDS banks.  One thread
+// per float4 of the image (input channels 2q, 2q+1 x output channels 2cp,
+// 2cp+1 of one tap): four independent loads and one store, so the whole
+// image costs about one memory round trip.  Grid: (float4s of the largest
+// phase block / 256, phases, ci tiles).
 __global__ __launch_bounds__(256) void weight_image_f32(const float *__restrict__ w,
                                                         float *__restrict__ wk, const HaloArgs A,
                                                         int kH, int kW) {
-    extern __shared__ float slab[];  // [8 co][64 ci][kH*kW]
-    const int chunk = blockIdx.x, ct = blockIdx.y;
+    const int p = blockIdx.y, ct = blockIdx.z;
+    const HaloPhase &P = A.ph[p];
+    const int T = P.J_h * P.J_w;
+    const int e = blockIdx.x * 256 + threadIdx.x;  // float4 within the phase block
+    if (e >= A.nchunks * T * 128) return;
+    const int qr = e & 31, cp = (e >> 5) & 3;
+    const int tap = (e >> 7) % T, chunk = (e >> 7) / T;
+    const int q = (qr - 8 * (cp & 1)) & 31;  // undo the rotation
+    const int j = tap / P.J_w, jw = tap - (tap / P.J_w) * P.J_w;
+    const int t = (P.r_h + A.stride * j) * kW + P.r_w + A.stride * jw;
     const int kHW = kH * kW;
-    const int run = kHalo64 * kHW;
-    const int ci_rows = min(kHaloCT, A.Ci - ct * kHaloCT);
-    // Thread -> offsets r, r + 256, ... of each channel's run (no division).
-    for (int r0 = 0; r0 < run; r0 += 256 * 2) {
-        float v[2][kHaloBC];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int r = r0 + u * 256 + threadIdx.x;
-#pragma unroll
-            for (int c = 0; c < kHaloBC; ++c) {
-                const int co = chunk * kHaloBC + c;
-                v[u][c] = (r < ci_rows * kHW && co < A.Co)
-                              ? w[((int64_t)co * A.Ci + (int64_t)ct * kHaloCT) * kHW + r]
-                              : 0.f;
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int r = r0 + u * 256 + threadIdx.x;
-            if (r < run) {
-#pragma unroll
-                for (int c = 0; c < kHaloBC; ++c) slab[c * run + r] = v[u][c];
-            }
-        }
-    }
-    __syncthreads();
-    for (int p = 0; p < A.nphases; ++p) {
-        const HaloPhase &P = A.ph[p];
-        const int T = P.J_h * P.J_w;
-        // float4 f4 -> (tap, co pair cp, ci pair): ci 2q and 2q+1, channels 2cp, 2cp+1.
-        v4f *out = (v4f *)(wk + (int64_t)ct * A.w_ci_stride + P.woff + (int64_t)chunk * T * 512);
-        for (int f4 = threadIdx.x; f4 < T * 128; f4 += 256) {
-            const int tap = f4 >> 7, cp = (f4 >> 5) & 3, q = f4 & 31;
-            const int j = tap / P.J_w, jw = tap - (tap / P.J_w) * P.J_w;
-            const int t = (P.r_h + A.stride * j) * kW + P.r_w + A.stride * jw;
-            const float *s0 = slab + (2 * cp) * run + (2 * q) * kHW + t;
-            out[tap * 128 + cp * 32 + ((q + 8 * (cp & 1)) & 31)] =
-                v4f{s0[0], s0[run], s0[kHW], s0[run + kHW]};
-        }
-    }
-}
-
-size_t weight_image_f32_lds(int kH, int kW) {
-    return (size_t)kHaloBC * kHalo64 * kH * kW * sizeof(float);
+    const int ci0 = ct * kHalo64 + 2 * q, co0 = chunk * kHaloBC + 2 * cp;
+    auto ld = [&](int co, int ci) {
+        return (co < A.Co && ci < A.Ci) ? w[((int64_t)co * A.Ci + ci) * kHW + t] : 0.f;
+    };
+    const v4f v = {ld(co0, ci0), ld(co0 + 1, ci0), ld(co0, ci0 + 1), ld(co0 + 1, ci0 + 1)};
+    ((v4f *)(wk + (int64_t)ct * A.w_ci_stride + P.woff))[e] = v;
 }
 
 hipError_t launch_weight_image_f32(const float *w, float *wk, const HaloArgs &a, int kH, int kW,
                                    int ci_tiles, int64_t total, hipStream_t s) {
     (void)total;
-    const size_t lds = weight_image_f32_lds(kH, kW);
-    if (lds > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute((const void *)weight_image_f32,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL(weight_image_f32, dim3(a.nchunks, ci_tiles), dim3(256), lds, s, w, wk, a,
-                       kH, kW);
+    int most = 0;
+    for (int p = 0; p < a.nphases; ++p)
+        most = std::max(most, a.nchunks * a.ph[p].J_h * a.ph[p].J_w * 128);
+    if (most == 0) return hipSuccess;
+    hipLaunchKernelGGL(weight_image_f32, dim3((most + 255) / 256, a.nphases, ci_tiles),
+                       dim3(256), 0, s, w, wk, a, kH, kW);
     return hipGetLastError();
 }
 

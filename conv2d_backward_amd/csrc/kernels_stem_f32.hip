@@ -14,11 +14,16 @@
 //
 // Work-group: 128 threads = 2 waves over a 16 x 16 tile of one phase grid;
 // wave w owns tile rows 8w .. 8w+7 as two 4 x 16 pixel blocks.  Output
-// channels are streamed 4 at a time: the tile's grad_out halo for the 4
-// channels is copied into LDS by direct global -> LDS loads (a position's 4
-// channels are one 16-byte word, so one LDS read serves 4 MFMAs), double-
-// buffered; the A fragments of every tap of the chunk come straight from a
-// weight image into registers, the next chunk's loaded while this one runs.
+// channels are streamed 4 at a time through a 3-stage LDS pipeline filled by
+// direct global -> LDS loads: per stage the tile's grad_out halo for the 4
+// channels (a position's 4 channels are one 16-byte word, so one LDS read
+// serves 4 MFMAs) and the chunk's weights of every tap (a 16-byte word per
+// (tap, input channel) holding its 4 output channels; the 64 lanes read 4
+// distinct words, a broadcast).  Weights come through LDS rather than from
+// memory per tap: a 16-byte-per-lane load per tap for 4 distinct values
+// would keep the texture units of the CU busy for longer than the matrix
+// cores.  When the halo pitch and the tap grid are compile-time constants
+// every tap's shift is an immediate offset of the fragment reads.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -34,7 +39,8 @@ namespace {
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9)
 constexpr int kOOB = 0x7ffffff0;         // byte offset past the end of every buffer
 constexpr int kStemTile = 16;            // tile side in phase-grid pixels
-constexpr int kStemGroups = 16;          // halo groups of 16 positions per wave (<= 512)
+constexpr int kStemStages = 3;           // LDS pipeline stages
+constexpr int kStemA = 64;               // v4f of weights per stage (taps x 4 <= 64)
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
@@ -42,122 +48,150 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint3
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (long)bytes, kRsrcWord3);
 }
 
-// One phase with T taps (compile time) for this work-group's tile.
-template <int T>
+template <int N>
+__device__ __forceinline__ void wait_dma() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// One phase with T taps (compile time) for this work-group's tile.  JW > 0
+// fixes the phase's tap columns and PITCH > 0 the halo row pitch at compile
+// time (they must equal P.J_w and A.pitch); 0 reads them at run time.  G:
+// halo loads of 16 positions per wave and stage (2G x 16 >= the halo).
+//
+// Accumulators: one per (output channel of the chunk, pixel block), so the
+// 8 MFMAs of a tap are independent and each chain advances once per tap (a
+// 4x4x1 MFMA that depends on the one issued just before it stalls).
+//
+// LDS stage (v4f): halo [HPmax positions], then weights [kStemA], plus one
+// scratch kilobyte after the last stage for the surplus loads.
+template <int T, int JW, int PITCH, int G>
 __device__ __forceinline__ void stem_phase(const StemArgs &A, const StemPhase &P, v4f *sm4,
-                                           v4f (&acc)[2], int n, int a0, int b0,
+                                           v4f (&acc)[4][2], int n, int a0, int b0,
                                            __amdgpu_buffer_rsrc_t grs,
                                            __amdgpu_buffer_rsrc_t wrs) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int HC = kStemTile + P.J_w - 1;
-    const int HR = kStemTile + P.J_h - 1;
-    const int hpos = HR * HC;
-    const int groups = (hpos + 15) / 16;
+    const int J_w = JW > 0 ? JW : P.J_w;
+    const int J_h = JW > 0 ? T / (JW > 0 ? JW : 1) : P.J_h;
+    const int HP = PITCH > 0 ? PITCH : A.pitch;
+    const int HC = kStemTile + J_w - 1;
+    const int HR = kStemTile + J_h - 1;
+    const int hpos = HR * HP;
     const int oHW = A.oH * A.oW;
+    const int stage = A.HPmax + kStemA;  // v4f per stage
+    v4f *const dummy = sm4 + kStemStages * stage;
+    // Direct loads per wave and stage: the halo groups, and one weight load
+    // (wave 0 real, wave 1 a dummy) so both waves issue the same count.
+    constexpr int kDma = G + 1;
+    static_assert(kDma <= 63, "vmcnt holds at most 63");
 
     // Halo DMA: group q = wave + 2k covers positions 16q .. 16q+15; lane ->
-    // (position 16q + lane/4, channel lane%4).
-    int goff[kStemGroups];
+    // (position 16q + lane/4, channel lane%4).  Positions past the halo's
+    // columns, or outside the image, read zeros.
+    int goff[G];
 #pragma unroll
-    for (int k = 0; k < kStemGroups; ++k) {
+    for (int k = 0; k < G; ++k) {
         const int q = wave + 2 * k;
         const int pos = q * 16 + (lane >> 2);
-        const int hr = pos / HC, hc = pos - (pos / HC) * HC;
-        const int oh = a0 + P.q_h - (P.J_h - 1) + hr;
-        const int ow = b0 + P.q_w - (P.J_w - 1) + hc;
-        const bool v = q < groups && pos < hpos && oh >= 0 && oh < A.oH && ow >= 0 && ow < A.oW;
+        const int hr = pos / HP, hc = pos - (pos / HP) * HP;
+        const int oh = a0 + P.q_h - (J_h - 1) + hr;
+        const int ow = b0 + P.q_w - (J_w - 1) + hc;
+        const bool v = pos < hpos && hc < HC && oh >= 0 && oh < A.oH && ow >= 0 && ow < A.oW;
         goff[k] = v ? ((n * A.Co) * oHW + oh * A.oW + ow) * 4 : kOOB;
     }
     const int co_l = lane & 3;
+    // Weights of (chunk): T x 4 consecutive v4f of the image, one 16-byte
+    // direct load (lanes past T x 4 read zeros).
+    const int wl = (P.woff * 4 + lane) * 16;
+    // Every wave issues kStemDma loads per stage, also past the last chunk
+    // (surplus loads read zeros into the scratch kilobyte), so "stage s has
+    // landed" is a wait on a compile-time count.
     auto issue = [&](int chunk, int buf) {
+        const bool live = chunk < A.nchunks;
+        v4f *st = sm4 + buf * stage;
 #pragma unroll
-        for (int k = 0; k < kStemGroups; ++k) {
+        for (int k = 0; k < G; ++k) {
             const int q = wave + 2 * k;
-            if (q < groups) {
-                const int co = chunk * 4 + co_l;
-                const int off = (goff[k] != kOOB && co < A.Co) ? goff[k] + co * oHW * 4 : kOOB;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    grs, (lds_ptr_t)(sm4 + buf * A.HPmax + q * 16), 4, off, 0, 0, 0);
-            }
+            const bool real = live && q * 16 < hpos;
+            const int co = chunk * 4 + co_l;
+            const int off = (real && goff[k] != kOOB && co < A.Co) ? goff[k] + co * oHW * 4 : kOOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(grs, (lds_ptr_t)(real ? st + q * 16 : dummy),
+                                                     4, off, 0, 0, 0);
         }
-    };
-    // A fragment of (chunk, tap): the 4 output channels of input channel lane%4.
-    const int wl = (P.woff * 4 + (lane & 3)) * 16;
-    auto aload = [&](int chunk, int t) {
-        const int off = wl + ((chunk * T + t) * 4) * 16;
-        return __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(wrs, off, 0, 0));
+        const bool wreal = live && wave == 0;
+        const int woff = (wreal && lane < T * 4) ? wl + chunk * T * 64 : kOOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            wrs, (lds_ptr_t)(wreal ? st + A.HPmax : dummy), 16, woff, 0, 0, 0);
     };
 
     // Halo position of this lane's pixel in each block, and tap shifts.
     const int r = lane >> 4, c = lane & 15;
     int pb[2];
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) pb[blk] = (8 * wave + 4 * blk + r) * HC + c;
+    for (int blk = 0; blk < 2; ++blk) pb[blk] = (8 * wave + 4 * blk + r) * HP + c;
     int shift[T];
     {
         int j = 0, jw = 0;
 #pragma unroll
         for (int t = 0; t < T; ++t) {
-            shift[t] = (P.J_h - 1 - j) * HC + (P.J_w - 1 - jw);
-            if (++jw == P.J_w) {
+            shift[t] = (J_h - 1 - j) * HP + (J_w - 1 - jw);
+            if (++jw == J_w) {
                 jw = 0;
                 ++j;
             }
         }
     }
 
-    v4f af[2][T];
-#pragma unroll
-    for (int t = 0; t < T; ++t) af[0][t] = aload(0, t);
+    wait_dma<0>();  // the previous phase's loads and stores count too: drain them
     issue(0, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    issue(1, 1);
+    wait_dma<kDma>();
     __syncthreads();
-
-    auto body = [&](int chunk, v4f(&cur_a)[T], v4f(&next_a)[T]) {
-        const int cur = chunk & 1;
-        if (chunk + 1 < A.nchunks) {
-            issue(chunk + 1, cur ^ 1);
-#pragma unroll
-            for (int t = 0; t < T; ++t) next_a[t] = aload(chunk + 1, t);
-        }
-        const v4f *hs = sm4 + cur * A.HPmax;
+    for (int chunk = 0; chunk < A.nchunks; ++chunk) {
+        const int cur = chunk % kStemStages;
+        issue(chunk + 2, (chunk + 2) % kStemStages);
+        const v4f *hs = sm4 + cur * stage;
+        const v4f *as = hs + A.HPmax + co_l;
         int pp[2];
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
             pp[blk] = pb[blk];
             asm volatile("" : "+v"(pp[blk]));
         }
-        // B fragments two taps ahead (three slots).
-        v4f fb[3][2];
+        // B fragments two taps ahead (three slots), A one tap ahead.
+        v4f fb[3][2], fa[2];
         auto bfetch = [&](int t, int sl) {
 #pragma unroll
             for (int blk = 0; blk < 2; ++blk) fb[sl][blk] = hs[pp[blk] + shift[t]];
         };
         bfetch(0, 0);
+        fa[0] = as[0];
         if (T > 1) bfetch(1, 1);
 #pragma unroll
         for (int t = 0; t < T; ++t) {
             if (t + 2 < T) bfetch(t + 2, (t + 2) % 3);
+            if (t + 1 < T) fa[(t + 1) & 1] = as[(t + 1) * 4];
             const int sl = t % 3;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
 #pragma unroll
                 for (int blk = 0; blk < 2; ++blk)
-                    acc[blk] = __builtin_amdgcn_mfma_f32_4x4x1f32(cur_a[t][e], fb[sl][blk][e],
-                                                                  acc[blk], 0, 0, 0);
+                    acc[e][blk] = __builtin_amdgcn_mfma_f32_4x4x1f32(
+                        fa[t & 1][e], fb[sl][blk][e], acc[e][blk], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        // Stage chunk+1 must have landed; the loads of chunk+2 may still be
+        // in flight.
+        wait_dma<kDma>();
         __syncthreads();
-    };
-    for (int chunk = 0; chunk < A.nchunks; chunk += 2) {
-        body(chunk, af[0], af[1]);
-        if (chunk + 1 < A.nchunks) body(chunk + 1, af[1], af[0]);
     }
+    // Nothing may still write LDS that a later phase or work-group uses.
+    wait_dma<0>();
 }
 
-__global__ __launch_bounds__(128, 2) void gi_stem_f32(const StemArgs A) {
+template <int PITCH>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(4))) void gi_stem_f32(
+    const StemArgs A) {
     extern __shared__ __attribute__((aligned(16))) v4f sm4[];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -176,12 +210,28 @@ __global__ __launch_bounds__(128, 2) void gi_stem_f32(const StemArgs A) {
     const __amdgpu_buffer_rsrc_t wrs = make_rsrc(A.wk, A.w_bytes);
     const __amdgpu_buffer_rsrc_t drs = make_rsrc(A.dst, A.d_bytes);
 
-    v4f acc[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+    v4f acc[4][2];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) acc[e][blk] = v4f{0.f, 0.f, 0.f, 0.f};
+    // Compile-time tap grids of the 7 x 7 stride-2 phases when the pitch is
+    // fixed; everything else through the run-time instances.
+    bool done = false;
+    if constexpr (PITCH > 0) {
+        switch (T * 16 + P.J_w) {
+            case 9 * 16 + 3: stem_phase<9, 3, PITCH, 12>(A, P, sm4, acc, n, a0, b0, grs, wrs); done = true; break;
+            case 12 * 16 + 3: stem_phase<12, 3, PITCH, 12>(A, P, sm4, acc, n, a0, b0, grs, wrs); done = true; break;
+            case 12 * 16 + 4: stem_phase<12, 4, PITCH, 12>(A, P, sm4, acc, n, a0, b0, grs, wrs); done = true; break;
+            case 16 * 16 + 4: stem_phase<16, 4, PITCH, 12>(A, P, sm4, acc, n, a0, b0, grs, wrs); done = true; break;
+            default: break;
+        }
+    }
 #define GI_STEM_CASE(TT)                                                        \
     case TT:                                                                    \
-        stem_phase<TT>(A, P, sm4, acc, n, a0, b0, grs, wrs);                    \
+        stem_phase<TT, 0, PITCH, 16>(A, P, sm4, acc, n, a0, b0, grs, wrs);      \
         break;
-    switch (T) {
+    if (!done) switch (T) {
         GI_STEM_CASE(1)
         GI_STEM_CASE(2)
         GI_STEM_CASE(3)
@@ -203,10 +253,11 @@ __global__ __launch_bounds__(128, 2) void gi_stem_f32(const StemArgs A) {
         const int b = b0 + (lane & 15);
         const bool pv = a < P.Ha && b < P.Wb;
         const int pix = (P.rho_h + A.stride * a) * A.W + P.rho_w + A.stride * b;
+        const v4f sum = (acc[0][blk] + acc[1][blk]) + (acc[2][blk] + acc[3][blk]);
 #pragma unroll
         for (int ci = 0; ci < 4; ++ci) {
             const int off = (pv && ci < A.Ci) ? ((n * A.Ci + ci) * plane + pix) * 4 : kOOB;
-            const float v = acc[blk][ci];
+            const float v = sum[ci];
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), drs, off, 0, 0);
         }
     }
@@ -253,11 +304,25 @@ bool stem_f32_taps_ok(int taps) {
     }
 }
 
+// Halo pitch fixed at compile time: 19 positions holds every phase of a
+// 7 x 7 kernel at stride 2 (tap grids 3 or 4 wide).
+constexpr int kStemPitch = 19;
+
+int stem_f32_fixed_pitch() { return kStemPitch; }
+
+size_t stem_f32_lds_bytes(int hpmax) {
+    return ((size_t)kStemStages * (hpmax + kStemA) + 64) * sizeof(v4f);
+}
+
 hipError_t launch_stem_f32(const StemArgs &a, hipStream_t s, const KernelEvents &ev) {
-    const size_t lds = (size_t)2 * a.HPmax * sizeof(v4f);
+    const size_t lds = stem_f32_lds_bytes(a.HPmax);
     const int64_t wgs = (int64_t)a.N * a.tiles_r * a.tiles_c * a.nphases;
-    hipExtLaunchKernelGGL(gi_stem_f32, dim3((unsigned)wgs), dim3(128), (uint32_t)lds, s, ev.start,
-                          ev.stop, 0, a);
+    if (a.pitch == kStemPitch)
+        hipExtLaunchKernelGGL(gi_stem_f32<kStemPitch>, dim3((unsigned)wgs), dim3(128),
+                              (uint32_t)lds, s, ev.start, ev.stop, 0, a);
+    else
+        hipExtLaunchKernelGGL(gi_stem_f32<0>, dim3((unsigned)wgs), dim3(128), (uint32_t)lds, s,
+                              ev.start, ev.stop, 0, a);
     return hipGetLastError();
 }
 
