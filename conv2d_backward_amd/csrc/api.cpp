@@ -437,10 +437,9 @@ bool plan_stem(const conv2d_gi_params &p, const std::vector<Phase> &phases, Stem
     }
     // One halo row pitch for every phase: the widest halo row.
     const int pitch = 16 + maxJw - 1;
-    // Largest halo in LDS positions, in whole 16-position loads (at most 2
-    // waves x 16 loads).
-    const int hpmax = ((16 + maxJh - 1) * pitch + 15) / 16 * 16;
-    if (hpmax > 512) return false;
+    // Every phase's halo must fit the kernel's per-stage halo region.
+    const int hpmax = gi::stem_f32_halo_positions(pitch);
+    if ((16 + maxJh - 1) * pitch > hpmax) return false;
     for (size_t i = 0; i < phases.size(); ++i) {
         const Phase &ph = phases[i];
         const int T = ph.J_h * ph.J_w;
@@ -580,11 +579,9 @@ int run(const T *grad_out, const T *weight, float *dst, const conv2d_gi_params *
             HaloBf16Plan &h = plan.hb;
             uint16_t *gp = (uint16_t *)ws;
             uint16_t *wk = (uint16_t *)((char *)ws + h.gp_bytes);
-            e = gi::launch_pad_planes_bf16((const uint16_t *)grad_out, gp, h.args, p->oH, p->oW,
-                                           p->pad_h, p->pad_w, stream);
-            if (e == hipSuccess)
-                e = gi::launch_weight_frag_bf16((const uint16_t *)weight, wk, h.args, h.ci_tiles,
-                                                stream);
+            e = gi::launch_prologues_bf16((const uint16_t *)grad_out, gp,
+                                          (const uint16_t *)weight, wk, h.args, p->oH, p->oW,
+                                          p->pad_h, p->pad_w, h.ci_tiles, stream);
         } else if (plan.variant == CONV2D_GI_VARIANT_HALO)
             e = gi::launch_weight_image_f32((const float *)weight, (float *)ws, plan.halo.args,
                                             p->kH, p->kW, plan.halo.ci_tiles,
@@ -670,7 +667,7 @@ std::string describe(const Plan &plan, bool bf16) {
     if (plan.variant == CONV2D_GI_VARIANT_HALO && bf16) {
         const HaloBf16Plan &h = plan.hb;
         const gi::HaloBf16Args &a = h.args;
-        s += " launches=3 [cfg=" + std::to_string(h.cfg) + " tile=" + std::to_string(a.TR) + "x" +
+        s += " launches=2 [cfg=" + std::to_string(h.cfg) + " tile=" + std::to_string(a.TR) + "x" +
              std::to_string(a.TC) + " wgs=" + std::to_string(h.tiles) + "x" +
              std::to_string(h.ci_tiles) + " lds=" + std::to_string(h.lds) +
              " halo=" + std::to_string(a.HR) + "x" + std::to_string(a.HC) + " pitch=" +

@@ -66,18 +66,21 @@ hipError_t launch_weight_image_f32(const float *w, float *wk, const HaloArgs &a,
 int halo_bf16_config(int nbw, int kH, int kW, int hp);
 hipError_t launch_halo_bf16(const HaloBf16Args &a, int cfg, int tiles, int ci_tiles, size_t lds,
                             hipStream_t s, const KernelEvents &ev);
-// Prologues of the bf16 halo kernel (layouts in gi_common.h).
-hipError_t launch_pad_planes_bf16(const uint16_t *g, uint16_t *gp, const HaloBf16Args &a, int oH,
-                                  int oW, int pad_h, int pad_w, hipStream_t s);
-hipError_t launch_weight_frag_bf16(const uint16_t *w, uint16_t *wk, const HaloBf16Args &a,
-                                   int ci_tiles, hipStream_t s);
+// Both prologues of the bf16 halo kernel in one launch (layouts in
+// gi_common.h): grad_out -> padded channel planes gp, weight -> fragment
+// image wk.
+hipError_t launch_prologues_bf16(const uint16_t *g, uint16_t *gp, const uint16_t *w, uint16_t *wk,
+                                 const HaloBf16Args &a, int oH, int oW, int pad_h, int pad_w,
+                                 int ci_tiles, hipStream_t s);
 
 // Small-Ci fp32 kernel (kernels_stem_f32.hip): Ci <= 4, any stride whose
 // phases have a tap count in the served set (stem_f32_taps_ok).
 bool stem_f32_taps_ok(int taps);
-// The halo pitch the stem kernel has a compile-time instance for, and the LDS
-// bytes of the kernel for a largest halo of hpmax positions.
+// The halo pitch the stem kernel has a compile-time instance for; the halo
+// positions per LDS stage of the instance used for a pitch (every phase's
+// halo must fit); the LDS bytes of the kernel for that many positions.
 int stem_f32_fixed_pitch();
+int stem_f32_halo_positions(int pitch);
 size_t stem_f32_lds_bytes(int hpmax);
 hipError_t launch_stem_f32(const StemArgs &a, hipStream_t s, const KernelEvents &ev);
 hipError_t launch_weight_stem_f32(const float *w, float *wk, const StemArgs &a, int kH, int kW,

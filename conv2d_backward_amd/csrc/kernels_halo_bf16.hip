@@ -274,12 +274,12 @@ constexpr int kCfg[][4] = {{7, 9, 3, 30}, {7, 9, 0, 0}, {4, 9, 0, 0}, {7, 3, 0, 
 // work-group per (image n, block of 64 channels, band of RB rows of gp): the
 // band is read along ow (coalesced), packed into channel pairs in LDS, and
 // written plane by plane as 16-byte positions (coalesced along x).
-__global__ __launch_bounds__(256) void pad_planes_bf16(const uint16_t *__restrict__ g,
-                                                       uint16_t *__restrict__ gp,
-                                                       const HaloBf16Args A, int oH, int oW,
-                                                       int pad_h, int pad_w, int RB) {
-    extern __shared__ uint32_t band[];  // [RB][oW][33] channel pairs
-    const int n = blockIdx.x, co0 = blockIdx.y * 64, y0 = blockIdx.z * RB;
+__device__ __forceinline__ void pad_planes_bf16(const uint16_t *__restrict__ g,
+                                                uint16_t *__restrict__ gp, const HaloBf16Args &A,
+                                                int oH, int oW, int pad_h, int pad_w, int RB,
+                                                int n, int cb, int yb, uint32_t *band) {
+    // band: [RB][oW][33] channel pairs
+    const int co0 = cb * 64, y0 = yb * RB;
     const int yoff = A.kH - 1 - pad_h;  // oh = y - yoff
     const int xoff = A.kW - 1 - pad_w;  // ow = x - xoff
     // Thread -> one position of the band (fixed), looping over channel pairs:
@@ -341,11 +341,10 @@ __global__ __launch_bounds__(256) void pad_planes_bf16(const uint16_t *__restric
 // reads the 8 output channels 8g .. 8g+7 of the chunk for the tile's input
 // channels and every tap (one contiguous run per channel) into LDS, and each
 // thread then writes one lane's 16 bytes.
-__global__ __launch_bounds__(256) void weight_frag_bf16(const uint16_t *__restrict__ w,
-                                                        uint16_t *__restrict__ wk,
-                                                        const HaloBf16Args A) {
-    extern __shared__ uint16_t slab[];  // [8 co][64 ci * T]
-    const int chunk = blockIdx.x, ct = blockIdx.y, g = blockIdx.z;
+__device__ __forceinline__ void weight_frag_bf16(const uint16_t *__restrict__ w,
+                                                 uint16_t *__restrict__ wk, const HaloBf16Args &A,
+                                                 int chunk, int ct, int g, uint16_t *slab) {
+    // slab: [8 co][64 ci * T]
     const int T = A.kH * A.kW;
     const int run = 64 * T;
     const int ci_rows = min(64, A.Ci - ct * 64);
@@ -387,6 +386,31 @@ __global__ __launch_bounds__(256) void weight_frag_bf16(const uint16_t *__restri
     }
 }
 
+// Both prologues in one launch (they are independent, so they overlap and
+// share one dispatch): work-groups [0, pad_wgs) pad grad_out, the rest
+// reorder the weight.
+__global__ __launch_bounds__(256) void prologues_bf16(const uint16_t *__restrict__ g,
+                                                      uint16_t *__restrict__ gp,
+                                                      const uint16_t *__restrict__ w,
+                                                      uint16_t *__restrict__ wk,
+                                                      const HaloBf16Args A, int oH, int oW,
+                                                      int pad_h, int pad_w, int RB, int pad_cb,
+                                                      int pad_yb, int ci_tiles) {
+    extern __shared__ uint32_t lds_u32[];
+    int b = blockIdx.x;
+    const int pad_wgs = A.N * pad_cb * pad_yb;
+    if (b < pad_wgs) {
+        const int yb = b % pad_yb;
+        b /= pad_yb;
+        pad_planes_bf16(g, gp, A, oH, oW, pad_h, pad_w, RB, b / pad_cb, b % pad_cb, yb, lds_u32);
+    } else {
+        b -= pad_wgs;
+        const int gq = b & 3;
+        b >>= 2;
+        weight_frag_bf16(w, wk, A, b / ci_tiles, b % ci_tiles, gq, (uint16_t *)lds_u32);
+    }
+}
+
 }  // namespace
 
 int halo_bf16_config(int nbw, int kH, int kW, int hp) {
@@ -409,36 +433,29 @@ hipError_t launch_halo_bf16(const HaloBf16Args &a, int cfg, int tiles, int ci_ti
     }
 }
 
-hipError_t launch_pad_planes_bf16(const uint16_t *g, uint16_t *gp, const HaloBf16Args &a, int oH,
-                                  int oW, int pad_h, int pad_w, hipStream_t s) {
-    // Rows per work-group: at most what fits 16 KB of LDS, and few enough that
-    // the grid has some 2048 work-groups to keep loads in flight.
+hipError_t launch_prologues_bf16(const uint16_t *g, uint16_t *gp, const uint16_t *w, uint16_t *wk,
+                                 const HaloBf16Args &a, int oH, int oW, int pad_h, int pad_w,
+                                 int ci_tiles, hipStream_t s) {
+    // Pad: rows per work-group at most what fits 16 KB of LDS, and few enough
+    // that the grid has some 2048 work-groups to keep loads in flight.
     int RB = (int)(16384 / ((size_t)oW * 33 * sizeof(uint32_t)));
     const int64_t others = (int64_t)a.N * ((a.Cop + 63) / 64);
     const int want = (int)((a.YP * others + 2047) / 2048);
     if (want < RB) RB = want;
     RB = RB < 1 ? 1 : (RB > a.YP ? a.YP : RB);
-    const size_t lds = (size_t)RB * oW * 33 * sizeof(uint32_t);
+    const int pad_cb = (a.Cop + 63) / 64, pad_yb = (a.YP + RB - 1) / RB;
+    const size_t pad_lds = (size_t)RB * oW * 33 * sizeof(uint32_t);
+    const size_t frag_lds = (size_t)8 * 64 * a.kH * a.kW * sizeof(uint16_t);
+    const size_t lds = pad_lds > frag_lds ? pad_lds : frag_lds;
+    const int64_t wgs = (int64_t)a.N * pad_cb * pad_yb + (int64_t)a.nchunks * ci_tiles * 4;
+    if (wgs > INT32_MAX) return hipErrorInvalidValue;
     if (lds > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute((const void *)pad_planes_bf16,
+        hipError_t e = hipFuncSetAttribute((const void *)prologues_bf16,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(pad_planes_bf16, dim3(a.N, (a.Cop + 63) / 64, (a.YP + RB - 1) / RB),
-                       dim3(256), lds, s, g, gp, a, oH, oW, pad_h, pad_w, RB);
-    return hipGetLastError();
-}
-
-hipError_t launch_weight_frag_bf16(const uint16_t *w, uint16_t *wk, const HaloBf16Args &a,
-                                   int ci_tiles, hipStream_t s) {
-    const size_t lds = (size_t)8 * 64 * a.kH * a.kW * sizeof(uint16_t);
-    if (lds > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute((const void *)weight_frag_bf16,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL(weight_frag_bf16, dim3(a.nchunks, ci_tiles, 4), dim3(256), lds, s, w, wk,
-                       a);
+    hipLaunchKernelGGL(prologues_bf16, dim3((unsigned)wgs), dim3(256), lds, s, g, gp, w, wk, a, oH,
+                       oW, pad_h, pad_w, RB, pad_cb, pad_yb, ci_tiles);
     return hipGetLastError();
 }
 

@@ -56,14 +56,17 @@ __device__ __forceinline__ void wait_dma() {
 // One phase with T taps (compile time) for this work-group's tile.  JW > 0
 // fixes the phase's tap columns and PITCH > 0 the halo row pitch at compile
 // time (they must equal P.J_w and A.pitch); 0 reads them at run time.  G:
-// halo loads of 16 positions per wave and stage (2G x 16 >= the halo).
+// halo loads of 16 positions per wave and stage; the stage's halo region is
+// 2G x 16 = A.HPmax positions, at least the phase's halo.
 //
 // Accumulators: one per (output channel of the chunk, pixel block), so the
 // 8 MFMAs of a tap are independent and each chain advances once per tap (a
 // 4x4x1 MFMA that depends on the one issued just before it stalls).
 //
-// LDS stage (v4f): halo [HPmax positions], then weights [kStemA], plus one
-// scratch kilobyte after the last stage for the surplus loads.
+// LDS stage (v4f): halo [HPmax positions], then weights [kStemA].  Every
+// load writes its own slot of the stage it fills, also past the last chunk
+// (that stage is not read again; such loads read zeros or unused weights),
+// so the issue carries no per-load selects.
 template <int T, int JW, int PITCH, int G>
 __device__ __forceinline__ void stem_phase(const StemArgs &A, const StemPhase &P, v4f *sm4,
                                            v4f (&acc)[4][2], int n, int a0, int b0,
@@ -79,15 +82,14 @@ __device__ __forceinline__ void stem_phase(const StemArgs &A, const StemPhase &P
     const int hpos = HR * HP;
     const int oHW = A.oH * A.oW;
     const int stage = A.HPmax + kStemA;  // v4f per stage
-    v4f *const dummy = sm4 + kStemStages * stage;
-    // Direct loads per wave and stage: the halo groups, and one weight load
-    // (wave 0 real, wave 1 a dummy) so both waves issue the same count.
+    // Direct loads per wave and stage: the halo groups and the weights (both
+    // waves load the same weights, so the count is the same for both).
     constexpr int kDma = G + 1;
     static_assert(kDma <= 63, "vmcnt holds at most 63");
 
     // Halo DMA: group q = wave + 2k covers positions 16q .. 16q+15; lane ->
-    // (position 16q + lane/4, channel lane%4).  Positions past the halo's
-    // columns, or outside the image, read zeros.
+    // (position 16q + lane/4, channel lane%4).  Positions past the halo or
+    // its columns, or outside the image, get an offset past the buffer.
     int goff[G];
 #pragma unroll
     for (int k = 0; k < G; ++k) {
@@ -100,28 +102,22 @@ __device__ __forceinline__ void stem_phase(const StemArgs &A, const StemPhase &P
         goff[k] = v ? ((n * A.Co) * oHW + oh * A.oW + ow) * 4 : kOOB;
     }
     const int co_l = lane & 3;
-    // Weights of (chunk): T x 4 consecutive v4f of the image, one 16-byte
-    // direct load (lanes past T x 4 read zeros).
-    const int wl = (P.woff * 4 + lane) * 16;
-    // Every wave issues kStemDma loads per stage, also past the last chunk
-    // (surplus loads read zeros into the scratch kilobyte), so "stage s has
-    // landed" is a wait on a compile-time count.
+    // Weights of a chunk: T x 4 consecutive v4f of the image, one 16-byte
+    // direct load (lanes past T x 4 read past the buffer: zeros).
+    const int wl = lane < T * 4 ? (P.woff * 4 + lane) * 16 : (int)A.w_bytes;
     auto issue = [&](int chunk, int buf) {
-        const bool live = chunk < A.nchunks;
+        // Channel part of this lane's offset; the buffer size (an offset past
+        // its end) for a channel past Co or a chunk past the last.  Offsets
+        // stay below 2^32: goff <= kOOB < 2^31 and this part <= g_bytes < 2^31.
+        const int co = chunk * 4 + co_l;
+        const int cc = (chunk < A.nchunks && co < A.Co) ? co * oHW * 4 : (int)A.g_bytes;
         v4f *st = sm4 + buf * stage;
 #pragma unroll
-        for (int k = 0; k < G; ++k) {
-            const int q = wave + 2 * k;
-            const bool real = live && q * 16 < hpos;
-            const int co = chunk * 4 + co_l;
-            const int off = (real && goff[k] != kOOB && co < A.Co) ? goff[k] + co * oHW * 4 : kOOB;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(grs, (lds_ptr_t)(real ? st + q * 16 : dummy),
-                                                     4, off, 0, 0, 0);
-        }
-        const bool wreal = live && wave == 0;
-        const int woff = (wreal && lane < T * 4) ? wl + chunk * T * 64 : kOOB;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            wrs, (lds_ptr_t)(wreal ? st + A.HPmax : dummy), 16, woff, 0, 0, 0);
+        for (int k = 0; k < G; ++k)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                grs, (lds_ptr_t)(st + (wave + 2 * k) * 16), 4, goff[k] + cc, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, (lds_ptr_t)(st + A.HPmax), 16,
+                                                 wl + chunk * T * 64, 0, 0, 0);
     };
 
     // Halo position of this lane's pixel in each block, and tap shifts.
@@ -147,9 +143,11 @@ __device__ __forceinline__ void stem_phase(const StemArgs &A, const StemPhase &P
     issue(1, 1);
     wait_dma<kDma>();
     __syncthreads();
+    static_assert(kStemStages == 3, "stage rotation below");
+    int cur = 0;
     for (int chunk = 0; chunk < A.nchunks; ++chunk) {
-        const int cur = chunk % kStemStages;
-        issue(chunk + 2, (chunk + 2) % kStemStages);
+        const int ahead = cur == 0 ? 2 : cur - 1;  // (chunk + 2) mod 3
+        issue(chunk + 2, ahead);
         const v4f *hs = sm4 + cur * stage;
         const v4f *as = hs + A.HPmax + co_l;
         int pp[2];
@@ -184,12 +182,13 @@ __device__ __forceinline__ void stem_phase(const StemArgs &A, const StemPhase &P
         // in flight.
         wait_dma<kDma>();
         __syncthreads();
+        cur = cur == 2 ? 0 : cur + 1;
     }
     // Nothing may still write LDS that a later phase or work-group uses.
     wait_dma<0>();
 }
 
-template <int PITCH>
+template <int PITCH, int G>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(4))) void gi_stem_f32(
     const StemArgs A) {
     extern __shared__ __attribute__((aligned(16))) v4f sm4[];
@@ -220,16 +219,16 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(4))) void g
     bool done = false;
     if constexpr (PITCH > 0) {
         switch (T * 16 + P.J_w) {
-            case 9 * 16 + 3: stem_phase<9, 3, PITCH, 12>(A, P, sm4, acc, n, a0, b0, grs, wrs); done = true; break;
-            case 12 * 16 + 3: stem_phase<12, 3, PITCH, 12>(A, P, sm4, acc, n, a0, b0, grs, wrs); done = true; break;
-            case 12 * 16 + 4: stem_phase<12, 4, PITCH, 12>(A, P, sm4, acc, n, a0, b0, grs, wrs); done = true; break;
-            case 16 * 16 + 4: stem_phase<16, 4, PITCH, 12>(A, P, sm4, acc, n, a0, b0, grs, wrs); done = true; break;
+            case 9 * 16 + 3: stem_phase<9, 3, PITCH, G>(A, P, sm4, acc, n, a0, b0, grs, wrs); done = true; break;
+            case 12 * 16 + 3: stem_phase<12, 3, PITCH, G>(A, P, sm4, acc, n, a0, b0, grs, wrs); done = true; break;
+            case 12 * 16 + 4: stem_phase<12, 4, PITCH, G>(A, P, sm4, acc, n, a0, b0, grs, wrs); done = true; break;
+            case 16 * 16 + 4: stem_phase<16, 4, PITCH, G>(A, P, sm4, acc, n, a0, b0, grs, wrs); done = true; break;
             default: break;
         }
     }
 #define GI_STEM_CASE(TT)                                                        \
     case TT:                                                                    \
-        stem_phase<TT, 0, PITCH, 16>(A, P, sm4, acc, n, a0, b0, grs, wrs);      \
+        stem_phase<TT, 0, PITCH, G>(A, P, sm4, acc, n, a0, b0, grs, wrs);       \
         break;
     if (!done) switch (T) {
         GI_STEM_CASE(1)
@@ -305,24 +304,34 @@ bool stem_f32_taps_ok(int taps) {
 }
 
 // Halo pitch fixed at compile time: 19 positions holds every phase of a
-// 7 x 7 kernel at stride 2 (tap grids 3 or 4 wide).
+// 7 x 7 kernel at stride 2 (tap grids 3 or 4 wide); its halos (at most 20
+// rows) fit 12 loads of 16 positions per wave.  Otherwise 16 loads per wave
+// (halos of up to 512 positions) and the pitch is read at run time.
 constexpr int kStemPitch = 19;
+constexpr int kStemFixedG = 12;
+constexpr int kStemG = 16;
 
 int stem_f32_fixed_pitch() { return kStemPitch; }
 
+int stem_f32_halo_positions(int pitch) {
+    return 2 * 16 * (pitch == kStemPitch ? kStemFixedG : kStemG);
+}
+
 size_t stem_f32_lds_bytes(int hpmax) {
-    return ((size_t)kStemStages * (hpmax + kStemA) + 64) * sizeof(v4f);
+    return (size_t)kStemStages * (hpmax + kStemA) * sizeof(v4f);
 }
 
 hipError_t launch_stem_f32(const StemArgs &a, hipStream_t s, const KernelEvents &ev) {
+    if (a.HPmax != stem_f32_halo_positions(a.pitch)) return hipErrorInvalidValue;
     const size_t lds = stem_f32_lds_bytes(a.HPmax);
     const int64_t wgs = (int64_t)a.N * a.tiles_r * a.tiles_c * a.nphases;
+    if (lds > 64 * 1024) return hipErrorInvalidValue;
     if (a.pitch == kStemPitch)
-        hipExtLaunchKernelGGL(gi_stem_f32<kStemPitch>, dim3((unsigned)wgs), dim3(128),
-                              (uint32_t)lds, s, ev.start, ev.stop, 0, a);
+        hipExtLaunchKernelGGL((gi_stem_f32<kStemPitch, kStemFixedG>), dim3((unsigned)wgs),
+                              dim3(128), (uint32_t)lds, s, ev.start, ev.stop, 0, a);
     else
-        hipExtLaunchKernelGGL(gi_stem_f32<0>, dim3((unsigned)wgs), dim3(128), (uint32_t)lds, s,
-                              ev.start, ev.stop, 0, a);
+        hipExtLaunchKernelGGL((gi_stem_f32<0, kStemG>), dim3((unsigned)wgs), dim3(128),
+                              (uint32_t)lds, s, ev.start, ev.stop, 0, a);
     return hipGetLastError();
 }
 
