@@ -5,11 +5,13 @@ fraction of the matrix-core roofline, with the CPU oracle timed beside it.
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
                     [--no-others]
 
-A step is one grad_input call (weight reorder + every GEMM launch) over one
-batch of synthetic inputs already resident in HBM.  W untimed steps (and
-more until 0.1 s has passed, so the clocks have settled), then K steps
-bracketed by a device synchronize on both sides; rank 0 prints ONE JSON
-line.  Effective work per call is 2*N*Co*oH*oW*Ci*kH*kW flops.
+A step is one grad_input call (prologue + main kernel) over one batch of
+synthetic inputs already resident in HBM.  After a device synchronize: at
+least W untimed steps (and at least 0.1 s of GPU work, so the clocks have
+settled), then exactly K steps timed between two events on the launch
+stream, enqueued back to back with the warm-up (no idle gap before them),
+then a device synchronize; rank 0 prints ONE JSON line.  Effective work per
+call is 2*N*Co*oH*oW*Ci*kH*kW flops.
 
 The main kernel's own duration is measured live with HIP events that its
 launch records with the dispatch's start and end timestamps (the
@@ -21,6 +23,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import platform
 import sys
@@ -39,7 +42,7 @@ METRIC = "effective TFLOP/s of conv2d grad_input per config; % of MFMA peak (1 G
 PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6}   # MI355X dense matrix-core peaks
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "resnet_stage_3x3"
-WARMUP_SECONDS = 0.1   # untimed warm-up also lasts at least this long
+WARMUP_SECONDS = 0.1   # untimed warm-up: at least this much GPU work
 
 
 def parse():
@@ -105,7 +108,15 @@ class HipEvents:
 
 
 def time_workload(wl, steps, warmup, torch, gi, dev):
-    """Returns dict with whole-call ms, GEMM-kernel ms (HIP events), flops."""
+    """Returns dict with whole-call ms, main-kernel ms (HIP events), flops.
+
+    Everything from the warm-up to the last timed call is enqueued without a
+    host synchronisation in between: an idle GPU lowers its clocks within
+    milliseconds, so a pause right before the timed calls would time the
+    clock ramp instead of the calls.  Both timed loops are bracketed by
+    events on the launch stream, and the host synchronises before the
+    warm-up and after the last loop.
+    """
     s = wl.shape
     _, tg, tw, out = device_inputs(wl, torch, dev)
     stream = torch.cuda.current_stream(dev)
@@ -114,45 +125,45 @@ def time_workload(wl, steps, warmup, torch, gi, dev):
         gi.grad_input(tg, tw, stride=s.stride, padding=(s.pad_h, s.pad_w),
                       input_hw=(s.H, s.W), out=out, stream=stream)
 
-    # Warm-up: W calls, and more until 0.1 s has passed, so both timed loops
-    # below run at the clocks of a busy GPU.
-    t_w = time.perf_counter()
-    n_w = 0
-    while n_w < warmup or time.perf_counter() - t_w < WARMUP_SECONDS:
-        call()
-        n_w += 1
-        if n_w % 8 == 0:
-            torch.cuda.synchronize()
-    torch.cuda.synchronize()
     hev = HipEvents()
     sp = stream.cuda_stream
-    # Main kernel alone: the library's main launch records a begin/end event
-    # pair with the dispatch's own timestamps.  This loop runs first, so the
-    # whole-call loop below also starts at the clocks of a busy GPU.
+    # Size the warm-up: at least W calls and at least WARMUP_SECONDS of GPU
+    # work, from the GPU time of 10 probe calls (taken on a cooler GPU, so an
+    # upper bound of the per-call time).
+    t0, t1 = hev.create(), hev.create()
+    torch.cuda.synchronize()
+    hev.hip.hipEventRecord(t0, sp)
+    for _ in range(10):
+        call()
+    hev.hip.hipEventRecord(t1, sp)
+    torch.cuda.synchronize()
+    per_call = max(hev.elapsed_ms(t0, t1) * 1e-3 / 10, 1e-6)
+    n_warm = int(min(max(warmup, math.ceil(WARMUP_SECONDS / per_call)), 20000))
     kb = [hev.create() for _ in range(steps)]
     ke = [hev.create() for _ in range(steps)]
+    wall0 = time.perf_counter()
+    for _ in range(n_warm):
+        call()
+    # Whole calls: exactly K steps between two events, nothing else recorded.
+    hev.hip.hipEventRecord(t0, sp)
+    for _ in range(steps):
+        call()
+    hev.hip.hipEventRecord(t1, sp)
+    # Main kernel alone: the library's main launch records a begin/end event
+    # pair with the dispatch's own timestamps.
     for i in range(steps):
         gi.set_profile_events(kb[i], ke[i])
         call()
     gi.set_profile_events(None, None)
     torch.cuda.synchronize()
-    kern_ms = [hev.elapsed_ms(kb[i], ke[i]) for i in range(steps)]
-    # Whole calls: K steps bracketed by two events, nothing else recorded.
-    t0, t1 = hev.create(), hev.create()
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    hev.hip.hipEventRecord(t0, sp)
-    for _ in range(steps):
-        call()
-    hev.hip.hipEventRecord(t1, sp)
-    torch.cuda.synchronize()
     wall1 = time.perf_counter()
     total_ms = hev.elapsed_ms(t0, t1)
+    kern_ms = [hev.elapsed_ms(kb[i], ke[i]) for i in range(steps)]
     for ev in kb + ke + [t0, t1]:
         hev.destroy(ev)
     return dict(ms_per_step=total_ms / steps, kernel_ms=float(np.mean(kern_ms)),
-                kernel_ms_min=float(np.min(kern_ms)), wall_ms=(wall1 - wall0) * 1e3 / steps,
-                flops=s.eff_flops)
+                kernel_ms_min=float(np.min(kern_ms)), wall_ms=(wall1 - wall0) * 1e3,
+                warmup_calls=n_warm, flops=s.eff_flops)
 
 
 def cpu_baseline(wl, target_s):
@@ -210,6 +221,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_calls": r["warmup_calls"],
         "ms_per_step": round(r["ms_per_step"], 5),
         "higher_is_better": True,
         "scaling": "weak",

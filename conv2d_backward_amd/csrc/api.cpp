@@ -426,11 +426,13 @@ bool plan_stem(const conv2d_gi_params &p, const std::vector<Phase> &phases, Stem
     const int64_t lim = 0x7fff0000LL;
     if ((int64_t)p.N * p.Co * p.oH * p.oW * 4 > lim) return false;
     if ((int64_t)p.N * p.Ci * p.H * p.W * 4 > lim) return false;
+    // Weight offsets: an out-of-range marker (the weight's size) plus a chunk
+    // offset must stay below 2^32.
+    if ((int64_t)p.Co * p.Ci * p.kH * p.kW * 4 > lim / 2) return false;
     gi::StemArgs &a = out.args;
     a = gi::StemArgs{};
     const int nchunks = (p.Co + 3) / 4;
     int maxHa = 0, maxWb = 0, maxJh = 1, maxJw = 1;
-    int64_t groups = 0;
     for (const Phase &ph : phases) {
         maxJh = std::max(maxJh, ph.J_h);
         maxJw = std::max(maxJw, ph.J_w);
@@ -457,10 +459,7 @@ bool plan_stem(const conv2d_gi_params &p, const std::vector<Phase> &phases, Stem
         s.J_w = ph.J_w;
         s.Ha = ph.Ha;
         s.Wb = ph.Wb;
-        s.woff = (int)groups;
-        groups += (int64_t)nchunks * T;
     }
-    if (groups * 64 > lim) return false;
     a.N = p.N;
     a.Ci = p.Ci;
     a.H = p.H;
@@ -477,9 +476,11 @@ bool plan_stem(const conv2d_gi_params &p, const std::vector<Phase> &phases, Stem
     a.pitch = pitch;
     a.g_bytes = (uint32_t)((int64_t)p.N * p.Co * p.oH * p.oW * 4);
     a.d_bytes = (uint32_t)((int64_t)p.N * p.Ci * p.H * p.W * 4);
-    a.w_bytes = (uint32_t)(groups * 64);
+    a.kH = p.kH;
+    a.kW = p.kW;
+    a.w_bytes = (uint32_t)((int64_t)p.Co * p.Ci * p.kH * p.kW * 4);
     if ((int64_t)p.N * a.tiles_r * a.tiles_c * a.nphases > INT32_MAX) return false;
-    out.ws_bytes = (size_t)std::max<int64_t>(groups * 64, 64);
+    out.ws_bytes = 0;  // the kernel reads the weight as given
     return true;
 }
 
@@ -572,10 +573,7 @@ int run(const T *grad_out, const T *weight, float *dst, const conv2d_gi_params *
         e = workspace_for(dev, stream, plan.ws_bytes, &ws);
         if (e != hipSuccess) return fail_hip(e);
         const int kHW = p->kH * p->kW;
-        if (plan.variant == CONV2D_GI_VARIANT_STEM) {
-            e = gi::launch_weight_stem_f32((const float *)weight, (float *)ws, plan.stem.args,
-                                           p->kH, p->kW, stream);
-        } else if (plan.variant == CONV2D_GI_VARIANT_HALO && bf16) {
+        if (plan.variant == CONV2D_GI_VARIANT_HALO && bf16) {
             HaloBf16Plan &h = plan.hb;
             uint16_t *gp = (uint16_t *)ws;
             uint16_t *wk = (uint16_t *)((char *)ws + h.gp_bytes);
@@ -603,7 +601,7 @@ int run(const T *grad_out, const T *weight, float *dst, const conv2d_gi_params *
         if (e == hipSuccess) {
             gi::StemArgs &a = plan.stem.args;
             a.grad_out = (const float *)grad_out;
-            a.wk = (const float *)ws;
+            a.w = (const float *)weight;
             a.dst = dst;
             e = gi::launch_stem_f32(a, stream, ev);
         }

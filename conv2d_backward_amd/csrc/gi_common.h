@@ -144,23 +144,18 @@ struct StemPhase {
     int32_t r_h, r_w;       // first tap of the phase: (rho + pad) mod stride
     int32_t J_h, J_w;       // taps of the phase per dimension
     int32_t Ha, Wb;         // pixels of the phase per image
-    int32_t woff;           // first (chunk, tap) group of the phase in the weight image
-    int32_t pad_;
 };
 
 // Arguments of the fp32 small-Ci kernel (Ci <= 4).  Work-groups are
 // (image, tile row, tile column, phase) with the phase fastest; a tile is
-// 16 x 16 pixels of the phase grid.
-//
-// Weight image (float4 units): wk[phase][chunk of 4 co][tap][ci of 4] holds
-// the four output channels chunk*4 .. +3 of one (ci, tap), zero past Ci / Co;
-// float4 index = (woff + chunk * taps + tap) * 4 + ci.
+// 16 x 16 pixels of the phase grid.  The kernel reads the weight in the
+// caller's layout [Co][Ci][kH][kW] (no reordered copy).
 struct StemArgs {
     const float *grad_out;  // [N, Co, oH, oW]
-    const float *wk;
+    const float *w;         // [Co, Ci, kH, kW]
     float *dst;             // [N, Ci, H, W]
     uint32_t g_bytes, w_bytes, d_bytes;
-    int32_t N, Ci, H, W, Co, oH, oW, stride;
+    int32_t N, Ci, H, W, Co, oH, oW, stride, kH, kW;
     int32_t nphases, nchunks;
     int32_t tiles_r, tiles_c;
     int32_t HPmax;          // LDS positions of the largest phase halo, rounded up to 16

@@ -83,7 +83,5 @@ int stem_f32_fixed_pitch();
 int stem_f32_halo_positions(int pitch);
 size_t stem_f32_lds_bytes(int hpmax);
 hipError_t launch_stem_f32(const StemArgs &a, hipStream_t s, const KernelEvents &ev);
-hipError_t launch_weight_stem_f32(const float *w, float *wk, const StemArgs &a, int kH, int kW,
-                                  hipStream_t s);
 
 }  // namespace gi

@@ -19,10 +19,12 @@
 // channels (a position's 4 channels are one 16-byte word, so one LDS read
 // serves 4 MFMAs) and the chunk's weights of every tap (a 16-byte word per
 // (tap, input channel) holding its 4 output channels; the 64 lanes read 4
-// distinct words, a broadcast).  Weights come through LDS rather than from
-// memory per tap: a 16-byte-per-lane load per tap for 4 distinct values
-// would keep the texture units of the CU busy for longer than the matrix
-// cores.  When the halo pitch and the tap grid are compile-time constants
+// distinct words, a broadcast).  The weights are gathered by the same direct
+// loads from the caller's [Co][Ci][kH][kW] tensor, 4 bytes per lane, so no
+// reordered copy (and no prologue launch) is needed; they come through LDS
+// rather than from memory per tap, since a 16-byte-per-lane load per tap for
+// 4 distinct values would keep the texture units of the CU busy for longer
+// than the matrix cores.  When the halo pitch and the tap grid are compile-time constants
 // every tap's shift is an immediate offset of the fragment reads.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -51,6 +53,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint3
 template <int N>
 __device__ __forceinline__ void wait_dma() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Column (0..15) of tile row `row` handled by lane: lane l = 16r + j takes
+// column (j - row * pitch) mod 16, so its halo position row * pitch + column
+// is j mod 16 plus a constant for every lane of a fragment read.  A 16-byte
+// LDS read is served 16 lanes per cycle, and on gfx950 the lanes of a cycle
+// are, within each half wave, those whose index bits 2..4 have the same
+// parity: rows r and r+1 then contribute complementary column quads, i.e.
+// 16 different j, i.e. 16 different bank groups, whatever the pitch.  (With
+// column j the rows' positions overlap mod 16 unless the pitch is a multiple
+// of 16.)
+__device__ __forceinline__ int stem_column(int lane, int row, int pitch) {
+    return ((lane & 15) - row * pitch) & 15;
 }
 
 // One phase with T taps (compile time) for this work-group's tile.  JW > 0
@@ -82,9 +97,9 @@ __device__ __forceinline__ void stem_phase(const StemArgs &A, const StemPhase &P
     const int hpos = HR * HP;
     const int oHW = A.oH * A.oW;
     const int stage = A.HPmax + kStemA;  // v4f per stage
-    // Direct loads per wave and stage: the halo groups and the weights (both
-    // waves load the same weights, so the count is the same for both).
-    constexpr int kDma = G + 1;
+    // Direct loads per wave and stage: the halo groups and two weight pieces.
+    constexpr int kWP = 2;  // weight pieces of 64 floats per wave: 4 x 64 >= 16 taps x 16
+    constexpr int kDma = G + kWP;
     static_assert(kDma <= 63, "vmcnt holds at most 63");
 
     // Halo DMA: group q = wave + 2k covers positions 16q .. 16q+15; lane ->
@@ -102,9 +117,23 @@ __device__ __forceinline__ void stem_phase(const StemArgs &A, const StemPhase &P
         goff[k] = v ? ((n * A.Co) * oHW + oh * A.oW + ow) * 4 : kOOB;
     }
     const int co_l = lane & 3;
-    // Weights of a chunk: T x 4 consecutive v4f of the image, one 16-byte
-    // direct load (lanes past T x 4 read past the buffer: zeros).
-    const int wl = lane < T * 4 ? (P.woff * 4 + lane) * 16 : (int)A.w_bytes;
+    // Weights of a chunk in LDS: float (tap * 4 + ci) * 4 + co, i.e. piece k
+    // of 64 floats holds taps 4k .. 4k+3; wave w loads pieces w and w + 2.
+    // Lane i of piece k reads weight[chunk*4 + i%4][(i/4)%4][kh][kw] of tap
+    // 4k + i/16 (an offset past the buffer, i.e. zero, for ci >= Ci or a tap
+    // past T; a channel past Co lies past the buffer by itself).
+    const int kHW = A.kH * A.kW;
+    int wofs[kWP];
+#pragma unroll
+    for (int u = 0; u < kWP; ++u) {
+        const int tap = 4 * (wave + 2 * u) + (lane >> 4);
+        const int ci = (lane >> 2) & 3;
+        const int j = tap / J_w, jw = tap - (tap / J_w) * J_w;
+        const int kh = P.r_h + A.stride * j, kw = P.r_w + A.stride * jw;
+        wofs[u] = (tap < T && ci < A.Ci) ? ((co_l * A.Ci + ci) * kHW + kh * A.kW + kw) * 4
+                                          : (int)A.w_bytes;
+    }
+    const int chunk_w = 4 * A.Ci * kHW * 4;  // bytes of 4 output channels
     auto issue = [&](int chunk, int buf) {
         // Channel part of this lane's offset; the buffer size (an offset past
         // its end) for a channel past Co or a chunk past the last.  Offsets
@@ -116,15 +145,21 @@ __device__ __forceinline__ void stem_phase(const StemArgs &A, const StemPhase &P
         for (int k = 0; k < G; ++k)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 grs, (lds_ptr_t)(st + (wave + 2 * k) * 16), 4, goff[k] + cc, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, (lds_ptr_t)(st + A.HPmax), 16,
-                                                 wl + chunk * T * 64, 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < kWP; ++u)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                wrs, (lds_ptr_t)(st + A.HPmax + (wave + 2 * u) * 16), 4, wofs[u],
+                chunk * chunk_w, 0, 0);
     };
 
-    // Halo position of this lane's pixel in each block, and tap shifts.
-    const int r = lane >> 4, c = lane & 15;
+    // Halo position of this lane's pixel in each block (column from
+    // stem_column), and tap shifts.
     int pb[2];
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) pb[blk] = (8 * wave + 4 * blk + r) * HP + c;
+    for (int blk = 0; blk < 2; ++blk) {
+        const int row = 8 * wave + 4 * blk + (lane >> 4);
+        pb[blk] = row * HP + stem_column(lane, row, HP);
+    }
     int shift[T];
     {
         int j = 0, jw = 0;
@@ -206,7 +241,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(4))) void g
     const int T = P.J_h * P.J_w;
     const int a0 = tr * kStemTile, b0 = tc * kStemTile;
     const __amdgpu_buffer_rsrc_t grs = make_rsrc(A.grad_out, A.g_bytes);
-    const __amdgpu_buffer_rsrc_t wrs = make_rsrc(A.wk, A.w_bytes);
+    const __amdgpu_buffer_rsrc_t wrs = make_rsrc(A.w, A.w_bytes);
     const __amdgpu_buffer_rsrc_t drs = make_rsrc(A.dst, A.d_bytes);
 
     v4f acc[4][2];
@@ -248,8 +283,9 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(4))) void g
     const int plane = A.H * A.W;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-        const int a = a0 + 8 * wave + 4 * blk + (lane >> 4);
-        const int b = b0 + (lane & 15);
+        const int row = 8 * wave + 4 * blk + (lane >> 4);
+        const int a = a0 + row;
+        const int b = b0 + stem_column(lane, row, A.pitch);
         const bool pv = a < P.Ha && b < P.Wb;
         const int pix = (P.rho_h + A.stride * a) * A.W + P.rho_w + A.stride * b;
         const v4f sum = (acc[0][blk] + acc[1][blk]) + (acc[2][blk] + acc[3][blk]);
@@ -259,36 +295,6 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(4))) void g
             const float v = sum[ci];
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), drs, off, 0, 0);
         }
-    }
-}
-
-// Weight image: one thread per float4 wk[phase][chunk][tap][ci] holding the
-// 4 output channels chunk*4 .. +3 (zero past Ci or Co).
-__global__ __launch_bounds__(256) void weight_stem_f32(const float *__restrict__ w,
-                                                       float *__restrict__ wk,
-                                                       const StemArgs A, int kH, int kW,
-                                                       int total4) {
-    for (int i = blockIdx.x * 256 + threadIdx.x; i < total4; i += gridDim.x * 256) {
-        int p = 0;
-        for (int k = 1; k < A.nphases; ++k)
-            if (i >= A.ph[k].woff * 4) p = k;
-        const StemPhase &P = A.ph[p];
-        const int T = P.J_h * P.J_w;
-        int r = i - P.woff * 4;
-        const int ci = r & 3;
-        r >>= 2;
-        const int t = r % T;
-        const int chunk = r / T;
-        const int j = t / P.J_w, jw = t - (t / P.J_w) * P.J_w;
-        const int kh = P.r_h + A.stride * j, kw = P.r_w + A.stride * jw;
-        float v[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int co = chunk * 4 + e;
-            v[e] = (ci < A.Ci && co < A.Co) ? w[(((int64_t)co * A.Ci + ci) * kH + kh) * kW + kw]
-                                            : 0.f;
-        }
-        ((v4f *)wk)[i] = v4f{v[0], v[1], v[2], v[3]};
     }
 }
 
@@ -332,17 +338,6 @@ hipError_t launch_stem_f32(const StemArgs &a, hipStream_t s, const KernelEvents 
     else
         hipExtLaunchKernelGGL((gi_stem_f32<0, kStemG>), dim3((unsigned)wgs), dim3(128),
                               (uint32_t)lds, s, ev.start, ev.stop, 0, a);
-    return hipGetLastError();
-}
-
-hipError_t launch_weight_stem_f32(const float *w, float *wk, const StemArgs &a, int kH, int kW,
-                                  hipStream_t s) {
-    int total4 = 0;
-    for (int p = 0; p < a.nphases; ++p)
-        total4 += a.nchunks * a.ph[p].J_h * a.ph[p].J_w * 4;
-    const int blocks = total4 > 0 ? (total4 + 255) / 256 : 1;
-    hipLaunchKernelGGL(weight_stem_f32, dim3(blocks < 4096 ? blocks : 4096), dim3(256), 0, s, w,
-                       wk, a, kH, kW, total4);
     return hipGetLastError();
 }
 

@@ -96,7 +96,7 @@ def _unprofiled_kernel_ms(bench_log: str, workload: str):
     o = line.get("other_workloads", {}).get(workload)
     if o is None:
         return None
-    return o["kernel_ms"], "bench.py (other workloads: 20 steps, 3 warm-up)"
+    return o["kernel_ms"], "bench.py (other workloads: 20 steps after at least 3 warm-up steps and 0.1 s)"
 
 
 def write_stats(run_dir: str, bench_log: str, workload: str, command: str,
