@@ -271,76 +271,39 @@ hipError_t launch_one(const HaloBf16Args &a, int tiles, int ci_tiles, size_t lds
 constexpr int kCfg[][4] = {{7, 9, 3, 30}, {7, 9, 0, 0}, {4, 9, 0, 0}, {7, 3, 0, 0}, {4, 3, 0, 0}};
 
 // grad_out NCHW bf16 -> zero-padded channel planes (gi_common.h).  One
-// work-group per (image n, block of 64 channels, band of RB rows of gp): the
-// band is read along ow (coalesced), packed into channel pairs in LDS, and
-// written plane by plane as 16-byte positions (coalesced along x).
+// thread per 16-byte position of one plane (8 channels): 8 two-byte loads
+// from the 8 channel images, one store.  Consecutive threads take consecutive
+// positions of a plane row, so every load and the store are coalesced along
+// the row; positions in the padding border load nothing.  `plane` is
+// (n * nchunks + chunk) * 4 + g, `pos` the position in the YP x XP plane.
 __device__ __forceinline__ void pad_planes_bf16(const uint16_t *__restrict__ g,
                                                 uint16_t *__restrict__ gp, const HaloBf16Args &A,
-                                                int oH, int oW, int pad_h, int pad_w, int RB,
-                                                int n, int cb, int yb, uint32_t *band) {
-    // band: [RB][oW][33] channel pairs
-    const int co0 = cb * 64, y0 = yb * RB;
-    const int yoff = A.kH - 1 - pad_h;  // oh = y - yoff
-    const int xoff = A.kW - 1 - pad_w;  // ow = x - xoff
-    // Thread -> one position of the band (fixed), looping over channel pairs:
-    // no division per element.
-    const int PB = RB * oW;
-    const int PBc = PB < 256 ? PB : 256;
-    const int cstep = 256 / PBc;
-    const int64_t plane = (int64_t)oH * oW;
-    for (int p0 = 0; p0 < PB; p0 += PBc) {
-        const int pos = p0 + threadIdx.x % PBc;
-        const int cp0 = threadIdx.x / PBc;
-        if (cp0 >= cstep || pos >= PB) continue;
-        const int ry = pos / oW, ow = pos - (pos / oW) * oW;
-        const int oh = y0 + ry - yoff;
-        const bool row_ok = y0 + ry < A.YP && oh >= 0 && oh < oH;
-        const int64_t base = ((int64_t)n * A.Co * oH + oh) * oW + ow;
-        uint32_t *dstb = band + pos * 33;
-        for (int cp = cp0; cp < 32; cp += 4 * cstep) {
-            uint32_t v[4];
+                                                int oH, int oW, int pad_h, int pad_w, int plane,
+                                                int pos) {
+    if (pos >= A.YP * A.XP) return;
+    const int y = pos / A.XP, x = pos - (pos / A.XP) * A.XP;
+    const int oh = y - (A.kH - 1 - pad_h), ow = x - (A.kW - 1 - pad_w);
+    const int gq = plane & 3, nc = plane >> 2;
+    const int n = nc / A.nchunks, chunk = nc - (nc / A.nchunks) * A.nchunks;
+    const int co0 = chunk * 32 + 8 * gq;
+    uint32_t h[4] = {0u, 0u, 0u, 0u};
+    if (oh >= 0 && oh < oH && ow >= 0 && ow < oW) {
+        const int64_t img = (int64_t)oH * oW;
+        const uint16_t *src = g + ((int64_t)n * A.Co + co0) * img + (int64_t)oh * oW + ow;
+        uint16_t v[8];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int c2 = cp + u * cstep;
-                const int co = co0 + 2 * c2;
-                uint32_t lo = 0, hi = 0;
-                if (row_ok && c2 < 32) {
-                    if (co < A.Co) lo = g[base + co * plane];
-                    if (co + 1 < A.Co) hi = g[base + (co + 1) * plane];
-                }
-                v[u] = lo | (hi << 16);
-            }
+        for (int e = 0; e < 8; ++e) v[e] = co0 + e < A.Co ? src[e * img] : (uint16_t)0;
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
-                if (cp + u * cstep < 32) dstb[cp + u * cstep] = v[u];
-        }
+        for (int q = 0; q < 4; ++q) h[q] = (uint32_t)v[2 * q] | ((uint32_t)v[2 * q + 1] << 16);
     }
-    __syncthreads();
-    // Plane q (channels co0 + 8q .. +7) of each band row: consecutive threads
-    // take consecutive x of one row (16-byte stores, coalesced).
-    const int groups = min(8, (A.Cop - co0) / 8);  // planes in this block
-    const int rows = min(RB, A.YP - y0);
-    const int per_plane = rows * A.XP;
-    for (int e = threadIdx.x; e < groups * per_plane; e += 256) {
-        const int q = e / per_plane, rem = e - q * per_plane;
-        const int ry = rem / A.XP, x = rem - ry * A.XP;
-        const int co = co0 + 8 * q;
-        const int64_t pl = ((int64_t)n * A.nchunks + co / 32) * 4 + (co / 8) % 4;
-        const int ow = x - xoff;
-        uint4 v = {0u, 0u, 0u, 0u};
-        if (ow >= 0 && ow < oW) {
-            const uint32_t *src = band + (ry * oW + ow) * 33 + 4 * q;
-            v = uint4{src[0], src[1], src[2], src[3]};
-        }
-        *(uint4 *)(gp + ((pl * A.YP + y0 + ry) * A.XP + x) * 8) = v;
-    }
+    *(uint4 *)(gp + ((int64_t)plane * A.YP * A.XP + pos) * 8) = uint4{h[0], h[1], h[2], h[3]};
 }
 
 // Weights [Co][Ci][kH][kW] bf16 -> A-fragment lane order (gi_common.h).  One
 // work-group per (chunk of 32 output channels, ci tile, lane group g): it
 // reads the 8 output channels 8g .. 8g+7 of the chunk for the tile's input
-// channels and every tap (one contiguous run per channel) into LDS, and each
-// thread then writes one lane's 16 bytes.
+// channels and every tap (one contiguous run per channel, coalesced) into
+// LDS, and each thread then writes one lane's 16 bytes.
 __device__ __forceinline__ void weight_frag_bf16(const uint16_t *__restrict__ w,
                                                  uint16_t *__restrict__ wk, const HaloBf16Args &A,
                                                  int chunk, int ct, int g, uint16_t *slab) {
@@ -387,27 +350,26 @@ __device__ __forceinline__ void weight_frag_bf16(const uint16_t *__restrict__ w,
 }
 
 // Both prologues in one launch (they are independent, so they overlap and
-// share one dispatch): work-groups [0, pad_wgs) pad grad_out, the rest
-// reorder the weight.
+// share one dispatch): the first frag_wgs work-groups reorder the weight
+// (the longer-lived ones, dispatched first), the rest pad grad_out (pad_bpp
+// per plane).
 __global__ __launch_bounds__(256) void prologues_bf16(const uint16_t *__restrict__ g,
                                                       uint16_t *__restrict__ gp,
                                                       const uint16_t *__restrict__ w,
                                                       uint16_t *__restrict__ wk,
                                                       const HaloBf16Args A, int oH, int oW,
-                                                      int pad_h, int pad_w, int RB, int pad_cb,
-                                                      int pad_yb, int ci_tiles) {
-    extern __shared__ uint32_t lds_u32[];
+                                                      int pad_h, int pad_w, int pad_bpp,
+                                                      int frag_wgs, int ci_tiles) {
+    extern __shared__ uint16_t slab[];
     int b = blockIdx.x;
-    const int pad_wgs = A.N * pad_cb * pad_yb;
-    if (b < pad_wgs) {
-        const int yb = b % pad_yb;
-        b /= pad_yb;
-        pad_planes_bf16(g, gp, A, oH, oW, pad_h, pad_w, RB, b / pad_cb, b % pad_cb, yb, lds_u32);
-    } else {
-        b -= pad_wgs;
+    if (b < frag_wgs) {
         const int gq = b & 3;
         b >>= 2;
-        weight_frag_bf16(w, wk, A, b / ci_tiles, b % ci_tiles, gq, (uint16_t *)lds_u32);
+        weight_frag_bf16(w, wk, A, b / ci_tiles, b % ci_tiles, gq, slab);
+    } else {
+        b -= frag_wgs;
+        const int plane = b / pad_bpp, pb = b - (b / pad_bpp) * pad_bpp;
+        pad_planes_bf16(g, gp, A, oH, oW, pad_h, pad_w, plane, pb * 256 + threadIdx.x);
     }
 }
 
@@ -436,18 +398,11 @@ hipError_t launch_halo_bf16(const HaloBf16Args &a, int cfg, int tiles, int ci_ti
 hipError_t launch_prologues_bf16(const uint16_t *g, uint16_t *gp, const uint16_t *w, uint16_t *wk,
                                  const HaloBf16Args &a, int oH, int oW, int pad_h, int pad_w,
                                  int ci_tiles, hipStream_t s) {
-    // Pad: rows per work-group at most what fits 16 KB of LDS, and few enough
-    // that the grid has some 2048 work-groups to keep loads in flight.
-    int RB = (int)(16384 / ((size_t)oW * 33 * sizeof(uint32_t)));
-    const int64_t others = (int64_t)a.N * ((a.Cop + 63) / 64);
-    const int want = (int)((a.YP * others + 2047) / 2048);
-    if (want < RB) RB = want;
-    RB = RB < 1 ? 1 : (RB > a.YP ? a.YP : RB);
-    const int pad_cb = (a.Cop + 63) / 64, pad_yb = (a.YP + RB - 1) / RB;
-    const size_t pad_lds = (size_t)RB * oW * 33 * sizeof(uint32_t);
-    const size_t frag_lds = (size_t)8 * 64 * a.kH * a.kW * sizeof(uint16_t);
-    const size_t lds = pad_lds > frag_lds ? pad_lds : frag_lds;
-    const int64_t wgs = (int64_t)a.N * pad_cb * pad_yb + (int64_t)a.nchunks * ci_tiles * 4;
+    const int pad_bpp = (a.YP * a.XP + 255) / 256;
+    const int64_t pad_wgs = (int64_t)a.N * a.nchunks * 4 * pad_bpp;
+    const int64_t frag_wgs = (int64_t)a.nchunks * ci_tiles * 4;
+    const int64_t wgs = pad_wgs + frag_wgs;
+    const size_t lds = (size_t)8 * 64 * a.kH * a.kW * sizeof(uint16_t);
     if (wgs > INT32_MAX) return hipErrorInvalidValue;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void *)prologues_bf16,
@@ -455,7 +410,7 @@ hipError_t launch_prologues_bf16(const uint16_t *g, uint16_t *gp, const uint16_t
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(prologues_bf16, dim3((unsigned)wgs), dim3(256), lds, s, g, gp, w, wk, a, oH,
-                       oW, pad_h, pad_w, RB, pad_cb, pad_yb, ci_tiles);
+                       oW, pad_h, pad_w, pad_bpp, (int)frag_wgs, ci_tiles);
     return hipGetLastError();
 }
 
