@@ -137,8 +137,9 @@ def set_variant(variant: int) -> int:
 
 
 def set_halo_tile(nb: int = 0, tile_rows: int = 0, tile_cols: int = 0, stages: int = 0):
-    """Force the fp32 HALO variant's pixel tile and pipeline depth (test hook);
-    set_halo_tile() restores the planner."""
+    """Force the HALO variant's pixel tile (fp32: blocks per work-group, tile
+    and pipeline depth; bf16: blocks per wave and tile) for later calls (test
+    hook); set_halo_tile() restores the planner."""
     _check(load_library().conv2d_gi_set_halo_tile(int(nb), int(tile_rows), int(tile_cols),
                                                   int(stages)))
 

@@ -352,14 +352,18 @@ bool plan_halo_bf16(const conv2d_gi_params &p, HaloBf16Plan &out) {
     if (gp_bytes > lim || wk_bytes > lim || (int64_t)p.N * p.Ci * p.H * p.W * 4 > lim)
         return false;
     static const int kNBW[] = {4, 7};
+    const int f_nb = g_tile_nb.load(), f_tr = g_tile_tr.load(), f_tc = g_tile_tc.load();
+    const bool forced = f_nb > 0;
     bool found = false;
     for (int nbw : kNBW) {
+        if (forced && nbw != f_nb) continue;
         const int maxpx = 2 * nbw * 16;
-        for (int cdiv = 1; cdiv <= 8; ++cdiv) {
-            const int TC = (p.W + cdiv - 1) / cdiv;
-            if (cdiv > 1 && TC == (p.W + cdiv - 2) / (cdiv - 1)) continue;
+        for (int cdiv = 1; cdiv <= (forced ? 1 : 8); ++cdiv) {
+            const int TC = forced ? f_tc : (p.W + cdiv - 1) / cdiv;
+            if (!forced && cdiv > 1 && TC == (p.W + cdiv - 2) / (cdiv - 1)) continue;
             if (TC > maxpx) continue;
-            for (int TR = std::min(maxpx / TC, p.H); TR >= 1; --TR) {
+            for (int TR = forced ? f_tr : std::min(maxpx / TC, p.H); TR >= 1; --TR) {
+                if (forced && (TR != f_tr || TR * TC > maxpx)) break;
                 const int HR = TR + p.kH - 1, HC = TC + p.kW - 1;
                 // Row pitch: holds a halo row, and = TC mod 16.
                 const int HP = round_to_residue(HC, 16, TC % 16);
@@ -757,8 +761,11 @@ int conv2d_gi_set_halo_tile(int nb, int tile_rows, int tile_cols, int stages) {
         g_tile_stages = 0;
         return CONV2D_GI_OK;
     }
-    if ((nb != 4 && nb != 8 && nb != 13) || tile_rows < 1 || tile_cols < 1 ||
-        tile_rows * tile_cols > nb * 16 || stages < 0 || stages == 1 || stages > 3)
+    // fp32 takes nb in {4, 8, 13} (blocks per work-group), bf16 nb in {4, 7}
+    // (blocks per wave, two waves across the tile).
+    const int most_px = (nb == 4 || nb == 7) ? 2 * nb * 16 : nb * 16;
+    if ((nb != 4 && nb != 7 && nb != 8 && nb != 13) || tile_rows < 1 || tile_cols < 1 ||
+        tile_rows * tile_cols > most_px || stages < 0 || stages == 1 || stages > 3)
         return CONV2D_GI_EINVAL;
     g_tile_tr = tile_rows;
     g_tile_tc = tile_cols;

@@ -311,6 +311,19 @@ __device__ __forceinline__ void weight_frag_bf16(const uint16_t *__restrict__ w,
     const int T = A.kH * A.kW;
     const int run = 64 * T;
     const int ci_rows = min(64, A.Ci - ct * 64);
+    if ((A.Ci * T) % 8 == 0 && (ci_rows * T) % 8 == 0) {
+        // Every channel's run starts 16-byte aligned and has whole 8-element
+        // pieces: 16-byte loads and stores.
+        const int pieces = run / 8;
+        for (int i = threadIdx.x; i < 8 * pieces; i += 256) {
+            const int c = i / pieces, r8 = i - (i / pieces) * pieces;
+            const int co = chunk * 32 + 8 * g + c;
+            uint4 v = {0u, 0u, 0u, 0u};
+            if (co < A.Co && r8 * 8 < ci_rows * T)
+                v = *(const uint4 *)(w + ((int64_t)co * A.Ci + (int64_t)ct * 64) * T + r8 * 8);
+            *(uint4 *)(slab + c * run + r8 * 8) = v;
+        }
+    } else {
     // Thread -> offsets r, r + 256, ... of each channel's run (no division).
     for (int r0 = 0; r0 < run; r0 += 256 * 2) {
         uint16_t v[2][8];
@@ -333,6 +346,7 @@ __device__ __forceinline__ void weight_frag_bf16(const uint16_t *__restrict__ w,
                 for (int c = 0; c < 8; ++c) slab[c * run + r] = v[u][c];
             }
         }
+    }
     }
     __syncthreads();
     // Lanes 16g .. 16g+15 of every (tap, ci block) of this (ci tile, chunk).

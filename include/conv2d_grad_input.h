@@ -145,13 +145,15 @@ CONV2D_GI_API const char *conv2d_gi_last_hip_error(void);
 CONV2D_GI_API int conv2d_gi_set_variant(int variant);
 
 /*
- * Test and diagnostic hook: force the pixel tile of the fp32 HALO variant for
- * later calls in this process: nb pixel blocks of 16 per work-group (4, 8 or
- * 13), a tile of tile_rows x tile_cols pixels of the stride-phase grid (at
- * most nb*16 pixels) and the LDS pipeline depth (2 or 3 stages; 0 lets the
- * planner choose).  A shape the forced tile does not fit (LDS, halo size) is
- * planned with GENERIC instead.  nb = 0 restores the planner.  Returns
- * CONV2D_GI_OK, or CONV2D_GI_EINVAL for values out of range.
+ * Test and diagnostic hook: force the pixel tile of the HALO variant for
+ * later calls in this process.  fp32: nb pixel blocks of 16 per work-group
+ * (4, 8 or 13), a tile of tile_rows x tile_cols pixels of the stride-phase
+ * grid (at most nb*16 pixels) and the LDS pipeline depth (2 or 3 stages; 0
+ * lets the planner choose).  bf16: nb pixel blocks of 16 per wave (4 or 7;
+ * two waves share the tile, so at most 2*nb*16 pixels); stages is ignored.
+ * A shape the forced tile does not fit (LDS, halo size) is planned with
+ * GENERIC instead.  nb = 0 restores the planner.  Returns CONV2D_GI_OK, or
+ * CONV2D_GI_EINVAL for values out of range.
  */
 CONV2D_GI_API int conv2d_gi_set_halo_tile(int nb, int tile_rows, int tile_cols, int stages);
 

@@ -233,6 +233,28 @@ def test_forced_halo_tile(idx):
         gi.set_halo_tile()
 
 
+# Every compile-time kernel instance on ragged channel counts (the planner
+# choices are pinned by tests/test_planner.py).
+from test_planner import FIXED_INSTANCES  # noqa: E402
+
+
+@pytest.mark.parametrize("idx", range(len(FIXED_INSTANCES)))
+def test_fixed_instances(idx):
+    shape, bf16, variant, tile, parts = FIXED_INSTANCES[idx]
+    if tile:
+        gi.set_halo_tile(tile[0], tile[1], tile[2], 0)
+    try:
+        gi.set_variant(variant)
+        desc = gi.plan(gi.make_params(*shape.as_tuple()[:10]), bf16)
+        gi.set_variant(gi.VARIANT_AUTO)
+        for part in parts:
+            assert part in desc, (part, desc)
+        full_parity(shape, 2100 + idx, "bf16" if bf16 else "f32", variant, dist="normal")
+    finally:
+        gi.set_variant(gi.VARIANT_AUTO)
+        gi.set_halo_tile()
+
+
 def test_tiny_workload_full():
     wl = workloads.BY_NAME["tiny"]
     s = wl.shape

@@ -1,0 +1,85 @@
+"""Host-only checks of the planner (no GPU): the graded workloads get the
+compile-time kernel instances documented for them, forced tiles reach each
+compile-time instance, and forced tiles are validated."""
+import pytest
+
+import conv2d_backward_amd as gi
+import workloads
+
+S = workloads.Shape
+
+
+@pytest.fixture(scope="module", autouse=True)
+def lib():
+    gi.load_library()
+    yield
+    gi.set_halo_tile()
+    gi.set_variant(gi.VARIANT_AUTO)
+
+
+def plan_of(shape, bf16=False):
+    return gi.plan(gi.make_params(*shape.as_tuple()[:10]), bf16)
+
+
+# Workload -> substrings its plan must contain.
+WORKLOAD_PLANS = {
+    "resnet_stage_3x3": ["variant=halo", "cfg=0", "HP=30"],
+    "deep_late_stage": ["variant=halo", "cfg=0", "tile=14x14", "HP=30"],
+    "strided_downsample": ["variant=halo", "cfg=2", "HP=15"],
+    "asym_1x7": ["variant=halo", "fold", "HP=23"],
+    "stem_7x7_s2": ["variant=stem", "ws_bytes=0"],
+    "deep_late_stage_bf16": ["variant=halo", "dtype=bf16", "cfg=0", "pitch=30"],
+    "tiny": ["variant=generic"],
+}
+
+
+@pytest.mark.parametrize("name", sorted(WORKLOAD_PLANS))
+def test_workload_plans(name):
+    wl = workloads.BY_NAME[name]
+    desc = plan_of(wl.shape, wl.dtype == "bf16")
+    for part in WORKLOAD_PLANS[name]:
+        assert part in desc, (name, part, desc)
+
+
+# (shape, bf16, variant, forced (nb, rows, cols) or None, plan substrings):
+# ragged channel counts on each compile-time instance.
+FIXED_INSTANCES = [
+    (S(3, 40, 28, 28, 20, 3, 3, 1, 1, 1), False, gi.VARIANT_HALO, (13, 14, 14),
+     ["cfg=0", "HP=30", "tile=14x14"]),
+    (S(3, 40, 28, 28, 20, 3, 3, 1, 1, 1), False, gi.VARIANT_HALO, (13, 7, 28),
+     ["cfg=0", "HP=30", "tile=7x28"]),
+    (S(2, 70, 28, 28, 20, 3, 3, 2, 1, 1), False, gi.VARIANT_HALO, (13, 14, 14),
+     ["cfg=2", "HP=15"]),
+    (S(4, 30, 17, 17, 36, 1, 7, 1, 0, 3), False, gi.VARIANT_HALO, (8, 7, 17),
+     ["cfg=4", "HP=33", "fold"]),
+    (S(3, 72, 14, 14, 40, 3, 3, 1, 1, 1), True, gi.VARIANT_HALO, (7, 14, 14),
+     ["cfg=0", "pitch=30"]),
+    (S(1, 2, 30, 30, 6, 7, 7, 2, 3, 3), False, gi.VARIANT_STEM, None,
+     ["variant=stem"]),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(FIXED_INSTANCES)))
+def test_fixed_instance_plans(idx):
+    shape, bf16, variant, tile, parts = FIXED_INSTANCES[idx]
+    try:
+        if tile:
+            gi.set_halo_tile(tile[0], tile[1], tile[2], 0)
+        gi.set_variant(variant)
+        desc = plan_of(shape, bf16)
+    finally:
+        gi.set_variant(gi.VARIANT_AUTO)
+        gi.set_halo_tile()
+    for part in parts:
+        assert part in desc, (part, desc)
+
+
+def test_forced_tile_validation():
+    with pytest.raises(gi.Conv2dGiError):
+        gi.set_halo_tile(5, 4, 4, 0)          # no such block count
+    with pytest.raises(gi.Conv2dGiError):
+        gi.set_halo_tile(7, 15, 15, 0)        # 225 > 2 * 7 * 16 pixels
+    with pytest.raises(gi.Conv2dGiError):
+        gi.set_halo_tile(13, 14, 14, 1)       # one stage is no pipeline
+    gi.set_halo_tile(7, 14, 14, 0)            # a bf16 tile of 196 pixels
+    gi.set_halo_tile()
