@@ -478,12 +478,26 @@ bool plan_stem(const conv2d_gi_params &p, const std::vector<Phase> &phases, Stem
     a.tiles_c = (maxWb + 15) / 16;
     a.HPmax = hpmax;
     a.pitch = pitch;
+    // Phase groups: the phases sorted by tap count, the largest paired with
+    // the smallest, so the groups' tap totals are close.
+    std::vector<int> order(phases.size());
+    for (size_t i = 0; i < order.size(); ++i) order[i] = (int)i;
+    std::stable_sort(order.begin(), order.end(), [&](int x, int y) {
+        return phases[x].J_h * phases[x].J_w > phases[y].J_h * phases[y].J_w;
+    });
+    const int np = (int)order.size();
+    a.ngroups = 0;
+    for (int lo = 0, hi = np - 1; lo <= hi; ++lo, --hi) {
+        a.group[a.ngroups][0] = (int8_t)order[lo];
+        a.group[a.ngroups][1] = (int8_t)(lo < hi ? order[hi] : -1);
+        ++a.ngroups;
+    }
     a.g_bytes = (uint32_t)((int64_t)p.N * p.Co * p.oH * p.oW * 4);
     a.d_bytes = (uint32_t)((int64_t)p.N * p.Ci * p.H * p.W * 4);
     a.kH = p.kH;
     a.kW = p.kW;
     a.w_bytes = (uint32_t)((int64_t)p.Co * p.Ci * p.kH * p.kW * 4);
-    if ((int64_t)p.N * a.tiles_r * a.tiles_c * a.nphases > INT32_MAX) return false;
+    if ((int64_t)p.N * a.tiles_r * a.tiles_c * a.ngroups > INT32_MAX) return false;
     out.ws_bytes = 0;  // the kernel reads the weight as given
     return true;
 }
@@ -655,7 +669,7 @@ std::string describe(const Plan &plan, bool bf16) {
     if (plan.variant == CONV2D_GI_VARIANT_STEM) {
         const gi::StemArgs &a = plan.stem.args;
         s += " launches=1 [tiles=" + std::to_string(a.N) + "x" + std::to_string(a.tiles_r) + "x" +
-             std::to_string(a.tiles_c) + "x" + std::to_string(a.nphases) +
+             std::to_string(a.tiles_c) + "x" + std::to_string(a.ngroups) +
              " chunks=" + std::to_string(a.nchunks);
         for (int i = 0; i < a.nphases; ++i) {
             const gi::StemPhase &ph = a.ph[i];

@@ -147,8 +147,9 @@ struct StemPhase {
 };
 
 // Arguments of the fp32 small-Ci kernel (Ci <= 4).  Work-groups are
-// (image, tile row, tile column, phase) with the phase fastest; a tile is
-// 16 x 16 pixels of the phase grid.  The kernel reads the weight in the
+// (image, tile row, tile column, phase group) with the group fastest; a tile
+// is 16 x 16 pixels of the phase grid, and a group is one or two phases whose
+// tap counts add up to about the same work as the other groups'.  The kernel reads the weight in the
 // caller's layout [Co][Ci][kH][kW] (no reordered copy).
 struct StemArgs {
     const float *grad_out;  // [N, Co, oH, oW]
@@ -160,6 +161,8 @@ struct StemArgs {
     int32_t tiles_r, tiles_c;
     int32_t HPmax;          // LDS positions of the largest phase halo, rounded up to 16
     int32_t pitch;          // halo row pitch in positions (>= 16 + J_w - 1 of every phase)
+    int32_t ngroups;        // work-groups per tile: phase groups of near-equal tap counts
+    int8_t group[kMaxPhasesPerLaunch][2];  // phases of each group (second -1 if alone)
     StemPhase ph[kMaxPhasesPerLaunch];
 };
 

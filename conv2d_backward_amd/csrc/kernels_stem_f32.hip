@@ -12,8 +12,11 @@
 // is pixel l of the wave's 64-pixel block, and after the contraction lane l
 // holds input channels 0..3 of its own pixel.
 //
-// Work-group: 128 threads = 2 waves over a 16 x 16 tile of one phase grid;
-// wave w owns tile rows 8w .. 8w+7 as two 4 x 16 pixel blocks.  Output
+// Work-group: 128 threads = 2 waves over a 16 x 16 tile of the phase grid,
+// for one or two phases in turn (pairs of near-equal total taps, so every
+// work-group does about the same work and the grid runs in one round
+// without a ragged tail); wave w owns tile rows 8w .. 8w+7 as two 4 x 16
+// pixel blocks.  Output
 // channels are streamed 4 at a time through a 3-stage LDS pipeline filled by
 // direct global -> LDS loads: per stage the tile's grad_out halo for the 4
 // channels (a position's 4 channels are one 16-byte word, so one LDS read
@@ -229,71 +232,76 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(4))) void g
     extern __shared__ __attribute__((aligned(16))) v4f sm4[];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    // Logical order: phase fastest, then tile column, row, image.
+    // Logical order: phase group fastest, then tile column, row, image.
     int bid = xcd_order(blockIdx.x, gridDim.x);
-    const int p = bid % A.nphases;
-    bid /= A.nphases;
+    const int grp = bid % A.ngroups;
+    bid /= A.ngroups;
     const int tc = bid % A.tiles_c;
     bid /= A.tiles_c;
     const int tr = bid % A.tiles_r;
     const int n = bid / A.tiles_r;
-    const StemPhase P = A.ph[p];
-    const int T = P.J_h * P.J_w;
     const int a0 = tr * kStemTile, b0 = tc * kStemTile;
     const __amdgpu_buffer_rsrc_t grs = make_rsrc(A.grad_out, A.g_bytes);
     const __amdgpu_buffer_rsrc_t wrs = make_rsrc(A.w, A.w_bytes);
     const __amdgpu_buffer_rsrc_t drs = make_rsrc(A.dst, A.d_bytes);
+    const int plane = A.H * A.W;
 
-    v4f acc[4][2];
+    for (int k = 0; k < 2; ++k) {
+        const int p = A.group[grp][k];
+        if (p < 0) break;
+        const StemPhase P = A.ph[p];
+        const int T = P.J_h * P.J_w;
+
+        v4f acc[4][2];
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
+        for (int e = 0; e < 4; ++e)
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk) acc[e][blk] = v4f{0.f, 0.f, 0.f, 0.f};
-    // Compile-time tap grids of the 7 x 7 stride-2 phases when the pitch is
-    // fixed; everything else through the run-time instances.
-    bool done = false;
-    if constexpr (PITCH > 0) {
-        switch (T * 16 + P.J_w) {
-            case 9 * 16 + 3: stem_phase<9, 3, PITCH, G>(A, P, sm4, acc, n, a0, b0, grs, wrs); done = true; break;
-            case 12 * 16 + 3: stem_phase<12, 3, PITCH, G>(A, P, sm4, acc, n, a0, b0, grs, wrs); done = true; break;
-            case 12 * 16 + 4: stem_phase<12, 4, PITCH, G>(A, P, sm4, acc, n, a0, b0, grs, wrs); done = true; break;
-            case 16 * 16 + 4: stem_phase<16, 4, PITCH, G>(A, P, sm4, acc, n, a0, b0, grs, wrs); done = true; break;
-            default: break;
+            for (int blk = 0; blk < 2; ++blk) acc[e][blk] = v4f{0.f, 0.f, 0.f, 0.f};
+        // Compile-time tap grids of the 7 x 7 stride-2 phases when the pitch is
+        // fixed; everything else through the run-time instances.
+        bool done = false;
+        if constexpr (PITCH > 0) {
+            switch (T * 16 + P.J_w) {
+                case 9 * 16 + 3: stem_phase<9, 3, PITCH, G>(A, P, sm4, acc, n, a0, b0, grs, wrs); done = true; break;
+                case 12 * 16 + 3: stem_phase<12, 3, PITCH, G>(A, P, sm4, acc, n, a0, b0, grs, wrs); done = true; break;
+                case 12 * 16 + 4: stem_phase<12, 4, PITCH, G>(A, P, sm4, acc, n, a0, b0, grs, wrs); done = true; break;
+                case 16 * 16 + 4: stem_phase<16, 4, PITCH, G>(A, P, sm4, acc, n, a0, b0, grs, wrs); done = true; break;
+                default: break;
+            }
         }
-    }
 #define GI_STEM_CASE(TT)                                                        \
     case TT:                                                                    \
         stem_phase<TT, 0, PITCH, G>(A, P, sm4, acc, n, a0, b0, grs, wrs);       \
         break;
-    if (!done) switch (T) {
-        GI_STEM_CASE(1)
-        GI_STEM_CASE(2)
-        GI_STEM_CASE(3)
-        GI_STEM_CASE(4)
-        GI_STEM_CASE(6)
-        GI_STEM_CASE(8)
-        GI_STEM_CASE(9)
-        GI_STEM_CASE(12)
-        GI_STEM_CASE(16)
-        default: break;  // no taps: the phase's pixels are zero
-    }
+        if (!done) switch (T) {
+            GI_STEM_CASE(1)
+            GI_STEM_CASE(2)
+            GI_STEM_CASE(3)
+            GI_STEM_CASE(4)
+            GI_STEM_CASE(6)
+            GI_STEM_CASE(8)
+            GI_STEM_CASE(9)
+            GI_STEM_CASE(12)
+            GI_STEM_CASE(16)
+            default: break;  // no taps: the phase's pixels are zero
+        }
 #undef GI_STEM_CASE
 
-    // Epilogue: lane l holds input channels 0..3 of pixel l of each block.
-    const int plane = A.H * A.W;
+        // Epilogue: lane l holds input channels 0..3 of its pixel of each block.
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-        const int row = 8 * wave + 4 * blk + (lane >> 4);
-        const int a = a0 + row;
-        const int b = b0 + stem_column(lane, row, A.pitch);
-        const bool pv = a < P.Ha && b < P.Wb;
-        const int pix = (P.rho_h + A.stride * a) * A.W + P.rho_w + A.stride * b;
-        const v4f sum = (acc[0][blk] + acc[1][blk]) + (acc[2][blk] + acc[3][blk]);
+        for (int blk = 0; blk < 2; ++blk) {
+            const int row = 8 * wave + 4 * blk + (lane >> 4);
+            const int a = a0 + row;
+            const int b = b0 + stem_column(lane, row, A.pitch);
+            const bool pv = a < P.Ha && b < P.Wb;
+            const int pix = (P.rho_h + A.stride * a) * A.W + P.rho_w + A.stride * b;
+            const v4f sum = (acc[0][blk] + acc[1][blk]) + (acc[2][blk] + acc[3][blk]);
 #pragma unroll
-        for (int ci = 0; ci < 4; ++ci) {
-            const int off = (pv && ci < A.Ci) ? ((n * A.Ci + ci) * plane + pix) * 4 : kOOB;
-            const float v = sum[ci];
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), drs, off, 0, 0);
+            for (int ci = 0; ci < 4; ++ci) {
+                const int off = (pv && ci < A.Ci) ? ((n * A.Ci + ci) * plane + pix) * 4 : kOOB;
+                const float v = sum[ci];
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), drs, off, 0, 0);
+            }
         }
     }
 }
@@ -330,7 +338,7 @@ size_t stem_f32_lds_bytes(int hpmax) {
 hipError_t launch_stem_f32(const StemArgs &a, hipStream_t s, const KernelEvents &ev) {
     if (a.HPmax != stem_f32_halo_positions(a.pitch)) return hipErrorInvalidValue;
     const size_t lds = stem_f32_lds_bytes(a.HPmax);
-    const int64_t wgs = (int64_t)a.N * a.tiles_r * a.tiles_c * a.nphases;
+    const int64_t wgs = (int64_t)a.N * a.tiles_r * a.tiles_c * a.ngroups;
     if (lds > 64 * 1024) return hipErrorInvalidValue;
     if (a.pitch == kStemPitch)
         hipExtLaunchKernelGGL((gi_stem_f32<kStemPitch, kStemFixedG>), dim3((unsigned)wgs),
