@@ -422,9 +422,10 @@ bool plan_halo_bf16(const conv2d_gi_params &p, HaloBf16Plan &out) {
     return true;
 }
 
-// Small-Ci plan (fp32, Ci <= 4): 16 x 16 phase-grid tiles, one work-group
-// per (image, tile, phase); every phase's tap count must be one the kernel
-// is built for and its halo must fit the kernel's staging.
+// Small-Ci plan (fp32, Ci <= 4): 16 x 16 phase-grid tiles; phase groups of
+// near-equal tap totals, run in sets of up to two per work-group over one
+// grad_out halo.  Every phase's tap count must be one the kernel is built
+// for, and every set's halo and taps must fit the kernel's staging.
 bool plan_stem(const conv2d_gi_params &p, const std::vector<Phase> &phases, StemPlan &out) {
     if (p.Ci > 4 || phases.empty() || (int)phases.size() > gi::kMaxPhasesPerLaunch) return false;
     const int64_t lim = 0x7fff0000LL;
@@ -436,20 +437,10 @@ bool plan_stem(const conv2d_gi_params &p, const std::vector<Phase> &phases, Stem
     gi::StemArgs &a = out.args;
     a = gi::StemArgs{};
     const int nchunks = (p.Co + 3) / 4;
-    int maxHa = 0, maxWb = 0, maxJh = 1, maxJw = 1;
-    for (const Phase &ph : phases) {
-        maxJh = std::max(maxJh, ph.J_h);
-        maxJw = std::max(maxJw, ph.J_w);
-    }
-    // One halo row pitch for every phase: the widest halo row.
-    const int pitch = 16 + maxJw - 1;
-    // Every phase's halo must fit the kernel's per-stage halo region.
-    const int hpmax = gi::stem_f32_halo_positions(pitch);
-    if ((16 + maxJh - 1) * pitch > hpmax) return false;
+    int maxHa = 0, maxWb = 0;
     for (size_t i = 0; i < phases.size(); ++i) {
         const Phase &ph = phases[i];
-        const int T = ph.J_h * ph.J_w;
-        if (!gi::stem_f32_taps_ok(T)) return false;
+        if (!gi::stem_f32_taps_ok(ph.J_h * ph.J_w)) return false;
         maxHa = std::max(maxHa, ph.Ha);
         maxWb = std::max(maxWb, ph.Wb);
         gi::StemPhase &s = a.ph[i];
@@ -464,20 +455,6 @@ bool plan_stem(const conv2d_gi_params &p, const std::vector<Phase> &phases, Stem
         s.Ha = ph.Ha;
         s.Wb = ph.Wb;
     }
-    a.N = p.N;
-    a.Ci = p.Ci;
-    a.H = p.H;
-    a.W = p.W;
-    a.Co = p.Co;
-    a.oH = p.oH;
-    a.oW = p.oW;
-    a.stride = p.stride;
-    a.nphases = (int)phases.size();
-    a.nchunks = nchunks;
-    a.tiles_r = (maxHa + 15) / 16;
-    a.tiles_c = (maxWb + 15) / 16;
-    a.HPmax = hpmax;
-    a.pitch = pitch;
     // Phase groups: the phases sorted by tap count, the largest paired with
     // the smallest, so the groups' tap totals are close.
     std::vector<int> order(phases.size());
@@ -492,12 +469,77 @@ bool plan_stem(const conv2d_gi_params &p, const std::vector<Phase> &phases, Stem
         a.group[a.ngroups][1] = (int8_t)(lo < hi ? order[hi] : -1);
         ++a.ngroups;
     }
+    const int G = gi::kStemGroupsPerWg;
+    a.nsets = (a.ngroups + G - 1) / G;
+    const int waves = gi::stem_f32_waves(a.ngroups);
+    // Per set: the halo covering every phase with taps (origin relative to
+    // the tile: q - (J - 1) rows and columns; extent 16 + J - 1), each
+    // phase's origin inside it, and the phase's first staged tap.
+    int pitch = 1, rows = 0;
+    for (int st = 0; st < a.nsets; ++st) {
+        int oh = INT32_MAX, ow = INT32_MAX, eh = INT32_MIN, ew = INT32_MIN, taps = 0;
+        for (int g = st * G; g < std::min(a.ngroups, (st + 1) * G); ++g)
+            for (int k = 0; k < 2; ++k) {
+                const int pi = a.group[g][k];
+                if (pi < 0) continue;
+                gi::StemPhase &s = a.ph[pi];
+                s.tb = taps;
+                taps += s.J_h * s.J_w;
+                if (s.J_h * s.J_w == 0) continue;
+                oh = std::min(oh, s.q_h - (s.J_h - 1));
+                ow = std::min(ow, s.q_w - (s.J_w - 1));
+                eh = std::max(eh, s.q_h + 16);
+                ew = std::max(ew, s.q_w + 16);
+            }
+        if (taps > waves * gi::kStemTapsPerWave) return false;
+        if (oh == INT32_MAX) {  // no phase of the set has taps: nothing to load
+            a.set_org[st][0] = a.set_org[st][1] = 0;
+            a.set_ext[st][0] = a.set_ext[st][1] = 0;
+            continue;
+        }
+        a.set_org[st][0] = oh;
+        a.set_org[st][1] = ow;
+        a.set_ext[st][0] = eh - oh;
+        a.set_ext[st][1] = ew - ow;
+        pitch = std::max(pitch, ew - ow);
+        rows = std::max(rows, eh - oh);
+        for (int g = st * G; g < std::min(a.ngroups, (st + 1) * G); ++g)
+            for (int k = 0; k < 2; ++k) {
+                const int pi = a.group[g][k];
+                if (pi < 0) continue;
+                gi::StemPhase &s = a.ph[pi];
+                s.dr = s.J_h * s.J_w ? s.q_h - (s.J_h - 1) - oh : 0;
+                s.dc = s.J_h * s.J_w ? s.q_w - (s.J_w - 1) - ow : 0;
+            }
+    }
+    // The fixed pitch when every halo fits it: its instance has compile-time
+    // tap shifts.
+    if (pitch <= gi::stem_f32_fixed_pitch() &&
+        rows * gi::stem_f32_fixed_pitch() <=
+            gi::stem_f32_halo_positions(gi::stem_f32_fixed_pitch()))
+        pitch = gi::stem_f32_fixed_pitch();
+    const int hpmax = gi::stem_f32_halo_positions(pitch);
+    if (rows * pitch > hpmax) return false;
+    a.N = p.N;
+    a.Ci = p.Ci;
+    a.H = p.H;
+    a.W = p.W;
+    a.Co = p.Co;
+    a.oH = p.oH;
+    a.oW = p.oW;
+    a.stride = p.stride;
+    a.nphases = (int)phases.size();
+    a.nchunks = nchunks;
+    a.tiles_r = (maxHa + 15) / 16;
+    a.tiles_c = (maxWb + 15) / 16;
+    a.HPmax = hpmax;
+    a.pitch = pitch;
     a.g_bytes = (uint32_t)((int64_t)p.N * p.Co * p.oH * p.oW * 4);
     a.d_bytes = (uint32_t)((int64_t)p.N * p.Ci * p.H * p.W * 4);
     a.kH = p.kH;
     a.kW = p.kW;
     a.w_bytes = (uint32_t)((int64_t)p.Co * p.Ci * p.kH * p.kW * 4);
-    if ((int64_t)p.N * a.tiles_r * a.tiles_c * a.ngroups > INT32_MAX) return false;
+    if ((int64_t)p.N * a.tiles_r * a.tiles_c * a.nsets > INT32_MAX) return false;
     out.ws_bytes = 0;  // the kernel reads the weight as given
     return true;
 }
@@ -669,8 +711,9 @@ std::string describe(const Plan &plan, bool bf16) {
     if (plan.variant == CONV2D_GI_VARIANT_STEM) {
         const gi::StemArgs &a = plan.stem.args;
         s += " launches=1 [tiles=" + std::to_string(a.N) + "x" + std::to_string(a.tiles_r) + "x" +
-             std::to_string(a.tiles_c) + "x" + std::to_string(a.ngroups) +
-             " chunks=" + std::to_string(a.nchunks);
+             std::to_string(a.tiles_c) + "x" + std::to_string(a.nsets) +
+             " waves=" + std::to_string(gi::stem_f32_waves(a.ngroups)) +
+             " pitch=" + std::to_string(a.pitch) + " chunks=" + std::to_string(a.nchunks);
         for (int i = 0; i < a.nphases; ++i) {
             const gi::StemPhase &ph = a.ph[i];
             s += " phase(" + std::to_string(ph.rho_h) + "," + std::to_string(ph.rho_w) +

@@ -144,13 +144,24 @@ struct StemPhase {
     int32_t r_h, r_w;       // first tap of the phase: (rho + pad) mod stride
     int32_t J_h, J_w;       // taps of the phase per dimension
     int32_t Ha, Wb;         // pixels of the phase per image
+    int32_t dr, dc;         // origin of the phase's halo inside its work-group's halo
+    int32_t tb;             // first tap of the phase in its work-group's weight staging
 };
 
+// Work-group shape of the small-Ci kernel: waves per work-group is
+// 2 * (phase groups per work-group), each wave owning 8 tile rows of one
+// group; the weights of up to kStemTapsPerWave taps per wave are staged.
+constexpr int kStemGroupsPerWg = 2;
+constexpr int kStemTapsPerWave = 16;
+
 // Arguments of the fp32 small-Ci kernel (Ci <= 4).  Work-groups are
-// (image, tile row, tile column, phase group) with the group fastest; a tile
-// is 16 x 16 pixels of the phase grid, and a group is one or two phases whose
-// tap counts add up to about the same work as the other groups'.  The kernel reads the weight in the
-// caller's layout [Co][Ci][kH][kW] (no reordered copy).
+// (image, tile row, tile column, set of phase groups), the set fastest; a tile
+// is 16 x 16 pixels of the phase grid.  A phase group is one or two phases
+// whose tap counts add up to about the same as the other groups'; a
+// work-group runs up to kStemGroupsPerWg groups side by side (two waves per
+// group) over one grad_out halo that covers every phase of the set.  The
+// kernel reads the weight in the caller's layout [Co][Ci][kH][kW] (no
+// reordered copy).
 struct StemArgs {
     const float *grad_out;  // [N, Co, oH, oW]
     const float *w;         // [Co, Ci, kH, kW]
@@ -159,10 +170,15 @@ struct StemArgs {
     int32_t N, Ci, H, W, Co, oH, oW, stride, kH, kW;
     int32_t nphases, nchunks;
     int32_t tiles_r, tiles_c;
-    int32_t HPmax;          // LDS positions of the largest phase halo, rounded up to 16
-    int32_t pitch;          // halo row pitch in positions (>= 16 + J_w - 1 of every phase)
-    int32_t ngroups;        // work-groups per tile: phase groups of near-equal tap counts
+    int32_t HPmax;          // LDS halo positions per stage (a multiple of 16 * waves)
+    int32_t pitch;          // halo row pitch in positions (>= every set's halo width)
+    int32_t ngroups;        // phase groups
+    int32_t nsets;          // sets of phase groups (work-groups per tile)
     int8_t group[kMaxPhasesPerLaunch][2];  // phases of each group (second -1 if alone)
+    // Per set: halo origin relative to the tile (rows, columns) and its
+    // extent (rows, columns).
+    int32_t set_org[kMaxPhasesPerLaunch][2];
+    int32_t set_ext[kMaxPhasesPerLaunch][2];
     StemPhase ph[kMaxPhasesPerLaunch];
 };
 

@@ -77,11 +77,13 @@ hipError_t launch_prologues_bf16(const uint16_t *g, uint16_t *gp, const uint16_t
 // phases have a tap count in the served set (stem_f32_taps_ok).
 bool stem_f32_taps_ok(int taps);
 // The halo pitch the stem kernel has a compile-time instance for; the halo
-// positions per LDS stage of the instance used for a pitch (every phase's
-// halo must fit); the LDS bytes of the kernel for that many positions.
+// positions per LDS stage of the instance used for a pitch (every set's
+// halo must fit); waves per work-group for a number of phase groups; the
+// LDS bytes of the kernel for that many positions and waves.
 int stem_f32_fixed_pitch();
 int stem_f32_halo_positions(int pitch);
-size_t stem_f32_lds_bytes(int hpmax);
+int stem_f32_waves(int ngroups);
+size_t stem_f32_lds_bytes(int hpmax, int waves);
 hipError_t launch_stem_f32(const StemArgs &a, hipStream_t s, const KernelEvents &ev);
 
 }  // namespace gi

@@ -188,6 +188,10 @@ STEM_SHAPES = [
     workloads.Shape(1, 3, 30, 30, 13, 5, 5, 2, 2, 2),      # 5x5 stride 2: 9, 6, 6, 4 taps
     workloads.Shape(2, 2, 11, 10, 3, 2, 2, 3, 0, 0),       # kernel < stride: empty phases
     workloads.Shape(1, 3, 40, 36, 64, 7, 7, 2, 3, 3),      # several tiles per phase
+    workloads.Shape(1, 3, 1, 40, 8, 7, 7, 2, 3, 3),        # one image row: one phase group
+    workloads.Shape(1, 3, 36, 36, 8, 6, 6, 2, 3, 3),       # phases' halos at different origins
+    workloads.Shape(2, 3, 20, 30, 8, 1, 6, 1, 0, 2),       # 1x6: run-time pitch, one group
+    workloads.Shape(1, 3, 20, 40, 10, 2, 12, 2, 0, 5),     # 2x12 stride 2: run-time pitch, two groups
 ]
 
 
