@@ -539,7 +539,15 @@ bool plan_stem(const conv2d_gi_params &p, const std::vector<Phase> &phases, Stem
     a.kH = p.kH;
     a.kW = p.kW;
     a.w_bytes = (uint32_t)((int64_t)p.Co * p.Ci * p.kH * p.kW * 4);
-    if ((int64_t)p.N * a.tiles_r * a.tiles_c * a.nsets > INT32_MAX) return false;
+    const int64_t units = (int64_t)p.N * a.tiles_r * a.tiles_c * a.nsets;
+    if (4 * units > INT32_MAX) return false;
+    // Units past the last whole wave of kCUs run as quarter tiles, so the
+    // compute units' shares differ by at most a quarter tile, provided every
+    // work-group still finds a slot in the first wave (4 per compute unit).
+    const int64_t rem = units % kCUs;
+    const int64_t nfull = units - rem;
+    a.nfull = (int32_t)units;
+    if (a.nsets == 1 && rem > 0 && nfull + 4 * rem <= 4LL * kCUs) a.nfull = (int32_t)nfull;
     out.ws_bytes = 0;  // the kernel reads the weight as given
     return true;
 }
@@ -712,6 +720,7 @@ std::string describe(const Plan &plan, bool bf16) {
         const gi::StemArgs &a = plan.stem.args;
         s += " launches=1 [tiles=" + std::to_string(a.N) + "x" + std::to_string(a.tiles_r) + "x" +
              std::to_string(a.tiles_c) + "x" + std::to_string(a.nsets) +
+             " whole=" + std::to_string(a.nfull) +
              " waves=" + std::to_string(gi::stem_f32_waves(a.ngroups)) +
              " pitch=" + std::to_string(a.pitch) + " chunks=" + std::to_string(a.nchunks);
         for (int i = 0; i < a.nphases; ++i) {

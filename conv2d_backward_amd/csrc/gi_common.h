@@ -154,9 +154,11 @@ struct StemPhase {
 constexpr int kStemGroupsPerWg = 2;
 constexpr int kStemTapsPerWave = 16;
 
-// Arguments of the fp32 small-Ci kernel (Ci <= 4).  Work-groups are
+// Arguments of the fp32 small-Ci kernel (Ci <= 4).  Work units are
 // (image, tile row, tile column, set of phase groups), the set fastest; a tile
-// is 16 x 16 pixels of the phase grid.  A phase group is one or two phases
+// is 16 x 16 pixels of the phase grid.  The first nfull units are one
+// work-group each; with one set per tile, the units after them are split
+// into four work-groups of 4 tile rows each.  A phase group is one or two phases
 // whose tap counts add up to about the same as the other groups'; a
 // work-group runs up to kStemGroupsPerWg groups side by side (two waves per
 // group) over one grad_out halo that covers every phase of the set.  The
@@ -174,6 +176,7 @@ struct StemArgs {
     int32_t pitch;          // halo row pitch in positions (>= every set's halo width)
     int32_t ngroups;        // phase groups
     int32_t nsets;          // sets of phase groups (work-groups per tile)
+    int32_t nfull;          // (image, tile, set) units run whole; the rest in quarters
     int8_t group[kMaxPhasesPerLaunch][2];  // phases of each group (second -1 if alone)
     // Per set: halo origin relative to the tile (rows, columns) and its
     // extent (rows, columns).

@@ -89,37 +89,37 @@ __device__ __forceinline__ void tap_shifts(int (&shift)[T], int J_h, int J_w, in
     }
 }
 
-// The taps of one phase over one staged chunk of 4 output channels.  JW > 0
-// fixes the phase's tap columns and PITCH > 0 the halo row pitch at compile
-// time (they must equal the run-time values); every tap's shift is then an
-// immediate offset of the fragment reads.  hs: the stage's halo; as: the
-// phase's first tap in the stage's weights, offset by this lane's input
-// channel; pp: this lane's halo position in each block, including the
-// phase's origin in the halo.
+// The taps of one phase over one staged chunk of 4 output channels, for NB
+// pixel blocks of this wave.  JW > 0 fixes the phase's tap columns and
+// PITCH > 0 the halo row pitch at compile time (they must equal the run-time
+// values); every tap's shift is then an immediate offset of the fragment
+// reads.  hs: the stage's halo; as: the phase's first tap in the stage's
+// weights, offset by this lane's input channel; pb: this lane's halo
+// position in each block, including the phase's origin in the halo.
 //
 // Accumulators: two per pixel block (even and odd output channels of the
 // chunk), so consecutive MFMAs never depend on each other; the other
 // waves of the SIMD cover the rest of the 4x4x1 latency.
-template <int T, int JW, int PITCH>
-__device__ __forceinline__ void stem_taps(const v4f *hs, const v4f *as, const int (&pb)[2],
+template <int T, int JW, int PITCH, int NB>
+__device__ __forceinline__ void stem_taps(const v4f *hs, const v4f *as, const int (&pb)[NB],
                                           int J_h_rt, int J_w_rt, int HP_rt,
-                                          v4f (&acc)[2][2]) {
+                                          v4f (&acc)[NB][2]) {
     const int J_w = JW > 0 ? JW : J_w_rt;
     const int J_h = JW > 0 ? T / (JW > 0 ? JW : 1) : J_h_rt;
     const int HP = PITCH > 0 ? PITCH : HP_rt;
     int shift[T];
     tap_shifts<T>(shift, J_h, J_w, HP);
-    int pp[2];
+    int pp[NB];
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
+    for (int blk = 0; blk < NB; ++blk) {
         pp[blk] = pb[blk];
         asm volatile("" : "+v"(pp[blk]));
     }
     // B fragments two taps ahead (three slots), A one tap ahead.
-    v4f fb[3][2], fa[2];
+    v4f fb[3][NB], fa[2];
     auto bfetch = [&](int t, int sl) {
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk) fb[sl][blk] = hs[pp[blk] + shift[t]];
+        for (int blk = 0; blk < NB; ++blk) fb[sl][blk] = hs[pp[blk] + shift[t]];
     };
     bfetch(0, 0);
     fa[0] = as[0];
@@ -132,7 +132,7 @@ __device__ __forceinline__ void stem_taps(const v4f *hs, const v4f *as, const in
 #pragma unroll
         for (int e = 0; e < 4; ++e)
 #pragma unroll
-            for (int blk = 0; blk < 2; ++blk)
+            for (int blk = 0; blk < NB; ++blk)
                 acc[blk][e & 1] = __builtin_amdgcn_mfma_f32_4x4x1f32(
                     fa[t & 1][e], fb[sl][blk][e], acc[blk][e & 1], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
@@ -140,25 +140,25 @@ __device__ __forceinline__ void stem_taps(const v4f *hs, const v4f *as, const in
 }
 
 // One phase's taps for one chunk, dispatched to a compile-time tap grid.
-template <int PITCH>
+template <int PITCH, int NB>
 __device__ __forceinline__ void stem_phase_chunk(const StemPhase &P, const v4f *hs,
-                                                 const v4f *as, const int (&pb)[2], int HP,
-                                                 v4f (&acc)[2][2]) {
+                                                 const v4f *as, const int (&pb)[NB], int HP,
+                                                 v4f (&acc)[NB][2]) {
     const int T = P.J_h * P.J_w;
     // Compile-time tap grids of the 7 x 7 stride-2 phases when the pitch is
     // fixed; everything else through the run-time instances.
     if constexpr (PITCH > 0) {
         switch (T * 16 + P.J_w) {
-            case 9 * 16 + 3: stem_taps<9, 3, PITCH>(hs, as, pb, P.J_h, P.J_w, HP, acc); return;
-            case 12 * 16 + 3: stem_taps<12, 3, PITCH>(hs, as, pb, P.J_h, P.J_w, HP, acc); return;
-            case 12 * 16 + 4: stem_taps<12, 4, PITCH>(hs, as, pb, P.J_h, P.J_w, HP, acc); return;
-            case 16 * 16 + 4: stem_taps<16, 4, PITCH>(hs, as, pb, P.J_h, P.J_w, HP, acc); return;
+            case 9 * 16 + 3: stem_taps<9, 3, PITCH, NB>(hs, as, pb, P.J_h, P.J_w, HP, acc); return;
+            case 12 * 16 + 3: stem_taps<12, 3, PITCH, NB>(hs, as, pb, P.J_h, P.J_w, HP, acc); return;
+            case 12 * 16 + 4: stem_taps<12, 4, PITCH, NB>(hs, as, pb, P.J_h, P.J_w, HP, acc); return;
+            case 16 * 16 + 4: stem_taps<16, 4, PITCH, NB>(hs, as, pb, P.J_h, P.J_w, HP, acc); return;
             default: break;
         }
     }
 #define GI_STEM_CASE(TT)                                                   \
     case TT:                                                               \
-        stem_taps<TT, 0, PITCH>(hs, as, pb, P.J_h, P.J_w, HP, acc);        \
+        stem_taps<TT, 0, PITCH, NB>(hs, as, pb, P.J_h, P.J_w, HP, acc);    \
         return;
     switch (T) {
         GI_STEM_CASE(1)
@@ -175,12 +175,11 @@ __device__ __forceinline__ void stem_phase_chunk(const StemPhase &P, const v4f *
 #undef GI_STEM_CASE
 }
 
-// Work-group: NW = 2 * (phase groups) waves over a 16 x 16 tile of the
-// phase grids of one set of phase groups; waves 2g and 2g+1 run group g
-// (one or two phases), each over 8 tile rows as two 4 x 16 pixel blocks.
-// PITCH > 0: the halo row pitch at compile time.  G: halo loads of 16
-// positions per wave and stage (the stage's halo region is NW * G * 16 =
-// A.HPmax positions).
+// The work of one wave over a tile: phases myph (up to two, -1 for none) of
+// NB pixel blocks of 4 x 16 starting at tile row row0.  Every wave of the
+// work-group runs it (it contains the work-group's barriers and its share of
+// the direct loads).  G: halo loads of 16 positions per wave and stage (the
+// stage's halo region is NW * G * 16 = A.HPmax positions).
 //
 // Per chunk of 4 output channels, one 3-stage LDS pipeline stage holds the
 // halo that covers every phase of the set (a position's 4 channels are one
@@ -193,21 +192,11 @@ __device__ __forceinline__ void stem_phase_chunk(const StemPhase &P, const v4f *
 // such loads read zeros or unused weights), so the issue carries no
 // per-load selects, and every wave issues the same fixed number of loads
 // per stage, so "this stage has landed" is a wait on a compile-time count.
-template <int PITCH, int G, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) void gi_stem_f32(
-    const StemArgs A) {
-    extern __shared__ __attribute__((aligned(16))) v4f sm4[];
+template <int PITCH, int G, int NW, int NB>
+__device__ __forceinline__ void stem_tile(const StemArgs &A, v4f *sm4, int n, int a0, int b0,
+                                          int set, const int (&myph)[2], int row0) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    // Logical order: set fastest, then tile column, row, image.
-    int bid = xcd_order(blockIdx.x, gridDim.x);
-    const int set = bid % A.nsets;
-    bid /= A.nsets;
-    const int tc = bid % A.tiles_c;
-    bid /= A.tiles_c;
-    const int tr = bid % A.tiles_r;
-    const int n = bid / A.tiles_r;
-    const int a0 = tr * kStemTile, b0 = tc * kStemTile;
     const __amdgpu_buffer_rsrc_t grs = make_rsrc(A.grad_out, A.g_bytes);
     const __amdgpu_buffer_rsrc_t wrs = make_rsrc(A.w, A.w_bytes);
     const __amdgpu_buffer_rsrc_t drs = make_rsrc(A.dst, A.d_bytes);
@@ -219,15 +208,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
     constexpr int kDma = G + kWP;               // direct loads per wave and stage
     static_assert(kDma <= 63, "vmcnt holds at most 63");
     static_assert(NW * kWP * 64 == 16 * kWT, "weight pieces cover the staged taps");
-
-    // This wave's group and its phases (-1: none).
-    const int grp = set * kStemGroupsPerWg + wave / 2;
-    const int half = wave & 1;
-    int myph[2] = {-1, -1};
-    if (grp < A.ngroups) {
-        myph[0] = A.group[grp][0];
-        myph[1] = A.group[grp][1];
-    }
 
     // Halo DMA: group q = wave + NW*k covers positions 16q .. 16q+15 of the
     // set's halo; lane -> (position 16q + lane/4, channel lane%4).
@@ -297,22 +277,22 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
 
     // Halo position of this lane's pixel in each block (column from
     // stem_column), per phase with the phase's origin in the set's halo.
-    int pb[2][2];
+    int pb[2][NB];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
         const int p = myph[k] < 0 ? 0 : myph[k];
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-            const int row = 8 * half + 4 * blk + (lane >> 4);
+        for (int blk = 0; blk < NB; ++blk) {
+            const int row = row0 + 4 * blk + (lane >> 4);
             pb[k][blk] = (row + A.ph[p].dr) * HP + A.ph[p].dc + stem_column(lane, row, HP);
         }
     }
 
-    v4f acc[2][2][2];
+    v4f acc[2][NB][2];
 #pragma unroll
     for (int k = 0; k < 2; ++k)
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
+        for (int blk = 0; blk < NB; ++blk)
             acc[k][blk][0] = acc[k][blk][1] = v4f{0.f, 0.f, 0.f, 0.f};
 
     issue(0, 0);
@@ -329,7 +309,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
         for (int k = 0; k < 2; ++k) {
             if (myph[k] < 0) continue;
             const StemPhase &P = A.ph[myph[k]];
-            stem_phase_chunk<PITCH>(P, hs, hs + A.HPmax + P.tb * 4 + co_l, pb[k], HP, acc[k]);
+            stem_phase_chunk<PITCH, NB>(P, hs, hs + A.HPmax + P.tb * 4 + co_l, pb[k], HP,
+                                        acc[k]);
         }
         // Stage chunk+1 must have landed; the loads of chunk+2 may still be
         // in flight.
@@ -347,8 +328,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
         if (myph[k] < 0) continue;
         const StemPhase &P = A.ph[myph[k]];
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-            const int row = 8 * half + 4 * blk + (lane >> 4);
+        for (int blk = 0; blk < NB; ++blk) {
+            const int row = row0 + 4 * blk + (lane >> 4);
             const int a = a0 + row;
             const int b = b0 + stem_column(lane, row, HP);
             const bool pv = a < P.Ha && b < P.Wb;
@@ -360,6 +341,57 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
                 __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sum[ci]), drs, off, 0, 0);
             }
         }
+    }
+}
+
+// Work-groups: NW = 2 * (phase groups per set) waves.  The first A.nfull
+// work-groups each take a whole (image, tile, set): waves 2g and 2g+1 run
+// group g over 8 tile rows each (two pixel blocks).  The remaining ones
+// (present only with one set per tile) each take a quarter of one of the
+// tiles left over: 4 tile rows, wave w running the w-th phase of the set on
+// one pixel block.  Spreading those last tiles as quarters keeps every
+// compute unit's share of the grid within a quarter tile of the others'.
+template <int PITCH, int G, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) void gi_stem_f32(
+    const StemArgs A) {
+    extern __shared__ __attribute__((aligned(16))) v4f sm4[];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const bool quarter = (int)blockIdx.x >= A.nfull;
+    // Logical order within each part: set (or quarter) fastest, then tile
+    // column, row, image.
+    int bid, set = 0, qr = 0;
+    if (!quarter) {
+        bid = xcd_order(blockIdx.x, A.nfull);
+        set = bid % A.nsets;
+        bid /= A.nsets;
+    } else {
+        bid = xcd_order(blockIdx.x - A.nfull, gridDim.x - A.nfull);
+        qr = bid & 3;
+        bid = A.nfull + (bid >> 2);
+    }
+    const int tc = bid % A.tiles_c;
+    bid /= A.tiles_c;
+    const int tr = bid % A.tiles_r;
+    const int n = bid / A.tiles_r;
+    const int a0 = tr * kStemTile, b0 = tc * kStemTile;
+
+    if (!quarter) {
+        // This wave's group and its phases (-1: none).
+        const int grp = set * kStemGroupsPerWg + wave / 2;
+        int myph[2] = {-1, -1};
+        if (grp < A.ngroups) {
+            myph[0] = A.group[grp][0];
+            myph[1] = A.group[grp][1];
+        }
+        stem_tile<PITCH, G, NW, 2>(A, sm4, n, a0, b0, set, myph, 8 * (wave & 1));
+    } else {
+        // The wave-th phase of the (only) set.
+        int myph[2] = {-1, -1};
+        int k = 0;
+        for (int g = 0; g < kStemGroupsPerWg && g < A.ngroups; ++g)
+            for (int e = 0; e < 2; ++e)
+                if (A.group[g][e] >= 0 && k++ == wave) myph[0] = A.group[g][e];
+        stem_tile<PITCH, G, NW, 1>(A, sm4, n, a0, b0, 0, myph, 4 * qr);
     }
 }
 
@@ -400,7 +432,9 @@ hipError_t launch_stem_f32(const StemArgs &a, hipStream_t s, const KernelEvents 
     const int nw = stem_f32_waves(a.ngroups);
     if (a.nsets != (a.ngroups + kStemGroupsPerWg - 1) / kStemGroupsPerWg) return hipErrorInvalidValue;
     const size_t lds = stem_f32_lds_bytes(a.HPmax, nw);
-    const int64_t wgs = (int64_t)a.N * a.tiles_r * a.tiles_c * a.nsets;
+    const int64_t units = (int64_t)a.N * a.tiles_r * a.tiles_c * a.nsets;
+    if (a.nfull > units || (a.nfull < units && a.nsets != 1)) return hipErrorInvalidValue;
+    const int64_t wgs = a.nfull + 4 * (units - a.nfull);
     if (lds > 64 * 1024) return hipErrorInvalidValue;
     const dim3 grid((unsigned)wgs), block(64 * nw);
     const uint32_t sh = (uint32_t)lds;

@@ -192,6 +192,8 @@ STEM_SHAPES = [
     workloads.Shape(1, 3, 36, 36, 8, 6, 6, 2, 3, 3),       # phases' halos at different origins
     workloads.Shape(2, 3, 20, 30, 8, 1, 6, 1, 0, 2),       # 1x6: run-time pitch, one group
     workloads.Shape(1, 3, 20, 40, 10, 2, 12, 2, 0, 5),     # 2x12 stride 2: run-time pitch, two groups
+    workloads.Shape(70, 3, 34, 34, 8, 7, 7, 2, 3, 3),      # whole tiles, then quarter tiles
+    workloads.Shape(65, 3, 20, 20, 5, 3, 3, 1, 1, 1),      # the same with one phase group
 ]
 
 

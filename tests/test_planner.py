@@ -27,7 +27,7 @@ WORKLOAD_PLANS = {
     "deep_late_stage": ["variant=halo", "cfg=0", "tile=14x14", "HP=30"],
     "strided_downsample": ["variant=halo", "cfg=2", "HP=15"],
     "asym_1x7": ["variant=halo", "fold", "HP=23"],
-    "stem_7x7_s2": ["variant=stem", "ws_bytes=0", "tiles=16x7x7x1 waves=4 pitch=19"],
+    "stem_7x7_s2": ["variant=stem", "ws_bytes=0", "tiles=16x7x7x1 whole=768 waves=4 pitch=19"],
     "deep_late_stage_bf16": ["variant=halo", "dtype=bf16", "cfg=0", "pitch=30"],
     "tiny": ["variant=generic"],
 }
