@@ -17,7 +17,7 @@ import os
 
 __all__ = [
     "grad_input", "Conv2dGiParams", "Conv2dGiError", "LibraryNotBuilt", "load_library",
-    "make_params", "validate", "plan", "set_variant", "set_halo_tile", "release_workspaces", "set_profile_events", "library_path", "exported_names",
+    "make_params", "validate", "plan", "set_variant", "set_halo_tile", "set_halo_split", "release_workspaces", "set_profile_events", "library_path", "exported_names",
     "OK", "EINVAL", "EUNSUPPORTED", "EHIP", "VARIANT_AUTO", "VARIANT_GENERIC", "VARIANT_HALO", "VARIANT_STEM",
 ]
 
@@ -79,6 +79,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.conv2d_gi_plan.restype = ctypes.c_int
     lib.conv2d_gi_set_halo_tile.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]
     lib.conv2d_gi_set_halo_tile.restype = ctypes.c_int
+    lib.conv2d_gi_set_halo_split.argtypes = [ctypes.c_int]
+    lib.conv2d_gi_set_halo_split.restype = ctypes.c_int
     lib.conv2d_gi_set_profile_events.argtypes = [P, P]
     lib.conv2d_gi_set_profile_events.restype = None
     lib.conv2d_gi_release_workspaces.argtypes = []
@@ -94,7 +96,8 @@ def exported_names():
     """Names of the C entry points the binding wraps."""
     return ["conv2d_grad_input", "conv2d_grad_input_bf16", "conv2d_gi_validate",
             "conv2d_gi_strerror", "conv2d_gi_last_hip_error", "conv2d_gi_set_variant",
-            "conv2d_gi_plan", "conv2d_gi_set_halo_tile", "conv2d_gi_set_profile_events",
+            "conv2d_gi_plan", "conv2d_gi_set_halo_tile", "conv2d_gi_set_halo_split",
+            "conv2d_gi_set_profile_events",
             "conv2d_gi_release_workspaces", "conv2d_gi_version"]
 
 
@@ -142,6 +145,13 @@ def set_halo_tile(nb: int = 0, tile_rows: int = 0, tile_cols: int = 0, stages: i
     hook); set_halo_tile() restores the planner."""
     _check(load_library().conv2d_gi_set_halo_tile(int(nb), int(tile_rows), int(tile_cols),
                                                   int(stages)))
+
+
+def set_halo_split(groups: int = 0):
+    """Force 1 or 2 thread groups splitting the output channels of an fp32
+    HALO work-group for later calls (test hook); set_halo_split() restores the
+    planner."""
+    _check(load_library().conv2d_gi_set_halo_split(int(groups)))
 
 
 def release_workspaces():

@@ -27,6 +27,7 @@ using gi::Phase;
 std::atomic<int> g_variant{CONV2D_GI_VARIANT_AUTO};
 // Forced halo tile (test hook): NB pixel blocks, TR x TC phase-grid pixels; 0 = planner.
 std::atomic<int> g_tile_nb{0}, g_tile_tr{0}, g_tile_tc{0}, g_tile_stages{0};
+std::atomic<int> g_halo_split{0};
 thread_local char g_last_hip[256] = "";
 thread_local hipEvent_t g_prof_begin = nullptr, g_prof_end = nullptr;
 
@@ -229,18 +230,23 @@ bool plan_halo(const conv2d_gi_params &p, const std::vector<Phase> &phases, Halo
                 // fall on disjoint banks.
                 const int groups = (HR * HP + 31) / 32;
                 const int bl = (groups + 3) / 4;
-                const int cfg = gi::halo_f32_config(nb, tmask, bl, HP, jw_common);
+                // ks thread groups split each work-group's output channels.
+                for (int ks = 1; ks <= 2; ++ks) {
+                const int f_ks = g_halo_split.load();
+                if (f_ks > 0 && ks != f_ks) continue;
+                const int cfg = gi::halo_f32_config(nb, tmask, bl, HP, jw_common, ks);
                 if (cfg < 0) continue;
                 const int HPc = round_to_residue(groups * 32, 32, 16);
                 const int cps = gi::halo_f32_cps(cfg);
-                // Three pipeline stages when two work-groups still fit a CU, or
-                // when one work-group per CU is all that fits anyway.
+                // Three pipeline stages when two work-groups (or two thread
+                // groups) still fit a CU, or when one is all that fits anyway.
+                const size_t budget = kLdsBytes / 2;
                 int stages = 3;
                 size_t lds = gi::halo_f32_lds_bytes(maxT, HPc, 3, cps);
-                if (lds > kLdsBytes / 2) {
+                if (lds > budget) {
                     stages = 2;
                     lds = gi::halo_f32_lds_bytes(maxT, HPc, 2, cps);
-                    if (lds > kLdsBytes / 2 &&
+                    if (lds > budget && ks == 1 &&
                         gi::halo_f32_lds_bytes(maxT, HPc, 3, cps) <= kLdsBytes) {
                         stages = 3;
                         lds = gi::halo_f32_lds_bytes(maxT, HPc, 3, cps);
@@ -250,6 +256,9 @@ bool plan_halo(const conv2d_gi_params &p, const std::vector<Phase> &phases, Halo
                     stages = g_tile_stages.load();
                     lds = gi::halo_f32_lds_bytes(maxT, HPc, stages, cps);
                 }
+                // A split work-group holds every group's stages, and its
+                // accumulators once, for the hand-over.
+                lds = std::max(lds * ks, ks > 1 ? (size_t)nb * 256 * 16 : (size_t)0);
                 if (lds > kLdsBytes) continue;
                 const int64_t row_tiles = (rows_total + TR - 1) / TR;
                 const int64_t col_tiles = (maxWb + TC - 1) / TC;
@@ -263,13 +272,16 @@ bool plan_halo(const conv2d_gi_params &p, const std::vector<Phase> &phases, Halo
                 // fragment reads with compile-time tap offsets save time.
                 const int64_t per_cu = (wgs + kCUs - 1) / kCUs;
                 const double eff_nb = nb >= 13 ? 1.0 : nb >= 8 ? 0.85 : 0.75;
-                const double eff_occ = per_cu >= 2 ? 1.0 : 0.9;
+                // One wave per SIMD (a lone unsplit work-group per CU) hides
+                // less latency.
+                const double eff_occ = per_cu >= 2 || ks > 1 ? 1.0 : 0.9;
                 const bool conflict_free = (HP - TC) % 16 == 0 || TC % 16 == 0;
                 const double eff_pitch = (gi::halo_f32_fixed_pitch(cfg) ? 1.05 : 1.0) *
                                          (conflict_free ? 1.03 : 1.0);
                 // 16x16x4 MFMA: 32 cycles per 16 pixels x 4 k; plus halo staging.
                 const double per_wg = 8.0 * nb * kall +
-                                      (double)nchunks * phases.size() * HR * HP * 2.0 + 4000.0;
+                                      (double)nchunks * phases.size() * HR * HP * 2.0 + 4000.0 +
+                                      (ks > 1 ? 1500.0 * phases.size() : 0.0);
                 // Among equal critical paths, fewer work-groups do less total work.
                 const double cost = (double)per_cu * per_wg / (eff_nb * eff_occ * eff_pitch) +
                                     0.05 * (double)wgs * per_wg / kCUs;
@@ -291,6 +303,7 @@ bool plan_halo(const conv2d_gi_params &p, const std::vector<Phase> &phases, Halo
                     a.HP = HP;
                     a.HPc = HPc;
                     a.stages = stages;
+                }
                 }
                 }
             }
@@ -747,6 +760,8 @@ std::string describe(const Plan &plan, bool bf16) {
         const HaloPlan &h = plan.halo;
         const gi::HaloArgs &a = h.args;
         s += " launches=1 [nb=" + std::to_string(h.nb) + " cfg=" + std::to_string(h.cfg) +
+             (gi::halo_f32_ks(h.cfg) > 1 ? " split=" + std::to_string(gi::halo_f32_ks(h.cfg))
+                                          : std::string()) +
              " bl=" + std::to_string(h.bl) + " tile=" + std::to_string(a.TR) + "x" +
              std::to_string(a.TC) + (a.fold ? " fold" : "") + " wgs=" + std::to_string(h.tiles) +
              "x" + std::to_string(h.ci_tiles) + " lds=" + std::to_string(h.lds) +
@@ -837,6 +852,12 @@ int conv2d_gi_set_halo_tile(int nb, int tile_rows, int tile_cols, int stages) {
     g_tile_tc = tile_cols;
     g_tile_stages = stages;
     g_tile_nb = nb;
+    return CONV2D_GI_OK;
+}
+
+int conv2d_gi_set_halo_split(int groups) {
+    if (groups < 0 || groups > 2) return CONV2D_GI_EINVAL;
+    g_halo_split = groups;
     return CONV2D_GI_OK;
 }
 

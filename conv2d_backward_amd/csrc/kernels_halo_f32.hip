@@ -115,13 +115,13 @@ __device__ __forceinline__ void wait_dma() {
 //   * halo: for co pair cp and a group of 32 positions, even lanes load
 //     output channel 2cp and odd lanes 2cp+1 of position base + lane/2, which
 //     lands exactly on the float2 layout.
-template <int T, int NB, int HG, int CPS, int PITCH, int JW>
+template <int T, int NB, int HG, int CPS, int PITCH, int JW, int KS>
 __device__ __forceinline__ void run_phase(const HaloArgs &A, const HaloPhase &P, v2f *smem2,
                                           const int (&pbase)[NB], v4f (&acc)[NB], int a0,
-                                          int b0, int n_img, int ci_tile,
+                                          int b0, int n_img, int ci_tile, int kg,
                                           __amdgpu_buffer_rsrc_t grs,
                                           __amdgpu_buffer_rsrc_t wrs) {
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x & 255;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, g4 = lane >> 4;
@@ -139,6 +139,11 @@ __device__ __forceinline__ void run_phase(const HaloArgs &A, const HaloPhase &P,
     const int groups = (hpos + 31) / 32;
     const int oHW = A.oH * A.oW;
     const int nstages = (A.nchunks + CPS - 1) / CPS;
+    // This thread group's stages [s0, s1): with KS groups, group kg takes the
+    // kg-th of KS near-equal runs; every group iterates h times (past s1 with
+    // no arithmetic and loads that read zeros) so the barriers line up.
+    const int h = (nstages + KS - 1) / KS;
+    const int s0 = kg * h, s1 = min(nstages, s0 + h);
 
     // Halo shift of every tap (j, jw): (J_h-1-j) rows and (J_w-1-jw) columns.
     int shift[T];
@@ -193,7 +198,8 @@ __device__ __forceinline__ void run_phase(const HaloArgs &A, const HaloPhase &P,
 #pragma unroll
         for (int i = 0; i < WPW; ++i) {
             const int m = wave + 4 * i;
-            const bool real = m < 2 * T * CPS && stg * CPS + m / (2 * T) < A.nchunks;
+            const bool real =
+                stg < s1 && m < 2 * T * CPS && stg * CPS + m / (2 * T) < A.nchunks;
             dma16(wrs, real ? st + m * 128 : dummy, real ? wb + m * 1024 : kOOB);
         }
         v2f *hs = st + wreg;
@@ -211,7 +217,7 @@ __device__ __forceinline__ void run_phase(const HaloArgs &A, const HaloPhase &P,
 #pragma unroll
             for (int k = 0; k < HG; ++k) {
                 const int g = wave + 4 * k;
-                const bool real = g < groups;
+                const bool real = g < groups && stg < s1;
 #pragma unroll
                 for (int cp = 0; cp < 4; ++cp) {
                     const int co = (stg * CPS + o) * kHaloBC + 2 * cp + co_lane;
@@ -227,21 +233,22 @@ __device__ __forceinline__ void run_phase(const HaloArgs &A, const HaloPhase &P,
     // is multiplied (with 2, stage s+1).
     const int D = A.stages - 1;
     wait_dma<0>();  // the previous phase's stores count too: drain them first
-    issue(0, 0);
-    if (D == 2 && nstages > 1) {
-        issue(1, 1);
+    issue(s0, 0);
+    if (D == 2 && h > 1) {
+        issue(s0 + 1, 1);
         wait_dma<NDMA>();
     } else {
         wait_dma<0>();
     }
     __syncthreads();
-    for (int stg = 0; stg < nstages; ++stg) {
-        const int cur = stg % A.stages;
-        const bool ahead = stg + D < nstages;
-        if (ahead) issue(stg + D, (stg + D) % A.stages);
+    for (int i = 0; i < h; ++i) {
+        const int stg = s0 + i;
+        const int cur = i % A.stages;
+        const bool ahead = i + D < h;
+        if (ahead) issue(stg + D, (i + D) % A.stages);
 #pragma unroll
         for (int o = 0; o < CPS; ++o) {
-            if (CPS > 1 && stg * CPS + o >= A.nchunks) break;
+            if (stg >= s1 || (CPS > 1 && stg * CPS + o >= A.nchunks)) break;
             // Odd co pairs hold their 64 input channels rotated by 16 (weight
             // image layout), so the two co pairs of a half-wave fall on
             // disjoint banks.
@@ -284,12 +291,20 @@ __device__ __forceinline__ void run_phase(const HaloArgs &A, const HaloPhase &P,
     }
 }
 
-template <int NB, int HG, unsigned TMASK, int CPS, int OCC, int PITCH, int JW>
-__global__ __launch_bounds__(256, OCC) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void gi_halo_f32(
+// KS > 1: the work-group is KS groups of 4 waves that split the output
+// channels of every phase (each group its own LDS stages, run to the same
+// barrier count), and sum their accumulators through LDS before the store:
+// for grids too small to put two work-groups on every compute unit, it gives
+// each SIMD two waves instead of one.
+template <int NB, int HG, unsigned TMASK, int CPS, int OCC, int PITCH, int JW, int KS>
+__global__ __launch_bounds__(256 * KS, OCC) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void gi_halo_f32(
     const HaloArgs A) {
-    extern __shared__ __attribute__((aligned(16))) v2f smem2[];
+    extern __shared__ __attribute__((aligned(16))) v2f smem_all[];
 
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x & 255;
+    const int kg = KS > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 8) : 0;
+    v2f *const smem2 =
+        smem_all + kg * (A.stages * CPS * (A.maxT * 4 * 64 + 4 * A.HPc) + 128);
     const int lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, g4 = lane >> 4;
 
@@ -344,8 +359,8 @@ __global__ __launch_bounds__(256, OCC) __attribute__((amdgpu_waves_per_eu(OCC, O
 #define GI_HALO_CASE_JW(TT, JJ)                                                              \
     case TT * 16 + JJ:                                                                       \
         if constexpr ((TMASK & tbit(TT)) != 0) {                                             \
-            run_phase<TT, NB, HG, CPS, PITCH, JJ>(A, P, smem2, pbase, acc, a0, b0, n_img,      \
-                                                  ci_tile, grs, wrs);                        \
+            run_phase<TT, NB, HG, CPS, PITCH, JJ, KS>(A, P, smem2, pbase, acc, a0, b0, n_img,  \
+                                                      ci_tile, kg, grs, wrs);                \
             done = true;                                                                     \
         }                                                                                    \
         break;
@@ -362,8 +377,8 @@ __global__ __launch_bounds__(256, OCC) __attribute__((amdgpu_waves_per_eu(OCC, O
 #define GI_HALO_CASE(TT)                                                                     \
     case TT:                                                                                 \
         if constexpr ((TMASK & tbit(TT)) != 0)                                               \
-            run_phase<TT, NB, HG, CPS, PITCH, (JW > 0 ? JW : 0)>(A, P, smem2, pbase, acc, a0, \
-                                                                b0, n_img, ci_tile, grs, wrs); \
+            run_phase<TT, NB, HG, CPS, PITCH, (JW > 0 ? JW : 0), KS>(                          \
+                A, P, smem2, pbase, acc, a0, b0, n_img, ci_tile, kg, grs, wrs);              \
         break;
         if (!done) switch (T) {
             GI_HALO_CASE(1)
@@ -377,9 +392,27 @@ __global__ __launch_bounds__(256, OCC) __attribute__((amdgpu_waves_per_eu(OCC, O
         }
 #undef GI_HALO_CASE
 
+        // Groups past the first hand their sums to the first through LDS
+        // (free once every group's last stage is done: run_phase ends on a
+        // barrier after its loads have landed), in group order.
+        if constexpr (KS > 1) {
+            v4f *red = (v4f *)smem_all;
+#pragma unroll
+            for (int g = 1; g < KS; ++g) {
+                if (kg == g)
+#pragma unroll
+                    for (int blk = 0; blk < NB; ++blk) red[blk * 256 + tid] = acc[blk];
+                __syncthreads();
+                if (kg == 0)
+#pragma unroll
+                    for (int blk = 0; blk < NB; ++blk) acc[blk] += red[blk * 256 + tid];
+                __syncthreads();
+            }
+        }
         // Epilogue: D[4*g4 + r][l16] of each block, NCHW.
 #pragma unroll
         for (int blk = 0; blk < NB; ++blk) {
+            if (KS > 1 && kg != 0) break;
             int img, a, b;
             const bool pv = tile_pixel(A, P, blk * 16 + l16, a0, b0, n_img, img, a, b);
             const int pix = (P.rho_h + A.stride * a) * A.W + P.rho_w + A.stride * b;
@@ -401,22 +434,26 @@ constexpr unsigned kT7 = tbit(7);
 constexpr unsigned kTs2 = tbit(1) | tbit(2) | tbit(4);
 constexpr unsigned kTall = tbit(1) | tbit(2) | tbit(3) | tbit(4) | tbit(6) | tbit(7) | tbit(9);
 
-template <int NB, int HG, unsigned TMASK, int CPS, int OCC, int PITCH, int JW>
+template <int NB, int HG, unsigned TMASK, int CPS, int OCC, int PITCH, int JW, int KS = 1>
 hipError_t launch_one(const HaloArgs &a, int tiles, int ci_tiles, size_t lds, hipStream_t s,
                       const KernelEvents &ev) {
+    // Every group's stages, and the accumulator hand-over of the split.
+    const size_t group = ((size_t)a.stages * CPS * (a.maxT * 4 * 64 + 4 * a.HPc) + 128) * 8;
+    if (lds < KS * group || (KS > 1 && lds < (size_t)NB * 256 * 16)) return hipErrorInvalidValue;
     if (PITCH > 0 && a.HP != PITCH) return hipErrorInvalidValue;
     // JW > 0: every phase with taps has that kernel-width tap count.
     for (int i = 0; JW > 0 && i < a.nphases; ++i)
         if (a.ph[i].J_w != JW && a.ph[i].J_h * a.ph[i].J_w != 0) return hipErrorInvalidValue;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(
-            (const void *)gi_halo_f32<NB, HG, TMASK, CPS, OCC, PITCH, JW>,
+            (const void *)gi_halo_f32<NB, HG, TMASK, CPS, OCC, PITCH, JW, KS>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
     if (a.ci_tiles != ci_tiles) return hipErrorInvalidValue;
-    hipExtLaunchKernelGGL((gi_halo_f32<NB, HG, TMASK, CPS, OCC, PITCH, JW>), dim3(tiles * ci_tiles),
-                          dim3(256), (uint32_t)lds, s, ev.start, ev.stop, 0, a);
+    hipExtLaunchKernelGGL((gi_halo_f32<NB, HG, TMASK, CPS, OCC, PITCH, JW, KS>),
+                          dim3(tiles * ci_tiles), dim3(256 * KS), (uint32_t)lds, s, ev.start,
+                          ev.stop, 0, a);
     return hipGetLastError();
 }
 
@@ -429,32 +466,36 @@ hipError_t launch_one(const HaloArgs &a, int tiles, int ci_tiles, size_t lds, hi
 // 3 x 3 stride-1 kernels on 14-wide tiles (conflict-free pitch 30) and
 // 28-wide ones (30), 1 x 7 kernels on 17-wide tiles (conflict-free 33, or
 // 23), and the four phases of 3 x 3 stride-2 kernels on 14-wide tiles (15).
+// ks: thread groups splitting the output channels (two for a 1 x 7 instance:
+// a 17 x 17 image batch of 32 gives fewer work-groups than compute units).
 struct HaloCfg {
     int nb, hg;
     unsigned tmask;
-    int cps, pitch, jw;
+    int cps, pitch, jw, ks;
 };
 constexpr HaloCfg kCfg[] = {
-    {13, 4, kT9, 1, 30, 3},   {13, 2, kT9, 1, 0, 0},   {13, 2, kTs2, 4, 15, -1},
-    {13, 2, kTs2, 4, 0, 0},   {8, 2, kT7, 1, 33, 7},   {8, 2, kT7, 1, 23, 7},
-    {8, 2, kT7, 1, 0, 0},     {13, 4, kTall, 1, 0, 0}, {8, 4, kTall, 1, 0, 0},
-    {4, 4, kTall, 1, 0, 0},
+    {13, 4, kT9, 1, 30, 3, 1},   {13, 2, kT9, 1, 0, 0, 1},   {13, 2, kTs2, 4, 15, -1, 1},
+    {13, 2, kTs2, 4, 0, 0, 1},   {8, 2, kT7, 1, 33, 7, 1},   {8, 2, kT7, 1, 23, 7, 1},
+    {8, 2, kT7, 1, 0, 0, 1},     {13, 4, kTall, 1, 0, 0, 1}, {8, 4, kTall, 1, 0, 0, 1},
+    {4, 4, kTall, 1, 0, 0, 1},   {8, 2, kT7, 1, 23, 7, 2},
 };
 
 }  // namespace
 
 unsigned halo_f32_tbit(int T) { return T >= 0 && T < 32 ? tbit(T) : 0u; }
 
-int halo_f32_config(int nb, unsigned tmask, int hg, int hp, int jw) {
+int halo_f32_config(int nb, unsigned tmask, int hg, int hp, int jw, int ks) {
     for (int i = 0; i < (int)(sizeof(kCfg) / sizeof(kCfg[0])); ++i) {
         const HaloCfg &c = kCfg[i];
-        if (c.nb != nb || c.hg < hg || (c.tmask & tmask) != tmask) continue;
+        if (c.nb != nb || c.ks != ks || c.hg < hg || (c.tmask & tmask) != tmask) continue;
         if (c.pitch == 0 || (c.pitch == hp && (c.jw == jw || c.jw < 0))) return i;
     }
     return -1;
 }
 
 int halo_f32_cps(int cfg) { return kCfg[cfg].cps; }
+
+int halo_f32_ks(int cfg) { return kCfg[cfg].ks; }
 
 bool halo_f32_fixed_pitch(int cfg) { return kCfg[cfg].pitch > 0; }
 
@@ -477,6 +518,7 @@ hipError_t launch_halo_f32(const HaloArgs &a, int cfg, int tiles, int ci_tiles, 
         case 7: return launch_one<13, 4, kTall, 1, 2, 0, 0>(a, tiles, ci_tiles, lds, s, ev);
         case 8: return launch_one<8, 4, kTall, 1, 2, 0, 0>(a, tiles, ci_tiles, lds, s, ev);
         case 9: return launch_one<4, 4, kTall, 1, 2, 0, 0>(a, tiles, ci_tiles, lds, s, ev);
+        case 10: return launch_one<8, 2, kT7, 1, 2, 23, 7, 2>(a, tiles, ci_tiles, lds, s, ev);
         default: return hipErrorInvalidValue;
     }
 }

@@ -158,6 +158,16 @@ CONV2D_GI_API int conv2d_gi_set_variant(int variant);
 CONV2D_GI_API int conv2d_gi_set_halo_tile(int nb, int tile_rows, int tile_cols, int stages);
 
 /*
+ * Test and diagnostic hook: force how many thread groups of 256 split the
+ * output channels of a work-group of the fp32 HALO variant for later calls
+ * in this process (1 or 2; each group stages its own share of the chunks
+ * and the first sums both before storing).  A shape no instance with that
+ * split serves is planned without it.  0 restores the planner.  Returns
+ * CONV2D_GI_OK, or CONV2D_GI_EINVAL for other values.
+ */
+CONV2D_GI_API int conv2d_gi_set_halo_split(int groups);
+
+/*
  * Host-only: describe the plan the entry point would run for this shape
  * (dtype_bf16 = 0 for fp32 inputs, 1 for bf16), as text written into buf
  * (NUL-terminated, truncated to len).  Returns a status code.

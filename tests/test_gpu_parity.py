@@ -249,6 +249,7 @@ def test_fixed_instances(idx):
     shape, bf16, variant, tile, parts = FIXED_INSTANCES[idx]
     if tile:
         gi.set_halo_tile(tile[0], tile[1], tile[2], 0)
+        gi.set_halo_split(tile[3])
     try:
         gi.set_variant(variant)
         desc = gi.plan(gi.make_params(*shape.as_tuple()[:10]), bf16)
@@ -259,6 +260,7 @@ def test_fixed_instances(idx):
     finally:
         gi.set_variant(gi.VARIANT_AUTO)
         gi.set_halo_tile()
+        gi.set_halo_split()
 
 
 def test_tiny_workload_full():

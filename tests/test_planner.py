@@ -14,6 +14,7 @@ def lib():
     gi.load_library()
     yield
     gi.set_halo_tile()
+    gi.set_halo_split()
     gi.set_variant(gi.VARIANT_AUTO)
 
 
@@ -26,7 +27,7 @@ WORKLOAD_PLANS = {
     "resnet_stage_3x3": ["variant=halo", "cfg=0", "HP=30"],
     "deep_late_stage": ["variant=halo", "cfg=0", "tile=14x14", "HP=30"],
     "strided_downsample": ["variant=halo", "cfg=2", "HP=15"],
-    "asym_1x7": ["variant=halo", "fold", "HP=23"],
+    "asym_1x7": ["variant=halo", "cfg=10 split=2", "fold", "HP=23"],
     "stem_7x7_s2": ["variant=stem", "ws_bytes=0", "tiles=16x7x7x1 whole=768 waves=4 pitch=19"],
     "deep_late_stage_bf16": ["variant=halo", "dtype=bf16", "cfg=0", "pitch=30"],
     "tiny": ["variant=generic"],
@@ -41,18 +42,24 @@ def test_workload_plans(name):
         assert part in desc, (name, part, desc)
 
 
-# (shape, bf16, variant, forced (nb, rows, cols) or None, plan substrings):
-# ragged channel counts on each compile-time instance.
+# (shape, bf16, variant, forced (nb, rows, cols, split) or None, plan
+# substrings): ragged channel counts on each compile-time instance (split: the
+# fp32 output-channel split forced to 1 or 2 thread groups, 0 for the
+# planner's choice).
 FIXED_INSTANCES = [
-    (S(3, 40, 28, 28, 20, 3, 3, 1, 1, 1), False, gi.VARIANT_HALO, (13, 14, 14),
+    (S(3, 40, 28, 28, 20, 3, 3, 1, 1, 1), False, gi.VARIANT_HALO, (13, 14, 14, 0),
      ["cfg=0", "HP=30", "tile=14x14"]),
-    (S(3, 40, 28, 28, 20, 3, 3, 1, 1, 1), False, gi.VARIANT_HALO, (13, 7, 28),
+    (S(3, 40, 28, 28, 20, 3, 3, 1, 1, 1), False, gi.VARIANT_HALO, (13, 7, 28, 0),
      ["cfg=0", "HP=30", "tile=7x28"]),
-    (S(2, 70, 28, 28, 20, 3, 3, 2, 1, 1), False, gi.VARIANT_HALO, (13, 14, 14),
+    (S(2, 70, 28, 28, 20, 3, 3, 2, 1, 1), False, gi.VARIANT_HALO, (13, 14, 14, 0),
      ["cfg=2", "HP=15"]),
-    (S(4, 30, 17, 17, 36, 1, 7, 1, 0, 3), False, gi.VARIANT_HALO, (8, 7, 17),
+    (S(4, 30, 17, 17, 36, 1, 7, 1, 0, 3), False, gi.VARIANT_HALO, (8, 7, 17, 1),
      ["cfg=4", "HP=33", "fold"]),
-    (S(3, 72, 14, 14, 40, 3, 3, 1, 1, 1), True, gi.VARIANT_HALO, (7, 14, 14),
+    (S(4, 30, 17, 17, 36, 1, 7, 1, 0, 3), False, gi.VARIANT_HALO, (8, 7, 17, 2),
+     ["cfg=10 split=2", "HP=23", "fold"]),
+    (S(3, 64, 17, 17, 80, 1, 7, 1, 0, 3), False, gi.VARIANT_HALO, (8, 4, 17, 2),
+     ["cfg=10 split=2", "HP=23", "fold", "tile=4x17"]),
+    (S(3, 72, 14, 14, 40, 3, 3, 1, 1, 1), True, gi.VARIANT_HALO, (7, 14, 14, 0),
      ["cfg=0", "pitch=30"]),
     (S(1, 2, 30, 30, 6, 7, 7, 2, 3, 3), False, gi.VARIANT_STEM, None,
      ["variant=stem"]),
@@ -65,11 +72,13 @@ def test_fixed_instance_plans(idx):
     try:
         if tile:
             gi.set_halo_tile(tile[0], tile[1], tile[2], 0)
+            gi.set_halo_split(tile[3])
         gi.set_variant(variant)
         desc = plan_of(shape, bf16)
     finally:
         gi.set_variant(gi.VARIANT_AUTO)
         gi.set_halo_tile()
+        gi.set_halo_split()
     for part in parts:
         assert part in desc, (part, desc)
 
