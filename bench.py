@@ -17,7 +17,9 @@ The main kernel's own duration is measured live with HIP events that its
 launch records with the dispatch's start and end timestamps (the
 ``roofline.achieved`` figure); the whole-call time gives ``value``.
 ``roofline.traffic`` is the HBM bytes per launch from the committed counter
-summary under profiles/, when its kernel sources and plan still match.
+summary under profiles/, and ``roofline.mfma_counters`` the matrix-core work
+and utilisation the MFMA counters saw per launch, each when its kernel
+sources and plan still match.
 """
 from __future__ import annotations
 
@@ -214,6 +216,7 @@ def main():
     achieved = r["flops"] / (r["kernel_ms"] * 1e-3) / 1e12
     alg_bytes = s.algorithmic_bytes(2 if wl.dtype == "bf16" else 4)
     traffic = profiling.read_traffic(kernel, wl.name, plan_desc, variant, wl.dtype)
+    mfma = profiling.read_mfma(kernel, wl.name, plan_desc, variant, wl.dtype)
     line = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -241,7 +244,8 @@ def main():
                      "kernel": kernel,
                      "kernel_ms": round(r["kernel_ms"], 5),
                      "per_unit": "2*Ci*kH*kW*Co flops per output pixel (n,oh,ow)",
-                     "units_per_launch": s.N * s.oH * s.oW},
+                     "units_per_launch": s.N * s.oH * s.oW,
+                     "mfma_counters": mfma},
         "frac_of_peak_whole_call": round(value / peak, 4),
     }
     if not args.no_others:
@@ -256,6 +260,8 @@ def main():
             vo = profiling.plan_variant(po)
             to = profiling.read_traffic(profiling.kernel_name(vo, o.dtype), o.name, po, vo,
                                         o.dtype)
+            mo = profiling.read_mfma(profiling.kernel_name(vo, o.dtype), o.name, po, vo,
+                                     o.dtype)
             others[o.name] = {"dtype": o.dtype, "tflops": round(v, 3),
                               "ms_per_call": round(ro["ms_per_step"], 5),
                               "kernel_ms": round(ro["kernel_ms"], 5),
@@ -264,6 +270,7 @@ def main():
                                   ro["flops"] / (ro["kernel_ms"] * 1e-3) / 1e12
                                   / PEAK_TFLOPS[o.dtype], 4),
                               "traffic": None if to is None else round(to["bytes"]),
+                              "mfma_counters": mo,
                               "algorithmic_bytes": so.algorithmic_bytes(
                                   2 if o.dtype == "bf16" else 4)}
         line["other_workloads"] = others

@@ -9,9 +9,13 @@ Two summaries are written under ``profiles/``, named for kernel and workload:
 * ``<kernel>_<workload>_traffic.txt`` -- HBM bytes per launch of the dominant
   kernel from two ``--pmc`` runs (FETCH_SIZE, then WRITE_SIZE, both in KiB per
   dispatch), each scaled by what the same counter reads for a plain
-  device-to-device copy of known size run at the end of the same program.
+  device-to-device copy of known size run at the end of the same program;
+* ``<kernel>_<workload>_mfma.txt`` -- the matrix-core work the counters saw
+  per launch (SQ_INSTS_VALU_MFMA_MOPS_F32 / _BF16, in units of 512 flops,
+  padded work included), the MFMA busy cycles, and the utilisation both imply
+  against the kernel-trace duration of the same workload.
 
-The traffic file records a fingerprint of the kernel's sources and the
+The traffic and MFMA files record a fingerprint of the kernel's sources and the
 planner's description of the launch; bench.py reports its figure only while
 both still match what it is about to run.
 
@@ -156,6 +160,22 @@ def _counter(run_dir: str, counter: str):
     return [(d, per[d][0], per[d][1]) for d in sorted(per)]
 
 
+def _counter_max(run_dir: str, counter: str):
+    """Per-dispatch (dispatch id, kernel name, value) of one counter, the
+    largest value over its hardware instances (for cycle counters that every
+    instance counts in parallel)."""
+    with open(_csv(run_dir, "counter_collection.csv")) as fh:
+        rows = list(csv.DictReader(fh))
+    per = {}
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        d = int(r["Dispatch_Id"])
+        name, v = per.get(d, (r["Kernel_Name"], 0.0))
+        per[d] = (name, max(v, float(r["Counter_Value"])))
+    return [(d, per[d][0], per[d][1]) for d in sorted(per)]
+
+
 def _kernel_and_copy(run_dir: str, counter: str, short: str):
     disp = _counter(run_dir, counter)
     copies = disp[-CALIBRATION_COPIES:]
@@ -206,6 +226,90 @@ def write_traffic(fetch_dir: str, write_dir: str, bench_log: str, workload: str,
     return out
 
 
+MFMA_COUNTERS = ["SQ_INSTS_VALU_MFMA_MOPS_F32", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+                 "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE"]
+SIMDS = 1024      # MI355X: 256 compute units x 4 SIMDs
+XCDS = 8          # GRBM_GUI_ACTIVE comes summed over the 8 XCDs' own counters
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6}
+
+
+def write_mfma(run_dir: str, stats_dir: str, bench_log: str, workload: str, command: str,
+               out_dir: str = PROFILES) -> str:
+    """MFMA counters per launch of the main kernel, from a --pmc run of
+    MFMA_COUNTERS; the launch duration is the kernel-trace average of the
+    --stats run in stats_dir."""
+    line = _bench_line(bench_log)
+    plan = line["config"]["plan"]
+    variant, dtype = plan_variant(plan), line["dtype"]
+    short = kernel_name(variant, dtype)
+
+    def per_launch(counter, reduce_max=False):
+        disp = (_counter_max if reduce_max else _counter)(run_dir, counter)
+        main = [(d, n, v) for d, n, v in disp if _matches(n, short)]
+        if not main:
+            raise ValueError("kernel %s not in %s" % (short, run_dir))
+        return main[0][1], len(main), sum(v for _, _, v in main) / len(main)
+
+    kname, nd, mops32 = per_launch("SQ_INSTS_VALU_MFMA_MOPS_F32")
+    _, _, mops16 = per_launch("SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    _, _, busy = per_launch("SQ_VALU_MFMA_BUSY_CYCLES")
+    _, _, gui = per_launch("GRBM_GUI_ACTIVE", reduce_max=True)
+    with open(_csv(stats_dir, "kernel_stats.csv")) as fh:
+        st = [r for r in csv.DictReader(fh) if _matches(r["Name"], short)]
+    if not st:
+        raise ValueError("kernel %s not in %s" % (short, stats_dir))
+    dur_s = float(st[0]["AverageNs"]) * 1e-9
+    flops = (mops32 + mops16) * 512.0
+    peak = PEAK_TFLOPS[dtype] * 1e12
+    out = os.path.join(out_dir, "%s_%s_mfma.txt" % (short, workload))
+    with open(out, "w") as fh:
+        fh.write("# Matrix-core work per launch of %s on %s (rocprofv3 --pmc %s)\n"
+                 "# counter_flops = (MOPS_F32 + MOPS_BF16) * 512, padded lanes included;\n"
+                 "# counter_util = counter_flops / (kernel-trace average duration * peak);\n"
+                 "# busy_util = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / %d XCDs * %d\n"
+                 "# SIMDs), rocprofv3's MfmaUtil expression with the GUI-active cycles, which\n"
+                 "# the counter reports summed over the XCDs, taken per XCD\n"
+                 % (short, workload, " ".join(MFMA_COUNTERS), XCDS, SIMDS))
+        for k, v in [("kernel", short), ("workload", workload), ("plan", plan),
+                     ("source_fingerprint", fingerprint(variant, dtype)),
+                     ("command", command), ("kernel_name", kname), ("dispatches", nd),
+                     ("mops_f32_per_dispatch", "%.0f" % mops32),
+                     ("mops_bf16_per_dispatch", "%.0f" % mops16),
+                     ("mfma_busy_cycles_per_dispatch", "%.0f" % busy),
+                     ("gui_active_cycles_per_dispatch", "%.0f" % gui),
+                     ("kernel_trace_avg_us", "%.3f" % (dur_s * 1e6)),
+                     ("peak_tflops", PEAK_TFLOPS[dtype]),
+                     ("counter_flops", "%.0f" % flops),
+                     ("counter_tflops", "%.3f" % (flops / dur_s / 1e12)),
+                     ("counter_util", "%.4f" % (flops / dur_s / peak)),
+                     ("busy_util", "%.4f" % (busy / (gui / XCDS * SIMDS) if gui else 0.0))]:
+            fh.write("%s: %s\n" % (k, v))
+    return out
+
+
+def read_mfma(kernel: str, workload: str, plan: str, variant: str, dtype: str):
+    """Counter-measured MFMA figures per launch from the committed summary, or
+    None when there is none or the kernel's sources or plan changed since."""
+    path = os.path.join(PROFILES, "%s_%s_mfma.txt" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for ln in fh:
+            if ln.startswith("#") or ":" not in ln:
+                continue
+            k, v = ln.split(":", 1)
+            kv[k.strip()] = v.strip()
+    try:
+        if kv.get("plan") != plan or kv.get("source_fingerprint") != fingerprint(variant, dtype):
+            return None
+        return {"counter_flops": float(kv["counter_flops"]),
+                "counter_util": float(kv["counter_util"]),
+                "busy_util": float(kv["busy_util"])}
+    except (KeyError, ValueError, FileNotFoundError):
+        return None
+
+
 def read_traffic(kernel: str, workload: str, plan: str, variant: str, dtype: str):
     """Scaled HBM bytes per launch from the committed traffic summary, or None
     when there is none or when the kernel's sources or plan changed since."""
@@ -248,10 +352,19 @@ def main(argv=None):
     t.add_argument("--command-fetch", required=True)
     t.add_argument("--command-write", required=True)
     t.add_argument("--out-dir", default=PROFILES)
+    m = sub.add_parser("mfma")
+    m.add_argument("--run-dir", required=True)
+    m.add_argument("--stats-dir", required=True)
+    m.add_argument("--bench-log", required=True)
+    m.add_argument("--workload", required=True)
+    m.add_argument("--command", required=True)
+    m.add_argument("--out-dir", default=PROFILES)
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         print(write_stats(a.run_dir, a.bench_log, a.workload, a.command, a.out_dir,
                           plain_log=a.plain_bench_log))
+    elif a.cmd == "mfma":
+        print(write_mfma(a.run_dir, a.stats_dir, a.bench_log, a.workload, a.command, a.out_dir))
     else:
         print(write_traffic(a.fetch_dir, a.write_dir, a.bench_log, a.workload, a.copy_mib,
                             a.command_fetch, a.command_write, a.out_dir))

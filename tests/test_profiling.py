@@ -85,3 +85,41 @@ def test_read_traffic_checks_plan_and_sources(tmp_path, monkeypatch):
 def test_fingerprint_covers_every_kernel():
     seen = {profiling.fingerprint(v, d) for v, d in profiling.KERNEL_SOURCES}
     assert len(seen) == 4   # generic f32 and bf16 share one source file
+
+
+def test_mfma_summary(tmp_path, monkeypatch):
+    """Counter flops and utilisation per launch: instance values add up for
+    the instruction and busy counters, the GUI-active cycles take the largest
+    instance (per XCD after dividing the reported sum by the XCD count), and
+    the duration comes from the kernel-trace statistics."""
+    os.makedirs(str(tmp_path / "m"))
+    with open(str(tmp_path / "m" / "run_counter_collection.csv"), "w", newline="") as fh:
+        w = csv.writer(fh)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        for d in (1, 2):
+            for v in (600.0, 400.0):
+                w.writerow([d, KNAME, "SQ_INSTS_VALU_MFMA_MOPS_F32", v])
+            w.writerow([d, KNAME, "SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0])
+            for v in (512.0, 512.0):
+                w.writerow([d, KNAME, "SQ_VALU_MFMA_BUSY_CYCLES", v])
+            for v in (1.0, 2.0):
+                w.writerow([d, KNAME, "GRBM_GUI_ACTIVE", v])
+        w.writerow([3, "other", "SQ_INSTS_VALU_MFMA_MOPS_F32", 9e9])
+    os.makedirs(str(tmp_path / "s"))
+    with open(str(tmp_path / "s" / "run_kernel_stats.csv"), "w", newline="") as fh:
+        w = csv.writer(fh)
+        w.writerow(["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage"])
+        w.writerow([KNAME, 10, 100, 10, 100])
+    _bench_log(str(tmp_path / "b.log"))
+    out = profiling.write_mfma(str(tmp_path / "m"), str(tmp_path / "s"),
+                               str(tmp_path / "b.log"), "wl", "cmd", out_dir=str(tmp_path))
+    kv = dict(ln.split(": ", 1) for ln in open(out).read().splitlines()
+              if not ln.startswith("#"))
+    assert float(kv["counter_flops"]) == 1000 * 512
+    # 512000 flops in 10 ns against 157.3 TFLOP/s.
+    assert float(kv["counter_util"]) == pytest.approx(512000 / 1e-8 / 157.3e12, rel=1e-3)
+    assert float(kv["busy_util"]) == pytest.approx(1024 / (2 / profiling.XCDS * profiling.SIMDS),
+                                                   rel=1e-6)
+    monkeypatch.setattr(profiling, "PROFILES", str(tmp_path))
+    assert profiling.read_mfma("gi_halo_f32", "wl", PLAN, "halo", "f32")["counter_flops"] == 512000
+    assert profiling.read_mfma("gi_halo_f32", "wl", PLAN + "x", "halo", "f32") is None
