@@ -17,7 +17,7 @@ import os
 
 __all__ = [
     "grad_input", "Conv2dGiParams", "Conv2dGiError", "LibraryNotBuilt", "load_library",
-    "make_params", "validate", "plan", "set_variant", "set_halo_tile", "set_halo_split", "release_workspaces", "set_profile_events", "library_path", "exported_names",
+    "make_params", "validate", "plan", "set_variant", "set_halo_tile", "set_halo_split", "set_halo_fusion", "release_workspaces", "set_profile_events", "library_path", "exported_names",
     "OK", "EINVAL", "EUNSUPPORTED", "EHIP", "VARIANT_AUTO", "VARIANT_GENERIC", "VARIANT_HALO", "VARIANT_STEM",
 ]
 
@@ -81,6 +81,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.conv2d_gi_set_halo_tile.restype = ctypes.c_int
     lib.conv2d_gi_set_halo_split.argtypes = [ctypes.c_int]
     lib.conv2d_gi_set_halo_split.restype = ctypes.c_int
+    lib.conv2d_gi_set_halo_fusion.argtypes = [ctypes.c_int]
+    lib.conv2d_gi_set_halo_fusion.restype = ctypes.c_int
     lib.conv2d_gi_set_profile_events.argtypes = [P, P]
     lib.conv2d_gi_set_profile_events.restype = None
     lib.conv2d_gi_release_workspaces.argtypes = []
@@ -97,6 +99,7 @@ def exported_names():
     return ["conv2d_grad_input", "conv2d_grad_input_bf16", "conv2d_gi_validate",
             "conv2d_gi_strerror", "conv2d_gi_last_hip_error", "conv2d_gi_set_variant",
             "conv2d_gi_plan", "conv2d_gi_set_halo_tile", "conv2d_gi_set_halo_split",
+            "conv2d_gi_set_halo_fusion",
             "conv2d_gi_set_profile_events",
             "conv2d_gi_release_workspaces", "conv2d_gi_version"]
 
@@ -152,6 +155,13 @@ def set_halo_split(groups: int = 0):
     HALO work-group for later calls (test hook); set_halo_split() restores the
     planner."""
     _check(load_library().conv2d_gi_set_halo_split(int(groups)))
+
+
+def set_halo_fusion(mode: int = 0):
+    """Force the fp32 HALO variant to run a tile's stride phases one after
+    another (1) or all per chunk over one shared halo (2) for later calls
+    (test hook); set_halo_fusion() restores the planner."""
+    _check(load_library().conv2d_gi_set_halo_fusion(int(mode)))
 
 
 def release_workspaces():

@@ -28,6 +28,7 @@ std::atomic<int> g_variant{CONV2D_GI_VARIANT_AUTO};
 // Forced halo tile (test hook): NB pixel blocks, TR x TC phase-grid pixels; 0 = planner.
 std::atomic<int> g_tile_nb{0}, g_tile_tr{0}, g_tile_tc{0}, g_tile_stages{0};
 std::atomic<int> g_halo_split{0};
+std::atomic<int> g_halo_fusion{0};  // 0 planner, 1 phase at a time, 2 fused
 thread_local char g_last_hip[256] = "";
 thread_local hipEvent_t g_prof_begin = nullptr, g_prof_end = nullptr;
 
@@ -127,6 +128,7 @@ struct HaloPlan {
     size_t lds = 0;
     double cost = 0.0;
     int64_t ws_floats = 0;  // weight image
+    int fused = 0;           // all phases per chunk over one shared halo
 };
 
 // A bf16 halo-kernel plan (stride 1): two prologues and one launch.
@@ -201,6 +203,26 @@ bool plan_halo(const conv2d_gi_params &p, const std::vector<Phase> &phases, Halo
     if (jw_common < 0) jw_common = 0;
     const int ci_tiles = (p.Ci + gi::kHaloCT - 1) / gi::kHaloCT;
     if (w_ci_stride * ci_tiles * 4 > lim || maxT == 0) return false;
+    // Fused launches (every phase per chunk over one halo): four phases with
+    // tap grids of at most 2 x 2.  The shared halo starts at the smallest
+    // phase origin q - (J - 1) and reaches TR + ur rows, TC + uc columns.
+    int Tall = 0, org_h = INT32_MAX, org_w = INT32_MAX, ur = 0, uc = 0;
+    bool fusable = phases.size() == 4 && !fold && g_halo_fusion.load() != 1;
+    for (const Phase &ph : phases) {
+        Tall += ph.J_h * ph.J_w;
+        if (ph.J_h > 2 || ph.J_w > 2) fusable = false;
+        if (ph.J_h * ph.J_w == 0) continue;
+        org_h = std::min(org_h, ph.q_h - (ph.J_h - 1));
+        org_w = std::min(org_w, ph.q_w - (ph.J_w - 1));
+    }
+    if (Tall == 0 || Tall > 12) fusable = false;
+    if (fusable)
+        for (const Phase &ph : phases) {
+            if (ph.J_h * ph.J_w == 0) continue;
+            ur = std::max(ur, ph.q_h - (ph.J_h - 1) - org_h + ph.J_h - 1);
+            uc = std::max(uc, ph.q_w - (ph.J_w - 1) - org_w + ph.J_w - 1);
+        }
+    const int fz_lo = g_halo_fusion.load() == 2 ? 1 : 0;
     static const int kNB[] = {4, 8, 13};
     const int f_nb = g_tile_nb.load(), f_tr = g_tile_tr.load(), f_tc = g_tile_tc.load();
     const bool forced = f_nb > 0;
@@ -216,7 +238,9 @@ bool plan_halo(const conv2d_gi_params &p, const std::vector<Phase> &phases, Halo
             for (int TR = forced ? f_tr : std::min(maxpx / TC, rows_total); TR >= 1; --TR) {
                 if (forced && (TR != f_tr || TR * TC > maxpx)) break;
                 if (!forced && nb > 4 && TR * TC <= (nb == 8 ? 4 : 8) * 16) break;
-                const int HR = TR + maxJh - 1, HC = TC + maxJw - 1;
+                for (int fz = fz_lo; fz <= (fusable ? 1 : 0); ++fz) {
+                const int HR = fz ? TR + ur : TR + maxJh - 1;
+                const int HC = fz ? TC + uc : TC + maxJw - 1;
                 // Halo row pitch: the padded one (= TC mod 16) puts the 16
                 // pixels of a block (which may wrap to the next tile row) at
                 // positions distinct mod 16, so the fragment reads of a
@@ -229,36 +253,41 @@ bool plan_halo(const conv2d_gi_params &p, const std::vector<Phase> &phases, Halo
                 // off a multiple of 32 so the co-pair rows of a fragment read
                 // fall on disjoint banks.
                 const int groups = (HR * HP + 31) / 32;
-                const int bl = (groups + 3) / 4;
-                // ks thread groups split each work-group's output channels.
-                for (int ks = 1; ks <= 2; ++ks) {
+                // ks thread groups split each work-group's output channels
+                // (phase at a time) or its phases (fused: always two, sharing
+                // every stage).
+                for (int ks = fz ? 2 : 1; ks <= 2; ++ks) {
                 const int f_ks = g_halo_split.load();
-                if (f_ks > 0 && ks != f_ks) continue;
-                const int cfg = gi::halo_f32_config(nb, tmask, bl, HP, jw_common, ks);
+                if (!fz && f_ks > 0 && ks != f_ks) continue;
+                const int bl = fz ? (groups + 4 * ks - 1) / (4 * ks) : (groups + 3) / 4;
+                const int cfg = gi::halo_f32_config(nb, tmask, bl, HP, jw_common, ks, fz ? 4 : 0);
                 if (cfg < 0) continue;
                 const int HPc = round_to_residue(groups * 32, 32, 16);
                 const int cps = gi::halo_f32_cps(cfg);
+                // A fused stage holds the weights of every phase's taps.
+                const int stage_taps = fz ? Tall : maxT;
                 // Three pipeline stages when two work-groups (or two thread
                 // groups) still fit a CU, or when one is all that fits anyway.
                 const size_t budget = kLdsBytes / 2;
                 int stages = 3;
-                size_t lds = gi::halo_f32_lds_bytes(maxT, HPc, 3, cps);
+                size_t lds = gi::halo_f32_lds_bytes(stage_taps, HPc, 3, cps);
                 if (lds > budget) {
                     stages = 2;
-                    lds = gi::halo_f32_lds_bytes(maxT, HPc, 2, cps);
+                    lds = gi::halo_f32_lds_bytes(stage_taps, HPc, 2, cps);
                     if (lds > budget && ks == 1 &&
-                        gi::halo_f32_lds_bytes(maxT, HPc, 3, cps) <= kLdsBytes) {
+                        gi::halo_f32_lds_bytes(stage_taps, HPc, 3, cps) <= kLdsBytes) {
                         stages = 3;
-                        lds = gi::halo_f32_lds_bytes(maxT, HPc, 3, cps);
+                        lds = gi::halo_f32_lds_bytes(stage_taps, HPc, 3, cps);
                     }
                 }
                 if (forced && g_tile_stages.load() > 0) {
                     stages = g_tile_stages.load();
-                    lds = gi::halo_f32_lds_bytes(maxT, HPc, stages, cps);
+                    lds = gi::halo_f32_lds_bytes(stage_taps, HPc, stages, cps);
                 }
                 // A split work-group holds every group's stages, and its
-                // accumulators once, for the hand-over.
-                lds = std::max(lds * ks, ks > 1 ? (size_t)nb * 256 * 16 : (size_t)0);
+                // accumulators once, for the hand-over (fused groups share
+                // the stages and hand nothing over).
+                if (!fz) lds = std::max(lds * ks, ks > 1 ? (size_t)nb * 256 * 16 : (size_t)0);
                 if (lds > kLdsBytes) continue;
                 const int64_t row_tiles = (rows_total + TR - 1) / TR;
                 const int64_t col_tiles = (maxWb + TC - 1) / TC;
@@ -279,9 +308,10 @@ bool plan_halo(const conv2d_gi_params &p, const std::vector<Phase> &phases, Halo
                 const double eff_pitch = (gi::halo_f32_fixed_pitch(cfg) ? 1.05 : 1.0) *
                                          (conflict_free ? 1.03 : 1.0);
                 // 16x16x4 MFMA: 32 cycles per 16 pixels x 4 k; plus halo staging.
+                // Halo staging: once per chunk when fused, else once per phase.
                 const double per_wg = 8.0 * nb * kall +
-                                      (double)nchunks * phases.size() * HR * HP * 2.0 + 4000.0 +
-                                      (ks > 1 ? 1500.0 * phases.size() : 0.0);
+                                      (double)nchunks * (fz ? 1 : phases.size()) * HR * HP * 2.0 +
+                                      4000.0 + (ks > 1 ? 1500.0 * phases.size() : 0.0);
                 // Among equal critical paths, fewer work-groups do less total work.
                 const double cost = (double)per_cu * per_wg / (eff_nb * eff_occ * eff_pitch) +
                                     0.05 * (double)wgs * per_wg / kCUs;
@@ -295,6 +325,7 @@ bool plan_halo(const conv2d_gi_params &p, const std::vector<Phase> &phases, Halo
                     out.tiles = (int)tiles;
                     out.ci_tiles = ci_tiles;
                     out.lds = lds;
+                    out.fused = fz;
                     gi::HaloArgs &a = out.args;
                     a.TR = TR;
                     a.TC = TC;
@@ -303,6 +334,9 @@ bool plan_halo(const conv2d_gi_params &p, const std::vector<Phase> &phases, Halo
                     a.HP = HP;
                     a.HPc = HPc;
                     a.stages = stages;
+                    a.HR = HR;
+                    a.HC = HC;
+                }
                 }
                 }
                 }
@@ -346,6 +380,36 @@ bool plan_halo(const conv2d_gi_params &p, const std::vector<Phase> &phases, Halo
         woff += (int64_t)nchunks * ph.J_h * ph.J_w * 512;
     }
     out.ws_floats = w_ci_stride * ci_tiles;
+    a.fused = out.fused;
+    if (out.fused) {
+        a.Tall = Tall;
+        a.org_h = org_h;
+        a.org_w = org_w;
+        int tb = 0;
+        for (size_t i = 0; i < phases.size(); ++i) {
+            const Phase &ph = phases[i];
+            gi::HaloPhase &h = a.ph[i];
+            h.tb = tb;
+            tb += ph.J_h * ph.J_w;
+            h.dr = ph.J_h * ph.J_w ? ph.q_h - (ph.J_h - 1) - org_h : 0;
+            h.dc = ph.J_h * ph.J_w ? ph.q_w - (ph.J_w - 1) - org_w : 0;
+        }
+        // Two thread groups: the phases sorted by taps, the largest with the
+        // smallest in one group and the middle two in the other, so the
+        // groups' tap totals are close.
+        int order[4] = {0, 1, 2, 3};
+        std::stable_sort(order, order + 4, [&](int x, int y) {
+            return phases[x].J_h * phases[x].J_w > phases[y].J_h * phases[y].J_w;
+        });
+        std::memset(a.gph, -1, sizeof(a.gph));
+        a.gph[0][0] = (int8_t)order[0];
+        a.gph[0][1] = (int8_t)order[3];
+        a.gph[1][0] = (int8_t)order[1];
+        a.gph[1][1] = (int8_t)order[2];
+    }
+    if (!out.fused) {
+        std::memset(a.gph, -1, sizeof(a.gph));
+    }
     return true;
 }
 
@@ -760,8 +824,9 @@ std::string describe(const Plan &plan, bool bf16) {
         const HaloPlan &h = plan.halo;
         const gi::HaloArgs &a = h.args;
         s += " launches=1 [nb=" + std::to_string(h.nb) + " cfg=" + std::to_string(h.cfg) +
-             (gi::halo_f32_ks(h.cfg) > 1 ? " split=" + std::to_string(gi::halo_f32_ks(h.cfg))
-                                          : std::string()) +
+             (h.fused                     ? std::string(" fused")
+              : gi::halo_f32_ks(h.cfg) > 1 ? " split=" + std::to_string(gi::halo_f32_ks(h.cfg))
+                                           : std::string()) +
              " bl=" + std::to_string(h.bl) + " tile=" + std::to_string(a.TR) + "x" +
              std::to_string(a.TC) + (a.fold ? " fold" : "") + " wgs=" + std::to_string(h.tiles) +
              "x" + std::to_string(h.ci_tiles) + " lds=" + std::to_string(h.lds) +
@@ -852,6 +917,12 @@ int conv2d_gi_set_halo_tile(int nb, int tile_rows, int tile_cols, int stages) {
     g_tile_tc = tile_cols;
     g_tile_stages = stages;
     g_tile_nb = nb;
+    return CONV2D_GI_OK;
+}
+
+int conv2d_gi_set_halo_fusion(int mode) {
+    if (mode < 0 || mode > 2) return CONV2D_GI_EINVAL;
+    g_halo_fusion = mode;
     return CONV2D_GI_OK;
 }
 

@@ -67,6 +67,8 @@ struct HaloPhase {
     int32_t J_h, J_w;       // taps of the phase per dimension
     int32_t Ha, Wb;         // pixels of the phase per image: rows, columns
     int32_t woff;           // first float of the phase's weight blocks in a ci tile
+    int32_t tb;             // fused launches: first tap of the phase in a chunk's taps
+    int32_t dr, dc;         // fused launches: origin of the phase's halo in the shared one
     int32_t pad_;
 };
 
@@ -77,7 +79,10 @@ struct HaloPhase {
 // Weight image (written by the prologue, zero-padded in ci and co):
 //   wk[ci_tile][phase][chunk of 8 co][tap][co pair cp][ci of 64][2]
 // so one chunk of one phase is a contiguous block of taps * 512 floats; a
-// ci tile spans w_ci_stride floats.
+// ci tile spans w_ci_stride floats.  Fused launches (fused = 1: every phase
+// of a chunk from one shared halo) order it chunk-major instead,
+//   wk[ci_tile][chunk][tap of any phase: tb + t][co pair cp][ci of 64][2],
+// so one chunk of every phase is one block of Tall * 512 floats.
 struct HaloArgs {
     const float *grad_out;  // [N, Co, oH, oW]
     const float *wk;        // weight image (above)
@@ -97,6 +102,11 @@ struct HaloArgs {
     int32_t maxT;           // most taps of any phase
     int32_t w_ci_stride;    // floats of the weight image per ci tile
     int32_t ci_tiles;       // ceil(Ci / 64); grid = tiles * ci_tiles (1-D, xcd_order)
+    int32_t fused;          // 1: all phases per chunk over one halo (see the weight image)
+    int32_t Tall;           // fused: taps of all phases
+    int32_t org_h, org_w;   // fused: shared halo origin relative to the tile
+    int32_t HR, HC;         // fused: shared halo rows / columns
+    int8_t gph[2][4];       // fused: phases of each thread group (-1: none)
     HaloPhase ph[kMaxPhasesPerLaunch];
 };
 

@@ -45,16 +45,19 @@ constexpr int kHaloCT = 64;    // input channels per work-group
 unsigned halo_f32_tbit(int T);
 // hp: halo row pitch in positions; jw: the kernel-width tap count shared by
 // every phase with taps (0 if they differ); ks: thread groups of 256 that
-// split the output channels of a work-group (1 or 2).
-int halo_f32_config(int nb, unsigned tmask, int hg, int hp, int jw, int ks);
+// split the output channels of a work-group (1 or 2); nph: phases of a fused
+// launch (0: phase at a time).
+int halo_f32_config(int nb, unsigned tmask, int hg, int hp, int jw, int ks, int nph);
 hipError_t launch_halo_f32(const HaloArgs &a, int cfg, int tiles, int ci_tiles, size_t lds,
                            hipStream_t s, const KernelEvents &ev);
 // Chunks of 8 output channels per LDS stage of instantiation cfg, and the LDS
 // bytes of the halo kernel: most taps of a phase, halo pitch (float2),
 // pipeline stages, chunks per stage.
 int halo_f32_cps(int cfg);
-// Thread groups of 256 per work-group of instantiation cfg.
+// Thread groups of 256 per work-group of instantiation cfg, and the phases
+// it fuses (0: none).
 int halo_f32_ks(int cfg);
+int halo_f32_nph(int cfg);
 // True when instantiation cfg has its halo pitch fixed at compile time.
 bool halo_f32_fixed_pitch(int cfg);
 size_t halo_f32_lds_bytes(int maxT, int HPc, int stages, int cps);  // per thread group

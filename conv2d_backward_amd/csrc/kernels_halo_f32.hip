@@ -291,18 +291,182 @@ __device__ __forceinline__ void run_phase(const HaloArgs &A, const HaloPhase &P,
     }
 }
 
+// Fused launches: the taps of one phase (tap grid JH x JW, compile time) over
+// one staged chunk.  as: the phase's first tap in the stage's weights (this
+// lane's A slot); hs: the shared halo of this lane's co pair, offset to the
+// phase's origin in it.
+template <int JH, int JW, int NB, int PITCH>
+__device__ __forceinline__ void fused_taps(const v2f *as, const v2f *hs, const int (&pbase)[NB],
+                                           int HP_rt, v4f (&acc)[NB]) {
+    constexpr int T = JH * JW;
+    const int HP = PITCH > 0 ? PITCH : HP_rt;
+    int shift[T];
+    {
+        int j = 0, jw = 0;
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            shift[t] = (JH - 1 - j) * HP + (JW - 1 - jw);
+            if (++jw == JW) {
+                jw = 0;
+                ++j;
+            }
+        }
+    }
+    v2f fa[2], fb[2][NB];
+    auto fetch = [&](int t, int slot) {
+        fa[slot] = as[t * 4 * 64];
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) fb[slot][blk] = hs[pbase[blk] + shift[t]];
+    };
+    fetch(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        const int slot = t & 1;
+        if (t + 1 < T) fetch(t + 1, slot ^ 1);
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk)
+            acc[blk] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[slot].x, fb[slot][blk].x, acc[blk],
+                                                            0, 0, 0);
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk)
+            acc[blk] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[slot].y, fb[slot][blk].y, acc[blk],
+                                                            0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// Fused launches: every phase of the tile per chunk of 8 output channels,
+// from one LDS stage holding the weights of all the phases' taps (one block
+// of the chunk-major weight image) and one grad_out halo covering every
+// phase (A.HR x A.HC positions from (A.org_h, A.org_w) relative to the tile,
+// pitch HP).  A stride-2 3 x 3 kernel has phases of 1, 2, 2 and 4 taps:
+// loading one halo per phase per chunk, as the phase-at-a-time path does,
+// gives each halo load a quarter of the matrix work.  Tap grids of 1 or 2 in
+// each direction are served (the stride-2 phases of kernels up to 4 x 4).
+//
+// KS thread groups of 4 waves share every stage; group kg computes the
+// phases A.gph[kg][0..MP-1] (-1: none), so each wave holds MP phases'
+// accumulators.  All 4*KS waves issue the stage's direct loads.
+constexpr int kFusedPieces = 24;  // 1 KB weight pieces per stage: up to 12 taps
+template <int NB, int HG, int MP, int KS, int PITCH>
+__device__ __forceinline__ void run_fused(const HaloArgs &A, v2f *smem2, const int (&pbase)[NB],
+                                          const int (&myph)[MP], v4f (&acc)[MP][NB], int a0,
+                                          int b0, int n_img, int ci_tile,
+                                          __amdgpu_buffer_rsrc_t grs,
+                                          __amdgpu_buffer_rsrc_t wrs) {
+    constexpr int NW = 4 * KS;                          // waves issuing loads
+    constexpr int WPW = (kFusedPieces + NW - 1) / NW;   // weight pieces per wave
+    const int lane = threadIdx.x & 63;
+    const int wall = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // 0 .. NW-1
+    const int wave = wall & 3;                          // within the thread group
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const int HP = PITCH > 0 ? PITCH : A.HP;
+    const int wreg = A.Tall * 256;
+    const int stage_f2 = wreg + 4 * A.HPc;
+    const int hpos = A.HR * HP;
+    const int groups = (hpos + 31) / 32;
+    const int oHW = A.oH * A.oW;
+
+    // Halo position of this lane in each of its wave's groups: grad_out byte
+    // offset of output channel 0 (kOOB outside the image or the halo).
+    int hoff[HG];
+#pragma unroll
+    for (int k = 0; k < HG; ++k) {
+        const int pos = (wall + NW * k) * 32 + (lane >> 1);
+        const int hr = pos / HP, hc = pos - (pos / HP) * HP;
+        const int oh = a0 + A.org_h + hr, ow = b0 + A.org_w + hc;
+        const bool v = pos < hpos && hc < A.HC && oh >= 0 && oh < A.oH && ow >= 0 && ow < A.oW;
+        hoff[k] = v ? ((n_img * A.Co) * oHW + oh * A.oW + ow) * 4 : kOOB;
+    }
+    const int wbyte0 = ci_tile * A.w_ci_stride * 4;
+    const int co_lane = lane & 1;
+    constexpr int NDMA = WPW + 4 * HG;  // direct loads per wave per stage
+    static_assert(NDMA <= 63, "vmcnt holds at most 63");
+    v2f *const dummy = smem2 + A.stages * stage_f2;
+    auto issue = [&](int chunk, int buf) {
+        v2f *st = smem2 + buf * stage_f2;
+        const bool live = chunk < A.nchunks;
+        const int wb = wbyte0 + chunk * (A.Tall * 2048) + lane * 16;
+#pragma unroll
+        for (int i = 0; i < WPW; ++i) {
+            const int m = wall + NW * i;
+            const bool real = live && m < 2 * A.Tall;
+            dma16(wrs, real ? st + m * 128 : dummy, real ? wb + m * 1024 : kOOB);
+        }
+        v2f *hs = st + wreg;
+        int ho[HG];
+#pragma unroll
+        for (int k = 0; k < HG; ++k) {
+            ho[k] = hoff[k];
+            asm volatile("" : "+v"(ho[k]));
+        }
+#pragma unroll
+        for (int k = 0; k < HG; ++k) {
+            const int g = wall + NW * k;
+            const bool real = live && g < groups;
+#pragma unroll
+            for (int cp = 0; cp < 4; ++cp) {
+                const int co = chunk * kHaloBC + 2 * cp + co_lane;
+                const int off = (real && ho[k] != kOOB && co < A.Co) ? ho[k] + co * oHW * 4 : kOOB;
+                dma4(grs, real ? hs + cp * A.HPc + g * 32 : dummy, off);
+            }
+        }
+    };
+
+    const int D = A.stages - 1;
+    issue(0, 0);
+    if (D == 2 && A.nchunks > 1) {
+        issue(1, 1);
+        wait_dma<NDMA>();
+    } else {
+        wait_dma<0>();
+    }
+    __syncthreads();
+    for (int chunk = 0; chunk < A.nchunks; ++chunk) {
+        const int cur = chunk % A.stages;
+        const bool ahead = chunk + D < A.nchunks;
+        if (ahead) issue(chunk + D, (chunk + D) % A.stages);
+        const v2f *st = smem2 + cur * stage_f2;
+        const v2f *as0 = st + g4 * 64 + ((wave * 16 + l16 + 16 * (g4 & 1)) & 63);
+        const v2f *hs0 = st + wreg + g4 * A.HPc;
+#pragma unroll
+        for (int k = 0; k < MP; ++k) {
+            if (myph[k] < 0) continue;
+            const HaloPhase &P = A.ph[myph[k]];
+            const v2f *as = as0 + P.tb * 256;
+            const v2f *hs = hs0 + P.dr * HP + P.dc;
+            switch (P.J_h * 4 + P.J_w) {
+                case 5: fused_taps<1, 1, NB, PITCH>(as, hs, pbase, HP, acc[k]); break;
+                case 6: fused_taps<1, 2, NB, PITCH>(as, hs, pbase, HP, acc[k]); break;
+                case 9: fused_taps<2, 1, NB, PITCH>(as, hs, pbase, HP, acc[k]); break;
+                case 10: fused_taps<2, 2, NB, PITCH>(as, hs, pbase, HP, acc[k]); break;
+                default: break;  // no taps: the phase's pixels are zero
+            }
+        }
+        if (D == 2 && ahead)
+            wait_dma<NDMA>();
+        else
+            wait_dma<0>();
+        __syncthreads();
+    }
+}
+
 // KS > 1: the work-group is KS groups of 4 waves that split the output
 // channels of every phase (each group its own LDS stages, run to the same
 // barrier count), and sum their accumulators through LDS before the store:
 // for grids too small to put two work-groups on every compute unit, it gives
 // each SIMD two waves instead of one.
-template <int NB, int HG, unsigned TMASK, int CPS, int OCC, int PITCH, int JW, int KS>
+//
+// NPH > 0: a fused launch of NPH phases (run_fused); CPS, TMASK, JW and KS
+// are then unused.
+template <int NB, int HG, unsigned TMASK, int CPS, int OCC, int PITCH, int JW, int KS, int NPH>
 __global__ __launch_bounds__(256 * KS, OCC) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void gi_halo_f32(
     const HaloArgs A) {
     extern __shared__ __attribute__((aligned(16))) v2f smem_all[];
 
     const int tid = threadIdx.x & 255;
-    const int kg = KS > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 8) : 0;
+    const int kg = KS > 1 && NPH == 0 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 8) : 0;
     v2f *const smem2 =
         smem_all + kg * (A.stages * CPS * (A.maxT * 4 * 64 + 4 * A.HPc) + 128);
     const int lane = tid & 63, wave = tid >> 6;
@@ -327,6 +491,60 @@ __global__ __launch_bounds__(256 * KS, OCC) __attribute__((amdgpu_waves_per_eu(O
     const __amdgpu_buffer_rsrc_t grs = make_rsrc(A.grad_out, A.g_bytes);
     const __amdgpu_buffer_rsrc_t wrs = make_rsrc(A.wk, A.w_bytes);
     const __amdgpu_buffer_rsrc_t drs = make_rsrc(A.dst, A.d_bytes);
+
+    if constexpr (NPH > 0) {
+        // Fused: thread group kg runs phases A.gph[kg][0 .. MP-1] over the
+        // stages both groups share (the LDS is not split).
+        constexpr int MP = NPH / KS;
+        const int gk = KS > 1 ? (int)(threadIdx.x >> 8) : 0;
+        int myph[MP];
+#pragma unroll
+        for (int k = 0; k < MP; ++k) myph[k] = A.gph[gk][k];
+        const int HP = PITCH > 0 ? PITCH : A.HP;
+        // Halo position of this lane's pixel in each block (the same tile in
+        // every phase).  Lanes past the tile read position l16 when every
+        // phase's largest shift keeps that inside the halo plane, else 0.
+        int max_shift = 0;
+        for (int p = 0; p < A.nphases; ++p) {
+            const HaloPhase &P = A.ph[p];
+            if (P.J_h * P.J_w > 0)
+                max_shift = max(max_shift, (P.dr + P.J_h - 1) * HP + P.dc + P.J_w - 1);
+        }
+        const int inv = l16 + max_shift < A.HPc ? l16 : 0;
+        int pbase[NB];
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) {
+            const int px = blk * 16 + l16;
+            pbase[blk] = px < A.TR * A.TC ? (px / A.TC) * HP + (px - (px / A.TC) * A.TC) : inv;
+        }
+        v4f acc[MP][NB];
+#pragma unroll
+        for (int k = 0; k < MP; ++k)
+#pragma unroll
+            for (int blk = 0; blk < NB; ++blk) acc[k][blk] = v4f{0.f, 0.f, 0.f, 0.f};
+        run_fused<NB, HG, MP, KS, PITCH>(A, smem_all, pbase, myph, acc,
+                                         a0, b0, n_img, ci_tile, grs, wrs);
+#pragma unroll
+        for (int k = 0; k < MP; ++k) {
+            if (myph[k] < 0) continue;
+            const HaloPhase &P = A.ph[myph[k]];
+#pragma unroll
+            for (int blk = 0; blk < NB; ++blk) {
+                int img, a, b;
+                const bool pv = tile_pixel(A, P, blk * 16 + l16, a0, b0, n_img, img, a, b);
+                const int pix = (P.rho_h + A.stride * a) * A.W + P.rho_w + A.stride * b;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int ci = ci0 + wave * 16 + 4 * g4 + r;
+                    const int off =
+                        (pv && ci < A.Ci) ? ((img * A.Ci + ci) * plane + pix) * 4 : kOOB;
+                    const float v = acc[k][blk][r];
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), drs, off, 0, 0);
+                }
+            }
+        }
+        return;
+    }
 
     for (int p = 0; p < A.nphases; ++p) {
         const HaloPhase P = A.ph[p];
@@ -434,24 +652,48 @@ constexpr unsigned kT7 = tbit(7);
 constexpr unsigned kTs2 = tbit(1) | tbit(2) | tbit(4);
 constexpr unsigned kTall = tbit(1) | tbit(2) | tbit(3) | tbit(4) | tbit(6) | tbit(7) | tbit(9);
 
-template <int NB, int HG, unsigned TMASK, int CPS, int OCC, int PITCH, int JW, int KS = 1>
+template <int NB, int HG, unsigned TMASK, int CPS, int OCC, int PITCH, int JW, int KS = 1,
+          int NPH = 0>
 hipError_t launch_one(const HaloArgs &a, int tiles, int ci_tiles, size_t lds, hipStream_t s,
                       const KernelEvents &ev) {
     // Every group's stages, and the accumulator hand-over of the split.
-    const size_t group = ((size_t)a.stages * CPS * (a.maxT * 4 * 64 + 4 * a.HPc) + 128) * 8;
-    if (lds < KS * group || (KS > 1 && lds < (size_t)NB * 256 * 16)) return hipErrorInvalidValue;
+    const size_t group =
+        NPH > 0 ? ((size_t)a.stages * (a.Tall * 4 * 64 + 4 * a.HPc) + 128) * 8
+                : ((size_t)a.stages * CPS * (a.maxT * 4 * 64 + 4 * a.HPc) + 128) * 8;
+    if (lds < (NPH > 0 ? 1 : KS) * group || (KS > 1 && NPH == 0 && lds < (size_t)NB * 256 * 16))
+        return hipErrorInvalidValue;
+    if (NPH > 0) {
+        // Fused: NPH phases of tap grids up to 2 x 2, the chunk's weights in
+        // at most kFusedPieces pieces of 1 KB, the halo in at most 4*KS*HG
+        // groups of 32 positions, and every phase in exactly one thread
+        // group's list.
+        if (a.fused != 1 || a.nphases != NPH || a.Tall * 2 > kFusedPieces ||
+            (a.HR * (PITCH > 0 ? PITCH : a.HP) + 31) / 32 > 4 * KS * HG)
+            return hipErrorInvalidValue;
+        int seen[NPH] = {};
+        for (int g = 0; g < KS; ++g)
+            for (int k = 0; k < NPH / KS; ++k) {
+                const int p = a.gph[g][k];
+                if (p >= NPH) return hipErrorInvalidValue;
+                if (p >= 0) ++seen[p];
+            }
+        for (int i = 0; i < NPH; ++i)
+            if (a.ph[i].J_h > 2 || a.ph[i].J_w > 2 || seen[i] != 1) return hipErrorInvalidValue;
+    } else if (a.fused != 0) {
+        return hipErrorInvalidValue;
+    }
     if (PITCH > 0 && a.HP != PITCH) return hipErrorInvalidValue;
     // JW > 0: every phase with taps has that kernel-width tap count.
     for (int i = 0; JW > 0 && i < a.nphases; ++i)
         if (a.ph[i].J_w != JW && a.ph[i].J_h * a.ph[i].J_w != 0) return hipErrorInvalidValue;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(
-            (const void *)gi_halo_f32<NB, HG, TMASK, CPS, OCC, PITCH, JW, KS>,
+            (const void *)gi_halo_f32<NB, HG, TMASK, CPS, OCC, PITCH, JW, KS, NPH>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
     if (a.ci_tiles != ci_tiles) return hipErrorInvalidValue;
-    hipExtLaunchKernelGGL((gi_halo_f32<NB, HG, TMASK, CPS, OCC, PITCH, JW, KS>),
+    hipExtLaunchKernelGGL((gi_halo_f32<NB, HG, TMASK, CPS, OCC, PITCH, JW, KS, NPH>),
                           dim3(tiles * ci_tiles), dim3(256 * KS), (uint32_t)lds, s, ev.start,
                           ev.stop, 0, a);
     return hipGetLastError();
@@ -468,26 +710,35 @@ hipError_t launch_one(const HaloArgs &a, int tiles, int ci_tiles, size_t lds, hi
 // 23), and the four phases of 3 x 3 stride-2 kernels on 14-wide tiles (15).
 // ks: thread groups splitting the output channels (two for a 1 x 7 instance:
 // a 17 x 17 image batch of 32 gives fewer work-groups than compute units).
+// nph > 0: fused launches of that many phases (tap grids up to 2 x 2; the
+// 3 x 3 stride-2 ones at pitch 15 on 14-wide tiles, fixed, or any pitch),
+// ks then the thread groups sharing each stage, each with nph / ks phases.
 struct HaloCfg {
     int nb, hg;
     unsigned tmask;
-    int cps, pitch, jw, ks;
+    int cps, pitch, jw, ks, nph;
 };
 constexpr HaloCfg kCfg[] = {
-    {13, 4, kT9, 1, 30, 3, 1},   {13, 2, kT9, 1, 0, 0, 1},   {13, 2, kTs2, 4, 15, -1, 1},
-    {13, 2, kTs2, 4, 0, 0, 1},   {8, 2, kT7, 1, 33, 7, 1},   {8, 2, kT7, 1, 23, 7, 1},
-    {8, 2, kT7, 1, 0, 0, 1},     {13, 4, kTall, 1, 0, 0, 1}, {8, 4, kTall, 1, 0, 0, 1},
-    {4, 4, kTall, 1, 0, 0, 1},   {8, 2, kT7, 1, 23, 7, 2},
+    {13, 4, kT9, 1, 30, 3, 1, 0},   {13, 2, kT9, 1, 0, 0, 1, 0},   {13, 2, kTs2, 4, 15, -1, 1, 0},
+    {13, 2, kTs2, 4, 0, 0, 1, 0},   {8, 2, kT7, 1, 33, 7, 1, 0},   {8, 2, kT7, 1, 23, 7, 1, 0},
+    {8, 2, kT7, 1, 0, 0, 1, 0},     {13, 4, kTall, 1, 0, 0, 1, 0}, {8, 4, kTall, 1, 0, 0, 1, 0},
+    {4, 4, kTall, 1, 0, 0, 1, 0},   {8, 2, kT7, 1, 23, 7, 2, 0},   {13, 1, kTs2, 1, 15, 0, 2, 4},
+    {8, 1, kTs2, 1, 15, 0, 2, 4},   {13, 2, kTs2, 1, 0, 0, 2, 4},
 };
 
 }  // namespace
 
 unsigned halo_f32_tbit(int T) { return T >= 0 && T < 32 ? tbit(T) : 0u; }
 
-int halo_f32_config(int nb, unsigned tmask, int hg, int hp, int jw, int ks) {
+int halo_f32_config(int nb, unsigned tmask, int hg, int hp, int jw, int ks, int nph) {
     for (int i = 0; i < (int)(sizeof(kCfg) / sizeof(kCfg[0])); ++i) {
         const HaloCfg &c = kCfg[i];
-        if (c.nb != nb || c.ks != ks || c.hg < hg || (c.tmask & tmask) != tmask) continue;
+        if (c.nb != nb || c.ks != ks || c.nph != nph || c.hg < hg || (c.tmask & tmask) != tmask)
+            continue;
+        if (nph > 0) {
+            if (c.pitch == 0 || c.pitch == hp) return i;
+            continue;
+        }
         if (c.pitch == 0 || (c.pitch == hp && (c.jw == jw || c.jw < 0))) return i;
     }
     return -1;
@@ -498,6 +749,8 @@ int halo_f32_cps(int cfg) { return kCfg[cfg].cps; }
 int halo_f32_ks(int cfg) { return kCfg[cfg].ks; }
 
 bool halo_f32_fixed_pitch(int cfg) { return kCfg[cfg].pitch > 0; }
+
+int halo_f32_nph(int cfg) { return kCfg[cfg].nph; }
 
 size_t halo_f32_lds_bytes(int maxT, int HPc, int stages, int cps) {
     // stages x (weights + halos of cps chunks), plus the kilobyte the
@@ -519,12 +772,15 @@ hipError_t launch_halo_f32(const HaloArgs &a, int cfg, int tiles, int ci_tiles, 
         case 8: return launch_one<8, 4, kTall, 1, 2, 0, 0>(a, tiles, ci_tiles, lds, s, ev);
         case 9: return launch_one<4, 4, kTall, 1, 2, 0, 0>(a, tiles, ci_tiles, lds, s, ev);
         case 10: return launch_one<8, 2, kT7, 1, 2, 23, 7, 2>(a, tiles, ci_tiles, lds, s, ev);
+        case 11: return launch_one<13, 1, kTs2, 1, 2, 15, 0, 2, 4>(a, tiles, ci_tiles, lds, s, ev);
+        case 12: return launch_one<8, 1, kTs2, 1, 2, 15, 0, 2, 4>(a, tiles, ci_tiles, lds, s, ev);
+        case 13: return launch_one<13, 2, kTs2, 1, 2, 0, 0, 2, 4>(a, tiles, ci_tiles, lds, s, ev);
         default: return hipErrorInvalidValue;
     }
 }
 
-// Weight image [ci_tile][phase][chunk][tap][cp][ci'][2], zero where ci >= Ci
-// or co >= Co; ci' = (ci + 16 * (cp & 1)) mod 64, a rotation that puts the
+// Weight image [ci_tile][phase][chunk][tap][cp][ci'][2] (fused launches:
+// [ci_tile][chunk][tb + tap][cp][ci'][2]), zero where ci >= Ci or co >= Co; ci' = (ci + 16 * (cp & 1)) mod 64, a rotation that puts the
 // fragment reads of neighbouring co pairs on disjoint LDS banks.  One thread
 // per float4 of the image (input channels 2q, 2q+1 x output channels 2cp,
 // 2cp+1 of one tap): four independent loads and one store, so the whole
@@ -549,7 +805,10 @@ __global__ __launch_bounds__(256) void weight_image_f32(const float *__restrict_
         return (co < A.Co && ci < A.Ci) ? w[((int64_t)co * A.Ci + ci) * kHW + t] : 0.f;
     };
     const v4f v = {ld(co0, ci0), ld(co0 + 1, ci0), ld(co0, ci0 + 1), ld(co0 + 1, ci0 + 1)};
-    ((v4f *)(wk + (int64_t)ct * A.w_ci_stride + P.woff))[e] = v;
+    // Fused launches read one chunk of every phase as one block.
+    const int64_t at = A.fused ? (int64_t)(chunk * A.Tall + P.tb + tap) * 128 + (e & 127)
+                               : (int64_t)P.woff / 4 + e;
+    ((v4f *)(wk + (int64_t)ct * A.w_ci_stride))[at] = v;
 }
 
 hipError_t launch_weight_image_f32(const float *w, float *wk, const HaloArgs &a, int kH, int kW,

@@ -168,6 +168,16 @@ CONV2D_GI_API int conv2d_gi_set_halo_tile(int nb, int tile_rows, int tile_cols, 
 CONV2D_GI_API int conv2d_gi_set_halo_split(int groups);
 
 /*
+ * Test and diagnostic hook: how the fp32 HALO variant runs the stride
+ * phases of a work-group's tile for later calls in this process: 1 one
+ * phase after another (each over its own grad_out halo), 2 all phases per
+ * chunk of output channels over one shared halo (four phases of tap grids
+ * up to 2 x 2 only; other shapes are planned phase at a time).  0 restores
+ * the planner.  Returns CONV2D_GI_OK, or CONV2D_GI_EINVAL for other values.
+ */
+CONV2D_GI_API int conv2d_gi_set_halo_fusion(int mode);
+
+/*
  * Host-only: describe the plan the entry point would run for this shape
  * (dtype_bf16 = 0 for fp32 inputs, 1 for bf16), as text written into buf
  * (NUL-terminated, truncated to len).  Returns a status code.

@@ -250,6 +250,7 @@ def test_fixed_instances(idx):
     if tile:
         gi.set_halo_tile(tile[0], tile[1], tile[2], 0)
         gi.set_halo_split(tile[3])
+        gi.set_halo_fusion(tile[4])
     try:
         gi.set_variant(variant)
         desc = gi.plan(gi.make_params(*shape.as_tuple()[:10]), bf16)
@@ -261,6 +262,7 @@ def test_fixed_instances(idx):
         gi.set_variant(gi.VARIANT_AUTO)
         gi.set_halo_tile()
         gi.set_halo_split()
+        gi.set_halo_fusion()
 
 
 def test_tiny_workload_full():

@@ -15,6 +15,7 @@ def lib():
     yield
     gi.set_halo_tile()
     gi.set_halo_split()
+    gi.set_halo_fusion()
     gi.set_variant(gi.VARIANT_AUTO)
 
 
@@ -26,7 +27,7 @@ def plan_of(shape, bf16=False):
 WORKLOAD_PLANS = {
     "resnet_stage_3x3": ["variant=halo", "cfg=0", "HP=30"],
     "deep_late_stage": ["variant=halo", "cfg=0", "tile=14x14", "HP=30"],
-    "strided_downsample": ["variant=halo", "cfg=2", "HP=15"],
+    "strided_downsample": ["variant=halo", "cfg=11 fused", "HP=15"],
     "asym_1x7": ["variant=halo", "cfg=10 split=2", "fold", "HP=23"],
     "stem_7x7_s2": ["variant=stem", "ws_bytes=0", "tiles=16x7x7x1 whole=768 waves=4 pitch=19"],
     "deep_late_stage_bf16": ["variant=halo", "dtype=bf16", "cfg=0", "pitch=30"],
@@ -42,24 +43,33 @@ def test_workload_plans(name):
         assert part in desc, (name, part, desc)
 
 
-# (shape, bf16, variant, forced (nb, rows, cols, split) or None, plan
+# (shape, bf16, variant, forced (nb, rows, cols, split, fusion) or None, plan
 # substrings): ragged channel counts on each compile-time instance (split: the
-# fp32 output-channel split forced to 1 or 2 thread groups, 0 for the
-# planner's choice).
+# fp32 output-channel split forced to 1 or 2 thread groups; fusion: the fp32
+# stride phases forced phase at a time (1) or fused (2); 0: the planner's
+# choice).
 FIXED_INSTANCES = [
-    (S(3, 40, 28, 28, 20, 3, 3, 1, 1, 1), False, gi.VARIANT_HALO, (13, 14, 14, 0),
+    (S(3, 40, 28, 28, 20, 3, 3, 1, 1, 1), False, gi.VARIANT_HALO, (13, 14, 14, 0, 0),
      ["cfg=0", "HP=30", "tile=14x14"]),
-    (S(3, 40, 28, 28, 20, 3, 3, 1, 1, 1), False, gi.VARIANT_HALO, (13, 7, 28, 0),
+    (S(3, 40, 28, 28, 20, 3, 3, 1, 1, 1), False, gi.VARIANT_HALO, (13, 7, 28, 0, 0),
      ["cfg=0", "HP=30", "tile=7x28"]),
-    (S(2, 70, 28, 28, 20, 3, 3, 2, 1, 1), False, gi.VARIANT_HALO, (13, 14, 14, 0),
+    (S(2, 70, 28, 28, 20, 3, 3, 2, 1, 1), False, gi.VARIANT_HALO, (13, 14, 14, 0, 1),
      ["cfg=2", "HP=15"]),
-    (S(4, 30, 17, 17, 36, 1, 7, 1, 0, 3), False, gi.VARIANT_HALO, (8, 7, 17, 1),
+    (S(2, 70, 28, 28, 20, 3, 3, 2, 1, 1), False, gi.VARIANT_HALO, (13, 14, 14, 0, 2),
+     ["cfg=11 fused", "HP=15"]),
+    (S(2, 70, 28, 28, 20, 3, 3, 2, 1, 1), False, gi.VARIANT_HALO, (8, 7, 14, 0, 2),
+     ["cfg=12 fused", "HP=15", "tile=7x14"]),
+    (S(2, 70, 27, 29, 20, 3, 3, 2, 1, 1), False, gi.VARIANT_HALO, (13, 7, 15, 0, 2),
+     ["cfg=13 fused"]),
+    (S(1, 40, 21, 22, 12, 3, 2, 2, 1, 0), False, gi.VARIANT_HALO, (13, 11, 11, 0, 2),
+     ["cfg=13 fused"]),
+    (S(4, 30, 17, 17, 36, 1, 7, 1, 0, 3), False, gi.VARIANT_HALO, (8, 7, 17, 1, 0),
      ["cfg=4", "HP=33", "fold"]),
-    (S(4, 30, 17, 17, 36, 1, 7, 1, 0, 3), False, gi.VARIANT_HALO, (8, 7, 17, 2),
+    (S(4, 30, 17, 17, 36, 1, 7, 1, 0, 3), False, gi.VARIANT_HALO, (8, 7, 17, 2, 0),
      ["cfg=10 split=2", "HP=23", "fold"]),
-    (S(3, 64, 17, 17, 80, 1, 7, 1, 0, 3), False, gi.VARIANT_HALO, (8, 4, 17, 2),
+    (S(3, 64, 17, 17, 80, 1, 7, 1, 0, 3), False, gi.VARIANT_HALO, (8, 4, 17, 2, 0),
      ["cfg=10 split=2", "HP=23", "fold", "tile=4x17"]),
-    (S(3, 72, 14, 14, 40, 3, 3, 1, 1, 1), True, gi.VARIANT_HALO, (7, 14, 14, 0),
+    (S(3, 72, 14, 14, 40, 3, 3, 1, 1, 1), True, gi.VARIANT_HALO, (7, 14, 14, 0, 0),
      ["cfg=0", "pitch=30"]),
     (S(1, 2, 30, 30, 6, 7, 7, 2, 3, 3), False, gi.VARIANT_STEM, None,
      ["variant=stem"]),
@@ -73,12 +83,14 @@ def test_fixed_instance_plans(idx):
         if tile:
             gi.set_halo_tile(tile[0], tile[1], tile[2], 0)
             gi.set_halo_split(tile[3])
+            gi.set_halo_fusion(tile[4])
         gi.set_variant(variant)
         desc = plan_of(shape, bf16)
     finally:
         gi.set_variant(gi.VARIANT_AUTO)
         gi.set_halo_tile()
         gi.set_halo_split()
+        gi.set_halo_fusion()
     for part in parts:
         assert part in desc, (part, desc)
 
