@@ -1,4 +1,4 @@
-"""CPU oracle for conv2d grad_input (fp64 accumulation).
+"""CPU oracle for conv2d grad_input and grad_weight (fp64 accumulation).
 
 TEST INFRASTRUCTURE.  Only the tests, the smoke check and the benchmark's
 CPU-baseline leg may import this package.  The GPU library never does, and this
@@ -15,6 +15,11 @@ function computes, and which page passage it follows, is stated in ``oracle.c``:
 * ``grad_input_at``  -- the same at chosen flat indices of [N,Ci,H,W].
 * ``conv2d_forward`` -- the forward cross-correlation, written separately from
   the output side (forward mapping stated in the doppler direct kernel).
+* ``grad_weight``    -- the gradient with respect to the weight (the
+  computeGradWeight branch of doppler ``conv2d_backward.js``: [Co,Ci,kH,kW]
+  from grad_out and the forward input), the derivative of the forward mapping,
+  written from the weight side.  Also returns sum |g*x| per element.
+* ``grad_weight_at`` -- the same at chosen flat indices of [Co,Ci,kH,kW].
 
 Every function is pinned by tests against hand-worked examples, closed forms,
 the adjoint identity, finite differences and torch-CPU float64 library
@@ -88,6 +93,10 @@ class Oracle:
         lib.oracle_grad_input_at_f64.restype = None
         lib.oracle_conv2d_fwd_f64.argtypes = [_P, _P, _P] + _SHAPE_ARGS
         lib.oracle_conv2d_fwd_f64.restype = None
+        lib.oracle_grad_weight_f64.argtypes = [_P, _P, _P, _P] + _SHAPE_ARGS
+        lib.oracle_grad_weight_f64.restype = None
+        lib.oracle_grad_weight_at_f64.argtypes = [_P, _P, _P, ctypes.c_int64, _P, _P] + _SHAPE_ARGS
+        lib.oracle_grad_weight_at_f64.restype = None
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = _I
         self.lib = lib
@@ -125,6 +134,49 @@ class Oracle:
         self.lib.oracle_grad_input_at_f64(_ptr(g), _ptr(w), _ptr(idx),
                                           ctypes.c_int64(idx.shape[0]), _ptr(out),
                                           _ptr(s), *sh)
+        return out, s
+
+    def _gw_shape(self, x, grad_out, stride, padding, kernel_hw):
+        N, Ci, H, W = x.shape
+        Ng, Co, oH, oW = grad_out.shape
+        if Ng != N:
+            raise ValueError("x has %d batch items, grad_out has %d" % (N, Ng))
+        kH, kW = kernel_hw
+        ph, pw = padding
+        if stride < 1 or ph < 0 or pw < 0:
+            raise ValueError("stride must be >= 1 and padding >= 0")
+        if (H + 2 * ph - kH) // stride + 1 != oH or (W + 2 * pw - kW) // stride + 1 != oW:
+            raise ValueError("grad_out size does not match the forward geometry")
+        return (int(N), int(Ci), int(H), int(W), int(Co), int(kH), int(kW), int(stride),
+                int(ph), int(pw), int(oH), int(oW))
+
+    def grad_weight(self, x, grad_out, stride, padding, kernel_hw, with_abs=True):
+        """grad_weight [Co,Ci,kH,kW] (float64) and, if asked, sum |g*x| per element.
+
+        x: the forward input [N,Ci,H,W]; grad_out: [N,Co,oH,oW];
+        padding = (pad_h, pad_w); kernel_hw = (kH, kW).
+        """
+        x = _f64(x)
+        g = _f64(grad_out)
+        sh = self._gw_shape(x, g, stride, padding, kernel_hw)
+        Ci, Co, kH, kW = sh[1], sh[4], sh[5], sh[6]
+        out = np.empty((Co, Ci, kH, kW), dtype=np.float64)
+        s = np.empty_like(out) if with_abs else None
+        self.lib.oracle_grad_weight_f64(_ptr(x), _ptr(g), _ptr(out),
+                                        _ptr(s) if s is not None else None, *sh)
+        return (out, s) if with_abs else out
+
+    def grad_weight_at(self, x, grad_out, stride, padding, kernel_hw, flat_idx):
+        """grad_weight and sum |g*x| at flat indices of the [Co,Ci,kH,kW] result."""
+        x = _f64(x)
+        g = _f64(grad_out)
+        sh = self._gw_shape(x, g, stride, padding, kernel_hw)
+        idx = np.ascontiguousarray(np.asarray(flat_idx, dtype=np.int64).ravel())
+        out = np.empty(idx.shape[0], dtype=np.float64)
+        s = np.empty_like(out)
+        self.lib.oracle_grad_weight_at_f64(_ptr(x), _ptr(g), _ptr(idx),
+                                           ctypes.c_int64(idx.shape[0]), _ptr(out), _ptr(s),
+                                           *sh)
         return out, s
 
     def conv2d_forward(self, x, weight, stride, padding):
@@ -174,6 +226,16 @@ def conv2d_forward(x, weight, stride, padding):
     return _get().conv2d_forward(x, weight, stride, padding)
 
 
+def grad_weight(x, grad_out, stride, padding, kernel_hw, with_abs=True):
+    return _get().grad_weight(x, grad_out, stride, padding, kernel_hw, with_abs)
+
+
+def grad_weight_at(x, grad_out, stride, padding, kernel_hw, flat_idx):
+    return _get().grad_weight_at(x, grad_out, stride, padding, kernel_hw, flat_idx)
+
+
 grad_input.__doc__ = Oracle.grad_input.__doc__
 grad_input_at.__doc__ = Oracle.grad_input_at.__doc__
 conv2d_forward.__doc__ = Oracle.conv2d_forward.__doc__
+grad_weight.__doc__ = Oracle.grad_weight.__doc__
+grad_weight_at.__doc__ = Oracle.grad_weight_at.__doc__

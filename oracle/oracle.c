@@ -41,6 +41,22 @@
  * It is written from the forward side on purpose (a loop over output pixels),
  * so the adjoint identity <conv(x,w), g> = <x, grad_input(g,w)> checks the two
  * against each other rather than against a shared index formula.
+ *
+ * grad_weight (doppler conv2d_backward.js, the computeGradWeight branch: a
+ * [outChannels, inChannels, kernelH, kernelW] result computed from gradOutput
+ * and the forward input; its shader is not on the pages, so the definition is
+ * the derivative of the forward mapping above with respect to w):
+ *
+ *   grad_weight[co,ci,kh,kw] = sum over n < N, oh < oH, ow < oW of
+ *                              grad_out[n,co,oh,ow] * x[n,ci,ih,iw]
+ *   with ih = oh*stride - pad_h + kh, iw = ow*stride - pad_w + kw; terms with
+ *   (ih, iw) outside [0,H) x [0,W) are absent.
+ *
+ * It is written from the weight side (a loop over the output pixels each
+ * weight element touched), so <conv(x,w), g> = <w, grad_weight(x,g)> checks
+ * it against the forward function, and <x, grad_input(g,w)> = <w,
+ * grad_weight(x,g)> against grad_input.  abs_sum is the same sum of
+ * |grad_out * x|.
  */
 #include <math.h>
 #include <stddef.h>
@@ -189,5 +205,86 @@ void oracle_conv2d_fwd_f64(const double *x, const double *w, double *y, int N,
                 y[(plane * oH + oh) * oW + ow] = acc;
             }
         }
+    }
+}
+
+/* One grad_weight element, straight from the definition above. */
+static void grad_weight_element(const double *x, const double *grad_out,
+                                const shape_t *s, int64_t co, int64_t ci,
+                                int64_t kh, int64_t kw, double *value,
+                                double *abs_value)
+{
+    double acc = 0.0, acc_abs = 0.0;
+    for (int64_t n = 0; n < s->N; ++n) {
+        const double *gp = grad_out + (n * s->Co + co) * s->oH * s->oW;
+        const double *xp = x + (n * s->Ci + ci) * s->H * s->W;
+        for (int64_t oh = 0; oh < s->oH; ++oh) {
+            int64_t ih = oh * s->stride - s->pad_h + kh;
+            if (ih < 0 || ih >= s->H) continue;
+            for (int64_t ow = 0; ow < s->oW; ++ow) {
+                int64_t iw = ow * s->stride - s->pad_w + kw;
+                if (iw < 0 || iw >= s->W) continue;
+                double t = gp[oh * s->oW + ow] * xp[ih * s->W + iw];
+                acc += t;
+                acc_abs += fabs(t);
+            }
+        }
+    }
+    *value = acc;
+    *abs_value = acc_abs;
+}
+
+/*
+ * Full grad_weight.  x [N,Ci,H,W], grad_out [N,Co,oH,oW], out and abs_sum
+ * [Co,Ci,kH,kW]; all contiguous doubles.  abs_sum may be NULL.
+ */
+void oracle_grad_weight_f64(const double *x, const double *grad_out, double *out,
+                            double *abs_sum, int N, int Ci, int H, int W, int Co,
+                            int kH, int kW, int stride, int pad_h, int pad_w, int oH,
+                            int oW)
+{
+    shape_t s = make_shape(N, Ci, H, W, Co, kH, kW, stride, pad_h, pad_w, oH, oW);
+    int64_t total = s.Co * s.Ci * s.kH * s.kW;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t e = 0; e < total; ++e) {
+        int64_t kw = e % s.kW;
+        int64_t kh = (e / s.kW) % s.kH;
+        int64_t ci = (e / (s.kW * s.kH)) % s.Ci;
+        int64_t co = e / (s.kW * s.kH * s.Ci);
+        double v, va;
+        grad_weight_element(x, grad_out, &s, co, ci, kh, kw, &v, &va);
+        out[e] = v;
+        if (abs_sum) abs_sum[e] = va;
+    }
+}
+
+/*
+ * The same result at chosen elements only: flat_idx[i] indexes the
+ * [Co,Ci,kH,kW] tensor; indices outside it give NaN.
+ */
+void oracle_grad_weight_at_f64(const double *x, const double *grad_out,
+                               const int64_t *flat_idx, int64_t count, double *out,
+                               double *abs_sum, int N, int Ci, int H, int W, int Co,
+                               int kH, int kW, int stride, int pad_h, int pad_w, int oH,
+                               int oW)
+{
+    shape_t s = make_shape(N, Ci, H, W, Co, kH, kW, stride, pad_h, pad_w, oH, oW);
+    int64_t total = s.Co * s.Ci * s.kH * s.kW;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < count; ++i) {
+        int64_t f = flat_idx[i];
+        if (f < 0 || f >= total) {
+            out[i] = NAN;
+            if (abs_sum) abs_sum[i] = NAN;
+            continue;
+        }
+        int64_t kw = f % s.kW;
+        int64_t kh = (f / s.kW) % s.kH;
+        int64_t ci = (f / (s.kW * s.kH)) % s.Ci;
+        int64_t co = f / (s.kW * s.kH * s.Ci);
+        double v, va;
+        grad_weight_element(x, grad_out, &s, co, ci, kh, kw, &v, &va);
+        out[i] = v;
+        if (abs_sum) abs_sum[i] = va;
     }
 }
