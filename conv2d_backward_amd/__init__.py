@@ -17,7 +17,7 @@ import os
 
 __all__ = [
     "grad_input", "Conv2dGiParams", "Conv2dGiError", "LibraryNotBuilt", "load_library",
-    "make_params", "validate", "plan", "set_variant", "set_halo_tile", "set_halo_split", "set_halo_fusion", "release_workspaces", "set_profile_events", "library_path", "exported_names",
+    "make_params", "validate", "plan", "grad_weight", "grad_weight_plan", "set_variant", "set_halo_tile", "set_halo_split", "set_halo_fusion", "release_workspaces", "set_profile_events", "library_path", "exported_names",
     "OK", "EINVAL", "EUNSUPPORTED", "EHIP", "VARIANT_AUTO", "VARIANT_GENERIC", "VARIANT_HALO", "VARIANT_STEM",
 ]
 
@@ -77,6 +77,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.conv2d_gi_set_variant.restype = ctypes.c_int
     lib.conv2d_gi_plan.argtypes = [PP, ctypes.c_int, ctypes.c_char_p, ctypes.c_size_t]
     lib.conv2d_gi_plan.restype = ctypes.c_int
+    lib.conv2d_grad_weight.argtypes = [P, P, P, PP, P]
+    lib.conv2d_grad_weight.restype = ctypes.c_int
+    lib.conv2d_gw_plan.argtypes = [PP, ctypes.c_char_p, ctypes.c_size_t]
+    lib.conv2d_gw_plan.restype = ctypes.c_int
     lib.conv2d_gi_set_halo_tile.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]
     lib.conv2d_gi_set_halo_tile.restype = ctypes.c_int
     lib.conv2d_gi_set_halo_split.argtypes = [ctypes.c_int]
@@ -96,7 +100,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
 
 def exported_names():
     """Names of the C entry points the binding wraps."""
-    return ["conv2d_grad_input", "conv2d_grad_input_bf16", "conv2d_gi_validate",
+    return ["conv2d_grad_input", "conv2d_grad_input_bf16", "conv2d_grad_weight",
+            "conv2d_gw_plan", "conv2d_gi_validate",
             "conv2d_gi_strerror", "conv2d_gi_last_hip_error", "conv2d_gi_set_variant",
             "conv2d_gi_plan", "conv2d_gi_set_halo_tile", "conv2d_gi_set_halo_split",
             "conv2d_gi_set_halo_fusion",
@@ -221,5 +226,58 @@ def grad_input(grad_out, weight, *, stride: int, padding, input_hw, out=None, st
         code = fn(ctypes.c_void_p(grad_out.data_ptr()), ctypes.c_void_p(weight.data_ptr()),
                   ctypes.c_void_p(out.data_ptr()), ctypes.byref(p),
                   ctypes.c_void_p(s.cuda_stream))
+    _check(code)
+    return out
+
+
+def grad_weight_plan(p: Conv2dGiParams) -> str:
+    """Description of the launches conv2d_grad_weight would make for shape p."""
+    buf = ctypes.create_string_buffer(1024)
+    _check(load_library().conv2d_gw_plan(ctypes.byref(p), buf, len(buf)))
+    return buf.value.decode()
+
+
+def grad_weight(grad_out, x, *, stride: int, padding, kernel_hw, out=None, stream=None):
+    """grad_weight [Co, Ci, kH, kW] (fp32) of a conv2d, computed on the GPU.
+
+    grad_out [N, Co, oH, oW] and x [N, Ci, H, W] (the forward input): float32,
+    contiguous, on the same ROCm device.  padding: int or (pad_h, pad_w).
+    kernel_hw: (kH, kW).  out: optional float32 [Co, Ci, kH, kW] tensor to write
+    (every element is overwritten).  stream: a torch stream (default: the
+    device's current stream).  The call is asynchronous on that stream.
+    """
+    import torch
+
+    if isinstance(padding, int):
+        padding = (padding, padding)
+    pad_h, pad_w = (int(v) for v in padding)
+    kH, kW = (int(v) for v in kernel_hw)
+    if grad_out.dim() != 4 or x.dim() != 4:
+        raise ValueError("grad_out and x must be 4-D NCHW tensors")
+    if not (grad_out.is_cuda and x.is_cuda) or grad_out.device != x.device:
+        raise ValueError("grad_out and x must be on the same GPU device")
+    if grad_out.dtype != torch.float32 or x.dtype != torch.float32:
+        raise ValueError("grad_out and x must be float32")
+    if not (grad_out.is_contiguous() and x.is_contiguous()):
+        raise ValueError("grad_out and x must be contiguous")
+    N, Co, oH, oW = (int(v) for v in grad_out.shape)
+    Nx, Ci, H, W = (int(v) for v in x.shape)
+    if Nx != N:
+        raise ValueError("x has %d batch items, grad_out %d" % (Nx, N))
+    p = Conv2dGiParams(N, Ci, H, W, Co, kH, kW, int(stride), pad_h, pad_w, oH, oW)
+    lib = load_library()
+    _check(lib.conv2d_gi_validate(ctypes.byref(p)))
+    dev = grad_out.device
+    if out is None:
+        out = torch.empty((Co, Ci, kH, kW), dtype=torch.float32, device=dev)
+    elif (out.dtype != torch.float32 or out.device != dev or not out.is_contiguous()
+          or tuple(out.shape) != (Co, Ci, kH, kW)):
+        raise ValueError("out must be a contiguous float32 [Co,Ci,kH,kW] tensor on %s" % dev)
+    with torch.cuda.device(dev):
+        s = stream if stream is not None else torch.cuda.current_stream(dev)
+        code = lib.conv2d_grad_weight(ctypes.c_void_p(grad_out.data_ptr()),
+                                      ctypes.c_void_p(x.data_ptr()),
+                                      ctypes.c_void_p(out.data_ptr()), ctypes.byref(p),
+                                      ctypes.c_void_p(s.cuda_stream))
     _check(code)
     return out

@@ -785,6 +785,87 @@ int run(const T *grad_out, const T *weight, float *dst, const conv2d_gi_params *
     return CONV2D_GI_OK;
 }
 
+// grad_weight plan (fp32): 64 output channels x 16 input channels x a group
+// of kernel rows (at most gw_f32_max_taps() taps) per work-group; output
+// rows in groups of RPC rows (about 64 padded pixels per group); the groups
+// split into slices so the grid holds about two work-groups per compute unit.
+struct GwPlan {
+    gi::GwArgs args{};
+    size_t ws_bytes = 0;   // partial sums: slices x Co x Ci x kH x kW floats
+    size_t lds = 0;
+};
+
+bool plan_gw(const conv2d_gi_params &p, GwPlan &out) {
+    const int64_t lim = 0x7fff0000LL;
+    if ((int64_t)p.N * p.Co * p.oH * p.oW * 4 > lim) return false;
+    if ((int64_t)p.N * p.Ci * p.H * p.W * 4 > lim) return false;
+    if (p.kW > gi::gw_f32_max_taps()) return false;
+    gi::GwArgs &a = out.args;
+    a = gi::GwArgs{};
+    a.N = p.N;
+    a.Ci = p.Ci;
+    a.H = p.H;
+    a.W = p.W;
+    a.Co = p.Co;
+    a.oH = p.oH;
+    a.oW = p.oW;
+    a.stride = p.stride;
+    a.pad_h = p.pad_h;
+    a.pad_w = p.pad_w;
+    a.kH = p.kH;
+    a.kW = p.kW;
+    a.x_bytes = (uint32_t)((int64_t)p.N * p.Ci * p.H * p.W * 4);
+    a.g_bytes = (uint32_t)((int64_t)p.N * p.Co * p.oH * p.oW * 4);
+    a.co_blocks = (p.Co + 63) / 64;
+    a.ci_blocks = (p.Ci + 15) / 16;
+    a.khg = std::max(1, std::min(p.kH, gi::gw_f32_max_taps() / p.kW));
+    a.tap_groups = (p.kH + a.khg - 1) / a.khg;
+    const int OWP = 4 * ((p.oW + 3) / 4);
+    if (OWP > 64 * gi::gw_f32_max_blocks()) return false;
+    // Rows per group: about 64 padded pixels, fewer while the two LDS stages
+    // do not fit; one stage (no overlap of loads and arithmetic) for a single
+    // row that still does not fit.
+    a.XP = (OWP - 1) * p.stride + p.kW;
+    a.XPM = (a.XP + 63) / 64 * 64;
+    bool fits = false;
+    for (int rpc = std::max(1, std::min(p.oH, 64 / OWP)); rpc >= 1 && !fits; --rpc) {
+        a.RPC = rpc;
+        a.GM = (a.RPC * OWP + 63) / 64;
+        a.XR = (a.RPC - 1) * p.stride + a.khg;
+        a.CIP = a.XR * a.XPM + 4;
+        for (int st = 2; st >= (rpc == 1 ? 1 : 2) && !fits; --st) {
+            a.stages = st;
+            out.lds = gi::gw_f32_lds_bytes(a);
+            fits = out.lds <= (size_t)kLdsBytes;
+        }
+    }
+    if (!fits) return false;
+    a.groups_img = (p.oH + a.RPC - 1) / a.RPC;
+    const int64_t groups = (int64_t)p.N * a.groups_img;
+    const int64_t tiles = (int64_t)a.co_blocks * a.ci_blocks * a.tap_groups;
+    int64_t slices = std::max<int64_t>(1, std::min<int64_t>(groups, (2 * kCUs + tiles - 1) / tiles));
+    // An empty batch still writes dw (zeros): one slice of no groups.
+    a.groups_slice = (int)std::max<int64_t>(1, (groups + slices - 1) / slices);
+    slices = std::max<int64_t>(1, (groups + a.groups_slice - 1) / a.groups_slice);
+    a.slices = (int)slices;
+    if (tiles * slices > INT32_MAX) return false;
+    const int64_t total = (int64_t)p.Co * p.Ci * p.kH * p.kW;
+    if (total * 4 > lim) return false;
+    out.ws_bytes = (size_t)(slices * total * 4);
+    return true;
+}
+
+std::string describe_gw(const GwPlan &g) {
+    const gi::GwArgs &a = g.args;
+    return "variant=gw dtype=f32 ws_bytes=" + std::to_string(g.ws_bytes) +
+           " launches=2 [tiles=" + std::to_string(a.co_blocks) + "x" +
+           std::to_string(a.ci_blocks) + "x" + std::to_string(a.tap_groups) +
+           " khg=" + std::to_string(a.khg) + " slices=" + std::to_string(a.slices) +
+           " rows_per_group=" + std::to_string(a.RPC) + " groups_per_slice=" +
+           std::to_string(a.groups_slice) + " stages=" + std::to_string(a.stages) +
+           " lds=" + std::to_string(g.lds) + "]";
+}
+
 std::string describe(const Plan &plan, bool bf16) {
     std::string s = "variant=";
     s += plan.variant == CONV2D_GI_VARIANT_HALO   ? "halo"
@@ -855,9 +936,55 @@ std::string describe(const Plan &plan, bool bf16) {
     return s;
 }
 
+int run_gw(const float *grad_out, const float *x, float *dw, const conv2d_gi_params *p,
+           hipStream_t stream) {
+    int rc = validate(p);
+    if (rc != CONV2D_GI_OK) return rc;
+    const int64_t n_x = (int64_t)p->N * p->Ci * p->H * p->W;
+    const int64_t n_g = (int64_t)p->N * p->Co * p->oH * p->oW;
+    const int64_t n_w = (int64_t)p->Co * p->Ci * p->kH * p->kW;
+    if ((has_elems(n_w) && !dw) || (has_elems(n_g) && !grad_out) || (has_elems(n_x) && !x))
+        return CONV2D_GI_EINVAL;
+    if (n_w == 0) return CONV2D_GI_OK;
+    GwPlan plan;
+    if (!plan_gw(*p, plan)) return CONV2D_GI_EUNSUPPORTED;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail_hip(e);
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    void *ws = nullptr;
+    e = workspace_for(dev, stream, plan.ws_bytes, &ws);
+    if (e != hipSuccess) return fail_hip(e);
+    gi::KernelEvents ev;
+    if (g_prof_begin && g_prof_end) ev = {g_prof_begin, g_prof_end};
+    gi::GwArgs &a = plan.args;
+    a.x = x;
+    a.grad_out = grad_out;
+    a.part = (float *)ws;
+    a.dw = dw;
+    e = gi::launch_gw_f32(a, stream, ev);
+    if (e != hipSuccess) return fail_hip(e);
+    return CONV2D_GI_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int conv2d_grad_weight(const float *grad_out, const float *x, float *dw,
+                       const conv2d_gi_params *p, hipStream_t stream) {
+    return run_gw(grad_out, x, dw, p, stream);
+}
+
+int conv2d_gw_plan(const conv2d_gi_params *p, char *buf, size_t len) {
+    int rc = validate(p);
+    if (rc != CONV2D_GI_OK) return rc;
+    if (!buf || len == 0) return CONV2D_GI_EINVAL;
+    GwPlan plan;
+    if (!plan_gw(*p, plan)) return CONV2D_GI_EUNSUPPORTED;
+    std::snprintf(buf, len, "%s", describe_gw(plan).c_str());
+    return CONV2D_GI_OK;
+}
 
 int conv2d_grad_input(const float *grad_out, const float *weight, float *dst,
                       const conv2d_gi_params *p, hipStream_t stream) {
@@ -875,7 +1002,8 @@ const char *conv2d_gi_strerror(int code) {
     switch (code) {
         case CONV2D_GI_OK: return "success";
         case CONV2D_GI_EINVAL: return "invalid argument (null pointer or inconsistent shape)";
-        case CONV2D_GI_EUNSUPPORTED: return "shape beyond the library's 32-bit index width";
+        case CONV2D_GI_EUNSUPPORTED:
+            return "shape the library does not serve (32-bit index width or kernel limits)";
         case CONV2D_GI_EHIP: return "HIP runtime error";
         default: return "unknown status code";
     }

@@ -197,3 +197,35 @@ struct StemArgs {
 
 }  // namespace gi
 
+
+namespace gi {
+
+// Arguments of the fp32 grad_weight kernels (kernels_gw_f32.hip).
+//
+//   dw[co,ci,kh,kw] = sum over n, oh, ow of g[n,co,oh,ow] * x[n,ci,ih,iw],
+//   ih = oh*stride - pad_h + kh, iw = ow*stride - pad_w + kw (x = 0 outside),
+//
+// an implicit GEMM with M = Co, N = Ci*kH*kW and a long K = N*oH*oW.  Each
+// image's output rows are cut into groups of RPC rows; a "slice" is a run of
+// consecutive groups.  A work-group owns 64 output channels x 16 input
+// channels x the kernel rows [kh0, kh0+khg) of one slice and writes its sums
+// to part[slice]; a second kernel adds the slices in order into dw.
+struct GwArgs {
+    const float *x;          // [N, Ci, H, W] forward input
+    const float *grad_out;   // [N, Co, oH, oW]
+    float *part;             // [slices][Co][Ci][kH][kW] partial sums
+    float *dw;               // [Co][Ci][kH][kW]
+    uint32_t x_bytes, g_bytes;
+    int32_t N, Ci, H, W, Co, oH, oW, stride, pad_h, pad_w, kH, kW;
+    int32_t co_blocks, ci_blocks, tap_groups, khg;  // work-group tiles; kernel rows per tap group
+    int32_t RPC;             // output rows per group (one image)
+    int32_t groups_img;      // groups per image: ceil(oH / RPC)
+    int32_t groups_slice;    // groups per slice
+    int32_t slices;
+    int32_t GM;              // grad_out LDS blocks of 64 pixels per group: ceil(RPC*oW / 64)
+    int32_t XR, XP, XPM;     // input rows and columns per group; XPM: XP rounded up to 64
+    int32_t CIP;             // LDS floats per input channel: XR*XPM + 4
+    int32_t stages;          // LDS stages: 2 (next group loads during this one's arithmetic) or 1
+};
+
+}  // namespace gi

@@ -178,6 +178,36 @@ CONV2D_GI_API int conv2d_gi_set_halo_split(int groups);
 CONV2D_GI_API int conv2d_gi_set_halo_fusion(int mode);
 
 /*
+ * Gradient with respect to the weight (the next step of the same backward
+ * pass; the computeGradWeight branch of doppler conv2d_backward.js, whose
+ * shader is not on the pages, so the definition is the derivative of the
+ * forward mapping):
+ *
+ *   dw[co,ci,kh,kw] = sum over n, oh, ow of grad_out[n,co,oh,ow] * x[n,ci,ih,iw]
+ *   with ih = oh*stride - pad_h + kh, iw = ow*stride - pad_w + kw and x = 0
+ *   outside [0,H) x [0,W).
+ *
+ * grad_out: device [N, Co, oH, oW] fp32; x: device [N, Ci, H, W] fp32 (the
+ * forward input); dw: device [Co, Ci, kH, kW] fp32, fully overwritten (no
+ * accumulation into it).  p: the same shape struct as conv2d_grad_input,
+ * validated the same way.  Enqueued on `stream` (asynchronous).  The
+ * partial sums of the split pixel axis live in the library's per-stream
+ * scratch buffer and are added in a fixed order, so the result does not
+ * depend on scheduling.  Returns CONV2D_GI_OK, CONV2D_GI_EINVAL (null pointer
+ * for a non-empty tensor, inconsistent shape), CONV2D_GI_EUNSUPPORTED (kernel
+ * width above 16, output rows wider than 256 pixels, tensors of 2 GiB or more)
+ * or CONV2D_GI_EHIP.
+ */
+CONV2D_GI_API int conv2d_grad_weight(const float *grad_out, const float *x, float *dw,
+                                     const conv2d_gi_params *p, hipStream_t stream);
+
+/*
+ * Host-only: describe the launch conv2d_grad_weight would make for this shape,
+ * as text written into buf (NUL-terminated, truncated to len).
+ */
+CONV2D_GI_API int conv2d_gw_plan(const conv2d_gi_params *p, char *buf, size_t len);
+
+/*
  * Host-only: describe the plan the entry point would run for this shape
  * (dtype_bf16 = 0 for fp32 inputs, 1 for bf16), as text written into buf
  * (NUL-terminated, truncated to len).  Returns a status code.

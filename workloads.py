@@ -8,7 +8,8 @@ and benchmark may take their inputs from it without sharing any of the method.
 Recipe (every workload): numpy ``Generator(PCG64(seed))``, draws in float64,
 scaled in float64, cast to float32.  ``seed = 1000*c + 10*sub + t`` where c is
 the workload's index, sub is 0 for the first (or only) shape of a workload and
-1 for the second, and t is 1 for grad_out and 2 for weight.  bf16 inputs are
+1 for the second, and t is 1 for grad_out, 2 for weight and 3 for the forward
+input x (N(0,1); read by grad_weight).  bf16 inputs are
 the float32 draws rounded to nearest-even bf16; both sides consume the same
 bf16 bit patterns.
 """
@@ -141,6 +142,12 @@ def make_inputs(w: Workload):
     if w.dtype == "bf16":
         return bf16_bits(g), bf16_bits(wt)
     return g, wt
+
+
+def make_forward_input(w: Workload) -> np.ndarray:
+    """The forward input x [N, Ci, H, W] of a named workload, float32 N(0,1)
+    (grad_weight's second operand)."""
+    return draw(w.shape.dst_shape, seed_of(w.index, w.sub, 3), "normal", 1.0)
 
 
 def make_case(shape: Shape, seed: int, dist: str = "uniform"):
