@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(workloads.BY_NAME))
+    ap.add_argument("--op", default="grad_input", choices=["grad_input", "grad_weight"],
+                    help="the operation of the headline line (grad_weight: fp32 workloads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-others", action="store_true",
                     help="skip the short timing of the other workloads")
@@ -109,7 +111,7 @@ class HipEvents:
         self.hip.hipEventDestroy(ev)
 
 
-def time_workload(wl, steps, warmup, torch, gi, dev):
+def time_workload(wl, steps, warmup, torch, gi, dev, op="grad_input"):
     """Returns dict with whole-call ms, main-kernel ms (HIP events), flops.
 
     Everything from the warm-up to the last timed call is enqueued without a
@@ -122,10 +124,17 @@ def time_workload(wl, steps, warmup, torch, gi, dev):
     s = wl.shape
     _, tg, tw, out = device_inputs(wl, torch, dev)
     stream = torch.cuda.current_stream(dev)
+    if op == "grad_weight":
+        tx = torch.from_numpy(workloads.make_forward_input(wl)).to(dev)
+        dw = torch.empty(s.weight_shape, dtype=torch.float32, device=dev)
 
-    def call():
-        gi.grad_input(tg, tw, stride=s.stride, padding=(s.pad_h, s.pad_w),
-                      input_hw=(s.H, s.W), out=out, stream=stream)
+        def call():
+            gi.grad_weight(tg, tx, stride=s.stride, padding=(s.pad_h, s.pad_w),
+                           kernel_hw=(s.kH, s.kW), out=dw, stream=stream)
+    else:
+        def call():
+            gi.grad_input(tg, tw, stride=s.stride, padding=(s.pad_h, s.pad_w),
+                          input_hw=(s.H, s.W), out=out, stream=stream)
 
     hev = HipEvents()
     sp = stream.cuda_stream
@@ -206,19 +215,31 @@ def main():
     dev = torch.device("cuda:0")
     wl = workloads.BY_NAME[args.workload]
     s = wl.shape
+    op = args.op
+    if op == "grad_weight" and wl.dtype != "f32":
+        print("grad_weight is fp32 only", file=sys.stderr)
+        sys.exit(2)
 
-    r = time_workload(wl, args.steps, args.warmup, torch, gi, dev)
+    r = time_workload(wl, args.steps, args.warmup, torch, gi, dev, op)
     value = r["flops"] / (r["ms_per_step"] * 1e-3) / 1e12
     peak = PEAK_TFLOPS[wl.dtype]
-    plan_desc = gi.plan(gi.make_params(*s.as_tuple()[:10]), wl.dtype == "bf16")
+    if op == "grad_weight":
+        plan_desc = gi.grad_weight_plan(gi.make_params(*s.as_tuple()[:10]))
+    else:
+        plan_desc = gi.plan(gi.make_params(*s.as_tuple()[:10]), wl.dtype == "bf16")
     variant = profiling.plan_variant(plan_desc)
     kernel = profiling.kernel_name(variant, wl.dtype)
     achieved = r["flops"] / (r["kernel_ms"] * 1e-3) / 1e12
-    alg_bytes = s.algorithmic_bytes(2 if wl.dtype == "bf16" else 4)
+    if op == "grad_weight":
+        # grad_out and x read once, dw written once (fp32).
+        alg_bytes = 4 * (s.N * s.Co * s.oH * s.oW + s.N * s.Ci * s.H * s.W +
+                         s.Co * s.Ci * s.kH * s.kW)
+    else:
+        alg_bytes = s.algorithmic_bytes(2 if wl.dtype == "bf16" else 4)
     traffic = profiling.read_traffic(kernel, wl.name, plan_desc, variant, wl.dtype)
     mfma = profiling.read_mfma(kernel, wl.name, plan_desc, variant, wl.dtype)
     line = {
-        "metric": METRIC,
+        "metric": METRIC if op == "grad_input" else METRIC.replace("grad_input", "grad_weight"),
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -230,8 +251,9 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": wl.dtype,
-        "data": "synthetic (seeded PCG64: grad_out N(0,1), weight Kaiming-normal)",
-        "config": {"workload": wl.name, "N": s.N, "Ci": s.Ci, "Co": s.Co, "H": s.H, "W": s.W,
+        "data": "synthetic (seeded PCG64: grad_out N(0,1), weight Kaiming-normal%s)"
+                % (", forward input N(0,1)" if op == "grad_weight" else ""),
+        "config": {"workload": wl.name, "op": op, "N": s.N, "Ci": s.Ci, "Co": s.Co, "H": s.H, "W": s.W,
                    "kH": s.kH, "kW": s.kW, "stride": s.stride, "pad_h": s.pad_h,
                    "pad_w": s.pad_w, "oH": s.oH, "oW": s.oW, "eff_gflop": s.eff_flops / 1e9,
                    "plan": plan_desc},
@@ -274,7 +296,24 @@ def main():
                               "algorithmic_bytes": so.algorithmic_bytes(
                                   2 if o.dtype == "bf16" else 4)}
         line["other_workloads"] = others
-    if not args.no_cpu_baseline:
+        # The next row of the same backward pass: grad_weight (fp32 runs).
+        nxt = {}
+        for o in workloads.WORKLOADS:
+            if o.dtype != "f32" or o.name == "tiny":
+                continue
+            rw = time_workload(o, 20, 3, torch, gi, dev, "grad_weight")
+            so = o.shape
+            pw = gi.grad_weight_plan(gi.make_params(*so.as_tuple()[:10]))
+            vw = rw["flops"] / (rw["ms_per_step"] * 1e-3) / 1e12
+            nxt[o.name] = {"tflops": round(vw, 3), "ms_per_call": round(rw["ms_per_step"], 5),
+                           "kernel_ms": round(rw["kernel_ms"], 5),
+                           "frac_of_peak": round(vw / PEAK_TFLOPS["f32"], 4),
+                           "kernel_frac_of_peak": round(
+                               rw["flops"] / (rw["kernel_ms"] * 1e-3) / 1e12
+                               / PEAK_TFLOPS["f32"], 4),
+                           "plan": pw}
+        line["next_rows"] = {"grad_weight": nxt}
+    if not args.no_cpu_baseline and op == "grad_input":
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     if args.calibration_copy_mib > 0:
         n = args.calibration_copy_mib * 1024 * 1024 // 4

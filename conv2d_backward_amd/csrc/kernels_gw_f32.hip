@@ -249,24 +249,24 @@ hipError_t launch_gw_f32(const GwArgs &a, hipStream_t s, const KernelEvents &ev)
     if (a.khg == 3 && a.kW == 3) {
         if ((e = go((const void *)gi_gw_f32<3, 3>)) != hipSuccess) return e;
         hipExtLaunchKernelGGL((gi_gw_f32<3, 3>), grid, block, (uint32_t)lds, s, ev.start,
-                              nullptr, 0, a);
+                              ev.stop, 0, a);
     } else if (a.khg == 1 && a.kW == 7) {
         if ((e = go((const void *)gi_gw_f32<1, 7>)) != hipSuccess) return e;
         hipExtLaunchKernelGGL((gi_gw_f32<1, 7>), grid, block, (uint32_t)lds, s, ev.start,
-                              nullptr, 0, a);
+                              ev.stop, 0, a);
     } else if (a.khg == 2 && a.kW == 7) {
         if ((e = go((const void *)gi_gw_f32<2, 7>)) != hipSuccess) return e;
         hipExtLaunchKernelGGL((gi_gw_f32<2, 7>), grid, block, (uint32_t)lds, s, ev.start,
-                              nullptr, 0, a);
+                              ev.stop, 0, a);
     } else {
         if ((e = go((const void *)gi_gw_f32<0, 0>)) != hipSuccess) return e;
         hipExtLaunchKernelGGL((gi_gw_f32<0, 0>), grid, block, (uint32_t)lds, s, ev.start,
-                              nullptr, 0, a);
+                              ev.stop, 0, a);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int total = a.Co * a.Ci * a.kH * a.kW;
     hipExtLaunchKernelGGL(gw_reduce_f32, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
-                          nullptr, ev.stop, 0, a.part, a.dw, total, a.slices);
+                          nullptr, nullptr, 0, a.part, a.dw, total, a.slices);
     return hipGetLastError();
 }
 

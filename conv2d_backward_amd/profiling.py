@@ -45,6 +45,7 @@ KERNEL_SOURCES = {
     ("halo", "f32"): ["kernels_halo_f32.hip"],
     ("halo", "bf16"): ["kernels_halo_bf16.hip"],
     ("stem", "f32"): ["kernels_stem_f32.hip"],
+    ("gw", "f32"): ["kernels_gw_f32.hip"],
     ("generic", "f32"): ["kernels_generic.hip"],
     ("generic", "bf16"): ["kernels_generic.hip"],
 }
@@ -90,17 +91,23 @@ def _csv(run_dir: str, suffix: str) -> str:
     return hits[0]
 
 
-def _unprofiled_kernel_ms(bench_log: str, workload: str):
-    """Main-kernel ms of `workload` in a bench.py run without the profiler
-    (its headline workload or one of its other_workloads), else None."""
+def _unprofiled_kernel_ms(bench_log: str, workload: str, op: str = "grad_input"):
+    """Main-kernel ms of `workload` for `op` in a bench.py run without the
+    profiler (its headline line, one of its other_workloads or, for
+    grad_weight, its next_rows), else None."""
     line = _bench_line(bench_log)
-    if line["config"]["workload"] == workload:
+    if line["config"]["workload"] == workload and line["config"].get("op", "grad_input") == op:
         return line["roofline"]["kernel_ms"], "bench.py --steps %d --warmup %d" % (
             line["steps"], line["warmup"])
-    o = line.get("other_workloads", {}).get(workload)
+    if op == "grad_input":
+        o = line.get("other_workloads", {}).get(workload)
+        what = "other workloads"
+    else:
+        o = line.get("next_rows", {}).get(op, {}).get(workload)
+        what = "next rows"
     if o is None:
         return None
-    return o["kernel_ms"], "bench.py (other workloads: 20 steps after at least 3 warm-up steps and 0.1 s)"
+    return o["kernel_ms"], "bench.py (%s: 20 steps after at least 3 warm-up steps and 0.1 s)" % what
 
 
 def write_stats(run_dir: str, bench_log: str, workload: str, command: str,
@@ -132,7 +139,7 @@ def write_stats(run_dir: str, bench_log: str, workload: str, command: str,
                  "ratio %.3f)\n" % (short, rf["kernel_ms"] * 1e3, avg_us,
                                     rf["kernel_ms"] * 1e3 / avg_us))
         if plain_log:
-            u = _unprofiled_kernel_ms(plain_log, workload)
+            u = _unprofiled_kernel_ms(plain_log, workload, line["config"].get("op", "grad_input"))
             if u is not None:
                 fh.write("- without the profiler (`python3 %s`): %.2f us per launch "
                          "(ratio to the rocprofv3 average %.3f); the profiler's own "

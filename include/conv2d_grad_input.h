@@ -221,6 +221,8 @@ CONV2D_GI_API int conv2d_gi_plan(const conv2d_gi_params *p, int dtype_bf16, char
  * with the dispatch's own start time and their last one so that it records
  * `end` with its completion time (hipExtLaunchKernelGGL), so the caller can
  * time the contraction kernels apart from the reorder prologues before them.
+ * For conv2d_grad_weight both events bracket its contraction kernel alone,
+ * without the slice reduction that follows it.
  * NULL, NULL switches it off.  The events (hipEvent_t) stay the caller's.
  */
 CONV2D_GI_API void conv2d_gi_set_profile_events(hipEvent_t begin, hipEvent_t end);
