@@ -17,7 +17,7 @@ import os
 
 __all__ = [
     "grad_input", "Conv2dGiParams", "Conv2dGiError", "LibraryNotBuilt", "load_library",
-    "make_params", "validate", "plan", "grad_weight", "grad_weight_plan", "set_variant", "set_halo_tile", "set_halo_split", "set_halo_fusion", "release_workspaces", "set_profile_events", "library_path", "exported_names",
+    "make_params", "validate", "plan", "grad_weight", "grad_weight_plan", "set_variant", "set_halo_tile", "set_halo_split", "set_halo_fusion", "set_gw_variant", "set_gw_tile", "release_workspaces", "set_profile_events", "library_path", "exported_names",
     "OK", "EINVAL", "EUNSUPPORTED", "EHIP", "VARIANT_AUTO", "VARIANT_GENERIC", "VARIANT_HALO", "VARIANT_STEM",
 ]
 
@@ -87,6 +87,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.conv2d_gi_set_halo_split.restype = ctypes.c_int
     lib.conv2d_gi_set_halo_fusion.argtypes = [ctypes.c_int]
     lib.conv2d_gi_set_halo_fusion.restype = ctypes.c_int
+    lib.conv2d_gw_set_variant.argtypes = [ctypes.c_int]
+    lib.conv2d_gw_set_variant.restype = ctypes.c_int
+    lib.conv2d_gw_set_tile.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    lib.conv2d_gw_set_tile.restype = ctypes.c_int
     lib.conv2d_gi_set_profile_events.argtypes = [P, P]
     lib.conv2d_gi_set_profile_events.restype = None
     lib.conv2d_gi_release_workspaces.argtypes = []
@@ -104,7 +108,7 @@ def exported_names():
             "conv2d_gw_plan", "conv2d_gi_validate",
             "conv2d_gi_strerror", "conv2d_gi_last_hip_error", "conv2d_gi_set_variant",
             "conv2d_gi_plan", "conv2d_gi_set_halo_tile", "conv2d_gi_set_halo_split",
-            "conv2d_gi_set_halo_fusion",
+            "conv2d_gi_set_halo_fusion", "conv2d_gw_set_variant", "conv2d_gw_set_tile",
             "conv2d_gi_set_profile_events",
             "conv2d_gi_release_workspaces", "conv2d_gi_version"]
 
@@ -167,6 +171,20 @@ def set_halo_fusion(mode: int = 0):
     another (1) or all per chunk over one shared halo (2) for later calls
     (test hook); set_halo_fusion() restores the planner."""
     _check(load_library().conv2d_gi_set_halo_fusion(int(mode)))
+
+
+def set_gw_variant(mode: int = 0):
+    """Force grad_weight onto the 4-byte-load kernel (1) or the 16-byte-load
+    kernel (2; shapes it does not cover raise) for later calls (test hook);
+    set_gw_variant() restores the planner."""
+    _check(load_library().conv2d_gw_set_variant(int(mode)))
+
+
+def set_gw_tile(rows: int = 0, stages: int = 0, max_slices: int = 0):
+    """Force the 16-byte-load grad_weight kernel's rows per pixel group, LDS
+    stages and most slices for later calls (test hook); set_gw_tile()
+    restores the planner."""
+    _check(load_library().conv2d_gw_set_tile(int(rows), int(stages), int(max_slices)))
 
 
 def release_workspaces():

@@ -29,6 +29,10 @@ std::atomic<int> g_variant{CONV2D_GI_VARIANT_AUTO};
 std::atomic<int> g_tile_nb{0}, g_tile_tr{0}, g_tile_tc{0}, g_tile_stages{0};
 std::atomic<int> g_halo_split{0};
 std::atomic<int> g_halo_fusion{0};  // 0 planner, 1 phase at a time, 2 fused
+std::atomic<int> g_gw_variant{0};   // grad_weight: 0 planner, 1 4-byte loads, 2 16-byte loads
+std::atomic<int> g_gw_rows{0};      // grad_weight, 16-byte loads: forced rows per group (0 planner)
+std::atomic<int> g_gw_stages{0};    // ... and LDS stages (0 planner)
+std::atomic<int> g_gw_slices{0};    // ... and most slices (0 planner)
 thread_local char g_last_hip[256] = "";
 thread_local hipEvent_t g_prof_begin = nullptr, g_prof_end = nullptr;
 
@@ -855,6 +859,184 @@ bool plan_gw(const conv2d_gi_params &p, GwPlan &out) {
     return true;
 }
 
+// grad_weight with 16-byte direct loads (gi_gwd_f32).  Layout and column
+// map from the shape; then the rows per group, LDS stages and slices that
+// minimise a cost model: MFMA cycles of the busiest compute unit (including
+// the padding pixels of a layout), a per-group synchronisation cost that
+// other work-groups on the compute unit hide, and the slice reduction's
+// traffic.
+struct GwdPlan {
+    gi::GwdArgs args{};
+    int cfg = -1;
+    int occ = 0;           // work-groups per compute unit that fit in LDS
+    size_t ws_bytes = 0;
+    size_t lds = 0;
+};
+
+uint32_t div_magic(int d) {
+    return d <= 1 ? 0u : (uint32_t)((1ULL << 32) / (uint64_t)d + 1);
+}
+
+int odd_quads(int64_t n) {   // smallest multiple of 4 >= n whose quarter is odd
+    int64_t v = (n + 3) / 4 * 4;
+    if ((v / 4) % 2 == 0) v += 4;
+    return (int)v;
+}
+
+bool plan_gwd(const conv2d_gi_params &p, GwdPlan &out) {
+    const int64_t lim = 0x7fff0000LL;
+    if ((int64_t)p.N * p.Co * p.oH * p.oW * 4 > lim) return false;
+    if ((int64_t)p.N * p.Ci * p.H * p.W * 4 > lim) return false;
+    const int64_t total = (int64_t)p.Co * p.Ci * p.kH * p.kW;
+    if (total * 4 > lim) return false;
+    const int64_t HW = (int64_t)p.H * p.W;
+    const bool flat = p.stride == 1 && p.oH == p.H && p.oW == p.W && p.W >= 4 &&
+                      (p.kW == 3 || p.kW == 7) && (HW % 4 == 0 || (p.kH == 1 && p.pad_h == 0));
+    const bool rowpad = p.W % 4 == 0 && p.oW % 4 == 0;
+    if (!flat && !rowpad) return false;
+    gi::GwdArgs a{};
+    a.N = p.N;
+    a.Ci = p.Ci;
+    a.H = p.H;
+    a.W = p.W;
+    a.Co = p.Co;
+    a.oH = p.oH;
+    a.oW = p.oW;
+    a.stride = p.stride;
+    a.pad_h = p.pad_h;
+    a.pad_w = p.pad_w;
+    a.kH = p.kH;
+    a.kW = p.kW;
+    a.x_bytes = (uint32_t)((int64_t)p.N * p.Ci * HW * 4);
+    a.g_bytes = (uint32_t)((int64_t)p.N * p.Co * p.oH * p.oW * 4);
+    a.flat = flat ? 1 : 0;
+    a.plane_zero = flat && HW % 4 == 0 ? 1 : 0;
+    a.co_blocks = (p.Co + 63) / 64;
+    int cfg;
+    if (flat) {
+        cfg = p.kW == 3 ? 0 : 1;
+        a.colmap = 0;
+        a.khg = p.kW == 3 ? 3 : 1;
+    } else if (p.kW == 3 && (p.stride == 1 || p.stride == 2) && p.Ci >= 16) {
+        cfg = p.stride == 1 ? 2 : 3;
+        a.colmap = 0;
+        a.khg = 3;
+    } else {
+        cfg = p.stride == 2 ? 4 : 5;
+        a.colmap = 1;
+    }
+    const int NB = gi::gwd_f32_blocks(cfg);
+    const int kHW = p.kH * p.kW;
+    if (a.colmap == 0) {
+        a.tap_groups = (p.kH + a.khg - 1) / a.khg;
+        a.col_tiles = (p.Ci + 15) / 16 * a.tap_groups;
+        a.XC = 16;
+    } else {
+        a.khg = p.kH;
+        a.tap_groups = 1;
+        a.col_tiles = (int)((total / p.Co + 16 * NB - 1) / (16 * NB));
+        a.XC = 1;
+        for (int t = 0; t < a.col_tiles; ++t) {
+            const int64_t c0 = (int64_t)t * 16 * NB;
+            const int64_t c1 = std::min<int64_t>(c0 + 16 * NB, (int64_t)p.Ci * kHW) - 1;
+            a.XC = std::max<int>(a.XC, (int)(c1 / kHW - c0 / kHW + 1));
+        }
+    }
+    if (!flat) {
+        a.OWP = (p.oW + 15) / 16 * 16;
+        a.XO = (p.pad_w + 3) / 4 * 4;
+        a.XW = (a.XO - p.pad_w + (a.OWP - 1) * p.stride + p.kW + 3) / 4 * 4;
+    } else {
+        a.OWP = 16;
+        a.XO = 0;
+        a.XW = 4;
+    }
+    const int64_t tiles = (int64_t)a.co_blocks * a.col_tiles;
+    bool found = false;
+    double best = 0;
+    for (int R = 1; R <= std::min(p.oH, 64); ++R) {
+        if (g_gw_rows.load() > 0 && R != std::min(g_gw_rows.load(), p.oH)) continue;
+        int64_t nkb, LA, LX;
+        if (flat) {
+            nkb = ((int64_t)R * p.oW + 15) / 16;
+            LA = odd_quads(16 * nkb + 3);
+            LX = odd_quads(16 * nkb + (int64_t)(a.khg - 1) * p.W + p.kW + 2);
+        } else {
+            nkb = (int64_t)R * (a.OWP / 16);
+            LA = odd_quads((int64_t)R * a.OWP);
+            LX = odd_quads((int64_t)((R - 1) * p.stride + a.khg) * a.XW);
+        }
+        const int64_t nslots = 16 * LA + a.XC * (LX / 4);
+        const int64_t stage_floats = (nslots + 63) / 64 * 256;
+        for (int stages = 2; stages >= 1; --stages) {
+            if (g_gw_stages.load() > 0 && stages != g_gw_stages.load()) continue;
+            const size_t lds = (size_t)stages * stage_floats * 4;
+            if (lds > kLdsBytes) continue;
+            const int occ = (int)std::min<size_t>(gi::gwd_f32_max_wgs(cfg), kLdsBytes / lds);
+            const int64_t groups_img = (p.oH + R - 1) / R;
+            const int64_t groups = (int64_t)p.N * groups_img;
+            int64_t slices = std::max<int64_t>(
+                1, std::min<int64_t>(groups, (occ * kCUs + tiles - 1) / tiles));
+            if (g_gw_slices.load() > 0) slices = std::min<int64_t>(slices, g_gw_slices.load());
+            const int64_t gs = std::max<int64_t>(1, (groups + slices - 1) / slices);
+            slices = std::max<int64_t>(1, (groups + gs - 1) / gs);
+            if (tiles * slices > INT32_MAX) continue;
+            const int64_t wgs = tiles * slices;
+            const int64_t per_cu = (wgs + kCUs - 1) / kCUs;
+            // One wave per SIMD leaves LDS and load latency exposed
+            // (measured: about 0.7 of the MFMA rate); a single stage waits
+            // for each group's loads, which a second work-group hides.
+            const double mfma = (double)nkb * 4 * NB * 32;         // cycles per group
+            const double eff = occ >= 2 ? 1.0 : 0.7;
+            const double sync = stages == 2 ? 400.0 : (occ >= 2 ? 800.0 : 3000.0);
+            const double t_main = (double)per_cu * gs * mfma / eff +
+                                  (double)gs * sync * (double)((per_cu + occ - 1) / occ);
+            const double t_red = (double)slices * total * 8 * 2.4e9 / 4.0e12;
+            const double cost = t_main + t_red;
+            if (!found || cost < best) {
+                found = true;
+                best = cost;
+                a.R = R;
+                a.groups_img = (int)groups_img;
+                a.groups_slice = (int)gs;
+                a.slices = (int)slices;
+                a.LA = (int)LA;
+                a.LX = (int)LX;
+                a.XR = (R - 1) * p.stride + a.khg;
+                a.nslots = (int)nslots;
+                a.stage_floats = (int)stage_floats;
+                a.stages = stages;
+                out.lds = lds;
+                out.occ = occ;
+            }
+        }
+    }
+    if (!found) return false;
+    if (flat) a.XR = 0;
+    a.m_la4 = div_magic(a.LA / 4);
+    a.m_owp4 = div_magic(a.OWP / 4);
+    a.m_lx4 = div_magic(a.LX / 4);
+    a.m_xw4 = div_magic(a.XW / 4);
+    a.m_w = div_magic(p.W);
+    out.args = a;
+    out.cfg = cfg;
+    out.ws_bytes = (size_t)((int64_t)a.slices * total * 4);
+    return true;
+}
+
+std::string describe_gwd(const GwdPlan &g) {
+    const gi::GwdArgs &a = g.args;
+    return "variant=gwd dtype=f32 ws_bytes=" + std::to_string(g.ws_bytes) +
+           " launches=2 [cfg=" + std::to_string(g.cfg) +
+           (a.flat ? " layout=flat" : " layout=rowpad") +
+           (a.colmap ? " map=flattened" : " map=tap") + " tiles=" +
+           std::to_string(a.co_blocks) + "x" + std::to_string(a.col_tiles) +
+           " slices=" + std::to_string(a.slices) + " rows_per_group=" + std::to_string(a.R) +
+           " groups_per_slice=" + std::to_string(a.groups_slice) +
+           " stages=" + std::to_string(a.stages) + " lds=" + std::to_string(g.lds) +
+           " occ=" + std::to_string(g.occ) + "]";
+}
+
 std::string describe_gw(const GwPlan &g) {
     const gi::GwArgs &a = g.args;
     return "variant=gw dtype=f32 ws_bytes=" + std::to_string(g.ws_bytes) +
@@ -946,17 +1128,31 @@ int run_gw(const float *grad_out, const float *x, float *dw, const conv2d_gi_par
     if ((has_elems(n_w) && !dw) || (has_elems(n_g) && !grad_out) || (has_elems(n_x) && !x))
         return CONV2D_GI_EINVAL;
     if (n_w == 0) return CONV2D_GI_OK;
+    const int variant = g_gw_variant.load();
+    GwdPlan dplan;
+    const bool use_d = variant != 1 && plan_gwd(*p, dplan);
+    if (variant == 2 && !use_d) return CONV2D_GI_EUNSUPPORTED;
     GwPlan plan;
-    if (!plan_gw(*p, plan)) return CONV2D_GI_EUNSUPPORTED;
+    if (!use_d && !plan_gw(*p, plan)) return CONV2D_GI_EUNSUPPORTED;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return fail_hip(e);
     std::lock_guard<std::mutex> lock(g_ws_mu);
     void *ws = nullptr;
-    e = workspace_for(dev, stream, plan.ws_bytes, &ws);
+    e = workspace_for(dev, stream, use_d ? dplan.ws_bytes : plan.ws_bytes, &ws);
     if (e != hipSuccess) return fail_hip(e);
     gi::KernelEvents ev;
     if (g_prof_begin && g_prof_end) ev = {g_prof_begin, g_prof_end};
+    if (use_d) {
+        gi::GwdArgs &d = dplan.args;
+        d.x = x;
+        d.grad_out = grad_out;
+        d.part = (float *)ws;
+        d.dw = dw;
+        e = gi::launch_gwd_f32(d, dplan.cfg, stream, ev);
+        if (e != hipSuccess) return fail_hip(e);
+        return CONV2D_GI_OK;
+    }
     gi::GwArgs &a = plan.args;
     a.x = x;
     a.grad_out = grad_out;
@@ -980,9 +1176,30 @@ int conv2d_gw_plan(const conv2d_gi_params *p, char *buf, size_t len) {
     int rc = validate(p);
     if (rc != CONV2D_GI_OK) return rc;
     if (!buf || len == 0) return CONV2D_GI_EINVAL;
+    const int variant = g_gw_variant.load();
+    GwdPlan dplan;
+    if (variant != 1 && plan_gwd(*p, dplan)) {
+        std::snprintf(buf, len, "%s", describe_gwd(dplan).c_str());
+        return CONV2D_GI_OK;
+    }
+    if (variant == 2) return CONV2D_GI_EUNSUPPORTED;
     GwPlan plan;
     if (!plan_gw(*p, plan)) return CONV2D_GI_EUNSUPPORTED;
     std::snprintf(buf, len, "%s", describe_gw(plan).c_str());
+    return CONV2D_GI_OK;
+}
+
+int conv2d_gw_set_tile(int rows, int stages, int max_slices) {
+    if (rows < 0 || stages < 0 || stages > 2 || max_slices < 0) return CONV2D_GI_EINVAL;
+    g_gw_rows = rows;
+    g_gw_stages = stages;
+    g_gw_slices = max_slices;
+    return CONV2D_GI_OK;
+}
+
+int conv2d_gw_set_variant(int mode) {
+    if (mode < 0 || mode > 2) return CONV2D_GI_EINVAL;
+    g_gw_variant = mode;
     return CONV2D_GI_OK;
 }
 

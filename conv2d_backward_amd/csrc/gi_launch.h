@@ -100,5 +100,11 @@ int gw_f32_max_taps();
 int gw_f32_max_blocks();
 size_t gw_f32_lds_bytes(const GwArgs &a);
 hipError_t launch_gw_f32(const GwArgs &a, hipStream_t s, const KernelEvents &ev);
+// grad_weight fp32 with 16-byte direct loads: column blocks of instantiation
+// cfg (0 if none), LDS bytes, launch (main kernel, then the slice reduction).
+int gwd_f32_blocks(int cfg);
+int gwd_f32_max_wgs(int cfg);
+size_t gwd_f32_lds_bytes(const GwdArgs &a);
+hipError_t launch_gwd_f32(const GwdArgs &a, int cfg, hipStream_t s, const KernelEvents &ev);
 
 }  // namespace gi

@@ -207,18 +207,337 @@ __global__ __launch_bounds__(256) void gi_gw_f32(const GwArgs A) {
     }
 }
 
-// dw[e] = sum of part[s][e] over the slices, in slice order.
+// dw[e] = sum of part[s][e] over the slices.  A work-group takes 64
+// elements; its four waves sum the slices s = w, w+4, w+8, ... in order
+// (eight loads in flight per lane), then wave 0 adds the four sums in wave
+// order: a fixed order, so the result does not depend on scheduling.
 __global__ __launch_bounds__(256) void gw_reduce_f32(const float *__restrict__ part,
                                                      float *__restrict__ dw, int total,
                                                      int slices) {
-    const int e = blockIdx.x * 256 + threadIdx.x;
-    if (e >= total) return;
+    __shared__ float red[4][64];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int e = blockIdx.x * 64 + lane;
     float s = 0.f;
-    for (int k = 0; k < slices; ++k) s += part[(size_t)k * total + e];
-    dw[e] = s;
+    if (e < total) {
+        int k = w;
+        for (; k + 28 < slices; k += 32) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = part[(size_t)(k + 4 * u) * total + e];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) s += v[u];
+        }
+        for (; k < slices; k += 4) s += part[(size_t)k * total + e];
+    }
+    red[w][lane] = s;
+    __syncthreads();
+    if (w == 0 && e < total) dw[e] = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+}
+
+// ---------------------------------------------------------------------------
+// gi_gwd_f32: the same GEMM with 16-byte direct loads and four pixels per
+// lane per fragment read.
+//
+// V_MFMA_F32_16X16X4_F32 with rows = 16 output channels, columns = 16 GEMM
+// columns (ci, kh, kw), k = 4 pixels.  A K block is 16 pixels; lane
+// l = 16g + i takes pixels g, g+4, g+8, g+12 of it as the k index g of four
+// MFMAs, so one lane reads A[co_i] and B[column_i] at four positions 4 floats
+// apart (two ds_read2_b32 each).  Per-channel LDS runs have a length that is
+// 4 times an odd number: the 16 channels of a fragment start in 16 different
+// groups of 4 banks and the lane group g adds g, so a stride-1 read touches
+// 64 different banks.
+//
+// Direct loads move 16 bytes per lane into 16 consecutive LDS bytes per
+// lane: the stage is a run of 1 KB pieces, grad_out's channel runs first
+// (16*LA pieces, a multiple of 64), then the input channels' runs; each lane
+// computes which 16 source bytes land in its piece (zeros where there are
+// none).  That needs the pieces to start on 16-byte boundaries of the
+// source: in the row-padded layout rows of W and oW floats (multiples of 4);
+// in the flat layout the LDS run starts at the 16-byte boundary at or below
+// the first float needed, and each lane adds the run's offset (0..3).
+//
+// Flat layout: pixel f of a group (its rows back to back, W == oW) reads
+// input float f + kh'*W + kw - pad_w of the group's first needed row; a tap
+// whose column leaves the row reads the neighbouring row's float there, so
+// the grad_out value is replaced by zero for that (pixel, kw), as it is for
+// pixels past the group's end.  Rows above or below the image read zeros:
+// the pieces outside the channel's plane are not loaded (plane_zero), or no
+// tap reaches such a row (one kernel row, no row padding).
+constexpr int kGwdThreads = 256;
+
+__device__ __forceinline__ int udiv(int s, int d, uint32_t m) {
+    return d == 1 ? s : (int)__umulhi((uint32_t)s, m);
+}
+
+// Direct global -> LDS load of 16 bytes per lane: lane i writes dst + 16i;
+// an out-of-range offset writes zeros.  dst is the same for the whole wave.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void *dst, int voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)dst, 16, voff, 0, 0, 0);
+}
+
+// NB column blocks of 16 per wave; KW kernel columns (tap-major map, 0 for
+// the flattened map); S stride (0: read from A); FLAT pixel layout.
+template <int NB, int KW, int S, bool FLAT>
+__global__ __launch_bounds__(kGwdThreads) void gi_gwd_f32(const GwdArgs A) {
+    extern __shared__ __attribute__((aligned(16))) float sm[];
+    static_assert(!FLAT || (KW > 0 && S == 1), "flat layout: tap-major map, stride 1");
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int i = lane & 15, g = lane >> 4;
+    const int st = S > 0 ? S : A.stride;
+    const int kHW = A.kH * A.kW;
+
+    const int tiles = A.co_blocks * A.col_tiles;
+    const int J = xcd_order(blockIdx.x, gridDim.x);
+    const int tile = J % tiles, slice = J / tiles;
+    const int ct = tile % A.col_tiles, cob = tile / A.col_tiles;
+    const int co0 = cob * 64;
+    int ci_lo, kh0, c0 = 0;
+    if (KW > 0) {   // tap-major
+        const int cib = ct / A.tap_groups;
+        ci_lo = cib * 16;
+        kh0 = (ct - cib * A.tap_groups) * A.khg;
+    } else {
+        c0 = ct * 16 * NB;
+        ci_lo = c0 / kHW;
+        kh0 = 0;
+    }
+
+    // LDS offset of each block's column within the input tile, for this
+    // lane's first pixel (lane group g).
+    const int rowp = FLAT ? A.W : A.XW;
+    int cb[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        int seg, khr, kw;
+        if (KW > 0) {
+            seg = i;
+            khr = b / KW;
+            kw = b % KW;
+        } else {
+            const int col = min(c0 + 16 * b + i, A.Ci * kHW - 1);
+            const int ci = col / kHW, t = col - (col / kHW) * kHW;
+            seg = ci - ci_lo;
+            khr = t / A.kW;
+            kw = t - khr * A.kW;
+        }
+        cb[b] = 64 * A.LA + seg * A.LX + khr * rowp + kw +
+                (FLAT ? g : A.XO - A.pad_w + g * st);
+    }
+    const int abase = (16 * wave + i) * A.LA + g;
+
+    const int oHW = A.oH * A.oW, HW = A.H * A.W;
+    const int g_total = A.N * A.groups_img;
+    const int grp0 = slice * A.groups_slice;
+    const int ngrp = max(0, min(g_total, grp0 + A.groups_slice) - grp0);
+    const __amdgpu_buffer_rsrc_t grs = make_rsrc(A.grad_out, A.g_bytes);
+    const __amdgpu_buffer_rsrc_t xrs = make_rsrc(A.x, A.x_bytes);
+    const int LA4 = A.LA >> 2, LX4 = A.LX >> 2, OWP4 = A.OWP >> 2, XW4 = A.XW >> 2;
+    const int nins = (A.nslots + 63) >> 6;
+
+    // Direct loads of group grp (< ngrp) into stage buf.
+    auto issue = [&](int grp, int buf) {
+        float *stp = sm + buf * A.stage_floats;
+        const int gg = grp0 + grp;
+        const int n = gg / A.groups_img;
+        const int oh0 = (gg - n * A.groups_img) * A.R;
+        const int rows_v = min(A.R, A.oH - oh0);
+        const int gplane0 = (n * A.Co + co0) * oHW;
+        const int xplane0 = (n * A.Ci + ci_lo) * HW;
+        // Row-padded: first input row; flat: first needed float of a plane.
+        const int ih0 = oh0 * st - A.pad_h + kh0;
+        const int fbase = (oh0 - A.pad_h + kh0) * A.W - A.pad_w;
+        for (int k = wave; k < nins; k += 4) {
+            const int s = 64 * k + lane;
+            int off = -1;
+            if (k < LA4) {   // grad_out pieces (16*LA of them: whole instructions)
+                const int co = udiv(s, LA4, A.m_la4), q = s - co * LA4;
+                if (co0 + co < A.Co) {
+                    const int plane = gplane0 + co * oHW;
+                    if (FLAT) {
+                        off = ((plane + oh0 * A.oW) & ~3) + 4 * q;
+                    } else {
+                        const int r = udiv(q, OWP4, A.m_owp4), cc = q - r * OWP4;
+                        if (r < rows_v && 4 * cc < A.oW) off = plane + (oh0 + r) * A.oW + 4 * cc;
+                    }
+                }
+                dma16(grs, stp + 256 * k, off >= 0 ? off * 4 : kOOB);
+            } else {         // input pieces
+                const int s2 = s - 16 * A.LA;
+                const int seg = udiv(s2, LX4, A.m_lx4), q = s2 - seg * LX4;
+                if (s2 < A.XC * LX4 && ci_lo + seg < A.Ci) {
+                    const int plane = xplane0 + seg * HW;
+                    if (FLAT) {
+                        const int o = ((plane + fbase) & ~3) + 4 * q;
+                        if (o >= 0 && (!A.plane_zero || (o >= plane && o < plane + HW))) off = o;
+                    } else {
+                        const int xr = udiv(q, XW4, A.m_xw4), cc = q - xr * XW4;
+                        const int ih = ih0 + xr, iw = 4 * cc - A.XO;
+                        if (xr < A.XR && ih >= 0 && ih < A.H && iw >= 0 && iw < A.W)
+                            off = plane + ih * A.W + iw;
+                    }
+                }
+                dma16(xrs, stp + 256 * k, off >= 0 ? off * 4 : kOOB);
+            }
+        }
+    };
+
+    v4f acc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[b] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    // Fragments of one K block: A at stp + ab + ua, B of block b at
+    // stp + cbg[b] + ub.
+    struct Frag {
+        float a[4];
+        float b[NB][4];
+    };
+    auto load = [&](Frag &F, const float *stp, int ab, const int *cbg, int ua, int ub) {
+        const float *sa = stp + ab + ua;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) F.a[j] = sa[4 * j];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const float *sb = stp + cbg[b] + ub;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) F.b[b][j] = sb[4 * j * st];
+        }
+    };
+    // The block's 4*NB MFMAs.  FLAT: f0 = first pixel of the block, kv =
+    // pixels of the group (grad_out is masked per kernel column).
+    auto mma = [&](const Frag &F, int f0, int kv) {
+        if (FLAT) {
+            constexpr int NKW = KW > 0 ? KW : 1;
+            float am[NKW][4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                // Column of the pixel (W >= 2 here), moved out of every
+                // kernel column's range past the group's end.
+                const int f = f0 + g + 4 * j;
+                const int ow = f < kv ? f - (int)__umulhi((uint32_t)f, A.m_w) * A.W : 1 << 24;
+#pragma unroll
+                for (int kw = 0; kw < NKW; ++kw)
+                    am[kw][j] = (uint32_t)(ow + kw - A.pad_w) < (uint32_t)A.W ? F.a[j] : 0.f;
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+                    acc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(am[b % NKW][j], F.b[b][j], acc[b],
+                                                                  0, 0, 0);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+                    acc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(F.a[j], F.b[b][j], acc[b], 0, 0,
+                                                                  0);
+        }
+    };
+
+    // K blocks of one group, two in flight: the fragments of block kb+1 are
+    // read from LDS while block kb's MFMAs run.
+    auto compute = [&](int grp, int buf) {
+        const float *stp = sm + buf * A.stage_floats;
+        const int gg = grp0 + grp;
+        const int n = gg / A.groups_img;
+        const int oh0 = (gg - n * A.groups_img) * A.R;
+        const int rows_v = min(A.R, A.oH - oh0);
+        int cbg[NB];
+        int ab, nkb, kv = 0;
+        if (FLAT) {
+            kv = rows_v * A.oW;
+            const int aplane = (n * A.Co + co0 + 16 * wave + i) * oHW + oh0 * A.oW;
+            const int fbase = (oh0 - A.pad_h + kh0) * A.W - A.pad_w;
+            const int xs = ((n * A.Ci + ci_lo + i) * HW + fbase) & 3;
+#pragma unroll
+            for (int b = 0; b < NB; ++b) cbg[b] = cb[b] + xs;
+            ab = abase + (aplane & 3);
+            nkb = (kv + 15) >> 4;
+        } else {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) cbg[b] = cb[b];
+            ab = abase;
+            nkb = rows_v * (A.OWP >> 4);
+        }
+        // Offsets of K block kb: flat 16kb for both operands; row-padded
+        // (row r, segment c) -> A r*OWP + 16c, B (r*XW + 16c)*stride.
+        const int segs = A.OWP >> 4;
+        int r = 0, c = 0;   // row-padded position of the next block to load
+        auto next = [&](Frag &F, int kb) {
+            if (FLAT) {
+                load(F, stp, ab, cbg, 16 * kb, 16 * kb);
+            } else {
+                load(F, stp, ab, cbg, r * A.OWP + 16 * c, (r * A.XW + 16 * c) * st);
+                if (++c == segs) {
+                    c = 0;
+                    ++r;
+                }
+            }
+        };
+        Frag F0, F1;
+        if (nkb > 0) next(F0, 0);
+        for (int kb = 0; kb < nkb; kb += 2) {
+            if (kb + 1 < nkb) next(F1, kb + 1);
+            mma(F0, 16 * kb, kv);
+            if (kb + 1 < nkb) {
+                if (kb + 2 < nkb) next(F0, kb + 2);
+                mma(F1, 16 * (kb + 1), kv);
+            }
+        }
+    };
+
+    const bool two = A.stages == 2;
+    if (ngrp > 0) issue(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int grp = 0; grp < ngrp; ++grp) {
+        const int cur = two ? (grp & 1) : 0;
+        if (two && grp + 1 < ngrp) issue(grp + 1, cur ^ 1);
+        compute(grp, cur);
+        if (!two) {
+            __syncthreads();
+            if (grp + 1 < ngrp) issue(grp + 1, 0);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    }
+
+    // Partial sums: D[4g + r][i] of block b -> part[slice][co][ci][kh][kw].
+    float *pout = A.part + (size_t)slice * A.Co * A.Ci * kHW;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        int ci, kh, kw;
+        bool ok;
+        if (KW > 0) {
+            ci = ci_lo + i;
+            kh = kh0 + b / KW;
+            kw = b % KW;
+            ok = ci < A.Ci && kh < A.kH;
+        } else {
+            const int col = c0 + 16 * b + i;
+            ok = col < A.Ci * kHW;
+            ci = col / kHW;
+            const int t = col - ci * kHW;
+            kh = t / A.kW;
+            kw = t - kh * A.kW;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int co = co0 + 16 * wave + 4 * g + r;
+            if (ok && co < A.Co)
+                pout[((size_t)co * A.Ci + ci) * kHW + kh * A.kW + kw] = acc[b][r];
+        }
+    }
 }
 
 }  // namespace
+
+hipError_t launch_gw_reduce(const float *part, float *dw, int total, int slices, hipStream_t s) {
+    hipExtLaunchKernelGGL(gw_reduce_f32, dim3((unsigned)((total + 63) / 64)), dim3(256), 0, s,
+                          nullptr, nullptr, 0, part, dw, total, slices);
+    return hipGetLastError();
+}
 
 int gw_f32_max_taps() { return kGwMaxTaps; }
 int gw_f32_max_blocks() { return kGwMaxGM; }
@@ -264,10 +583,65 @@ hipError_t launch_gw_f32(const GwArgs &a, hipStream_t s, const KernelEvents &ev)
                               ev.stop, 0, a);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const int total = a.Co * a.Ci * a.kH * a.kW;
-    hipExtLaunchKernelGGL(gw_reduce_f32, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
-                          nullptr, nullptr, 0, a.part, a.dw, total, a.slices);
-    return hipGetLastError();
+    return launch_gw_reduce(a.part, a.dw, a.Co * a.Ci * a.kH * a.kW, a.slices, s);
+}
+
+// Instantiations of gi_gwd_f32: (NB, KW, S, FLAT).
+//   0: flat, tap-major, 3 kernel columns x 3 rows
+//   1: flat, tap-major, 7 kernel columns x 1 row
+//   2: row-padded, tap-major, 3 x 3, stride 1
+//   3: row-padded, tap-major, 3 x 3, stride 2
+//   4: row-padded, flattened map, 10 blocks, stride 2
+//   5: row-padded, flattened map, 8 blocks, any stride
+int gwd_f32_blocks(int cfg) {
+    static const int nb[] = {9, 7, 9, 9, 10, 8};
+    return cfg >= 0 && cfg < 6 ? nb[cfg] : 0;
+}
+
+// Work-groups per compute unit that the registers allow: one wave of each
+// work-group per SIMD, 512 registers per lane per SIMD shared by VGPRs and
+// AGPRs; the counts are those of the gfx950 build of each instantiation
+// (cfg 0: 180 + 36, cfg 1: 128 + 28, cfg 2: 128 + 36, cfg 3: 128 + 36,
+// cfg 4: 164 + 40, cfg 5: 136 + 32).
+int gwd_f32_max_wgs(int cfg) {
+    static const int occ[] = {2, 3, 3, 3, 2, 3};
+    return cfg >= 0 && cfg < 6 ? occ[cfg] : 1;
+}
+
+size_t gwd_f32_lds_bytes(const GwdArgs &a) {
+    return (size_t)a.stages * (size_t)a.stage_floats * sizeof(float);
+}
+
+hipError_t launch_gwd_f32(const GwdArgs &a, int cfg, hipStream_t s, const KernelEvents &ev) {
+    if (cfg < 0 || cfg > 5 || a.LA % 8 != 4 || a.LX % 8 != 4 || a.stages < 1 || a.stages > 2 ||
+        a.stage_floats % 256 != 0 || a.nslots != 16 * a.LA + a.XC * (a.LX / 4) ||
+        4 * a.nslots > a.stage_floats || (!a.flat && (a.OWP % 16 != 0 || a.XW % 4 != 0 ||
+                                                        a.XO % 4 != 0)))
+        return hipErrorInvalidValue;
+    const size_t lds = gwd_f32_lds_bytes(a);
+    if (lds > 160 * 1024) return hipErrorInvalidValue;
+    const int64_t wgs = (int64_t)a.co_blocks * a.col_tiles * a.slices;
+    const dim3 grid((unsigned)wgs), block(kGwdThreads);
+    auto go = [&](auto kern) -> hipError_t {
+        if (lds > 64 * 1024) {
+            hipError_t e = hipFuncSetAttribute((const void *)kern,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (e != hipSuccess) return e;
+        }
+        hipExtLaunchKernelGGL(kern, grid, block, (uint32_t)lds, s, ev.start, ev.stop, 0, a);
+        return hipGetLastError();
+    };
+    hipError_t e;
+    switch (cfg) {
+        case 0: e = go(gi_gwd_f32<9, 3, 1, true>); break;
+        case 1: e = go(gi_gwd_f32<7, 7, 1, true>); break;
+        case 2: e = go(gi_gwd_f32<9, 3, 1, false>); break;
+        case 3: e = go(gi_gwd_f32<9, 3, 2, false>); break;
+        case 4: e = go(gi_gwd_f32<10, 0, 2, false>); break;
+        default: e = go(gi_gwd_f32<8, 0, 0, false>); break;
+    }
+    if (e != hipSuccess) return e;
+    return launch_gw_reduce(a.part, a.dw, a.Co * a.Ci * a.kH * a.kW, a.slices, s);
 }
 
 }  // namespace gi

@@ -208,6 +208,26 @@ CONV2D_GI_API int conv2d_grad_weight(const float *grad_out, const float *x, floa
 CONV2D_GI_API int conv2d_gw_plan(const conv2d_gi_params *p, char *buf, size_t len);
 
 /*
+ * Test and diagnostic hook: which grad_weight kernel later calls in this
+ * process use: 1 the one with 4-byte direct loads (any shape the entry point
+ * accepts), 2 the one with 16-byte direct loads (shapes it does not cover
+ * return CONV2D_GI_EUNSUPPORTED), 0 restores the planner (16-byte loads
+ * where they apply).  Returns CONV2D_GI_OK, or CONV2D_GI_EINVAL for other
+ * values.
+ */
+CONV2D_GI_API int conv2d_gw_set_variant(int mode);
+
+/*
+ * Test and diagnostic hook for the 16-byte-load grad_weight kernel: output
+ * rows per pixel group (clamped to oH), LDS stages (1 or 2) and the most
+ * slices of the pixel axis, for later calls in this process; 0 leaves each
+ * to the planner.  A shape whose forced tile does not fit in LDS is planned
+ * on the 4-byte-load kernel.  Returns CONV2D_GI_OK, or CONV2D_GI_EINVAL for
+ * negative values or stages above 2.
+ */
+CONV2D_GI_API int conv2d_gw_set_tile(int rows, int stages, int max_slices);
+
+/*
  * Host-only: describe the plan the entry point would run for this shape
  * (dtype_bf16 = 0 for fp32 inputs, 1 for bf16), as text written into buf
  * (NUL-terminated, truncated to len).  Returns a status code.

@@ -99,6 +99,55 @@ def test_grad_weight_parity(idx):
     full_parity(SHAPES[idx], 5000 + idx)
 
 
+# Shapes for the 16-byte-load kernel's layouts and column maps.
+GWD_SHAPES = [
+    S(2, 20, 12, 12, 70, 3, 3, 1, 1, 1),     # flat 3x3: ragged Co and Ci blocks
+    S(2, 17, 9, 9, 64, 1, 7, 1, 0, 3),       # flat 1x7: planes not 16-byte aligned
+    S(3, 16, 14, 14, 64, 3, 3, 1, 1, 1),     # flat 14x14: groups end inside a K block
+    S(2, 20, 16, 16, 64, 3, 3, 2, 1, 1),     # row-padded, tap map, stride 2
+    S(2, 16, 10, 16, 64, 3, 3, 1, 0, 1),     # row-padded, tap map, stride 1 (oH != H)
+    S(1, 16, 8, 40, 64, 3, 3, 2, 1, 1),      # row-padded: two 16-pixel segments per row
+    S(1, 3, 24, 24, 64, 7, 7, 2, 3, 3),      # flattened map, stride 2 (stem-like)
+    S(1, 5, 16, 16, 20, 5, 5, 1, 2, 2),      # flattened map, any stride (1)
+    S(1, 4, 12, 12, 8, 2, 3, 3, 1, 1),       # flattened map, stride 3
+    S(2, 24, 8, 8, 130, 3, 3, 1, 1, 1),      # three Co blocks, last one ragged
+]
+
+
+@pytest.mark.parametrize("idx", range(len(GWD_SHAPES)))
+def test_grad_weight_parity_16byte_loads(idx):
+    sh = GWD_SHAPES[idx]
+    gi.set_gw_variant(2)
+    try:
+        full_parity(sh, 6000 + idx)
+    finally:
+        gi.set_gw_variant(0)
+
+
+@pytest.mark.parametrize("idx", range(len(GWD_SHAPES)))
+def test_grad_weight_parity_4byte_loads(idx):
+    gi.set_gw_variant(1)
+    try:
+        full_parity(GWD_SHAPES[idx], 6100 + idx)
+    finally:
+        gi.set_gw_variant(0)
+
+
+@pytest.mark.parametrize("rows,stages,slices", [(1, 1, 0), (2, 1, 3), (3, 2, 2), (5, 2, 0),
+                                               (14, 1, 1), (4, 2, 1)])
+def test_grad_weight_forced_tiles(rows, stages, slices):
+    """Forced rows per group, LDS stages and slices (several groups per
+    work-group through both pipelines) on the 16-byte-load kernel."""
+    gi.set_gw_variant(2)
+    gi.set_gw_tile(rows, stages, slices)
+    try:
+        full_parity(S(2, 16, 14, 14, 64, 3, 3, 1, 1, 1), 6200 + rows)
+        full_parity(S(2, 16, 12, 16, 64, 3, 3, 2, 1, 1), 6300 + rows)
+    finally:
+        gi.set_gw_tile(0, 0)
+        gi.set_gw_variant(0)
+
+
 def test_grad_weight_empty_batch_writes_zeros():
     sh = S(0, 5, 6, 6, 7, 3, 3, 1, 1, 1)
     got, ok = run_gw(np.zeros(sh.dst_shape, np.float32), np.zeros(sh.grad_out_shape, np.float32),
@@ -106,10 +155,18 @@ def test_grad_weight_empty_batch_writes_zeros():
     assert ok and np.array_equal(got, np.zeros(sh.weight_shape))
 
 
-def test_grad_weight_rejects_wide_kernels():
+def test_grad_weight_wide_kernels():
+    """kW = 17: past the 4-byte-load kernel's tap limit (it rejects the
+    shape); the 16-byte-load kernel's flattened map serves it."""
     sh = S(1, 2, 4, 40, 2, 1, 17, 1, 0, 8)
-    with pytest.raises(gi.Conv2dGiError):
-        run_gw(np.zeros(sh.dst_shape, np.float32), np.zeros(sh.grad_out_shape, np.float32), sh)
+    gi.set_gw_variant(1)
+    try:
+        with pytest.raises(gi.Conv2dGiError):
+            run_gw(np.zeros(sh.dst_shape, np.float32), np.zeros(sh.grad_out_shape, np.float32),
+                   sh)
+    finally:
+        gi.set_gw_variant(0)
+    full_parity(sh, 6400)
 
 
 GRADED = ["resnet_stage_3x3", "strided_downsample", "stem_7x7_s2", "asym_1x7",
