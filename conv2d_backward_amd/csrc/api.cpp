@@ -18,6 +18,7 @@
 #include "conv2d_grad_input.h"
 #include "gi_common.h"
 #include "gi_launch.h"
+#include "gw_common.h"
 
 namespace {
 

@@ -92,19 +92,4 @@ int stem_f32_waves(int ngroups);
 size_t stem_f32_lds_bytes(int hpmax, int waves);
 hipError_t launch_stem_f32(const StemArgs &a, hipStream_t s, const KernelEvents &ev);
 
-// grad_weight fp32 (kernels_gw_f32.hip): most taps per work-group, most
-// 64-pixel blocks per row group, the LDS bytes of a plan, and the launch of
-// the main kernel (events: its start) and the slice reduction (events: its
-// end).
-int gw_f32_max_taps();
-int gw_f32_max_blocks();
-size_t gw_f32_lds_bytes(const GwArgs &a);
-hipError_t launch_gw_f32(const GwArgs &a, hipStream_t s, const KernelEvents &ev);
-// grad_weight fp32 with 16-byte direct loads: column blocks of instantiation
-// cfg (0 if none), LDS bytes, launch (main kernel, then the slice reduction).
-int gwd_f32_blocks(int cfg);
-int gwd_f32_max_wgs(int cfg);
-size_t gwd_f32_lds_bytes(const GwdArgs &a);
-hipError_t launch_gwd_f32(const GwdArgs &a, int cfg, hipStream_t s, const KernelEvents &ev);
-
 }  // namespace gi

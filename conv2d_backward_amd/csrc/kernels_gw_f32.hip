@@ -34,8 +34,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "gi_common.h"
-#include "gi_launch.h"
+#include "gw_common.h"
 
 namespace gi {
 

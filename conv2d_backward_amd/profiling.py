@@ -45,7 +45,8 @@ KERNEL_SOURCES = {
     ("halo", "f32"): ["kernels_halo_f32.hip"],
     ("halo", "bf16"): ["kernels_halo_bf16.hip"],
     ("stem", "f32"): ["kernels_stem_f32.hip"],
-    ("gw", "f32"): ["kernels_gw_f32.hip"],
+    ("gw", "f32"): ["kernels_gw_f32.hip", "gw_common.h"],
+    ("gwd", "f32"): ["kernels_gw_f32.hip", "gw_common.h"],
     ("generic", "f32"): ["kernels_generic.hip"],
     ("generic", "bf16"): ["kernels_generic.hip"],
 }
