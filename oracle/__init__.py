@@ -20,6 +20,10 @@ function computes, and which page passage it follows, is stated in ``oracle.c``:
   from grad_out and the forward input), the derivative of the forward mapping,
   written from the weight side.  Also returns sum |g*x| per element.
 * ``grad_weight_at`` -- the same at chosen flat indices of [Co,Ci,kH,kW].
+* ``conv2d_forward_abs`` / ``conv2d_forward_at`` -- the forward result with
+  sum |x*w| per output element, full or at chosen flat indices of [N,Co,oH,oW].
+* ``grad_bias``      -- the per-output-channel bias gradient: grad_out summed
+  over (n, oh, ow) (doppler ``bias_add_backward.wgsl``), with sum |g|.
 
 Every function is pinned by tests against hand-worked examples, closed forms,
 the adjoint identity, finite differences and torch-CPU float64 library
@@ -97,6 +101,12 @@ class Oracle:
         lib.oracle_grad_weight_f64.restype = None
         lib.oracle_grad_weight_at_f64.argtypes = [_P, _P, _P, ctypes.c_int64, _P, _P] + _SHAPE_ARGS
         lib.oracle_grad_weight_at_f64.restype = None
+        lib.oracle_conv2d_fwd_abs_f64.argtypes = [_P, _P, _P, _P] + _SHAPE_ARGS
+        lib.oracle_conv2d_fwd_abs_f64.restype = None
+        lib.oracle_conv2d_fwd_at_f64.argtypes = [_P, _P, _P, ctypes.c_int64, _P, _P] + _SHAPE_ARGS
+        lib.oracle_conv2d_fwd_at_f64.restype = None
+        lib.oracle_grad_bias_f64.argtypes = [_P, _P, _P, _I, _I, _I, _I]
+        lib.oracle_grad_bias_f64.restype = None
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = _I
         self.lib = lib
@@ -198,6 +208,55 @@ class Oracle:
         return y
 
 
+    def _fwd_shape(self, x, w, stride, padding):
+        N, Ci, H, W = x.shape
+        Co, Ci_w, kH, kW = w.shape
+        if Ci_w != Ci:
+            raise ValueError("weight has %d input channels, x has %d" % (Ci_w, Ci))
+        ph, pw = padding
+        if stride < 1 or ph < 0 or pw < 0:
+            raise ValueError("stride must be >= 1 and padding >= 0")
+        oH = (H + 2 * ph - kH) // stride + 1
+        oW = (W + 2 * pw - kW) // stride + 1
+        if oH < 1 or oW < 1:
+            raise ValueError("empty forward output")
+        return (int(N), int(Ci), int(H), int(W), int(Co), int(kH), int(kW), int(stride),
+                int(ph), int(pw), int(oH), int(oW))
+
+    def conv2d_forward_abs(self, x, weight, stride, padding, with_abs=True):
+        """Forward y [N,Co,oH,oW] and, if asked, sum |x*w| per output element."""
+        x = _f64(x)
+        w = _f64(weight)
+        sh = self._fwd_shape(x, w, stride, padding)
+        y = np.empty((sh[0], sh[4], sh[10], sh[11]), dtype=np.float64)
+        s = np.empty_like(y) if with_abs else None
+        self.lib.oracle_conv2d_fwd_abs_f64(_ptr(x), _ptr(w), _ptr(y),
+                                           _ptr(s) if s is not None else None, *sh)
+        return (y, s) if with_abs else y
+
+    def conv2d_forward_at(self, x, weight, stride, padding, flat_idx):
+        """Forward result and sum |x*w| at flat indices of [N,Co,oH,oW]."""
+        x = _f64(x)
+        w = _f64(weight)
+        sh = self._fwd_shape(x, w, stride, padding)
+        idx = np.ascontiguousarray(np.asarray(flat_idx, dtype=np.int64).ravel())
+        out = np.empty(idx.shape[0], dtype=np.float64)
+        s = np.empty_like(out)
+        self.lib.oracle_conv2d_fwd_at_f64(_ptr(x), _ptr(w), _ptr(idx),
+                                          ctypes.c_int64(idx.shape[0]), _ptr(out), _ptr(s), *sh)
+        return out, s
+
+    def grad_bias(self, grad_out, with_abs=True):
+        """grad_bias [Co] (float64) and, if asked, sum |g| per channel."""
+        g = _f64(grad_out)
+        N, Co, oH, oW = g.shape
+        out = np.empty(Co, dtype=np.float64)
+        s = np.empty_like(out) if with_abs else None
+        self.lib.oracle_grad_bias_f64(_ptr(g), _ptr(out), _ptr(s) if s is not None else None,
+                                      int(N), int(Co), int(oH), int(oW))
+        return (out, s) if with_abs else out
+
+
 _default = None
 
 
@@ -234,8 +293,23 @@ def grad_weight_at(x, grad_out, stride, padding, kernel_hw, flat_idx):
     return _get().grad_weight_at(x, grad_out, stride, padding, kernel_hw, flat_idx)
 
 
+def conv2d_forward_abs(x, weight, stride, padding, with_abs=True):
+    return _get().conv2d_forward_abs(x, weight, stride, padding, with_abs)
+
+
+def conv2d_forward_at(x, weight, stride, padding, flat_idx):
+    return _get().conv2d_forward_at(x, weight, stride, padding, flat_idx)
+
+
+def grad_bias(grad_out, with_abs=True):
+    return _get().grad_bias(grad_out, with_abs)
+
+
 grad_input.__doc__ = Oracle.grad_input.__doc__
 grad_input_at.__doc__ = Oracle.grad_input_at.__doc__
 conv2d_forward.__doc__ = Oracle.conv2d_forward.__doc__
 grad_weight.__doc__ = Oracle.grad_weight.__doc__
 grad_weight_at.__doc__ = Oracle.grad_weight_at.__doc__
+conv2d_forward_abs.__doc__ = Oracle.conv2d_forward_abs.__doc__
+conv2d_forward_at.__doc__ = Oracle.conv2d_forward_at.__doc__
+grad_bias.__doc__ = Oracle.grad_bias.__doc__

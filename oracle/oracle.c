@@ -57,6 +57,18 @@
  * it against the forward function, and <x, grad_input(g,w)> = <w,
  * grad_weight(x,g)> against grad_input.  abs_sum is the same sum of
  * |grad_out * x|.
+ *
+ * grad_bias (doppler bias_add_backward.wgsl: the bias gradient is the output
+ * gradient summed over every position the bias was added to; for a
+ * convolution's per-output-channel bias those are all (n, oh, ow)):
+ *
+ *   grad_bias[co] = sum over n < N, oh < oH, ow < oW of grad_out[n,co,oh,ow]
+ *
+ * in the order n, oh, ow; abs_sum is the sum of |grad_out|.
+ *
+ * The forward function also comes with the sum of |x * w| per output element
+ * (the scale of a GPU forward result's tolerance) and a sampled form, both
+ * from one per-element routine that sums in the same order as the full loop.
  */
 #include <math.h>
 #include <stddef.h>
@@ -205,6 +217,107 @@ void oracle_conv2d_fwd_f64(const double *x, const double *w, double *y, int N,
                 y[(plane * oH + oh) * oW + ow] = acc;
             }
         }
+    }
+}
+
+/* One forward element and its sum of |x * w|, in the order ci, kh, kw. */
+static void forward_element(const double *x, const double *w, const shape_t *s,
+                            int64_t n, int64_t co, int64_t oh, int64_t ow,
+                            double *value, double *abs_value)
+{
+    double acc = 0.0, acc_abs = 0.0;
+    for (int64_t ci = 0; ci < s->Ci; ++ci) {
+        const double *xp = x + (n * s->Ci + ci) * s->H * s->W;
+        const double *wp = w + (co * s->Ci + ci) * s->kH * s->kW;
+        for (int64_t kh = 0; kh < s->kH; ++kh) {
+            int64_t ih = oh * s->stride - s->pad_h + kh;
+            if (ih < 0 || ih >= s->H) continue;
+            for (int64_t kw = 0; kw < s->kW; ++kw) {
+                int64_t iw = ow * s->stride - s->pad_w + kw;
+                if (iw < 0 || iw >= s->W) continue;
+                double t = xp[ih * s->W + iw] * wp[kh * s->kW + kw];
+                acc += t;
+                acc_abs += fabs(t);
+            }
+        }
+    }
+    *value = acc;
+    *abs_value = acc_abs;
+}
+
+/*
+ * Forward cross-correlation with the sum of |x * w| per output element.
+ * x [N,Ci,H,W], w [Co,Ci,kH,kW], y and abs_sum [N,Co,oH,oW]; abs_sum may be
+ * NULL.
+ */
+void oracle_conv2d_fwd_abs_f64(const double *x, const double *w, double *y, double *abs_sum,
+                               int N, int Ci, int H, int W, int Co, int kH, int kW,
+                               int stride, int pad_h, int pad_w, int oH, int oW)
+{
+    shape_t s = make_shape(N, Ci, H, W, Co, kH, kW, stride, pad_h, pad_w, oH, oW);
+    int64_t planes = s.N * s.Co;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t plane = 0; plane < planes; ++plane) {
+        int64_t n = plane / s.Co, co = plane % s.Co;
+        for (int64_t oh = 0; oh < s.oH; ++oh)
+            for (int64_t ow = 0; ow < s.oW; ++ow) {
+                double v, va;
+                forward_element(x, w, &s, n, co, oh, ow, &v, &va);
+                y[(plane * s.oH + oh) * s.oW + ow] = v;
+                if (abs_sum) abs_sum[(plane * s.oH + oh) * s.oW + ow] = va;
+            }
+    }
+}
+
+/*
+ * The forward result and its abs-sum at chosen elements: flat_idx[i] indexes
+ * the [N,Co,oH,oW] tensor; indices outside it give NaN.
+ */
+void oracle_conv2d_fwd_at_f64(const double *x, const double *w, const int64_t *flat_idx,
+                              int64_t count, double *out, double *abs_sum, int N, int Ci,
+                              int H, int W, int Co, int kH, int kW, int stride, int pad_h,
+                              int pad_w, int oH, int oW)
+{
+    shape_t s = make_shape(N, Ci, H, W, Co, kH, kW, stride, pad_h, pad_w, oH, oW);
+    int64_t total = s.N * s.Co * s.oH * s.oW;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < count; ++i) {
+        int64_t f = flat_idx[i];
+        if (f < 0 || f >= total) {
+            out[i] = NAN;
+            if (abs_sum) abs_sum[i] = NAN;
+            continue;
+        }
+        int64_t ow = f % s.oW;
+        int64_t oh = (f / s.oW) % s.oH;
+        int64_t co = (f / (s.oW * s.oH)) % s.Co;
+        int64_t n = f / (s.oW * s.oH * s.Co);
+        double v, va;
+        forward_element(x, w, &s, n, co, oh, ow, &v, &va);
+        out[i] = v;
+        if (abs_sum) abs_sum[i] = va;
+    }
+}
+
+/*
+ * grad_bias [Co] from grad_out [N,Co,oH,oW]; abs_sum [Co] may be NULL.
+ */
+void oracle_grad_bias_f64(const double *grad_out, double *out, double *abs_sum, int N,
+                          int Co, int oH, int oW)
+{
+    int64_t plane = (int64_t)oH * oW;
+#pragma omp parallel for schedule(static)
+    for (int64_t co = 0; co < Co; ++co) {
+        double acc = 0.0, acc_abs = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+            const double *gp = grad_out + (n * Co + co) * plane;
+            for (int64_t p = 0; p < plane; ++p) {
+                acc += gp[p];
+                acc_abs += fabs(gp[p]);
+            }
+        }
+        out[co] = acc;
+        if (abs_sum) abs_sum[co] = acc_abs;
     }
 }
 
