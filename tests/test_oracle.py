@@ -313,7 +313,8 @@ MUTANTS = {
     "drop_last_co": ("for (int64_t co = 0; co < s->Co; ++co)",
                      "for (int64_t co = 0; co < s->Co - 1; ++co)"),
     # the abs-sum accumulates signed terms
-    "abs_sum_signed": ("acc_abs += fabs(t);", "acc_abs += t;"),
+    "abs_sum_signed": ("double t = g * w;\n                acc += t;\n                acc_abs += fabs(t);",
+                       "double t = g * w;\n                acc += t;\n                acc_abs += t;"),
     # the sampled entry point decodes the flat index with H and W swapped
     "at_index_swap": ("int64_t ih = (f / s.W) % s.H;", "int64_t ih = (f / s.H) % s.W;"),
 }
@@ -323,7 +324,7 @@ MUTANTS = {
 def test_mutant_is_caught(tmp_path, name):
     old, new = MUTANTS[name]
     src = open(oracle.SOURCE).read()
-    assert src.count(old) >= 1, "mutation anchor not found: %s" % name
+    assert src.count(old) == 1, "mutation anchor not found or not unique: %s" % name
     mutated = src.replace(old, new, 1)
     cpath = tmp_path / ("mut_%s.c" % name)
     cpath.write_text(mutated)

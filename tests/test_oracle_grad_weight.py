@@ -167,22 +167,23 @@ def test_gw_pin(o, pin):
 
 GW_MUTANTS = {
     # wrong sign of the tap offset in the row gather
-    "kh_sign": ("int64_t ih = oh * s->stride - s->pad_h + kh;",
-                "int64_t ih = oh * s->stride + s->pad_h - kh;"),
+    "kh_sign": ("for (int64_t oh = 0; oh < s->oH; ++oh) {\n            int64_t ih = oh * s->stride - s->pad_h + kh;",
+                "for (int64_t oh = 0; oh < s->oH; ++oh) {\n            int64_t ih = oh * s->stride + s->pad_h - kh;"),
     # pad_w used for the rows
-    "pad_h_from_w": ("int64_t ih = oh * s->stride - s->pad_h + kh;",
-                     "int64_t ih = oh * s->stride - s->pad_w + kh;"),
+    "pad_h_from_w": ("for (int64_t oh = 0; oh < s->oH; ++oh) {\n            int64_t ih = oh * s->stride - s->pad_h + kh;",
+                     "for (int64_t oh = 0; oh < s->oH; ++oh) {\n            int64_t ih = oh * s->stride - s->pad_w + kh;"),
     # stride dropped from the column gather
-    "no_w_stride": ("int64_t iw = ow * s->stride - s->pad_w + kw;",
-                    "int64_t iw = ow - s->pad_w + kw;"),
+    "no_w_stride": ("for (int64_t ow = 0; ow < s->oW; ++ow) {\n                int64_t iw = ow * s->stride - s->pad_w + kw;",
+                    "for (int64_t ow = 0; ow < s->oW; ++ow) {\n                int64_t iw = ow - s->pad_w + kw;"),
     # off-by-one image bound in w
-    "iw_bound": ("if (iw < 0 || iw >= s->W) continue;", "if (iw < 0 || iw > s->W) continue;"),
+    "iw_bound": ("if (iw < 0 || iw >= s->W) continue;\n                double t = gp[",
+                 "if (iw < 0 || iw > s->W) continue;\n                double t = gp["),
     # the last batch item dropped
     "drop_last_n": ("for (int64_t n = 0; n < s->N; ++n) {\n        const double *gp",
                     "for (int64_t n = 0; n < s->N - 1; ++n) {\n        const double *gp"),
     # input read with the channel index of the gradient (operands mixed up)
-    "x_channel_co": ("const double *xp = x + (n * s->Ci + ci) * s->H * s->W;",
-                     "const double *xp = x + (n * s->Ci + co % s->Ci) * s->H * s->W;"),
+    "x_channel_co": ("const double *gp = grad_out + (n * s->Co + co) * s->oH * s->oW;\n        const double *xp = x + (n * s->Ci + ci) * s->H * s->W;",
+                     "const double *gp = grad_out + (n * s->Co + co) * s->oH * s->oW;\n        const double *xp = x + (n * s->Ci + co % s->Ci) * s->H * s->W;"),
     # the abs-sum accumulates signed terms
     "abs_sum_signed": ("double t = gp[oh * s->oW + ow] * xp[ih * s->W + iw];\n                acc += t;\n                acc_abs += fabs(t);",
                        "double t = gp[oh * s->oW + ow] * xp[ih * s->W + iw];\n                acc += t;\n                acc_abs += t;"),
@@ -195,7 +196,7 @@ GW_MUTANTS = {
 def test_gw_mutant_is_caught(tmp_path, name):
     old, new = GW_MUTANTS[name]
     src = open(oracle.SOURCE).read()
-    assert src.count(old) >= 1, "mutation anchor not found: %s" % name
+    assert src.count(old) == 1, "mutation anchor not found or not unique: %s" % name
     mutated = src.replace(old, new, 1)
     cpath = tmp_path / ("mut_%s.c" % name)
     cpath.write_text(mutated)
