@@ -53,7 +53,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(workloads.BY_NAME))
-    ap.add_argument("--op", default="grad_input", choices=["grad_input", "grad_weight"],
+    ap.add_argument("--op", default="grad_input", choices=["grad_input", "grad_weight", "backward"],
                     help="the operation of the headline line (grad_weight: fp32 workloads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-others", action="store_true",
@@ -131,6 +131,17 @@ def time_workload(wl, steps, warmup, torch, gi, dev, op="grad_input"):
         def call():
             gi.grad_weight(tg, tx, stride=s.stride, padding=(s.pad_h, s.pad_w),
                            kernel_hw=(s.kH, s.kW), out=dw, stream=stream)
+    elif op == "backward":
+        # dx, dw and db in one library call (its main-kernel events bracket
+        # the last main kernel, grad_weight's).
+        tx = torch.from_numpy(workloads.make_forward_input(wl)).to(dev)
+        dw = torch.empty(s.weight_shape, dtype=torch.float32, device=dev)
+        db = torch.empty((s.Co,), dtype=torch.float32, device=dev)
+
+        def call():
+            gi.backward(tg, tx, tw, stride=s.stride, padding=(s.pad_h, s.pad_w),
+                        kernel_hw=(s.kH, s.kW), want_db=True, dx=out, dw=dw, db=db,
+                        stream=stream)
     else:
         def call():
             gi.grad_input(tg, tw, stride=s.stride, padding=(s.pad_h, s.pad_w),
@@ -174,7 +185,8 @@ def time_workload(wl, steps, warmup, torch, gi, dev, op="grad_input"):
         hev.destroy(ev)
     return dict(ms_per_step=total_ms / steps, kernel_ms=float(np.mean(kern_ms)),
                 kernel_ms_min=float(np.min(kern_ms)), wall_ms=(wall1 - wall0) * 1e3,
-                warmup_calls=n_warm, flops=s.eff_flops)
+                warmup_calls=n_warm,
+                flops=s.eff_flops * (2 if op == "backward" else 1))
 
 
 def cpu_baseline(wl, target_s):
@@ -216,30 +228,44 @@ def main():
     wl = workloads.BY_NAME[args.workload]
     s = wl.shape
     op = args.op
-    if op == "grad_weight" and wl.dtype != "f32":
-        print("grad_weight is fp32 only", file=sys.stderr)
+    if op != "grad_input" and wl.dtype != "f32":
+        print("%s is fp32 only" % op, file=sys.stderr)
         sys.exit(2)
 
     r = time_workload(wl, args.steps, args.warmup, torch, gi, dev, op)
     value = r["flops"] / (r["ms_per_step"] * 1e-3) / 1e12
     peak = PEAK_TFLOPS[wl.dtype]
+    params = gi.make_params(*s.as_tuple()[:10])
     if op == "grad_weight":
-        plan_desc = gi.grad_weight_plan(gi.make_params(*s.as_tuple()[:10]))
+        plan_desc = gi.grad_weight_plan(params)
+    elif op == "backward":
+        plan_desc = gi.plan(params, False) + " | " + gi.grad_weight_plan(params)
     else:
-        plan_desc = gi.plan(gi.make_params(*s.as_tuple()[:10]), wl.dtype == "bf16")
-    variant = profiling.plan_variant(plan_desc)
-    kernel = profiling.kernel_name(variant, wl.dtype)
-    achieved = r["flops"] / (r["kernel_ms"] * 1e-3) / 1e12
-    if op == "grad_weight":
-        # grad_out and x read once, dw written once (fp32).
-        alg_bytes = 4 * (s.N * s.Co * s.oH * s.oW + s.N * s.Ci * s.H * s.W +
-                         s.Co * s.Ci * s.kH * s.kW)
+        plan_desc = gi.plan(params, wl.dtype == "bf16")
+    if op == "backward":
+        # Several main kernels per call: the roofline is the whole call's.
+        kernel = "whole call (grad_input and grad_weight kernels, prologue, reduction)"
+        kernel_ms = r["ms_per_step"]
+        traffic = mfma = None
+        # grad_out, x and weight read once; dx, dw and db written once.
+        alg_bytes = 4 * (s.N * s.Co * s.oH * s.oW + 2 * s.N * s.Ci * s.H * s.W +
+                         2 * s.Co * s.Ci * s.kH * s.kW + s.Co)
     else:
-        alg_bytes = s.algorithmic_bytes(2 if wl.dtype == "bf16" else 4)
-    traffic = profiling.read_traffic(kernel, wl.name, plan_desc, variant, wl.dtype)
-    mfma = profiling.read_mfma(kernel, wl.name, plan_desc, variant, wl.dtype)
+        variant = profiling.plan_variant(plan_desc)
+        kernel = profiling.kernel_name(variant, wl.dtype)
+        kernel_ms = r["kernel_ms"]
+        if op == "grad_weight":
+            # grad_out and x read once, dw written once (fp32).
+            alg_bytes = 4 * (s.N * s.Co * s.oH * s.oW + s.N * s.Ci * s.H * s.W +
+                             s.Co * s.Ci * s.kH * s.kW)
+        else:
+            alg_bytes = s.algorithmic_bytes(2 if wl.dtype == "bf16" else 4)
+        traffic = profiling.read_traffic(kernel, wl.name, plan_desc, variant, wl.dtype)
+        mfma = profiling.read_mfma(kernel, wl.name, plan_desc, variant, wl.dtype)
+    achieved = r["flops"] / (kernel_ms * 1e-3) / 1e12
     line = {
-        "metric": METRIC if op == "grad_input" else METRIC.replace("grad_input", "grad_weight"),
+        "metric": METRIC if op == "grad_input" else METRIC.replace(
+            "grad_input", "grad_weight" if op == "grad_weight" else "backward (dx + dw + db)"),
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -252,7 +278,7 @@ def main():
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic (seeded PCG64: grad_out N(0,1), weight Kaiming-normal%s)"
-                % (", forward input N(0,1)" if op == "grad_weight" else ""),
+                % (", forward input N(0,1)" if op != "grad_input" else ""),
         "config": {"workload": wl.name, "op": op, "N": s.N, "Ci": s.Ci, "Co": s.Co, "H": s.H, "W": s.W,
                    "kH": s.kH, "kW": s.kW, "stride": s.stride, "pad_h": s.pad_h,
                    "pad_w": s.pad_w, "oH": s.oH, "oW": s.oW, "eff_gflop": s.eff_flops / 1e9,
@@ -262,15 +288,16 @@ def main():
                      "traffic": None if traffic is None else round(traffic["bytes"]),
                      "algorithmic_bytes": alg_bytes,
                      "hbm_gbs": None if traffic is None else
-                     round(traffic["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9, 1),
+                     round(traffic["bytes"] / (kernel_ms * 1e-3) / 1e9, 1),
                      "kernel": kernel,
-                     "kernel_ms": round(r["kernel_ms"], 5),
-                     "per_unit": "2*Ci*kH*kW*Co flops per output pixel (n,oh,ow)",
+                     "kernel_ms": round(kernel_ms, 5),
+                     "per_unit": "%d*Ci*kH*kW*Co flops per output pixel (n,oh,ow)"
+                                 % (4 if op == "backward" else 2),
                      "units_per_launch": s.N * s.oH * s.oW,
                      "mfma_counters": mfma},
         "frac_of_peak_whole_call": round(value / peak, 4),
     }
-    if not args.no_others:
+    if not args.no_others and op == "grad_input":
         others = {}
         for o in workloads.WORKLOADS:
             if o.name == wl.name:
@@ -312,7 +339,21 @@ def main():
                                rw["flops"] / (rw["kernel_ms"] * 1e-3) / 1e12
                                / PEAK_TFLOPS["f32"], 4),
                            "plan": pw}
-        line["next_rows"] = {"grad_weight": nxt}
+        # The whole backward pass of the layer in one call: dx + dw + db
+        # (flops of dx and dw; the bias sums ride on the grad_weight kernel).
+        bwd = {}
+        for o in workloads.WORKLOADS:
+            if o.dtype != "f32" or o.name == "tiny":
+                continue
+            rb = time_workload(o, 20, 3, torch, gi, dev, "backward")
+            vb = rb["flops"] / (rb["ms_per_step"] * 1e-3) / 1e12
+            bwd[o.name] = {"tflops": round(vb, 3), "ms_per_call": round(rb["ms_per_step"], 5),
+                           "frac_of_peak": round(vb / PEAK_TFLOPS["f32"], 4),
+                           "ms_dx_plus_dw_separately": round(
+                               others.get(o.name, {}).get("ms_per_call", r["ms_per_step"]
+                                                          if o.name == wl.name else float("nan"))
+                               + nxt[o.name]["ms_per_call"], 5)}
+        line["next_rows"] = {"grad_weight": nxt, "backward_dx_dw_db": bwd}
     if not args.no_cpu_baseline and op == "grad_input":
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     if args.calibration_copy_mib > 0:

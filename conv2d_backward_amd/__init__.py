@@ -17,7 +17,7 @@ import os
 
 __all__ = [
     "grad_input", "Conv2dGiParams", "Conv2dGiError", "LibraryNotBuilt", "load_library",
-    "make_params", "validate", "plan", "grad_weight", "grad_weight_plan", "set_variant", "set_halo_tile", "set_halo_split", "set_halo_fusion", "set_gw_variant", "set_gw_tile", "release_workspaces", "set_profile_events", "library_path", "exported_names",
+    "make_params", "validate", "plan", "grad_weight", "grad_weight_plan", "grad_bias", "backward", "set_variant", "set_halo_tile", "set_halo_split", "set_halo_fusion", "set_gw_variant", "set_gw_tile", "release_workspaces", "set_profile_events", "library_path", "exported_names",
     "OK", "EINVAL", "EUNSUPPORTED", "EHIP", "VARIANT_AUTO", "VARIANT_GENERIC", "VARIANT_HALO", "VARIANT_STEM",
 ]
 
@@ -79,6 +79,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.conv2d_gi_plan.restype = ctypes.c_int
     lib.conv2d_grad_weight.argtypes = [P, P, P, PP, P]
     lib.conv2d_grad_weight.restype = ctypes.c_int
+    lib.conv2d_backward.argtypes = [P, P, P, P, P, P, PP, P]
+    lib.conv2d_backward.restype = ctypes.c_int
+    lib.conv2d_grad_bias.argtypes = [P, P, PP, P]
+    lib.conv2d_grad_bias.restype = ctypes.c_int
     lib.conv2d_gw_plan.argtypes = [PP, ctypes.c_char_p, ctypes.c_size_t]
     lib.conv2d_gw_plan.restype = ctypes.c_int
     lib.conv2d_gi_set_halo_tile.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]
@@ -105,6 +109,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
 def exported_names():
     """Names of the C entry points the binding wraps."""
     return ["conv2d_grad_input", "conv2d_grad_input_bf16", "conv2d_grad_weight",
+            "conv2d_backward", "conv2d_grad_bias",
             "conv2d_gw_plan", "conv2d_gi_validate",
             "conv2d_gi_strerror", "conv2d_gi_last_hip_error", "conv2d_gi_set_variant",
             "conv2d_gi_plan", "conv2d_gi_set_halo_tile", "conv2d_gi_set_halo_split",
@@ -297,5 +302,98 @@ def grad_weight(grad_out, x, *, stride: int, padding, kernel_hw, out=None, strea
                                       ctypes.c_void_p(x.data_ptr()),
                                       ctypes.c_void_p(out.data_ptr()), ctypes.byref(p),
                                       ctypes.c_void_p(s.cuda_stream))
+    _check(code)
+    return out
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr() if t is not None else 0)
+
+
+def backward(grad_out, x=None, weight=None, *, stride: int, padding, kernel_hw=None,
+             want_dx=True, want_dw=True, want_db=False, dx=None, dw=None, db=None, stream=None):
+    """The backward pass of a conv2d layer in one library call.
+
+    Returns (dx, dw, db), each None when not asked for.  grad_out [N, Co, oH, oW],
+    x [N, Ci, H, W] (needed for dw, and for the input size), weight [Co, Ci, kH,
+    kW] (needed for dx): float32, contiguous, on one ROCm device.  kernel_hw
+    defaults to the weight's.  dx / dw / db: optional output tensors to write.
+    Asynchronous on `stream` (default: the device's current stream).
+    """
+    import torch
+
+    if isinstance(padding, int):
+        padding = (padding, padding)
+    pad_h, pad_w = (int(v) for v in padding)
+    if x is None:
+        raise ValueError("x (or a tensor of its shape) gives the input size")
+    if kernel_hw is None:
+        if weight is None:
+            raise ValueError("kernel_hw is needed without the weight")
+        kernel_hw = tuple(weight.shape[2:])
+    kH, kW = (int(v) for v in kernel_hw)
+    tens = [t for t in (grad_out, x, weight) if t is not None]
+    dev = grad_out.device
+    for t in tens:
+        if t.dim() != 4 or not t.is_cuda or t.device != dev:
+            raise ValueError("inputs must be 4-D tensors on one GPU device")
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("inputs must be contiguous float32")
+    N, Co, oH, oW = (int(v) for v in grad_out.shape)
+    Nx, Ci, H, W = (int(v) for v in x.shape)
+    if Nx != N:
+        raise ValueError("x has %d batch items, grad_out %d" % (Nx, N))
+    if want_dx and weight is None:
+        raise ValueError("dx needs the weight")
+    if weight is not None and tuple(weight.shape) != (Co, Ci, kH, kW):
+        raise ValueError("weight must be [Co, Ci, kH, kW] = %r" % ((Co, Ci, kH, kW),))
+    p = Conv2dGiParams(N, Ci, H, W, Co, kH, kW, int(stride), pad_h, pad_w, oH, oW)
+    lib = load_library()
+    _check(lib.conv2d_gi_validate(ctypes.byref(p)))
+
+    def out_tensor(t, want, shape, name):
+        if not want:
+            return None
+        if t is None:
+            return torch.empty(shape, dtype=torch.float32, device=dev)
+        if (t.dtype != torch.float32 or t.device != dev or not t.is_contiguous()
+                or tuple(t.shape) != tuple(shape)):
+            raise ValueError("%s must be a contiguous float32 %r tensor on %s" % (name, shape, dev))
+        return t
+
+    dx = out_tensor(dx, want_dx, (N, Ci, H, W), "dx")
+    dw = out_tensor(dw, want_dw, (Co, Ci, kH, kW), "dw")
+    db = out_tensor(db, want_db, (Co,), "db")
+    with torch.cuda.device(dev):
+        s = stream if stream is not None else torch.cuda.current_stream(dev)
+        code = lib.conv2d_backward(_ptr(grad_out), _ptr(x if want_dw else None),
+                                   _ptr(weight if want_dx else None), _ptr(dx), _ptr(dw),
+                                   _ptr(db), ctypes.byref(p), ctypes.c_void_p(s.cuda_stream))
+    _check(code)
+    return dx, dw, db
+
+
+def grad_bias(grad_out, *, out=None, stream=None):
+    """Bias gradient [Co] (fp32): grad_out [N, Co, oH, oW] summed per channel."""
+    import torch
+
+    if grad_out.dim() != 4 or not grad_out.is_cuda:
+        raise ValueError("grad_out must be a 4-D tensor on a GPU device")
+    if grad_out.dtype != torch.float32 or not grad_out.is_contiguous():
+        raise ValueError("grad_out must be contiguous float32")
+    N, Co, oH, oW = (int(v) for v in grad_out.shape)
+    # A 1x1 stride-1 geometry with the same output plane: only N, Co, oH, oW matter.
+    p = Conv2dGiParams(N, 1, oH, oW, Co, 1, 1, 1, 0, 0, oH, oW)
+    dev = grad_out.device
+    if out is None:
+        out = torch.empty((Co,), dtype=torch.float32, device=dev)
+    elif (out.dtype != torch.float32 or out.device != dev or not out.is_contiguous()
+          or tuple(out.shape) != (Co,)):
+        raise ValueError("out must be a contiguous float32 [Co] tensor on %s" % dev)
+    lib = load_library()
+    with torch.cuda.device(dev):
+        s = stream if stream is not None else torch.cuda.current_stream(dev)
+        code = lib.conv2d_grad_bias(_ptr(grad_out), _ptr(out), ctypes.byref(p),
+                                    ctypes.c_void_p(s.cuda_stream))
     _check(code)
     return out

@@ -884,7 +884,7 @@ int odd_quads(int64_t n) {   // smallest multiple of 4 >= n whose quarter is odd
     return (int)v;
 }
 
-bool plan_gwd(const conv2d_gi_params &p, GwdPlan &out) {
+bool plan_gwd(const conv2d_gi_params &p, GwdPlan &out, bool bias = false) {
     const int64_t lim = 0x7fff0000LL;
     if ((int64_t)p.N * p.Co * p.oH * p.oW * 4 > lim) return false;
     if ((int64_t)p.N * p.Ci * p.H * p.W * 4 > lim) return false;
@@ -1021,7 +1021,9 @@ bool plan_gwd(const conv2d_gi_params &p, GwdPlan &out) {
     a.m_w = div_magic(p.W);
     out.args = a;
     out.cfg = cfg;
-    out.ws_bytes = (size_t)((int64_t)a.slices * total * 4);
+    out.args.bias = bias ? 1 : 0;
+    out.args.part_stride = (int)(total + (bias ? p.Co : 0));
+    out.ws_bytes = (size_t)((int64_t)a.slices * out.args.part_stride * 4);
     return true;
 }
 
@@ -1119,19 +1121,20 @@ std::string describe(const Plan &plan, bool bf16) {
     return s;
 }
 
-int run_gw(const float *grad_out, const float *x, float *dw, const conv2d_gi_params *p,
-           hipStream_t stream) {
-    int rc = validate(p);
-    if (rc != CONV2D_GI_OK) return rc;
-    const int64_t n_x = (int64_t)p->N * p->Ci * p->H * p->W;
-    const int64_t n_g = (int64_t)p->N * p->Co * p->oH * p->oW;
-    const int64_t n_w = (int64_t)p->Co * p->Ci * p->kH * p->kW;
-    if ((has_elems(n_w) && !dw) || (has_elems(n_g) && !grad_out) || (has_elems(n_x) && !x))
-        return CONV2D_GI_EINVAL;
-    if (n_w == 0) return CONV2D_GI_OK;
+// Scratch floats of the bias gradient alone (per-channel partial sums).
+size_t bias_ws_bytes(const conv2d_gi_params &p) {
+    return (size_t)gi::channel_sum_blocks(p.N, p.Co, p.oH * p.oW) * p.Co * 4;
+}
+
+// grad_weight into dw and, when db is not null, the bias gradient into db:
+// summed by the 16-byte-load kernel from the grad_out values it reads, else
+// (the 4-byte-load kernel) by a separate per-channel pass.  Arguments are
+// validated by the caller.
+int run_gw_checked(const float *grad_out, const float *x, float *dw, float *db,
+                   const conv2d_gi_params *p, hipStream_t stream) {
     const int variant = g_gw_variant.load();
     GwdPlan dplan;
-    const bool use_d = variant != 1 && plan_gwd(*p, dplan);
+    const bool use_d = variant != 1 && plan_gwd(*p, dplan, db != nullptr);
     if (variant == 2 && !use_d) return CONV2D_GI_EUNSUPPORTED;
     GwPlan plan;
     if (!use_d && !plan_gw(*p, plan)) return CONV2D_GI_EUNSUPPORTED;
@@ -1140,7 +1143,9 @@ int run_gw(const float *grad_out, const float *x, float *dw, const conv2d_gi_par
     if (e != hipSuccess) return fail_hip(e);
     std::lock_guard<std::mutex> lock(g_ws_mu);
     void *ws = nullptr;
-    e = workspace_for(dev, stream, use_d ? dplan.ws_bytes : plan.ws_bytes, &ws);
+    size_t need = use_d ? dplan.ws_bytes : plan.ws_bytes;
+    if (!use_d && db) need = std::max(need, bias_ws_bytes(*p));
+    e = workspace_for(dev, stream, need, &ws);
     if (e != hipSuccess) return fail_hip(e);
     gi::KernelEvents ev;
     if (g_prof_begin && g_prof_end) ev = {g_prof_begin, g_prof_end};
@@ -1150,6 +1155,7 @@ int run_gw(const float *grad_out, const float *x, float *dw, const conv2d_gi_par
         d.grad_out = grad_out;
         d.part = (float *)ws;
         d.dw = dw;
+        d.db = db;
         e = gi::launch_gwd_f32(d, dplan.cfg, stream, ev);
         if (e != hipSuccess) return fail_hip(e);
         return CONV2D_GI_OK;
@@ -1161,6 +1167,59 @@ int run_gw(const float *grad_out, const float *x, float *dw, const conv2d_gi_par
     a.dw = dw;
     e = gi::launch_gw_f32(a, stream, ev);
     if (e != hipSuccess) return fail_hip(e);
+    if (db) {
+        e = gi::launch_channel_sum(grad_out, (float *)ws, db, p->N, p->Co, p->oH * p->oW, stream);
+        if (e != hipSuccess) return fail_hip(e);
+    }
+    return CONV2D_GI_OK;
+}
+
+int run_gw(const float *grad_out, const float *x, float *dw, const conv2d_gi_params *p,
+           hipStream_t stream) {
+    int rc = validate(p);
+    if (rc != CONV2D_GI_OK) return rc;
+    const int64_t n_x = (int64_t)p->N * p->Ci * p->H * p->W;
+    const int64_t n_g = (int64_t)p->N * p->Co * p->oH * p->oW;
+    const int64_t n_w = (int64_t)p->Co * p->Ci * p->kH * p->kW;
+    if ((has_elems(n_w) && !dw) || (has_elems(n_g) && !grad_out) || (has_elems(n_x) && !x))
+        return CONV2D_GI_EINVAL;
+    if (n_w == 0) return CONV2D_GI_OK;
+    return run_gw_checked(grad_out, x, dw, nullptr, p, stream);
+}
+
+// The bias gradient alone (arguments validated by the caller).
+int run_bias_checked(const float *grad_out, float *db, const conv2d_gi_params *p,
+                     hipStream_t stream) {
+    if (p->Co == 0) return CONV2D_GI_OK;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail_hip(e);
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    void *ws = nullptr;
+    e = workspace_for(dev, stream, bias_ws_bytes(*p), &ws);
+    if (e != hipSuccess) return fail_hip(e);
+    e = gi::launch_channel_sum(grad_out, (float *)ws, db, p->N, p->Co, p->oH * p->oW, stream);
+    if (e != hipSuccess) return fail_hip(e);
+    return CONV2D_GI_OK;
+}
+
+int run_backward(const float *grad_out, const float *x, const float *weight, float *dx,
+                 float *dw, float *db, const conv2d_gi_params *p, hipStream_t stream) {
+    int rc = validate(p);
+    if (rc != CONV2D_GI_OK) return rc;
+    const int64_t n_x = (int64_t)p->N * p->Ci * p->H * p->W;
+    const int64_t n_g = (int64_t)p->N * p->Co * p->oH * p->oW;
+    const int64_t n_w = (int64_t)p->Co * p->Ci * p->kH * p->kW;
+    // Every requested output needs grad_out; dx needs the weight, dw the input.
+    if ((dx || dw || db) && has_elems(n_g) && !grad_out) return CONV2D_GI_EINVAL;
+    if (dx && has_elems(n_w) && !weight) return CONV2D_GI_EINVAL;
+    if (dw && has_elems(n_x) && !x) return CONV2D_GI_EINVAL;
+    if (dx) {
+        rc = run<float>(grad_out, weight, dx, p, stream, false);
+        if (rc != CONV2D_GI_OK) return rc;
+    }
+    if (dw && n_w > 0) return run_gw_checked(grad_out, x, dw, db, p, stream);
+    if (db) return run_bias_checked(grad_out, db, p, stream);
     return CONV2D_GI_OK;
 }
 
@@ -1171,6 +1230,19 @@ extern "C" {
 int conv2d_grad_weight(const float *grad_out, const float *x, float *dw,
                        const conv2d_gi_params *p, hipStream_t stream) {
     return run_gw(grad_out, x, dw, p, stream);
+}
+
+int conv2d_backward(const float *grad_out, const float *x, const float *weight, float *dx,
+                    float *dw, float *db, const conv2d_gi_params *p, hipStream_t stream) {
+    return run_backward(grad_out, x, weight, dx, dw, db, p, stream);
+}
+
+int conv2d_grad_bias(const float *grad_out, float *db, const conv2d_gi_params *p,
+                     hipStream_t stream) {
+    int rc = validate(p);
+    if (rc != CONV2D_GI_OK) return rc;
+    if (!db && p->Co > 0) return CONV2D_GI_EINVAL;
+    return run_backward(grad_out, nullptr, nullptr, nullptr, nullptr, db, p, stream);
 }
 
 int conv2d_gw_plan(const conv2d_gi_params *p, char *buf, size_t len) {

@@ -58,8 +58,11 @@ struct GwdArgs {
     const float *grad_out;   // [N, Co, oH, oW]
     float *part;             // [slices][Co][Ci][kH][kW] partial sums
     float *dw;               // [Co][Ci][kH][kW]
+    float *db;               // [Co] bias gradient (with `bias`), else unused
     uint32_t x_bytes, g_bytes;
     int32_t N, Ci, H, W, Co, oH, oW, stride, pad_h, pad_w, kH, kW;
+    int32_t bias;            // 1: also the bias gradient from the grad_out values read
+    int32_t part_stride;     // floats per slice of part: Co*Ci*kH*kW (+ Co with the bias)
     int32_t flat;            // 1: flat pixel layout, 0: row-padded
     int32_t colmap;          // 0: tap-major, 1: flattened
     int32_t co_blocks, col_tiles;
@@ -98,5 +101,14 @@ int gwd_f32_blocks(int cfg);
 int gwd_f32_max_wgs(int cfg);
 size_t gwd_f32_lds_bytes(const GwdArgs &a);
 hipError_t launch_gwd_f32(const GwdArgs &a, int cfg, hipStream_t s, const KernelEvents &ev);
+// Sum over slices (deterministic order): part [slices][total] -> out0[e] for
+// e < n0, out1[e - n0] for the rest.
+hipError_t launch_gw_reduce(const float *part, float *out0, float *out1, int n0, int total,
+                            int slices, hipStream_t s);
+// Bias gradient alone: per-channel sums of grad_out [N, Co, plane] into
+// part [channel_sum_blocks(...)][Co] (scratch), then db [Co].
+int channel_sum_blocks(int N, int Co, int plane);
+hipError_t launch_channel_sum(const float *g, float *part, float *db, int N, int Co, int plane,
+                              hipStream_t s);
 
 }  // namespace gi

@@ -34,6 +34,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "gw_common.h"
 
 namespace gi {
@@ -206,13 +208,16 @@ __global__ __launch_bounds__(256) void gi_gw_f32(const GwArgs A) {
     }
 }
 
-// dw[e] = sum of part[s][e] over the slices.  A work-group takes 64
-// elements; its four waves sum the slices s = w, w+4, w+8, ... in order
-// (eight loads in flight per lane), then wave 0 adds the four sums in wave
-// order: a fixed order, so the result does not depend on scheduling.
+// out[e] = sum of part[s][e] over the slices (slice stride `total`); the
+// elements e >= n0 go to out1[e - n0] instead of out0[e] (the bias sums that
+// follow the weight sums).  A work-group takes 64 elements; its four waves
+// sum the slices s = w, w+4, w+8, ... in order (eight loads in flight per
+// lane), then wave 0 adds the four sums in wave order: a fixed order, so the
+// result does not depend on scheduling.
 __global__ __launch_bounds__(256) void gw_reduce_f32(const float *__restrict__ part,
-                                                     float *__restrict__ dw, int total,
-                                                     int slices) {
+                                                     float *__restrict__ out0,
+                                                     float *__restrict__ out1, int n0,
+                                                     int total, int slices) {
     __shared__ float red[4][64];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int e = blockIdx.x * 64 + lane;
@@ -230,7 +235,37 @@ __global__ __launch_bounds__(256) void gw_reduce_f32(const float *__restrict__ p
     }
     red[w][lane] = s;
     __syncthreads();
-    if (w == 0 && e < total) dw[e] = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+    if (w == 0 && e < total) {
+        const float v = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+        if (e < n0)
+            out0[e] = v;
+        else
+            out1[e - n0] = v;
+    }
+}
+
+// Per-channel sums of grad_out [N, Co, oH*oW] over images [b*ipb, (b+1)*ipb)
+// of each channel: work-group (co, b) writes part[b][co].  Threads stride
+// over the pixels of each image in turn; the 256 sums are then added in a
+// fixed tree order.
+__global__ __launch_bounds__(256) void gw_channel_sum_f32(const float *__restrict__ g,
+                                                          float *__restrict__ part, int N,
+                                                          int Co, int plane, int ipb) {
+    __shared__ float red[256];
+    const int co = blockIdx.x, b = blockIdx.y;
+    const int n1 = min(N, (b + 1) * ipb);
+    float s = 0.f;
+    for (int n = b * ipb; n < n1; ++n) {
+        const float *gp = g + ((size_t)n * Co + co) * plane;
+        for (int p = threadIdx.x; p < plane; p += 256) s += gp[p];
+    }
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (int h = 128; h > 0; h >>= 1) {
+        if ((int)threadIdx.x < h) red[threadIdx.x] += red[threadIdx.x + h];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) part[(size_t)b * Co + co] = red[0];
 }
 
 // ---------------------------------------------------------------------------
@@ -384,6 +419,9 @@ __global__ __launch_bounds__(kGwdThreads) void gi_gwd_f32(const GwdArgs A) {
     v4f acc[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[b] = v4f{0.f, 0.f, 0.f, 0.f};
+    // Sum of the grad_out values this lane feeds to the MFMAs (padding and
+    // past-the-end pixels as zeros): the bias gradient's partial sum.
+    float bsum = 0.f;
 
     // Fragments of one K block: A at stp + ab + ua, B of block b at
     // stp + cbg[b] + ub.
@@ -417,6 +455,9 @@ __global__ __launch_bounds__(kGwdThreads) void gi_gwd_f32(const GwdArgs A) {
 #pragma unroll
                 for (int kw = 0; kw < NKW; ++kw)
                     am[kw][j] = (uint32_t)(ow + kw - A.pad_w) < (uint32_t)A.W ? F.a[j] : 0.f;
+                // The centre column (kw == pad_w, as oW == W) masks only the
+                // pixels past the group's end.
+                bsum += am[(NKW - 1) / 2][j];
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j)
@@ -426,11 +467,13 @@ __global__ __launch_bounds__(kGwdThreads) void gi_gwd_f32(const GwdArgs A) {
                                                                   0, 0, 0);
         } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 4; ++j) {
+                bsum += F.a[j];
 #pragma unroll
                 for (int b = 0; b < NB; ++b)
                     acc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(F.a[j], F.b[b][j], acc[b], 0, 0,
                                                                   0);
+            }
         }
     };
 
@@ -502,8 +545,16 @@ __global__ __launch_bounds__(kGwdThreads) void gi_gwd_f32(const GwdArgs A) {
         __syncthreads();
     }
 
-    // Partial sums: D[4g + r][i] of block b -> part[slice][co][ci][kh][kw].
-    float *pout = A.part + (size_t)slice * A.Co * A.Ci * kHW;
+    // Partial sums: D[4g + r][i] of block b -> part[slice][co][ci][kh][kw];
+    // with the bias, the first column tile adds part[slice][Co*Ci*kH*kW + co]
+    // (lane groups g = 0..3 summed in that order).
+    float *pout = A.part + (size_t)slice * A.part_stride;
+    if (A.bias && ct == 0) {
+        float t = bsum + __shfl_xor(bsum, 16);
+        t = t + __shfl_xor(t, 32);
+        const int co = co0 + 16 * wave + i;
+        if (g == 0 && co < A.Co) pout[(size_t)A.Co * A.Ci * kHW + co] = t;
+    }
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
         int ci, kh, kw;
@@ -532,10 +583,29 @@ __global__ __launch_bounds__(kGwdThreads) void gi_gwd_f32(const GwdArgs A) {
 
 }  // namespace
 
-hipError_t launch_gw_reduce(const float *part, float *dw, int total, int slices, hipStream_t s) {
+hipError_t launch_gw_reduce(const float *part, float *out0, float *out1, int n0, int total,
+                            int slices, hipStream_t s) {
     hipExtLaunchKernelGGL(gw_reduce_f32, dim3((unsigned)((total + 63) / 64)), dim3(256), 0, s,
-                          nullptr, nullptr, 0, part, dw, total, slices);
+                          nullptr, nullptr, 0, part, out0, out1, n0, total, slices);
     return hipGetLastError();
+}
+
+int channel_sum_blocks(int N, int Co, int plane) {
+    // About 16K floats per work-group, at least one block.
+    (void)Co;
+    const int ipb = std::max(1, 16384 / std::max(1, plane));
+    return std::max(1, (N + ipb - 1) / ipb);
+}
+
+hipError_t launch_channel_sum(const float *g, float *part, float *db, int N, int Co, int plane,
+                              hipStream_t s) {
+    const int nblk = channel_sum_blocks(N, Co, plane);
+    const int ipb = std::max(1, (N + nblk - 1) / nblk);
+    hipExtLaunchKernelGGL(gw_channel_sum_f32, dim3((unsigned)Co, (unsigned)nblk), dim3(256), 0, s,
+                          nullptr, nullptr, 0, g, part, N, Co, plane, ipb);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_gw_reduce(part, db, nullptr, Co, Co, nblk, s);
 }
 
 int gw_f32_max_taps() { return kGwMaxTaps; }
@@ -582,7 +652,8 @@ hipError_t launch_gw_f32(const GwArgs &a, hipStream_t s, const KernelEvents &ev)
                               ev.stop, 0, a);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    return launch_gw_reduce(a.part, a.dw, a.Co * a.Ci * a.kH * a.kW, a.slices, s);
+    const int total = a.Co * a.Ci * a.kH * a.kW;
+    return launch_gw_reduce(a.part, a.dw, nullptr, total, total, a.slices, s);
 }
 
 // Instantiations of gi_gwd_f32: (NB, KW, S, FLAT).
@@ -640,7 +711,8 @@ hipError_t launch_gwd_f32(const GwdArgs &a, int cfg, hipStream_t s, const Kernel
         default: e = go(gi_gwd_f32<8, 0, 0, false>); break;
     }
     if (e != hipSuccess) return e;
-    return launch_gw_reduce(a.part, a.dw, a.Co * a.Ci * a.kH * a.kW, a.slices, s);
+    const int total = a.Co * a.Ci * a.kH * a.kW;
+    return launch_gw_reduce(a.part, a.dw, a.db, total, a.part_stride, a.slices, s);
 }
 
 }  // namespace gi

@@ -202,6 +202,38 @@ CONV2D_GI_API int conv2d_grad_weight(const float *grad_out, const float *x, floa
                                      const conv2d_gi_params *p, hipStream_t stream);
 
 /*
+ * The whole backward pass of a convolution layer in one call, after the
+ * doppler conv2d_backward.js wrapper (its computeGradInput and
+ * computeGradWeight options become "output pointer not NULL") with the
+ * per-channel bias gradient of bias_add_backward.wgsl beside them:
+ *
+ *   dx = conv2d_grad_input(grad_out, weight)     (when dx is not NULL)
+ *   dw = conv2d_grad_weight(grad_out, x)         (when dw is not NULL)
+ *   db[co] = sum over n, oh, ow of grad_out[n,co,oh,ow]   (when db is not NULL)
+ *
+ * Same shapes, layouts and validation as the single calls; db is device
+ * [Co] fp32.  weight may be NULL when dx is, x when dw is.  With dw, the
+ * bias sums come from the grad_out values the grad_weight kernel already
+ * reads (no second pass over grad_out where the 16-byte-load kernel runs);
+ * without dw a per-channel reduction computes them.  All sums are in a fixed
+ * order (deterministic).  Every output is overwritten.  Returns the first
+ * failing step's status; the steps before it have been enqueued.
+ */
+CONV2D_GI_API int conv2d_backward(const float *grad_out, const float *x, const float *weight,
+                                  float *dx, float *dw, float *db, const conv2d_gi_params *p,
+                                  hipStream_t stream);
+
+/*
+ * The bias gradient alone: db[co] = sum over n, oh, ow of grad_out[n,co,oh,ow]
+ * (bias_add_backward.wgsl's sum over the positions the bias was added to).
+ * grad_out: device [N, Co, oH, oW] fp32; db: device [Co] fp32, overwritten
+ * (zeros for an empty batch).  p is validated as for the other calls.
+ * Returns CONV2D_GI_OK, CONV2D_GI_EINVAL or CONV2D_GI_EHIP.
+ */
+CONV2D_GI_API int conv2d_grad_bias(const float *grad_out, float *db, const conv2d_gi_params *p,
+                                   hipStream_t stream);
+
+/*
  * Host-only: describe the launch conv2d_grad_weight would make for this shape,
  * as text written into buf (NUL-terminated, truncated to len).
  */
