@@ -53,7 +53,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(workloads.BY_NAME))
-    ap.add_argument("--op", default="grad_input", choices=["grad_input", "grad_weight", "backward"],
+    ap.add_argument("--op", default="grad_input",
+                    choices=["grad_input", "grad_weight", "backward", "forward"],
                     help="the operation of the headline line (grad_weight: fp32 workloads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-others", action="store_true",
@@ -131,6 +132,13 @@ def time_workload(wl, steps, warmup, torch, gi, dev, op="grad_input"):
         def call():
             gi.grad_weight(tg, tx, stride=s.stride, padding=(s.pad_h, s.pad_w),
                            kernel_hw=(s.kH, s.kW), out=dw, stream=stream)
+    elif op == "forward":
+        tx = torch.from_numpy(workloads.make_forward_input(wl)).to(dev)
+        y = torch.empty(s.grad_out_shape, dtype=torch.float32, device=dev)
+
+        def call():
+            gi.forward(tx, tw, stride=s.stride, padding=(s.pad_h, s.pad_w), out=y,
+                       stream=stream)
     elif op == "backward":
         # dx, dw and db in one library call (its main-kernel events bracket
         # the last main kernel, grad_weight's).
@@ -238,6 +246,8 @@ def main():
     params = gi.make_params(*s.as_tuple()[:10])
     if op == "grad_weight":
         plan_desc = gi.grad_weight_plan(params)
+    elif op == "forward":
+        plan_desc = gi.forward_plan(params)
     elif op == "backward":
         plan_desc = gi.plan(params, False) + " | " + gi.grad_weight_plan(params)
     else:
@@ -265,7 +275,8 @@ def main():
     achieved = r["flops"] / (kernel_ms * 1e-3) / 1e12
     line = {
         "metric": METRIC if op == "grad_input" else METRIC.replace(
-            "grad_input", "grad_weight" if op == "grad_weight" else "backward (dx + dw + db)"),
+            "grad_input", {"grad_weight": "grad_weight", "forward": "forward",
+                           "backward": "backward (dx + dw + db)"}[op]),
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -353,7 +364,18 @@ def main():
                                others.get(o.name, {}).get("ms_per_call", r["ms_per_step"]
                                                           if o.name == wl.name else float("nan"))
                                + nxt[o.name]["ms_per_call"], 5)}
-        line["next_rows"] = {"grad_weight": nxt, "backward_dx_dw_db": bwd}
+        # The forward convolution of the same layer.
+        fwd = {}
+        for o in workloads.WORKLOADS:
+            if o.dtype != "f32" or o.name == "tiny":
+                continue
+            rf = time_workload(o, 20, 3, torch, gi, dev, "forward")
+            vf = rf["flops"] / (rf["ms_per_step"] * 1e-3) / 1e12
+            fwd[o.name] = {"tflops": round(vf, 3), "ms_per_call": round(rf["ms_per_step"], 5),
+                           "kernel_ms": round(rf["kernel_ms"], 5),
+                           "frac_of_peak": round(vf / PEAK_TFLOPS["f32"], 4),
+                           "plan": gi.forward_plan(gi.make_params(*o.shape.as_tuple()[:10]))}
+        line["next_rows"] = {"grad_weight": nxt, "backward_dx_dw_db": bwd, "forward": fwd}
     if not args.no_cpu_baseline and op == "grad_input":
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     if args.calibration_copy_mib > 0:

@@ -17,7 +17,7 @@ import os
 
 __all__ = [
     "grad_input", "Conv2dGiParams", "Conv2dGiError", "LibraryNotBuilt", "load_library",
-    "make_params", "validate", "plan", "grad_weight", "grad_weight_plan", "grad_bias", "backward", "set_variant", "set_halo_tile", "set_halo_split", "set_halo_fusion", "set_gw_variant", "set_gw_tile", "release_workspaces", "set_profile_events", "library_path", "exported_names",
+    "make_params", "validate", "plan", "grad_weight", "grad_weight_plan", "grad_bias", "backward", "forward", "forward_plan", "set_fwd_variant", "set_variant", "set_halo_tile", "set_halo_split", "set_halo_fusion", "set_gw_variant", "set_gw_tile", "release_workspaces", "set_profile_events", "library_path", "exported_names",
     "OK", "EINVAL", "EUNSUPPORTED", "EHIP", "VARIANT_AUTO", "VARIANT_GENERIC", "VARIANT_HALO", "VARIANT_STEM",
 ]
 
@@ -81,6 +81,12 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.conv2d_grad_weight.restype = ctypes.c_int
     lib.conv2d_backward.argtypes = [P, P, P, P, P, P, PP, P]
     lib.conv2d_backward.restype = ctypes.c_int
+    lib.conv2d_forward.argtypes = [P, P, P, PP, P]
+    lib.conv2d_forward.restype = ctypes.c_int
+    lib.conv2d_fwd_plan.argtypes = [PP, ctypes.c_char_p, ctypes.c_size_t]
+    lib.conv2d_fwd_plan.restype = ctypes.c_int
+    lib.conv2d_fwd_set_variant.argtypes = [ctypes.c_int]
+    lib.conv2d_fwd_set_variant.restype = ctypes.c_int
     lib.conv2d_grad_bias.argtypes = [P, P, PP, P]
     lib.conv2d_grad_bias.restype = ctypes.c_int
     lib.conv2d_gw_plan.argtypes = [PP, ctypes.c_char_p, ctypes.c_size_t]
@@ -109,7 +115,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
 def exported_names():
     """Names of the C entry points the binding wraps."""
     return ["conv2d_grad_input", "conv2d_grad_input_bf16", "conv2d_grad_weight",
-            "conv2d_backward", "conv2d_grad_bias",
+            "conv2d_backward", "conv2d_grad_bias", "conv2d_forward", "conv2d_fwd_plan",
+            "conv2d_fwd_set_variant",
             "conv2d_gw_plan", "conv2d_gi_validate",
             "conv2d_gi_strerror", "conv2d_gi_last_hip_error", "conv2d_gi_set_variant",
             "conv2d_gi_plan", "conv2d_gi_set_halo_tile", "conv2d_gi_set_halo_split",
@@ -395,5 +402,55 @@ def grad_bias(grad_out, *, out=None, stream=None):
         s = stream if stream is not None else torch.cuda.current_stream(dev)
         code = lib.conv2d_grad_bias(_ptr(grad_out), _ptr(out), ctypes.byref(p),
                                     ctypes.c_void_p(s.cuda_stream))
+    _check(code)
+    return out
+
+
+def forward_plan(p: Conv2dGiParams) -> str:
+    """Description of the launches conv2d_forward would make for shape p."""
+    buf = ctypes.create_string_buffer(1024)
+    _check(load_library().conv2d_fwd_plan(ctypes.byref(p), buf, len(buf)))
+    return buf.value.decode()
+
+
+def set_fwd_variant(mode: int = 0):
+    """Force the forward onto the grad_input kernels (1, stride 1 only) or the
+    generic forward kernel (2) for later calls (test hook); set_fwd_variant()
+    restores the planner."""
+    _check(load_library().conv2d_fwd_set_variant(int(mode)))
+
+
+def forward(x, weight, *, stride: int, padding, out=None, stream=None):
+    """Forward conv2d y [N, Co, oH, oW] (fp32) on the GPU: x [N, Ci, H, W] and
+    weight [Co, Ci, kH, kW], float32, contiguous, on one ROCm device;
+    padding: int or (pad_h, pad_w).  Asynchronous on `stream`."""
+    import torch
+
+    if isinstance(padding, int):
+        padding = (padding, padding)
+    pad_h, pad_w = (int(v) for v in padding)
+    for t in (x, weight):
+        if t.dim() != 4 or not t.is_cuda or t.device != x.device:
+            raise ValueError("x and weight must be 4-D tensors on one GPU device")
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("x and weight must be contiguous float32")
+    N, Ci, H, W = (int(v) for v in x.shape)
+    Co, Ci_w, kH, kW = (int(v) for v in weight.shape)
+    if Ci_w != Ci:
+        raise ValueError("weight has %d input channels, x has %d" % (Ci_w, Ci))
+    p = make_params(N, Ci, H, W, Co, kH, kW, int(stride), pad_h, pad_w)
+    lib = load_library()
+    _check(lib.conv2d_gi_validate(ctypes.byref(p)))
+    dev = x.device
+    if out is None:
+        out = torch.empty((N, Co, p.oH, p.oW), dtype=torch.float32, device=dev)
+    elif (out.dtype != torch.float32 or out.device != dev or not out.is_contiguous()
+          or tuple(out.shape) != (N, Co, p.oH, p.oW)):
+        raise ValueError("out must be a contiguous float32 %r tensor on %s"
+                         % ((N, Co, p.oH, p.oW), dev))
+    with torch.cuda.device(dev):
+        s = stream if stream is not None else torch.cuda.current_stream(dev)
+        code = lib.conv2d_forward(_ptr(x), _ptr(weight), _ptr(out), ctypes.byref(p),
+                                  ctypes.c_void_p(s.cuda_stream))
     _check(code)
     return out

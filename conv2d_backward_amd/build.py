@@ -28,6 +28,7 @@ SOURCES = [
     "kernels_halo_bf16.hip",
     "kernels_stem_f32.hip",
     "kernels_gw_f32.hip",
+    "kernels_fwd_f32.hip",
 ]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", "-Werror",

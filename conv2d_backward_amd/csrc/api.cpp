@@ -12,12 +12,14 @@
 #include <map>
 #include <mutex>
 #include <string>
+#include <tuple>
 #include <utility>
 #include <vector>
 
 #include "conv2d_grad_input.h"
 #include "gi_common.h"
 #include "gi_launch.h"
+#include "fwd_common.h"
 #include "gw_common.h"
 
 namespace {
@@ -31,6 +33,7 @@ std::atomic<int> g_tile_nb{0}, g_tile_tr{0}, g_tile_tc{0}, g_tile_stages{0};
 std::atomic<int> g_halo_split{0};
 std::atomic<int> g_halo_fusion{0};  // 0 planner, 1 phase at a time, 2 fused
 std::atomic<int> g_gw_variant{0};   // grad_weight: 0 planner, 1 4-byte loads, 2 16-byte loads
+std::atomic<int> g_fwd_variant{0};  // forward: 0 planner, 1 grad_input kernels, 2 generic
 std::atomic<int> g_gw_rows{0};      // grad_weight, 16-byte loads: forced rows per group (0 planner)
 std::atomic<int> g_gw_stages{0};    // ... and LDS stages (0 planner)
 std::atomic<int> g_gw_slices{0};    // ... and most slices (0 planner)
@@ -46,10 +49,13 @@ struct Workspace {
     size_t bytes = 0;
 };
 std::mutex g_ws_mu;
-std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+// Scratch per (device, stream, slot): slot 0 serves every kernel's own
+// scratch, slot 1 a reordered operand that a later call in the same entry
+// point reads (the forward's reversed weight).
+std::map<std::tuple<int, hipStream_t, int>, Workspace> g_ws;
 
-hipError_t workspace_for(int dev, hipStream_t s, size_t bytes, void **out) {
-    Workspace &w = g_ws[{dev, s}];
+hipError_t workspace_for(int dev, hipStream_t s, size_t bytes, void **out, int slot = 0) {
+    Workspace &w = g_ws[std::make_tuple(dev, s, slot)];
     if (w.bytes < bytes) {
         if (w.ptr) {
             hipError_t e = hipFreeAsync(w.ptr, s);
@@ -1223,9 +1229,134 @@ int run_backward(const float *grad_out, const float *x, const float *weight, flo
     return CONV2D_GI_OK;
 }
 
+// The forward convolution.  Stride 1 with pad <= k-1 runs on the grad_input
+// path: y = sum over ci, kh, kw of x[oh-ph+kh, ow-pw+kw] * w[co,ci,kh,kw] is,
+// with kh' = kH-1-kh, the grad_input sum of grad_out := x (Ci channels) and
+// weight wf[ci][co][kh'][kw'] = w[co][ci][kH-1-kh'][kW-1-kw'] under the pad
+// kH-1-ph (and kW-1-pw): an input-side problem with Ci' = Co, H' = oH,
+// Co' = Ci, oH' = H.  Other shapes run on the generic forward kernel.
+bool fwd_via_grad_input(const conv2d_gi_params &p) {
+    return g_fwd_variant.load() != 2 && p.stride == 1 && p.pad_h <= p.kH - 1 &&
+           p.pad_w <= p.kW - 1;
+}
+
+conv2d_gi_params fwd_as_grad_input(const conv2d_gi_params &p) {
+    conv2d_gi_params q{};
+    q.N = p.N;
+    q.Ci = p.Co;
+    q.H = p.oH;
+    q.W = p.oW;
+    q.Co = p.Ci;
+    q.kH = p.kH;
+    q.kW = p.kW;
+    q.stride = 1;
+    q.pad_h = p.kH - 1 - p.pad_h;
+    q.pad_w = p.kW - 1 - p.pad_w;
+    q.oH = p.H;
+    q.oW = p.W;
+    return q;
+}
+
+int run_forward(const float *x, const float *w, float *y, const conv2d_gi_params *p,
+                hipStream_t stream) {
+    int rc = validate(p);
+    if (rc != CONV2D_GI_OK) return rc;
+    const int64_t n_x = (int64_t)p->N * p->Ci * p->H * p->W;
+    const int64_t n_y = (int64_t)p->N * p->Co * p->oH * p->oW;
+    const int64_t n_w = (int64_t)p->Co * p->Ci * p->kH * p->kW;
+    if ((has_elems(n_y) && !y) || (has_elems(n_x) && !x) || (has_elems(n_w) && !w))
+        return CONV2D_GI_EINVAL;
+    if (n_y == 0) return CONV2D_GI_OK;
+    if (g_fwd_variant.load() == 1 && !fwd_via_grad_input(*p)) return CONV2D_GI_EUNSUPPORTED;
+    const int kHW = p->kH * p->kW;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail_hip(e);
+    if (fwd_via_grad_input(*p)) {
+        const conv2d_gi_params q = fwd_as_grad_input(*p);
+        rc = validate(&q);
+        if (rc != CONV2D_GI_OK) return rc;
+        void *wf = nullptr;
+        {
+            std::lock_guard<std::mutex> lock(g_ws_mu);
+            e = workspace_for(dev, stream, (size_t)std::max<int64_t>(n_w, 1) * 4, &wf, 1);
+            if (e != hipSuccess) return fail_hip(e);
+            if (n_w > 0) {
+                e = gi::launch_fwd_weight_flip_f32(w, (float *)wf, p->Co, p->Ci, kHW, stream);
+                if (e != hipSuccess) return fail_hip(e);
+            }
+        }
+        return run<float>(x, (const float *)wf, y, &q, stream, false);
+    }
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    void *ws = nullptr;
+    e = workspace_for(dev, stream, (size_t)std::max<int64_t>(n_w, 1) * 4, &ws);
+    if (e != hipSuccess) return fail_hip(e);
+    gi::FwdArgs a{};
+    a.x = x;
+    a.wt = (const float *)ws;
+    a.y = y;
+    a.N = p->N;
+    a.Ci = p->Ci;
+    a.H = p->H;
+    a.W = p->W;
+    a.Co = p->Co;
+    a.kH = p->kH;
+    a.kW = p->kW;
+    a.stride = p->stride;
+    a.pad_h = p->pad_h;
+    a.pad_w = p->pad_w;
+    a.oH = p->oH;
+    a.oW = p->oW;
+    if (n_w > 0) {
+        e = gi::fwd_flat_k(a)
+                ? gi::launch_fwd_weight_k_co_f32(w, (float *)ws, p->Co, p->Ci * kHW, stream)
+                : gi::launch_fwd_weight_tap_ci_co_f32(w, (float *)ws, p->Co, p->Ci, kHW, stream);
+        if (e != hipSuccess) return fail_hip(e);
+    }
+    gi::KernelEvents ev;
+    if (g_prof_begin && g_prof_end) ev = {g_prof_begin, g_prof_end};
+    e = gi::launch_fwd_generic_f32(a, stream, ev);
+    if (e != hipSuccess) return fail_hip(e);
+    return CONV2D_GI_OK;
+}
+
+std::string describe_forward(const conv2d_gi_params &p) {
+    if (fwd_via_grad_input(p)) {
+        const conv2d_gi_params q = fwd_as_grad_input(p);
+        return describe(make_plan(q, false), false) + " (forward as grad_input: weight "
+               "transposed and reversed)";
+    }
+    const int64_t npix = (int64_t)p.N * p.oH * p.oW;
+    return "variant=fwd dtype=f32 ws_bytes=" +
+           std::to_string((int64_t)p.Co * p.Ci * p.kH * p.kW * 4) + " launches=2 [tiles=" +
+           std::to_string((npix + gi::kFwdBN - 1) / gi::kFwdBN) + "x" +
+           std::to_string((p.Co + gi::kFwdBM - 1) / gi::kFwdBM) + "]";
+}
+
 }  // namespace
 
 extern "C" {
+
+int conv2d_forward(const float *x, const float *w, float *y, const conv2d_gi_params *p,
+                   hipStream_t stream) {
+    return run_forward(x, w, y, p, stream);
+}
+
+int conv2d_fwd_plan(const conv2d_gi_params *p, char *buf, size_t len) {
+    int rc = validate(p);
+    if (rc != CONV2D_GI_OK) return rc;
+    if (!buf || len == 0) return CONV2D_GI_EINVAL;
+    if (g_fwd_variant.load() == 1 && !fwd_via_grad_input(*p)) return CONV2D_GI_EUNSUPPORTED;
+    std::snprintf(buf, len, "%s", describe_forward(*p).c_str());
+    return CONV2D_GI_OK;
+}
+
+int conv2d_fwd_set_variant(int mode) {
+    if (mode < 0 || mode > 2) return CONV2D_GI_EINVAL;
+    g_fwd_variant = mode;
+    return CONV2D_GI_OK;
+}
 
 int conv2d_grad_weight(const float *grad_out, const float *x, float *dw,
                        const conv2d_gi_params *p, hipStream_t stream) {
@@ -1357,9 +1488,9 @@ int conv2d_gi_release_workspaces(void) {
     hipError_t first = hipSuccess;
     for (auto &kv : g_ws) {
         if (!kv.second.ptr) continue;
-        hipError_t e = hipSetDevice(kv.first.first);
-        if (e == hipSuccess) e = hipFreeAsync(kv.second.ptr, kv.first.second);
-        if (e == hipSuccess) e = hipStreamSynchronize(kv.first.second);
+        hipError_t e = hipSetDevice(std::get<0>(kv.first));
+        if (e == hipSuccess) e = hipFreeAsync(kv.second.ptr, std::get<1>(kv.first));
+        if (e == hipSuccess) e = hipStreamSynchronize(std::get<1>(kv.first));
         if (first == hipSuccess) first = e;
     }
     g_ws.clear();

@@ -1,0 +1,252 @@
+// kernels_fwd_f32.hip -- the forward convolution (fp32) for gfx950: weight
+// reorders and the generic implicit-GEMM kernel.  Stride-1 forwards run on
+// the grad_input kernels instead (a forward correlation with pad p is the
+// grad_input sum of the transposed, tap-reversed weight with pad k-1-p); the
+// generic kernel serves every stride.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fwd_common.h"
+
+namespace gi {
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+namespace {
+
+// wt[(tap*Ci + ci)*Co + co] = w[(co*Ci + ci)*kHW + tap]; one thread per
+// output element, writes coalesced.
+__global__ __launch_bounds__(256) void fwd_weight_tap_ci_co_f32(const float *__restrict__ w,
+                                                                float *__restrict__ wt, int Co,
+                                                                int Ci, int kHW, int64_t total) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * 256) {
+        const int64_t co = i % Co;
+        const int64_t ci = (i / Co) % Ci;
+        const int64_t tap = i / ((int64_t)Ci * Co);
+        wt[i] = w[(co * Ci + ci) * kHW + tap];
+    }
+}
+
+// wf[((ci*Co + co)*kHW) + t] = w[(co*Ci + ci)*kHW + kHW-1-t]: [Ci][Co][kH][kW]
+// with both kernel axes reversed.
+__global__ __launch_bounds__(256) void fwd_weight_flip_f32(const float *__restrict__ w,
+                                                           float *__restrict__ wf, int Co, int Ci,
+                                                           int kHW, int64_t total) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * 256) {
+        const int64_t t = i % kHW;
+        const int64_t co = (i / kHW) % Co;
+        const int64_t ci = i / ((int64_t)kHW * Co);
+        wf[i] = w[(co * Ci + ci) * kHW + (kHW - 1 - t)];
+    }
+}
+
+// wt[k*Co + co] = w[co*K + k] (K = Ci*kH*kW): the weight as [K][Co] with k in
+// the caller's (ci, kh, kw) order, for the flattened K axis.
+__global__ __launch_bounds__(256) void fwd_weight_k_co_f32(const float *__restrict__ w,
+                                                           float *__restrict__ wt, int Co, int K,
+                                                           int64_t total) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * 256) {
+        const int64_t co = i % Co;
+        const int64_t k = i / Co;
+        wt[i] = w[co * K + k];
+    }
+}
+
+int reorder_blocks(int64_t total) {
+    const int64_t b = (total + 255) / 256;
+    return (int)(b < 8192 ? (b > 0 ? b : 1) : 8192);
+}
+
+// Output row of 32x32 accumulator register r for lane `lane`.
+__device__ __forceinline__ int acc_row32(int r, int lane) {
+    return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+}
+
+// ---------------------------------------------------------------------------
+// Generic forward kernel: 256 threads, tile 64 co x 128 pixels, K step 16.
+// Waves form 2 x 2; each owns 32 co x 64 pixels = two V_MFMA_F32_32X32X2_F32
+// accumulators.  Global tiles are prefetched into registers one K step ahead
+// and double-buffered in LDS.  K order: FLATK = false, (tap, ci) with a K
+// step = one tap x 16 input channels (one bounds test per pixel and step);
+// FLATK = true, the caller's (ci, kh, kw) order (few input channels: no
+// padding of Ci to 16), each k's plane offset and tap read from an LDS table.
+// ---------------------------------------------------------------------------
+template <bool FLATK>
+__global__ __launch_bounds__(256) void gi_fwd_f32(const FwdArgs A) {
+    constexpr int BM = kFwdBM, BN = kFwdBN, BK = 16, NT = 256;
+    constexpr int LDA = BM + 32, LDB = BN + 32;   // row pads keep half-waves on distinct banks
+    constexpr int B_RPP = NT / BN, B_PT = BK / B_RPP;
+    constexpr int A_RPP = NT / BM, A_PT = BK / A_RPP;
+    __shared__ float As[2][BK][LDA];
+    __shared__ float Bs[2][BK][LDB];
+    __shared__ int2 ktab[FLATK ? kFwdMaxFlatK : 1];   // (ci*H*W + kh*W + kw, kh << 16 | kw)
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int pix0 = blockIdx.x * BN;
+    const int co0 = blockIdx.y * BM;
+    const int oHW = A.oH * A.oW;
+    const int npix = A.N * oHW;
+    const int HW = A.H * A.W;
+    const int kHW = A.kH * A.kW;
+    const int nci = (A.Ci + BK - 1) / BK;
+    const int K = A.Ci * kHW;
+    const int T = FLATK ? (K + BK - 1) / BK : kHW * nci;
+    if (FLATK) {
+        for (int k = tid; k < K; k += NT) {
+            const int ci = k / kHW, r = k - (k / kHW) * kHW;
+            const int kh = r / A.kW, kw = r - (r / A.kW) * A.kW;
+            ktab[k] = make_int2(ci * HW + kh * A.W + kw, (kh << 16) | kw);
+        }
+        __syncthreads();
+    }
+
+    // B gather assignment: one pixel column, rows kb0, kb0 + B_RPP, ...
+    const int pc = tid % BN, kb0 = tid / BN;
+    const int pix = pix0 + pc;
+    const bool pin = pix < npix;
+    int n = 0, oh = 0, ow = 0;
+    if (pin) {
+        n = pix / oHW;
+        const int rem = pix - n * oHW;
+        oh = rem / A.oW;
+        ow = rem - oh * A.oW;
+    }
+    const int ih0 = oh * A.stride - A.pad_h, iw0 = ow * A.stride - A.pad_w;
+    const float *ximg = A.x + (int64_t)n * A.Ci * HW;
+    // A load assignment: one co column, rows ka0, ka0 + A_RPP, ...
+    const int ac = tid % BM, ka0 = tid / BM;
+    const bool ain = co0 + ac < A.Co;
+
+    float ra[A_PT], rb[B_PT];
+    auto gload_flat = [&](int it) {
+        const int base = ih0 * A.W + iw0;
+#pragma unroll
+        for (int i = 0; i < B_PT; ++i) {
+            const int k = it * BK + kb0 + i * B_RPP;
+            float v = 0.f;
+            if (pin && k < K) {
+                const int2 e = ktab[k];
+                const int kh = e.y >> 16, kw = e.y & 0xffff;
+                if ((unsigned)(ih0 + kh) < (unsigned)A.H && (unsigned)(iw0 + kw) < (unsigned)A.W)
+                    v = ximg[e.x + base];
+            }
+            rb[i] = v;
+        }
+#pragma unroll
+        for (int i = 0; i < A_PT; ++i) {
+            const int k = it * BK + ka0 + i * A_RPP;
+            ra[i] = (ain && k < K) ? A.wt[(int64_t)k * A.Co + co0 + ac] : 0.f;
+        }
+    };
+    auto gload = [&](int it) {
+        if (FLATK) {
+            gload_flat(it);
+            return;
+        }
+        const int tap = it / nci;
+        const int ci0 = (it - tap * nci) * BK;
+        const int kh = tap / A.kW, kw = tap - (tap / A.kW) * A.kW;
+        const int ih = ih0 + kh, iw = iw0 + kw;
+        const bool v = pin && ih >= 0 && ih < A.H && iw >= 0 && iw < A.W;
+        const int off = v ? ih * A.W + iw : 0;
+#pragma unroll
+        for (int i = 0; i < B_PT; ++i) {
+            const int ci = ci0 + kb0 + i * B_RPP;
+            rb[i] = (v && ci < A.Ci) ? ximg[(int64_t)ci * HW + off] : 0.f;
+        }
+        const float *ws = A.wt + (int64_t)tap * A.Ci * A.Co + co0 + ac;
+#pragma unroll
+        for (int i = 0; i < A_PT; ++i) {
+            const int ci = ci0 + ka0 + i * A_RPP;
+            ra[i] = (ain && ci < A.Ci) ? ws[(int64_t)ci * A.Co] : 0.f;
+        }
+    };
+    auto sstore = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < A_PT; ++i) As[buf][ka0 + i * A_RPP][ac] = ra[i];
+#pragma unroll
+        for (int i = 0; i < B_PT; ++i) Bs[buf][kb0 + i * B_RPP][pc] = rb[i];
+    };
+
+    v16f acc0 = {}, acc1 = {};
+    const int wm = wave >> 1, wn = wave & 1;
+    const int kl = lane >> 5, ml = lane & 31;
+    if (T > 0) {
+        gload(0);
+        sstore(0);
+        __syncthreads();
+        for (int it = 0; it < T; ++it) {
+            const int cur = it & 1;
+            if (it + 1 < T) gload(it + 1);
+#pragma unroll
+            for (int kk = 0; kk < BK; kk += 2) {
+                const float af = As[cur][kk + kl][wm * 32 + ml];
+                const float b0 = Bs[cur][kk + kl][wn * 64 + ml];
+                const float b1 = Bs[cur][kk + kl][wn * 64 + 32 + ml];
+                acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(af, b0, acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(af, b1, acc1, 0, 0, 0);
+            }
+            if (it + 1 < T) sstore(cur ^ 1);
+            __syncthreads();
+        }
+    }
+    // Store: rows = output channels, column = this lane's pixel.
+    auto store = [&](const v16f &acc, int pcol) {
+        if (pcol >= npix) return;
+        const int nn = pcol / oHW;
+        const int rem = pcol - nn * oHW;
+        float *d = A.y + (int64_t)nn * A.Co * oHW + rem;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int co = co0 + wm * 32 + acc_row32(r, lane);
+            if (co < A.Co) d[(int64_t)co * oHW] = acc[r];
+        }
+    };
+    store(acc0, pix0 + wn * 64 + ml);
+    store(acc1, pix0 + wn * 64 + 32 + ml);
+}
+
+}  // namespace
+
+hipError_t launch_fwd_weight_tap_ci_co_f32(const float *w, float *wt, int Co, int Ci, int kHW,
+                                           hipStream_t s) {
+    const int64_t total = (int64_t)Co * Ci * kHW;
+    hipLaunchKernelGGL(fwd_weight_tap_ci_co_f32, dim3(reorder_blocks(total)), dim3(256), 0, s, w,
+                       wt, Co, Ci, kHW, total);
+    return hipGetLastError();
+}
+
+hipError_t launch_fwd_weight_flip_f32(const float *w, float *wf, int Co, int Ci, int kHW,
+                                      hipStream_t s) {
+    const int64_t total = (int64_t)Co * Ci * kHW;
+    hipLaunchKernelGGL(fwd_weight_flip_f32, dim3(reorder_blocks(total)), dim3(256), 0, s, w, wf,
+                       Co, Ci, kHW, total);
+    return hipGetLastError();
+}
+
+hipError_t launch_fwd_weight_k_co_f32(const float *w, float *wt, int Co, int K, hipStream_t s) {
+    const int64_t total = (int64_t)Co * K;
+    hipLaunchKernelGGL(fwd_weight_k_co_f32, dim3(reorder_blocks(total)), dim3(256), 0, s, w, wt,
+                       Co, K, total);
+    return hipGetLastError();
+}
+
+bool fwd_flat_k(const FwdArgs &a) {
+    return a.Ci < 16 && (int64_t)a.Ci * a.kH * a.kW <= kFwdMaxFlatK;
+}
+
+hipError_t launch_fwd_generic_f32(const FwdArgs &a, hipStream_t s, const KernelEvents &ev) {
+    const int64_t npix = (int64_t)a.N * a.oH * a.oW;
+    if (npix == 0 || a.Co == 0) return hipSuccess;
+    const dim3 grid((unsigned)((npix + kFwdBN - 1) / kFwdBN), (unsigned)((a.Co + kFwdBM - 1) / kFwdBM));
+    if (fwd_flat_k(a))
+        hipExtLaunchKernelGGL(gi_fwd_f32<true>, grid, dim3(256), 0, s, ev.start, ev.stop, 0, a);
+    else
+        hipExtLaunchKernelGGL(gi_fwd_f32<false>, grid, dim3(256), 0, s, ev.start, ev.stop, 0, a);
+    return hipGetLastError();
+}
+
+}  // namespace gi

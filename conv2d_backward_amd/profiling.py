@@ -47,6 +47,7 @@ KERNEL_SOURCES = {
     ("stem", "f32"): ["kernels_stem_f32.hip"],
     ("gw", "f32"): ["kernels_gw_f32.hip", "gw_common.h"],
     ("gwd", "f32"): ["kernels_gw_f32.hip", "gw_common.h"],
+    ("fwd", "f32"): ["kernels_fwd_f32.hip", "fwd_common.h"],
     ("generic", "f32"): ["kernels_generic.hip"],
     ("generic", "bf16"): ["kernels_generic.hip"],
 }

@@ -234,6 +234,41 @@ CONV2D_GI_API int conv2d_grad_bias(const float *grad_out, float *db, const conv2
                                    hipStream_t stream);
 
 /*
+ * The forward convolution (cross-correlation), the mapping the doppler direct
+ * grad_input kernel's comment states (output pixel oh reads input row
+ * oh*stride - pad + kh):
+ *
+ *   y[n,co,oh,ow] = sum over ci, kh, kw of
+ *                   x[n,ci,oh*stride-pad_h+kh, ow*stride-pad_w+kw] * w[co,ci,kh,kw]
+ *   with x = 0 outside [0,H) x [0,W).
+ *
+ * x: device [N, Ci, H, W] fp32; w: device [Co, Ci, kH, kW] fp32; y: device
+ * [N, Co, oH, oW] fp32, fully overwritten.  p: the same shape struct as the
+ * gradient calls, validated the same way.  Stride 1 (pad <= kernel size - 1)
+ * runs on the grad_input kernels with the weight transposed and its taps
+ * reversed into library scratch (a second per-stream buffer); other shapes
+ * on a generic implicit-GEMM kernel.  Enqueued on `stream`.  Returns
+ * CONV2D_GI_OK, CONV2D_GI_EINVAL, CONV2D_GI_EUNSUPPORTED (forced variant that
+ * does not apply) or CONV2D_GI_EHIP.
+ */
+CONV2D_GI_API int conv2d_forward(const float *x, const float *w, float *y,
+                                 const conv2d_gi_params *p, hipStream_t stream);
+
+/*
+ * Host-only: describe the launches conv2d_forward would make for this shape,
+ * as text written into buf (NUL-terminated, truncated to len).
+ */
+CONV2D_GI_API int conv2d_fwd_plan(const conv2d_gi_params *p, char *buf, size_t len);
+
+/*
+ * Test and diagnostic hook: which path later conv2d_forward calls in this
+ * process take: 1 the grad_input kernels (stride 1 only; other shapes return
+ * CONV2D_GI_EUNSUPPORTED), 2 the generic forward kernel, 0 restores the
+ * planner.  Returns CONV2D_GI_OK, or CONV2D_GI_EINVAL for other values.
+ */
+CONV2D_GI_API int conv2d_fwd_set_variant(int mode);
+
+/*
  * Host-only: describe the launch conv2d_grad_weight would make for this shape,
  * as text written into buf (NUL-terminated, truncated to len).
  */
