@@ -41,7 +41,8 @@ import workloads  # noqa: E402
 from conv2d_backward_amd import profiling  # noqa: E402
 
 METRIC = "effective TFLOP/s of conv2d grad_input per config; % of MFMA peak (1 GPU)"
-PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6}   # MI355X dense matrix-core peaks
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6, "f16": 2516.6}   # MI355X dense matrix-core peaks
+PLAN_KIND = {"f32": 0, "bf16": 1, "f16": 2}   # the dtype argument of the plan description
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "resnet_stage_3x3"
 WARMUP_SECONDS = 0.1   # untimed warm-up: at least this much GPU work
@@ -70,9 +71,10 @@ def parse():
 
 def device_inputs(wl, torch, dev):
     g, w = workloads.make_inputs(wl)
-    if wl.dtype == "bf16":
-        tg = torch.from_numpy(g.view(np.int16)).to(dev).view(torch.bfloat16)
-        tw = torch.from_numpy(w.view(np.int16)).to(dev).view(torch.bfloat16)
+    if wl.dtype in ("bf16", "f16"):
+        t16 = torch.bfloat16 if wl.dtype == "bf16" else torch.float16
+        tg = torch.from_numpy(g.view(np.int16)).to(dev).view(t16)
+        tw = torch.from_numpy(w.view(np.int16)).to(dev).view(t16)
     else:
         tg = torch.from_numpy(g).to(dev)
         tw = torch.from_numpy(w).to(dev)
@@ -205,6 +207,8 @@ def cpu_baseline(wl, target_s):
     g, w = workloads.make_inputs(wl)
     if wl.dtype == "bf16":
         g, w = workloads.bf16_to_f32(g), workloads.bf16_to_f32(w)
+    elif wl.dtype == "f16":
+        g, w = workloads.f16_to_f32(g), workloads.f16_to_f32(w)
     t = time.perf_counter()
     oracle.grad_input(g[:1], w, s.stride, (s.pad_h, s.pad_w), (s.H, s.W), with_abs=False)
     one = max(time.perf_counter() - t, 1e-4)
@@ -251,7 +255,7 @@ def main():
     elif op == "backward":
         plan_desc = gi.plan(params, False) + " | " + gi.grad_weight_plan(params)
     else:
-        plan_desc = gi.plan(params, wl.dtype == "bf16")
+        plan_desc = gi.plan(params, PLAN_KIND[wl.dtype])
     if op == "backward":
         # Several main kernels per call: the roofline is the whole call's.
         kernel = "whole call (grad_input and grad_weight kernels, prologue, reduction)"
@@ -269,7 +273,7 @@ def main():
             alg_bytes = 4 * (s.N * s.Co * s.oH * s.oW + s.N * s.Ci * s.H * s.W +
                              s.Co * s.Ci * s.kH * s.kW)
         else:
-            alg_bytes = s.algorithmic_bytes(2 if wl.dtype == "bf16" else 4)
+            alg_bytes = s.algorithmic_bytes(4 if wl.dtype == "f32" else 2)
         traffic = profiling.read_traffic(kernel, wl.name, plan_desc, variant, wl.dtype)
         mfma = profiling.read_mfma(kernel, wl.name, plan_desc, variant, wl.dtype)
     achieved = r["flops"] / (kernel_ms * 1e-3) / 1e12
@@ -316,7 +320,7 @@ def main():
             ro = time_workload(o, 20, 3, torch, gi, dev)
             v = ro["flops"] / (ro["ms_per_step"] * 1e-3) / 1e12
             so = o.shape
-            po = gi.plan(gi.make_params(*so.as_tuple()[:10]), o.dtype == "bf16")
+            po = gi.plan(gi.make_params(*so.as_tuple()[:10]), PLAN_KIND[o.dtype])
             vo = profiling.plan_variant(po)
             to = profiling.read_traffic(profiling.kernel_name(vo, o.dtype), o.name, po, vo,
                                         o.dtype)
@@ -332,7 +336,7 @@ def main():
                               "traffic": None if to is None else round(to["bytes"]),
                               "mfma_counters": mo,
                               "algorithmic_bytes": so.algorithmic_bytes(
-                                  2 if o.dtype == "bf16" else 4)}
+                                  4 if o.dtype == "f32" else 2)}
         line["other_workloads"] = others
         # The next row of the same backward pass: grad_weight (fp32 runs).
         nxt = {}

@@ -67,6 +67,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.conv2d_grad_input.restype = ctypes.c_int
     lib.conv2d_grad_input_bf16.argtypes = [P, P, P, PP, P]
     lib.conv2d_grad_input_bf16.restype = ctypes.c_int
+    lib.conv2d_grad_input_f16.argtypes = [P, P, P, PP, P]
+    lib.conv2d_grad_input_f16.restype = ctypes.c_int
     lib.conv2d_gi_validate.argtypes = [PP]
     lib.conv2d_gi_validate.restype = ctypes.c_int
     lib.conv2d_gi_strerror.argtypes = [ctypes.c_int]
@@ -114,7 +116,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
 
 def exported_names():
     """Names of the C entry points the binding wraps."""
-    return ["conv2d_grad_input", "conv2d_grad_input_bf16", "conv2d_grad_weight",
+    return ["conv2d_grad_input", "conv2d_grad_input_bf16", "conv2d_grad_input_f16",
+            "conv2d_grad_weight",
             "conv2d_backward", "conv2d_grad_bias", "conv2d_forward", "conv2d_fwd_plan",
             "conv2d_fwd_set_variant",
             "conv2d_gw_plan", "conv2d_gi_validate",
@@ -148,10 +151,11 @@ def validate(p: Conv2dGiParams) -> int:
     return load_library().conv2d_gi_validate(ctypes.byref(p))
 
 
-def plan(p: Conv2dGiParams, bf16: bool = False) -> str:
-    """Host-only: the plan the library would run for this shape."""
+def plan(p: Conv2dGiParams, bf16=False) -> str:
+    """Host-only: the plan the library would run for this shape; bf16: False
+    or 0 for fp32 inputs, True or 1 for bf16, 2 for fp16."""
     buf = ctypes.create_string_buffer(8192)
-    _check(load_library().conv2d_gi_plan(ctypes.byref(p), int(bool(bf16)), buf, len(buf)))
+    _check(load_library().conv2d_gi_plan(ctypes.byref(p), int(bf16), buf, len(buf)))
     return buf.value.decode()
 
 
@@ -216,8 +220,8 @@ def set_profile_events(begin, end):
 def grad_input(grad_out, weight, *, stride: int, padding, input_hw, out=None, stream=None):
     """grad_input [N, Ci, H, W] (fp32) of a conv2d, computed on the GPU.
 
-    grad_out [N, Co, oH, oW] and weight [Co, Ci, kH, kW]: both float32 or both
-    bfloat16, contiguous, on the same ROCm device.  padding: int or (pad_h, pad_w).
+    grad_out [N, Co, oH, oW] and weight [Co, Ci, kH, kW]: both float32, both
+    bfloat16 or both float16, contiguous, on the same ROCm device.  padding: int or (pad_h, pad_w).
     input_hw: (H, W) of the forward input.  out: optional float32 [N, Ci, H, W]
     tensor to write (every element is overwritten).  stream: a torch stream
     (default: the device's current stream).  The call is asynchronous on that stream.
@@ -232,8 +236,9 @@ def grad_input(grad_out, weight, *, stride: int, padding, input_hw, out=None, st
         raise ValueError("grad_out and weight must be 4-D (NCHW and [Co,Ci,kH,kW])")
     if not (grad_out.is_cuda and weight.is_cuda) or grad_out.device != weight.device:
         raise ValueError("grad_out and weight must be on the same GPU device")
-    if grad_out.dtype != weight.dtype or grad_out.dtype not in (torch.float32, torch.bfloat16):
-        raise ValueError("grad_out and weight must both be float32 or both bfloat16")
+    if grad_out.dtype != weight.dtype or grad_out.dtype not in (torch.float32, torch.bfloat16,
+                                                                torch.float16):
+        raise ValueError("grad_out and weight must both be float32, bfloat16 or float16")
     if not (grad_out.is_contiguous() and weight.is_contiguous()):
         raise ValueError("grad_out and weight must be contiguous")
     N, Co, oH, oW = (int(v) for v in grad_out.shape)
@@ -252,7 +257,8 @@ def grad_input(grad_out, weight, *, stride: int, padding, input_hw, out=None, st
             raise ValueError("out must be a contiguous float32 [N,Ci,H,W] tensor on %s" % dev)
     with torch.cuda.device(dev):
         s = stream if stream is not None else torch.cuda.current_stream(dev)
-        fn = lib.conv2d_grad_input_bf16 if grad_out.dtype == torch.bfloat16 else lib.conv2d_grad_input
+        fn = {torch.bfloat16: lib.conv2d_grad_input_bf16, torch.float16: lib.conv2d_grad_input_f16,
+              torch.float32: lib.conv2d_grad_input}[grad_out.dtype]
         code = fn(ctypes.c_void_p(grad_out.data_ptr()), ctypes.c_void_p(weight.data_ptr()),
                   ctypes.c_void_p(out.data_ptr()), ctypes.byref(p),
                   ctypes.c_void_p(s.cuda_stream))

@@ -21,6 +21,7 @@
 #include "gi_launch.h"
 #include "fwd_common.h"
 #include "gw_common.h"
+#include "half_launch.h"
 
 namespace {
 
@@ -705,9 +706,13 @@ Plan make_plan(const conv2d_gi_params &p, bool bf16) {
 
 bool has_elems(int64_t n) { return n > 0; }
 
+// dt: 0 fp32 inputs, 1 bf16, 2 fp16 (the 16-bit kinds share plans, prologues
+// and kernels up to the MFMA instruction).
 template <typename T>
 int run(const T *grad_out, const T *weight, float *dst, const conv2d_gi_params *p,
-        hipStream_t stream, bool bf16) {
+        hipStream_t stream, int dt) {
+    const bool bf16 = dt != 0;   // a 16-bit input kind
+    const bool f16 = dt == 2;
     int rc = validate(p);
     if (rc != CONV2D_GI_OK) return rc;
     const int64_t n_dst = (int64_t)p->N * p->Ci * p->H * p->W;
@@ -767,7 +772,8 @@ int run(const T *grad_out, const T *weight, float *dst, const conv2d_gi_params *
             h.args.gp = (const uint16_t *)ws;
             h.args.wk = (const uint16_t *)((char *)ws + h.gp_bytes);
             h.args.dst = dst;
-            e = gi::launch_halo_bf16(h.args, h.cfg, h.tiles, h.ci_tiles, h.lds, stream, ev);
+            e = f16 ? gi::launch_halo_f16(h.args, h.cfg, h.tiles, h.ci_tiles, h.lds, stream, ev)
+                    : gi::launch_halo_bf16(h.args, h.cfg, h.tiles, h.ci_tiles, h.lds, stream, ev);
         }
     } else if (plan.variant == CONV2D_GI_VARIANT_HALO) {
         if (e == hipSuccess) {
@@ -788,8 +794,9 @@ int run(const T *grad_out, const T *weight, float *dst, const conv2d_gi_params *
             gi::KernelEvents li;
             li.start = i == 0 ? ev.start : nullptr;
             li.stop = i + 1 == nl ? ev.stop : nullptr;
-            e = bf16 ? gi::launch_generic_bf16(L.args, L.tiles_x, stream, li)
-                     : gi::launch_generic_f32(L.args, L.tiles_x, stream, li);
+            e = f16    ? gi::launch_generic_f16(L.args, L.tiles_x, stream, li)
+                : bf16 ? gi::launch_generic_bf16(L.args, L.tiles_x, stream, li)
+                       : gi::launch_generic_f32(L.args, L.tiles_x, stream, li);
         }
     }
     if (e != hipSuccess) return fail_hip(e);
@@ -1057,13 +1064,15 @@ std::string describe_gw(const GwPlan &g) {
            " lds=" + std::to_string(g.lds) + "]";
 }
 
-std::string describe(const Plan &plan, bool bf16) {
+// dt: 0 fp32, 1 bf16, 2 fp16 inputs.
+std::string describe(const Plan &plan, int dt) {
+    const bool bf16 = dt != 0;
     std::string s = "variant=";
     s += plan.variant == CONV2D_GI_VARIANT_HALO   ? "halo"
          : plan.variant == CONV2D_GI_VARIANT_STEM ? "stem"
                                                   : "generic";
     s += " dtype=";
-    s += bf16 ? "bf16" : "f32";
+    s += dt == 2 ? "f16" : bf16 ? "bf16" : "f32";
     s += " ws_bytes=" + std::to_string(plan.ws_bytes);
     if (plan.variant == CONV2D_GI_VARIANT_STEM) {
         const gi::StemArgs &a = plan.stem.args;
@@ -1221,7 +1230,7 @@ int run_backward(const float *grad_out, const float *x, const float *weight, flo
     if (dx && has_elems(n_w) && !weight) return CONV2D_GI_EINVAL;
     if (dw && has_elems(n_x) && !x) return CONV2D_GI_EINVAL;
     if (dx) {
-        rc = run<float>(grad_out, weight, dx, p, stream, false);
+        rc = run<float>(grad_out, weight, dx, p, stream, 0);
         if (rc != CONV2D_GI_OK) return rc;
     }
     if (dw && n_w > 0) return run_gw_checked(grad_out, x, dw, db, p, stream);
@@ -1286,7 +1295,7 @@ int run_forward(const float *x, const float *w, float *y, const conv2d_gi_params
                 if (e != hipSuccess) return fail_hip(e);
             }
         }
-        return run<float>(x, (const float *)wf, y, &q, stream, false);
+        return run<float>(x, (const float *)wf, y, &q, stream, 0);
     }
     std::lock_guard<std::mutex> lock(g_ws_mu);
     void *ws = nullptr;
@@ -1409,12 +1418,17 @@ int conv2d_gw_set_variant(int mode) {
 
 int conv2d_grad_input(const float *grad_out, const float *weight, float *dst,
                       const conv2d_gi_params *p, hipStream_t stream) {
-    return run<float>(grad_out, weight, dst, p, stream, false);
+    return run<float>(grad_out, weight, dst, p, stream, 0);
 }
 
 int conv2d_grad_input_bf16(const uint16_t *grad_out, const uint16_t *weight, float *dst,
                            const conv2d_gi_params *p, hipStream_t stream) {
-    return run<uint16_t>(grad_out, weight, dst, p, stream, true);
+    return run<uint16_t>(grad_out, weight, dst, p, stream, 1);
+}
+
+int conv2d_grad_input_f16(const uint16_t *grad_out, const uint16_t *weight, float *dst,
+                          const conv2d_gi_params *p, hipStream_t stream) {
+    return run<uint16_t>(grad_out, weight, dst, p, stream, 2);
 }
 
 int conv2d_gi_validate(const conv2d_gi_params *p) { return validate(p); }
@@ -1443,8 +1457,9 @@ int conv2d_gi_plan(const conv2d_gi_params *p, int dtype_bf16, char *buf, size_t 
     int rc = validate(p);
     if (rc != CONV2D_GI_OK) return rc;
     if (!buf || len == 0) return CONV2D_GI_EINVAL;
+    if (dtype_bf16 < 0 || dtype_bf16 > 2) return CONV2D_GI_EINVAL;
     Plan plan = make_plan(*p, dtype_bf16 != 0);
-    std::snprintf(buf, len, "%s", describe(plan, dtype_bf16 != 0).c_str());
+    std::snprintf(buf, len, "%s", describe(plan, dtype_bf16).c_str());
     return CONV2D_GI_OK;
 }
 

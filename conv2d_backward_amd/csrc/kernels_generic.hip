@@ -19,11 +19,13 @@
 
 #include "gi_common.h"
 #include "gi_launch.h"
+#include "half_launch.h"
 
 namespace gi {
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
 // ---------------------------------------------------------------------------
 // Weight reorder prologues: one thread per output element, writes coalesced.
@@ -215,6 +217,8 @@ __global__ __launch_bounds__(256) void gi_generic_f32(const GemmArgs A) {
 // weight prologue stores co fastest, so A rows are contiguous in HBM; the B
 // gather reads co rows of grad_out and transposes them on the LDS write.
 // ---------------------------------------------------------------------------
+// F16: fp16 inputs (V_MFMA_F32_32X32X16_F16), else bf16; same data path.
+template <bool F16>
 __global__ __launch_bounds__(256) void gi_generic_bf16(const GemmArgs A) {
     constexpr int BM = kGenericBM, BN = kGenericBN, BK = 16, NT = 256;
     constexpr int LDK = BK + 8;  // 48-byte rows: 16-byte aligned fragments
@@ -290,8 +294,16 @@ __global__ __launch_bounds__(256) void gi_generic_bf16(const GemmArgs A) {
             const v8bf af = *(const v8bf *)&As[cur][wm * 32 + ml][kl];
             const v8bf b0 = *(const v8bf *)&Bs[cur][wn * 64 + ml][kl];
             const v8bf b1 = *(const v8bf *)&Bs[cur][wn * 64 + 32 + ml][kl];
-            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, b0, acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, b1, acc1, 0, 0, 0);
+            if constexpr (F16) {
+                const v8h ah = __builtin_bit_cast(v8h, af);
+                acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, __builtin_bit_cast(v8h, b0), acc0,
+                                                              0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, __builtin_bit_cast(v8h, b1), acc1,
+                                                              0, 0, 0);
+            } else {
+                acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, b0, acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, b1, acc1, 0, 0, 0);
+            }
             if (it + 1 < T) sstore(cur ^ 1);
             __syncthreads();
         }
@@ -309,8 +321,15 @@ hipError_t launch_generic_f32(const GemmArgs &a, int tiles_x, hipStream_t s,
 
 hipError_t launch_generic_bf16(const GemmArgs &a, int tiles_x, hipStream_t s,
                                const KernelEvents &ev) {
-    hipExtLaunchKernelGGL(gi_generic_bf16, dim3(tiles_x, a.ci_tiles), dim3(256), 0, s, ev.start,
-                          ev.stop, 0, a);
+    hipExtLaunchKernelGGL(gi_generic_bf16<false>, dim3(tiles_x, a.ci_tiles), dim3(256), 0, s,
+                          ev.start, ev.stop, 0, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_generic_f16(const GemmArgs &a, int tiles_x, hipStream_t s,
+                              const KernelEvents &ev) {
+    hipExtLaunchKernelGGL(gi_generic_bf16<true>, dim3(tiles_x, a.ci_tiles), dim3(256), 0, s,
+                          ev.start, ev.stop, 0, a);
     return hipGetLastError();
 }
 

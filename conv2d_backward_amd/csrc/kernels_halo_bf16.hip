@@ -42,11 +42,13 @@
 
 #include "gi_common.h"
 #include "gi_launch.h"
+#include "half_launch.h"
 
 namespace gi {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
 namespace {
 
@@ -60,9 +62,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint3
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (long)bytes, kRsrcWord3);
 }
 
-// NBW pixel blocks per wave, T taps; KW > 0: kernel width and HPT halo pitch
-// known at compile time (they must equal A.kW and A.HP), else read from A.
-template <int NBW, int T, int KW, int HPT>
+// F16: the 16-bit inputs are fp16 (V_MFMA_F32_16X16X32_F16), else bf16; the
+// data path is the same bits either way.  NBW pixel blocks per wave, T taps;
+// KW > 0: kernel width and HPT halo pitch known at compile time (they must
+// equal A.kW and A.HP), else read from A.
+template <bool F16, int NBW, int T, int KW, int HPT>
 __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void gi_halo_bf16(
     const HaloBf16Args A) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -213,8 +217,13 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
             for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
                 for (int b = 0; b < NBW; ++b)
-                    acc[cb][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[tp][cb], fb[sl][b],
-                                                                         acc[cb][b], 0, 0, 0);
+                    if constexpr (F16)
+                        acc[cb][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            __builtin_bit_cast(v8h, fa[tp][cb]), __builtin_bit_cast(v8h, fb[sl][b]),
+                            acc[cb][b], 0, 0, 0);
+                    else
+                        acc[cb][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            fa[tp][cb], fb[sl][b], acc[cb][b], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
         // The next chunk's halo must have landed before the barrier.  Loads
@@ -249,18 +258,18 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     }
 }
 
-template <int NBW, int T, int KW, int HPT>
+template <bool F16, int NBW, int T, int KW, int HPT>
 hipError_t launch_one(const HaloBf16Args &a, int tiles, int ci_tiles, size_t lds, hipStream_t s,
                       const KernelEvents &ev) {
     if ((KW > 0 && (a.kW != KW || a.kH * a.kW != T)) || (HPT > 0 && a.HP != HPT))
         return hipErrorInvalidValue;
     if (lds > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute((const void *)gi_halo_bf16<NBW, T, KW, HPT>,
+        hipError_t e = hipFuncSetAttribute((const void *)gi_halo_bf16<F16, NBW, T, KW, HPT>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
     if (a.ci_tiles != ci_tiles) return hipErrorInvalidValue;
-    hipExtLaunchKernelGGL((gi_halo_bf16<NBW, T, KW, HPT>), dim3(tiles * ci_tiles), dim3(256),
+    hipExtLaunchKernelGGL((gi_halo_bf16<F16, NBW, T, KW, HPT>), dim3(tiles * ci_tiles), dim3(256),
                           (uint32_t)lds, s, ev.start, ev.stop, 0, a);
     return hipGetLastError();
 }
@@ -397,16 +406,27 @@ int halo_bf16_config(int nbw, int kH, int kW, int hp) {
     return -1;
 }
 
-hipError_t launch_halo_bf16(const HaloBf16Args &a, int cfg, int tiles, int ci_tiles, size_t lds,
-                            hipStream_t s, const KernelEvents &ev) {
+template <bool F16>
+hipError_t launch_halo_16(const HaloBf16Args &a, int cfg, int tiles, int ci_tiles, size_t lds,
+                          hipStream_t s, const KernelEvents &ev) {
     switch (cfg) {
-        case 0: return launch_one<7, 9, 3, 30>(a, tiles, ci_tiles, lds, s, ev);
-        case 1: return launch_one<7, 9, 0, 0>(a, tiles, ci_tiles, lds, s, ev);
-        case 2: return launch_one<4, 9, 0, 0>(a, tiles, ci_tiles, lds, s, ev);
-        case 3: return launch_one<7, 3, 0, 0>(a, tiles, ci_tiles, lds, s, ev);
-        case 4: return launch_one<4, 3, 0, 0>(a, tiles, ci_tiles, lds, s, ev);
+        case 0: return launch_one<F16, 7, 9, 3, 30>(a, tiles, ci_tiles, lds, s, ev);
+        case 1: return launch_one<F16, 7, 9, 0, 0>(a, tiles, ci_tiles, lds, s, ev);
+        case 2: return launch_one<F16, 4, 9, 0, 0>(a, tiles, ci_tiles, lds, s, ev);
+        case 3: return launch_one<F16, 7, 3, 0, 0>(a, tiles, ci_tiles, lds, s, ev);
+        case 4: return launch_one<F16, 4, 3, 0, 0>(a, tiles, ci_tiles, lds, s, ev);
         default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_halo_bf16(const HaloBf16Args &a, int cfg, int tiles, int ci_tiles, size_t lds,
+                            hipStream_t s, const KernelEvents &ev) {
+    return launch_halo_16<false>(a, cfg, tiles, ci_tiles, lds, s, ev);
+}
+
+hipError_t launch_halo_f16(const HaloBf16Args &a, int cfg, int tiles, int ci_tiles, size_t lds,
+                           hipStream_t s, const KernelEvents &ev) {
+    return launch_halo_16<true>(a, cfg, tiles, ci_tiles, lds, s, ev);
 }
 
 hipError_t launch_prologues_bf16(const uint16_t *g, uint16_t *gp, const uint16_t *w, uint16_t *wk,

@@ -43,13 +43,15 @@ PROFILES = os.path.join(ROOT, "profiles")
 # planner, whose result is matched separately through the plan description).
 KERNEL_SOURCES = {
     ("halo", "f32"): ["kernels_halo_f32.hip"],
-    ("halo", "bf16"): ["kernels_halo_bf16.hip"],
+    ("halo", "bf16"): ["kernels_halo_bf16.hip", "half_launch.h"],
+    ("halo", "f16"): ["kernels_halo_bf16.hip", "half_launch.h"],
     ("stem", "f32"): ["kernels_stem_f32.hip"],
     ("gw", "f32"): ["kernels_gw_f32.hip", "gw_common.h"],
     ("gwd", "f32"): ["kernels_gw_f32.hip", "gw_common.h"],
     ("fwd", "f32"): ["kernels_fwd_f32.hip", "fwd_common.h"],
-    ("generic", "f32"): ["kernels_generic.hip"],
-    ("generic", "bf16"): ["kernels_generic.hip"],
+    ("generic", "f32"): ["kernels_generic.hip", "half_launch.h"],
+    ("generic", "bf16"): ["kernels_generic.hip", "half_launch.h"],
+    ("generic", "f16"): ["kernels_generic.hip", "half_launch.h"],
 }
 COMMON_SOURCES = ["gi_common.h", "gi_launch.h"]
 CALIBRATION_COPIES = 3   # copies bench.py runs for --calibration-copy-mib
@@ -236,10 +238,10 @@ def write_traffic(fetch_dir: str, write_dir: str, bench_log: str, workload: str,
 
 
 MFMA_COUNTERS = ["SQ_INSTS_VALU_MFMA_MOPS_F32", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
-                 "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE"]
+                 "SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE"]
 SIMDS = 1024      # MI355X: 256 compute units x 4 SIMDs
 XCDS = 8          # GRBM_GUI_ACTIVE comes summed over the 8 XCDs' own counters
-PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6}
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6, "f16": 2516.6}
 
 
 def write_mfma(run_dir: str, stats_dir: str, bench_log: str, workload: str, command: str,
@@ -252,15 +254,19 @@ def write_mfma(run_dir: str, stats_dir: str, bench_log: str, workload: str, comm
     variant, dtype = plan_variant(plan), line["dtype"]
     short = kernel_name(variant, dtype)
 
-    def per_launch(counter, reduce_max=False):
+    def per_launch(counter, reduce_max=False, optional=False):
         disp = (_counter_max if reduce_max else _counter)(run_dir, counter)
+        if not disp and optional:
+            return None, 0, 0.0
         main = [(d, n, v) for d, n, v in disp if _matches(n, short)]
         if not main:
             raise ValueError("kernel %s not in %s" % (short, run_dir))
         return main[0][1], len(main), sum(v for _, _, v in main) / len(main)
 
     kname, nd, mops32 = per_launch("SQ_INSTS_VALU_MFMA_MOPS_F32")
-    _, _, mops16 = per_launch("SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    _, _, mopsbf = per_launch("SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    _, _, mopsh = per_launch("SQ_INSTS_VALU_MFMA_MOPS_F16", optional=True)
+    mops16 = mopsbf + mopsh
     _, _, busy = per_launch("SQ_VALU_MFMA_BUSY_CYCLES")
     _, _, gui = per_launch("GRBM_GUI_ACTIVE", reduce_max=True)
     with open(_csv(stats_dir, "kernel_stats.csv")) as fh:
@@ -273,7 +279,8 @@ def write_mfma(run_dir: str, stats_dir: str, bench_log: str, workload: str, comm
     out = os.path.join(out_dir, "%s_%s_mfma.txt" % (short, workload))
     with open(out, "w") as fh:
         fh.write("# Matrix-core work per launch of %s on %s (rocprofv3 --pmc %s)\n"
-                 "# counter_flops = (MOPS_F32 + MOPS_BF16) * 512, padded lanes included;\n"
+                 "# counter_flops = (MOPS_F32 + MOPS_BF16 + MOPS_F16) * 512, padded lanes\n"
+                 "# included;\n"
                  "# counter_util = counter_flops / (kernel-trace average duration * peak);\n"
                  "# busy_util = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / %d XCDs * %d\n"
                  "# SIMDs), rocprofv3's MfmaUtil expression with the GUI-active cycles, which\n"
@@ -283,7 +290,8 @@ def write_mfma(run_dir: str, stats_dir: str, bench_log: str, workload: str, comm
                      ("source_fingerprint", fingerprint(variant, dtype)),
                      ("command", command), ("kernel_name", kname), ("dispatches", nd),
                      ("mops_f32_per_dispatch", "%.0f" % mops32),
-                     ("mops_bf16_per_dispatch", "%.0f" % mops16),
+                     ("mops_bf16_per_dispatch", "%.0f" % mopsbf),
+                     ("mops_f16_per_dispatch", "%.0f" % mopsh),
                      ("mfma_busy_cycles_per_dispatch", "%.0f" % busy),
                      ("gui_active_cycles_per_dispatch", "%.0f" % gui),
                      ("kernel_trace_avg_us", "%.3f" % (dur_s * 1e6)),

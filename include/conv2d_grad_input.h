@@ -128,6 +128,19 @@ CONV2D_GI_API int conv2d_grad_input_bf16(const uint16_t *grad_out, const uint16_
                            float *dst, const conv2d_gi_params *p,
                            hipStream_t stream);
 
+/*
+ * fp16 inputs: grad_out and weight as IEEE binary16 bit patterns (uint16_t,
+ * same layouts), fp32 accumulation, fp32 dst.  The same plans, prologues and
+ * kernels as the bf16 entry point with the fp16 MFMA (16x16x32 / 32x32x16
+ * f16); the products of two fp16 values are exact in fp32.  This is the
+ * fp16 precision the pages cast to (doppler ensureF32 and the f16 casts of
+ * the other pages), taken as an input type.  Same validation and status
+ * codes as conv2d_grad_input.
+ */
+CONV2D_GI_API int conv2d_grad_input_f16(const uint16_t *grad_out, const uint16_t *weight,
+                                        float *dst, const conv2d_gi_params *p,
+                                        hipStream_t stream);
+
 /* Host-only check of a shape, as done by the entry points (no HIP call). */
 CONV2D_GI_API int conv2d_gi_validate(const conv2d_gi_params *p);
 
@@ -296,7 +309,7 @@ CONV2D_GI_API int conv2d_gw_set_tile(int rows, int stages, int max_slices);
 
 /*
  * Host-only: describe the plan the entry point would run for this shape
- * (dtype_bf16 = 0 for fp32 inputs, 1 for bf16), as text written into buf
+ * (dtype_bf16 = 0 for fp32 inputs, 1 for bf16, 2 for fp16), as text written into buf
  * (NUL-terminated, truncated to len).  Returns a status code.
  */
 CONV2D_GI_API int conv2d_gi_plan(const conv2d_gi_params *p, int dtype_bf16, char *buf,

@@ -4,6 +4,9 @@ Criteria (element by element, S = sum |grad_out * weight| over the element's ter
   fp32 inputs:  |gpu - oracle| <= 1e-5 * S + 1e-6
   bf16 inputs:  ||gpu - oracle||_2 <= 1e-2 * ||oracle||_2  and
                 |gpu - oracle| <= 1e-2 * S + 1e-6        (oracle on the same bf16 values)
+  fp16 inputs:  |gpu - oracle| <= 1e-5 * S + 1e-6        (oracle on the same fp16 values:
+                products of two fp16 values are exact in fp32 and the sums are fp32,
+                so the fp32 criterion applies)
 dst is pre-filled with NaN (an unwritten element fails) and framed by guard
 bands that must stay untouched (an out-of-bounds write fails).
 """
@@ -44,9 +47,10 @@ def device():
 def run_gpu(g_np, w_np, shape, dtype, variant=gi.VARIANT_AUTO, stream=None):
     """Run the library on numpy inputs; returns (dst numpy float64, guard ok)."""
     dev = torch.device("cuda:0")
-    if dtype == "bf16":
-        g = torch.from_numpy(g_np.view(np.int16)).to(dev).view(torch.bfloat16)
-        w = torch.from_numpy(w_np.view(np.int16)).to(dev).view(torch.bfloat16)
+    if dtype in ("bf16", "f16"):
+        t16 = torch.bfloat16 if dtype == "bf16" else torch.float16
+        g = torch.from_numpy(g_np.view(np.int16)).to(dev).view(t16)
+        w = torch.from_numpy(w_np.view(np.int16)).to(dev).view(t16)
     else:
         g = torch.from_numpy(np.ascontiguousarray(g_np, dtype=np.float32)).to(dev)
         w = torch.from_numpy(np.ascontiguousarray(w_np, dtype=np.float32)).to(dev)
@@ -69,6 +73,8 @@ def run_gpu(g_np, w_np, shape, dtype, variant=gi.VARIANT_AUTO, stream=None):
 def oracle_inputs(g_np, w_np, dtype):
     if dtype == "bf16":
         return workloads.bf16_to_f32(g_np), workloads.bf16_to_f32(w_np)
+    if dtype == "f16":
+        return workloads.f16_to_f32(g_np), workloads.f16_to_f32(w_np)
     return g_np, w_np
 
 
@@ -94,6 +100,8 @@ def full_parity(shape, seed, dtype, variant=gi.VARIANT_AUTO, dist="uniform"):
     g, w = workloads.make_case(shape, seed, dist)
     if dtype == "bf16":
         g, w = workloads.bf16_bits(g), workloads.bf16_bits(w)
+    elif dtype == "f16":
+        g, w = workloads.f16_bits(g), workloads.f16_bits(w)
     say("case %s dtype=%s variant=%d seed=%d" % (shape, dtype, variant, seed))
     got, guard_ok = run_gpu(g, w, shape, dtype, variant)
     assert guard_ok, "write outside dst"
@@ -106,7 +114,7 @@ def full_parity(shape, seed, dtype, variant=gi.VARIANT_AUTO, dist="uniform"):
 SWEEP = workloads.sweep_shapes()
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("idx", range(len(SWEEP)))
 def test_sweep(idx, dtype):
     full_parity(SWEEP[idx], 100 + idx, dtype)
@@ -123,13 +131,13 @@ MID = [
 ]
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("idx", range(len(MID)))
 def test_mid(idx, dtype):
     full_parity(MID[idx], 500 + idx, dtype, dist="normal")
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_forced_generic(dtype):
     for i, s in enumerate([SWEEP[4], SWEEP[9], MID[0], MID[2]]):
         full_parity(s, 900 + i, dtype, gi.VARIANT_GENERIC)
@@ -168,14 +176,15 @@ HALO_BF16_SHAPES = [
 ]
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("idx", range(len(HALO_BF16_SHAPES)))
-def test_forced_halo_bf16(idx):
+def test_forced_halo_bf16(idx, dtype):
     s = HALO_BF16_SHAPES[idx]
     gi.set_variant(gi.VARIANT_HALO)
-    desc = gi.plan(gi.make_params(*s.as_tuple()[:10]), True)
+    desc = gi.plan(gi.make_params(*s.as_tuple()[:10]), 1 if dtype == "bf16" else 2)
     gi.set_variant(gi.VARIANT_AUTO)
-    assert "variant=halo" in desc, desc
-    full_parity(s, 1500 + idx, "bf16", gi.VARIANT_HALO, dist="normal")
+    assert "variant=halo" in desc and ("dtype=" + dtype) in desc, desc
+    full_parity(s, 1500 + idx, dtype, gi.VARIANT_HALO, dist="normal")
 
 
 STEM_SHAPES = [

@@ -77,7 +77,7 @@ class Workload:
     index: int      # c in the seed formula
     sub: int        # sub in the seed formula
     shape: Shape
-    dtype: str      # "f32" or "bf16" (inputs); dst is always fp32
+    dtype: str      # "f32", "bf16" or "f16" (inputs); dst is always fp32
     dist: str       # "uniform" (both U[-1,1]) or "kaiming" (g ~ N(0,1), w ~ N(0, 2/fan_in))
 
 
@@ -91,6 +91,7 @@ WORKLOADS = [
     Workload("asym_1x7", 3, 1, Shape(32, 192, 17, 17, 192, 1, 7, 1, 0, 3), "f32", "kaiming"),
     Workload("deep_late_stage", 4, 0, Shape(64, 512, 14, 14, 512, 3, 3, 1, 1, 1), "f32", "kaiming"),
     Workload("deep_late_stage_bf16", 4, 0, Shape(64, 512, 14, 14, 512, 3, 3, 1, 1, 1), "bf16", "kaiming"),
+    Workload("deep_late_stage_f16", 4, 0, Shape(64, 512, 14, 14, 512, 3, 3, 1, 1, 1), "f16", "kaiming"),
 ]
 BY_NAME = {w.name: w for w in WORKLOADS}
 
@@ -121,6 +122,17 @@ def bf16_bits(a: np.ndarray) -> np.ndarray:
     return r
 
 
+def f16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 to IEEE binary16 (nearest, ties to even; numpy's cast) and
+    return the uint16 bit patterns."""
+    return np.ascontiguousarray(a, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def f16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Widen binary16 bit patterns to float32 (exact)."""
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float32)
+
+
 def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
     """Widen bf16 bit patterns to float32 (exact)."""
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
@@ -129,8 +141,8 @@ def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
 def make_inputs(w: Workload):
     """(grad_out, weight) for a named workload.
 
-    f32: two float32 arrays.  bf16: two uint16 arrays of bf16 bit patterns
-    (the float32 draws of the same seeds, rounded)."""
+    f32: two float32 arrays.  bf16 / f16: two uint16 arrays of bf16 / binary16
+    bit patterns (the float32 draws of the same seeds, rounded)."""
     s = w.shape
     if w.dist == "uniform":
         g = draw(s.grad_out_shape, seed_of(w.index, w.sub, 1), "uniform")
@@ -141,6 +153,8 @@ def make_inputs(w: Workload):
         wt = draw(s.weight_shape, seed_of(w.index, w.sub, 2), "normal", math.sqrt(2.0 / fan_in))
     if w.dtype == "bf16":
         return bf16_bits(g), bf16_bits(wt)
+    if w.dtype == "f16":
+        return f16_bits(g), f16_bits(wt)
     return g, wt
 
 
