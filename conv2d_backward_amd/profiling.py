@@ -76,6 +76,11 @@ def fingerprint(variant: str, dtype: str) -> str:
 
 
 def _matches(name: str, short: str) -> bool:
+    """Whether kernel `name` (as the trace prints it) is the kernel `short`
+    names.  fp16 inputs run the 16-bit kernels' fp16 instantiations:
+    gi_halo_f16 is gi_halo_bf16<true, ...>, gi_generic_f16 gi_generic_bf16<true>."""
+    if short.endswith("_f16"):
+        return (short[:-4] + "_bf16<true") in name
     return (short + "<") in name or (short + "(") in name
 
 
