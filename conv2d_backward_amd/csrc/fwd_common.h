@@ -44,7 +44,8 @@ hipError_t launch_fwd_weight_k_co_f32(const float *w, float *wt, int Co, int K, 
 // (fewer than 16 input channels; its weight then comes from
 // launch_fwd_weight_k_co_f32, else from launch_fwd_weight_tap_ci_co_f32).
 bool fwd_flat_k(const FwdArgs &a);
-// The generic forward kernel: grid ceil(N*oH*oW / kFwdBN) x ceil(Co / kFwdBM).
+// The generic forward kernel: a 1-D grid of ceil(N*oH*oW / kFwdBN) *
+// ceil(Co / kFwdBM) work-groups, output-channel tile fastest.
 hipError_t launch_fwd_generic_f32(const FwdArgs &a, hipStream_t s, const KernelEvents &ev);
 
 }  // namespace gi

@@ -85,8 +85,12 @@ __global__ __launch_bounds__(256) void gi_fwd_f32(const FwdArgs A) {
     __shared__ int2 ktab[FLATK ? kFwdMaxFlatK : 1];   // (ci*H*W + kh*W + kw, kh << 16 | kw)
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int pix0 = blockIdx.x * BN;
-    const int co0 = blockIdx.y * BM;
+    // Logical order: output-channel tile fastest, so the work-groups that
+    // gather the same input pixels run together on one XCD's L2.
+    const int co_tiles = (A.Co + BM - 1) / BM;
+    const int J = xcd_order(blockIdx.x, gridDim.x);
+    const int pix0 = (J / co_tiles) * BN;
+    const int co0 = (J % co_tiles) * BM;
     const int oHW = A.oH * A.oW;
     const int npix = A.N * oHW;
     const int HW = A.H * A.W;
@@ -241,7 +245,9 @@ bool fwd_flat_k(const FwdArgs &a) {
 hipError_t launch_fwd_generic_f32(const FwdArgs &a, hipStream_t s, const KernelEvents &ev) {
     const int64_t npix = (int64_t)a.N * a.oH * a.oW;
     if (npix == 0 || a.Co == 0) return hipSuccess;
-    const dim3 grid((unsigned)((npix + kFwdBN - 1) / kFwdBN), (unsigned)((a.Co + kFwdBM - 1) / kFwdBM));
+    const int64_t wgs = (npix + kFwdBN - 1) / kFwdBN * ((a.Co + kFwdBM - 1) / kFwdBM);
+    if (wgs > INT32_MAX) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)wgs);
     if (fwd_flat_k(a))
         hipExtLaunchKernelGGL(gi_fwd_f32<true>, grid, dim3(256), 0, s, ev.start, ev.stop, 0, a);
     else
