@@ -44,12 +44,14 @@ thread_local hipEvent_t g_prof_begin = nullptr, g_prof_end = nullptr;
 // Scratch (the reordered weight) cached per (device, stream): allocated
 // stream-ordered on first use, grown when a call needs more, reused by later
 // calls on the same stream (stream order keeps them apart), released by
-// conv2d_gi_release_workspaces.  The lock is held while a call enqueues.
+// conv2d_gi_release_workspaces.  The lock is held while a call enqueues; it is
+// recursive so that an entry point that fills one slot and then runs another
+// path reading it keeps the lock across both.
 struct Workspace {
     void *ptr = nullptr;
     size_t bytes = 0;
 };
-std::mutex g_ws_mu;
+std::recursive_mutex g_ws_mu;
 // Scratch per (device, stream, slot): slot 0 serves every kernel's own
 // scratch, slot 1 a reordered operand that a later call in the same entry
 // point reads (the forward's reversed weight).
@@ -729,7 +731,7 @@ int run(const T *grad_out, const T *weight, float *dst, const conv2d_gi_params *
     int dev = 0;
     e = hipGetDevice(&dev);
     if (e != hipSuccess) return fail_hip(e);
-    std::lock_guard<std::mutex> lock(g_ws_mu);
+    std::lock_guard<std::recursive_mutex> lock(g_ws_mu);
     if (plan.ws_bytes > 0) {
         e = workspace_for(dev, stream, plan.ws_bytes, &ws);
         if (e != hipSuccess) return fail_hip(e);
@@ -1156,7 +1158,7 @@ int run_gw_checked(const float *grad_out, const float *x, float *dw, float *db,
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return fail_hip(e);
-    std::lock_guard<std::mutex> lock(g_ws_mu);
+    std::lock_guard<std::recursive_mutex> lock(g_ws_mu);
     void *ws = nullptr;
     size_t need = use_d ? dplan.ws_bytes : plan.ws_bytes;
     if (!use_d && db) need = std::max(need, bias_ws_bytes(*p));
@@ -1209,7 +1211,7 @@ int run_bias_checked(const float *grad_out, float *db, const conv2d_gi_params *p
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return fail_hip(e);
-    std::lock_guard<std::mutex> lock(g_ws_mu);
+    std::lock_guard<std::recursive_mutex> lock(g_ws_mu);
     void *ws = nullptr;
     e = workspace_for(dev, stream, bias_ws_bytes(*p), &ws);
     if (e != hipSuccess) return fail_hip(e);
@@ -1286,18 +1288,18 @@ int run_forward(const float *x, const float *w, float *y, const conv2d_gi_params
         rc = validate(&q);
         if (rc != CONV2D_GI_OK) return rc;
         void *wf = nullptr;
-        {
-            std::lock_guard<std::mutex> lock(g_ws_mu);
-            e = workspace_for(dev, stream, (size_t)std::max<int64_t>(n_w, 1) * 4, &wf, 1);
+        // Held across the grad_input call too: another thread enqueueing a
+        // forward on this stream in between would overwrite slot 1.
+        std::lock_guard<std::recursive_mutex> lock(g_ws_mu);
+        e = workspace_for(dev, stream, (size_t)std::max<int64_t>(n_w, 1) * 4, &wf, 1);
+        if (e != hipSuccess) return fail_hip(e);
+        if (n_w > 0) {
+            e = gi::launch_fwd_weight_flip_f32(w, (float *)wf, p->Co, p->Ci, kHW, stream);
             if (e != hipSuccess) return fail_hip(e);
-            if (n_w > 0) {
-                e = gi::launch_fwd_weight_flip_f32(w, (float *)wf, p->Co, p->Ci, kHW, stream);
-                if (e != hipSuccess) return fail_hip(e);
-            }
         }
         return run<float>(x, (const float *)wf, y, &q, stream, 0);
     }
-    std::lock_guard<std::mutex> lock(g_ws_mu);
+    std::lock_guard<std::recursive_mutex> lock(g_ws_mu);
     void *ws = nullptr;
     e = workspace_for(dev, stream, (size_t)std::max<int64_t>(n_w, 1) * 4, &ws);
     if (e != hipSuccess) return fail_hip(e);
@@ -1497,7 +1499,7 @@ int conv2d_gi_set_halo_split(int groups) {
 }
 
 int conv2d_gi_release_workspaces(void) {
-    std::lock_guard<std::mutex> lock(g_ws_mu);
+    std::lock_guard<std::recursive_mutex> lock(g_ws_mu);
     int prev = 0;
     if (hipGetDevice(&prev) != hipSuccess) return fail_hip(hipErrorNoDevice);
     hipError_t first = hipSuccess;

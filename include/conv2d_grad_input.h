@@ -32,12 +32,16 @@
  *   weight   [Co, Ci, kH, kW]  read only
  *   dst      [N, Ci, H, W]     fp32, written (every element, never accumulated)
  * The caller allocates and owns all three; the library never frees them.  dst
- * must not overlap either input.  The library keeps one scratch buffer (the
- * weight in kernel order, about Co*Ci*kH*kW elements) per (device, stream):
- * allocated stream-ordered on `stream` (hipMallocAsync) at the first call
- * that needs it, grown when a later call needs more, and reused by later
- * calls on that stream, which stream order keeps apart.  Calls on different
- * streams share no state.  conv2d_gi_release_workspaces frees the buffers
+ * must not overlap either input.  The library keeps scratch buffers per
+ * (device, stream): one for every kernel's own scratch (the weight in kernel
+ * order, about Co*Ci*kH*kW elements, or grad_weight's partial sums) and one
+ * for the tap-reversed weight of conv2d_forward.  Each is allocated
+ * stream-ordered on `stream` (hipMallocAsync) at the first call that needs
+ * it, grown when a later call needs more, and reused by later calls on that
+ * stream, which stream order keeps apart.  An internal lock is held while a
+ * call enqueues, so calls from several host threads on one stream are safe
+ * (they run in the order they took the lock).  Calls on different streams
+ * share no state.  conv2d_gi_release_workspaces frees the buffers
  * (call it before destroying a stream the library ran on, since a new stream
  * could receive the same handle).  Both convolution stride dimensions take `stride`; padding
  * is symmetric per dimension (pad_h top and bottom, pad_w left and right).
