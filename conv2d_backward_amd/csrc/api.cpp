@@ -1301,11 +1301,12 @@ int run_forward(const float *x, const float *w, float *y, const conv2d_gi_params
     }
     std::lock_guard<std::recursive_mutex> lock(g_ws_mu);
     void *ws = nullptr;
-    e = workspace_for(dev, stream, (size_t)std::max<int64_t>(n_w, 1) * 4, &ws);
+    e = workspace_for(dev, stream, (size_t)(n_w + gi::kFwdZeroTail) * 4, &ws);
     if (e != hipSuccess) return fail_hip(e);
     gi::FwdArgs a{};
     a.x = x;
     a.wt = (const float *)ws;
+    a.zero = (const float *)ws + n_w;
     a.y = y;
     a.N = p->N;
     a.Ci = p->Ci;
@@ -1340,7 +1341,8 @@ std::string describe_forward(const conv2d_gi_params &p) {
     }
     const int64_t npix = (int64_t)p.N * p.oH * p.oW;
     return "variant=fwd dtype=f32 ws_bytes=" +
-           std::to_string((int64_t)p.Co * p.Ci * p.kH * p.kW * 4) + " launches=2 [tiles=" +
+           std::to_string(((int64_t)p.Co * p.Ci * p.kH * p.kW + gi::kFwdZeroTail) * 4) +
+           " launches=2 [tiles=" +
            std::to_string((npix + gi::kFwdBN - 1) / gi::kFwdBN) + "x" +
            std::to_string((p.Co + gi::kFwdBM - 1) / gi::kFwdBM) + "]";
 }

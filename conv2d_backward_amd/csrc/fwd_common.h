@@ -23,6 +23,7 @@ namespace gi {
 struct FwdArgs {
     const float *x;    // [N, Ci, H, W]
     const float *wt;   // [kH*kW][Ci][Co] (prologue output)
+    const float *zero; // kFwdZeroTail zeros (prologue output): out-of-range lanes load here
     float *y;          // [N, Co, oH, oW]
     int32_t N, Ci, H, W, Co, kH, kW, stride, pad_h, pad_w, oH, oW;
 };
@@ -30,15 +31,19 @@ struct FwdArgs {
 constexpr int kFwdBM = 64;    // output channels per work-group
 constexpr int kFwdBN = 128;   // pixels per work-group
 constexpr int kFwdMaxFlatK = 2048;   // most K = Ci*kH*kW of the flattened K order
+constexpr int kFwdZeroTail = 16;     // zeros the weight reorders write after the weight
 
 // Weight reorders: w [Co, Ci, kH, kW] -> wt [kH*kW][Ci][Co] for the generic
-// forward kernel; and -> wf [Ci][Co][kH][kW] with the taps reversed, the
-// weight of the equivalent stride-1 grad_input problem (see api.cpp).
+// forward kernel (followed by kFwdZeroTail zeros: wt must hold
+// Co*Ci*kH*kW + kFwdZeroTail floats); and -> wf [Ci][Co][kH][kW] with the
+// taps reversed, the weight of the equivalent stride-1 grad_input problem
+// (see api.cpp).
 hipError_t launch_fwd_weight_tap_ci_co_f32(const float *w, float *wt, int Co, int Ci, int kHW,
                                            hipStream_t s);
 hipError_t launch_fwd_weight_flip_f32(const float *w, float *wf, int Co, int Ci, int kHW,
                                       hipStream_t s);
-// w [Co][K] -> wt [K][Co] (the flattened K order's A operand).
+// w [Co][K] -> wt [K][Co] (the flattened K order's A operand), followed by
+// kFwdZeroTail zeros.
 hipError_t launch_fwd_weight_k_co_f32(const float *w, float *wt, int Co, int K, hipStream_t s);
 // Whether the generic kernel takes K in the caller's (ci, kh, kw) order
 // (fewer than 16 input channels; its weight then comes from

@@ -14,13 +14,17 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 
 namespace {
 
-// wt[(tap*Ci + ci)*Co + co] = w[(co*Ci + ci)*kHW + tap]; one thread per
-// output element, writes coalesced.
+// wt[(tap*Ci + ci)*Co + co] = w[(co*Ci + ci)*kHW + tap], then kFwdZeroTail
+// zeros; one thread per output element, writes coalesced.
 __global__ __launch_bounds__(256) void fwd_weight_tap_ci_co_f32(const float *__restrict__ w,
                                                                 float *__restrict__ wt, int Co,
                                                                 int Ci, int kHW, int64_t total) {
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total + kFwdZeroTail;
          i += (int64_t)gridDim.x * 256) {
+        if (i >= total) {
+            wt[i] = 0.f;
+            continue;
+        }
         const int64_t co = i % Co;
         const int64_t ci = (i / Co) % Ci;
         const int64_t tap = i / ((int64_t)Ci * Co);
@@ -43,12 +47,17 @@ __global__ __launch_bounds__(256) void fwd_weight_flip_f32(const float *__restri
 }
 
 // wt[k*Co + co] = w[co*K + k] (K = Ci*kH*kW): the weight as [K][Co] with k in
-// the caller's (ci, kh, kw) order, for the flattened K axis.
+// the caller's (ci, kh, kw) order, for the flattened K axis; then
+// kFwdZeroTail zeros.
 __global__ __launch_bounds__(256) void fwd_weight_k_co_f32(const float *__restrict__ w,
                                                            float *__restrict__ wt, int Co, int K,
                                                            int64_t total) {
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total + kFwdZeroTail;
          i += (int64_t)gridDim.x * 256) {
+        if (i >= total) {
+            wt[i] = 0.f;
+            continue;
+        }
         const int64_t co = i % Co;
         const int64_t k = i / Co;
         wt[i] = w[co * K + k];
@@ -77,12 +86,15 @@ __device__ __forceinline__ int acc_row32(int r, int lane) {
 template <bool FLATK>
 __global__ __launch_bounds__(256) void gi_fwd_f32(const FwdArgs A) {
     constexpr int BM = kFwdBM, BN = kFwdBN, BK = 16, NT = 256;
-    constexpr int LDA = BM + 32, LDB = BN + 32;   // row pads keep half-waves on distinct banks
     constexpr int B_RPP = NT / BN, B_PT = BK / B_RPP;
     constexpr int A_RPP = NT / BM, A_PT = BK / A_RPP;
-    __shared__ float As[2][BK][LDA];
-    __shared__ float Bs[2][BK][LDB];
-    __shared__ int2 ktab[FLATK ? kFwdMaxFlatK : 1];   // (ci*H*W + kh*W + kw, kh << 16 | kw)
+    // No row pads: odd k rows store their columns XOR 32, so the two half
+    // waves of an MFMA operand read (rows k and k+1, same columns) fall on
+    // opposite halves of the 64 banks; a row write stays a bank permutation.
+    __shared__ float As[2][BK][BM];
+    __shared__ float Bs[2][BK][BN];
+    // FLATK: (ci*H*W + kh*W + kw, kh << 16 | kw) per k, sized K at launch.
+    extern __shared__ int2 ktab[];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     // Logical order: output-channel tile fastest, so the work-groups that
@@ -124,76 +136,113 @@ __global__ __launch_bounds__(256) void gi_fwd_f32(const FwdArgs A) {
     const int ac = tid % BM, ka0 = tid / BM;
     const bool ain = co0 + ac < A.Co;
 
-    float ra[A_PT], rb[B_PT];
-    auto gload_flat = [&](int it) {
-        const int base = ih0 * A.W + iw0;
-#pragma unroll
-        for (int i = 0; i < B_PT; ++i) {
-            const int k = it * BK + kb0 + i * B_RPP;
-            float v = 0.f;
-            if (pin && k < K) {
-                const int2 e = ktab[k];
-                const int kh = e.y >> 16, kw = e.y & 0xffff;
-                if ((unsigned)(ih0 + kh) < (unsigned)A.H && (unsigned)(iw0 + kw) < (unsigned)A.W)
-                    v = ximg[e.x + base];
-            }
-            rb[i] = v;
-        }
-#pragma unroll
-        for (int i = 0; i < A_PT; ++i) {
-            const int k = it * BK + ka0 + i * A_RPP;
-            ra[i] = (ain && k < K) ? A.wt[(int64_t)k * A.Co + co0 + ac] : 0.f;
-        }
-    };
-    auto gload = [&](int it) {
+    // Every global load is issued unconditionally; an out-of-range lane
+    // loads from the zeros after the reordered weight, so nothing touches the
+    // loaded registers until they are stored to LDS after the step's MFMAs
+    // (a select on the loaded value would make the compiler wait for the
+    // loads in the middle of them).
+    typedef float RegA[A_PT];
+    typedef float RegB[B_PT];
+    struct {
+        int kh, kw, ci0;
+    } nk = {0, 0, 0};   // position of the next tap-major step to load
+    auto gload = [&](int it, RegA &ra, RegB &rb) {
         if (FLATK) {
-            gload_flat(it);
+            const int base = ih0 * A.W + iw0;
+            // k is the same across a wave: the step's table entries are read
+            // up front (broadcast reads, one wait), not one per load.
+            int2 e[B_PT];
+#pragma unroll
+            for (int i = 0; i < B_PT; ++i) {
+                const int k = it * BK + kb0 + i * B_RPP;
+                e[i] = ktab[k < K ? k : K - 1];
+                __asm__ volatile("" : : "v"(e[i].x), "v"(e[i].y));
+            }
+#pragma unroll
+            for (int i = 0; i < B_PT; ++i) {
+                const int k = it * BK + kb0 + i * B_RPP;
+                const int kh = e[i].y >> 16, kw = e[i].y & 0xffff;
+                const bool ok = pin && k < K && (unsigned)(ih0 + kh) < (unsigned)A.H &&
+                                (unsigned)(iw0 + kw) < (unsigned)A.W;
+                rb[i] = *(ok ? ximg + (e[i].x + base) : A.zero);
+            }
+#pragma unroll
+            for (int i = 0; i < A_PT; ++i) {
+                const int k = it * BK + ka0 + i * A_RPP;
+                const bool ok = ain && k < K;
+                ra[i] = *(ok ? A.wt + ((int64_t)k * A.Co + co0 + ac) : A.zero);
+            }
             return;
         }
-        const int tap = it / nci;
-        const int ci0 = (it - tap * nci) * BK;
-        const int kh = tap / A.kW, kw = tap - (tap / A.kW) * A.kW;
+        // Steps are loaded in order: (kh, kw, ci0) advance by one channel
+        // block per call instead of being divided out of it.
+        const bool live = it < T;
+        const int kh = nk.kh, kw = nk.kw, ci0 = nk.ci0, tap = kh * A.kW + kw;
+        nk.ci0 += BK;
+        if (nk.ci0 >= A.Ci) {
+            nk.ci0 = 0;
+            if (++nk.kw == A.kW) {
+                nk.kw = 0;
+                ++nk.kh;
+            }
+        }
         const int ih = ih0 + kh, iw = iw0 + kw;
-        const bool v = pin && ih >= 0 && ih < A.H && iw >= 0 && iw < A.W;
+        const bool v = live && pin && ih >= 0 && ih < A.H && iw >= 0 && iw < A.W;
         const int off = v ? ih * A.W + iw : 0;
 #pragma unroll
         for (int i = 0; i < B_PT; ++i) {
             const int ci = ci0 + kb0 + i * B_RPP;
-            rb[i] = (v && ci < A.Ci) ? ximg[(int64_t)ci * HW + off] : 0.f;
+            const bool ok = v && ci < A.Ci;
+            rb[i] = *(ok ? ximg + ((int64_t)ci * HW + off) : A.zero);
         }
-        const float *ws = A.wt + (int64_t)tap * A.Ci * A.Co + co0 + ac;
 #pragma unroll
         for (int i = 0; i < A_PT; ++i) {
             const int ci = ci0 + ka0 + i * A_RPP;
-            ra[i] = (ain && ci < A.Ci) ? ws[(int64_t)ci * A.Co] : 0.f;
+            const bool ok = live && ain && ci < A.Ci;
+            ra[i] = *(ok ? A.wt + (((int64_t)tap * A.Ci + ci) * A.Co + co0 + ac) : A.zero);
         }
     };
-    auto sstore = [&](int buf) {
+    auto sw = [](int row, int col) { return col ^ ((row & 1) << 5); };
+    auto sstore = [&](int buf, const RegA &ra, const RegB &rb) {
 #pragma unroll
-        for (int i = 0; i < A_PT; ++i) As[buf][ka0 + i * A_RPP][ac] = ra[i];
+        for (int i = 0; i < A_PT; ++i) {
+            const int r = ka0 + i * A_RPP;
+            As[buf][r][sw(r, ac)] = ra[i];
+        }
 #pragma unroll
-        for (int i = 0; i < B_PT; ++i) Bs[buf][kb0 + i * B_RPP][pc] = rb[i];
+        for (int i = 0; i < B_PT; ++i) {
+            const int r = kb0 + i * B_RPP;
+            Bs[buf][r][sw(r, pc)] = rb[i];
+        }
     };
 
     v16f acc0 = {}, acc1 = {};
     const int wm = wave >> 1, wn = wave & 1;
     const int kl = lane >> 5, ml = lane & 31;
+    auto mma = [&](int cur) {
+#pragma unroll
+        for (int kk = 0; kk < BK; kk += 2) {
+            // Row kk + kl with kk even: the swizzle is XOR 32 for kl = 1.
+            const int x = kl << 5;
+            const float af = As[cur][kk + kl][(wm * 32 + ml) ^ x];
+            const float b0 = Bs[cur][kk + kl][(wn * 64 + ml) ^ x];
+            const float b1 = Bs[cur][kk + kl][(wn * 64 + 32 + ml) ^ x];
+            acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(af, b0, acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(af, b1, acc1, 0, 0, 0);
+        }
+    };
+    // Two register sets: step it + 2 is loaded while step it multiplies out
+    // of one LDS buffer and step it + 1 moves into the other.
     if (T > 0) {
-        gload(0);
-        sstore(0);
+        RegA ra;
+        RegB rb;
+        gload(0, ra, rb);
+        sstore(0, ra, rb);
         __syncthreads();
         for (int it = 0; it < T; ++it) {
-            const int cur = it & 1;
-            if (it + 1 < T) gload(it + 1);
-#pragma unroll
-            for (int kk = 0; kk < BK; kk += 2) {
-                const float af = As[cur][kk + kl][wm * 32 + ml];
-                const float b0 = Bs[cur][kk + kl][wn * 64 + ml];
-                const float b1 = Bs[cur][kk + kl][wn * 64 + 32 + ml];
-                acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(af, b0, acc0, 0, 0, 0);
-                acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(af, b1, acc1, 0, 0, 0);
-            }
-            if (it + 1 < T) sstore(cur ^ 1);
+            gload(it + 1, ra, rb);
+            mma(it & 1);
+            sstore((it & 1) ^ 1, ra, rb);
             __syncthreads();
         }
     }
@@ -218,8 +267,8 @@ __global__ __launch_bounds__(256) void gi_fwd_f32(const FwdArgs A) {
 hipError_t launch_fwd_weight_tap_ci_co_f32(const float *w, float *wt, int Co, int Ci, int kHW,
                                            hipStream_t s) {
     const int64_t total = (int64_t)Co * Ci * kHW;
-    hipLaunchKernelGGL(fwd_weight_tap_ci_co_f32, dim3(reorder_blocks(total)), dim3(256), 0, s, w,
-                       wt, Co, Ci, kHW, total);
+    hipLaunchKernelGGL(fwd_weight_tap_ci_co_f32, dim3(reorder_blocks(total + kFwdZeroTail)),
+                       dim3(256), 0, s, w, wt, Co, Ci, kHW, total);
     return hipGetLastError();
 }
 
@@ -233,8 +282,8 @@ hipError_t launch_fwd_weight_flip_f32(const float *w, float *wf, int Co, int Ci,
 
 hipError_t launch_fwd_weight_k_co_f32(const float *w, float *wt, int Co, int K, hipStream_t s) {
     const int64_t total = (int64_t)Co * K;
-    hipLaunchKernelGGL(fwd_weight_k_co_f32, dim3(reorder_blocks(total)), dim3(256), 0, s, w, wt,
-                       Co, K, total);
+    hipLaunchKernelGGL(fwd_weight_k_co_f32, dim3(reorder_blocks(total + kFwdZeroTail)),
+                       dim3(256), 0, s, w, wt, Co, K, total);
     return hipGetLastError();
 }
 
@@ -248,9 +297,11 @@ hipError_t launch_fwd_generic_f32(const FwdArgs &a, hipStream_t s, const KernelE
     const int64_t wgs = (npix + kFwdBN - 1) / kFwdBN * ((a.Co + kFwdBM - 1) / kFwdBM);
     if (wgs > INT32_MAX) return hipErrorInvalidValue;
     const dim3 grid((unsigned)wgs);
-    if (fwd_flat_k(a))
-        hipExtLaunchKernelGGL(gi_fwd_f32<true>, grid, dim3(256), 0, s, ev.start, ev.stop, 0, a);
-    else
+    if (fwd_flat_k(a)) {
+        const size_t ktab = (size_t)a.Ci * a.kH * a.kW * sizeof(int2);
+        hipExtLaunchKernelGGL(gi_fwd_f32<true>, grid, dim3(256), ktab, s, ev.start, ev.stop, 0,
+                              a);
+    } else
         hipExtLaunchKernelGGL(gi_fwd_f32<false>, grid, dim3(256), 0, s, ev.start, ev.stop, 0, a);
     return hipGetLastError();
 }
