@@ -16,10 +16,11 @@ namespace gi {
 //   y[n,co,oh,ow] = sum over ci, kh, kw of
 //                   x[n,ci,oh*stride-pad_h+kh, ow*stride-pad_w+kw] * w[co,ci,kh,kw]
 //
-// as an implicit GEMM C[co, pixel] = A[co, k] * B[k, pixel] with k = (tap,
-// ci), tap-major: A from the weight reordered to wt[(tap*Ci + ci)*Co + co]
-// (co fastest), B gathered from x per tap (0 outside the image); pixels of
-// all images folded into the column axis.
+// as an implicit GEMM C[co, pixel] = A[co, k] * B[k, pixel] with k = (block
+// of 16 input channels, tap, channel in the block): A from the weight
+// reordered to wt[(tap*Ci + ci)*Co + co] (co fastest), B gathered from x per
+// tap (0 outside the image); pixels of all images folded into the column
+// axis.
 struct FwdArgs {
     const float *x;    // [N, Ci, H, W]
     const float *wt;   // [kH*kW][Ci][Co] (prologue output)

@@ -78,8 +78,9 @@ __device__ __forceinline__ int acc_row32(int r, int lane) {
 // Generic forward kernel: 256 threads, tile 64 co x 128 pixels, K step 16.
 // Waves form 2 x 2; each owns 32 co x 64 pixels = two V_MFMA_F32_32X32X2_F32
 // accumulators.  Global tiles are prefetched into registers one K step ahead
-// and double-buffered in LDS.  K order: FLATK = false, (tap, ci) with a K
-// step = one tap x 16 input channels (one bounds test per pixel and step);
+// and double-buffered in LDS.  K order: FLATK = false, (ci block of 16, tap)
+// with a K step = one tap x 16 input channels (one bounds test per pixel and
+// step);
 // FLATK = true, the caller's (ci, kh, kw) order (few input channels: no
 // padding of Ci to 16), each k's plane offset and tap read from an LDS table.
 // ---------------------------------------------------------------------------
@@ -174,16 +175,18 @@ __global__ __launch_bounds__(256) void gi_fwd_f32(const FwdArgs A) {
             }
             return;
         }
-        // Steps are loaded in order: (kh, kw, ci0) advance by one channel
-        // block per call instead of being divided out of it.
+        // Steps are loaded in order, channel block outer and tap inner: the
+        // kH*kW consecutive steps of one block gather from the same input
+        // rows, which stay in cache (tap-major order swept every channel
+        // between two taps and re-fetched the input from HBM per tap).
+        // (kh, kw, ci0) advance per call instead of being divided out of it.
         const bool live = it < T;
         const int kh = nk.kh, kw = nk.kw, ci0 = nk.ci0, tap = kh * A.kW + kw;
-        nk.ci0 += BK;
-        if (nk.ci0 >= A.Ci) {
-            nk.ci0 = 0;
-            if (++nk.kw == A.kW) {
-                nk.kw = 0;
-                ++nk.kh;
+        if (++nk.kw == A.kW) {
+            nk.kw = 0;
+            if (++nk.kh == A.kH) {
+                nk.kh = 0;
+                nk.ci0 += BK;
             }
         }
         const int ih = ih0 + kh, iw = iw0 + kw;
