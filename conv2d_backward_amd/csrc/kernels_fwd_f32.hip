@@ -84,7 +84,7 @@ __device__ __forceinline__ int acc_row32(int r, int lane) {
 // FLATK = true, the caller's (ci, kh, kw) order (few input channels: no
 // padding of Ci to 16), each k's plane offset and tap read from an LDS table.
 // ---------------------------------------------------------------------------
-template <bool FLATK>
+template <bool FLATK, bool VECA>
 __global__ __launch_bounds__(256) void gi_fwd_f32(const FwdArgs A) {
     constexpr int BM = kFwdBM, BN = kFwdBN, BK = 16, NT = 256;
     constexpr int B_RPP = NT / BN, B_PT = BK / B_RPP;
@@ -92,8 +92,8 @@ __global__ __launch_bounds__(256) void gi_fwd_f32(const FwdArgs A) {
     // No row pads: odd k rows store their columns XOR 32, so the two half
     // waves of an MFMA operand read (rows k and k+1, same columns) fall on
     // opposite halves of the 64 banks; a row write stays a bank permutation.
-    __shared__ float As[2][BK][BM];
-    __shared__ float Bs[2][BK][BN];
+    __shared__ __attribute__((aligned(16))) float As[2][BK][BM];
+    __shared__ __attribute__((aligned(16))) float Bs[2][BK][BN];
     // FLATK: (ci*H*W + kh*W + kw, kh << 16 | kw) per k, sized K at launch.
     extern __shared__ int2 ktab[];
 
@@ -133,9 +133,16 @@ __global__ __launch_bounds__(256) void gi_fwd_f32(const FwdArgs A) {
     }
     const int ih0 = oh * A.stride - A.pad_h, iw0 = ow * A.stride - A.pad_w;
     const float *ximg = A.x + (int64_t)n * A.Ci * HW;
-    // A load assignment: one co column, rows ka0, ka0 + A_RPP, ...
+    // A load assignment.  Co % 4 == 0 (VECA): four consecutive co of row
+    // ka4, one 16-byte load (a group lies wholly below or above Co, and the
+    // weight rows and the zero tail are 16-byte aligned).  Otherwise one co
+    // column at rows ka0, ka0 + A_RPP, ...: four 4-byte loads.
     const int ac = tid % BM, ka0 = tid / BM;
     const bool ain = co0 + ac < A.Co;
+    constexpr int A_CG = BM / 4;
+    static_assert(A_PT == 4 && NT / A_CG == BK, "one 16-byte A load per thread and step");
+    const int ac4 = (tid % A_CG) * 4, ka4 = tid / A_CG;
+    const bool ain4 = co0 + ac4 < A.Co;
 
     // Every global load is issued unconditionally; an out-of-range lane
     // loads from the zeros after the reordered weight, so nothing touches the
@@ -146,7 +153,7 @@ __global__ __launch_bounds__(256) void gi_fwd_f32(const FwdArgs A) {
     typedef float RegB[B_PT];
     struct {
         int kh, kw, ci0;
-    } nk = {0, 0, 0};   // position of the next tap-major step to load
+    } nk = {0, 0, 0};   // position of the next step to load (FLATK = false)
     auto gload = [&](int it, RegA &ra, RegB &rb) {
         if (FLATK) {
             const int base = ih0 * A.W + iw0;
@@ -166,6 +173,17 @@ __global__ __launch_bounds__(256) void gi_fwd_f32(const FwdArgs A) {
                 const bool ok = pin && k < K && (unsigned)(ih0 + kh) < (unsigned)A.H &&
                                 (unsigned)(iw0 + kw) < (unsigned)A.W;
                 rb[i] = *(ok ? ximg + (e[i].x + base) : A.zero);
+            }
+            if (VECA) {
+                const int k = it * BK + ka4;
+                const bool ok = ain4 && k < K;
+                const float4 w4 = *(const float4 *)(ok ? A.wt + ((int64_t)k * A.Co + co0 + ac4)
+                                                       : A.zero);
+                ra[0] = w4.x;
+                ra[1] = w4.y;
+                ra[2] = w4.z;
+                ra[3] = w4.w;
+                return;
             }
 #pragma unroll
             for (int i = 0; i < A_PT; ++i) {
@@ -198,6 +216,17 @@ __global__ __launch_bounds__(256) void gi_fwd_f32(const FwdArgs A) {
             const bool ok = v && ci < A.Ci;
             rb[i] = *(ok ? ximg + ((int64_t)ci * HW + off) : A.zero);
         }
+        if (VECA) {
+            const int ci = ci0 + ka4;
+            const bool ok = live && ain4 && ci < A.Ci;
+            const float4 w4 = *(const float4 *)(
+                ok ? A.wt + (((int64_t)tap * A.Ci + ci) * A.Co + co0 + ac4) : A.zero);
+            ra[0] = w4.x;
+            ra[1] = w4.y;
+            ra[2] = w4.z;
+            ra[3] = w4.w;
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < A_PT; ++i) {
             const int ci = ci0 + ka0 + i * A_RPP;
@@ -207,10 +236,14 @@ __global__ __launch_bounds__(256) void gi_fwd_f32(const FwdArgs A) {
     };
     auto sw = [](int row, int col) { return col ^ ((row & 1) << 5); };
     auto sstore = [&](int buf, const RegA &ra, const RegB &rb) {
+        if (VECA) {
+            *(float4 *)&As[buf][ka4][sw(ka4, ac4)] = make_float4(ra[0], ra[1], ra[2], ra[3]);
+        } else {
 #pragma unroll
-        for (int i = 0; i < A_PT; ++i) {
-            const int r = ka0 + i * A_RPP;
-            As[buf][r][sw(r, ac)] = ra[i];
+            for (int i = 0; i < A_PT; ++i) {
+                const int r = ka0 + i * A_RPP;
+                As[buf][r][sw(r, ac)] = ra[i];
+            }
         }
 #pragma unroll
         for (int i = 0; i < B_PT; ++i) {
@@ -300,12 +333,22 @@ hipError_t launch_fwd_generic_f32(const FwdArgs &a, hipStream_t s, const KernelE
     const int64_t wgs = (npix + kFwdBN - 1) / kFwdBN * ((a.Co + kFwdBM - 1) / kFwdBM);
     if (wgs > INT32_MAX) return hipErrorInvalidValue;
     const dim3 grid((unsigned)wgs);
+    const bool veca = a.Co % 4 == 0;
     if (fwd_flat_k(a)) {
         const size_t ktab = (size_t)a.Ci * a.kH * a.kW * sizeof(int2);
-        hipExtLaunchKernelGGL(gi_fwd_f32<true>, grid, dim3(256), ktab, s, ev.start, ev.stop, 0,
-                              a);
-    } else
-        hipExtLaunchKernelGGL(gi_fwd_f32<false>, grid, dim3(256), 0, s, ev.start, ev.stop, 0, a);
+        if (veca)
+            hipExtLaunchKernelGGL(gi_fwd_f32<true, true>, grid, dim3(256), ktab, s, ev.start,
+                                  ev.stop, 0, a);
+        else
+            hipExtLaunchKernelGGL(gi_fwd_f32<true, false>, grid, dim3(256), ktab, s, ev.start,
+                                  ev.stop, 0, a);
+    } else if (veca) {
+        hipExtLaunchKernelGGL(gi_fwd_f32<false, true>, grid, dim3(256), 0, s, ev.start, ev.stop,
+                              0, a);
+    } else {
+        hipExtLaunchKernelGGL(gi_fwd_f32<false, false>, grid, dim3(256), 0, s, ev.start, ev.stop,
+                              0, a);
+    }
     return hipGetLastError();
 }
 
