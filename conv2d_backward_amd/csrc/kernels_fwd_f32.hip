@@ -277,6 +277,10 @@ __global__ __launch_bounds__(256) void gi_fwd_f32(const FwdArgs A) {
         __syncthreads();
         for (int it = 0; it < T; ++it) {
             gload(it + 1, ra, rb);
+            // Keep every load of the next step above this step's MFMAs (the
+            // scheduler otherwise sinks some next to their LDS store, where
+            // the wait for them exposes their whole latency).
+            __builtin_amdgcn_sched_barrier(0);
             mma(it & 1);
             sstore((it & 1) ^ 1, ra, rb);
             __syncthreads();
