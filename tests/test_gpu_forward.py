@@ -144,3 +144,45 @@ def test_forward_workload_sampled(name):
     idx = rng.integers(0, got.size, size=200)
     ref, Ss = oracle.conv2d_forward_at(x, w, sh.stride, (sh.pad_h, sh.pad_w), idx)
     check(got.ravel()[idx], ref, Ss, name)
+
+
+def test_forward_threads_one_stream():
+    """Forward calls from four host threads on the same stream, each with its
+    own weight: the stride-1 path stages the tap-reversed weight in a scratch
+    slot shared per stream, so a call must keep the slot until its
+    grad_input kernel is enqueued.  Every call writes its own output, and
+    every output is checked against the oracle."""
+    import threading
+    sh = S(2, 16, 10, 10, 24, 3, 3, 1, 1, 1)
+    dev = torch.device("cuda:0")
+    nthreads, calls = 4, 8
+    rng = np.random.default_rng(8300)
+    x = rng.standard_normal(sh.dst_shape).astype(np.float32)
+    ws = [rng.standard_normal(sh.weight_shape).astype(np.float32) for _ in range(nthreads)]
+    tx = torch.from_numpy(x).to(dev)
+    tws = [torch.from_numpy(w).to(dev) for w in ws]
+    outs = [[torch.full(sh.grad_out_shape, float("nan"), device=dev) for _ in range(calls)]
+            for _ in range(nthreads)]
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    errors = []
+
+    def worker(t):
+        try:
+            for c in range(calls):
+                gi.forward(tx, tws[t], stride=1, padding=1, out=outs[t][c], stream=stream)
+        except Exception as e:  # reported after the join
+            errors.append(e)
+
+    say("forward threads: %d threads x %d calls, shape %s" % (nthreads, calls, sh))
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(nthreads)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for t in range(nthreads):
+        ref, Ss = oracle.conv2d_forward_abs(x, ws[t], sh.stride, (sh.pad_h, sh.pad_w))
+        for c in range(calls):
+            check(outs[t][c].double().cpu().numpy(), ref, Ss, "thread %d call %d" % (t, c))
