@@ -76,6 +76,13 @@ SHAPES = [
     S(1, 4, 12, 13, 8, 2, 3, 3, 1, 1),       # stride 3, even kernel height
     S(2, 5, 11, 10, 3, 5, 5, 1, 2, 2),       # Co = 3 (grad_input path: its stem kernel)
     S(3, 33, 7, 6, 130, 3, 2, 2, 1, 0),      # ragged channel tiles, asymmetric pads
+    # Generic-kernel paths: channel-block-major K with kH != kW, 16-byte weight
+    # loads (Co % 4 == 0) with a partial output-channel tile, the flattened K
+    # just below 16 input channels, an odd output width, a partial last
+    # channel block.
+    S(2, 16, 9, 11, 68, 2, 3, 3, 1, 1),      # Ci = 16: one block; Co = 68: 64 + 4
+    S(1, 15, 10, 10, 4, 3, 3, 2, 1, 1),      # Ci = 15: flattened K; Co = 4; oW = 5
+    S(2, 40, 9, 9, 36, 3, 3, 2, 0, 0),       # blocks of 16, 16, 8 channels; Co = 36
 ]
 
 
