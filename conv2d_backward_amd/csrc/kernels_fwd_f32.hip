@@ -80,9 +80,9 @@ __device__ __forceinline__ int acc_row32(int r, int lane) {
 // accumulators.  Global tiles are prefetched into registers one K step ahead
 // and double-buffered in LDS.  K order: FLATK = false, (ci block of 16, tap)
 // with a K step = one tap x 16 input channels (one bounds test per pixel and
-// step);
-// FLATK = true, the caller's (ci, kh, kw) order (few input channels: no
-// padding of Ci to 16), each k's plane offset and tap read from an LDS table.
+// step); FLATK = true, the caller's (ci, kh, kw) order (few input channels:
+// no padding of Ci to 16), each k's plane offset and tap read from an LDS
+// table.  VECA (Co % 4 == 0): the weight tile is loaded 16 bytes per thread.
 // ---------------------------------------------------------------------------
 template <bool FLATK, bool VECA>
 __global__ __launch_bounds__(256) void gi_fwd_f32(const FwdArgs A) {
@@ -158,7 +158,10 @@ __global__ __launch_bounds__(256) void gi_fwd_f32(const FwdArgs A) {
         if (FLATK) {
             const int base = ih0 * A.W + iw0;
             // k is the same across a wave: the step's table entries are read
-            // up front (broadcast reads, one wait), not one per load.
+            // up front (broadcast reads, one wait), not one per load.  The
+            // empty asm statement uses both halves of each entry, so the
+            // compiler cannot sink a half of the read into the branch of the
+            // lanes that need it (which made one LDS wait per element).
             int2 e[B_PT];
 #pragma unroll
             for (int i = 0; i < B_PT; ++i) {
