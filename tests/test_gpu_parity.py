@@ -59,6 +59,10 @@ def run_gpu(g_np, w_np, shape, dtype, variant=gi.VARIANT_AUTO, stream=None):
     buf[GUARD:GUARD + n_dst] = float("nan")
     out = buf[GUARD:GUARD + n_dst].view(shape.dst_shape)
     old = gi.set_variant(variant)
+    if stream is not None:
+        # The library orders work within the caller's stream only: the fills
+        # above are queued on the current stream, so the side stream waits.
+        stream.wait_stream(torch.cuda.current_stream())
     try:
         gi.grad_input(g, w, stride=shape.stride, padding=(shape.pad_h, shape.pad_w),
                       input_hw=(shape.H, shape.W), out=out, stream=stream)
