@@ -25,8 +25,11 @@
  * The doppler kernel has one batch item and one pad; meganeura carries the
  * batch on the grid and separate pad_h / pad_w.  Both are merged here: N
  * independent batch items, per-dimension symmetric zero padding, one stride
- * for both dimensions.  The sign test comes before the divisibility test, as
- * in both pages, so C's sign-following remainder never sees a negative value.
+ * for both dimensions.  Rather than testing every tap against the three
+ * conditions, each element enumerates the output rows and columns whose
+ * forward window covered it (a range per dimension, from the forward mapping
+ * below) and recovers each term's tap from that mapping: the same terms, so
+ * the same sum.
  *
  * abs_sum[n,ci,ih,iw] = the same sum of |grad_out * weight| (used to scale the
  * floating-point tolerance of a GPU result).
@@ -88,29 +91,47 @@ static shape_t make_shape(int N, int Ci, int H, int W, int Co, int kH, int kW,
     return s;
 }
 
-/* One grad_input element, straight from the definition above. */
+/*
+ * Along one dimension: the output positions whose forward window covered
+ * input index i.  Output position o reads input index o*stride - pad + k for
+ * the taps k in [0, K), so o covers i exactly when k = i + pad - o*stride
+ * lies in [0, K), i.e. when i + pad - K < o*stride <= i + pad.  The first
+ * such o is ceil((i + pad - K + 1) / stride), at least 0; the last is
+ * floor((i + pad) / stride), at most out - 1.  lo > hi means none.
+ */
+static void covering_outputs(int64_t i, int64_t pad, int64_t K, int64_t stride,
+                             int64_t out, int64_t *lo, int64_t *hi)
+{
+    const int64_t top = i + pad;          /* >= 0: i and pad are */
+    const int64_t bottom = top - K + 1;   /* may be negative */
+    *lo = bottom <= 0 ? 0 : (bottom + stride - 1) / stride;
+    *hi = top / stride;
+    if (*hi > out - 1) *hi = out - 1;
+}
+
+/*
+ * One grad_input element: the sum over output channels of every output
+ * gradient value this input pixel fed in the forward pass, each times the
+ * weight tap that carried it.  The covering output rows and columns come
+ * from covering_outputs; the tap is recovered from the forward mapping.
+ */
 static void grad_input_element(const double *grad_out, const double *weight,
                                const shape_t *s, int64_t n, int64_t ci,
                                int64_t ih, int64_t iw, double *value,
                                double *abs_value)
 {
+    int64_t oh_lo, oh_hi, ow_lo, ow_hi;
+    covering_outputs(ih, s->pad_h, s->kH, s->stride, s->oH, &oh_lo, &oh_hi);
+    covering_outputs(iw, s->pad_w, s->kW, s->stride, s->oW, &ow_lo, &ow_hi);
     double acc = 0.0, acc_abs = 0.0;
     for (int64_t co = 0; co < s->Co; ++co) {
-        for (int64_t kh = 0; kh < s->kH; ++kh) {
-            int64_t a = ih + s->pad_h - kh;
-            if (a < 0) continue;
-            if (a % s->stride != 0) continue;
-            int64_t oh = a / s->stride;
-            if (oh >= s->oH) continue;
-            for (int64_t kw = 0; kw < s->kW; ++kw) {
-                int64_t b = iw + s->pad_w - kw;
-                if (b < 0) continue;
-                if (b % s->stride != 0) continue;
-                int64_t ow = b / s->stride;
-                if (ow >= s->oW) continue;
-                double g = grad_out[((n * s->Co + co) * s->oH + oh) * s->oW + ow];
-                double w = weight[((co * s->Ci + ci) * s->kH + kh) * s->kW + kw];
-                double t = g * w;
+        const double *g_plane = grad_out + (n * s->Co + co) * s->oH * s->oW;
+        const double *w_taps = weight + (co * s->Ci + ci) * s->kH * s->kW;
+        for (int64_t oh = oh_lo; oh <= oh_hi; ++oh) {
+            const int64_t kh = ih + s->pad_h - oh * s->stride;
+            for (int64_t ow = ow_lo; ow <= ow_hi; ++ow) {
+                const int64_t kw = iw + s->pad_w - ow * s->stride;
+                const double t = g_plane[oh * s->oW + ow] * w_taps[kh * s->kW + kw];
                 acc += t;
                 acc_abs += fabs(t);
             }

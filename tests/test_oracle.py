@@ -295,29 +295,65 @@ def test_bf16_rounding_is_nearest_even():
 # ----------------------------------------------------------------------------
 
 MUTANTS = {
-    # wrong sign of the tap offset in the row gather
-    "kh_sign": ("int64_t a = ih + s->pad_h - kh;", "int64_t a = ih - s->pad_h + kh;"),
-    # dropped stride-divisibility test in w
-    "no_w_divisibility": ("if (b % s->stride != 0) continue;", ""),
+    # the tap row read mirrored (kh' = kH-1-kh): a rotated-kernel mix-up in one dimension
+    "kh_mirrored": ("const int64_t kh = ih + s->pad_h - oh * s->stride;",
+                    "const int64_t kh = s->kH - 1 - (ih + s->pad_h - oh * s->stride);"),
+    # the first covering output rounded down instead of up (keeps a position
+    # whose window ends before the pixel)
+    "lo_floor": ("*lo = bottom <= 0 ? 0 : (bottom + stride - 1) / stride;",
+                 "*lo = bottom <= 0 ? 0 : bottom / stride;"),
+    # the stride dropped when recovering the tap column
+    "kw_no_stride": ("const int64_t kw = iw + s->pad_w - ow * s->stride;",
+                     "const int64_t kw = iw + s->pad_w - ow;"),
     # weight read as [Ci,Co,...] (transposed operand)
-    "weight_transposed": ("weight[((co * s->Ci + ci) * s->kH + kh) * s->kW + kw]",
-                          "weight[((ci * s->Co + co) * s->kH + kh) * s->kW + kw]"),
+    "weight_transposed": ("weight + (co * s->Ci + ci) * s->kH * s->kW;",
+                          "weight + (ci * s->Co + co) * s->kH * s->kW;"),
     # kernel rotated by 180 degrees (the transposed-conv view applied twice)
-    "weight_rotated": ("* s->kH + kh) * s->kW + kw]",
-                       "* s->kH + (s->kH - 1 - kh)) * s->kW + (s->kW - 1 - kw)]"),
-    # pad_w used for both dimensions
-    "pad_h_from_w": ("int64_t a = ih + s->pad_h - kh;", "int64_t a = ih + s->pad_w - kh;"),
-    # off-by-one output bound
-    "oh_bound": ("if (oh >= s->oH) continue;", "if (oh > s->oH) continue;"),
+    "weight_rotated": ("w_taps[kh * s->kW + kw]",
+                       "w_taps[(s->kH - 1 - kh) * s->kW + (s->kW - 1 - kw)]"),
+    # pad_w used for the row range
+    "pad_h_from_w": ("covering_outputs(ih, s->pad_h,", "covering_outputs(ih, s->pad_w,"),
+    # off-by-one clip of the last covering output
+    "hi_bound": ("if (*hi > out - 1) *hi = out - 1;", "if (*hi > out) *hi = out;"),
     # a dropped channel (loop stops one short)
-    "drop_last_co": ("for (int64_t co = 0; co < s->Co; ++co)",
-                     "for (int64_t co = 0; co < s->Co - 1; ++co)"),
+    "drop_last_co": ("for (int64_t co = 0; co < s->Co; ++co) {\n        const double *g_plane",
+                     "for (int64_t co = 0; co < s->Co - 1; ++co) {\n        const double *g_plane"),
     # the abs-sum accumulates signed terms
-    "abs_sum_signed": ("double t = g * w;\n                acc += t;\n                acc_abs += fabs(t);",
-                       "double t = g * w;\n                acc += t;\n                acc_abs += t;"),
+    "abs_sum_signed": ("w_taps[kh * s->kW + kw];\n                acc += t;\n                acc_abs += fabs(t);",
+                       "w_taps[kh * s->kW + kw];\n                acc += t;\n                acc_abs += t;"),
     # the sampled entry point decodes the flat index with H and W swapped
     "at_index_swap": ("int64_t ih = (f / s.W) % s.H;", "int64_t ih = (f / s.H) % s.W;"),
 }
+
+# Run a mutant's pins in a child process: a planted mistake may index outside
+# an array, and a crash there must fail the mutant, not the test run.
+_RUN_PINS = r"""
+import sys
+sys.path[:0] = [sys.argv[1], sys.argv[2]]
+import oracle, test_oracle
+m = oracle.Oracle(sys.argv[3])
+caught = []
+for pin in test_oracle.ALL_PINS + [test_oracle.test_abs_sum_bounds_value]:
+    try:
+        pin(m)
+    except AssertionError:
+        caught.append(pin.__name__)
+print("CAUGHT " + ",".join(caught))
+"""
+
+
+def mutant_caught_by(lib_path):
+    """Names of the pins the library at lib_path fails ("crashed" when the
+    child process dies before it can report)."""
+    import subprocess
+    import sys
+    here = os.path.dirname(os.path.abspath(__file__))
+    r = subprocess.run([sys.executable, "-c", _RUN_PINS, os.path.dirname(here), here, lib_path],
+                       capture_output=True, text=True, timeout=600)
+    lines = [l for l in r.stdout.splitlines() if l.startswith("CAUGHT ")]
+    if r.returncode != 0 or not lines:
+        return ["crashed (exit %d)" % r.returncode]
+    return [n for n in lines[-1][len("CAUGHT "):].split(",") if n]
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
@@ -329,11 +365,5 @@ def test_mutant_is_caught(tmp_path, name):
     cpath = tmp_path / ("mut_%s.c" % name)
     cpath.write_text(mutated)
     lib = oracle.compile_library(str(cpath), str(tmp_path / ("libmut_%s.so" % name)))
-    m = oracle.Oracle(lib)
-    caught = []
-    for pin in ALL_PINS + [test_abs_sum_bounds_value]:
-        try:
-            pin(m)
-        except AssertionError:
-            caught.append(pin.__name__)
+    caught = mutant_caught_by(lib)
     assert caught, "mutant %s passed every pin" % name
