@@ -8,7 +8,8 @@ If the library has not been built, importing works but every call raises
     from conv2d_backward_amd import grad_input
     dx = grad_input(dy, w, stride=2, padding=(1, 1), input_hw=(56, 56))
 
-The C entry points mirror these names (see include/conv2d_grad_input.h).
+The C entry points mirror these names (include/conv2d_grad_input.h; the test
+hooks are in include/conv2d_grad_input_testing.h and are thread-local).
 """
 from __future__ import annotations
 
@@ -62,7 +63,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
             "%s is missing: build it with `python -m conv2d_backward_amd.build`" % p)
     lib = ctypes.CDLL(p)
     P = ctypes.c_void_p
-    PP = ctypes.POINTER(Conv2dGiParams)
+    PP = Conv2dGiParams  # passed by value
     lib.conv2d_grad_input.argtypes = [P, P, P, PP, P]
     lib.conv2d_grad_input.restype = ctypes.c_int
     lib.conv2d_grad_input_bf16.argtypes = [P, P, P, PP, P]
@@ -148,14 +149,14 @@ def _check(code: int):
 
 def validate(p: Conv2dGiParams) -> int:
     """Host-only shape check; returns the status code (no HIP call)."""
-    return load_library().conv2d_gi_validate(ctypes.byref(p))
+    return load_library().conv2d_gi_validate(p)
 
 
 def plan(p: Conv2dGiParams, bf16=False) -> str:
     """Host-only: the plan the library would run for this shape; bf16: False
     or 0 for fp32 inputs, True or 1 for bf16, 2 for fp16."""
     buf = ctypes.create_string_buffer(8192)
-    _check(load_library().conv2d_gi_plan(ctypes.byref(p), int(bf16), buf, len(buf)))
+    _check(load_library().conv2d_gi_plan(p, int(bf16), buf, len(buf)))
     return buf.value.decode()
 
 
@@ -169,7 +170,7 @@ def set_variant(variant: int) -> int:
 
 def set_halo_tile(nb: int = 0, tile_rows: int = 0, tile_cols: int = 0, stages: int = 0):
     """Force the HALO variant's pixel tile (fp32: blocks per work-group, tile
-    and pipeline depth; bf16: blocks per wave and tile) for later calls (test
+    and pipeline depth; bf16: blocks per wave and tile) for this thread's later calls (test
     hook); set_halo_tile() restores the planner."""
     _check(load_library().conv2d_gi_set_halo_tile(int(nb), int(tile_rows), int(tile_cols),
                                                   int(stages)))
@@ -177,28 +178,28 @@ def set_halo_tile(nb: int = 0, tile_rows: int = 0, tile_cols: int = 0, stages: i
 
 def set_halo_split(groups: int = 0):
     """Force 1 or 2 thread groups splitting the output channels of an fp32
-    HALO work-group for later calls (test hook); set_halo_split() restores the
+    HALO work-group for this thread's later calls (test hook); set_halo_split() restores the
     planner."""
     _check(load_library().conv2d_gi_set_halo_split(int(groups)))
 
 
 def set_halo_fusion(mode: int = 0):
     """Force the fp32 HALO variant to run a tile's stride phases one after
-    another (1) or all per chunk over one shared halo (2) for later calls
-    (test hook); set_halo_fusion() restores the planner."""
+    another (1) or all per chunk over one shared halo (2) for this thread's later
+    calls (test hook); set_halo_fusion() restores the planner."""
     _check(load_library().conv2d_gi_set_halo_fusion(int(mode)))
 
 
 def set_gw_variant(mode: int = 0):
     """Force grad_weight onto the 4-byte-load kernel (1) or the 16-byte-load
-    kernel (2; shapes it does not cover raise) for later calls (test hook);
+    kernel (2; shapes it does not cover raise) for this thread's later calls (test hook);
     set_gw_variant() restores the planner."""
     _check(load_library().conv2d_gw_set_variant(int(mode)))
 
 
 def set_gw_tile(rows: int = 0, stages: int = 0, max_slices: int = 0):
     """Force the 16-byte-load grad_weight kernel's rows per pixel group, LDS
-    stages and most slices for later calls (test hook); set_gw_tile()
+    stages and most slices for this thread's later calls (test hook); set_gw_tile()
     restores the planner."""
     _check(load_library().conv2d_gw_set_tile(int(rows), int(stages), int(max_slices)))
 
@@ -247,7 +248,7 @@ def grad_input(grad_out, weight, *, stride: int, padding, input_hw, out=None, st
         raise ValueError("weight has %d output channels, grad_out %d" % (Co_w, Co))
     p = Conv2dGiParams(N, Ci, H, W, Co, kH, kW, int(stride), pad_h, pad_w, oH, oW)
     lib = load_library()
-    _check(lib.conv2d_gi_validate(ctypes.byref(p)))
+    _check(lib.conv2d_gi_validate(p))
     dev = grad_out.device
     if out is None:
         out = torch.empty((N, Ci, H, W), dtype=torch.float32, device=dev)
@@ -260,7 +261,7 @@ def grad_input(grad_out, weight, *, stride: int, padding, input_hw, out=None, st
         fn = {torch.bfloat16: lib.conv2d_grad_input_bf16, torch.float16: lib.conv2d_grad_input_f16,
               torch.float32: lib.conv2d_grad_input}[grad_out.dtype]
         code = fn(ctypes.c_void_p(grad_out.data_ptr()), ctypes.c_void_p(weight.data_ptr()),
-                  ctypes.c_void_p(out.data_ptr()), ctypes.byref(p),
+                  ctypes.c_void_p(out.data_ptr()), p,
                   ctypes.c_void_p(s.cuda_stream))
     _check(code)
     return out
@@ -269,7 +270,7 @@ def grad_input(grad_out, weight, *, stride: int, padding, input_hw, out=None, st
 def grad_weight_plan(p: Conv2dGiParams) -> str:
     """Description of the launches conv2d_grad_weight would make for shape p."""
     buf = ctypes.create_string_buffer(1024)
-    _check(load_library().conv2d_gw_plan(ctypes.byref(p), buf, len(buf)))
+    _check(load_library().conv2d_gw_plan(p, buf, len(buf)))
     return buf.value.decode()
 
 
@@ -302,7 +303,7 @@ def grad_weight(grad_out, x, *, stride: int, padding, kernel_hw, out=None, strea
         raise ValueError("x has %d batch items, grad_out %d" % (Nx, N))
     p = Conv2dGiParams(N, Ci, H, W, Co, kH, kW, int(stride), pad_h, pad_w, oH, oW)
     lib = load_library()
-    _check(lib.conv2d_gi_validate(ctypes.byref(p)))
+    _check(lib.conv2d_gi_validate(p))
     dev = grad_out.device
     if out is None:
         out = torch.empty((Co, Ci, kH, kW), dtype=torch.float32, device=dev)
@@ -313,7 +314,7 @@ def grad_weight(grad_out, x, *, stride: int, padding, kernel_hw, out=None, strea
         s = stream if stream is not None else torch.cuda.current_stream(dev)
         code = lib.conv2d_grad_weight(ctypes.c_void_p(grad_out.data_ptr()),
                                       ctypes.c_void_p(x.data_ptr()),
-                                      ctypes.c_void_p(out.data_ptr()), ctypes.byref(p),
+                                      ctypes.c_void_p(out.data_ptr()), p,
                                       ctypes.c_void_p(s.cuda_stream))
     _check(code)
     return out
@@ -362,7 +363,7 @@ def backward(grad_out, x=None, weight=None, *, stride: int, padding, kernel_hw=N
         raise ValueError("weight must be [Co, Ci, kH, kW] = %r" % ((Co, Ci, kH, kW),))
     p = Conv2dGiParams(N, Ci, H, W, Co, kH, kW, int(stride), pad_h, pad_w, oH, oW)
     lib = load_library()
-    _check(lib.conv2d_gi_validate(ctypes.byref(p)))
+    _check(lib.conv2d_gi_validate(p))
 
     def out_tensor(t, want, shape, name):
         if not want:
@@ -381,7 +382,7 @@ def backward(grad_out, x=None, weight=None, *, stride: int, padding, kernel_hw=N
         s = stream if stream is not None else torch.cuda.current_stream(dev)
         code = lib.conv2d_backward(_ptr(grad_out), _ptr(x if want_dw else None),
                                    _ptr(weight if want_dx else None), _ptr(dx), _ptr(dw),
-                                   _ptr(db), ctypes.byref(p), ctypes.c_void_p(s.cuda_stream))
+                                   _ptr(db), p, ctypes.c_void_p(s.cuda_stream))
     _check(code)
     return dx, dw, db
 
@@ -406,7 +407,7 @@ def grad_bias(grad_out, *, out=None, stream=None):
     lib = load_library()
     with torch.cuda.device(dev):
         s = stream if stream is not None else torch.cuda.current_stream(dev)
-        code = lib.conv2d_grad_bias(_ptr(grad_out), _ptr(out), ctypes.byref(p),
+        code = lib.conv2d_grad_bias(_ptr(grad_out), _ptr(out), p,
                                     ctypes.c_void_p(s.cuda_stream))
     _check(code)
     return out
@@ -415,13 +416,13 @@ def grad_bias(grad_out, *, out=None, stream=None):
 def forward_plan(p: Conv2dGiParams) -> str:
     """Description of the launches conv2d_forward would make for shape p."""
     buf = ctypes.create_string_buffer(1024)
-    _check(load_library().conv2d_fwd_plan(ctypes.byref(p), buf, len(buf)))
+    _check(load_library().conv2d_fwd_plan(p, buf, len(buf)))
     return buf.value.decode()
 
 
 def set_fwd_variant(mode: int = 0):
     """Force the forward onto the grad_input kernels (1, stride 1 only) or the
-    generic forward kernel (2) for later calls (test hook); set_fwd_variant()
+    generic forward kernel (2) for this thread's later calls (test hook); set_fwd_variant()
     restores the planner."""
     _check(load_library().conv2d_fwd_set_variant(int(mode)))
 
@@ -446,7 +447,7 @@ def forward(x, weight, *, stride: int, padding, out=None, stream=None):
         raise ValueError("weight has %d input channels, x has %d" % (Ci_w, Ci))
     p = make_params(N, Ci, H, W, Co, kH, kW, int(stride), pad_h, pad_w)
     lib = load_library()
-    _check(lib.conv2d_gi_validate(ctypes.byref(p)))
+    _check(lib.conv2d_gi_validate(p))
     dev = x.device
     if out is None:
         out = torch.empty((N, Co, p.oH, p.oW), dtype=torch.float32, device=dev)
@@ -456,7 +457,7 @@ def forward(x, weight, *, stride: int, padding, out=None, stream=None):
                          % ((N, Co, p.oH, p.oW), dev))
     with torch.cuda.device(dev):
         s = stream if stream is not None else torch.cuda.current_stream(dev)
-        code = lib.conv2d_forward(_ptr(x), _ptr(weight), _ptr(out), ctypes.byref(p),
+        code = lib.conv2d_forward(_ptr(x), _ptr(weight), _ptr(out), p,
                                   ctypes.c_void_p(s.cuda_stream))
     _check(code)
     return out

@@ -6,7 +6,6 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
-#include <atomic>
 #include <cstdio>
 #include <cstring>
 #include <map>
@@ -17,6 +16,7 @@
 #include <vector>
 
 #include "conv2d_grad_input.h"
+#include "conv2d_grad_input_testing.h"
 #include "gi_common.h"
 #include "gi_launch.h"
 #include "fwd_common.h"
@@ -28,16 +28,18 @@ namespace {
 using gi::GemmArgs;
 using gi::Phase;
 
-std::atomic<int> g_variant{CONV2D_GI_VARIANT_AUTO};
-// Forced halo tile (test hook): NB pixel blocks, TR x TC phase-grid pixels; 0 = planner.
-std::atomic<int> g_tile_nb{0}, g_tile_tr{0}, g_tile_tc{0}, g_tile_stages{0};
-std::atomic<int> g_halo_split{0};
-std::atomic<int> g_halo_fusion{0};  // 0 planner, 1 phase at a time, 2 fused
-std::atomic<int> g_gw_variant{0};   // grad_weight: 0 planner, 1 4-byte loads, 2 16-byte loads
-std::atomic<int> g_fwd_variant{0};  // forward: 0 planner, 1 grad_input kernels, 2 generic
-std::atomic<int> g_gw_rows{0};      // grad_weight, 16-byte loads: forced rows per group (0 planner)
-std::atomic<int> g_gw_stages{0};    // ... and LDS stages (0 planner)
-std::atomic<int> g_gw_slices{0};    // ... and most slices (0 planner)
+// Test and diagnostic hooks (conv2d_grad_input_testing.h): thread-local, so a
+// setting changes only the plans of the thread that made it.
+thread_local int g_variant = CONV2D_GI_VARIANT_AUTO;
+// Forced halo tile: NB pixel blocks, TR x TC phase-grid pixels; 0 = planner.
+thread_local int g_tile_nb = 0, g_tile_tr = 0, g_tile_tc = 0, g_tile_stages = 0;
+thread_local int g_halo_split = 0;
+thread_local int g_halo_fusion = 0;  // 0 planner, 1 phase at a time, 2 fused
+thread_local int g_gw_variant = 0;   // grad_weight: 0 planner, 1 4-byte loads, 2 16-byte loads
+thread_local int g_fwd_variant = 0;  // forward: 0 planner, 1 grad_input kernels, 2 generic
+thread_local int g_gw_rows = 0;      // grad_weight, 16-byte loads: forced rows per group (0 planner)
+thread_local int g_gw_stages = 0;    // ... and LDS stages (0 planner)
+thread_local int g_gw_slices = 0;    // ... and most slices (0 planner)
 thread_local char g_last_hip[256] = "";
 thread_local hipEvent_t g_prof_begin = nullptr, g_prof_end = nullptr;
 
@@ -87,22 +89,27 @@ int64_t floordiv(int64_t a, int64_t b) {  // b > 0
     return a >= 0 ? a / b : -((-a + b - 1) / b);
 }
 
+// Shape checks shared by every entry point (host only, no HIP call).
 int validate(const conv2d_gi_params *p) {
     if (!p) return CONV2D_GI_EINVAL;
-    if (p->N < 0 || p->Ci < 0 || p->Co < 0) return CONV2D_GI_EINVAL;
+    // Every size is at least 1: the doppler wrappers throw on a missing or
+    // zero size, so a valid call always has elements in every tensor.
+    if (p->N < 1 || p->Ci < 1 || p->Co < 1) return CONV2D_GI_EINVAL;
     if (p->H < 1 || p->W < 1 || p->kH < 1 || p->kW < 1 || p->stride < 1) return CONV2D_GI_EINVAL;
     if (p->pad_h < 0 || p->pad_w < 0) return CONV2D_GI_EINVAL;
     const int64_t oH = floordiv((int64_t)p->H + 2LL * p->pad_h - p->kH, p->stride) + 1;
     const int64_t oW = floordiv((int64_t)p->W + 2LL * p->pad_w - p->kW, p->stride) + 1;
     if (oH < 1 || oW < 1) return CONV2D_GI_EINVAL;
     if (p->oH != oH || p->oW != oW) return CONV2D_GI_EINVAL;
-    // Index width: per-image planes, the weight and the folded pixel axis are
-    // addressed with 32-bit offsets inside the kernels; batch offsets are 64-bit.
+    // Index width: per-image planes, the weight and the folded pixel axes
+    // (input and output side) are addressed with 32-bit offsets inside the
+    // kernels; batch offsets are 64-bit.
     const int64_t lim = INT32_MAX;
     if ((int64_t)p->Ci * p->H * p->W > lim) return CONV2D_GI_EUNSUPPORTED;
     if ((int64_t)p->Co * oH * oW > lim) return CONV2D_GI_EUNSUPPORTED;
     if ((int64_t)p->Co * p->Ci * p->kH * p->kW > lim) return CONV2D_GI_EUNSUPPORTED;
     if ((int64_t)p->N * p->H * p->W > lim) return CONV2D_GI_EUNSUPPORTED;
+    if ((int64_t)p->N * oH * oW > lim) return CONV2D_GI_EUNSUPPORTED;
     if ((p->Ci + gi::kGenericBM - 1) / gi::kGenericBM > 65535) return CONV2D_GI_EUNSUPPORTED;
     return CONV2D_GI_OK;
 }
@@ -221,7 +228,7 @@ bool plan_halo(const conv2d_gi_params &p, const std::vector<Phase> &phases, Halo
     // tap grids of at most 2 x 2.  The shared halo starts at the smallest
     // phase origin q - (J - 1) and reaches TR + ur rows, TC + uc columns.
     int Tall = 0, org_h = INT32_MAX, org_w = INT32_MAX, ur = 0, uc = 0;
-    bool fusable = phases.size() == 4 && !fold && g_halo_fusion.load() != 1;
+    bool fusable = phases.size() == 4 && !fold && g_halo_fusion != 1;
     for (const Phase &ph : phases) {
         Tall += ph.J_h * ph.J_w;
         if (ph.J_h > 2 || ph.J_w > 2) fusable = false;
@@ -236,9 +243,9 @@ bool plan_halo(const conv2d_gi_params &p, const std::vector<Phase> &phases, Halo
             ur = std::max(ur, ph.q_h - (ph.J_h - 1) - org_h + ph.J_h - 1);
             uc = std::max(uc, ph.q_w - (ph.J_w - 1) - org_w + ph.J_w - 1);
         }
-    const int fz_lo = g_halo_fusion.load() == 2 ? 1 : 0;
+    const int fz_lo = g_halo_fusion == 2 ? 1 : 0;
     static const int kNB[] = {4, 8, 13};
-    const int f_nb = g_tile_nb.load(), f_tr = g_tile_tr.load(), f_tc = g_tile_tc.load();
+    const int f_nb = g_tile_nb, f_tr = g_tile_tr, f_tc = g_tile_tc;
     const bool forced = f_nb > 0;
     bool found = false;
     for (int nb : kNB) {
@@ -271,7 +278,7 @@ bool plan_halo(const conv2d_gi_params &p, const std::vector<Phase> &phases, Halo
                 // (phase at a time) or its phases (fused: always two, sharing
                 // every stage).
                 for (int ks = fz ? 2 : 1; ks <= 2; ++ks) {
-                const int f_ks = g_halo_split.load();
+                const int f_ks = g_halo_split;
                 if (!fz && f_ks > 0 && ks != f_ks) continue;
                 const int bl = fz ? (groups + 4 * ks - 1) / (4 * ks) : (groups + 3) / 4;
                 const int cfg = gi::halo_f32_config(nb, tmask, bl, HP, jw_common, ks, fz ? 4 : 0);
@@ -294,8 +301,8 @@ bool plan_halo(const conv2d_gi_params &p, const std::vector<Phase> &phases, Halo
                         lds = gi::halo_f32_lds_bytes(stage_taps, HPc, 3, cps);
                     }
                 }
-                if (forced && g_tile_stages.load() > 0) {
-                    stages = g_tile_stages.load();
+                if (forced && g_tile_stages > 0) {
+                    stages = g_tile_stages;
                     lds = gi::halo_f32_lds_bytes(stage_taps, HPc, stages, cps);
                 }
                 // A split work-group holds every group's stages, and its
@@ -443,7 +450,7 @@ bool plan_halo_bf16(const conv2d_gi_params &p, HaloBf16Plan &out) {
     if (gp_bytes > lim || wk_bytes > lim || (int64_t)p.N * p.Ci * p.H * p.W * 4 > lim)
         return false;
     static const int kNBW[] = {4, 7};
-    const int f_nb = g_tile_nb.load(), f_tr = g_tile_tr.load(), f_tc = g_tile_tc.load();
+    const int f_nb = g_tile_nb, f_tr = g_tile_tr, f_tc = g_tile_tc;
     const bool forced = f_nb > 0;
     bool found = false;
     for (int nbw : kNBW) {
@@ -682,7 +689,7 @@ Plan make_plan(const conv2d_gi_params &p, bool bf16) {
     Plan plan;
     plan.bf16 = bf16;
     std::vector<Phase> phases = make_phases(p);
-    const int forced = g_variant.load();
+    const int forced = g_variant;
     bool want_halo = !bf16 && p.Ci >= 16 &&
                      (forced == CONV2D_GI_VARIANT_HALO || forced == CONV2D_GI_VARIANT_AUTO);
     if (want_halo && plan_halo(p, phases, plan.halo)) {
@@ -706,8 +713,6 @@ Plan make_plan(const conv2d_gi_params &p, bool bf16) {
     return plan;
 }
 
-bool has_elems(int64_t n) { return n > 0; }
-
 // dt: 0 fp32 inputs, 1 bf16, 2 fp16 (the 16-bit kinds share plans, prologues
 // and kernels up to the MFMA instruction).
 template <typename T>
@@ -717,13 +722,7 @@ int run(const T *grad_out, const T *weight, float *dst, const conv2d_gi_params *
     const bool f16 = dt == 2;
     int rc = validate(p);
     if (rc != CONV2D_GI_OK) return rc;
-    const int64_t n_dst = (int64_t)p->N * p->Ci * p->H * p->W;
-    const int64_t n_g = (int64_t)p->N * p->Co * p->oH * p->oW;
-    const int64_t n_w = (int64_t)p->Co * p->Ci * p->kH * p->kW;
-    if ((has_elems(n_dst) && !dst) || (has_elems(n_g) && !grad_out) ||
-        (has_elems(n_w) && !weight))
-        return CONV2D_GI_EINVAL;
-    if (n_dst == 0) return CONV2D_GI_OK;
+    if (!dst || !grad_out || !weight) return CONV2D_GI_EINVAL;
 
     Plan plan = make_plan(*p, bf16);
     void *ws = nullptr;
@@ -971,7 +970,7 @@ bool plan_gwd(const conv2d_gi_params &p, GwdPlan &out, bool bias = false) {
     bool found = false;
     double best = 0;
     for (int R = 1; R <= std::min(p.oH, 64); ++R) {
-        if (g_gw_rows.load() > 0 && R != std::min(g_gw_rows.load(), p.oH)) continue;
+        if (g_gw_rows > 0 && R != std::min(g_gw_rows, p.oH)) continue;
         int64_t nkb, LA, LX;
         if (flat) {
             nkb = ((int64_t)R * p.oW + 15) / 16;
@@ -985,7 +984,7 @@ bool plan_gwd(const conv2d_gi_params &p, GwdPlan &out, bool bias = false) {
         const int64_t nslots = 16 * LA + a.XC * (LX / 4);
         const int64_t stage_floats = (nslots + 63) / 64 * 256;
         for (int stages = 2; stages >= 1; --stages) {
-            if (g_gw_stages.load() > 0 && stages != g_gw_stages.load()) continue;
+            if (g_gw_stages > 0 && stages != g_gw_stages) continue;
             const size_t lds = (size_t)stages * stage_floats * 4;
             if (lds > kLdsBytes) continue;
             const int occ = (int)std::min<size_t>(gi::gwd_f32_max_wgs(cfg), kLdsBytes / lds);
@@ -993,7 +992,7 @@ bool plan_gwd(const conv2d_gi_params &p, GwdPlan &out, bool bias = false) {
             const int64_t groups = (int64_t)p.N * groups_img;
             int64_t slices = std::max<int64_t>(
                 1, std::min<int64_t>(groups, (occ * kCUs + tiles - 1) / tiles));
-            if (g_gw_slices.load() > 0) slices = std::min<int64_t>(slices, g_gw_slices.load());
+            if (g_gw_slices > 0) slices = std::min<int64_t>(slices, g_gw_slices);
             const int64_t gs = std::max<int64_t>(1, (groups + slices - 1) / slices);
             slices = std::max<int64_t>(1, (groups + gs - 1) / gs);
             if (tiles * slices > INT32_MAX) continue;
@@ -1149,7 +1148,7 @@ size_t bias_ws_bytes(const conv2d_gi_params &p) {
 // validated by the caller.
 int run_gw_checked(const float *grad_out, const float *x, float *dw, float *db,
                    const conv2d_gi_params *p, hipStream_t stream) {
-    const int variant = g_gw_variant.load();
+    const int variant = g_gw_variant;
     GwdPlan dplan;
     const bool use_d = variant != 1 && plan_gwd(*p, dplan, db != nullptr);
     if (variant == 2 && !use_d) return CONV2D_GI_EUNSUPPORTED;
@@ -1195,19 +1194,13 @@ int run_gw(const float *grad_out, const float *x, float *dw, const conv2d_gi_par
            hipStream_t stream) {
     int rc = validate(p);
     if (rc != CONV2D_GI_OK) return rc;
-    const int64_t n_x = (int64_t)p->N * p->Ci * p->H * p->W;
-    const int64_t n_g = (int64_t)p->N * p->Co * p->oH * p->oW;
-    const int64_t n_w = (int64_t)p->Co * p->Ci * p->kH * p->kW;
-    if ((has_elems(n_w) && !dw) || (has_elems(n_g) && !grad_out) || (has_elems(n_x) && !x))
-        return CONV2D_GI_EINVAL;
-    if (n_w == 0) return CONV2D_GI_OK;
+    if (!dw || !grad_out || !x) return CONV2D_GI_EINVAL;
     return run_gw_checked(grad_out, x, dw, nullptr, p, stream);
 }
 
 // The bias gradient alone (arguments validated by the caller).
 int run_bias_checked(const float *grad_out, float *db, const conv2d_gi_params *p,
                      hipStream_t stream) {
-    if (p->Co == 0) return CONV2D_GI_OK;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return fail_hip(e);
@@ -1224,18 +1217,15 @@ int run_backward(const float *grad_out, const float *x, const float *weight, flo
                  float *dw, float *db, const conv2d_gi_params *p, hipStream_t stream) {
     int rc = validate(p);
     if (rc != CONV2D_GI_OK) return rc;
-    const int64_t n_x = (int64_t)p->N * p->Ci * p->H * p->W;
-    const int64_t n_g = (int64_t)p->N * p->Co * p->oH * p->oW;
-    const int64_t n_w = (int64_t)p->Co * p->Ci * p->kH * p->kW;
     // Every requested output needs grad_out; dx needs the weight, dw the input.
-    if ((dx || dw || db) && has_elems(n_g) && !grad_out) return CONV2D_GI_EINVAL;
-    if (dx && has_elems(n_w) && !weight) return CONV2D_GI_EINVAL;
-    if (dw && has_elems(n_x) && !x) return CONV2D_GI_EINVAL;
+    if ((dx || dw || db) && !grad_out) return CONV2D_GI_EINVAL;
+    if (dx && !weight) return CONV2D_GI_EINVAL;
+    if (dw && !x) return CONV2D_GI_EINVAL;
     if (dx) {
         rc = run<float>(grad_out, weight, dx, p, stream, 0);
         if (rc != CONV2D_GI_OK) return rc;
     }
-    if (dw && n_w > 0) return run_gw_checked(grad_out, x, dw, db, p, stream);
+    if (dw) return run_gw_checked(grad_out, x, dw, db, p, stream);
     if (db) return run_bias_checked(grad_out, db, p, stream);
     return CONV2D_GI_OK;
 }
@@ -1247,7 +1237,7 @@ int run_backward(const float *grad_out, const float *x, const float *weight, flo
 // kH-1-ph (and kW-1-pw): an input-side problem with Ci' = Co, H' = oH,
 // Co' = Ci, oH' = H.  Other shapes run on the generic forward kernel.
 bool fwd_via_grad_input(const conv2d_gi_params &p) {
-    return g_fwd_variant.load() != 2 && p.stride == 1 && p.pad_h <= p.kH - 1 &&
+    return g_fwd_variant != 2 && p.stride == 1 && p.pad_h <= p.kH - 1 &&
            p.pad_w <= p.kW - 1;
 }
 
@@ -1272,13 +1262,9 @@ int run_forward(const float *x, const float *w, float *y, const conv2d_gi_params
                 hipStream_t stream) {
     int rc = validate(p);
     if (rc != CONV2D_GI_OK) return rc;
-    const int64_t n_x = (int64_t)p->N * p->Ci * p->H * p->W;
-    const int64_t n_y = (int64_t)p->N * p->Co * p->oH * p->oW;
+    if (!y || !x || !w) return CONV2D_GI_EINVAL;
     const int64_t n_w = (int64_t)p->Co * p->Ci * p->kH * p->kW;
-    if ((has_elems(n_y) && !y) || (has_elems(n_x) && !x) || (has_elems(n_w) && !w))
-        return CONV2D_GI_EINVAL;
-    if (n_y == 0) return CONV2D_GI_OK;
-    if (g_fwd_variant.load() == 1 && !fwd_via_grad_input(*p)) return CONV2D_GI_EUNSUPPORTED;
+    if (g_fwd_variant == 1 && !fwd_via_grad_input(*p)) return CONV2D_GI_EUNSUPPORTED;
     const int kHW = p->kH * p->kW;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -1351,17 +1337,17 @@ std::string describe_forward(const conv2d_gi_params &p) {
 
 extern "C" {
 
-int conv2d_forward(const float *x, const float *w, float *y, const conv2d_gi_params *p,
+int conv2d_forward(const float *x, const float *w, float *y, conv2d_gi_params p,
                    hipStream_t stream) {
-    return run_forward(x, w, y, p, stream);
+    return run_forward(x, w, y, &p, stream);
 }
 
-int conv2d_fwd_plan(const conv2d_gi_params *p, char *buf, size_t len) {
-    int rc = validate(p);
+int conv2d_fwd_plan(conv2d_gi_params p, char *buf, size_t len) {
+    int rc = validate(&p);
     if (rc != CONV2D_GI_OK) return rc;
     if (!buf || len == 0) return CONV2D_GI_EINVAL;
-    if (g_fwd_variant.load() == 1 && !fwd_via_grad_input(*p)) return CONV2D_GI_EUNSUPPORTED;
-    std::snprintf(buf, len, "%s", describe_forward(*p).c_str());
+    if (g_fwd_variant == 1 && !fwd_via_grad_input(p)) return CONV2D_GI_EUNSUPPORTED;
+    std::snprintf(buf, len, "%s", describe_forward(p).c_str());
     return CONV2D_GI_OK;
 }
 
@@ -1372,36 +1358,36 @@ int conv2d_fwd_set_variant(int mode) {
 }
 
 int conv2d_grad_weight(const float *grad_out, const float *x, float *dw,
-                       const conv2d_gi_params *p, hipStream_t stream) {
-    return run_gw(grad_out, x, dw, p, stream);
+                       conv2d_gi_params p, hipStream_t stream) {
+    return run_gw(grad_out, x, dw, &p, stream);
 }
 
 int conv2d_backward(const float *grad_out, const float *x, const float *weight, float *dx,
-                    float *dw, float *db, const conv2d_gi_params *p, hipStream_t stream) {
-    return run_backward(grad_out, x, weight, dx, dw, db, p, stream);
+                    float *dw, float *db, conv2d_gi_params p, hipStream_t stream) {
+    return run_backward(grad_out, x, weight, dx, dw, db, &p, stream);
 }
 
-int conv2d_grad_bias(const float *grad_out, float *db, const conv2d_gi_params *p,
+int conv2d_grad_bias(const float *grad_out, float *db, conv2d_gi_params p,
                      hipStream_t stream) {
-    int rc = validate(p);
+    int rc = validate(&p);
     if (rc != CONV2D_GI_OK) return rc;
-    if (!db && p->Co > 0) return CONV2D_GI_EINVAL;
-    return run_backward(grad_out, nullptr, nullptr, nullptr, nullptr, db, p, stream);
+    if (!db) return CONV2D_GI_EINVAL;
+    return run_backward(grad_out, nullptr, nullptr, nullptr, nullptr, db, &p, stream);
 }
 
-int conv2d_gw_plan(const conv2d_gi_params *p, char *buf, size_t len) {
-    int rc = validate(p);
+int conv2d_gw_plan(conv2d_gi_params p, char *buf, size_t len) {
+    int rc = validate(&p);
     if (rc != CONV2D_GI_OK) return rc;
     if (!buf || len == 0) return CONV2D_GI_EINVAL;
-    const int variant = g_gw_variant.load();
+    const int variant = g_gw_variant;
     GwdPlan dplan;
-    if (variant != 1 && plan_gwd(*p, dplan)) {
+    if (variant != 1 && plan_gwd(p, dplan)) {
         std::snprintf(buf, len, "%s", describe_gwd(dplan).c_str());
         return CONV2D_GI_OK;
     }
     if (variant == 2) return CONV2D_GI_EUNSUPPORTED;
     GwPlan plan;
-    if (!plan_gw(*p, plan)) return CONV2D_GI_EUNSUPPORTED;
+    if (!plan_gw(p, plan)) return CONV2D_GI_EUNSUPPORTED;
     std::snprintf(buf, len, "%s", describe_gw(plan).c_str());
     return CONV2D_GI_OK;
 }
@@ -1421,21 +1407,21 @@ int conv2d_gw_set_variant(int mode) {
 }
 
 int conv2d_grad_input(const float *grad_out, const float *weight, float *dst,
-                      const conv2d_gi_params *p, hipStream_t stream) {
-    return run<float>(grad_out, weight, dst, p, stream, 0);
+                      conv2d_gi_params p, hipStream_t stream) {
+    return run<float>(grad_out, weight, dst, &p, stream, 0);
 }
 
 int conv2d_grad_input_bf16(const uint16_t *grad_out, const uint16_t *weight, float *dst,
-                           const conv2d_gi_params *p, hipStream_t stream) {
-    return run<uint16_t>(grad_out, weight, dst, p, stream, 1);
+                           conv2d_gi_params p, hipStream_t stream) {
+    return run<uint16_t>(grad_out, weight, dst, &p, stream, 1);
 }
 
 int conv2d_grad_input_f16(const uint16_t *grad_out, const uint16_t *weight, float *dst,
-                          const conv2d_gi_params *p, hipStream_t stream) {
-    return run<uint16_t>(grad_out, weight, dst, p, stream, 2);
+                          conv2d_gi_params p, hipStream_t stream) {
+    return run<uint16_t>(grad_out, weight, dst, &p, stream, 2);
 }
 
-int conv2d_gi_validate(const conv2d_gi_params *p) { return validate(p); }
+int conv2d_gi_validate(conv2d_gi_params p) { return validate(&p); }
 
 const char *conv2d_gi_strerror(int code) {
     switch (code) {
@@ -1454,15 +1440,17 @@ int conv2d_gi_set_variant(int variant) {
     if (variant != CONV2D_GI_VARIANT_AUTO && variant != CONV2D_GI_VARIANT_GENERIC &&
         variant != CONV2D_GI_VARIANT_HALO && variant != CONV2D_GI_VARIANT_STEM)
         return -1;
-    return g_variant.exchange(variant);
+    const int old = g_variant;
+    g_variant = variant;
+    return old;
 }
 
-int conv2d_gi_plan(const conv2d_gi_params *p, int dtype_bf16, char *buf, size_t len) {
-    int rc = validate(p);
+int conv2d_gi_plan(conv2d_gi_params p, int dtype_bf16, char *buf, size_t len) {
+    int rc = validate(&p);
     if (rc != CONV2D_GI_OK) return rc;
     if (!buf || len == 0) return CONV2D_GI_EINVAL;
     if (dtype_bf16 < 0 || dtype_bf16 > 2) return CONV2D_GI_EINVAL;
-    Plan plan = make_plan(*p, dtype_bf16 != 0);
+    Plan plan = make_plan(p, dtype_bf16 != 0);
     std::snprintf(buf, len, "%s", describe(plan, dtype_bf16).c_str());
     return CONV2D_GI_OK;
 }

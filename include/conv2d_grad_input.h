@@ -32,27 +32,36 @@
  *   weight   [Co, Ci, kH, kW]  read only
  *   dst      [N, Ci, H, W]     fp32, written (every element, never accumulated)
  * The caller allocates and owns all three; the library never frees them.  dst
- * must not overlap either input.  The library keeps scratch buffers per
- * (device, stream): one for every kernel's own scratch (the weight in kernel
- * order, about Co*Ci*kH*kW elements, or grad_weight's partial sums) and one
- * for the tap-reversed weight of conv2d_forward.  Each is allocated
- * stream-ordered on `stream` (hipMallocAsync) at the first call that needs
- * it, grown when a later call needs more, and reused by later calls on that
- * stream, which stream order keeps apart.  An internal lock is held while a
- * call enqueues, so calls from several host threads on one stream are safe
- * (they run in the order they took the lock).  Calls on different streams
- * share no state.  conv2d_gi_release_workspaces frees the buffers
- * (call it before destroying a stream the library ran on, since a new stream
- * could receive the same handle).  Both convolution stride dimensions take `stride`; padding
- * is symmetric per dimension (pad_h top and bottom, pad_w left and right).
+ * must not overlap either input.  Both convolution stride dimensions take
+ * `stride`; padding is symmetric per dimension (pad_h top and bottom, pad_w
+ * left and right).
  *
+ * Library scratch
+ * ---------------
+ * Some plans need device scratch: the weight reordered into the order a kernel
+ * reads it (about Co*Ci*kH*kW elements), grad_weight's partial sums, the
+ * forward's tap-reversed weight.  The library keeps one buffer per (device,
+ * stream, purpose), allocated stream-ordered on `stream` (hipMallocAsync) by
+ * the first call that needs it, grown when a later call needs more (the old
+ * one is freed stream-ordered), and reused by later calls on that stream;
+ * stream order keeps the calls apart.  Nothing is carried from one call to the
+ * next: every call rewrites what it reads.  An internal lock is held while a
+ * call enqueues, so calls from several host threads on one stream are safe
+ * (they run in the order they took the lock), and calls on different streams
+ * share no buffer.  The cache is keyed by the stream handle, so a stream the
+ * library ran on must outlive its buffers: call conv2d_gi_release_workspaces
+ * (which waits for each stream's queued work, then frees) before destroying
+ * it, or a new stream that receives the same handle would inherit them.
+
  * Asynchrony and errors
  * ---------------------
  * Calls enqueue work on `stream` (0 = the device's null stream) and return
  * without waiting; dst is valid once the stream has reached that point.  The
  * current HIP device must own the buffers.  All arguments are checked on the
  * host before anything is enqueued: on CONV2D_GI_EINVAL or
- * CONV2D_GI_EUNSUPPORTED nothing is launched and dst is untouched.
+ * CONV2D_GI_EUNSUPPORTED nothing is launched and dst is untouched.  Zero or
+ * negative sizes are invalid (as the doppler wrappers throw on a missing or
+ * zero size): every tensor of a valid call has elements.
  * CONV2D_GI_EHIP reports a HIP runtime error from an allocation or launch
  * (the error string of the last one is kept for conv2d_gi_last_hip_error).
  */
@@ -82,10 +91,10 @@ extern "C" {
  * same oH and oW.
  */
 typedef struct conv2d_gi_params {
-    int32_t N;        /* batch items; 0 is allowed (nothing is done)          */
-    int32_t Ci;       /* input channels = channels of dst; 0 allowed          */
+    int32_t N;        /* batch items, >= 1                                    */
+    int32_t Ci;       /* input channels = channels of dst, >= 1               */
     int32_t H, W;     /* input (dst) spatial size, >= 1                       */
-    int32_t Co;       /* output channels; 0 allowed (dst is zero-filled)      */
+    int32_t Co;       /* output channels, >= 1                                */
     int32_t kH, kW;   /* kernel size, >= 1                                    */
     int32_t stride;   /* one stride for both dimensions, >= 1                 */
     int32_t pad_h;    /* zero padding above and below, >= 0                   */
@@ -93,35 +102,24 @@ typedef struct conv2d_gi_params {
     int32_t oH, oW;   /* grad_out spatial size; must equal
                          (H + 2*pad_h - kH)/stride + 1 and
                          (W + 2*pad_w - kW)/stride + 1 (floor division), >= 1 */
-} conv2d_gi_params;
+} conv2d_gi_params;   /* passed by value to every entry point */
 
 /* Status codes returned by every entry point. */
 enum {
     CONV2D_GI_OK = 0,
-    CONV2D_GI_EINVAL = 1,       /* bad pointer or shape; nothing launched      */
-    CONV2D_GI_EUNSUPPORTED = 2, /* valid but beyond the library's index width  */
+    CONV2D_GI_EINVAL = 1,       /* null pointer or bad shape; nothing launched */
+    CONV2D_GI_EUNSUPPORTED = 2, /* valid but beyond the library's limits (index
+                                   width, the no-alloc scratch size)          */
     CONV2D_GI_EHIP = 3          /* HIP runtime error from allocation or launch */
-};
-
-/* Kernel variants, for conv2d_gi_set_variant and conv2d_gi_plan. */
-enum {
-    CONV2D_GI_VARIANT_AUTO = 0,    /* the planner chooses                      */
-    CONV2D_GI_VARIANT_GENERIC = 1, /* any shape: phase split, gathered B tile  */
-    CONV2D_GI_VARIANT_HALO = 2,    /* Ci >= 16 (bf16: stride 1): grad_out halo
-                                      tile in LDS, every tap a shifted view of
-                                      it; other shapes fall back to GENERIC    */
-    CONV2D_GI_VARIANT_STEM = 3     /* fp32, Ci <= 4: 4x4 matrix-core blocks with
-                                      the input channels on one side; other
-                                      shapes fall back to GENERIC              */
 };
 
 /*
  * fp32 grad_input.  grad_out and weight fp32, dst fp32 (layouts above).
- * Contraction on the fp32 matrix cores, fp32 accumulation.
- * Pointers may be NULL only when the tensor they point to has no elements.
+ * Contraction on the fp32 matrix cores, fp32 accumulation.  No pointer may
+ * be NULL.
  */
 CONV2D_GI_API int conv2d_grad_input(const float *grad_out, const float *weight, float *dst,
-                      const conv2d_gi_params *p, hipStream_t stream);
+                      conv2d_gi_params p, hipStream_t stream);
 
 /*
  * bf16-input grad_input.  grad_out and weight hold bf16 bit patterns (the top
@@ -129,7 +127,7 @@ CONV2D_GI_API int conv2d_grad_input(const float *grad_out, const float *weight, 
  * exact in fp32; accumulation is fp32 on the bf16 matrix cores.
  */
 CONV2D_GI_API int conv2d_grad_input_bf16(const uint16_t *grad_out, const uint16_t *weight,
-                           float *dst, const conv2d_gi_params *p,
+                           float *dst, conv2d_gi_params p,
                            hipStream_t stream);
 
 /*
@@ -142,57 +140,17 @@ CONV2D_GI_API int conv2d_grad_input_bf16(const uint16_t *grad_out, const uint16_
  * codes as conv2d_grad_input.
  */
 CONV2D_GI_API int conv2d_grad_input_f16(const uint16_t *grad_out, const uint16_t *weight,
-                                        float *dst, const conv2d_gi_params *p,
+                                        float *dst, conv2d_gi_params p,
                                         hipStream_t stream);
 
 /* Host-only check of a shape, as done by the entry points (no HIP call). */
-CONV2D_GI_API int conv2d_gi_validate(const conv2d_gi_params *p);
+CONV2D_GI_API int conv2d_gi_validate(conv2d_gi_params p);
 
 /* Static text for a status code. */
 CONV2D_GI_API const char *conv2d_gi_strerror(int code);
 
 /* Text of the last HIP error seen by this thread's calls ("" if none). */
 CONV2D_GI_API const char *conv2d_gi_last_hip_error(void);
-
-/*
- * Test and diagnostic hook: force a kernel variant for later calls in this
- * process (CONV2D_GI_VARIANT_AUTO restores the planner).  Returns the
- * previous setting, or -1 for an unknown variant (setting unchanged).
- */
-CONV2D_GI_API int conv2d_gi_set_variant(int variant);
-
-/*
- * Test and diagnostic hook: force the pixel tile of the HALO variant for
- * later calls in this process.  fp32: nb pixel blocks of 16 per work-group
- * (4, 8 or 13), a tile of tile_rows x tile_cols pixels of the stride-phase
- * grid (at most nb*16 pixels) and the LDS pipeline depth (2 or 3 stages; 0
- * lets the planner choose).  bf16: nb pixel blocks of 16 per wave (4 or 7;
- * two waves share the tile, so at most 2*nb*16 pixels); stages is ignored.
- * A shape the forced tile does not fit (LDS, halo size) is planned with
- * GENERIC instead.  nb = 0 restores the planner.  Returns CONV2D_GI_OK, or
- * CONV2D_GI_EINVAL for values out of range.
- */
-CONV2D_GI_API int conv2d_gi_set_halo_tile(int nb, int tile_rows, int tile_cols, int stages);
-
-/*
- * Test and diagnostic hook: force how many thread groups of 256 split the
- * output channels of a work-group of the fp32 HALO variant for later calls
- * in this process (1 or 2; each group stages its own share of the chunks
- * and the first sums both before storing).  A shape no instance with that
- * split serves is planned without it.  0 restores the planner.  Returns
- * CONV2D_GI_OK, or CONV2D_GI_EINVAL for other values.
- */
-CONV2D_GI_API int conv2d_gi_set_halo_split(int groups);
-
-/*
- * Test and diagnostic hook: how the fp32 HALO variant runs the stride
- * phases of a work-group's tile for later calls in this process: 1 one
- * phase after another (each over its own grad_out halo), 2 all phases per
- * chunk of output channels over one shared halo (four phases of tap grids
- * up to 2 x 2 only; other shapes are planned phase at a time).  0 restores
- * the planner.  Returns CONV2D_GI_OK, or CONV2D_GI_EINVAL for other values.
- */
-CONV2D_GI_API int conv2d_gi_set_halo_fusion(int mode);
 
 /*
  * Gradient with respect to the weight (the next step of the same backward
@@ -210,13 +168,13 @@ CONV2D_GI_API int conv2d_gi_set_halo_fusion(int mode);
  * validated the same way.  Enqueued on `stream` (asynchronous).  The
  * partial sums of the split pixel axis live in the library's per-stream
  * scratch buffer and are added in a fixed order, so the result does not
- * depend on scheduling.  Returns CONV2D_GI_OK, CONV2D_GI_EINVAL (null pointer
- * for a non-empty tensor, inconsistent shape), CONV2D_GI_EUNSUPPORTED (kernel
+ * depend on scheduling.  Returns CONV2D_GI_OK, CONV2D_GI_EINVAL (null pointer,
+ * inconsistent shape), CONV2D_GI_EUNSUPPORTED (kernel
  * width above 16, output rows wider than 256 pixels, tensors of 2 GiB or more)
  * or CONV2D_GI_EHIP.
  */
 CONV2D_GI_API int conv2d_grad_weight(const float *grad_out, const float *x, float *dw,
-                                     const conv2d_gi_params *p, hipStream_t stream);
+                                     conv2d_gi_params p, hipStream_t stream);
 
 /*
  * The whole backward pass of a convolution layer in one call, after the
@@ -229,7 +187,8 @@ CONV2D_GI_API int conv2d_grad_weight(const float *grad_out, const float *x, floa
  *   db[co] = sum over n, oh, ow of grad_out[n,co,oh,ow]   (when db is not NULL)
  *
  * Same shapes, layouts and validation as the single calls; db is device
- * [Co] fp32.  weight may be NULL when dx is, x when dw is.  With dw, the
+ * [Co] fp32.  weight may be NULL when dx is, x when dw is; grad_out is
+ * required when any output is asked for.  With dw, the
  * bias sums come from the grad_out values the grad_weight kernel already
  * reads (no second pass over grad_out where the 16-byte-load kernel runs);
  * without dw a per-channel reduction computes them.  All sums are in a fixed
@@ -237,17 +196,17 @@ CONV2D_GI_API int conv2d_grad_weight(const float *grad_out, const float *x, floa
  * failing step's status; the steps before it have been enqueued.
  */
 CONV2D_GI_API int conv2d_backward(const float *grad_out, const float *x, const float *weight,
-                                  float *dx, float *dw, float *db, const conv2d_gi_params *p,
+                                  float *dx, float *dw, float *db, conv2d_gi_params p,
                                   hipStream_t stream);
 
 /*
  * The bias gradient alone: db[co] = sum over n, oh, ow of grad_out[n,co,oh,ow]
  * (bias_add_backward.wgsl's sum over the positions the bias was added to).
- * grad_out: device [N, Co, oH, oW] fp32; db: device [Co] fp32, overwritten
- * (zeros for an empty batch).  p is validated as for the other calls.
+ * grad_out: device [N, Co, oH, oW] fp32; db: device [Co] fp32, overwritten.
+ * p is validated as for the other calls.
  * Returns CONV2D_GI_OK, CONV2D_GI_EINVAL or CONV2D_GI_EHIP.
  */
-CONV2D_GI_API int conv2d_grad_bias(const float *grad_out, float *db, const conv2d_gi_params *p,
+CONV2D_GI_API int conv2d_grad_bias(const float *grad_out, float *db, conv2d_gi_params p,
                                    hipStream_t stream);
 
 /*
@@ -269,67 +228,29 @@ CONV2D_GI_API int conv2d_grad_bias(const float *grad_out, float *db, const conv2
  * does not apply) or CONV2D_GI_EHIP.
  */
 CONV2D_GI_API int conv2d_forward(const float *x, const float *w, float *y,
-                                 const conv2d_gi_params *p, hipStream_t stream);
+                                 conv2d_gi_params p, hipStream_t stream);
 
 /*
  * Host-only: describe the launches conv2d_forward would make for this shape,
  * as text written into buf (NUL-terminated, truncated to len).
  */
-CONV2D_GI_API int conv2d_fwd_plan(const conv2d_gi_params *p, char *buf, size_t len);
-
-/*
- * Test and diagnostic hook: which path later conv2d_forward calls in this
- * process take: 1 the grad_input kernels (stride 1 only; other shapes return
- * CONV2D_GI_EUNSUPPORTED), 2 the generic forward kernel, 0 restores the
- * planner.  Returns CONV2D_GI_OK, or CONV2D_GI_EINVAL for other values.
- */
-CONV2D_GI_API int conv2d_fwd_set_variant(int mode);
+CONV2D_GI_API int conv2d_fwd_plan(conv2d_gi_params p, char *buf, size_t len);
 
 /*
  * Host-only: describe the launch conv2d_grad_weight would make for this shape,
  * as text written into buf (NUL-terminated, truncated to len).
  */
-CONV2D_GI_API int conv2d_gw_plan(const conv2d_gi_params *p, char *buf, size_t len);
-
-/*
- * Test and diagnostic hook: which grad_weight kernel later calls in this
- * process use: 1 the one with 4-byte direct loads (any shape the entry point
- * accepts), 2 the one with 16-byte direct loads (shapes it does not cover
- * return CONV2D_GI_EUNSUPPORTED), 0 restores the planner (16-byte loads
- * where they apply).  Returns CONV2D_GI_OK, or CONV2D_GI_EINVAL for other
- * values.
- */
-CONV2D_GI_API int conv2d_gw_set_variant(int mode);
-
-/*
- * Test and diagnostic hook for the 16-byte-load grad_weight kernel: output
- * rows per pixel group (clamped to oH), LDS stages (1 or 2) and the most
- * slices of the pixel axis, for later calls in this process; 0 leaves each
- * to the planner.  A shape whose forced tile does not fit in LDS is planned
- * on the 4-byte-load kernel.  Returns CONV2D_GI_OK, or CONV2D_GI_EINVAL for
- * negative values or stages above 2.
- */
-CONV2D_GI_API int conv2d_gw_set_tile(int rows, int stages, int max_slices);
+CONV2D_GI_API int conv2d_gw_plan(conv2d_gi_params p, char *buf, size_t len);
 
 /*
  * Host-only: describe the plan the entry point would run for this shape
- * (dtype_bf16 = 0 for fp32 inputs, 1 for bf16, 2 for fp16), as text written into buf
- * (NUL-terminated, truncated to len).  Returns a status code.
+ * (dtype_bf16 = 0 for fp32 inputs, 1 for bf16, 2 for fp16), as text written
+ * into buf (NUL-terminated, truncated to len).  Returns a status code.  The
+ * test and diagnostic hooks of conv2d_grad_input_testing.h (this thread's
+ * settings) apply.
  */
-CONV2D_GI_API int conv2d_gi_plan(const conv2d_gi_params *p, int dtype_bf16, char *buf,
+CONV2D_GI_API int conv2d_gi_plan(conv2d_gi_params p, int dtype_bf16, char *buf,
                    size_t len);
-
-/*
- * Measurement hook: when both events are non-NULL, later calls from this
- * thread launch their first contraction kernel so that it records `begin`
- * with the dispatch's own start time and their last one so that it records
- * `end` with its completion time (hipExtLaunchKernelGGL), so the caller can
- * time the contraction kernels apart from the reorder prologues before them.
- * For conv2d_grad_weight both events bracket its contraction kernel alone,
- * without the slice reduction that follows it.
- * NULL, NULL switches it off.  The events (hipEvent_t) stay the caller's.
- */
-CONV2D_GI_API void conv2d_gi_set_profile_events(hipEvent_t begin, hipEvent_t end);
 
 /*
  * Free every cached scratch buffer (each after the work queued on its stream

@@ -65,6 +65,7 @@ def test_validate_accepts_workloads(lib):
 BAD = [
     dict(H=0), dict(W=-1), dict(kH=0), dict(kW=0), dict(stride=0), dict(stride=-2),
     dict(pad_h=-1), dict(pad_w=-1), dict(N=-1), dict(Ci=-1), dict(Co=-1),
+    dict(N=0), dict(Ci=0), dict(Co=0),   # zero sizes: the doppler wrappers throw on them
     dict(oH=57), dict(oW=55), dict(oH=0),
     dict(kH=61, pad_h=1, oH=1),   # H + 2*pad < kH: empty forward output
 ]
@@ -85,13 +86,23 @@ def test_validate_index_width(lib):
     assert gi.validate(p) == gi.EUNSUPPORTED
 
 
-def test_validate_null(lib):
-    assert lib.conv2d_gi_validate(None) == gi.EINVAL
+def test_validate_forward_index_width(lib):
+    """N*oH*oW above 2^31 - 1 (the folded output-pixel axis) is refused even
+    where N*H*W fits: padding beyond k - 1 makes the output plane larger than
+    the input plane."""
+    p = gi.make_params(100000, 1, 100, 100, 1, 1, 1, 1, 30, 30)   # oH = oW = 160
+    assert 100000 * 100 * 100 < 2 ** 31 and 100000 * p.oH * p.oW >= 2 ** 31
+    assert gi.validate(p) == gi.EUNSUPPORTED
+
+
+def test_params_passed_by_value(lib):
+    """The struct travels by value: the argtypes name the struct itself."""
+    assert lib.conv2d_grad_input.argtypes[3] is gi.Conv2dGiParams
+    assert lib.conv2d_gi_validate.argtypes[0] is gi.Conv2dGiParams
 
 
 def _call(lib, fn, g, w, d, p):
-    return getattr(lib, fn)(ctypes.c_void_p(g), ctypes.c_void_p(w), ctypes.c_void_p(d),
-                            ctypes.byref(p) if p is not None else None, None)
+    return getattr(lib, fn)(ctypes.c_void_p(g), ctypes.c_void_p(w), ctypes.c_void_p(d), p, None)
 
 
 @pytest.mark.parametrize("fn", ["conv2d_grad_input", "conv2d_grad_input_bf16"])
@@ -99,7 +110,6 @@ def test_entry_rejects_before_any_hip_call(lib, fn):
     """Invalid calls return EINVAL without touching the (fake) pointers."""
     good = gi.make_params(2, 3, 8, 8, 4, 3, 3, 1, 1, 1)
     fake = 0x1000
-    assert _call(lib, fn, fake, fake, fake, None) == gi.EINVAL
     bad = gi.make_params(2, 3, 8, 8, 4, 3, 3, 1, 1, 1, oH=9)
     assert _call(lib, fn, fake, fake, fake, bad) == gi.EINVAL
     assert _call(lib, fn, 0, fake, fake, good) == gi.EINVAL
@@ -109,17 +119,51 @@ def test_entry_rejects_before_any_hip_call(lib, fn):
     assert _call(lib, fn, fake, fake, fake, big) == gi.EUNSUPPORTED
 
 
-@pytest.mark.parametrize("fn", ["conv2d_grad_input", "conv2d_grad_input_bf16"])
-def test_empty_outputs_do_nothing(lib, fn):
-    """N = 0 or Ci = 0: dst has no elements, the call succeeds with no work.
-    Null is accepted exactly for the tensors that have no elements (a fake
-    pointer stands for the non-empty one, which is never read)."""
+@pytest.mark.parametrize("fn", ["conv2d_grad_input", "conv2d_grad_input_bf16",
+                                "conv2d_grad_input_f16", "conv2d_grad_weight",
+                                "conv2d_forward"])
+def test_zero_sizes_rejected(lib, fn):
+    """N, Ci or Co = 0: EINVAL before any HIP call (the fake pointers are
+    never touched), as the doppler wrappers throw on zero sizes."""
     fake = 0x1000
-    # N = 0: grad_out and dst are empty, the weight is not
-    assert _call(lib, fn, 0, fake, 0, gi.make_params(0, 3, 8, 8, 4, 3, 3, 1, 1, 1)) == gi.OK
-    assert _call(lib, fn, 0, 0, 0, gi.make_params(0, 3, 8, 8, 4, 3, 3, 1, 1, 1)) == gi.EINVAL
-    # Ci = 0: weight and dst are empty, grad_out is not
-    assert _call(lib, fn, fake, 0, 0, gi.make_params(2, 0, 8, 8, 4, 3, 3, 1, 1, 1)) == gi.OK
+    for p in (gi.make_params(0, 3, 8, 8, 4, 3, 3, 1, 1, 1),
+              gi.make_params(2, 0, 8, 8, 4, 3, 3, 1, 1, 1),
+              gi.make_params(2, 3, 8, 8, 0, 3, 3, 1, 1, 1)):
+        assert _call(lib, fn, fake, fake, fake, p) == gi.EINVAL, p
+
+
+def test_backward_rejects_before_any_hip_call(lib):
+    fake = ctypes.c_void_p(0x1000)
+    null = ctypes.c_void_p(0)
+    p = gi.make_params(2, 3, 8, 8, 4, 3, 3, 1, 1, 1)
+    # dx without the weight, dw without the input, any output without grad_out
+    assert lib.conv2d_backward(fake, null, null, fake, null, null, p, None) == gi.EINVAL
+    assert lib.conv2d_backward(fake, null, null, null, fake, null, p, None) == gi.EINVAL
+    assert lib.conv2d_backward(null, null, null, null, null, fake, p, None) == gi.EINVAL
+    assert lib.conv2d_grad_bias(fake, null, p, None) == gi.EINVAL
+    # a zero size
+    q = gi.make_params(0, 3, 8, 8, 4, 3, 3, 1, 1, 1)
+    assert lib.conv2d_backward(fake, fake, fake, fake, fake, fake, q, None) == gi.EINVAL
+    # nothing asked: nothing to do
+    assert lib.conv2d_backward(null, null, null, null, null, null, p, None) == gi.OK
+
+
+def test_hooks_are_thread_local(lib):
+    """A hook set in one thread leaves another thread's plans alone."""
+    import threading
+    s = workloads.BY_NAME["resnet_stage_3x3"].shape
+    p = gi.make_params(*s.as_tuple()[:10])
+    assert "variant=halo" in gi.plan(p)
+    seen = {}
+    old = gi.set_variant(gi.VARIANT_GENERIC)
+    try:
+        assert "variant=generic" in gi.plan(p)
+        t = threading.Thread(target=lambda: seen.setdefault("plan", gi.plan(p)))
+        t.start()
+        t.join()
+    finally:
+        gi.set_variant(old)
+    assert "variant=halo" in seen["plan"]
 
 
 def test_set_variant(lib):

@@ -125,17 +125,19 @@ def test_grad_bias_alone():
         check(out.cpu().numpy().astype(np.float64), ref, Ss, "grad_bias %r" % (shape,))
 
 
-def test_backward_empty_batch_writes_zeros():
-    sh = S(0, 5, 6, 6, 7, 3, 3, 1, 1, 1)
+def test_backward_empty_batch_rejected():
+    """N = 0 is an invalid shape: the call raises EINVAL and writes nothing."""
+    sh = S(1, 5, 6, 6, 7, 3, 3, 1, 1, 1)
     dev = torch.device("cuda:0")
-    x = torch.zeros(sh.dst_shape, device=dev)
+    x = torch.zeros((0, 5, 6, 6), device=dev)
     w = torch.zeros(sh.weight_shape, device=dev)
-    g = torch.zeros(sh.grad_out_shape, device=dev)
-    dx, dw, db = gi.backward(g, x, w, stride=1, padding=1, want_db=True,
-                             dw=torch.full(sh.weight_shape, float("nan"), device=dev),
-                             db=torch.full((sh.Co,), float("nan"), device=dev))
+    g = torch.zeros((0, 7, 6, 6), device=dev)
+    dw = torch.full(sh.weight_shape, 3.0, device=dev)
+    with pytest.raises(gi.Conv2dGiError) as e:
+        gi.backward(g, x, w, stride=1, padding=1, want_db=True, dw=dw)
+    assert e.value.code == gi.EINVAL
     torch.cuda.synchronize()
-    assert torch.all(dw == 0) and torch.all(db == 0) and dx.numel() == 0
+    assert torch.all(dw == 3.0)
 
 
 def test_backward_null_inputs_rejected():
@@ -150,12 +152,12 @@ def test_backward_null_inputs_rejected():
     ptr = lambda t: ctypes.c_void_p(t.data_ptr())
     s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     # dx without the weight, dw without the input, any output without grad_out
-    assert lib.conv2d_backward(ptr(g), null, null, ptr(d), null, null, ctypes.byref(p), s) == 1
-    assert lib.conv2d_backward(ptr(g), null, null, null, ptr(d), null, ctypes.byref(p), s) == 1
-    assert lib.conv2d_backward(null, null, null, null, null, ptr(d), ctypes.byref(p), s) == 1
-    assert lib.conv2d_grad_bias(ptr(g), null, ctypes.byref(p), s) == 1
+    assert lib.conv2d_backward(ptr(g), null, null, ptr(d), null, null, p, s) == 1
+    assert lib.conv2d_backward(ptr(g), null, null, null, ptr(d), null, p, s) == 1
+    assert lib.conv2d_backward(null, null, null, null, null, ptr(d), p, s) == 1
+    assert lib.conv2d_grad_bias(ptr(g), null, p, s) == 1
     # nothing asked: nothing to do
-    assert lib.conv2d_backward(null, null, null, null, null, null, ctypes.byref(p), s) == 0
+    assert lib.conv2d_backward(null, null, null, null, null, null, p, s) == 0
 
 
 @pytest.mark.parametrize("name", ["resnet_stage_3x3", "strided_downsample", "stem_7x7_s2",

@@ -109,11 +109,12 @@ def test_forward_variant_hook_rejects_strided():
         gi.set_fwd_variant(0)
 
 
-def test_forward_empty_batch():
+def test_forward_empty_batch_rejected():
     dev = torch.device("cuda:0")
-    y = gi.forward(torch.zeros((0, 4, 6, 6), device=dev), torch.zeros((5, 4, 3, 3), device=dev),
+    with pytest.raises(gi.Conv2dGiError) as e:
+        gi.forward(torch.zeros((0, 4, 6, 6), device=dev), torch.zeros((5, 4, 3, 3), device=dev),
                    stride=1, padding=1)
-    assert tuple(y.shape) == (0, 5, 6, 6)
+    assert e.value.code == gi.EINVAL
 
 
 @pytest.mark.parametrize("idx", [0, 5, 6])

@@ -148,11 +148,11 @@ def test_grad_weight_forced_tiles(rows, stages, slices):
         gi.set_gw_variant(0)
 
 
-def test_grad_weight_empty_batch_writes_zeros():
+def test_grad_weight_empty_batch_rejected():
     sh = S(0, 5, 6, 6, 7, 3, 3, 1, 1, 1)
-    got, ok = run_gw(np.zeros(sh.dst_shape, np.float32), np.zeros(sh.grad_out_shape, np.float32),
-                     sh)
-    assert ok and np.array_equal(got, np.zeros(sh.weight_shape))
+    with pytest.raises(gi.Conv2dGiError) as e:
+        run_gw(np.zeros(sh.dst_shape, np.float32), np.zeros(sh.grad_out_shape, np.float32), sh)
+    assert e.value.code == gi.EINVAL
 
 
 def test_grad_weight_wide_kernels():

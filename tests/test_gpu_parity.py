@@ -327,13 +327,14 @@ def test_deterministic():
     assert np.array_equal(a, b)
 
 
-def test_zero_output_channels_zero_fill():
-    """Co = 0: every sum is empty, so dst must be all zeros (not left as is)."""
+def test_zero_output_channels_rejected():
+    """Co = 0 is an invalid shape: EINVAL, and dst keeps what it held."""
     s = workloads.Shape(2, 5, 6, 6, 0, 3, 3, 1, 1, 1)
     g = np.zeros(s.grad_out_shape, np.float32)
     w = np.zeros(s.weight_shape, np.float32)
-    got, ok = run_gpu(g, w, s, "f32")
-    assert ok and np.array_equal(got, np.zeros(s.dst_shape))
+    with pytest.raises(gi.Conv2dGiError) as e:
+        run_gpu(g, w, s, "f32")
+    assert e.value.code == gi.EINVAL
 
 
 def test_side_stream():
