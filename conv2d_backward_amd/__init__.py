@@ -17,7 +17,7 @@ import ctypes
 import os
 
 __all__ = [
-    "grad_input", "Conv2dGiParams", "Conv2dGiError", "LibraryNotBuilt", "load_library",
+    "grad_input", "grad_input_noalloc", "Conv2dGiParams", "Conv2dGiError", "LibraryNotBuilt", "load_library",
     "make_params", "validate", "plan", "grad_weight", "grad_weight_plan", "grad_bias", "backward", "forward", "forward_plan", "set_fwd_variant", "set_variant", "set_halo_tile", "set_halo_split", "set_halo_fusion", "set_gw_variant", "set_gw_tile", "release_workspaces", "set_profile_events", "library_path", "exported_names",
     "OK", "EINVAL", "EUNSUPPORTED", "EHIP", "VARIANT_AUTO", "VARIANT_GENERIC", "VARIANT_HALO", "VARIANT_STEM",
 ]
@@ -69,6 +69,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.conv2d_grad_input_bf16.argtypes = [P, P, P, PP, P]
     lib.conv2d_grad_input_bf16.restype = ctypes.c_int
     lib.conv2d_grad_input_f16.argtypes = [P, P, P, PP, P]
+    lib.conv2d_grad_input_noalloc.argtypes = [P, P, P, PP, P]
+    lib.conv2d_grad_input_noalloc.restype = ctypes.c_int
     lib.conv2d_grad_input_f16.restype = ctypes.c_int
     lib.conv2d_gi_validate.argtypes = [PP]
     lib.conv2d_gi_validate.restype = ctypes.c_int
@@ -118,6 +120,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
 def exported_names():
     """Names of the C entry points the binding wraps."""
     return ["conv2d_grad_input", "conv2d_grad_input_bf16", "conv2d_grad_input_f16",
+            "conv2d_grad_input_noalloc",
             "conv2d_grad_weight",
             "conv2d_backward", "conv2d_grad_bias", "conv2d_forward", "conv2d_fwd_plan",
             "conv2d_fwd_set_variant",
@@ -263,6 +266,36 @@ def grad_input(grad_out, weight, *, stride: int, padding, input_hw, out=None, st
         code = fn(ctypes.c_void_p(grad_out.data_ptr()), ctypes.c_void_p(weight.data_ptr()),
                   ctypes.c_void_p(out.data_ptr()), p,
                   ctypes.c_void_p(s.cuda_stream))
+    _check(code)
+    return out
+
+
+def grad_input_noalloc(grad_out, weight, *, stride: int, padding, input_hw, out, stream=None):
+    """fp32 grad_input through ``conv2d_grad_input_noalloc``: the library
+    allocates nothing (its scratch is a fixed per-GPU array; plans needing more
+    raise with EUNSUPPORTED).  ``out`` (float32 [N, Ci, H, W], contiguous) is
+    required.  Calls that can overlap on one GPU race on that array."""
+    import torch
+
+    if isinstance(padding, int):
+        padding = (padding, padding)
+    pad_h, pad_w = (int(v) for v in padding)
+    H, W = (int(v) for v in input_hw)
+    for t in (grad_out, weight, out):
+        if t.dim() != 4 or not t.is_cuda or t.device != grad_out.device:
+            raise ValueError("grad_out, weight and out must be 4-D tensors on one GPU device")
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("grad_out, weight and out must be contiguous float32")
+    N, Co, oH, oW = (int(v) for v in grad_out.shape)
+    Co_w, Ci, kH, kW = (int(v) for v in weight.shape)
+    if Co_w != Co or tuple(out.shape) != (N, Ci, H, W):
+        raise ValueError("inconsistent shapes: weight [Co,Ci,kH,kW], out [N,Ci,H,W]")
+    p = Conv2dGiParams(N, Ci, H, W, Co, kH, kW, int(stride), pad_h, pad_w, oH, oW)
+    lib = load_library()
+    with torch.cuda.device(grad_out.device):
+        s = stream if stream is not None else torch.cuda.current_stream(grad_out.device)
+        code = lib.conv2d_grad_input_noalloc(_ptr(grad_out), _ptr(weight), _ptr(out), p,
+                                             ctypes.c_void_p(s.cuda_stream))
     _check(code)
     return out
 

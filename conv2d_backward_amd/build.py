@@ -29,6 +29,7 @@ SOURCES = [
     "kernels_stem_f32.hip",
     "kernels_gw_f32.hip",
     "kernels_fwd_f32.hip",
+    "noalloc.hip",
 ]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", "-Werror",

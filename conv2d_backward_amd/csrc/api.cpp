@@ -22,6 +22,7 @@
 #include "fwd_common.h"
 #include "gw_common.h"
 #include "half_launch.h"
+#include "api_internal.h"
 
 namespace {
 
@@ -715,9 +716,12 @@ Plan make_plan(const conv2d_gi_params &p, bool bf16) {
 
 // dt: 0 fp32 inputs, 1 bf16, 2 fp16 (the 16-bit kinds share plans, prologues
 // and kernels up to the MFMA instruction).
+// ext_ws, when not null, is caller-provided scratch of ext_cap bytes used in
+// place of the per-stream cache (no allocation, no cache lock); a plan that
+// needs more returns CONV2D_GI_EUNSUPPORTED before any HIP call.
 template <typename T>
 int run(const T *grad_out, const T *weight, float *dst, const conv2d_gi_params *p,
-        hipStream_t stream, int dt) {
+        hipStream_t stream, int dt, void *ext_ws = nullptr, size_t ext_cap = 0) {
     const bool bf16 = dt != 0;   // a 16-bit input kind
     const bool f16 = dt == 2;
     int rc = validate(p);
@@ -725,14 +729,19 @@ int run(const T *grad_out, const T *weight, float *dst, const conv2d_gi_params *
     if (!dst || !grad_out || !weight) return CONV2D_GI_EINVAL;
 
     Plan plan = make_plan(*p, bf16);
+    if (ext_ws && plan.ws_bytes > ext_cap) return CONV2D_GI_EUNSUPPORTED;
     void *ws = nullptr;
     hipError_t e;
     int dev = 0;
     e = hipGetDevice(&dev);
     if (e != hipSuccess) return fail_hip(e);
-    std::lock_guard<std::recursive_mutex> lock(g_ws_mu);
+    std::unique_lock<std::recursive_mutex> lock(g_ws_mu, std::defer_lock);
+    if (!ext_ws) lock.lock();
     if (plan.ws_bytes > 0) {
-        e = workspace_for(dev, stream, plan.ws_bytes, &ws);
+        if (ext_ws)
+            ws = ext_ws;
+        else
+            e = workspace_for(dev, stream, plan.ws_bytes, &ws);
         if (e != hipSuccess) return fail_hip(e);
         const int kHW = p->kH * p->kW;
         if (plan.variant == CONV2D_GI_VARIANT_HALO && bf16) {
@@ -1334,6 +1343,28 @@ std::string describe_forward(const conv2d_gi_params &p) {
 }
 
 }  // namespace
+
+namespace gi {
+
+int record_hip_error(hipError_t e) { return fail_hip(e); }
+
+// Scratch bytes the fp32 grad_input plan for p needs (0 when the shape is
+// invalid); host only.
+size_t grad_input_f32_scratch_bytes(const conv2d_gi_params &p) {
+    if (validate(&p) != CONV2D_GI_OK) return 0;
+    return make_plan(p, false).ws_bytes;
+}
+
+// fp32 grad_input on caller-provided device scratch (cap bytes): nothing is
+// allocated and the per-stream cache is not touched.
+int grad_input_f32_on_scratch(const float *grad_out, const float *weight, float *dst,
+                              const conv2d_gi_params &p, hipStream_t stream, void *scratch,
+                              size_t cap) {
+    if (!scratch) return CONV2D_GI_EINVAL;
+    return run<float>(grad_out, weight, dst, &p, stream, 0, scratch, cap);
+}
+
+}  // namespace gi
 
 extern "C" {
 

@@ -52,6 +52,8 @@
  * library ran on must outlive its buffers: call conv2d_gi_release_workspaces
  * (which waits for each stream's queued work, then frees) before destroying
  * it, or a new stream that receives the same handle would inherit them.
+ * conv2d_grad_input_noalloc (below) allocates nothing and uses a fixed
+ * per-device buffer instead.
 
  * Asynchrony and errors
  * ---------------------
@@ -142,6 +144,28 @@ CONV2D_GI_API int conv2d_grad_input_bf16(const uint16_t *grad_out, const uint16_
 CONV2D_GI_API int conv2d_grad_input_f16(const uint16_t *grad_out, const uint16_t *weight,
                                         float *dst, conv2d_gi_params p,
                                         hipStream_t stream);
+
+/*
+ * fp32 grad_input that allocates nothing: for callers that cannot call
+ * hipMalloc (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments, result and validation as
+ * conv2d_grad_input; the caller still passes every input and output.
+ *
+ * The scratch the fp32 plans need (the weight reordered into kernel order,
+ * about Co*Ci*kH*kW floats; the Ci <= 4 plan needs none) is a fixed
+ * CONV2D_GI_NOALLOC_SCRATCH_BYTES device array inside the library, one copy
+ * per GPU, held until the process ends.  A shape whose plan needs more returns
+ * CONV2D_GI_EUNSUPPORTED before anything is enqueued.  Every call on one GPU
+ * uses that GPU's array: calls that can overlap on a GPU (different streams
+ * with no ordering between them) race, so callers keep them on one stream or
+ * order them with events.  Nothing is carried from one call to the next.
+ * The first call on a device looks the array's device address up
+ * (hipGetSymbolAddress); a failure there returns CONV2D_GI_EHIP.
+ */
+#define CONV2D_GI_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+CONV2D_GI_API int conv2d_grad_input_noalloc(const float *grad_out, const float *weight,
+                                            float *dst, conv2d_gi_params p,
+                                            hipStream_t stream);
 
 /* Host-only check of a shape, as done by the entry points (no HIP call). */
 CONV2D_GI_API int conv2d_gi_validate(conv2d_gi_params p);

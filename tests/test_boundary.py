@@ -132,6 +132,18 @@ def test_zero_sizes_rejected(lib, fn):
         assert _call(lib, fn, fake, fake, fake, p) == gi.EINVAL, p
 
 
+def test_noalloc_rejects_before_any_hip_call(lib):
+    """The no-allocation entry point: bad shapes and null pointers return
+    EINVAL, and a plan needing more than its fixed scratch EUNSUPPORTED, all
+    before any HIP call (no GPU here)."""
+    fake = 0x1000
+    fn = "conv2d_grad_input_noalloc"
+    assert _call(lib, fn, fake, fake, fake, gi.make_params(0, 3, 8, 8, 4, 3, 3, 1, 1, 1)) == gi.EINVAL
+    assert _call(lib, fn, 0, fake, fake, gi.make_params(2, 3, 8, 8, 4, 3, 3, 1, 1, 1)) == gi.EINVAL
+    big = gi.make_params(1, 1024, 4, 4, 1024, 3, 3, 1, 1, 1)   # ~37.7 MB weight image
+    assert _call(lib, fn, fake, fake, fake, big) == gi.EUNSUPPORTED
+
+
 def test_backward_rejects_before_any_hip_call(lib):
     fake = ctypes.c_void_p(0x1000)
     null = ctypes.c_void_p(0)
