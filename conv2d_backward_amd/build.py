@@ -26,6 +26,7 @@ SOURCES = [
     "kernels_generic.hip",
     "kernels_halo_f32.hip",
     "kernels_halo_bf16.hip",
+    "kernels_img16.hip",
     "kernels_stem_f32.hip",
     "kernels_gw_f32.hip",
     "kernels_fwd_f32.hip",

@@ -162,6 +162,15 @@ struct HaloBf16Plan {
     double cost = 0.0;
 };
 
+// A whole-image 16-bit plan (stride 1): a weight prologue and one launch.
+struct Img16Plan {
+    gi::Img16Args args{};
+    int cfg = -1;
+    size_t lds = 0;
+    size_t wk_bytes = 0;   // workspace: the weight fragment image
+    int wtiles = 0;        // its 64-channel ci tiles
+};
+
 // A small-Ci plan (fp32, Ci <= 4): one prologue and one launch.
 struct StemPlan {
     gi::StemArgs args{};
@@ -175,6 +184,8 @@ struct Plan {
     std::vector<Launch> launches;  // generic
     HaloPlan halo;                 // halo, fp32
     HaloBf16Plan hb;               // halo, bf16
+    bool img16 = false;            // 16-bit inputs on the whole-image kernel
+    Img16Plan im;
     StemPlan stem;                 // small Ci, fp32
 };
 
@@ -521,6 +532,66 @@ bool plan_halo_bf16(const conv2d_gi_params &p, HaloBf16Plan &out) {
     return true;
 }
 
+// Whole-image 16-bit plan (stride 1): one work-group per (image, 128 input
+// channels), every pixel of the image in the wave's 16-pixel blocks.  Needs
+// an instance for the pixel blocks, taps, kernel width and halo pitch, a
+// grad_out plane of whole 4-pixel quads of which 8 planes fit a wave's 4 KB
+// landing area, and 32-bit byte offsets.
+bool plan_img16(const conv2d_gi_params &p, Img16Plan &out) {
+    if (p.stride != 1) return false;
+    const int HW = p.H * p.W, oHW = p.oH * p.oW;
+    // Each wave copies 8 grad_out planes (plus up to 8 bytes of alignment)
+    // into a 4 KB landing area, and its lanes take one 4-pixel quad each.
+    if (oHW % 4 != 0 || 8 + 16 * oHW > 4096) return false;
+    const int HR = p.H + p.kH - 1, HC = p.W + p.kW - 1;
+    const int HP = round_to_residue(HC, 16, p.W % 16);
+    int cfg = -1;
+    for (int nb = 1; nb <= 16 && cfg < 0; ++nb)
+        if (HW <= 16 * nb) cfg = gi::img16_config(nb, p.kH, p.kW, HP, HR);
+    if (cfg < 0) return false;
+    // Slots past the image read position j16 + the tap shift: inside the plane.
+    if (15 + (p.kH - 1) * HP + p.kW - 1 >= HR * HP) return false;
+    const int nchunks = (p.Co + 31) / 32;
+    const int wtiles = (p.Ci + 63) / 64;
+    const int ci_tiles = (p.Ci + 127) / 128;
+    const int64_t lim = 0x7fff0000LL;
+    const int64_t wk = (int64_t)wtiles * nchunks * p.kH * p.kW * 4096;
+    if (wk > lim || (int64_t)p.N * p.Co * oHW * 2 > lim ||
+        (int64_t)p.N * p.Ci * HW * 4 > lim || (int64_t)p.N * ci_tiles > INT32_MAX)
+        return false;
+    const int PS = gi::img16_plane(cfg);
+    const size_t lds = gi::img16_lds(cfg);
+    if (lds > kLdsBytes) return false;
+    gi::Img16Args &a = out.args;
+    a = gi::Img16Args{};
+    a.g_bytes = (uint32_t)((int64_t)p.N * p.Co * oHW * 2);
+    a.wk_bytes = (uint32_t)wk;
+    a.d_bytes = (uint32_t)((int64_t)p.N * p.Ci * HW * 4);
+    a.N = p.N;
+    a.Ci = p.Ci;
+    a.H = p.H;
+    a.W = p.W;
+    a.Co = p.Co;
+    a.oH = p.oH;
+    a.oW = p.oW;
+    a.kH = p.kH;
+    a.kW = p.kW;
+    a.oy = p.kH - 1 - p.pad_h;
+    a.ox = p.kW - 1 - p.pad_w;
+    a.HR = HR;
+    a.HC = HC;
+    a.HP = HP;
+    a.PS = PS;
+    a.nchunks = nchunks;
+    a.ci_tiles = ci_tiles;
+    a.nq = oHW / 4;
+    out.cfg = cfg;
+    out.lds = lds;
+    out.wk_bytes = (size_t)wk;
+    out.wtiles = wtiles;
+    return true;
+}
+
 // Small-Ci plan (fp32, Ci <= 4): 16 x 16 phase-grid tiles; phase groups of
 // near-equal tap totals, run in sets of up to two per work-group over one
 // grad_out halo.  Every phase's tap count must be one the kernel is built
@@ -704,8 +775,19 @@ Plan make_plan(const conv2d_gi_params &p, bool bf16) {
         plan.ws_bytes = plan.stem.ws_bytes;
         return plan;
     }
+    // 16-bit inputs: the whole-image kernel where it applies and fills the
+    // chip (a work-group per image and 128 channels), or when the tile hook
+    // asks for its 13 blocks; else the halo-tile kernel.
     if (bf16 && (forced == CONV2D_GI_VARIANT_HALO || forced == CONV2D_GI_VARIANT_AUTO) &&
-        plan_halo_bf16(p, plan.hb)) {
+        (g_tile_nb == 0 || g_tile_nb == 13) && plan_img16(p, plan.im) &&
+        (g_tile_nb == 13 || (int64_t)p.N * plan.im.args.ci_tiles >= kCUs)) {
+        plan.variant = CONV2D_GI_VARIANT_HALO;
+        plan.img16 = true;
+        plan.ws_bytes = plan.im.wk_bytes;
+        return plan;
+    }
+    if (bf16 && (forced == CONV2D_GI_VARIANT_HALO || forced == CONV2D_GI_VARIANT_AUTO) &&
+        g_tile_nb != 13 && plan_halo_bf16(p, plan.hb)) {
         plan.variant = CONV2D_GI_VARIANT_HALO;
         plan.ws_bytes = plan.hb.gp_bytes + plan.hb.wk_bytes;
         return plan;
@@ -744,7 +826,10 @@ int run(const T *grad_out, const T *weight, float *dst, const conv2d_gi_params *
             e = workspace_for(dev, stream, plan.ws_bytes, &ws);
         if (e != hipSuccess) return fail_hip(e);
         const int kHW = p->kH * p->kW;
-        if (plan.variant == CONV2D_GI_VARIANT_HALO && bf16) {
+        if (plan.variant == CONV2D_GI_VARIANT_HALO && plan.img16) {
+            e = gi::launch_weight_frag16((const uint16_t *)weight, (uint16_t *)ws, p->Co, p->Ci,
+                                         kHW, plan.im.args.nchunks, plan.im.wtiles, stream);
+        } else if (plan.variant == CONV2D_GI_VARIANT_HALO && bf16) {
             HaloBf16Plan &h = plan.hb;
             uint16_t *gp = (uint16_t *)ws;
             uint16_t *wk = (uint16_t *)((char *)ws + h.gp_bytes);
@@ -775,6 +860,14 @@ int run(const T *grad_out, const T *weight, float *dst, const conv2d_gi_params *
             a.w = (const float *)weight;
             a.dst = dst;
             e = gi::launch_stem_f32(a, stream, ev);
+        }
+    } else if (plan.variant == CONV2D_GI_VARIANT_HALO && plan.img16) {
+        if (e == hipSuccess) {
+            Img16Plan &m = plan.im;
+            m.args.g = (const uint16_t *)grad_out;
+            m.args.wk = (const uint16_t *)ws;
+            m.args.dst = dst;
+            e = gi::launch_img16(m.args, m.cfg, f16, m.lds, stream, ev);
         }
     } else if (plan.variant == CONV2D_GI_VARIANT_HALO && bf16) {
         if (e == hipSuccess) {
@@ -1098,6 +1191,16 @@ std::string describe(const Plan &plan, int dt) {
                  " px=" + std::to_string(ph.Ha) + "x" + std::to_string(ph.Wb);
         }
         s += "]";
+        return s;
+    }
+    if (plan.variant == CONV2D_GI_VARIANT_HALO && plan.img16) {
+        const Img16Plan &m = plan.im;
+        const gi::Img16Args &a = m.args;
+        s += " launches=2 [image kernel cfg=" + std::to_string(m.cfg) +
+             " nb=" + std::to_string(gi::img16_blocks(m.cfg)) + " wgs=" + std::to_string(a.N) +
+             "x" + std::to_string(a.ci_tiles) + " lds=" + std::to_string(m.lds) +
+             " halo=" + std::to_string(a.HR) + "x" + std::to_string(a.HC) + " pitch=" +
+             std::to_string(a.HP) + " chunks=" + std::to_string(a.nchunks) + "]";
         return s;
     }
     if (plan.variant == CONV2D_GI_VARIANT_HALO && bf16) {

@@ -197,3 +197,32 @@ struct StemArgs {
 
 }  // namespace gi
 
+namespace gi {
+
+// Arguments of the whole-image 16-bit kernel (kernels_img16.hip, stride 1).
+// A work-group owns one image and 128 input channels; grad_out is read from
+// the caller's NCHW tensor (no padded copy) and the weight from the fragment
+// image wk of the bf16 halo kernel (layout above; its ci tiles are 64 wide,
+// so a 128-channel work-group reads two of them).
+//
+// LDS: two stages, each 4 channel planes of PS bytes; plane g of a stage
+// holds output channels chunk*32 + 8g .. +7 as 16-byte positions, halo row
+// pitch HP, and position (hr, hc) holds grad_out[hr - oy][hc - ox], zero
+// outside the grad_out plane (the transposed padding: oy = kH-1-pad_h,
+// ox = kW-1-pad_w).  Input pixel (ih, iw) at tap (kh, kw) reads position
+// (ih + kH-1-kh, iw + kW-1-kw).
+struct Img16Args {
+    const uint16_t *g;      // grad_out [N, Co, oH, oW], bf16 or fp16 bits
+    const uint16_t *wk;     // weight fragment image (64-channel ci tiles)
+    float *dst;             // [N, Ci, H, W] fp32
+    uint32_t g_bytes, wk_bytes, d_bytes;
+    int32_t N, Ci, H, W, Co, oH, oW, kH, kW;
+    int32_t oy, ox;         // halo position of grad_out pixel (0, 0)
+    int32_t HR, HC, HP;     // halo rows (H + kH - 1), columns (W + kW - 1), row pitch
+    int32_t PS;             // LDS bytes of one channel plane (multiple of 256)
+    int32_t nchunks;        // ceil(Co / 32)
+    int32_t ci_tiles;       // ceil(Ci / 128); grid = N * ci_tiles (1-D, xcd_order)
+    int32_t nq;             // 4-pixel quads of one grad_out plane: oH * oW / 4
+};
+
+}  // namespace gi

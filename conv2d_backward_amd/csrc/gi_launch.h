@@ -79,6 +79,22 @@ hipError_t launch_prologues_bf16(const uint16_t *g, uint16_t *gp, const uint16_t
                                  const HaloBf16Args &a, int oH, int oW, int pad_h, int pad_w,
                                  int ci_tiles, hipStream_t s);
 
+// Whole-image 16-bit kernel (kernels_img16.hip), stride 1: one work-group
+// per (image, 128 input channels).  img16_config returns the instantiation
+// for (pixel blocks of 16, taps, kernel width, halo pitch, halo rows), -1 if
+// none; img16_plane the LDS bytes of one channel plane it is built for,
+// img16_lds the dynamic LDS of a launch.
+int img16_config(int nb, int kH, int kW, int hp, int hr);
+int img16_blocks(int cfg);
+int img16_plane(int cfg);
+size_t img16_lds(int cfg);
+hipError_t launch_img16(const Img16Args &a, int cfg, bool f16, size_t lds, hipStream_t s,
+                        const KernelEvents &ev);
+// Weight -> fragment image wk (layout of HaloBf16Args.wk) for Co output and
+// Ci input channels, kHW taps, nchunks chunks of 32, wtiles ci tiles of 64.
+hipError_t launch_weight_frag16(const uint16_t *w, uint16_t *wk, int Co, int Ci, int kHW,
+                                int nchunks, int wtiles, hipStream_t s);
+
 // Small-Ci fp32 kernel (kernels_stem_f32.hip): Ci <= 4, any stride whose
 // phases have a tap count in the served set (stem_f32_taps_ok).
 bool stem_f32_taps_ok(int taps);

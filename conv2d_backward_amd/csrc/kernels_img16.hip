@@ -1,0 +1,451 @@
+// kernels_img16.hip -- whole-image implicit-GEMM kernel for 16-bit inputs
+// (bf16 or fp16) on gfx950, stride 1, fp32 accumulation and output.
+//
+// The contraction is the implicit GEMM of meganeura conv2d_grad_input_gemm.wgsl
+// (header comment: C[Ci, pixels] = A[Ci, K] x B[K, pixels], K = Co*kH*kW),
+// with K ordered (chunk of 32 output channels, tap, channel).  The 16-bit
+// matrix cores take 8 consecutive k per lane from both operands:
+//   * A (the weight read as [Ci, K]) comes from a fragment image that a
+//     prologue writes in the exact lane order of the MFMA A fragments;
+//   * B (the im2col of grad_out) is read from the caller's NCHW tensor and
+//     turned channel-minor on its way into LDS: each thread loads 8 channels
+//     x 4 consecutive pixels (eight 8-byte loads), transposes the 8 x 4 block
+//     of 16-bit values in registers (v_perm_b32) and writes 4 positions of 8
+//     channels (16 bytes each).  Positions outside the grad_out plane stay
+//     zero: that border is the transposed padding kH-1-pad of the shader's
+//     header comment.
+//
+// Work-group: 256 threads (4 waves) own one image and 128 input channels.
+// Wave w owns input-channel blocks 2w, 2w+1 (16 channels each) and all NB
+// pixel blocks of 16 of the image, so no A fragment is loaded by two waves,
+// and the image's pixels fill the blocks with at most 15 slots to spare (the
+// 14 x 14 deep stage: 196 pixels in 208 slots).  Per chunk of 32 output
+// channels and tap, a wave issues 2 x NB MFMAs, 2 A-fragment loads (from L2,
+// several taps ahead) and NB LDS reads (the next tap's B fragments).  The
+// next chunk's grad_out block is loaded into registers while the current
+// chunk computes, and transposed into the other LDS stage at its end.
+//
+// LDS banks: a 16-byte-per-lane LDS read is served 16 lanes per cycle (64
+// banks of 4 bytes); within each half of the wave, the lanes whose index bits
+// 2, 3 and 4 have even parity form one cycle and the odd ones the other.
+// Each channel plane starts at a multiple of 256 bytes and halo rows sit HP
+// positions apart with HP = W (mod 16), so the 16 pixels of a block (which
+// wrap across image rows) sit at 16 positions that are consecutive mod 16
+// whatever the tap shift: every cycle's lanes touch 16 different bank groups.
+//
+// V_MFMA_F32_16X16X32_BF16 / _F16: lane l = 16*g + i supplies A[i][k = 8g ..
+// 8g+7] and B[k = 8g .. 8g+7][i] and receives D[4g + r][i], r = 0..3.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "gi_common.h"
+#include "gi_launch.h"
+
+namespace gi {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+
+namespace {
+
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9)
+constexpr int kOOB = 0x7ffffff0;         // byte offset past the end of every buffer
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (long)bytes, kRsrcWord3);
+}
+
+// Low (sel = kLo) or high (kHi) 16-bit halves of a and b packed as
+// half(a) | half(b) << 16.
+constexpr unsigned kLo = 0x05040100u, kHi = 0x07060302u;
+__device__ __forceinline__ unsigned pack2(unsigned a, unsigned b, unsigned sel) {
+    return __builtin_amdgcn_perm(b, a, sel);
+}
+
+// F16: fp16 inputs (V_MFMA_F32_16X16X32_F16), else bf16.  NB pixel blocks of
+// 16 per wave (the image's pixels, H*W <= 16*NB), T taps, KW the kernel
+// width, HPT the halo pitch and HRT the most halo rows (all fixed at compile
+// time; A.PS must equal the plane size they give).
+template <int HRT, int HPT>
+constexpr int img16_plane_bytes() { return (HRT * HPT * 16 + 255) / 256 * 256; }
+
+constexpr int kLand = 4096;    // landing area of one wave's direct loads (4 x 1 KB)
+constexpr int kStages = 3;     // LDS stages of channel planes
+
+// Three stages of 4 channel planes, then the 4 waves' landing areas.
+template <int HRT, int HPT>
+constexpr int img16_lds_bytes() { return kStages * 4 * img16_plane_bytes<HRT, HPT>() + 4 * kLand; }
+
+template <bool F16, int NB, int T, int KW, int HPT, int HRT>
+__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void gi_img16(
+    const Img16Args A) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    constexpr int KH = T / KW;
+    constexpr int HP = HPT;
+    constexpr int PS = img16_plane_bytes<HRT, HPT>();   // bytes of one channel plane
+    constexpr int kStage = 4 * PS;                      // bytes of one stage: 4 planes
+    // Within a chunk's taps: the next chunk is transposed into its stage
+    // during tap kStageTap and made visible by the barrier of tap kBarTap;
+    // the last tap reads the next chunk's first B fragments.
+    constexpr int kStageTap = T > 2 ? 2 : 0;
+    constexpr int kBarTap = T > 4 ? 4 : T - 1;
+    static_assert(kStageTap <= kBarTap && kBarTap < T, "tap schedule");
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j16 = lane & 15, g = lane >> 4;
+
+    // Logical order: image fastest, then the 128-channel tile, so the
+    // work-groups of one L2 (a contiguous logical range, xcd_order) share the
+    // weight fragments of one or two tiles.
+    const int J = xcd_order(blockIdx.x, gridDim.x);
+    const int ci_tile = J / A.N;
+    const int n = J - ci_tile * A.N;
+
+    const __amdgpu_buffer_rsrc_t grs = make_rsrc(A.g, A.g_bytes);
+    const __amdgpu_buffer_rsrc_t wrs = make_rsrc(A.wk, A.wk_bytes);
+    const __amdgpu_buffer_rsrc_t drs = make_rsrc(A.dst, A.d_bytes);
+
+    // Staging.  Wave w stages channels 8w .. 8w+7 of every chunk: four
+    // 16-byte direct loads per lane copy those 8 channel planes of grad_out
+    // (contiguous in NCHW) into the wave's own 4 KB landing area a chunk
+    // ahead, and lane q later transposes pixel quad q of them (8 channels x
+    // 4 pixels: eight 8-byte LDS reads and 16 v_perm_b32) into 4 positions
+    // of the chunk's stage.  A wave transposes only what it loaded itself, so
+    // its own load counter is the only wait.  The copy starts at the 16-byte
+    // boundary at or below the planes, which then sit `shift` bytes into the
+    // landing area (0 or 8: whole 4-pixel quads keep every plane 8-byte
+    // aligned).
+    const int oHW = A.oH * A.oW;
+    const int plane_bytes = oHW * 2;
+    const int chunk_bytes = 32 * plane_bytes;
+    const int base = (n * A.Co + 8 * wave) * plane_bytes;
+    const int shift = base & 15;
+    const int loff = base - shift + lane * 16;   // + 1024 * load, + chunk * chunk_bytes
+    unsigned char *const land = smem + kStages * kStage + wave * kLand;
+    // Every wave issues all four loads per chunk (past the tensor they read
+    // zeros, past the chunk's channels data the transposition ignores), so
+    // the number of loads in flight is known at compile time.
+    auto sload = [&](int c) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(grs, (lds_ptr_t)(land + 1024 * k), 16,
+                                                     loff + 1024 * k, c * chunk_bytes, 0, 0);
+    };
+    // LDS byte offset (within a stage) of each pixel of quad `lane`, -1
+    // outside the halo (only with padding beyond kH-1) or past the plane.
+    const bool qv = lane < A.nq;
+    int wpos[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int p = 4 * lane + k;
+        const int oh = p / A.oW, ow = p - (p / A.oW) * A.oW;
+        const int hr = oh + A.oy, hc = ow + A.ox;
+        const bool v = qv && hr >= 0 && hr < A.HR && hc >= 0 && hc < A.HC;
+        wpos[k] = v ? wave * PS + (hr * HP + hc) * 16 : -1;
+    }
+    // Transpose quad `lane` of the landed planes of chunk c (channels past
+    // Co read as 0) into stage `buf`.
+    auto swrite = [&](int c, int buf) {
+        const int room = A.Co - 32 * c - 8 * wave;   // channels of the wave's 8 that exist
+        v2u v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            v[i] = *(const v2u *)(land + shift + i * plane_bytes + 8 * lane);
+            if (i >= room) v[i] = v2u{0u, 0u};
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if (wpos[k] < 0) continue;
+            const unsigned sel = (k & 1) ? kHi : kLo;
+            v4u o;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const unsigned a = (k < 2) ? v[2 * m].x : v[2 * m].y;
+                const unsigned b = (k < 2) ? v[2 * m + 1].x : v[2 * m + 1].y;
+                o[m] = pack2(a, b, sel);
+            }
+            *(v4u *)(smem + buf * kStage + wpos[k]) = o;
+        }
+    };
+
+    // A fragments: wave w's ci blocks 2w, 2w+1 of the 128-channel tile are
+    // blocks 2*(w&1) + cb of the image's 64-channel tile 2*ci_tile + (w>>1).
+    // Past the last chunk the offset is out of range (zeros); every prefetch
+    // is issued unconditionally so the compiler's wait counts stay exact.
+    const int t64 = 2 * ci_tile + (wave >> 1);
+    const int wlane = ((t64 * A.nchunks * T) * 4 + 2 * (wave & 1)) * 1024 + lane * 16;
+    auto aload = [&](int chunk, int tap, int cb) {
+        const int soff = chunk < A.nchunks ? ((chunk * T + tap) * 4 + cb) * 1024 : kOOB;
+        return __builtin_bit_cast(v8bf, __builtin_amdgcn_raw_buffer_load_b128(wrs, wlane, soff, 0));
+    };
+
+    // This lane's pixel in each block: LDS byte offset of its halo position
+    // in plane g of a stage.  Slots past the image read position j16 (their
+    // column is never stored; distinct positions keep the read conflict-free).
+    const int HW = A.H * A.W;
+    int bbase[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        const int p = b * 16 + j16;
+        const int ih = p / A.W, iw = p - (p / A.W) * A.W;
+        bbase[b] = g * PS + (p < HW ? ih * HP + iw : j16) * 16;
+    }
+
+    // Zero the stages: positions the staging never writes (the border) stay
+    // zero for the whole kernel.
+    for (int i = tid; i < kStages * kStage / 16; i += 256) ((v4u *)smem)[i] = v4u{0u, 0u, 0u, 0u};
+
+    v4f acc[2][NB];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[cb][b] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    // Byte offset of tap tp in stage `st`: the stage plus a shift of
+    // (kH-1-kh) rows and (kW-1-kw) columns; a compile-time immediate.
+    auto tap_offset = [&](int st, int tp) {
+        const int kh = tp / KW, kw = tp - (tp / KW) * KW;
+        return st * kStage + ((KH - 1 - kh) * HP + (KW - 1 - kw)) * 16;
+    };
+
+    // A ring of T slots indexed by tap: step s = chunk*T + tap uses slot
+    // tap, and step s + AD is loaded while step s computes.  Every chunk
+    // brings fresh weight lines, which each L2 fetches once for all of its
+    // work-groups, so their first use waits for memory beyond the L2: they
+    // are fetched nearly a chunk ahead.
+    constexpr int AD = T - 1;
+    static_assert(AD >= 1, "prefetch distance");
+    v8bf fa[T][2];
+    v8bf fb[NB];
+    // Loads issued after a chunk's landing loads until the next chunk's
+    // transposition: every tap's two A prefetches in between.
+    constexpr int kAfterLanding = 2 * T;
+
+    // Set-up: chunk 0 staged into stage 0, chunk 1's copy in flight, the
+    // first A fragments in flight, chunk 0's first B fragments read.
+    sload(0);
+    __syncthreads();   // the zeroing is done before any position is staged
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    swrite(0, 0);
+    sload(1);
+#pragma unroll
+    for (int s0 = 0; s0 < AD; ++s0) {
+        fa[s0][0] = aload(0, s0, 0);
+        fa[s0][1] = aload(0, s0, 1);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int b = 0; b < NB; ++b) fb[b] = *(const v8bf *)(smem + bbase[b] + tap_offset(0, 0));
+
+    // One chunk of 32 output channels on stage ST (a compile-time index, so
+    // every LDS address is a base register plus an immediate).  The B
+    // fragments are single-buffered: block b's fragment for the next tap is
+    // read right after block b's two MFMAs of this tap are issued (in the
+    // last tap: the next chunk's first tap, from its stage, staged and made
+    // visible earlier in this chunk).
+    auto run_chunk = [&](const int chunk, auto st_c) {
+        constexpr int ST = decltype(st_c)::value;
+        constexpr int NX = (ST + 1) % kStages;   // stage of the next chunk
+        const bool more = chunk + 1 < A.nchunks;
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int tp = 0; tp < T; ++tp) {
+            {
+                const int t2 = tp + AD;
+                const int c2 = t2 < T ? chunk : chunk + 1;
+                const int t2m = t2 < T ? t2 : t2 - T;
+                fa[t2m][0] = aload(c2, t2m, 0);
+                fa[t2m][1] = aload(c2, t2m, 1);
+            }
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb)
+                    if constexpr (F16)
+                        acc[cb][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            __builtin_bit_cast(v8h, fa[tp][cb]), __builtin_bit_cast(v8h, fb[b]),
+                            acc[cb][b], 0, 0, 0);
+                    else
+                        acc[cb][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            fa[tp][cb], fb[b], acc[cb][b], 0, 0, 0);
+                if (tp + 1 < T)
+                    fb[b] = *(const v8bf *)(smem + bbase[b] + tap_offset(ST, tp + 1));
+                else if (more)
+                    fb[b] = *(const v8bf *)(smem + bbase[b] + tap_offset(NX, 0));
+            }
+            if (tp == kStageTap && more) {
+                // The next chunk's copy was issued a chunk ago; only this
+                // chunk's A prefetches were issued after it.  Its stage was
+                // last read two chunks ago, before the last barrier.
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kAfterLanding) : "memory");
+                swrite(chunk + 1, NX);
+                sload(chunk + 2);
+            }
+            if (tp == kBarTap) __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    for (int chunk = 0; chunk < A.nchunks; chunk += kStages) {
+        run_chunk(chunk, std::integral_constant<int, 0>{});
+        if (chunk + 1 < A.nchunks) run_chunk(chunk + 1, std::integral_constant<int, 1>{});
+        if (chunk + 2 < A.nchunks) run_chunk(chunk + 2, std::integral_constant<int, 2>{});
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+    // Epilogue: D[4g + r][j16] of each block, NCHW fp32; one image's pixels
+    // are contiguous, so block b covers pixels 16b .. 16b+15.
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        const int p = b * 16 + j16;
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int ci = ci_tile * 128 + (2 * wave + cb) * 16 + 4 * g + rr;
+                const int off = (p < HW && ci < A.Ci) ? ((n * A.Ci + ci) * HW + p) * 4 : kOOB;
+                const float v = acc[cb][b][rr];
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), drs, off, 0, 0);
+            }
+        }
+    }
+}
+
+template <bool F16, int NB, int T, int KW, int HPT, int HRT>
+hipError_t launch_one(const Img16Args &a, size_t lds, hipStream_t s, const KernelEvents &ev) {
+    if (a.kW != KW || a.kH * a.kW != T || a.HP != HPT || a.HR > HRT ||
+        a.PS != img16_plane_bytes<HRT, HPT>() || lds != (size_t)img16_lds_bytes<HRT, HPT>() ||
+        a.H * a.W > 16 * NB || a.nq > 64 || 4 * a.nq != a.oH * a.oW ||
+        8 + 16 * a.oH * a.oW > kLand)
+        return hipErrorInvalidValue;
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute((const void *)gi_img16<F16, NB, T, KW, HPT, HRT>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    const int64_t wgs = (int64_t)a.N * a.ci_tiles;
+    if (wgs > INT32_MAX) return hipErrorInvalidValue;
+    hipExtLaunchKernelGGL((gi_img16<F16, NB, T, KW, HPT, HRT>), dim3((unsigned)wgs), dim3(256),
+                          (uint32_t)lds, s, ev.start, ev.stop, 0, a);
+    return hipGetLastError();
+}
+
+// Instantiations: (pixel blocks of 16 per wave, taps, kernel width, halo
+// pitch, most halo rows).  The first serves 3 x 3 kernels on images of up to
+// 14 rows and 14 columns (pitch 30 = 14 mod 16, at least 16 columns).
+constexpr int kCfg[][5] = {{13, 9, 3, 30, 16}};
+
+// Weight [Co][Ci][T] -> fragment image wk[ci tile of 64][chunk][tap][block of
+// 16][lane][8] (gi_common.h), zero past Ci and Co.  Thread (octet O of output
+// channels, run r of 8 consecutive (ci, tap) elements): eight 16-byte loads
+// (one per output channel of the octet, along its contiguous [Ci][T] row),
+// an 8 x 8 transpose of 16-bit values in registers, and eight 16-byte stores
+// (one per element: the octet's 8 channels at that (ci, tap)).  Consecutive
+// threads take consecutive runs of one row, so the loads are coalesced.
+// Rows whose length Ci*T is not a multiple of 8 take the same path with
+// 2-byte loads.
+__global__ __launch_bounds__(256) void weight_frag16(const uint16_t *__restrict__ w,
+                                                     uint16_t *__restrict__ wk, int Co, int Ci,
+                                                     int T, int nchunks, int wtiles, int runs) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int O = (int)(t / runs);
+    const int r = (int)(t - (int64_t)O * runs);
+    if (O >= nchunks * 4) return;
+    const int64_t rowlen = (int64_t)Ci * T;
+    const int64_t e0 = (int64_t)r * 8;
+    v4u v[8];
+    const bool vec = rowlen % 8 == 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int co = O * 8 + i;
+        const uint16_t *row = w + (int64_t)co * rowlen;
+        if (co >= Co || e0 >= rowlen) {
+            v[i] = v4u{0u, 0u, 0u, 0u};
+        } else if (vec) {
+            v[i] = *(const v4u *)(row + e0);
+        } else {
+            unsigned h[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) h[k] = e0 + k < rowlen ? row[e0 + k] : 0u;
+            v[i] = v4u{h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16};
+        }
+    }
+    const int chunk = O >> 2, gq = O & 3;
+    int ci = (int)(e0 / T), tap = (int)(e0 - (int64_t)ci * T);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        // Element k of the run: channel i's value is 16-bit half (k & 1) of
+        // dword k / 2 of v[i].
+        const unsigned sel = (k & 1) ? kHi : kLo;
+        v4u o;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) o[m] = pack2(v[2 * m][k >> 1], v[2 * m + 1][k >> 1], sel);
+        if (ci < wtiles * 64) {
+            const int ct = ci >> 6, cb = (ci >> 4) & 3, l16 = ci & 15;
+            const int64_t at = ((((int64_t)ct * nchunks + chunk) * T + tap) * 4 + cb) * 64 +
+                               16 * gq + l16;
+            ((v4u *)wk)[at] = o;
+        }
+        if (++tap == T) {
+            tap = 0;
+            ++ci;
+        }
+    }
+}
+
+}  // namespace
+
+int img16_config(int nb, int kH, int kW, int hp, int hr) {
+    for (int i = 0; i < (int)(sizeof(kCfg) / sizeof(kCfg[0])); ++i)
+        if (kCfg[i][0] == nb && kCfg[i][1] == kH * kW && kCfg[i][2] == kW && kCfg[i][3] == hp &&
+            hr <= kCfg[i][4])
+            return i;
+    return -1;
+}
+
+int img16_plane(int cfg) {
+    switch (cfg) {
+        case 0: return img16_plane_bytes<16, 30>();
+        default: return 0;
+    }
+}
+
+size_t img16_lds(int cfg) {
+    switch (cfg) {
+        case 0: return img16_lds_bytes<16, 30>();
+        default: return 0;
+    }
+}
+
+int img16_blocks(int cfg) { return cfg >= 0 ? kCfg[cfg][0] : 0; }
+
+hipError_t launch_img16(const Img16Args &a, int cfg, bool f16, size_t lds, hipStream_t s,
+                        const KernelEvents &ev) {
+    switch (cfg) {
+        case 0:
+            return f16 ? launch_one<true, 13, 9, 3, 30, 16>(a, lds, s, ev)
+                       : launch_one<false, 13, 9, 3, 30, 16>(a, lds, s, ev);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_weight_frag16(const uint16_t *w, uint16_t *wk, int Co, int Ci, int kHW,
+                                int nchunks, int wtiles, hipStream_t s) {
+    // Runs of 8 elements per row, covering every (ci, tap) of the image's
+    // wtiles*64 channels (runs past the row write zeros).
+    const int64_t runs = ((int64_t)wtiles * 64 * kHW + 7) / 8;
+    const int64_t threads = (int64_t)nchunks * 4 * runs;
+    const int64_t wgs = (threads + 255) / 256;
+    if (wgs > INT32_MAX || runs > INT32_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(weight_frag16, dim3((unsigned)wgs), dim3(256), 0, s, w, wk, Co, Ci, kHW,
+                       nchunks, wtiles, (int)runs);
+    return hipGetLastError();
+}
+
+}  // namespace gi

@@ -43,7 +43,9 @@ CONV2D_GI_API int conv2d_gi_set_variant(int variant);
  * tile_rows x tile_cols pixels of the stride-phase grid (at most nb*16
  * pixels) and the LDS pipeline depth (2 or 3 stages; 0 lets the planner
  * choose).  bf16 / fp16: nb pixel blocks of 16 per wave (4 or 7; two waves
- * share the tile, so at most 2*nb*16 pixels); stages is ignored.  A shape the
+ * share the tile, so at most 2*nb*16 pixels), or 13 for the whole-image
+ * kernel (a work-group per image and 128 input channels; the tile is then
+ * the image); stages is ignored.  A shape the
  * forced tile does not fit (LDS, halo size) is planned with GENERIC instead.
  * nb = 0 restores the planner.  Returns CONV2D_GI_OK, or CONV2D_GI_EINVAL for
  * values out of range.
@@ -54,9 +56,9 @@ CONV2D_GI_API int conv2d_gi_set_halo_tile(int nb, int tile_rows, int tile_cols, 
  * Force how many thread groups of 256 split the output channels of a
  * work-group of the fp32 HALO variant for this thread's later calls (1 or 2;
  * each group stages its own share of the chunks and the first sums both
- * before storing).  A shape no instance with that split serves is planned
- * without it.  0 restores the planner.  Returns CONV2D_GI_OK, or
- * CONV2D_GI_EINVAL for other values.
+ * before storing).  A shape no instance
+ * with that split serves is planned without it.  0 restores the planner.
+ * Returns CONV2D_GI_OK, or CONV2D_GI_EINVAL for other values.
  */
 CONV2D_GI_API int conv2d_gi_set_halo_split(int groups);
 

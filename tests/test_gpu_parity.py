@@ -191,6 +191,36 @@ def test_forced_halo_bf16(idx, dtype):
     full_parity(s, 1500 + idx, dtype, gi.VARIANT_HALO, dist="normal")
 
 
+# The whole-image 16-bit kernel (forced with its 13 pixel blocks): ragged
+# input-channel tiles, a partial last output-channel chunk, pad 0 and pad 2
+# (grad_out planes smaller and larger than the image), short images, an odd
+# batch and four 128-channel tiles.
+IMAGE_SHAPES = [
+    workloads.Shape(2, 64, 14, 14, 64, 3, 3, 1, 1, 1),
+    workloads.Shape(3, 130, 14, 14, 70, 3, 3, 1, 1, 1),
+    workloads.Shape(2, 40, 8, 14, 33, 3, 3, 1, 0, 0),
+    workloads.Shape(1, 24, 12, 14, 16, 3, 3, 1, 2, 2),
+    workloads.Shape(2, 512, 14, 14, 40, 3, 3, 1, 1, 1),
+    workloads.Shape(5, 128, 14, 14, 96, 3, 3, 1, 1, 1),
+    workloads.Shape(2, 16, 2, 14, 8, 3, 3, 1, 1, 1),
+    workloads.Shape(2, 64, 14, 14, 128, 3, 3, 1, 1, 1),     # 4 chunks: one past a stage cycle
+    workloads.Shape(1, 64, 14, 14, 160, 3, 3, 1, 1, 1),     # 5 chunks
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("idx", range(len(IMAGE_SHAPES)))
+def test_forced_image_kernel(idx, dtype):
+    s = IMAGE_SHAPES[idx]
+    gi.set_halo_tile(13, s.H, s.W, 0)
+    try:
+        desc = gi.plan(gi.make_params(*s.as_tuple()[:10]), 1 if dtype == "bf16" else 2)
+        assert "image kernel" in desc, desc
+        full_parity(s, 1600 + idx, dtype, gi.VARIANT_AUTO, dist="normal")
+    finally:
+        gi.set_halo_tile()
+
+
 STEM_SHAPES = [
     workloads.Shape(2, 3, 45, 44, 64, 7, 7, 2, 3, 3),      # stem-like, ragged tiles
     workloads.Shape(1, 4, 20, 19, 7, 3, 3, 1, 1, 1),       # Ci = 4, Co not a multiple of 4

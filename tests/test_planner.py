@@ -30,7 +30,9 @@ WORKLOAD_PLANS = {
     "strided_downsample": ["variant=halo", "cfg=11 fused", "HP=15"],
     "asym_1x7": ["variant=halo", "cfg=10 split=2", "fold", "HP=23"],
     "stem_7x7_s2": ["variant=stem", "ws_bytes=0", "tiles=16x7x7x1 whole=768 waves=4 pitch=19"],
-    "deep_late_stage_bf16": ["variant=halo", "dtype=bf16", "cfg=0", "pitch=30"],
+    "deep_late_stage_bf16": ["variant=halo", "dtype=bf16", "image kernel cfg=0", "nb=13",
+                             "wgs=64x4", "pitch=30"],
+    "deep_late_stage_f16": ["variant=halo", "dtype=f16", "image kernel cfg=0", "wgs=64x4"],
     "tiny": ["variant=generic"],
 }
 
@@ -38,7 +40,7 @@ WORKLOAD_PLANS = {
 @pytest.mark.parametrize("name", sorted(WORKLOAD_PLANS))
 def test_workload_plans(name):
     wl = workloads.BY_NAME[name]
-    desc = plan_of(wl.shape, wl.dtype == "bf16")
+    desc = plan_of(wl.shape, {"f32": 0, "bf16": 1, "f16": 2}[wl.dtype])
     for part in WORKLOAD_PLANS[name]:
         assert part in desc, (name, part, desc)
 
@@ -71,6 +73,8 @@ FIXED_INSTANCES = [
      ["cfg=10 split=2", "HP=23", "fold", "tile=4x17"]),
     (S(3, 72, 14, 14, 40, 3, 3, 1, 1, 1), True, gi.VARIANT_HALO, (7, 14, 14, 0, 0),
      ["cfg=0", "pitch=30"]),
+    (S(3, 130, 14, 14, 70, 3, 3, 1, 1, 1), True, gi.VARIANT_HALO, (13, 14, 14, 0, 0),
+     ["image kernel cfg=0", "wgs=3x2", "pitch=30"]),
     (S(1, 2, 30, 30, 6, 7, 7, 2, 3, 3), False, gi.VARIANT_STEM, None,
      ["variant=stem"]),
 ]
@@ -104,3 +108,21 @@ def test_forced_tile_validation():
         gi.set_halo_tile(13, 14, 14, 1)       # one stage is no pipeline
     gi.set_halo_tile(7, 14, 14, 0)            # a bf16 tile of 196 pixels
     gi.set_halo_tile()
+
+
+def test_image_kernel_needs_its_instance():
+    """The whole-image 16-bit kernel serves 3x3 kernels on images of up to
+    14 x 14 with 14 columns (pitch 30) and whole 4-pixel grad_out quads; other
+    shapes keep the halo-tile kernel even when its tile is forced."""
+    gi.set_halo_tile(13, 14, 14, 0)
+    try:
+        assert "image kernel" in plan_of(S(2, 64, 10, 14, 64, 3, 3, 1, 1, 1), 1)
+        assert "image kernel" not in plan_of(S(2, 64, 14, 13, 64, 3, 3, 1, 1, 1), 1)  # W = 13
+        assert "image kernel" not in plan_of(S(2, 64, 16, 14, 64, 3, 3, 1, 1, 1), 1)  # H = 16
+        assert "image kernel" not in plan_of(S(2, 64, 7, 14, 64, 3, 3, 1, 1, 1), 1)   # 98 pixels: 24.5 quads
+        assert "image kernel" not in plan_of(S(2, 64, 14, 14, 64, 3, 3, 1, 1, 1), 0)  # fp32
+    finally:
+        gi.set_halo_tile()
+    # Unforced, it needs a grid of at least one work-group per compute unit.
+    assert "image kernel" not in plan_of(S(2, 64, 14, 14, 64, 3, 3, 1, 1, 1), 1)
+    assert "image kernel" in plan_of(S(128, 256, 14, 14, 64, 3, 3, 1, 1, 1), 2)
