@@ -536,13 +536,14 @@ bool plan_halo_bf16(const conv2d_gi_params &p, HaloBf16Plan &out) {
 // channels), every pixel of the image in the wave's 16-pixel blocks.  Needs
 // an instance for the pixel blocks, taps, kernel width and halo pitch, a
 // grad_out plane of whole 4-pixel quads of which 8 planes fit a wave's 4 KB
-// landing area, and 32-bit byte offsets.
+// landing area, an image of whole 4-pixel quads, and 32-bit byte offsets.
 bool plan_img16(const conv2d_gi_params &p, Img16Plan &out) {
     if (p.stride != 1) return false;
     const int HW = p.H * p.W, oHW = p.oH * p.oW;
     // Each wave copies 8 grad_out planes (plus up to 8 bytes of alignment)
-    // into a 4 KB landing area, and its lanes take one 4-pixel quad each.
-    if (oHW % 4 != 0 || 8 + 16 * oHW > 4096) return false;
+    // into a 4 KB landing area, and its lanes take one 4-pixel quad each;
+    // the epilogue stores whole 4-pixel quads of the image.
+    if (oHW % 4 != 0 || 8 + 16 * oHW > 4096 || HW % 4 != 0) return false;
     const int HR = p.H + p.kH - 1, HC = p.W + p.kW - 1;
     const int HP = round_to_residue(HC, 16, p.W % 16);
     int cfg = -1;

@@ -299,21 +299,39 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-    // Epilogue: D[4g + r][j16] of each block, NCHW fp32; one image's pixels
-    // are contiguous, so block b covers pixels 16b .. 16b+15.
+    // Epilogue.  Lane (j16, g) holds D[4g + r][j16] of each block: four
+    // consecutive input channels of one pixel.  Each wave turns its 32
+    // channels x NB*16 pixels around through LDS (the stages are free: every
+    // wave passed the last chunk's barrier) so that a lane stores 4
+    // consecutive pixels of one channel with one 16-byte store: a quarter of
+    // the store instructions of 4-byte stores, each a full 64-byte run per
+    // 4 lanes.  LDS rows are NB*16 + 4 floats apart, so the 16 lanes of a
+    // row write (4g + r, j16) at banks distinct within each 16-lane quarter.
+    __syncthreads();
+    constexpr int RW = NB * 16 + 4;               // floats per LDS row (one channel)
+    static_assert(4 * 32 * RW * 4 <= img16_lds_bytes<HRT, HPT>(), "epilogue transpose fits");
+    float *const tw = (float *)smem + wave * 32 * RW;
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-        const int p = b * 16 + j16;
+    for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int ci = ci_tile * 128 + (2 * wave + cb) * 16 + 4 * g + rr;
-                const int off = (p < HW && ci < A.Ci) ? ((n * A.Ci + ci) * HW + p) * 4 : kOOB;
-                const float v = acc[cb][b][rr];
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), drs, off, 0, 0);
-            }
-        }
+            for (int rr = 0; rr < 4; ++rr)
+                tw[(cb * 16 + 4 * g + rr) * RW + b * 16 + j16] = acc[cb][b][rr];
+    // Own rows only: a wave reads back what it wrote, so its own LDS wait
+    // (inserted by the compiler) orders the two.
+    constexpr int QPR = NB * 4;                   // 4-pixel quads per channel row
+#pragma unroll
+    for (int k = 0; k < (32 * QPR + 63) / 64; ++k) {
+        const int e = k * 64 + lane;              // (channel row, quad) of this store
+        const int row = e / QPR, qd = e - (e / QPR) * QPR;
+        const int ci = ci_tile * 128 + wave * 32 + row;
+        const int p = 4 * qd;
+        const bool ok = e < 32 * QPR && p < HW && ci < A.Ci;
+        const v4u v = ok ? *(const v4u *)(tw + row * RW + p) : v4u{0u, 0u, 0u, 0u};
+        // A quad is whole: H*W is a multiple of 4 (checked at launch).
+        const int off = ok ? ((n * A.Ci + ci) * HW + p) * 4 : kOOB;
+        __builtin_amdgcn_raw_buffer_store_b128(v, drs, off, 0, 0);
     }
 }
 
@@ -321,7 +339,7 @@ template <bool F16, int NB, int T, int KW, int HPT, int HRT>
 hipError_t launch_one(const Img16Args &a, size_t lds, hipStream_t s, const KernelEvents &ev) {
     if (a.kW != KW || a.kH * a.kW != T || a.HP != HPT || a.HR > HRT ||
         a.PS != img16_plane_bytes<HRT, HPT>() || lds != (size_t)img16_lds_bytes<HRT, HPT>() ||
-        a.H * a.W > 16 * NB || a.nq > 64 || 4 * a.nq != a.oH * a.oW ||
+        a.H * a.W > 16 * NB || (a.H * a.W) % 4 != 0 || a.nq > 64 || 4 * a.nq != a.oH * a.oW ||
         8 + 16 * a.oH * a.oW > kLand)
         return hipErrorInvalidValue;
     if (lds > 64 * 1024) {
@@ -342,60 +360,51 @@ hipError_t launch_one(const Img16Args &a, size_t lds, hipStream_t s, const Kerne
 constexpr int kCfg[][5] = {{13, 9, 3, 30, 16}};
 
 // Weight [Co][Ci][T] -> fragment image wk[ci tile of 64][chunk][tap][block of
-// 16][lane][8] (gi_common.h), zero past Ci and Co.  Thread (octet O of output
-// channels, run r of 8 consecutive (ci, tap) elements): eight 16-byte loads
-// (one per output channel of the octet, along its contiguous [Ci][T] row),
-// an 8 x 8 transpose of 16-bit values in registers, and eight 16-byte stores
-// (one per element: the octet's 8 channels at that (ci, tap)).  Consecutive
-// threads take consecutive runs of one row, so the loads are coalesced.
-// Rows whose length Ci*T is not a multiple of 8 take the same path with
-// 2-byte loads.
+// 16][lane][8] (gi_common.h), zero past Ci and Co.  Work-group (chunk of 32
+// output channels, block of 16 input channels): the 32 rows of the block's
+// 16*T contiguous (ci, tap) elements are copied into LDS with 16-byte loads,
+// then each thread gathers one lane's 8 output channels at one (ci, tap) from
+// LDS and writes it; consecutive threads write consecutive lanes, so every
+// tap's 1 KB fragment block is stored whole.
 __global__ __launch_bounds__(256) void weight_frag16(const uint16_t *__restrict__ w,
                                                      uint16_t *__restrict__ wk, int Co, int Ci,
-                                                     int T, int nchunks, int wtiles, int runs) {
-    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int O = (int)(t / runs);
-    const int r = (int)(t - (int64_t)O * runs);
-    if (O >= nchunks * 4) return;
+                                                     int T, int nchunks) {
+    extern __shared__ uint16_t raw[];   // [32 rows][16*T + 8]
+    const int chunk = blockIdx.x, blk = blockIdx.y;
+    const int pitch = 16 * T + 8;
     const int64_t rowlen = (int64_t)Ci * T;
-    const int64_t e0 = (int64_t)r * 8;
-    v4u v[8];
+    const int64_t e0 = (int64_t)blk * 16 * T;   // first element of the block in a row
+    const int pieces = 2 * T;                  // 8-element pieces per row of the block
     const bool vec = rowlen % 8 == 0;
+    for (int i = threadIdx.x; i < 32 * pieces; i += 256) {
+        const int r = i / pieces, pc = i - (i / pieces) * pieces;
+        const int co = chunk * 32 + r;
+        const int64_t e = e0 + 8 * pc;
+        v4u v = v4u{0u, 0u, 0u, 0u};
+        if (co < Co && e < rowlen) {
+            const uint16_t *src = w + (int64_t)co * rowlen + e;
+            if (vec) {
+                v = *(const v4u *)src;
+            } else {
+                unsigned h[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int co = O * 8 + i;
-        const uint16_t *row = w + (int64_t)co * rowlen;
-        if (co >= Co || e0 >= rowlen) {
-            v[i] = v4u{0u, 0u, 0u, 0u};
-        } else if (vec) {
-            v[i] = *(const v4u *)(row + e0);
-        } else {
-            unsigned h[8];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) h[k] = e0 + k < rowlen ? row[e0 + k] : 0u;
-            v[i] = v4u{h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16};
+                for (int k = 0; k < 8; ++k) h[k] = e + k < rowlen ? src[k] : 0u;
+                v = v4u{h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16};
+            }
         }
+        *(v4u *)(raw + r * pitch + 8 * pc) = v;
     }
-    const int chunk = O >> 2, gq = O & 3;
-    int ci = (int)(e0 / T), tap = (int)(e0 - (int64_t)ci * T);
+    __syncthreads();
+    const int ct = blk >> 2, cb = blk & 3;
+    for (int o = threadIdx.x; o < T * 64; o += 256) {
+        const int tap = o >> 6, ln = o & 63;
+        const int gq = ln >> 4, l16 = ln & 15;
+        const uint16_t *col = raw + 8 * gq * pitch + l16 * T + tap;
+        v4u v;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        // Element k of the run: channel i's value is 16-bit half (k & 1) of
-        // dword k / 2 of v[i].
-        const unsigned sel = (k & 1) ? kHi : kLo;
-        v4u o;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) o[m] = pack2(v[2 * m][k >> 1], v[2 * m + 1][k >> 1], sel);
-        if (ci < wtiles * 64) {
-            const int ct = ci >> 6, cb = (ci >> 4) & 3, l16 = ci & 15;
-            const int64_t at = ((((int64_t)ct * nchunks + chunk) * T + tap) * 4 + cb) * 64 +
-                               16 * gq + l16;
-            ((v4u *)wk)[at] = o;
-        }
-        if (++tap == T) {
-            tap = 0;
-            ++ci;
-        }
+        for (int m = 0; m < 4; ++m)
+            v[m] = (unsigned)col[(2 * m) * pitch] | (unsigned)col[(2 * m + 1) * pitch] << 16;
+        ((v4u *)wk)[((((int64_t)ct * nchunks + chunk) * T + tap) * 4 + cb) * 64 + ln] = v;
     }
 }
 
@@ -437,14 +446,17 @@ hipError_t launch_img16(const Img16Args &a, int cfg, bool f16, size_t lds, hipSt
 
 hipError_t launch_weight_frag16(const uint16_t *w, uint16_t *wk, int Co, int Ci, int kHW,
                                 int nchunks, int wtiles, hipStream_t s) {
-    // Runs of 8 elements per row, covering every (ci, tap) of the image's
-    // wtiles*64 channels (runs past the row write zeros).
-    const int64_t runs = ((int64_t)wtiles * 64 * kHW + 7) / 8;
-    const int64_t threads = (int64_t)nchunks * 4 * runs;
-    const int64_t wgs = (threads + 255) / 256;
-    if (wgs > INT32_MAX || runs > INT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(weight_frag16, dim3((unsigned)wgs), dim3(256), 0, s, w, wk, Co, Ci, kHW,
-                       nchunks, wtiles, (int)runs);
+    // One work-group per (chunk, block of 16 input channels) of the image,
+    // including the zero blocks past Ci up to wtiles*64 channels.
+    const size_t lds = (size_t)32 * (16 * kHW + 8) * sizeof(uint16_t);
+    if (lds > 160 * 1024 || wtiles * 4 > 65535) return hipErrorInvalidValue;
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute((const void *)weight_frag16,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(weight_frag16, dim3(nchunks, wtiles * 4), dim3(256), lds, s, w, wk, Co, Ci,
+                       kHW, nchunks);
     return hipGetLastError();
 }
 

@@ -120,6 +120,7 @@ def test_image_kernel_needs_its_instance():
         assert "image kernel" not in plan_of(S(2, 64, 14, 13, 64, 3, 3, 1, 1, 1), 1)  # W = 13
         assert "image kernel" not in plan_of(S(2, 64, 16, 14, 64, 3, 3, 1, 1, 1), 1)  # H = 16
         assert "image kernel" not in plan_of(S(2, 64, 7, 14, 64, 3, 3, 1, 1, 1), 1)   # 98 pixels: 24.5 quads
+        assert "image kernel" not in plan_of(S(2, 64, 7, 14, 64, 3, 3, 1, 0, 0), 1)   # 60 grad_out pixels, 98 image pixels
         assert "image kernel" not in plan_of(S(2, 64, 14, 14, 64, 3, 3, 1, 1, 1), 0)  # fp32
     finally:
         gi.set_halo_tile()
