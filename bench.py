@@ -20,6 +20,14 @@ launch records with the dispatch's start and end timestamps (the
 summary under profiles/, and ``roofline.mfma_counters`` the matrix-core work
 and utilisation the MFMA counters saw per launch, each when its kernel
 sources and plan still match.
+
+Beside the warm figure, every workload is also timed cold: before each of
+``--cold-steps`` calls a 512 MiB device buffer is overwritten (more than the
+L2s and the 256 MB last-level cache hold), and each call is bracketed by its
+own events; the line reports their median, min and max.  The matrix-core
+peaks are measured too (a probe kernel of back-to-back MFMAs on varied data)
+and each roofline fraction is given against both the published and the
+measured peak.
 """
 from __future__ import annotations
 
@@ -44,6 +52,7 @@ METRIC = "effective TFLOP/s of conv2d grad_input per config; % of MFMA peak (1 G
 PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6, "f16": 2516.6}   # MI355X dense matrix-core peaks
 PLAN_KIND = {"f32": 0, "bf16": 1, "f16": 2}   # the dtype argument of the plan description
 HBM_PEAK_GBS = 8000.0
+EVICT_MIB = 512        # written before each cold call: > L2s (8 x 4 MB) + 256 MB MALL
 DEFAULT_WORKLOAD = "resnet_stage_3x3"
 WARMUP_SECONDS = 0.1   # untimed warm-up: at least this much GPU work
 
@@ -62,6 +71,8 @@ def parse():
                     help="skip the short timing of the other workloads")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--cold-steps", type=int, default=20,
+                    help="calls timed one by one after evicting the caches (0: skip)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="end with %d plain device copies of this many MiB (the "
                          "reference kernel for scaling HBM byte counters)"
@@ -199,6 +210,67 @@ def time_workload(wl, steps, warmup, torch, gi, dev, op="grad_input"):
                 flops=s.eff_flops * (2 if op == "backward" else 1))
 
 
+def make_call(wl, torch, gi, dev, op="grad_input"):
+    """The workload's library call on device-resident inputs (a closure)."""
+    s = wl.shape
+    _, tg, tw, out = device_inputs(wl, torch, dev)
+    stream = torch.cuda.current_stream(dev)
+    if op != "grad_input":
+        raise ValueError(op)
+
+    def call():
+        gi.grad_input(tg, tw, stride=s.stride, padding=(s.pad_h, s.pad_w),
+                      input_hw=(s.H, s.W), out=out, stream=stream)
+    return call
+
+
+def time_cold(wl, steps, torch, gi, dev, evict):
+    """Per-call times (ms) with the caches evicted before each call: the
+    eviction write and the call are enqueued back to back (the GPU stays
+    busy), and each call is bracketed by its own events."""
+    call = make_call(wl, torch, gi, dev)
+    call()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    for e0, e1 in evs:
+        evict.fill_(1.0)
+        e0.record()
+        call()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    med = ms[len(ms) // 2] if len(ms) % 2 else 0.5 * (ms[len(ms) // 2 - 1] + ms[len(ms) // 2])
+    return {"evict_mib": EVICT_MIB, "calls": steps, "median_ms": round(med, 5),
+            "min_ms": round(ms[0], 5), "max_ms": round(ms[-1], 5),
+            "tflops_median": round(wl.shape.eff_flops / (med * 1e-3) / 1e12, 3)}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def roofline_block(flops, kernel_ms, peak, measured_peak, kernel, traffic, alg_bytes, mfma):
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    return {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "measured_peak": None if measured_peak is None else round(measured_peak, 1),
+            "frac_of_measured_peak": None if not measured_peak else
+            round(achieved / measured_peak, 4),
+            "traffic": None if traffic is None else round(traffic["bytes"]),
+            "algorithmic_bytes": alg_bytes,
+            "hbm_gbs": None if traffic is None else
+            round(traffic["bytes"] / (kernel_ms * 1e-3) / 1e9, 1),
+            "kernel": kernel, "kernel_ms": round(kernel_ms, 5), "mfma_counters": mfma}
+
+
 def cpu_baseline(wl, target_s):
     """The oracle, untuned, on a bounded sample: the first n batch items of the
     same workload (n chosen from a one-item probe to take about target_s)."""
@@ -220,7 +292,8 @@ def cpu_baseline(wl, target_s):
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
             "kind": "oracle",
             "sample": "first %d of %d batch items of %s (fp64 direct loop, %.2f s, %s)"
-                      % (n, s.N, wl.name, dt, platform.processor() or platform.machine())}
+                      % (n, s.N, wl.name, dt, cpu_model()),
+            "cpu_model": cpu_model()}
 
 
 def main():
@@ -247,6 +320,13 @@ def main():
     r = time_workload(wl, args.steps, args.warmup, torch, gi, dev, op)
     value = r["flops"] / (r["ms_per_step"] * 1e-3) / 1e12
     peak = PEAK_TFLOPS[wl.dtype]
+    # Matrix-core rates the chip sustains (fp16 takes the bf16 figure: the
+    # same MFMA shape and rate).
+    measured = {"f32": gi.mfma_peak("f32"), "bf16": gi.mfma_peak("bf16")}
+    measured["f16"] = measured["bf16"]
+    evict = None
+    if args.cold_steps > 0 and op == "grad_input":
+        evict = torch.empty(EVICT_MIB * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
     params = gi.make_params(*s.as_tuple()[:10])
     if op == "grad_weight":
         plan_desc = gi.grad_weight_plan(params)
@@ -298,20 +378,16 @@ def main():
                    "kH": s.kH, "kW": s.kW, "stride": s.stride, "pad_h": s.pad_h,
                    "pad_w": s.pad_w, "oH": s.oH, "oW": s.oW, "eff_gflop": s.eff_flops / 1e9,
                    "plan": plan_desc},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": None if traffic is None else round(traffic["bytes"]),
-                     "algorithmic_bytes": alg_bytes,
-                     "hbm_gbs": None if traffic is None else
-                     round(traffic["bytes"] / (kernel_ms * 1e-3) / 1e9, 1),
-                     "kernel": kernel,
-                     "kernel_ms": round(kernel_ms, 5),
-                     "per_unit": "%d*Ci*kH*kW*Co flops per output pixel (n,oh,ow)"
-                                 % (4 if op == "backward" else 2),
-                     "units_per_launch": s.N * s.oH * s.oW,
-                     "mfma_counters": mfma},
+        "roofline": dict(roofline_block(r["flops"], kernel_ms, peak, measured[wl.dtype], kernel,
+                                        traffic, alg_bytes, mfma),
+                         per_unit="%d*Ci*kH*kW*Co flops per output pixel (n,oh,ow)"
+                                  % (4 if op == "backward" else 2),
+                         units_per_launch=s.N * s.oH * s.oW),
         "frac_of_peak_whole_call": round(value / peak, 4),
+        "measured_mfma_peak_tflops": {k: round(v, 1) for k, v in measured.items()},
     }
+    if evict is not None:
+        line["cold"] = time_cold(wl, args.cold_steps, torch, gi, dev, evict)
     if not args.no_others and op == "grad_input":
         others = {}
         for o in workloads.WORKLOADS:
@@ -328,15 +404,14 @@ def main():
                                      o.dtype)
             others[o.name] = {"dtype": o.dtype, "tflops": round(v, 3),
                               "ms_per_call": round(ro["ms_per_step"], 5),
-                              "kernel_ms": round(ro["kernel_ms"], 5),
                               "frac_of_peak": round(v / PEAK_TFLOPS[o.dtype], 4),
-                              "kernel_frac_of_peak": round(
-                                  ro["flops"] / (ro["kernel_ms"] * 1e-3) / 1e12
-                                  / PEAK_TFLOPS[o.dtype], 4),
-                              "traffic": None if to is None else round(to["bytes"]),
-                              "mfma_counters": mo,
-                              "algorithmic_bytes": so.algorithmic_bytes(
-                                  4 if o.dtype == "f32" else 2)}
+                              "plan": po,
+                              "roofline": roofline_block(
+                                  ro["flops"], ro["kernel_ms"], PEAK_TFLOPS[o.dtype],
+                                  measured[o.dtype], profiling.kernel_name(vo, o.dtype), to,
+                                  so.algorithmic_bytes(4 if o.dtype == "f32" else 2), mo)}
+            if evict is not None:
+                others[o.name]["cold"] = time_cold(o, args.cold_steps, torch, gi, dev, evict)
         line["other_workloads"] = others
         # The next row of the same backward pass: grad_weight (fp32 runs).
         nxt = {}

@@ -18,7 +18,7 @@ import os
 
 __all__ = [
     "grad_input", "grad_input_noalloc", "Conv2dGiParams", "Conv2dGiError", "LibraryNotBuilt", "load_library",
-    "make_params", "validate", "plan", "grad_weight", "grad_weight_plan", "grad_bias", "backward", "forward", "forward_plan", "set_fwd_variant", "set_variant", "set_halo_tile", "set_halo_split", "set_halo_fusion", "set_gw_variant", "set_gw_tile", "release_workspaces", "set_profile_events", "library_path", "exported_names",
+    "make_params", "validate", "plan", "grad_weight", "grad_weight_plan", "grad_bias", "backward", "forward", "forward_plan", "set_fwd_variant", "set_variant", "set_halo_tile", "set_halo_split", "set_halo_fusion", "set_gw_variant", "set_gw_tile", "release_workspaces", "set_profile_events", "mfma_peak", "library_path", "exported_names",
     "OK", "EINVAL", "EUNSUPPORTED", "EHIP", "VARIANT_AUTO", "VARIANT_GENERIC", "VARIANT_HALO", "VARIANT_STEM",
 ]
 
@@ -112,6 +112,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.conv2d_gi_release_workspaces.restype = ctypes.c_int
     lib.conv2d_gi_version.argtypes = []
     lib.conv2d_gi_version.restype = ctypes.c_char_p
+    lib.conv2d_gi_mfma_peak_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P,
+                                              ctypes.POINTER(ctypes.c_double)]
+    lib.conv2d_gi_mfma_peak_probe.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -129,7 +132,7 @@ def exported_names():
             "conv2d_gi_plan", "conv2d_gi_set_halo_tile", "conv2d_gi_set_halo_split",
             "conv2d_gi_set_halo_fusion", "conv2d_gw_set_variant", "conv2d_gw_set_tile",
             "conv2d_gi_set_profile_events",
-            "conv2d_gi_release_workspaces", "conv2d_gi_version"]
+            "conv2d_gi_release_workspaces", "conv2d_gi_version", "conv2d_gi_mfma_peak_probe"]
 
 
 def make_params(N, Ci, H, W, Co, kH, kW, stride, pad_h, pad_w, oH=None, oW=None):
@@ -210,6 +213,43 @@ def set_gw_tile(rows: int = 0, stages: int = 0, max_slices: int = 0):
 def release_workspaces():
     """Free the library's cached per-stream scratch buffers."""
     _check(load_library().conv2d_gi_release_workspaces())
+
+
+def mfma_peak(kind: str, seconds: float = 0.05):
+    """Sustained matrix-core rate in TFLOP/s ("f32": V_MFMA_F32_16X16X4_F32,
+    "bf16": V_MFMA_F32_16X16X32_BF16) on the current device: a probe kernel
+    of back-to-back independent MFMAs on varied data, two waves per SIMD of
+    every compute unit, timed with events after a warm-up of about the same
+    length (so the clock has settled)."""
+    import torch
+
+    lib = load_library()
+    k = {"f32": 0, "bf16": 1}[kind]
+    dev = torch.cuda.current_device()
+    # Two work-groups of 4 waves per compute unit: two waves per SIMD.
+    wgs = 2 * torch.cuda.get_device_properties(dev).multi_processor_count
+    scratch = torch.empty(wgs, dtype=torch.float32, device="cuda")
+    s = torch.cuda.current_stream()
+    fl = ctypes.c_double()
+
+    def launch(iters):
+        _check(lib.conv2d_gi_mfma_peak_probe(k, wgs, iters, _ptr(scratch),
+                                             ctypes.c_void_p(s.cuda_stream), ctypes.byref(fl)))
+
+    launch(1000)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    launch(1000)
+    e1.record()
+    torch.cuda.synchronize()
+    iters = max(1000, int(1000 * seconds / max(e0.elapsed_time(e1) * 1e-3, 1e-6)))
+    launch(iters)   # warm-up of about `seconds`
+    e0.record()
+    launch(iters)
+    e1.record()
+    torch.cuda.synchronize()
+    return fl.value / (e0.elapsed_time(e1) * 1e-3) / 1e12
 
 
 def set_profile_events(begin, end):

@@ -31,6 +31,7 @@ SOURCES = [
     "kernels_gw_f32.hip",
     "kernels_fwd_f32.hip",
     "noalloc.hip",
+    "kernels_peak.hip",
 ]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", "-Werror",

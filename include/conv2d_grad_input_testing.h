@@ -111,6 +111,20 @@ CONV2D_GI_API int conv2d_gw_set_tile(int rows, int stages, int max_slices);
  */
 CONV2D_GI_API void conv2d_gi_set_profile_events(hipEvent_t begin, hipEvent_t end);
 
+/*
+ * Measurement probe: enqueue a kernel of `workgroups` work-groups of 4
+ * waves that each issue `iters` rounds of 8 independent matrix-core
+ * instructions on varied data (kind 0: fp32 V_MFMA_F32_16X16X4_F32, kind 1:
+ * bf16 V_MFMA_F32_16X16X32_BF16), so that timing it with events on `stream`
+ * gives the matrix-core rate the chip sustains at the clock it settles to.
+ * *flops receives the kernel's flop count.  scratch: device memory of at
+ * least `workgroups` floats (written only in a case that does not occur;
+ * it keeps the work from being optimised away).  Returns CONV2D_GI_OK,
+ * CONV2D_GI_EINVAL or CONV2D_GI_EHIP.
+ */
+CONV2D_GI_API int conv2d_gi_mfma_peak_probe(int kind, int workgroups, int iters, float *scratch,
+                                            hipStream_t stream, double *flops);
+
 #ifdef __cplusplus
 }
 #endif
