@@ -217,7 +217,13 @@ bool plan_halo(const conv2d_gi_params &p, const std::vector<Phase> &phases, Halo
     unsigned tmask = 0;
     for (const Phase &ph : phases) {
         const int T = ph.J_h * ph.J_w;
-        if (T > 0) tmask |= gi::halo_f32_tbit(T);
+        if (T > 0) {
+            // A tap count no instance serves (0: past the mask's range) rules
+            // the halo kernels out.
+            const unsigned bit = gi::halo_f32_tbit(T);
+            if (bit == 0) return false;
+            tmask |= bit;
+        }
         maxT = std::max(maxT, T);
         maxJh = std::max(maxJh, ph.J_h);
         maxJw = std::max(maxJw, ph.J_w);

@@ -37,7 +37,7 @@ hipError_t launch_generic_bf16(const GemmArgs &a, int tiles_x, hipStream_t s,
 // Halo-tile fp32 kernel (kernels_halo_f32.hip).  Instantiations are indexed
 // by (NB pixel blocks of 16 per work-group, HG halo groups of 32 positions
 // per wave, the set of per-phase tap counts served as a bit mask of
-// halo_f32_tbit(T));
+// halo_f32_tbit(T), 0 for a tap count no instantiation serves);
 // halo_f32_config returns the first instantiation that covers the request, or
 // -1 when none does.
 constexpr int kHaloBC = 8;     // output channels per LDS stage (chunk)

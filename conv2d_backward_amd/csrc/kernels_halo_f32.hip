@@ -683,6 +683,12 @@ hipError_t launch_one(const HaloArgs &a, int tiles, int ci_tiles, size_t lds, hi
         return hipErrorInvalidValue;
     }
     if (PITCH > 0 && a.HP != PITCH) return hipErrorInvalidValue;
+    // Every phase-at-a-time phase with taps has its tap count in TMASK (a
+    // phase the kernel has no case for would be left at zero).
+    for (int i = 0; NPH == 0 && i < a.nphases; ++i) {
+        const int T = a.ph[i].J_h * a.ph[i].J_w;
+        if (T > 0 && (T >= 32 || (TMASK & tbit(T)) == 0)) return hipErrorInvalidValue;
+    }
     // JW > 0: every phase with taps has that kernel-width tap count.
     for (int i = 0; JW > 0 && i < a.nphases; ++i)
         if (a.ph[i].J_w != JW && a.ph[i].J_h * a.ph[i].J_w != 0) return hipErrorInvalidValue;
@@ -728,7 +734,7 @@ constexpr HaloCfg kCfg[] = {
 
 }  // namespace
 
-unsigned halo_f32_tbit(int T) { return T >= 0 && T < 32 ? tbit(T) : 0u; }
+unsigned halo_f32_tbit(int T) { return T >= 1 && T < 32 ? tbit(T) & kTall : 0u; }
 
 int halo_f32_config(int nb, unsigned tmask, int hg, int hp, int jw, int ks, int nph) {
     for (int i = 0; i < (int)(sizeof(kCfg) / sizeof(kCfg[0])); ++i) {

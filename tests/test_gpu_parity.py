@@ -391,3 +391,32 @@ def test_invalid_leaves_dst_untouched():
         gi.grad_input(g, w.to(torch.bfloat16), stride=1, padding=1, input_hw=(8, 8))
     torch.cuda.synchronize()
     assert torch.all(out == 7.0)
+
+
+def test_generic_past_2gib_sampled():
+    """dst of exactly 2^31 bytes (N=8, Ci=64, 1024 x 1024): past the halo
+    kernels' 32-bit byte offsets, so the planner takes the generic kernel with
+    64-bit batch offsets.  Every element is checked for NaN (unwritten) and
+    the guard bands for stray writes on the GPU; sampled elements (random,
+    plus corners and edges of the first and last image) against the oracle."""
+    s = workloads.Shape(8, 64, 1024, 1024, 16, 3, 3, 1, 1, 1)
+    n_dst = s.N * s.Ci * s.H * s.W
+    assert n_dst * 4 == 2 ** 31
+    desc = gi.plan(gi.make_params(*s.as_tuple()[:10]), False)
+    assert "variant=generic" in desc, desc
+    g, w = workloads.make_case(s, 4711, "normal")
+    dev = torch.device("cuda:0")
+    tg, tw = torch.from_numpy(g).to(dev), torch.from_numpy(w).to(dev)
+    buf = torch.full((n_dst + 2 * GUARD,), SENTINEL, dtype=torch.float32, device=dev)
+    buf[GUARD:GUARD + n_dst] = float("nan")
+    out = buf[GUARD:GUARD + n_dst].view(s.dst_shape)
+    say("case %s (2 GiB dst) plan %s" % (s, desc))
+    gi.grad_input(tg, tw, stride=1, padding=1, input_hw=(s.H, s.W), out=out)
+    torch.cuda.synchronize()
+    assert not bool(torch.isnan(out).any()), "unwritten (NaN) elements"
+    assert bool((buf[:GUARD] == SENTINEL).all()) and bool((buf[GUARD + n_dst:] == SENTINEL).all())
+    idx = sample_indices(s, np.random.default_rng(4712), count=4000)
+    got = out.view(-1)[torch.from_numpy(idx).to(dev)].double().cpu().numpy()
+    del buf, out
+    ref, S = oracle.grad_input_at(g, w, 1, (1, 1), (s.H, s.W), idx)
+    check(got, ref, S, "f32", str(s))

@@ -1,0 +1,226 @@
+"""LDS bank model of gfx950 and the kernels' fragment-read layouts (CPU).
+
+The model (measured on the GPU with the SQ_LDS_BANK_CONFLICT and
+SQ_LDS_IDX_ACTIVE counters over many address patterns; the LDS has 64 banks
+of 4 bytes):
+  * ds_read_b64: each cycle serves 32 consecutive lanes (a half wave); the
+    cycle is conflict-free iff their distinct 8-byte units are distinct
+    mod 32 (lanes reading the same address share one access);
+  * ds_read_b128: each cycle serves 16 lanes.  Within each half wave, the
+    lanes whose index bits 2, 3 and 4 have even parity form one cycle and the
+    odd ones the other; conflict-free iff their distinct 16-byte units are
+    distinct mod 16.
+Every fragment read the kernels issue in their steady state is rebuilt here
+from the same address arithmetic as the kernel source, for the plans of the
+graded workloads.  The 16-bit kernels and the stem need no extra cycle on
+any of them; the fp32 halo-tile planner trades a compile-time pitch against
+conflicts, and the model must agree with the rule it uses for that.  A
+layout with a planted conflict must show one (so a model that sees none
+anywhere would fail).
+"""
+import re
+
+import pytest
+
+import conv2d_backward_amd as gi
+import workloads
+
+
+def extra_cycles_b64(addr):
+    """Extra LDS cycles of one ds_read_b64 (64 byte addresses)."""
+    extra = 0
+    for h in (0, 32):
+        units = {a // 8 for a in addr[h:h + 32]}
+        per_bank = {}
+        for u in units:
+            per_bank[u % 32] = per_bank.get(u % 32, 0) + 1
+        extra += max(per_bank.values()) - 1
+    return extra
+
+
+def b128_cycles(lanes_in_half):
+    even = [l for l in lanes_in_half if bin((l >> 2) & 7).count("1") % 2 == 0]
+    odd = [l for l in lanes_in_half if bin((l >> 2) & 7).count("1") % 2 == 1]
+    return even, odd
+
+
+def extra_cycles_b128(addr):
+    """Extra LDS cycles of one ds_read_b128 (64 byte addresses)."""
+    extra = 0
+    for h in (0, 32):
+        for cyc in b128_cycles(range(h, h + 32)):
+            units = {addr[l] // 16 for l in cyc}
+            per_bank = {}
+            for u in units:
+                per_bank[u % 16] = per_bank.get(u % 16, 0) + 1
+            extra += max(per_bank.values()) - 1
+    return extra
+
+
+def test_model_cycle_split():
+    """The b128 rule puts 16 lanes in each cycle, two cycles per half wave."""
+    for h in (0, 32):
+        even, odd = b128_cycles(range(h, h + 32))
+        assert len(even) == len(odd) == 16
+    assert b128_cycles(range(32))[0] == [0, 1, 2, 3, 12, 13, 14, 15, 20, 21, 22, 23,
+                                         24, 25, 26, 27]
+
+
+def test_model_sees_planted_conflicts():
+    # 16-byte reads with a 256-byte lane stride: every lane on bank group 0.
+    assert extra_cycles_b128([l * 256 for l in range(64)]) == 4 * 15
+    # 8-byte reads with a 256-byte stride: 32 lanes per half on one bank pair.
+    assert extra_cycles_b64([l * 256 for l in range(64)]) == 2 * 31
+    # Broadcast: one address for every lane costs nothing.
+    assert extra_cycles_b128([64] * 64) == 0
+    # Consecutive 16-byte words are conflict-free.
+    assert extra_cycles_b128([l * 16 for l in range(64)]) == 0
+
+
+# ----------------------------------------------------------------------------
+# The 16-bit whole-image kernel (kernels_img16.hip): B fragment of block b,
+# tap (kh, kw): plane g = lane/16 at PS bytes per plane, halo position of
+# pixel p = 16b + lane%16 (row-major in the image, rows HP positions apart;
+# slots past the image read position lane%16), shifted by (kH-1-kh, kW-1-kw).
+# ----------------------------------------------------------------------------
+
+def image_b_addrs(H, W, HP, PS, kH, kW, b, kh, kw):
+    out = []
+    for lane in range(64):
+        g, j16 = lane >> 4, lane & 15
+        p = 16 * b + j16
+        pos = (p // W) * HP + p % W if p < H * W else j16
+        out.append(g * PS + (pos + (kH - 1 - kh) * HP + (kW - 1 - kw)) * 16)
+    return out
+
+
+def test_image_kernel_b_reads_conflict_free():
+    s = workloads.BY_NAME["deep_late_stage_bf16"].shape
+    desc = gi.plan(gi.make_params(*s.as_tuple()[:10]), 1)
+    assert "image kernel" in desc and "pitch=30" in desc
+    HP = 30
+    PS = (16 * HP * 16 + 255) // 256 * 256
+    for b in range(13):
+        for kh in range(3):
+            for kw in range(3):
+                assert extra_cycles_b128(image_b_addrs(14, 14, HP, PS, 3, 3, b, kh, kw)) == 0, \
+                    (b, kh, kw)
+    # The same layout with the pitch not congruent to W mod 16 conflicts.
+    assert any(extra_cycles_b128(image_b_addrs(14, 14, 32, 8192, 3, 3, b, 1, 1)) > 0
+               for b in range(13))
+
+
+# ----------------------------------------------------------------------------
+# The 16-bit halo-tile kernel (kernels_halo_bf16.hip): wave (wm, wn) reads
+# pixel p = (wn*NBW + b)*16 + lane%16 of a TR x TC tile, position
+# (p / TC)*HP + p % TC in plane lane/16 (PS bytes apart), shifted by the tap.
+# ----------------------------------------------------------------------------
+
+def halo16_b_addrs(TR, TC, HP, PS, nbw, wn, b, shift):
+    out = []
+    for lane in range(64):
+        g, j16 = lane >> 4, lane & 15
+        p = (wn * nbw + b) * 16 + j16
+        pos = (p // TC) * HP + p % TC if p < TR * TC else j16
+        out.append(g * PS + (pos + shift) * 16)
+    return out
+
+
+def test_halo16_b_reads_conflict_free():
+    TR = TC = 14
+    HP, nbw = 30, 7
+    PS = ((TR + 2) * HP * 16 + 1023) // 1024 * 1024
+    for wn in range(2):
+        for b in range(nbw):
+            for kh in range(3):
+                for kw in range(3):
+                    shift = (2 - kh) * HP + (2 - kw)
+                    assert extra_cycles_b128(halo16_b_addrs(TR, TC, HP, PS, nbw, wn, b, shift)) == 0
+
+
+# ----------------------------------------------------------------------------
+# The fp32 halo-tile kernel (kernels_halo_f32.hip): float2 fragments.  B:
+# lane reads float2 (cp*HPc + pbase + shift) of its co pair cp = lane/16,
+# pbase = (px / TC)*HP + px % TC for px = blk*16 + lane%16, HPc = 16 mod 32.
+# A: float2 cp*64 + ((wave*16 + lane%16 + 16*(cp & 1)) & 63).
+# ----------------------------------------------------------------------------
+
+def plan_fields(desc):
+    f = dict(re.findall(r"\b(TR|TC|HP|HPc|nb|tile)=(\S+)", desc))
+    tr, tc = (int(v) for v in f["tile"].split("x"))
+    return tr, tc, int(f["HP"]), int(f["HPc"]), int(f["nb"])
+
+
+def halo32_b_extra(TR, TC, HP, HPc, nb, taps):
+    """Extra cycles over every B-fragment read of one work-group's phase."""
+    extra = 0
+    for jh, jw in taps:
+        for blk in range(nb):
+            for j in range(jh):
+                for jw_ in range(jw):
+                    shift = (jh - 1 - j) * HP + (jw - 1 - jw_)
+                    addr = []
+                    for lane in range(64):
+                        cp, l16 = lane >> 4, lane & 15
+                        px = blk * 16 + l16
+                        pb = (px // TC) * HP + px % TC if px < TR * TC else l16
+                        addr.append((cp * HPc + pb + shift) * 8)
+                    extra += extra_cycles_b64(addr)
+    return extra
+
+
+@pytest.mark.parametrize("name", ["resnet_stage_3x3", "deep_late_stage", "strided_downsample",
+                                  "asym_1x7"])
+def test_halo32_planner_conflict_rule(name):
+    """The planner counts a plan's fragment reads as conflict-free iff the
+    pitch is congruent to the tile width mod 16 (or the width is a multiple
+    of 16); it weighs that against a compile-time pitch.  The model agrees
+    with that rule on every graded plan, both ways."""
+    s = workloads.BY_NAME[name].shape
+    desc = gi.plan(gi.make_params(*s.as_tuple()[:10]), 0)
+    TR, TC, HP, HPc, nb = plan_fields(desc)
+    assert HPc % 32 == 16
+    taps = {(int(a), int(b)) for a, b in re.findall(r"taps=(\d+)x(\d+)", desc)}
+    predicted = (HP - TC) % 16 == 0 or TC % 16 == 0
+    assert (halo32_b_extra(TR, TC, HP, HPc, nb, taps) == 0) == predicted, (name, desc)
+
+
+@pytest.mark.parametrize("TR,TC,HP", [(7, 28, 44), (14, 14, 30), (14, 14, 46), (7, 17, 33),
+                                      (4, 32, 34), (13, 16, 18)])
+def test_halo32_congruent_pitch_conflict_free(TR, TC, HP):
+    """Any tile whose pitch is congruent to its width mod 16 (or whose width
+    is a multiple of 16) reads conflict-free, for 3x3 and 1x7 tap grids."""
+    HPc = ((TR + 6) * HP + 31) // 32 * 32 + 16
+    nb = (TR * TC + 15) // 16
+    assert halo32_b_extra(TR, TC, HP, HPc, nb, {(3, 3), (1, 7)}) == 0
+
+
+def test_halo32_a_reads_conflict_free():
+    for wave in range(4):
+        addr = [(cp * 64 + ((wave * 16 + l16 + 16 * (cp & 1)) & 63)) * 8
+                for cp in range(4) for l16 in range(16)]
+        assert extra_cycles_b64(addr) == 0
+
+
+# ----------------------------------------------------------------------------
+# The stem kernel (kernels_stem_f32.hip): 16-byte words (4 channels of a
+# position); lane l = 16r + j of tile row `row` = row0 + r reads position
+# row*pitch + ((j - row*pitch) mod 16) plus the tap shift.
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("pitch", [19, 20, 23, 32, 37])
+def test_stem_b_reads_conflict_free(pitch):
+    for row0 in (0, 4, 8, 12):
+        for shift in (0, 1, 2, pitch, pitch + 3, 3 * pitch + 3):
+            addr = []
+            for lane in range(64):
+                row = row0 + (lane >> 4)
+                col = ((lane & 15) - row * pitch) & 15
+                addr.append((row * pitch + col + shift) * 16)
+            assert extra_cycles_b128(addr) == 0, (pitch, row0, shift)
+    # With the plain column j the rows of a half wave collide unless the
+    # pitch is a multiple of 16.
+    if pitch % 16:
+        addr = [((row0 + (lane >> 4)) * pitch + (lane & 15)) * 16 for lane in range(64)
+                for row0 in (0,)]
+        assert extra_cycles_b128(addr) > 0

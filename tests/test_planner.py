@@ -127,3 +127,105 @@ def test_image_kernel_needs_its_instance():
     # Unforced, it needs a grid of at least one work-group per compute unit.
     assert "image kernel" not in plan_of(S(2, 64, 14, 14, 64, 3, 3, 1, 1, 1), 1)
     assert "image kernel" in plan_of(S(128, 256, 14, 14, 64, 3, 3, 1, 1, 1), 2)
+
+
+# ----------------------------------------------------------------------------
+# Planner invariants over seeded random shapes (host only).
+# ----------------------------------------------------------------------------
+
+def planner_shapes(seed, count):
+    """Shapes from tiny to production sizes: channel counts up to 640, planes
+    up to 120x120, batches up to 64, kernels 1..7, strides 1..4; a quarter
+    are network-style layers (channels in multiples of 32, square planes of
+    7..56, 3x3 or 1x1 at stride 1 or 2), the shapes the tiled kernels take."""
+    import random
+    rng = random.Random(seed)
+    out = []
+    while len(out) < count:
+        if rng.random() < 0.25:
+            k = rng.choice([1, 3, 3, 3])
+            hw = rng.choice([7, 14, 28, 56])
+            out.append(S(rng.choice([8, 16, 32, 64]), 32 * rng.randint(1, 16), hw, hw,
+                         32 * rng.randint(1, 16), k, k, rng.choice([1, 1, 1, 2]), k // 2, k // 2))
+            continue
+        k_h, k_w = rng.randint(1, 7), rng.randint(1, 7)
+        stride = rng.choice([1, 1, 1, 2, 2, 3, 4])
+        H, W = rng.randint(1, 120), rng.randint(1, 120)
+        ph, pw = rng.randint(0, k_h), rng.randint(0, k_w)
+        if H + 2 * ph < k_h or W + 2 * pw < k_w:
+            continue
+        out.append(S(rng.choice([1, 2, 4, 8, 16, 32, 64]), rng.randint(1, 640), H, W,
+                     rng.randint(1, 640), k_h, k_w, stride, ph, pw))
+    return out
+
+
+def fp32_bytes_over_limit(s):
+    oH = (s.H + 2 * s.pad_h - s.kH) // s.stride + 1
+    oW = (s.W + 2 * s.pad_w - s.kW) // s.stride + 1
+    return max(s.N * s.Ci * s.H * s.W, s.N * s.Co * oH * oW) * 4 > 0x7fff0000
+
+
+FP32_HALO_TAPS = {0, 1, 2, 3, 4, 6, 7, 9}
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_planner_invariants(seed):
+    import re
+    for s in planner_shapes(seed, 400):
+        p = gi.make_params(*s.as_tuple()[:10])
+        if gi.validate(p) != 0:
+            continue
+        for dt in (0, 1, 2):
+            desc = gi.plan(p, dt)
+            assert desc == gi.plan(p, dt), "plan is not deterministic"
+            variant = re.match(r"variant=(\w+) ", desc).group(1)
+            assert variant in ("generic", "halo", "stem"), desc
+            assert int(re.search(r"ws_bytes=(\d+)", desc).group(1)) >= 0
+            if variant == "stem":
+                assert dt == 0, desc
+            if "image kernel" in desc:
+                assert dt != 0 and s.stride == 1, desc
+            lds = re.search(r"\blds=(\d+)", desc)
+            if lds:
+                assert 0 < int(lds.group(1)) <= 160 * 1024, desc
+            wgs = re.search(r"\bwgs=(\d+)x(\d+)", desc)
+            if wgs:
+                a, b = int(wgs.group(1)), int(wgs.group(2))
+                assert a >= 1 and b >= 1 and a * b < 2 ** 31, desc
+            phases = re.findall(r"taps=(\d+)x(\d+) px=(\d+)x(\d+)", desc)
+            if phases and "fused" not in desc:
+                # Every input pixel falls in exactly one phase, and so does
+                # every tap when every residue class owns a pixel.
+                if s.H >= s.stride and s.W >= s.stride:
+                    assert sum(int(a) * int(b) for a, b, _, _ in phases) == s.kH * s.kW, desc
+                assert sum(int(c) * int(d) for _, _, c, d in phases) == s.H * s.W, desc
+            if fp32_bytes_over_limit(s):
+                assert variant == "generic", desc
+            if variant == "halo" and dt == 0:
+                # The fp32 halo kernel has cases for these tap counts only.
+                for a, b, _, _ in phases:
+                    assert int(a) * int(b) in FP32_HALO_TAPS, desc
+
+
+def test_planner_picks_generic_past_buffer_range():
+    """Tensors past the 32-bit buffer range go to the generic kernel, whose
+    batch offsets are 64-bit, for every element type."""
+    for s in [S(8, 64, 1024, 1024, 16, 3, 3, 1, 1, 1), S(1, 16, 64, 64, 512, 3, 3, 1, 1, 1),
+              S(600, 512, 40, 40, 64, 1, 1, 1, 0, 0), S(2, 64, 1200, 1200, 64, 7, 7, 2, 3, 3)]:
+        p = gi.make_params(*s.as_tuple()[:10])
+        assert gi.validate(p) == 0
+        for dt in (0, 1, 2):
+            desc = gi.plan(p, dt)
+            if fp32_bytes_over_limit(s):
+                assert desc.startswith("variant=generic"), (s, dt, desc)
+
+
+@pytest.mark.parametrize("shape", [S(3, 49, 15, 1, 9, 7, 5, 1, 3, 4), S(2, 64, 20, 20, 32, 5, 7, 1, 2, 3),
+                                   S(1, 64, 12, 12, 16, 6, 6, 1, 2, 2), S(1, 64, 12, 12, 16, 1, 5, 1, 0, 2),
+                                   S(1, 64, 24, 24, 16, 7, 7, 1, 3, 3)])
+def test_fp32_halo_rejects_unserved_tap_counts(shape):
+    """Tap counts the fp32 halo kernel has no case for (5, 35, 36, 49 ...;
+    past 31 a shift-built mask would wrap onto a served count) go to another
+    kernel rather than to a halo plan that would leave the pixels at zero."""
+    desc = plan_of(shape)
+    assert not desc.startswith("variant=halo"), desc

@@ -198,3 +198,25 @@ def sweep_shapes():
         S(1, 8, 4, 4, 8, 5, 5, 1, 4, 4),       # pad > kernel-1: taps land in padding
         S(1, 16, 3, 3, 32, 3, 3, 1, 0, 0),     # oH = 1
     ]
+
+
+def random_shapes(seed: int, count: int):
+    """`count` seeded random small shapes for sweeps: strides 1-4, kernels
+    1-7 per dimension (kH != kW allowed), pads 0..k per dimension, ragged
+    channel counts (a third of them Ci <= 4, a third Ci >= 16), H and W
+    1-24; every shape has oH, oW >= 1."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = []
+    while len(out) < count:
+        kH, kW = int(rng.integers(1, 8)), int(rng.integers(1, 8))
+        s = int(rng.integers(1, 5))
+        ph, pw = int(rng.integers(0, kH + 1)), int(rng.integers(0, kW + 1))
+        H, W = int(rng.integers(1, 25)), int(rng.integers(1, 25))
+        if (H + 2 * ph - kH) // s + 1 < 1 or (W + 2 * pw - kW) // s + 1 < 1:
+            continue
+        kind = len(out) % 3
+        Ci = int(rng.integers(1, 5)) if kind == 0 else (
+            int(rng.integers(16, 81)) if kind == 1 else int(rng.integers(5, 16)))
+        out.append(Shape(int(rng.integers(1, 4)), Ci, H, W, int(rng.integers(1, 49)), kH, kW, s,
+                         ph, pw))
+    return out
