@@ -20,13 +20,14 @@ __all__ = [
     "grad_input", "grad_input_noalloc", "Conv2dGiParams", "Conv2dGiError", "LibraryNotBuilt", "load_library",
     "make_params", "validate", "plan", "grad_weight", "grad_weight_plan", "grad_bias", "backward", "forward", "forward_plan", "set_fwd_variant", "set_variant", "set_halo_tile", "set_halo_split", "set_halo_fusion", "set_gw_variant", "set_gw_tile", "release_workspaces", "set_profile_events", "mfma_peak", "library_path", "exported_names",
     "OK", "EINVAL", "EUNSUPPORTED", "EHIP", "VARIANT_AUTO", "VARIANT_GENERIC", "VARIANT_HALO", "VARIANT_STEM",
+    "VARIANT_COL2IM",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_PKG, "libconv2d_gi.so")
 
 OK, EINVAL, EUNSUPPORTED, EHIP = 0, 1, 2, 3
-VARIANT_AUTO, VARIANT_GENERIC, VARIANT_HALO, VARIANT_STEM = 0, 1, 2, 3
+VARIANT_AUTO, VARIANT_GENERIC, VARIANT_HALO, VARIANT_STEM, VARIANT_COL2IM = 0, 1, 2, 3, 4
 
 _FIELDS = ("N", "Ci", "H", "W", "Co", "kH", "kW", "stride", "pad_h", "pad_w", "oH", "oW")
 

@@ -28,6 +28,7 @@ SOURCES = [
     "kernels_halo_bf16.hip",
     "kernels_img16.hip",
     "kernels_stem_f32.hip",
+    "kernels_col2im_f32.hip",
     "kernels_gw_f32.hip",
     "kernels_fwd_f32.hip",
     "noalloc.hip",

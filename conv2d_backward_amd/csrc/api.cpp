@@ -177,6 +177,11 @@ struct StemPlan {
     size_t ws_bytes = 0;
 };
 
+struct Col2imPlan {
+    gi::Col2imArgs args{};
+    size_t lds = 0;
+};
+
 struct Plan {
     int variant = CONV2D_GI_VARIANT_GENERIC;
     bool bf16 = false;
@@ -187,6 +192,7 @@ struct Plan {
     bool img16 = false;            // 16-bit inputs on the whole-image kernel
     Img16Plan im;
     StemPlan stem;                 // small Ci, fp32
+    Col2imPlan c2i;                // few columns, fp32
 };
 
 constexpr int kCUs = 256;               // MI355X compute units
@@ -599,6 +605,91 @@ bool plan_img16(const conv2d_gi_params &p, Img16Plan &out) {
     return true;
 }
 
+// Column plan (fp32): Ci*kH*kW columns in at most kCol2imMaxBlocks blocks
+// of 16, kCol2imMinCo < Co <= kCol2imMaxCo, kW <= 4*stride.  Chooses the
+// TH x TW input tile that minimises ceil(work-groups / CUs) x the busiest
+// wave's blocks of 16 grad_out positions (each a 16 x NBN MFMA product and
+// its fold), the work-groups running one per compute unit.
+bool plan_col2im(const conv2d_gi_params &p, Col2imPlan &out) {
+    const int ncols = p.Ci * p.kH * p.kW;
+    const int nbn = (ncols + 15) / 16;
+    if (nbn > gi::kCol2imMaxBlocks || p.Co <= gi::kCol2imMinCo || p.Co > gi::kCol2imMaxCo ||
+        p.stride > gi::kCol2imMaxStride || p.kW > 4 * p.stride)
+        return false;
+    const int64_t lim = 0x7fff0000LL;
+    if ((int64_t)p.N * p.Co * p.oH * p.oW * 4 > lim) return false;
+    if ((int64_t)p.N * p.Ci * p.H * p.W * 4 > lim) return false;
+    if ((int64_t)p.Co * ncols * 4 > lim) return false;
+    const int s = p.stride;
+    const int r0 = p.kH - 1, c0 = (p.kW - 1 + 3) / 4 * 4;
+    bool found = false;
+    double best = 0;
+    const int Wq = (p.W + 3) / 4 * 4;
+    for (int TH = 1; TH <= p.H; ++TH) {
+        // Only the smallest TH for each row-tile count.
+        const int tiles_r = (p.H + TH - 1) / TH;
+        if (TH > 1 && (p.H + TH - 2) / (TH - 1) == tiles_r) continue;
+        for (int TW = 4; TW <= Wq; TW += 4) {
+            const int tiles_c = (p.W + TW - 1) / TW;
+            if (TW > 4 && (p.W + TW - 5) / (TW - 4) == tiles_c) continue;
+            const int nq = (TH + p.kH - 2) / s + 1;   // grad_out rows meeting a tile
+            const int ncq = (TW + p.kW - 2) / s + 1;  // and columns
+            // Rows per wave: even, each half at least D = ceil(kH / stride).
+            const int RW = std::max((nq + 3) / 4 + ((nq + 3) / 4 & 1), 2 * ((p.kH + s - 1) / s));
+            if (ncq > 16 * gi::kCol2imBlocksPerRow) continue;
+            const int ncb = gi::kCol2imBlocksPerRow;
+            const int LR = r0 + TH + p.kH - 1;
+            const int LP = (std::max(c0 + TW + p.kW - 1,
+                                     c0 + 16 * s * gi::kCol2imBlocksPerRow + p.kW) + 15) / 16 * 16;
+            const size_t lds = (((size_t)p.Ci * LR * LP + 64 + 16 * s + 3) / 4 * 4 +
+                                (size_t)gi::kCol2imMaxCo * ncols) * 4;
+            if (lds > kLdsBytes) continue;
+            const int64_t wgs = (int64_t)p.N * tiles_r * tiles_c;
+            if (wgs > INT32_MAX) continue;
+            const double per_wg =
+                (double)RW * ncb * (16.0 * nbn * 32 + 400.0) + 6000.0;
+            const double cost = (double)((wgs + kCUs - 1) / kCUs) * per_wg +
+                                0.02 * (double)wgs * per_wg / kCUs;
+            if (!found || cost < best) {
+                found = true;
+                best = cost;
+                gi::Col2imArgs &a = out.args;
+                a = gi::Col2imArgs{};
+                a.TH = TH;
+                a.TW = TW;
+                a.tiles_r = tiles_r;
+                a.tiles_c = tiles_c;
+                a.RW = RW;
+                a.LR = LR;
+                a.LP = LP;
+            }
+        }
+    }
+    if (!found) return false;
+    gi::Col2imArgs &a = out.args;
+    a.g_bytes = (uint32_t)((int64_t)p.N * p.Co * p.oH * p.oW * 4);
+    a.w_bytes = (uint32_t)((int64_t)p.Co * ncols * 4);
+    a.d_bytes = (uint32_t)((int64_t)p.N * p.Ci * p.H * p.W * 4);
+    a.N = p.N;
+    a.Ci = p.Ci;
+    a.H = p.H;
+    a.W = p.W;
+    a.Co = p.Co;
+    a.oH = p.oH;
+    a.oW = p.oW;
+    a.kH = p.kH;
+    a.kW = p.kW;
+    a.stride = p.stride;
+    a.pad_h = p.pad_h;
+    a.pad_w = p.pad_w;
+    a.ncols = ncols;
+    a.r0 = r0;
+    a.c0 = c0;
+    a.wofs = gi::col2im_f32_weight_offset(a);
+    out.lds = gi::col2im_f32_lds_bytes(a);
+    return true;
+}
+
 // Small-Ci plan (fp32, Ci <= 4): 16 x 16 phase-grid tiles; phase groups of
 // near-equal tap totals, run in sets of up to two per work-group over one
 // grad_out halo.  Every phase's tap count must be one the kernel is built
@@ -776,6 +867,11 @@ Plan make_plan(const conv2d_gi_params &p, bool bf16) {
         plan.ws_bytes = (size_t)plan.halo.ws_floats * sizeof(float);
         return plan;
     }
+    if (!bf16 && (forced == CONV2D_GI_VARIANT_COL2IM || forced == CONV2D_GI_VARIANT_AUTO) &&
+        plan_col2im(p, plan.c2i)) {
+        plan.variant = CONV2D_GI_VARIANT_COL2IM;
+        return plan;
+    }
     if (!bf16 && (forced == CONV2D_GI_VARIANT_STEM || forced == CONV2D_GI_VARIANT_AUTO) &&
         plan_stem(p, phases, plan.stem)) {
         plan.variant = CONV2D_GI_VARIANT_STEM;
@@ -860,7 +956,13 @@ int run(const T *grad_out, const T *weight, float *dst, const conv2d_gi_params *
     // timestamps (first and last launch when there are several).
     gi::KernelEvents ev;
     if (g_prof_begin && g_prof_end) ev = {g_prof_begin, g_prof_end};
-    if (plan.variant == CONV2D_GI_VARIANT_STEM) {
+    if (plan.variant == CONV2D_GI_VARIANT_COL2IM) {
+        gi::Col2imArgs &a = plan.c2i.args;
+        a.grad_out = (const float *)grad_out;
+        a.w = (const float *)weight;
+        a.dst = dst;
+        e = gi::launch_col2im_f32(a, stream, ev);
+    } else if (plan.variant == CONV2D_GI_VARIANT_STEM) {
         if (e == hipSuccess) {
             gi::StemArgs &a = plan.stem.args;
             a.grad_out = (const float *)grad_out;
@@ -1180,10 +1282,19 @@ std::string describe(const Plan &plan, int dt) {
     std::string s = "variant=";
     s += plan.variant == CONV2D_GI_VARIANT_HALO   ? "halo"
          : plan.variant == CONV2D_GI_VARIANT_STEM ? "stem"
+         : plan.variant == CONV2D_GI_VARIANT_COL2IM ? "col2im"
                                                   : "generic";
     s += " dtype=";
     s += dt == 2 ? "f16" : bf16 ? "bf16" : "f32";
     s += " ws_bytes=" + std::to_string(plan.ws_bytes);
+    if (plan.variant == CONV2D_GI_VARIANT_COL2IM) {
+        const gi::Col2imArgs &a = plan.c2i.args;
+        s += " launches=1 [tile=" + std::to_string(a.TH) + "x" + std::to_string(a.TW) +
+             " wgs=" + std::to_string((int64_t)a.N * a.tiles_r * a.tiles_c) +
+             " cols=" + std::to_string(a.ncols) + " rows_per_wave=" + std::to_string(a.RW) +
+             " lds=" + std::to_string(plan.c2i.lds) + " pitch=" + std::to_string(a.LP) + "]";
+        return s;
+    }
     if (plan.variant == CONV2D_GI_VARIANT_STEM) {
         const gi::StemArgs &a = plan.stem.args;
         s += " launches=1 [tiles=" + std::to_string(a.N) + "x" + std::to_string(a.tiles_r) + "x" +
@@ -1579,7 +1690,8 @@ const char *conv2d_gi_last_hip_error(void) { return g_last_hip; }
 
 int conv2d_gi_set_variant(int variant) {
     if (variant != CONV2D_GI_VARIANT_AUTO && variant != CONV2D_GI_VARIANT_GENERIC &&
-        variant != CONV2D_GI_VARIANT_HALO && variant != CONV2D_GI_VARIANT_STEM)
+        variant != CONV2D_GI_VARIANT_HALO && variant != CONV2D_GI_VARIANT_STEM &&
+        variant != CONV2D_GI_VARIANT_COL2IM)
         return -1;
     const int old = g_variant;
     g_variant = variant;

@@ -226,3 +226,33 @@ struct Img16Args {
 };
 
 }  // namespace gi
+
+namespace gi {
+
+// Arguments of the column kernel (kernels_col2im_f32.hip: fp32, few input
+// channels).  The sum over (co, kh, kw) is taken in two steps: for every
+// grad_out position q = (oh, ow) the columns
+//   Y[q][c] = sum_co grad_out[co][q] * w[co][c],   c = (ci, kh, kw),
+// a GEMM with K = Co on the matrix cores, and then every Y[q][c] is added to
+// grad_input[ci][s*oh - pad_h + kh][s*ow - pad_w + kw] (the fold of the
+// columns) in an LDS tile.  Each column lands on exactly one input pixel, so
+// no tap that the stride rules out is ever multiplied.  A work-group owns a
+// TH x TW tile of one image and computes the columns of every grad_out
+// position whose footprint meets the tile (those on the tile's border are
+// also computed by the neighbouring work-group, each keeping its own part).
+struct Col2imArgs {
+    const float *grad_out;  // [N, Co, oH, oW]
+    const float *w;         // [Co, Ci, kH, kW], i.e. [Co][ncols]
+    float *dst;             // [N, Ci, H, W]
+    uint32_t g_bytes, w_bytes, d_bytes;
+    int32_t N, Ci, H, W, Co, oH, oW, kH, kW, stride, pad_h, pad_w;
+    int32_t ncols;          // Ci * kH * kW
+    int32_t TH, TW;         // input pixels owned by a work-group
+    int32_t tiles_r, tiles_c;  // grid = N * tiles_r * tiles_c (1-D, xcd_order)
+    int32_t RW;             // grad_out rows per wave and tile; stride * RW >= kH
+    int32_t LR, LP;         // LDS tile rows and row pitch (floats), per input channel
+    int32_t r0, c0;         // LDS row and column of tile pixel (0, 0)
+    int32_t wofs;           // LDS float offset of the staged weight
+};
+
+}  // namespace gi

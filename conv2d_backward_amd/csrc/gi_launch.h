@@ -108,4 +108,18 @@ int stem_f32_waves(int ngroups);
 size_t stem_f32_lds_bytes(int hpmax, int waves);
 hipError_t launch_stem_f32(const StemArgs &a, hipStream_t s, const KernelEvents &ev);
 
+// Column kernel (kernels_col2im_f32.hip): fp32, Ci * kH * kW <= 16 *
+// kCol2imMaxBlocks columns, kCol2imMinCo < Co <= kCol2imMaxCo, stride <=
+// kCol2imMaxStride, kW <= 4 * stride (no two columns of one fold batch meet
+// on the same pixel), and tiles whose grad_out rows take at most
+// kCol2imBlocksPerRow blocks of 16 positions.
+constexpr int kCol2imMaxBlocks = 10;
+constexpr int kCol2imMinCo = 48;
+constexpr int kCol2imMaxCo = 64;
+constexpr int kCol2imMaxStride = 2;
+constexpr int kCol2imBlocksPerRow = 2;
+int col2im_f32_weight_offset(const Col2imArgs &a);
+size_t col2im_f32_lds_bytes(const Col2imArgs &a);
+hipError_t launch_col2im_f32(const Col2imArgs &a, hipStream_t s, const KernelEvents &ev);
+
 }  // namespace gi

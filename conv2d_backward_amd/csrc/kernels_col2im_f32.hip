@@ -1,0 +1,426 @@
+// kernels_col2im_f32.hip -- fp32 column kernel for few input channels (gfx950).
+//
+// The gradient is the sum over (co, kh, kw) of weight x grad_out that the
+// implicit GEMM of meganeura conv2d_grad_input_gemm.wgsl (header comment:
+// C[Ci, pixels] = A[Ci, K] x B[K, pixels], K = Co*kH*kW) contracts in one
+// go.  With Ci <= 4 that GEMM has at most 4 rows, so any matrix-core shape
+// but the 4x4 blocks is mostly padding.  This kernel takes the same sum in
+// two steps instead:
+//   * columns: Y[q][c] = sum_co grad_out[co][q] * w[co][c] for every
+//     grad_out position q = (oh, ow) and every column c = (ci, kh, kw): a
+//     GEMM with M = positions, N = Ci*kH*kW (147 for an RGB 7x7 stem) and
+//     K = Co, on V_MFMA_F32_16X16X4_F32;
+//   * fold: Y[q][c] is added to input pixel (s*oh - pad_h + kh,
+//     s*ow - pad_w + kw) of channel ci, the pixel whose gradient that
+//     product belongs to (doppler conv2d_backward_input.wgsl: an input pixel
+//     sums the contributions of every output pixel it fed).  Each column
+//     lands on exactly one pixel, so taps that the stride rules out are never
+//     formed.
+//
+// Work-group: 4 waves (one per SIMD) own a TH x TW tile of one image, held
+// in LDS for every input channel with a border of kH-1 rows and at least
+// kW-1 columns, and compute the columns of every grad_out position whose
+// footprint meets the tile (positions on the border are also computed by
+// the neighbouring work-group; each keeps what falls on its own tile).
+//
+// Matrix cores: lane l = 16g + i supplies A[i][k=g] = grad_out[4c+g][q_i]
+// and B[k=g][i] = w[4c+g][16nb+i] for k step c and column block nb, and
+// receives Y[q_{4g+r}][16nb+i] in register r.  The weight is staged once in
+// LDS and its B fragments of every (c, nb) held in registers (16 x 10 for
+// Co <= 64 and 160 columns); grad_out is read as blocks of 16 positions of
+// one row.
+//
+// Fold: the accumulators of a block start as the tile values its columns
+// land on (read from LDS), the block's 16 k steps add its products onto
+// them, and they are written back: the fold costs LDS reads and writes but
+// no vector ALU work, which on one wave per SIMD would hold up the matrix
+// cores.  That needs the 64 pixels x 16 columns of a block to be distinct
+// pixels, so a block's 16 positions are spread out: 8 positions 4 apart of
+// grad_out row k and the same 8 columns of row k + RW/2 (4*stride >= kW and
+// (RW/2)*stride >= kH, so no two of them feed a common pixel).  Lane l =
+// 16g + i: A row i is position i (row k for i < 8), D row 4g + r position
+// 4g + r.  A pair of rows takes 4 such blocks (column classes 0..3, 32
+// positions of each row).
+//
+// Order: between two blocks of a pair the last k step of one and the first
+// of the next run back to back, with the first block's writes issued two
+// MFMAs after the MFMA that finishes each column block, and each of the
+// next block's reads after the write of the column block above it (a pixel
+// is only reached by columns of one (ci, kh), i.e. of at most two adjacent
+// column blocks).  The next block's loads are issued during the current
+// block's middle k steps.  The four waves' rows are RW apart and a barrier
+// after every pair keeps them in step, so no two waves touch a pixel at the
+// same time.  Every pixel receives its columns in a fixed order and the
+// result is deterministic.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gi_common.h"
+#include "gi_launch.h"
+
+namespace gi {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+namespace {
+
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9)
+constexpr int kOOB = 0x7ffffff0;        // byte offset past the end of every buffer
+constexpr int kSteps = kCol2imMaxCo / 4;  // k steps of 4 output channels
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (long)bytes, kRsrcWord3);
+}
+
+// Load at byte offset voff (per lane) + soff (uniform).
+__device__ __forceinline__ float load_f32s(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+
+// NBN: column blocks of 16 (Ci*kH*kW <= 16*NBN); S: the stride; CO: 64 when
+// Co is 64 (every k step whole), 4 when Co is another multiple of 4 (k
+// steps wholly inside or past Co), 0 otherwise.  Every grad_out row of a
+// tile takes kCol2imBlocksPerRow = 2 windows of 16 positions.
+template <int NBN, int S, int CO>
+__global__ __launch_bounds__(256, 1) void gi_col2im_f32(const Col2imArgs A) {
+    extern __shared__ __attribute__((aligned(16))) float tile[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, i = lane & 15;
+
+    // Logical order: tile column fastest, then tile row, image.
+    int bid = xcd_order(blockIdx.x, gridDim.x);
+    const int tc = bid % A.tiles_c;
+    bid /= A.tiles_c;
+    const int tr = bid % A.tiles_r;
+    const int n = bid / A.tiles_r;
+    const int ih0 = tr * A.TH, iw0 = tc * A.TW;
+
+    // grad_out rows and columns whose footprint meets the tile: position oh
+    // feeds input rows S*oh - pad_h .. S*oh - pad_h + kH - 1.
+    const int xr = ih0 + A.pad_h - A.kH + 1, xc = iw0 + A.pad_w - A.kW + 1;
+    const int oh_lo = xr <= 0 ? 0 : (xr + S - 1) / S;
+    const int ow_lo = xc <= 0 ? 0 : (xc + S - 1) / S;
+    const int oh_hi = min(A.oH - 1, (ih0 + A.TH - 1 + A.pad_h) / S);
+    const int ow_hi = min(A.oW - 1, (iw0 + A.TW - 1 + A.pad_w) / S);
+    const int row0 = oh_lo + wave * A.RW;
+    const int rows_w = max(0, min(A.RW, oh_hi - row0 + 1));  // this wave's rows
+
+    const __amdgpu_buffer_rsrc_t wrs = make_rsrc(A.w, A.w_bytes);
+    const __amdgpu_buffer_rsrc_t drs = make_rsrc(A.dst, A.d_bytes);
+
+    // LDS: the tile [Ci][LR][LP], one slot per lane (plus the fold's
+    // position and class offsets) for columns past the last, then the
+    // weight staged as [kCol2imMaxCo][ncols] (rows past Co zero).
+    const int plane = A.LR * A.LP;
+    const int tfl = A.Ci * plane;
+    const int dummy = tfl + lane;
+    float *const wst = tile + A.wofs;
+    for (int k = tid * 4; k < tfl; k += 1024) *(v4f *)(tile + k) = v4f{0.f, 0.f, 0.f, 0.f};
+    {
+        const int wreal = A.Co * A.ncols, wall = kCol2imMaxCo * A.ncols;
+        // 16 bytes per lane; the words past the weight's end read zero.
+        for (int e = tid * 4; e < wall; e += 1024) {
+            v4f v = v4f{0.f, 0.f, 0.f, 0.f};
+            if (e < wreal)
+                v = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(wrs, e * 4, 0, 0));
+            *(v4f *)(wst + e) = v;
+        }
+    }
+
+    // grad_out of a block: lane i loads position i (row k of the pair for i
+    // < 8, row k + RW/2 for i >= 8; column ow_lo + 4 (i mod 8) + class),
+    // output channel 4c + g at byte offset vo (the pair and the lane) +
+    // 4 class + c * 16 * oH * oW (uniform); zeros past the wave's rows, the
+    // tile's positions or Co.  Steps wholly past Co are not loaded; with
+    // CO = 0 the channels of the last step past Co take the kOOB offset.
+    const int oHW = A.oH * A.oW;
+    const int csteps = (A.Co + 3) / 4;
+    const int RWh = A.RW / 2;
+    const int owl = ow_lo + 4 * (i & 7);  // this lane's position column, class 0
+    auto pair_vo = [&](int k) {
+        const int row = k + (i >= 8 ? RWh : 0);
+        return row < rows_w ? (((n * A.Co + g) * A.oH + row0 + row) * A.oW + owl) * 4 : kOOB;
+    };
+    // k step c reads through a descriptor whose base is advanced to output
+    // channel 4c (scalar arithmetic; its range is the rest of grad_out), and
+    // the class is the load's immediate offset.
+    // Steps wholly past Co are never loaded (their weights are zero and x
+    // keeps its zero).  That also keeps the range from wrapping: below
+    // csteps, 4c < Co, so what is left after the base is advanced is at
+    // least one output channel's plane (a wrapped range would let the kOOB
+    // offset through to memory past the buffer).
+    auto gload1 = [&](int c, int vo, int cls, float &x) {
+        // (Formed afresh at each use: holding all 16 descriptors would not
+        // fit the scalar registers.)
+        const float *pc = A.grad_out + (size_t)c * 4 * oHW;
+        const uint32_t used = (uint32_t)c * 16 * oHW;
+        uint32_t nc = A.g_bytes - used;
+        asm volatile("" : "+s"(pc), "+s"(nc));
+        const __amdgpu_buffer_rsrc_t rc = make_rsrc(pc, nc);
+        if (CO == 64 || c < csteps)
+            x = load_f32s(rc, CO != 0 || 4 * c + g < A.Co ? vo + 4 * cls : kOOB, 0);
+    };
+    // The lane's load offset for class cls (kOOB past the tile's positions).
+    auto class_vo = [&](int vo, int cls) { return owl + cls <= ow_hi ? vo : kOOB; };
+    float gA[kSteps], gB[kSteps];
+#pragma unroll
+    for (int c = 0; c < kSteps; ++c) gA[c] = gB[c] = 0.f;
+    {
+        const int vo = class_vo(pair_vo(0), 0);
+#pragma unroll
+        for (int c = 0; c < kSteps; ++c) gload1(c, vo, 0, gA[c]);
+    }
+    __syncthreads();  // the tile is zero and the weight staged
+
+    // B fragments of every k step and column block.
+    float wv[kSteps][NBN];
+#pragma unroll
+    for (int c = 0; c < kSteps; ++c)
+#pragma unroll
+        for (int nb = 0; nb < NBN; ++nb) {
+            const int col = 16 * nb + i;
+            const float x = wst[(4 * c + g) * A.ncols + (col < A.ncols ? col : 0)];
+            wv[c][nb] = col < A.ncols ? x : 0.f;
+            // Held in the accumulator file (the MFMAs read them from there),
+            // leaving the vector registers to the operands and addresses.
+            asm volatile("" : "+a"(wv[c][nb]));
+        }
+
+    // Tile offset of this lane's column 16nb + i relative to its position's
+    // first pixel: channel plane, kh rows, kw columns.
+    const int khw = A.kH * A.kW;
+    int cbase[NBN];
+#pragma unroll
+    for (int nb = 0; nb < NBN; ++nb) {
+        const int col = 16 * nb + i;
+        const int ci = col / khw, rem = col - (col / khw) * khw;
+        const int kh = rem / A.kW, kw = rem - (rem / A.kW) * A.kW;
+        cbase[nb] = ci * plane + kh * A.LP + kw;
+    }
+    const bool last_ok = 16 * (NBN - 1) + i < A.ncols;
+
+    // Fold byte addresses of the pair of rows (k, k + RW/2), class 0, r = 0:
+    // D row 4g + r is position 4 (4 (g & 1) + r) + class of row k + RW/2
+    // (g >= 2); r and the class are immediate offsets (4 S r + S class
+    // floats).  Columns past the last and a missing second row go to the
+    // lane's own slot past the tile.
+    int ad[NBN];
+    auto pair_addr = [&](int k) {
+        const bool hi = g >= 2;
+        const bool rv = !hi || k + RWh < rows_w;
+        const int qoff = (S * (row0 + k + (hi ? RWh : 0)) - A.pad_h - ih0 + A.r0) * A.LP +
+                         S * (ow_lo + 16 * (g & 1)) - A.pad_w - iw0 + A.c0;
+#pragma unroll
+        for (int nb = 0; nb < NBN; ++nb) {
+            const bool ok = rv && (nb < NBN - 1 || last_ok);
+            ad[nb] = (ok ? cbase[nb] + qoff : dummy) * 4;
+        }
+    };
+    // Tile reads and writes of column block nb for class cls, r = 0..3.
+    auto tread = [&](int nb, int cls, v4f(&acc)[NBN]) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            acc[nb][r] = *(const float *)((const char *)tile + ad[nb] + (4 * S * r + S * cls) * 4);
+    };
+    auto twrite = [&](int nb, int cls, const v4f(&acc)[NBN]) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            *(float *)((char *)tile + ad[nb] + (4 * S * r + S * cls) * 4) = acc[nb][r];
+            asm volatile("" ::: "memory");  // single-word writes, straight from the accumulators
+        }
+    };
+    auto mfma = [&](const float(&gc)[kSteps], int c, int nb, v4f(&acc)[NBN]) {
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(gc[c], wv[c][nb], acc[nb], 0, 0, 0);
+    };
+
+    // The middle k steps 1..14 of a block (operands gc), with the loads of
+    // the next block (class ncls at pair offset nvo, into gn) among them.
+    auto middle = [&](const float(&gc)[kSteps], v4f(&acc)[NBN], float(&gn)[kSteps], int nvo,
+                      int ncls) {
+        const int vo = class_vo(nvo, ncls);
+#pragma unroll
+        for (int c = 1; c < kSteps - 1; ++c) {
+#pragma unroll
+            for (int nb = 0; nb < NBN; ++nb) {
+                mfma(gc, c, nb, acc);
+                if (nb == 0) gload1(c - 1, vo, ncls, gn[c - 1]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        gload1(kSteps - 2, vo, ncls, gn[kSteps - 2]);
+        gload1(kSteps - 1, vo, ncls, gn[kSteps - 1]);
+    };
+    // The last k step of class cls (operands gc) and the first of class
+    // cls + 1 (operands gn), with the writes of cls and the reads of cls + 1.
+    auto boundary = [&](const float(&gc)[kSteps], const float(&gn)[kSteps], int cls,
+                        v4f(&acc)[NBN]) {
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int t = 0; t < NBN; ++t) {
+            mfma(gc, kSteps - 1, t, acc);
+            if (t >= 2) twrite(t - 2, cls, acc);
+            if (t >= 3) tread(t - 3, cls + 1, acc);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int w = NBN - 2; w < NBN; ++w)
+            if (w >= 0) twrite(w, cls, acc);
+#pragma unroll
+        for (int r = NBN - 3; r < NBN; ++r)
+            if (r >= 0) tread(r, cls + 1, acc);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int nb = 0; nb < NBN; ++nb) {
+            mfma(gn, 0, nb, acc);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    v4f acc[NBN];
+    // Pairs of rows (k, k + RW/2): four blocks (classes 0..3); a barrier
+    // after each pair.  gA holds class 0 of the pair when it starts.
+    for (int k = 0; k < RWh; ++k) {
+        if (k < rows_w) {
+            pair_addr(k);
+            const int vo = pair_vo(k);
+            const int vo_next = pair_vo(k + 1);
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int nb = 0; nb < NBN; ++nb) tread(nb, 0, acc);
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int nb = 0; nb < NBN; ++nb) mfma(gA, 0, nb, acc);
+            middle(gA, acc, gB, vo, 1);
+            boundary(gA, gB, 0, acc);
+            middle(gB, acc, gA, vo, 2);
+            boundary(gB, gA, 1, acc);
+            middle(gA, acc, gB, vo, 3);
+            boundary(gA, gB, 2, acc);
+            middle(gB, acc, gA, vo_next, 0);
+#pragma unroll
+            for (int nb = 0; nb < NBN; ++nb) mfma(gB, kSteps - 1, nb, acc);
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int nb = 0; nb < NBN; ++nb) twrite(nb, 3, acc);
+            asm volatile("" ::: "memory");
+        }
+        __syncthreads();
+    }
+
+    // Epilogue: the tile's pixels inside the image, 16 bytes per lane where
+    // rows are whole quads (lanes: 16 quads of a row, 16 rows at a time).
+    const int H = A.H, W = A.W;
+    if ((W & 3) == 0 && (A.TW & 3) == 0) {
+        const int qr = A.TW / 4;
+        for (int qc = tid & 15; qc < qr; qc += 16)
+            for (int ci = 0; ci < A.Ci; ++ci)
+                for (int row = tid >> 4; row < A.TH; row += 16) {
+                    const int ih = ih0 + row, iw = iw0 + 4 * qc;
+                    const v4f v =
+                        *(const v4f *)(tile + ci * plane + (A.r0 + row) * A.LP + A.c0 + 4 * qc);
+                    const int off =
+                        (ih < H && iw < W) ? (((n * A.Ci + ci) * H + ih) * W + iw) * 4 : kOOB;
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, v), drs,
+                        off, 0, 0);
+                }
+    } else {
+        for (int col = tid & 15; col < A.TW; col += 16)
+            for (int ci = 0; ci < A.Ci; ++ci)
+                for (int row = tid >> 4; row < A.TH; row += 16) {
+                    const int ih = ih0 + row, iw = iw0 + col;
+                    const float v = tile[ci * plane + (A.r0 + row) * A.LP + A.c0 + col];
+                    const int off =
+                        (ih < H && iw < W) ? (((n * A.Ci + ci) * H + ih) * W + iw) * 4 : kOOB;
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), drs, off, 0, 0);
+                }
+    }
+}
+
+// Work-groups of this kernel run one per compute unit: its four waves take
+// a SIMD each, and asking for more than half the CU's LDS keeps a second
+// work-group from sharing it.
+constexpr size_t kOnePerCuLds = 80 * 1024 + 256;
+
+}  // namespace
+
+int col2im_f32_weight_offset(const Col2imArgs &a) {
+    // The tile, then one slot per lane (plus the fold's position and class offsets)
+    // for columns past the last; the weight stage starts 16-byte aligned.
+    return (a.Ci * a.LR * a.LP + 64 + 16 * a.stride + 3) / 4 * 4;
+}
+
+size_t col2im_f32_lds_bytes(const Col2imArgs &a) {
+    const size_t bytes =
+        ((size_t)col2im_f32_weight_offset(a) + (size_t)kCol2imMaxCo * a.ncols) * sizeof(float);
+    return bytes > kOnePerCuLds ? bytes : kOnePerCuLds;
+}
+
+namespace {
+
+template <int S, int CO>
+const void *col2im_fn(int nbn) {
+    switch (nbn) {
+        case 1: return (const void *)gi_col2im_f32<1, S, CO>;
+        case 2: return (const void *)gi_col2im_f32<2, S, CO>;
+        case 3: return (const void *)gi_col2im_f32<3, S, CO>;
+        case 4: return (const void *)gi_col2im_f32<4, S, CO>;
+        case 5: return (const void *)gi_col2im_f32<5, S, CO>;
+        case 6: return (const void *)gi_col2im_f32<6, S, CO>;
+        case 7: return (const void *)gi_col2im_f32<7, S, CO>;
+        case 8: return (const void *)gi_col2im_f32<8, S, CO>;
+        case 9: return (const void *)gi_col2im_f32<9, S, CO>;
+        case 10: return (const void *)gi_col2im_f32<10, S, CO>;
+        default: return nullptr;
+    }
+}
+
+template <int S>
+const void *col2im_fn_co(int nbn, int Co) {
+    return Co == 64 ? col2im_fn<S, 64>(nbn) : Co % 4 == 0 ? col2im_fn<S, 4>(nbn) : col2im_fn<S, 0>(nbn);
+}
+
+}  // namespace
+
+hipError_t launch_col2im_f32(const Col2imArgs &a, hipStream_t s, const KernelEvents &ev) {
+    const int nbn = (a.ncols + 15) / 16;
+    // The shapes the kernel's indexing assumes.
+    if (a.ncols != a.Ci * a.kH * a.kW || nbn < 1 || nbn > kCol2imMaxBlocks)
+        return hipErrorInvalidValue;
+    if (a.Co <= kCol2imMinCo || a.Co > kCol2imMaxCo || a.stride < 1 ||
+        a.stride > kCol2imMaxStride || a.kW > 4 * a.stride)
+        return hipErrorInvalidValue;
+    // Every tile's grad_out rows fit the four waves' RW rows each, a wave's
+    // two row sets are D apart (RW even, RW/2 >= D), and every row's
+    // positions fit its blocks.
+    const int D = (a.kH + a.stride - 1) / a.stride;
+    if ((a.RW & 1) || a.RW / 2 < D || 4 * a.RW < (a.TH + a.kH - 2) / a.stride + 1)
+        return hipErrorInvalidValue;
+    if (a.wofs != col2im_f32_weight_offset(a)) return hipErrorInvalidValue;
+    if ((a.TW + a.kW - 2) / a.stride + 1 > 16 * kCol2imBlocksPerRow) return hipErrorInvalidValue;
+    // Border and alignment of the LDS tile; its row pitch holds the pixels of
+    // every position of a row's blocks (those past the tile's positions fold
+    // zeros into the border).
+    if (a.r0 < a.kH - 1 || a.LR < a.r0 + a.TH + a.kH - 1 || a.c0 < a.kW - 1 || (a.c0 & 3) ||
+        (a.LP & 3) || a.LP < a.c0 + 16 * a.stride * kCol2imBlocksPerRow + a.kW ||
+        a.LP < a.c0 + a.TW + a.kW - 1)
+        return hipErrorInvalidValue;
+    if ((int64_t)a.tiles_r * a.TH < a.H || (int64_t)a.tiles_c * a.TW < a.W)
+        return hipErrorInvalidValue;
+    const size_t lds = col2im_f32_lds_bytes(a);
+    if (lds > 160 * 1024) return hipErrorInvalidValue;
+    const int64_t wgs = (int64_t)a.N * a.tiles_r * a.tiles_c;
+    if (wgs < 1 || wgs > INT32_MAX) return hipErrorInvalidValue;
+    const void *fn = a.stride == 1 ? col2im_fn_co<1>(nbn, a.Co) : col2im_fn_co<2>(nbn, a.Co);
+    if (!fn) return hipErrorInvalidValue;
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    void *args[] = {const_cast<Col2imArgs *>(&a)};
+    return hipExtLaunchKernel(fn, dim3((unsigned)wgs), dim3(256), args, lds, s, ev.start, ev.stop,
+                              0);
+}
+
+}  // namespace gi

@@ -46,6 +46,7 @@ KERNEL_SOURCES = {
     ("halo", "bf16"): ["kernels_halo_bf16.hip", "half_launch.h"],
     ("halo", "f16"): ["kernels_halo_bf16.hip", "half_launch.h"],
     ("stem", "f32"): ["kernels_stem_f32.hip"],
+    ("col2im", "f32"): ["kernels_col2im_f32.hip"],
     ("gw", "f32"): ["kernels_gw_f32.hip", "gw_common.h"],
     ("gwd", "f32"): ["kernels_gw_f32.hip", "gw_common.h"],
     ("fwd", "f32"): ["kernels_fwd_f32.hip", "fwd_common.h"],

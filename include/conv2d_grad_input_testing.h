@@ -25,9 +25,15 @@ enum {
     CONV2D_GI_VARIANT_HALO = 2,    /* Ci >= 16 (bf16: stride 1): grad_out halo
                                       tile in LDS, every tap a shifted view of
                                       it; other shapes fall back to GENERIC    */
-    CONV2D_GI_VARIANT_STEM = 3     /* fp32, Ci <= 4: 4x4 matrix-core blocks with
+    CONV2D_GI_VARIANT_STEM = 3,    /* fp32, Ci <= 4: 4x4 matrix-core blocks with
                                       the input channels on one side; other
                                       shapes fall back to GENERIC              */
+    CONV2D_GI_VARIANT_COL2IM = 4   /* fp32, Ci*kH*kW <= 160, 48 < Co <= 64,
+                                      kW <= 4*stride: per grad_out position the
+                                      products with every (ci, kh, kw) column
+                                      on the matrix cores, folded onto their
+                                      input pixels in LDS; other shapes fall
+                                      back to GENERIC                          */
 };
 
 /*

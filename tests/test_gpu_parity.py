@@ -250,6 +250,35 @@ def test_forced_stem(idx):
     full_parity(s, 1900 + idx, "f32", gi.VARIANT_STEM, dist="normal")
 
 
+COL2IM_SHAPES = [
+    workloads.Shape(2, 3, 45, 44, 64, 7, 7, 2, 3, 3),      # stem-like, ragged tiles
+    workloads.Shape(1, 3, 40, 36, 64, 7, 7, 2, 3, 3),      # several tiles per image
+    workloads.Shape(2, 3, 23, 19, 50, 7, 7, 2, 3, 3),      # Co not a multiple of 4, W % 4 != 0
+    workloads.Shape(1, 4, 17, 30, 64, 3, 3, 1, 1, 1),      # stride 1
+    workloads.Shape(1, 10, 9, 13, 60, 3, 4, 1, 0, 2),      # Ci = 10, kH != kW
+    workloads.Shape(1, 2, 11, 14, 57, 5, 8, 2, 4, 1),      # pad > k - 1, kW = 4 * stride
+    workloads.Shape(1, 1, 7, 7, 64, 2, 2, 2, 2, 2),        # kernel = stride, pad = k
+    workloads.Shape(1, 3, 30, 30, 64, 7, 7, 2, 0, 6),      # asymmetric pads
+    workloads.Shape(3, 16, 14, 14, 49, 3, 3, 1, 1, 1),     # 144 columns
+    workloads.Shape(1, 3, 1, 40, 64, 7, 7, 2, 3, 3),       # one image row
+    workloads.Shape(1, 5, 50, 9, 64, 2, 3, 1, 1, 0),       # tall, narrow, even kernel
+    workloads.Shape(300, 3, 8, 8, 64, 3, 3, 1, 1, 1),      # more work-groups than CUs
+    workloads.Shape(2, 1, 30, 31, 64, 1, 1, 1, 0, 0),      # 1 x 1: one column
+    workloads.Shape(1, 6, 19, 21, 64, 5, 5, 2, 2, 2),      # 150 columns: last block partial
+    workloads.Shape(1, 3, 224, 224, 64, 7, 7, 2, 3, 3),    # one stem image at full size
+]
+
+
+@pytest.mark.parametrize("idx", range(len(COL2IM_SHAPES)))
+def test_forced_col2im(idx):
+    s = COL2IM_SHAPES[idx]
+    gi.set_variant(gi.VARIANT_COL2IM)
+    desc = gi.plan(gi.make_params(*s.as_tuple()[:10]), False)
+    gi.set_variant(gi.VARIANT_AUTO)
+    assert "variant=col2im" in desc, desc
+    full_parity(s, 2100 + idx, "f32", gi.VARIANT_COL2IM, dist="normal")
+
+
 # (shape, nb, tile_rows, tile_cols): tiles with ragged row and column tails,
 # tiles wider than the image, rows folded across images, strided phases.
 FORCED_TILES = [

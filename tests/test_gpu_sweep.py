@@ -35,3 +35,14 @@ def device():
 def test_random_sweep(dtype, variant):
     for i, s in enumerate(SHAPES):
         gp.full_parity(s, 30000 + i, dtype, variant, dist="normal")
+
+
+# Output-channel counts the column kernel serves (48 < Co <= 64), the same
+# kind of random shapes otherwise; the shapes it does not serve (more than
+# 160 columns, kW > 4 * stride) fall back to the generic kernel.
+SHAPES_COL2IM = workloads.random_shapes(20241203, 160, co_range=(49, 64))
+
+
+def test_random_sweep_col2im():
+    for i, s in enumerate(SHAPES_COL2IM):
+        gp.full_parity(s, 40000 + i, "f32", gi.VARIANT_COL2IM, dist="normal")

@@ -29,7 +29,8 @@ WORKLOAD_PLANS = {
     "deep_late_stage": ["variant=halo", "cfg=0", "tile=14x14", "HP=30"],
     "strided_downsample": ["variant=halo", "cfg=11 fused", "HP=15"],
     "asym_1x7": ["variant=halo", "cfg=10 split=2", "fold", "HP=23"],
-    "stem_7x7_s2": ["variant=stem", "ws_bytes=0", "tiles=16x7x7x1 whole=768 waves=4 pitch=19"],
+    "stem_7x7_s2": ["variant=col2im", "ws_bytes=0", "tile=56x56 wgs=256 cols=147",
+                    "rows_per_wave=8"],
     "deep_late_stage_bf16": ["variant=halo", "dtype=bf16", "image kernel cfg=0", "nb=13",
                              "wgs=64x4", "pitch=30"],
     "deep_late_stage_f16": ["variant=halo", "dtype=f16", "image kernel cfg=0", "wgs=64x4"],
@@ -179,7 +180,10 @@ def test_planner_invariants(seed):
             desc = gi.plan(p, dt)
             assert desc == gi.plan(p, dt), "plan is not deterministic"
             variant = re.match(r"variant=(\w+) ", desc).group(1)
-            assert variant in ("generic", "halo", "stem"), desc
+            assert variant in ("generic", "halo", "stem", "col2im"), desc
+            if variant == "col2im":
+                assert dt == 0 and s.Ci * s.kH * s.kW <= 160 and 48 < s.Co <= 64, desc
+                assert s.kW <= 4 * s.stride, desc
             assert int(re.search(r"ws_bytes=(\d+)", desc).group(1)) >= 0
             if variant == "stem":
                 assert dt == 0, desc
@@ -229,3 +233,20 @@ def test_fp32_halo_rejects_unserved_tap_counts(shape):
     kernel rather than to a halo plan that would leave the pixels at zero."""
     desc = plan_of(shape)
     assert not desc.startswith("variant=halo"), desc
+
+
+def test_col2im_scope():
+    """The column kernel takes fp32 shapes of at most 160 columns, 48 < Co <=
+    64 and kW <= 4 * stride; the 7x7 stride-2 stem can still be forced onto
+    the 4x4-block kernel."""
+    stem = S(16, 3, 224, 224, 64, 7, 7, 2, 3, 3)
+    assert plan_of(stem).startswith("variant=col2im")
+    assert not plan_of(stem, True).startswith("variant=col2im")
+    for s in [S(16, 3, 224, 224, 48, 7, 7, 2, 3, 3), S(16, 3, 224, 224, 65, 7, 7, 2, 3, 3),
+              S(4, 4, 32, 32, 64, 7, 7, 2, 3, 3), S(4, 3, 32, 32, 64, 3, 5, 1, 1, 2)]:
+        assert not plan_of(s).startswith("variant=col2im"), s
+    old = gi.set_variant(gi.VARIANT_STEM)
+    try:
+        assert plan_of(stem).startswith("variant=stem")
+    finally:
+        gi.set_variant(old)

@@ -84,7 +84,7 @@ def test_read_traffic_checks_plan_and_sources(tmp_path, monkeypatch):
 
 def test_fingerprint_covers_every_kernel():
     seen = {profiling.fingerprint(v, d) for v, d in profiling.KERNEL_SOURCES}
-    assert len(seen) == 6   # generic f32 and bf16 share one source file, so do gw and gwd
+    assert len(seen) == 7   # generic f32 and bf16 share one source file, so do gw and gwd
 
 
 def test_mfma_summary(tmp_path, monkeypatch):

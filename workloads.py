@@ -200,11 +200,11 @@ def sweep_shapes():
     ]
 
 
-def random_shapes(seed: int, count: int):
+def random_shapes(seed: int, count: int, co_range=(1, 48)):
     """`count` seeded random small shapes for sweeps: strides 1-4, kernels
     1-7 per dimension (kH != kW allowed), pads 0..k per dimension, ragged
-    channel counts (a third of them Ci <= 4, a third Ci >= 16), H and W
-    1-24; every shape has oH, oW >= 1."""
+    channel counts (a third of them Ci <= 4, a third Ci >= 16; Co drawn from
+    co_range, both ends included), H and W 1-24; every shape has oH, oW >= 1."""
     rng = np.random.Generator(np.random.PCG64(seed))
     out = []
     while len(out) < count:
@@ -217,6 +217,7 @@ def random_shapes(seed: int, count: int):
         kind = len(out) % 3
         Ci = int(rng.integers(1, 5)) if kind == 0 else (
             int(rng.integers(16, 81)) if kind == 1 else int(rng.integers(5, 16)))
-        out.append(Shape(int(rng.integers(1, 4)), Ci, H, W, int(rng.integers(1, 49)), kH, kW, s,
+        out.append(Shape(int(rng.integers(1, 4)), Ci, H, W,
+                         int(rng.integers(co_range[0], co_range[1] + 1)), kH, kW, s,
                          ph, pw))
     return out
