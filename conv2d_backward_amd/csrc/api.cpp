@@ -638,12 +638,15 @@ bool plan_col2im(const conv2d_gi_params &p, Col2imPlan &out) {
             const int RW = std::max((nq + 3) / 4 + ((nq + 3) / 4 & 1), 2 * ((p.kH + s - 1) / s));
             if (ncq > 16 * gi::kCol2imBlocksPerRow) continue;
             const int ncb = gi::kCol2imBlocksPerRow;
-            const int LR = r0 + TH + p.kH - 1;
-            const int LP = (std::max(c0 + TW + p.kW - 1,
-                                     c0 + 16 * s * gi::kCol2imBlocksPerRow + p.kW) + 15) / 16 * 16;
-            const size_t lds = (((size_t)p.Ci * LR * LP + 64 + 16 * s + 3) / 4 * 4 +
-                                (size_t)gi::kCol2imMaxCo * ncols) * 4;
-            if (lds > kLdsBytes) continue;
+            gi::Col2imArgs t{};
+            t.Ci = p.Ci;
+            t.ncols = ncols;
+            t.LR = r0 + TH + p.kH - 1;
+            gi::col2im_f32_layout(p.kH, p.kW, t.LR,
+                                  std::max(c0 + TW + p.kW - 1,
+                                           c0 + 16 * s * gi::kCol2imBlocksPerRow + p.kW),
+                                  t.LP, t.plane);
+            if (gi::col2im_f32_lds_bytes(t) > kLdsBytes) continue;
             const int64_t wgs = (int64_t)p.N * tiles_r * tiles_c;
             if (wgs > INT32_MAX) continue;
             const double per_wg =
@@ -660,8 +663,9 @@ bool plan_col2im(const conv2d_gi_params &p, Col2imPlan &out) {
                 a.tiles_r = tiles_r;
                 a.tiles_c = tiles_c;
                 a.RW = RW;
-                a.LR = LR;
-                a.LP = LP;
+                a.LR = t.LR;
+                a.LP = t.LP;
+                a.plane = t.plane;
             }
         }
     }
@@ -1292,7 +1296,8 @@ std::string describe(const Plan &plan, int dt) {
         s += " launches=1 [tile=" + std::to_string(a.TH) + "x" + std::to_string(a.TW) +
              " wgs=" + std::to_string((int64_t)a.N * a.tiles_r * a.tiles_c) +
              " cols=" + std::to_string(a.ncols) + " rows_per_wave=" + std::to_string(a.RW) +
-             " lds=" + std::to_string(plan.c2i.lds) + " pitch=" + std::to_string(a.LP) + "]";
+             " lds=" + std::to_string(plan.c2i.lds) + " pitch=" + std::to_string(a.LP) +
+             " plane=" + std::to_string(a.plane) + "]";
         return s;
     }
     if (plan.variant == CONV2D_GI_VARIANT_STEM) {

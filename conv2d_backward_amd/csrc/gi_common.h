@@ -251,6 +251,7 @@ struct Col2imArgs {
     int32_t tiles_r, tiles_c;  // grid = N * tiles_r * tiles_c (1-D, xcd_order)
     int32_t RW;             // grad_out rows per wave and tile; stride * RW >= kH
     int32_t LR, LP;         // LDS tile rows and row pitch (floats), per input channel
+    int32_t plane;          // LDS floats per input channel (>= LR * LP)
     int32_t r0, c0;         // LDS row and column of tile pixel (0, 0)
     int32_t wofs;           // LDS float offset of the staged weight
 };

@@ -118,6 +118,17 @@ constexpr int kCol2imMinCo = 48;
 constexpr int kCol2imMaxCo = 64;
 constexpr int kCol2imMaxStride = 2;
 constexpr int kCol2imBlocksPerRow = 2;
+// Row pitch and channel plane of the column kernel's LDS tile: the least
+// pitch >= min_pitch with pitch = kW (mod 32), and the least plane >=
+// LR * pitch with plane = kH * kW (mod 32).  Column (ci, kh, kw), at
+// ci * plane + kh * pitch + kw, then sits on LDS bank (its column index) plus
+// a per-lane constant, mod 32, which the kernel's assignment of columns to
+// blocks and of positions to lanes makes conflict-free.
+inline void col2im_f32_layout(int kH, int kW, int LR, int min_pitch, int &pitch, int &plane) {
+    pitch = min_pitch + ((kW - min_pitch) % 32 + 32) % 32;
+    const int base = LR * pitch;
+    plane = base + ((kH * kW - base) % 32 + 32) % 32;
+}
 int col2im_f32_weight_offset(const Col2imArgs &a);
 size_t col2im_f32_lds_bytes(const Col2imArgs &a);
 hipError_t launch_col2im_f32(const Col2imArgs &a, hipStream_t s, const KernelEvents &ev);

@@ -36,11 +36,22 @@
 // no vector ALU work, which on one wave per SIMD would hold up the matrix
 // cores.  That needs the 64 pixels x 16 columns of a block to be distinct
 // pixels, so a block's 16 positions are spread out: 8 positions 4 apart of
-// grad_out row k and the same 8 columns of row k + RW/2 (4*stride >= kW and
-// (RW/2)*stride >= kH, so no two of them feed a common pixel).  Lane l =
-// 16g + i: A row i is position i (row k for i < 8), D row 4g + r position
-// 4g + r.  A pair of rows takes 4 such blocks (column classes 0..3, 32
-// positions of each row).
+// grad_out row k (slots u = 0..7, column 4u + class) and the same 8 columns
+// of row k + RW/2 (4*stride >= kW and (RW/2)*stride >= kH, so no two of
+// them feed a common pixel).  D row 4g + r (lane group g, register r) is
+// row k + RW/2 for g >= 2 and slot 4 (g & 1) + r at stride 1, (g & 1) + 2r
+// at stride 2; lane i loads the position of D row i as its A row.  A pair of
+// rows takes 4 such blocks (column classes 0..3, 32 positions of each row).
+//
+// LDS banks (64 of 4 bytes; a single-word read serves 32 lanes a cycle and
+// needs their words distinct mod 32, a write serves 16): the tile's pitch and
+// channel plane (kW and kH * kW mod 32) put column (ci, kh, kw) on bank
+// (column index) + a per-lane constant, mod 32.  At stride 1 a block holds 16 consecutive
+// columns and lane groups 0 and 1 are 16 words apart; at stride 2 they are 8
+// apart and a pair of blocks splits 32 consecutive columns into alternate
+// runs of 8.  Either way the 32 lanes of a half wave hit 32 distinct banks
+// in every fold read and write.  Columns of one (ci, kh) still lie in one
+// block or two adjacent ones.
 //
 // Order: between two blocks of a pair the last k step of one and the first
 // of the next run back to back, with the first block's writes issued two
@@ -88,6 +99,8 @@ __global__ __launch_bounds__(256, 1) void gi_col2im_f32(const Col2imArgs A) {
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, i = lane & 15;
+    // Position slots between a lane group's registers r and r + 1.
+    constexpr int DELTA = S == 2 ? 2 : 1;
 
     // Logical order: tile column fastest, then tile row, image.
     int bid = xcd_order(blockIdx.x, gridDim.x);
@@ -110,12 +123,13 @@ __global__ __launch_bounds__(256, 1) void gi_col2im_f32(const Col2imArgs A) {
     const __amdgpu_buffer_rsrc_t wrs = make_rsrc(A.w, A.w_bytes);
     const __amdgpu_buffer_rsrc_t drs = make_rsrc(A.dst, A.d_bytes);
 
-    // LDS: the tile [Ci][LR][LP], one slot per lane (plus the fold's
-    // position and class offsets) for columns past the last, then the
-    // weight staged as [kCol2imMaxCo][ncols] (rows past Co zero).
-    const int plane = A.LR * A.LP;
+    // LDS: the tile [Ci][plane] (rows of LP floats), 32 slots (plus the
+    // fold's position and class offsets) on 32 banks for columns past the
+    // last and missing rows, then the weight staged as [kCol2imMaxCo][ncols]
+    // (rows past Co zero).
+    const int plane = A.plane;
     const int tfl = A.Ci * plane;
-    const int dummy = tfl + lane;
+    const int dbase = (tfl + 31) / 32 * 32;
     float *const wst = tile + A.wofs;
     for (int k = tid * 4; k < tfl; k += 1024) *(v4f *)(tile + k) = v4f{0.f, 0.f, 0.f, 0.f};
     {
@@ -138,7 +152,8 @@ __global__ __launch_bounds__(256, 1) void gi_col2im_f32(const Col2imArgs A) {
     const int oHW = A.oH * A.oW;
     const int csteps = (A.Co + 3) / 4;
     const int RWh = A.RW / 2;
-    const int owl = ow_lo + 4 * (i & 7);  // this lane's position column, class 0
+    // This lane's position column (class 0): D row i's slot.
+    const int owl = ow_lo + 4 * (DELTA == 1 ? (i & 7) : ((i >> 2) & 1) + 2 * (i & 3));
     auto pair_vo = [&](int k) {
         const int row = k + (i >= 8 ? RWh : 0);
         return row < rows_w ? (((n * A.Co + g) * A.oH + row0 + row) * A.oW + owl) * 4 : kOOB;
@@ -151,14 +166,16 @@ __global__ __launch_bounds__(256, 1) void gi_col2im_f32(const Col2imArgs A) {
     // csteps, 4c < Co, so what is left after the base is advanced is at
     // least one output channel's plane (a wrapped range would let the kOOB
     // offset through to memory past the buffer).
+    const uint32_t step_bytes = 16u * (uint32_t)oHW;  // 4 output channels
     auto gload1 = [&](int c, int vo, int cls, float &x) {
-        // (Formed afresh at each use: holding all 16 descriptors would not
-        // fit the scalar registers.)
-        const float *pc = A.grad_out + (size_t)c * 4 * oHW;
-        const uint32_t used = (uint32_t)c * 16 * oHW;
-        uint32_t nc = A.g_bytes - used;
-        asm volatile("" : "+s"(pc), "+s"(nc));
-        const __amdgpu_buffer_rsrc_t rc = make_rsrc(pc, nc);
+        // (Formed afresh at each use from values the compiler cannot see
+        // through: holding all 16 descriptors would not fit the scalar
+        // registers.)
+        const char *pg = (const char *)A.grad_out;
+        uint32_t gb = A.g_bytes, sb = step_bytes;
+        asm volatile("" : "+s"(pg), "+s"(gb), "+s"(sb));
+        const uint32_t used = (uint32_t)c * sb;
+        const __amdgpu_buffer_rsrc_t rc = make_rsrc(pg + used, gb - used);
         if (CO == 64 || c < csteps)
             x = load_f32s(rc, CO != 0 || 4 * c + g < A.Co ? vo + 4 * cls : kOOB, 0);
     };
@@ -174,13 +191,20 @@ __global__ __launch_bounds__(256, 1) void gi_col2im_f32(const Col2imArgs A) {
     }
     __syncthreads();  // the tile is zero and the weight staged
 
+    // Column of lane i in block nb: at stride 2, blocks 2q and 2q + 1 take
+    // the alternate runs of 8 of columns 32q .. 32q + 31 (a last unpaired
+    // block takes 16 consecutive ones).
+    auto column = [&](int nb) {
+        if (S == 2 && nb < (NBN & ~1)) return 32 * (nb >> 1) + 8 * (nb & 1) + (i & 7) + 16 * (i >> 3);
+        return 16 * nb + i;
+    };
     // B fragments of every k step and column block.
     float wv[kSteps][NBN];
 #pragma unroll
     for (int c = 0; c < kSteps; ++c)
 #pragma unroll
         for (int nb = 0; nb < NBN; ++nb) {
-            const int col = 16 * nb + i;
+            const int col = column(nb);
             const float x = wst[(4 * c + g) * A.ncols + (col < A.ncols ? col : 0)];
             wv[c][nb] = col < A.ncols ? x : 0.f;
             // Held in the accumulator file (the MFMAs read them from there),
@@ -188,46 +212,50 @@ __global__ __launch_bounds__(256, 1) void gi_col2im_f32(const Col2imArgs A) {
             asm volatile("" : "+a"(wv[c][nb]));
         }
 
-    // Tile offset of this lane's column 16nb + i relative to its position's
-    // first pixel: channel plane, kh rows, kw columns.
+    // Tile offset of this lane's column in block nb relative to its
+    // position's first pixel: channel plane, kh rows, kw columns (the same
+    // arithmetic past the last column gives the bank its slot takes).
     const int khw = A.kH * A.kW;
     int cbase[NBN];
+    unsigned colok = 0;
 #pragma unroll
     for (int nb = 0; nb < NBN; ++nb) {
-        const int col = 16 * nb + i;
+        const int col = column(nb);
         const int ci = col / khw, rem = col - (col / khw) * khw;
         const int kh = rem / A.kW, kw = rem - (rem / A.kW) * A.kW;
         cbase[nb] = ci * plane + kh * A.LP + kw;
+        if (col < A.ncols) colok |= 1u << nb;
     }
-    const bool last_ok = 16 * (NBN - 1) + i < A.ncols;
 
-    // Fold byte addresses of the pair of rows (k, k + RW/2), class 0, r = 0:
-    // D row 4g + r is position 4 (4 (g & 1) + r) + class of row k + RW/2
-    // (g >= 2); r and the class are immediate offsets (4 S r + S class
-    // floats).  Columns past the last and a missing second row go to the
-    // lane's own slot past the tile.
+    // Fold byte addresses of the pair of rows (k, k + RW/2), class 0, r = 0
+    // (D row 4g + r: row k + RW/2 for g >= 2, slot u0 + DELTA r); r and the
+    // class are immediate offsets (4 DELTA S r + S class floats).  Columns
+    // past the last and a missing second row go to the slot past the tile
+    // on the bank the real address would take.
     int ad[NBN];
     auto pair_addr = [&](int k) {
         const bool hi = g >= 2;
         const bool rv = !hi || k + RWh < rows_w;
+        const int u0 = DELTA == 1 ? 4 * (g & 1) : (g & 1);
         const int qoff = (S * (row0 + k + (hi ? RWh : 0)) - A.pad_h - ih0 + A.r0) * A.LP +
-                         S * (ow_lo + 16 * (g & 1)) - A.pad_w - iw0 + A.c0;
+                         S * (ow_lo + 4 * u0) - A.pad_w - iw0 + A.c0;
 #pragma unroll
         for (int nb = 0; nb < NBN; ++nb) {
-            const bool ok = rv && (nb < NBN - 1 || last_ok);
-            ad[nb] = (ok ? cbase[nb] + qoff : dummy) * 4;
+            const int real = cbase[nb] + qoff;
+            ad[nb] = (rv && (colok >> nb & 1u) ? real : dbase + (real & 31)) * 4;
         }
     };
     // Tile reads and writes of column block nb for class cls, r = 0..3.
     auto tread = [&](int nb, int cls, v4f(&acc)[NBN]) {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            acc[nb][r] = *(const float *)((const char *)tile + ad[nb] + (4 * S * r + S * cls) * 4);
+            acc[nb][r] = *(const float *)((const char *)tile + ad[nb] +
+                                          (4 * DELTA * S * r + S * cls) * 4);
     };
     auto twrite = [&](int nb, int cls, const v4f(&acc)[NBN]) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            *(float *)((char *)tile + ad[nb] + (4 * S * r + S * cls) * 4) = acc[nb][r];
+            *(float *)((char *)tile + ad[nb] + (4 * DELTA * S * r + S * cls) * 4) = acc[nb][r];
             asm volatile("" ::: "memory");  // single-word writes, straight from the accumulators
         }
     };
@@ -311,7 +339,8 @@ __global__ __launch_bounds__(256, 1) void gi_col2im_f32(const Col2imArgs A) {
     }
 
     // Epilogue: the tile's pixels inside the image, 16 bytes per lane where
-    // rows are whole quads (lanes: 16 quads of a row, 16 rows at a time).
+    // rows are whole quads (lanes: 16 quads of a row, 16 rows at a time; the
+    // LDS rows need not be 16-byte aligned, so four single-word reads).
     const int H = A.H, W = A.W;
     if ((W & 3) == 0 && (A.TW & 3) == 0) {
         const int qr = A.TW / 4;
@@ -319,8 +348,8 @@ __global__ __launch_bounds__(256, 1) void gi_col2im_f32(const Col2imArgs A) {
             for (int ci = 0; ci < A.Ci; ++ci)
                 for (int row = tid >> 4; row < A.TH; row += 16) {
                     const int ih = ih0 + row, iw = iw0 + 4 * qc;
-                    const v4f v =
-                        *(const v4f *)(tile + ci * plane + (A.r0 + row) * A.LP + A.c0 + 4 * qc);
+                    const float *t = tile + ci * plane + (A.r0 + row) * A.LP + A.c0 + 4 * qc;
+                    const v4f v = v4f{t[0], t[1], t[2], t[3]};
                     const int off =
                         (ih < H && iw < W) ? (((n * A.Ci + ci) * H + ih) * W + iw) * 4 : kOOB;
                     __builtin_amdgcn_raw_buffer_store_b128(
@@ -348,9 +377,10 @@ constexpr size_t kOnePerCuLds = 80 * 1024 + 256;
 }  // namespace
 
 int col2im_f32_weight_offset(const Col2imArgs &a) {
-    // The tile, then one slot per lane (plus the fold's position and class offsets)
-    // for columns past the last; the weight stage starts 16-byte aligned.
-    return (a.Ci * a.LR * a.LP + 64 + 16 * a.stride + 3) / 4 * 4;
+    // The tile, then 32 slots on 32 banks plus the fold's largest immediate
+    // offset (4 DELTA S * 3 + S * 3 <= 54 floats) for columns past the last;
+    // the weight stage starts 16-byte aligned.
+    return (a.Ci * a.plane + 31) / 32 * 32 + 96;
 }
 
 size_t col2im_f32_lds_bytes(const Col2imArgs &a) {
@@ -404,9 +434,9 @@ hipError_t launch_col2im_f32(const Col2imArgs &a, hipStream_t s, const KernelEve
     // Border and alignment of the LDS tile; its row pitch holds the pixels of
     // every position of a row's blocks (those past the tile's positions fold
     // zeros into the border).
-    if (a.r0 < a.kH - 1 || a.LR < a.r0 + a.TH + a.kH - 1 || a.c0 < a.kW - 1 || (a.c0 & 3) ||
-        (a.LP & 3) || a.LP < a.c0 + 16 * a.stride * kCol2imBlocksPerRow + a.kW ||
-        a.LP < a.c0 + a.TW + a.kW - 1)
+    if (a.r0 < a.kH - 1 || a.LR < a.r0 + a.TH + a.kH - 1 || a.c0 < a.kW - 1 ||
+        a.LP < a.c0 + 16 * a.stride * kCol2imBlocksPerRow + a.kW ||
+        a.LP < a.c0 + a.TW + a.kW - 1 || a.plane < a.LR * a.LP)
         return hipErrorInvalidValue;
     if ((int64_t)a.tiles_r * a.TH < a.H || (int64_t)a.tiles_c * a.TW < a.W)
         return hipErrorInvalidValue;
