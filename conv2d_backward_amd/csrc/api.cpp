@@ -641,6 +641,8 @@ bool plan_col2im(const conv2d_gi_params &p, Col2imPlan &out) {
             gi::Col2imArgs t{};
             t.Ci = p.Ci;
             t.ncols = ncols;
+            t.stride = s;
+            t.ws = gi::col2im_f32_stage_stride(ncols, s);
             t.LR = r0 + TH + p.kH - 1;
             gi::col2im_f32_layout(p.kH, p.kW, t.LR,
                                   std::max(c0 + TW + p.kW - 1,
@@ -689,6 +691,9 @@ bool plan_col2im(const conv2d_gi_params &p, Col2imPlan &out) {
     a.ncols = ncols;
     a.r0 = r0;
     a.c0 = c0;
+    a.ws = gi::col2im_f32_stage_stride(ncols, p.stride);
+    a.magic_khw = gi::col2im_magic16(p.kH * p.kW);
+    a.magic_kw = gi::col2im_magic16(p.kW);
     a.wofs = gi::col2im_f32_weight_offset(a);
     out.lds = gi::col2im_f32_lds_bytes(a);
     return true;
@@ -1297,7 +1302,7 @@ std::string describe(const Plan &plan, int dt) {
              " wgs=" + std::to_string((int64_t)a.N * a.tiles_r * a.tiles_c) +
              " cols=" + std::to_string(a.ncols) + " rows_per_wave=" + std::to_string(a.RW) +
              " lds=" + std::to_string(plan.c2i.lds) + " pitch=" + std::to_string(a.LP) +
-             " plane=" + std::to_string(a.plane) + "]";
+             " plane=" + std::to_string(a.plane) + " stage=" + std::to_string(a.ws) + "]";
         return s;
     }
     if (plan.variant == CONV2D_GI_VARIANT_STEM) {

@@ -254,6 +254,8 @@ struct Col2imArgs {
     int32_t plane;          // LDS floats per input channel (>= LR * LP)
     int32_t r0, c0;         // LDS row and column of tile pixel (0, 0)
     int32_t wofs;           // LDS float offset of the staged weight
+    int32_t ws;             // staged weight row stride (floats), >= 16 * column blocks
+    uint32_t magic_khw, magic_kw;  // ceil(2^16 / (kH * kW)), ceil(2^16 / kW)
 };
 
 }  // namespace gi

@@ -129,6 +129,16 @@ inline void col2im_f32_layout(int kH, int kW, int LR, int min_pitch, int &pitch,
     const int base = LR * pitch;
     plane = base + ((kH * kW - base) % 32 + 32) % 32;
 }
+// Row stride of the column kernel's staged weight: at least 16 * (column
+// blocks), and 8 (stride 2) or 16 (stride 1) mod 32, so that a B-fragment
+// read (lane groups one weight row apart) meets 32 distinct banks per half
+// wave for the kernel's columns of a block.
+inline int col2im_f32_stage_stride(int ncols, int stride) {
+    const int need = (ncols + 15) / 16 * 16, want = stride == 2 ? 8 : 16;
+    return need + ((want - need) % 32 + 32) % 32;
+}
+// ceil(2^16 / d): for 0 <= x < 256 and 1 <= d < 256, (x * m) >> 16 = x / d.
+inline uint32_t col2im_magic16(int d) { return (65536u + (uint32_t)d - 1u) / (uint32_t)d; }
 int col2im_f32_weight_offset(const Col2imArgs &a);
 size_t col2im_f32_lds_bytes(const Col2imArgs &a);
 hipError_t launch_col2im_f32(const Col2imArgs &a, hipStream_t s, const KernelEvents &ev);

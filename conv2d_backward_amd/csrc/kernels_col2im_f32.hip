@@ -125,22 +125,36 @@ __global__ __launch_bounds__(256, 1) void gi_col2im_f32(const Col2imArgs A) {
 
     // LDS: the tile [Ci][plane] (rows of LP floats), 32 slots (plus the
     // fold's position and class offsets) on 32 banks for columns past the
-    // last and missing rows, then the weight staged as [kCol2imMaxCo][ncols]
-    // (rows past Co zero).
+    // last and missing rows, then the weight staged as [kCol2imMaxCo][ws]
+    // (rows past Co and columns past ncols zero).
     const int plane = A.plane;
     const int tfl = A.Ci * plane;
     const int dbase = (tfl + 31) / 32 * 32;
     float *const wst = tile + A.wofs;
+    // Weight rows: four lanes per row of output channel co = tid / 4, 16
+    // bytes each at columns j = 4 (tid mod 4) + 16 m, all loads issued
+    // before the tile is cleared.  Buffer loads need 4-byte alignment only;
+    // words of a quad past ncols (the next row's) are replaced by zeros.
+    // (Columns j < 16 NBN: every column block's; pass m covers 16.)
+    const int sco = tid >> 2, sj = 4 * (tid & 3);
+    v4f wq[NBN];
+#pragma unroll
+    for (int m = 0; m < NBN; ++m) {
+        const int j = sj + 16 * m;
+        wq[m] = v4f{0.f, 0.f, 0.f, 0.f};
+        if (sco < A.Co && j < A.ncols)
+            wq[m] = __builtin_bit_cast(
+                v4f, __builtin_amdgcn_raw_buffer_load_b128(wrs, (sco * A.ncols + j) * 4, 0, 0));
+    }
     for (int k = tid * 4; k < tfl; k += 1024) *(v4f *)(tile + k) = v4f{0.f, 0.f, 0.f, 0.f};
-    {
-        const int wreal = A.Co * A.ncols, wall = kCol2imMaxCo * A.ncols;
-        // 16 bytes per lane; the words past the weight's end read zero.
-        for (int e = tid * 4; e < wall; e += 1024) {
-            v4f v = v4f{0.f, 0.f, 0.f, 0.f};
-            if (e < wreal)
-                v = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(wrs, e * 4, 0, 0));
-            *(v4f *)(wst + e) = v;
-        }
+#pragma unroll
+    for (int m = 0; m < NBN; ++m) {
+        const int j = sj + 16 * m;
+        v4f v = wq[m];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (j + e >= A.ncols) v[e] = 0.f;
+        *(v4f *)(wst + sco * A.ws + j) = v;
     }
 
     // grad_out of a block: lane i loads position i (row k of the pair for i
@@ -198,19 +212,13 @@ __global__ __launch_bounds__(256, 1) void gi_col2im_f32(const Col2imArgs A) {
         if (S == 2 && nb < (NBN & ~1)) return 32 * (nb >> 1) + 8 * (nb & 1) + (i & 7) + 16 * (i >> 3);
         return 16 * nb + i;
     };
-    // B fragments of every k step and column block.
+    // B fragments of every k step and column block (zero past Co and
+    // ncols, as staged).
     float wv[kSteps][NBN];
 #pragma unroll
     for (int c = 0; c < kSteps; ++c)
 #pragma unroll
-        for (int nb = 0; nb < NBN; ++nb) {
-            const int col = column(nb);
-            const float x = wst[(4 * c + g) * A.ncols + (col < A.ncols ? col : 0)];
-            wv[c][nb] = col < A.ncols ? x : 0.f;
-            // Held in the accumulator file (the MFMAs read them from there),
-            // leaving the vector registers to the operands and addresses.
-            asm volatile("" : "+a"(wv[c][nb]));
-        }
+        for (int nb = 0; nb < NBN; ++nb) wv[c][nb] = wst[(4 * c + g) * A.ws + column(nb)];
 
     // Tile offset of this lane's column in block nb relative to its
     // position's first pixel: channel plane, kh rows, kw columns (the same
@@ -220,9 +228,10 @@ __global__ __launch_bounds__(256, 1) void gi_col2im_f32(const Col2imArgs A) {
     unsigned colok = 0;
 #pragma unroll
     for (int nb = 0; nb < NBN; ++nb) {
+        // (x * ceil(2^16 / d)) >> 16 = x / d for x, d < 256.
         const int col = column(nb);
-        const int ci = col / khw, rem = col - (col / khw) * khw;
-        const int kh = rem / A.kW, kw = rem - (rem / A.kW) * A.kW;
+        const int ci = (int)(((uint32_t)col * A.magic_khw) >> 16), rem = col - ci * khw;
+        const int kh = (int)(((uint32_t)rem * A.magic_kw) >> 16), kw = rem - kh * A.kW;
         cbase[nb] = ci * plane + kh * A.LP + kw;
         if (col < A.ncols) colok |= 1u << nb;
     }
@@ -385,7 +394,7 @@ int col2im_f32_weight_offset(const Col2imArgs &a) {
 
 size_t col2im_f32_lds_bytes(const Col2imArgs &a) {
     const size_t bytes =
-        ((size_t)col2im_f32_weight_offset(a) + (size_t)kCol2imMaxCo * a.ncols) * sizeof(float);
+        ((size_t)col2im_f32_weight_offset(a) + (size_t)kCol2imMaxCo * a.ws) * sizeof(float);
     return bytes > kOnePerCuLds ? bytes : kOnePerCuLds;
 }
 
@@ -430,6 +439,11 @@ hipError_t launch_col2im_f32(const Col2imArgs &a, hipStream_t s, const KernelEve
     if ((a.RW & 1) || a.RW / 2 < D || 4 * a.RW < (a.TH + a.kH - 2) / a.stride + 1)
         return hipErrorInvalidValue;
     if (a.wofs != col2im_f32_weight_offset(a)) return hipErrorInvalidValue;
+    // Staged weight rows hold every column block; the divisions by
+    // reciprocal are exact for the column indices (< 256) and divisors.
+    if (a.ws < 16 * nbn || (a.ws & 3) || a.kH * a.kW > 255 ||
+        a.magic_khw != col2im_magic16(a.kH * a.kW) || a.magic_kw != col2im_magic16(a.kW))
+        return hipErrorInvalidValue;
     if ((a.TW + a.kW - 2) / a.stride + 1 > 16 * kCol2imBlocksPerRow) return hipErrorInvalidValue;
     // Border and alignment of the LDS tile; its row pitch holds the pixels of
     // every position of a row's blocks (those past the tile's positions fold

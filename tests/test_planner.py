@@ -1,6 +1,8 @@
 """Host-only checks of the planner (no GPU): the graded workloads get the
 compile-time kernel instances documented for them, forced tiles reach each
 compile-time instance, and forced tiles are validated."""
+import re
+
 import pytest
 
 import conv2d_backward_amd as gi
@@ -250,3 +252,37 @@ def test_col2im_scope():
         assert plan_of(stem).startswith("variant=stem")
     finally:
         gi.set_variant(old)
+
+
+def test_col2im_reciprocal_division_exact():
+    """The column kernel splits a column index into (ci, kh, kw) as
+    (x * ceil(2^16 / d)) >> 16: exact for every x, d below 256 (the error
+    x * (ceil(2^16/d) - 2^16/d) / 2^16 < x / 2^16 < 1/256 <= 1/d stays under
+    the distance from x/d to the next integer)."""
+    import numpy as np
+    x = np.arange(256, dtype=np.int64)
+    for d in range(1, 256):
+        m = (65536 + d - 1) // d
+        assert np.array_equal((x * m) >> 16, x // d), d
+    # outside that range the shortcut does fail (the bound is needed)
+    xs = np.arange(1 << 15, dtype=np.int64)
+    assert (((xs * ((65536 + 299) // 300)) >> 16) != xs // 300).any()
+
+
+def test_col2im_bank_layout():
+    """Column-kernel plans: tile pitch = kW and channel plane = kH*kW (mod 32),
+    so a column's LDS bank is its index plus a per-lane constant; the staged
+    weight's row stride covers every column block and is 8 (stride 2) or
+    16 (stride 1) mod 32."""
+    import workloads as wl
+    seen = 0
+    for s in wl.random_shapes(20241203, 160, co_range=(49, 64)) + [S(16, 3, 224, 224, 64, 7, 7, 2, 3, 3)]:
+        txt = plan_of(s)
+        if not txt.startswith("variant=col2im"):
+            continue
+        seen += 1
+        f = dict(re.findall(r"\b(pitch|plane|stage|cols)=(\d+)", txt))
+        lp, plane, ws, ncols = (int(f[k]) for k in ("pitch", "plane", "stage", "cols"))
+        assert (lp - s.kW) % 32 == 0 and (plane - s.kH * s.kW) % 32 == 0, txt
+        assert ws >= 16 * ((ncols + 15) // 16) and ws % 32 == (8 if s.stride == 2 else 16), txt
+    assert seen >= 10
