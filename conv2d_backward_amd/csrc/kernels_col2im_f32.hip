@@ -131,10 +131,44 @@ __global__ __launch_bounds__(256, 1) void gi_col2im_f32(const Col2imArgs A) {
     const int tfl = A.Ci * plane;
     const int dbase = (tfl + 31) / 32 * 32;
     float *const wst = tile + A.wofs;
+    // grad_out of a block: lane i loads the position of D row i (row k of
+    // the pair for i < 8, row k + RW/2 for i >= 8), output channel 4c + g at
+    // byte offset vo (the pair and the lane) + 4 class + c * 16 * oH * oW
+    // (uniform); zeros past the wave's rows, the tile's positions or Co.
+    // Steps wholly past Co are not loaded; with CO = 0 the channels of the
+    // last step past Co take the kOOB offset.
+    const int oHW = A.oH * A.oW;
+    const int csteps = (A.Co + 3) / 4;
+    const int RWh = A.RW / 2;
+    // This lane's position column (class 0): D row i's slot.
+    const int owl = ow_lo + 4 * (DELTA == 1 ? (i & 7) : ((i >> 2) & 1) + 2 * (i & 3));
+    auto pair_vo = [&](int k) {
+        const int row = k + (i >= 8 ? RWh : 0);
+        return row < rows_w ? (((n * A.Co + g) * A.oH + row0 + row) * A.oW + owl) * 4 : kOOB;
+    };
+    // k step c reads through one descriptor over all of grad_out with the
+    // step's 4 output channels (c * 16 * oH * oW bytes) as the load's scalar
+    // offset; the class is part of the lane offset.  Steps wholly past Co are
+    // never loaded (their weights are zero and x keeps its zero).  A lane
+    // offset of kOOB is past the range whether or not the range check counts
+    // the scalar offset (kOOB plus any step offset stays below 2^32).
+    const __amdgpu_buffer_rsrc_t grs = make_rsrc(A.grad_out, A.g_bytes);
+    const uint32_t step_bytes = 16u * (uint32_t)oHW;  // 4 output channels
+    auto gload1 = [&](int c, int vo, int cls, float &x) {
+        if (CO != 64 && c >= csteps) return;
+        const int lo = CO != 0 || 4 * c + g < A.Co ? vo + 4 * cls : kOOB;
+        x = load_f32s(grs, lo, (int)((uint32_t)c * step_bytes));
+    };
+    // The lane's load offset for class cls (kOOB past the tile's positions).
+    auto class_vo = [&](int vo, int cls) { return owl + cls <= ow_hi ? vo : kOOB; };
+    float gA[kSteps], gB[kSteps];
+#pragma unroll
+    for (int c = 0; c < kSteps; ++c) gA[c] = gB[c] = 0.f;
     // Weight rows: four lanes per row of output channel co = tid / 4, 16
-    // bytes each at columns j = 4 (tid mod 4) + 16 m, all loads issued
-    // before the tile is cleared.  Buffer loads need 4-byte alignment only;
-    // words of a quad past ncols (the next row's) are replaced by zeros.
+    // bytes each at columns j = 4 (tid mod 4) + 16 m; these loads and the
+    // first block's grad_out are issued before the tile is cleared.  Buffer
+    // loads need 4-byte alignment only; words of a quad past ncols (the next
+    // row's) are replaced by zeros.
     // (Columns j < 16 NBN: every column block's; pass m covers 16.)
     const int sco = tid >> 2, sj = 4 * (tid & 3);
     v4f wq[NBN];
@@ -145,6 +179,11 @@ __global__ __launch_bounds__(256, 1) void gi_col2im_f32(const Col2imArgs A) {
         if (sco < A.Co && j < A.ncols)
             wq[m] = __builtin_bit_cast(
                 v4f, __builtin_amdgcn_raw_buffer_load_b128(wrs, (sco * A.ncols + j) * 4, 0, 0));
+    }
+    {
+        const int vo = class_vo(pair_vo(0), 0);
+#pragma unroll
+        for (int c = 0; c < kSteps; ++c) gload1(c, vo, 0, gA[c]);
     }
     for (int k = tid * 4; k < tfl; k += 1024) *(v4f *)(tile + k) = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -157,52 +196,6 @@ __global__ __launch_bounds__(256, 1) void gi_col2im_f32(const Col2imArgs A) {
         *(v4f *)(wst + sco * A.ws + j) = v;
     }
 
-    // grad_out of a block: lane i loads position i (row k of the pair for i
-    // < 8, row k + RW/2 for i >= 8; column ow_lo + 4 (i mod 8) + class),
-    // output channel 4c + g at byte offset vo (the pair and the lane) +
-    // 4 class + c * 16 * oH * oW (uniform); zeros past the wave's rows, the
-    // tile's positions or Co.  Steps wholly past Co are not loaded; with
-    // CO = 0 the channels of the last step past Co take the kOOB offset.
-    const int oHW = A.oH * A.oW;
-    const int csteps = (A.Co + 3) / 4;
-    const int RWh = A.RW / 2;
-    // This lane's position column (class 0): D row i's slot.
-    const int owl = ow_lo + 4 * (DELTA == 1 ? (i & 7) : ((i >> 2) & 1) + 2 * (i & 3));
-    auto pair_vo = [&](int k) {
-        const int row = k + (i >= 8 ? RWh : 0);
-        return row < rows_w ? (((n * A.Co + g) * A.oH + row0 + row) * A.oW + owl) * 4 : kOOB;
-    };
-    // k step c reads through a descriptor whose base is advanced to output
-    // channel 4c (scalar arithmetic; its range is the rest of grad_out), and
-    // the class is the load's immediate offset.
-    // Steps wholly past Co are never loaded (their weights are zero and x
-    // keeps its zero).  That also keeps the range from wrapping: below
-    // csteps, 4c < Co, so what is left after the base is advanced is at
-    // least one output channel's plane (a wrapped range would let the kOOB
-    // offset through to memory past the buffer).
-    const uint32_t step_bytes = 16u * (uint32_t)oHW;  // 4 output channels
-    auto gload1 = [&](int c, int vo, int cls, float &x) {
-        // (Formed afresh at each use from values the compiler cannot see
-        // through: holding all 16 descriptors would not fit the scalar
-        // registers.)
-        const char *pg = (const char *)A.grad_out;
-        uint32_t gb = A.g_bytes, sb = step_bytes;
-        asm volatile("" : "+s"(pg), "+s"(gb), "+s"(sb));
-        const uint32_t used = (uint32_t)c * sb;
-        const __amdgpu_buffer_rsrc_t rc = make_rsrc(pg + used, gb - used);
-        if (CO == 64 || c < csteps)
-            x = load_f32s(rc, CO != 0 || 4 * c + g < A.Co ? vo + 4 * cls : kOOB, 0);
-    };
-    // The lane's load offset for class cls (kOOB past the tile's positions).
-    auto class_vo = [&](int vo, int cls) { return owl + cls <= ow_hi ? vo : kOOB; };
-    float gA[kSteps], gB[kSteps];
-#pragma unroll
-    for (int c = 0; c < kSteps; ++c) gA[c] = gB[c] = 0.f;
-    {
-        const int vo = class_vo(pair_vo(0), 0);
-#pragma unroll
-        for (int c = 0; c < kSteps; ++c) gload1(c, vo, 0, gA[c]);
-    }
     __syncthreads();  // the tile is zero and the weight staged
 
     // Column of lane i in block nb: at stride 2, blocks 2q and 2q + 1 take
