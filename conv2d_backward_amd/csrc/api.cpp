@@ -598,6 +598,8 @@ bool plan_img16(const conv2d_gi_params &p, Img16Plan &out) {
     a.nchunks = nchunks;
     a.ci_tiles = ci_tiles;
     a.nq = oHW / 4;
+    a.rcp_w = gi::recip16(p.W);
+    a.rcp_ow = gi::recip16(p.oW);
     out.cfg = cfg;
     out.lds = lds;
     out.wk_bytes = (size_t)wk;
@@ -692,8 +694,8 @@ bool plan_col2im(const conv2d_gi_params &p, Col2imPlan &out) {
     a.r0 = r0;
     a.c0 = c0;
     a.ws = gi::col2im_f32_stage_stride(ncols, p.stride);
-    a.magic_khw = gi::col2im_magic16(p.kH * p.kW);
-    a.magic_kw = gi::col2im_magic16(p.kW);
+    a.magic_khw = gi::recip16(p.kH * p.kW);
+    a.magic_kw = gi::recip16(p.kW);
     a.wofs = gi::col2im_f32_weight_offset(a);
     out.lds = gi::col2im_f32_lds_bytes(a);
     return true;

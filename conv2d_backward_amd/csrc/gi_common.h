@@ -223,6 +223,7 @@ struct Img16Args {
     int32_t nchunks;        // ceil(Co / 32)
     int32_t ci_tiles;       // ceil(Ci / 128); grid = N * ci_tiles (1-D, xcd_order)
     int32_t nq;             // 4-pixel quads of one grad_out plane: oH * oW / 4
+    uint32_t rcp_w, rcp_ow;  // ceil(2^16 / W), ceil(2^16 / oW): pixel index -> row
 };
 
 }  // namespace gi

@@ -137,8 +137,10 @@ inline int col2im_f32_stage_stride(int ncols, int stride) {
     const int need = (ncols + 15) / 16 * 16, want = stride == 2 ? 8 : 16;
     return need + ((want - need) % 32 + 32) % 32;
 }
-// ceil(2^16 / d): for 0 <= x < 256 and 1 <= d < 256, (x * m) >> 16 = x / d.
-inline uint32_t col2im_magic16(int d) { return (65536u + (uint32_t)d - 1u) / (uint32_t)d; }
+// ceil(2^16 / d): for 0 <= x < 256 and 1 <= d <= 256, (x * m) >> 16 = x / d
+// (the error x * (m - 2^16/d) / 2^16 < x / 2^16 stays below 1/d, the least
+// distance from x/d up to the next integer, since x * d < 2^16).
+inline uint32_t recip16(int d) { return (65536u + (uint32_t)d - 1u) / (uint32_t)d; }
 int col2im_f32_weight_offset(const Col2imArgs &a);
 size_t col2im_f32_lds_bytes(const Col2imArgs &a);
 hipError_t launch_col2im_f32(const Col2imArgs &a, hipStream_t s, const KernelEvents &ev);

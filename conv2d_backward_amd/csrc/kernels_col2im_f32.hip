@@ -435,7 +435,7 @@ hipError_t launch_col2im_f32(const Col2imArgs &a, hipStream_t s, const KernelEve
     // Staged weight rows hold every column block; the divisions by
     // reciprocal are exact for the column indices (< 256) and divisors.
     if (a.ws < 16 * nbn || (a.ws & 3) || a.kH * a.kW > 255 ||
-        a.magic_khw != col2im_magic16(a.kH * a.kW) || a.magic_kw != col2im_magic16(a.kW))
+        a.magic_khw != recip16(a.kH * a.kW) || a.magic_kw != recip16(a.kW))
         return hipErrorInvalidValue;
     if ((a.TW + a.kW - 2) / a.stride + 1 > 16 * kCol2imBlocksPerRow) return hipErrorInvalidValue;
     // Border and alignment of the LDS tile; its row pitch holds the pixels of

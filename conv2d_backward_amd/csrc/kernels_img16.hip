@@ -34,7 +34,11 @@
 // whatever the tap shift: every cycle's lanes touch 16 different bank groups.
 //
 // V_MFMA_F32_16X16X32_BF16 / _F16: lane l = 16*g + i supplies A[i][k = 8g ..
-// 8g+7] and B[k = 8g .. 8g+7][i] and receives D[4g + r][i], r = 0..3.
+// 8g+7] and B[k = 8g .. 8g+7][i] and receives D[4g + r][i], r = 0..3.  The
+// two fragments have the same lane layout, so the kernel computes the
+// transpose C^T[pixels, Ci] = B^T x A^T: the grad_out fragment goes in as the
+// MFMA's A operand and the weight fragment as its B operand, and each lane
+// ends with 4 consecutive pixels of one input channel, stored as 16 bytes.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -78,9 +82,13 @@ constexpr int img16_plane_bytes() { return (HRT * HPT * 16 + 255) / 256 * 256; }
 constexpr int kLand = 4096;    // landing area of one wave's direct loads (4 x 1 KB)
 constexpr int kStages = 3;     // LDS stages of channel planes
 
-// Three stages of 4 channel planes, then the 4 waves' landing areas.
+// Three stages of 4 channel planes, the 4 waves' landing areas, then one
+// 16-byte slot per lane that takes the staging writes of quads past the
+// grad_out plane.
 template <int HRT, int HPT>
-constexpr int img16_lds_bytes() { return kStages * 4 * img16_plane_bytes<HRT, HPT>() + 4 * kLand; }
+constexpr int img16_lds_bytes() {
+    return kStages * 4 * img16_plane_bytes<HRT, HPT>() + 4 * kLand + 64 * 16;
+}
 
 template <bool F16, int NB, int T, int KW, int HPT, int HRT>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void gi_img16(
@@ -138,31 +146,38 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             __builtin_amdgcn_raw_ptr_buffer_load_lds(grs, (lds_ptr_t)(land + 1024 * k), 16,
                                                      loff + 1024 * k, c * chunk_bytes, 0, 0);
     };
-    // LDS byte offset (within a stage) of each pixel of quad `lane`, -1
-    // outside the halo (only with padding beyond kH-1) or past the plane.
+    // LDS byte address, in each stage, of each pixel of quad `lane`; pixels
+    // outside the halo (only with padding beyond kH-1) or past the plane go
+    // to the lane's own slot past the landing areas, so the transposition
+    // writes every quad without a branch.  (Pixel index p < 256 and oW <= 256:
+    // the reciprocal multiply is the exact row.)
     const bool qv = lane < A.nq;
-    int wpos[4];
+    const int dummy = kStages * kStage + 4 * kLand + lane * 16;
+    int wdst[kStages][4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const int p = 4 * lane + k;
-        const int oh = p / A.oW, ow = p - (p / A.oW) * A.oW;
+        const int oh = (int)(((uint32_t)p * A.rcp_ow) >> 16), ow = p - oh * A.oW;
         const int hr = oh + A.oy, hc = ow + A.ox;
         const bool v = qv && hr >= 0 && hr < A.HR && hc >= 0 && hc < A.HC;
-        wpos[k] = v ? wave * PS + (hr * HP + hc) * 16 : -1;
+#pragma unroll
+        for (int st = 0; st < kStages; ++st)
+            wdst[st][k] = v ? st * kStage + wave * PS + (hr * HP + hc) * 16 : dummy;
     }
     // Transpose quad `lane` of the landed planes of chunk c (channels past
-    // Co read as 0) into stage `buf`.
+    // Co read as 0) into stage `buf` (a compile-time index).
     auto swrite = [&](int c, int buf) {
         const int room = A.Co - 32 * c - 8 * wave;   // channels of the wave's 8 that exist
         v2u v[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            v[i] = *(const v2u *)(land + shift + i * plane_bytes + 8 * lane);
-            if (i >= room) v[i] = v2u{0u, 0u};
+        for (int i = 0; i < 8; ++i) v[i] = *(const v2u *)(land + shift + i * plane_bytes + 8 * lane);
+        if (room < 8) {   // (uniform: only the last chunk of a ragged Co)
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (i >= room) v[i] = v2u{0u, 0u};
         }
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            if (wpos[k] < 0) continue;
             const unsigned sel = (k & 1) ? kHi : kLo;
             v4u o;
 #pragma unroll
@@ -171,7 +186,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                 const unsigned b = (k < 2) ? v[2 * m + 1].x : v[2 * m + 1].y;
                 o[m] = pack2(a, b, sel);
             }
-            *(v4u *)(smem + buf * kStage + wpos[k]) = o;
+            *(v4u *)(smem + wdst[buf][k]) = o;
         }
     };
 
@@ -193,11 +208,32 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     int bbase[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-        const int p = b * 16 + j16;
-        const int ih = p / A.W, iw = p - (p / A.W) * A.W;
+        const int p = b * 16 + j16;   // < 256, and W <= 256: exact row by reciprocal
+        const int ih = (int)(((uint32_t)p * A.rcp_w) >> 16), iw = p - ih * A.W;
         bbase[b] = g * PS + (p < HW ? ih * HP + iw : j16) * 16;
     }
 
+    // A ring of T slots indexed by tap: step s = chunk*T + tap uses slot
+    // tap, and step s + AD is loaded while step s computes.  Every chunk
+    // brings fresh weight lines, which each L2 fetches once for all of its
+    // work-groups, so their first use waits for memory beyond the L2: they
+    // are fetched nearly a chunk ahead.
+    constexpr int AD = T - 1;
+    static_assert(AD >= 1, "prefetch distance");
+    v8bf fa[T][2];
+    v8bf fb[NB];
+    // Loads issued after a chunk's landing loads until the next chunk's
+    // transposition: every tap's two A prefetches in between.
+    constexpr int kAfterLanding = 2 * T;
+
+    // Chunk 0's copy and the first A fragments go out before the stages are
+    // zeroed (the landing areas lie past the stages).
+    sload(0);
+#pragma unroll
+    for (int s0 = 0; s0 < AD; ++s0) {
+        fa[s0][0] = aload(0, s0, 0);
+        fa[s0][1] = aload(0, s0, 1);
+    }
     // Zero the stages: positions the staging never writes (the border) stay
     // zero for the whole kernel.
     for (int i = tid; i < kStages * kStage / 16; i += 256) ((v4u *)smem)[i] = v4u{0u, 0u, 0u, 0u};
@@ -215,31 +251,16 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         return st * kStage + ((KH - 1 - kh) * HP + (KW - 1 - kw)) * 16;
     };
 
-    // A ring of T slots indexed by tap: step s = chunk*T + tap uses slot
-    // tap, and step s + AD is loaded while step s computes.  Every chunk
-    // brings fresh weight lines, which each L2 fetches once for all of its
-    // work-groups, so their first use waits for memory beyond the L2: they
-    // are fetched nearly a chunk ahead.
-    constexpr int AD = T - 1;
-    static_assert(AD >= 1, "prefetch distance");
-    v8bf fa[T][2];
-    v8bf fb[NB];
-    // Loads issued after a chunk's landing loads until the next chunk's
-    // transposition: every tap's two A prefetches in between.
-    constexpr int kAfterLanding = 2 * T;
-
     // Set-up: chunk 0 staged into stage 0, chunk 1's copy in flight, the
     // first A fragments in flight, chunk 0's first B fragments read.
-    sload(0);
     __syncthreads();   // the zeroing is done before any position is staged
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // (Chunk 0's copy and the first A fragments went out before the zeroing,
+    // into the landing areas and registers, so their latencies overlap it
+    // and each other; the copy is complete once at most the 2 AD fragment
+    // loads issued after it are outstanding.)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * AD) : "memory");
     swrite(0, 0);
     sload(1);
-#pragma unroll
-    for (int s0 = 0; s0 < AD; ++s0) {
-        fa[s0][0] = aload(0, s0, 0);
-        fa[s0][1] = aload(0, s0, 1);
-    }
     __syncthreads();
 #pragma unroll
     for (int b = 0; b < NB; ++b) fb[b] = *(const v8bf *)(smem + bbase[b] + tap_offset(0, 0));
@@ -247,8 +268,9 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // One chunk of 32 output channels on stage ST (a compile-time index, so
     // every LDS address is a base register plus an immediate).  The B
     // fragments are single-buffered: block b's fragment for the next tap is
-    // read right after block b's two MFMAs of this tap are issued (in the
-    // last tap: the next chunk's first tap, from its stage, staged and made
+    // read after block b + 1's MFMAs of this tap are issued, so the read
+    // never waits for the MFMAs that still read the register (in the last
+    // tap: the next chunk's first tap, from its stage, staged and made
     // visible earlier in this chunk).
     auto run_chunk = [&](const int chunk, auto st_c) {
         constexpr int ST = decltype(st_c)::value;
@@ -257,6 +279,13 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int tp = 0; tp < T; ++tp) {
+            // Block b's B fragment for the step after tap tp.
+            auto next_b = [&](int b) {
+                if (tp + 1 < T)
+                    fb[b] = *(const v8bf *)(smem + bbase[b] + tap_offset(ST, tp + 1));
+                else if (more)
+                    fb[b] = *(const v8bf *)(smem + bbase[b] + tap_offset(NX, 0));
+            };
             {
                 const int t2 = tp + AD;
                 const int c2 = t2 < T ? chunk : chunk + 1;
@@ -270,21 +299,26 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                 for (int cb = 0; cb < 2; ++cb)
                     if constexpr (F16)
                         acc[cb][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                            __builtin_bit_cast(v8h, fa[tp][cb]), __builtin_bit_cast(v8h, fb[b]),
+                            __builtin_bit_cast(v8h, fb[b]), __builtin_bit_cast(v8h, fa[tp][cb]),
                             acc[cb][b], 0, 0, 0);
                     else
                         acc[cb][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            fa[tp][cb], fb[b], acc[cb][b], 0, 0, 0);
-                if (tp + 1 < T)
-                    fb[b] = *(const v8bf *)(smem + bbase[b] + tap_offset(ST, tp + 1));
-                else if (more)
-                    fb[b] = *(const v8bf *)(smem + bbase[b] + tap_offset(NX, 0));
+                            fb[b], fa[tp][cb], acc[cb][b], 0, 0, 0);
+                if (b >= 1) next_b(b - 1);
+                __builtin_amdgcn_sched_barrier(0);
             }
+            next_b(NB - 1);
             if (tp == kStageTap && more) {
-                // The next chunk's copy was issued a chunk ago; only this
-                // chunk's A prefetches were issued after it.  Its stage was
-                // last read two chunks ago, before the last barrier.
-                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kAfterLanding) : "memory");
+                // The next chunk's copy was issued a chunk ago; only A
+                // prefetches were issued after it: the previous chunk's
+                // from tap kStageTap + 1 on and this chunk's up to here, or
+                // in chunk 0 (whose set-up fragments went out before the
+                // copy) this chunk's alone.  Its stage was last read two
+                // chunks ago, before the last barrier.
+                if (chunk == 0)
+                    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (kStageTap + 1)) : "memory");
+                else
+                    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kAfterLanding) : "memory");
                 swrite(chunk + 1, NX);
                 sload(chunk + 2);
             }
@@ -299,39 +333,23 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-    // Epilogue.  Lane (j16, g) holds D[4g + r][j16] of each block: four
-    // consecutive input channels of one pixel.  Each wave turns its 32
-    // channels x NB*16 pixels around through LDS (the stages are free: every
-    // wave passed the last chunk's barrier) so that a lane stores 4
-    // consecutive pixels of one channel with one 16-byte store: a quarter of
-    // the store instructions of 4-byte stores, each a full 64-byte run per
-    // 4 lanes.  LDS rows are NB*16 + 4 floats apart, so the 16 lanes of a
-    // row write (4g + r, j16) at banks distinct within each 16-lane quarter.
-    __syncthreads();
-    constexpr int RW = NB * 16 + 4;               // floats per LDS row (one channel)
-    static_assert(4 * 32 * RW * 4 <= img16_lds_bytes<HRT, HPT>(), "epilogue transpose fits");
-    float *const tw = (float *)smem + wave * 32 * RW;
+    // Epilogue.  grad_out is the MFMA's A operand and the weight its B
+    // operand, so lane (j16, g) holds D[4g + r][j16] of each block: pixels
+    // 16b + 4g .. 16b + 4g + 3 (consecutive in the NCHW plane, and 16-byte
+    // aligned as H*W is a multiple of 4, checked at launch) of input channel
+    // j16 of the wave's channel block cb.  One 16-byte store each, every
+    // 4 lanes of a channel a full 64-byte run; slots past the image are not
+    // stored.
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
+    for (int cb = 0; cb < 2; ++cb) {
+        const int ci = ci_tile * 128 + wave * 32 + cb * 16 + j16;
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr)
-                tw[(cb * 16 + 4 * g + rr) * RW + b * 16 + j16] = acc[cb][b][rr];
-    // Own rows only: a wave reads back what it wrote, so its own LDS wait
-    // (inserted by the compiler) orders the two.
-    constexpr int QPR = NB * 4;                   // 4-pixel quads per channel row
-#pragma unroll
-    for (int k = 0; k < (32 * QPR + 63) / 64; ++k) {
-        const int e = k * 64 + lane;              // (channel row, quad) of this store
-        const int row = e / QPR, qd = e - (e / QPR) * QPR;
-        const int ci = ci_tile * 128 + wave * 32 + row;
-        const int p = 4 * qd;
-        const bool ok = e < 32 * QPR && p < HW && ci < A.Ci;
-        const v4u v = ok ? *(const v4u *)(tw + row * RW + p) : v4u{0u, 0u, 0u, 0u};
-        // A quad is whole: H*W is a multiple of 4 (checked at launch).
-        const int off = ok ? ((n * A.Ci + ci) * HW + p) * 4 : kOOB;
-        __builtin_amdgcn_raw_buffer_store_b128(v, drs, off, 0, 0);
+        for (int b = 0; b < NB; ++b) {
+            const int p = 16 * b + 4 * g;
+            const int off = (p < HW && ci < A.Ci) ? ((n * A.Ci + ci) * HW + p) * 4 : kOOB;
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, acc[cb][b]), drs, off,
+                                                   0, 0);
+        }
     }
 }
 
@@ -339,6 +357,7 @@ template <bool F16, int NB, int T, int KW, int HPT, int HRT>
 hipError_t launch_one(const Img16Args &a, size_t lds, hipStream_t s, const KernelEvents &ev) {
     if (a.kW != KW || a.kH * a.kW != T || a.HP != HPT || a.HR > HRT ||
         a.PS != img16_plane_bytes<HRT, HPT>() || lds != (size_t)img16_lds_bytes<HRT, HPT>() ||
+        a.rcp_w != recip16(a.W) || a.rcp_ow != recip16(a.oW) || a.W > 256 || a.oW > 256 ||
         a.H * a.W > 16 * NB || (a.H * a.W) % 4 != 0 || a.nq > 64 || 4 * a.nq != a.oH * a.oW ||
         8 + 16 * a.oH * a.oW > kLand)
         return hipErrorInvalidValue;
