@@ -47,6 +47,8 @@ KERNEL_SOURCES = {
     ("halo", "f16"): ["kernels_halo_bf16.hip", "half_launch.h"],
     ("stem", "f32"): ["kernels_stem_f32.hip"],
     ("col2im", "f32"): ["kernels_col2im_f32.hip"],
+    ("img16", "bf16"): ["kernels_img16.hip", "half_launch.h"],
+    ("img16", "f16"): ["kernels_img16.hip", "half_launch.h"],
     ("gw", "f32"): ["kernels_gw_f32.hip", "gw_common.h"],
     ("gwd", "f32"): ["kernels_gw_f32.hip", "gw_common.h"],
     ("fwd", "f32"): ["kernels_fwd_f32.hip", "fwd_common.h"],
@@ -64,6 +66,10 @@ def kernel_name(variant: str, dtype: str) -> str:
 
 
 def plan_variant(plan_desc: str) -> str:
+    """The plan's main kernel family: its variant, except that a 16-bit plan
+    on the whole-image kernel (described as ``[image kernel ...]``) is img16."""
+    if "[image kernel" in plan_desc:
+        return "img16"
     return plan_desc.split()[0].split("=", 1)[1]
 
 
@@ -79,7 +85,10 @@ def fingerprint(variant: str, dtype: str) -> str:
 def _matches(name: str, short: str) -> bool:
     """Whether kernel `name` (as the trace prints it) is the kernel `short`
     names.  fp16 inputs run the 16-bit kernels' fp16 instantiations:
-    gi_halo_f16 is gi_halo_bf16<true, ...>, gi_generic_f16 gi_generic_bf16<true>."""
+    gi_halo_f16 is gi_halo_bf16<true, ...>, gi_generic_f16 gi_generic_bf16<true>;
+    the image kernel is gi_img16<false, ...> for bf16 and <true, ...> for fp16."""
+    if short.startswith("gi_img16_"):
+        return ("gi_img16<%s" % ("true" if short.endswith("_f16") else "false")) in name
     if short.endswith("_f16"):
         return (short[:-4] + "_bf16<true") in name
     return (short + "<") in name or (short + "(") in name

@@ -84,7 +84,9 @@ def test_read_traffic_checks_plan_and_sources(tmp_path, monkeypatch):
 
 def test_fingerprint_covers_every_kernel():
     seen = {profiling.fingerprint(v, d) for v, d in profiling.KERNEL_SOURCES}
-    assert len(seen) == 7   # generic f32 and bf16 share one source file, so do gw and gwd
+    # generic f32 and bf16 share one source file, so do gw and gwd, and the
+    # 16-bit halo and image kernels' bf16 and fp16 instantiations
+    assert len(seen) == 8
 
 
 def test_mfma_summary(tmp_path, monkeypatch):
@@ -123,3 +125,22 @@ def test_mfma_summary(tmp_path, monkeypatch):
     monkeypatch.setattr(profiling, "PROFILES", str(tmp_path))
     assert profiling.read_mfma("gi_halo_f32", "wl", PLAN, "halo", "f32")["counter_flops"] == 512000
     assert profiling.read_mfma("gi_halo_f32", "wl", PLAN + "x", "halo", "f32") is None
+
+
+def test_plan_variant_and_kernel_names():
+    """Plans map to the kernel that runs them: the 16-bit whole-image plan to
+    gi_img16 (its bf16 and fp16 instantiations), the column plan to
+    gi_col2im_f32."""
+    img = ("variant=halo dtype=bf16 ws_bytes=4718592 launches=2 [image kernel cfg=0 nb=13 "
+           "wgs=64x4 lds=109568 halo=16x16 pitch=30 chunks=16]")
+    assert profiling.plan_variant(img) == "img16"
+    assert profiling.kernel_name("img16", "bf16") == "gi_img16_bf16"
+    bf = "void gi::(anonymous namespace)::gi_img16<false, 13, 9, 3, 30, 16>(gi::Img16Args)"
+    hf = "void gi::(anonymous namespace)::gi_img16<true, 13, 9, 3, 30, 16>(gi::Img16Args)"
+    assert profiling._matches(bf, "gi_img16_bf16") and not profiling._matches(hf, "gi_img16_bf16")
+    assert profiling._matches(hf, "gi_img16_f16") and not profiling._matches(bf, "gi_img16_f16")
+    col = "variant=col2im dtype=f32 ws_bytes=0 launches=1 [tile=56x56 wgs=256 cols=147]"
+    assert profiling.plan_variant(col) == "col2im"
+    assert profiling._matches("void gi::(anonymous namespace)::gi_col2im_f32<10, 2, 64>"
+                              "(gi::Col2imArgs)", profiling.kernel_name("col2im", "f32"))
+    assert profiling.plan_variant("variant=halo dtype=f32 ws_bytes=1 launches=1 [nb=13]") == "halo"
