@@ -59,10 +59,13 @@
 // next block's reads after the write of the column block above it (a pixel
 // is only reached by columns of one (ci, kh), i.e. of at most two adjacent
 // column blocks).  The next block's loads are issued during the current
-// block's middle k steps.  The four waves' rows are RW apart and a barrier
-// after every pair keeps them in step, so no two waves touch a pixel at the
-// same time.  Every pixel receives its columns in a fixed order and the
-// result is deterministic.
+// block's middle k steps.  The four waves' rows are RW apart: wave w's pair
+// k can only meet pixels of wave w + 1's earlier pairs, so wave w starts
+// pair k once wave w + 1 has finished pair k - 1 (a count per wave in LDS),
+// and the waves run staggered by an eighth of a block, so that their folds
+// reach the LDS at different moments.  A pixel that two waves reach receives wave
+// w + 1's columns first; every pixel receives its columns in a fixed order
+// and the result is deterministic.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -78,6 +81,7 @@ namespace {
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9)
 constexpr int kOOB = 0x7ffffff0;        // byte offset past the end of every buffer
 constexpr int kSteps = kCol2imMaxCo / 4;  // k steps of 4 output channels
+constexpr int kDephaseSleep = 10;         // s_sleep units (64 cycles): an eighth of a block
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (long)bytes, kRsrcWord3);
@@ -131,6 +135,9 @@ __global__ __launch_bounds__(256, 1) void gi_col2im_f32(const Col2imArgs A) {
     const int tfl = A.Ci * plane;
     const int dbase = (tfl + 31) / 32 * 32;
     float *const wst = tile + A.wofs;
+    // Pairs finished per wave (LDS), past the dummy slots.
+    volatile int *const done = (volatile int *)(tile + dbase + 96);
+    if (tid < 4) done[tid] = 0;
     // grad_out of a block: lane i loads the position of D row i (row k of
     // the pair for i < 8, row k + RW/2 for i >= 8), output channel 4c + g at
     // byte offset vo (the pair and the lane) + 4 class + c * 16 * oH * oW
@@ -310,9 +317,25 @@ __global__ __launch_bounds__(256, 1) void gi_col2im_f32(const Col2imArgs A) {
     };
 
     v4f acc[NBN];
-    // Pairs of rows (k, k + RW/2): four blocks (classes 0..3); a barrier
-    // after each pair.  gA holds class 0 of the pair when it starts.
+    // Pairs of rows (k, k + RW/2): four blocks (classes 0..3).  gA holds
+    // class 0 of the pair when it starts.  Wave w's pair k meets another
+    // wave's pixels only where wave w + 1 is still on an earlier pair (rows
+    // RW apart, RW/2 >= ceil(kH / S)), so before pair k >= 1 wave w waits
+    // until wave w + 1 has finished pair k - 1 (its count in LDS); wave 3
+    // never waits and no wave waits on a lower one, so every wait ends.  The
+    // waves start staggered, wave w + 1 an eighth of a block ahead of wave w,
+    // so that their folds do not reach the LDS at the same moments (measured
+    // on the stem: no stagger 48.7 us, an eighth 46.8, a quarter 47.6).
+    for (int z = wave; z < 3; ++z) __builtin_amdgcn_s_sleep(kDephaseSleep);
     for (int k = 0; k < RWh; ++k) {
+        if (wave < 3 && k > 0) {
+            // (Bounded: far past any wait the protocol allows.)
+            for (int spin = 0; spin < (1 << 22) &&
+                               __builtin_amdgcn_readfirstlane(done[wave + 1]) < k;
+                 ++spin)
+                __builtin_amdgcn_s_sleep(1);
+            asm volatile("" ::: "memory");
+        }
         if (k < rows_w) {
             pair_addr(k);
             const int vo = pair_vo(k);
@@ -337,8 +360,12 @@ __global__ __launch_bounds__(256, 1) void gi_col2im_f32(const Col2imArgs A) {
             for (int nb = 0; nb < NBN; ++nb) twrite(nb, 3, acc);
             asm volatile("" ::: "memory");
         }
-        __syncthreads();
+        // The pair's writes are complete before its count goes up.
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (lane == 0) done[wave] = k + 1;
+        asm volatile("" ::: "memory");
     }
+    __syncthreads();  // every wave's fold is in the tile
 
     // Epilogue: the tile's pixels inside the image, 16 bytes per lane where
     // rows are whole quads (lanes: 16 quads of a row, 16 rows at a time; the
@@ -380,9 +407,9 @@ constexpr size_t kOnePerCuLds = 80 * 1024 + 256;
 
 int col2im_f32_weight_offset(const Col2imArgs &a) {
     // The tile, then 32 slots on 32 banks plus the fold's largest immediate
-    // offset (4 DELTA S * 3 + S * 3 <= 54 floats) for columns past the last;
-    // the weight stage starts 16-byte aligned.
-    return (a.Ci * a.plane + 31) / 32 * 32 + 96;
+    // offset (4 DELTA S * 3 + S * 3 <= 54 floats) for columns past the last,
+    // then the 4 waves' pair counts; the weight stage starts 16-byte aligned.
+    return (a.Ci * a.plane + 31) / 32 * 32 + 96 + 8;
 }
 
 size_t col2im_f32_lds_bytes(const Col2imArgs &a) {
