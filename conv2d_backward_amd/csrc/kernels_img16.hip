@@ -98,10 +98,12 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     constexpr int HP = HPT;
     constexpr int PS = img16_plane_bytes<HRT, HPT>();   // bytes of one channel plane
     constexpr int kStage = 4 * PS;                      // bytes of one stage: 4 planes
-    // Within a chunk's taps: the next chunk is transposed into its stage
-    // during tap kStageTap and made visible by the barrier of tap kBarTap;
-    // the last tap reads the next chunk's first B fragments.
+    // Within a chunk's taps: the next chunk's landed planes are read into
+    // registers in tap kReadTap, transposed into its stage during tap
+    // kStageTap and made visible by the barrier of tap kBarTap; the last tap
+    // reads the next chunk's first B fragments.
     constexpr int kStageTap = T > 2 ? 2 : 0;
+    constexpr int kReadTap = kStageTap > 0 ? kStageTap - 1 : 0;
     constexpr int kBarTap = T > 4 ? 4 : T - 1;
     static_assert(kStageTap <= kBarTap && kBarTap < T, "tap schedule");
     const int tid = threadIdx.x;
@@ -165,12 +167,16 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             wdst[st][k] = v ? st * kStage + wave * PS + (hr * HP + hc) * 16 : dummy;
     }
     // Transpose quad `lane` of the landed planes of chunk c (channels past
-    // Co read as 0) into stage `buf` (a compile-time index).
-    auto swrite = [&](int c, int buf) {
-        const int room = A.Co - 32 * c - 8 * wave;   // channels of the wave's 8 that exist
-        v2u v[8];
+    // Co read as 0) into stage `buf` (a compile-time index), in two parts a
+    // tap apart: sread takes the quad into registers, swrite turns it round
+    // and writes it, so the writes never wait on the reads' LDS round trip.
+    v2u v[8];
+    auto sread = [&]() {
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = *(const v2u *)(land + shift + i * plane_bytes + 8 * lane);
+    };
+    auto swrite = [&](int c, int buf) {
+        const int room = A.Co - 32 * c - 8 * wave;   // channels of the wave's 8 that exist
         if (room < 8) {   // (uniform: only the last chunk of a ragged Co)
 #pragma unroll
             for (int i = 0; i < 8; ++i)
@@ -223,8 +229,9 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     v8bf fa[T][2];
     v8bf fb[NB];
     // Loads issued after a chunk's landing loads until the next chunk's
-    // transposition: every tap's two A prefetches in between.
-    constexpr int kAfterLanding = 2 * T;
+    // landed planes are read: the two A prefetches of every tap from tap
+    // kStageTap + 1 of one chunk to tap kReadTap of the next.
+    constexpr int kAfterLanding = 2 * (T - kStageTap + kReadTap);
 
     // Chunk 0's copy and the first A fragments go out before the stages are
     // zeroed (the landing areas lie past the stages).
@@ -259,6 +266,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // and each other; the copy is complete once at most the 2 AD fragment
     // loads issued after it are outstanding.)
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * AD) : "memory");
+    sread();
     swrite(0, 0);
     sload(1);
     __syncthreads();
@@ -308,17 +316,21 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                 __builtin_amdgcn_sched_barrier(0);
             }
             next_b(NB - 1);
-            if (tp == kStageTap && more) {
+            if (tp == kReadTap && more) {
                 // The next chunk's copy was issued a chunk ago; only A
                 // prefetches were issued after it: the previous chunk's
                 // from tap kStageTap + 1 on and this chunk's up to here, or
                 // in chunk 0 (whose set-up fragments went out before the
-                // copy) this chunk's alone.  Its stage was last read two
-                // chunks ago, before the last barrier.
+                // copy) this chunk's alone.
                 if (chunk == 0)
-                    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (kStageTap + 1)) : "memory");
+                    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (kReadTap + 1)) : "memory");
                 else
                     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kAfterLanding) : "memory");
+                sread();
+            }
+            if (tp == kStageTap && more) {
+                // The stage was last read two chunks ago, before the last
+                // barrier.
                 swrite(chunk + 1, NX);
                 sload(chunk + 2);
             }
