@@ -397,33 +397,54 @@ constexpr int kCfg[][5] = {{13, 9, 3, 30, 16}};
 // then each thread gathers one lane's 8 output channels at one (ci, tap) from
 // LDS and writes it; consecutive threads write consecutive lanes, so every
 // tap's 1 KB fragment block is stored whole.
+// VEC: every row of the weight is a whole number of 16-byte pieces (Ci*T a
+// multiple of 8), read with range-checked 16-byte buffer loads (w_bytes <
+// 2^31); else 2-byte reads.
+template <bool VEC>
 __global__ __launch_bounds__(256) void weight_frag16(const uint16_t *__restrict__ w,
                                                      uint16_t *__restrict__ wk, int Co, int Ci,
-                                                     int T, int nchunks) {
+                                                     int T, int nchunks, uint32_t w_bytes) {
     extern __shared__ uint16_t raw[];   // [32 rows][16*T + 8]
     const int chunk = blockIdx.x, blk = blockIdx.y;
     const int pitch = 16 * T + 8;
     const int64_t rowlen = (int64_t)Ci * T;
     const int64_t e0 = (int64_t)blk * 16 * T;   // first element of the block in a row
     const int pieces = 2 * T;                  // 8-element pieces per row of the block
-    const bool vec = rowlen % 8 == 0;
-    for (int i = threadIdx.x; i < 32 * pieces; i += 256) {
-        const int r = i / pieces, pc = i - (i / pieces) * pieces;
-        const int co = chunk * 32 + r;
-        const int64_t e = e0 + 8 * pc;
-        v4u v = v4u{0u, 0u, 0u, 0u};
-        if (co < Co && e < rowlen) {
-            const uint16_t *src = w + (int64_t)co * rowlen + e;
-            if (vec) {
-                v = *(const v4u *)src;
-            } else {
-                unsigned h[8];
+    const __amdgpu_buffer_rsrc_t wrs = make_rsrc(w, w_bytes);
+    // Four pieces per thread per pass, all loaded before any is stored, so a
+    // pass costs one memory round trip (a 3x3 kernel's block is one pass).
+    constexpr int kPer = 4;
+    for (int i0 = threadIdx.x; i0 < 32 * pieces; i0 += 256 * kPer) {
+        v4u v[kPer];
 #pragma unroll
-                for (int k = 0; k < 8; ++k) h[k] = e + k < rowlen ? src[k] : 0u;
-                v = v4u{h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16};
+        for (int u = 0; u < kPer; ++u) {
+            const int i = i0 + 256 * u;
+            const int r = i / pieces, pc = i - (i / pieces) * pieces;
+            const int co = chunk * 32 + r;
+            const int64_t e = e0 + 8 * pc;
+            const bool ok = i < 32 * pieces && co < Co && e < rowlen;
+            if (VEC) {
+                v[u] = __builtin_bit_cast(
+                    v4u, __builtin_amdgcn_raw_buffer_load_b128(
+                             wrs, ok ? (int)(((int64_t)co * rowlen + e) * 2) : kOOB, 0, 0));
+            } else {
+                v[u] = v4u{0u, 0u, 0u, 0u};
+                if (ok) {
+                    const uint16_t *src = w + (int64_t)co * rowlen + e;
+                    unsigned h[8];
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) h[k] = e + k < rowlen ? src[k] : 0u;
+                    v[u] = v4u{h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16,
+                               h[6] | h[7] << 16};
+                }
             }
         }
-        *(v4u *)(raw + r * pitch + 8 * pc) = v;
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int i = i0 + 256 * u;
+            const int r = i / pieces, pc = i - (i / pieces) * pieces;
+            if (i < 32 * pieces) *(v4u *)(raw + r * pitch + 8 * pc) = v[u];
+        }
     }
     __syncthreads();
     const int ct = blk >> 2, cb = blk & 3;
@@ -481,13 +502,22 @@ hipError_t launch_weight_frag16(const uint16_t *w, uint16_t *wk, int Co, int Ci,
     // including the zero blocks past Ci up to wtiles*64 channels.
     const size_t lds = (size_t)32 * (16 * kHW + 8) * sizeof(uint16_t);
     if (lds > 160 * 1024 || wtiles * 4 > 65535) return hipErrorInvalidValue;
+    const int64_t wbytes = (int64_t)Co * Ci * kHW * 2;
+    // 16-byte buffer loads where rows are whole pieces and byte offsets fit
+    // (kOOB stays past the range).
+    const bool vec = ((int64_t)Ci * kHW) % 8 == 0 && wbytes < 0x7fff0000LL;
+    const void *fn = vec ? (const void *)weight_frag16<true> : (const void *)weight_frag16<false>;
     if (lds > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute((const void *)weight_frag16,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(weight_frag16, dim3(nchunks, wtiles * 4), dim3(256), lds, s, w, wk, Co, Ci,
-                       kHW, nchunks);
+    const uint32_t wb = vec ? (uint32_t)wbytes : 0u;
+    if (vec)
+        hipLaunchKernelGGL(weight_frag16<true>, dim3(nchunks, wtiles * 4), dim3(256), lds, s, w, wk,
+                           Co, Ci, kHW, nchunks, wb);
+    else
+        hipLaunchKernelGGL(weight_frag16<false>, dim3(nchunks, wtiles * 4), dim3(256), lds, s, w,
+                           wk, Co, Ci, kHW, nchunks, wb);
     return hipGetLastError();
 }
 
