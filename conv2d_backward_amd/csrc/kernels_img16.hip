@@ -148,24 +148,12 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             __builtin_amdgcn_raw_ptr_buffer_load_lds(grs, (lds_ptr_t)(land + 1024 * k), 16,
                                                      loff + 1024 * k, c * chunk_bytes, 0, 0);
     };
-    // LDS byte address, in each stage, of each pixel of quad `lane`; pixels
-    // outside the halo (only with padding beyond kH-1) or past the plane go
-    // to the lane's own slot past the landing areas, so the transposition
-    // writes every quad without a branch.  (Pixel index p < 256 and oW <= 256:
-    // the reciprocal multiply is the exact row.)
-    const bool qv = lane < A.nq;
-    const int dummy = kStages * kStage + 4 * kLand + lane * 16;
+    // Filled after the stages are zeroed (below): the LDS byte address, in
+    // each stage, of each pixel of quad `lane`, and this lane's pixel in each
+    // block.
     int wdst[kStages][4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int p = 4 * lane + k;
-        const int oh = (int)(((uint32_t)p * A.rcp_ow) >> 16), ow = p - oh * A.oW;
-        const int hr = oh + A.oy, hc = ow + A.ox;
-        const bool v = qv && hr >= 0 && hr < A.HR && hc >= 0 && hc < A.HC;
-#pragma unroll
-        for (int st = 0; st < kStages; ++st)
-            wdst[st][k] = v ? st * kStage + wave * PS + (hr * HP + hc) * 16 : dummy;
-    }
+    const int HW = A.H * A.W;
+    int bbase[NB];
     // Transpose quad `lane` of the landed planes of chunk c (channels past
     // Co read as 0) into stage `buf` (a compile-time index), in two parts a
     // tap apart: sread takes the quad into registers, swrite turns it round
@@ -207,18 +195,6 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         return __builtin_bit_cast(v8bf, __builtin_amdgcn_raw_buffer_load_b128(wrs, wlane, soff, 0));
     };
 
-    // This lane's pixel in each block: LDS byte offset of its halo position
-    // in plane g of a stage.  Slots past the image read position j16 (their
-    // column is never stored; distinct positions keep the read conflict-free).
-    const int HW = A.H * A.W;
-    int bbase[NB];
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-        const int p = b * 16 + j16;   // < 256, and W <= 256: exact row by reciprocal
-        const int ih = (int)(((uint32_t)p * A.rcp_w) >> 16), iw = p - ih * A.W;
-        bbase[b] = g * PS + (p < HW ? ih * HP + iw : j16) * 16;
-    }
-
     // A ring of T slots indexed by tap: step s = chunk*T + tap uses slot
     // tap, and step s + AD is loaded while step s computes.  Every chunk
     // brings fresh weight lines, which each L2 fetches once for all of its
@@ -233,17 +209,50 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // kStageTap + 1 of one chunk to tap kReadTap of the next.
     constexpr int kAfterLanding = 2 * (T - kStageTap + kReadTap);
 
-    // Chunk 0's copy and the first A fragments go out before the stages are
-    // zeroed (the landing areas lie past the stages).
+    // Chunk 0's copy goes out first, then the first A fragments interleaved
+    // with the zeroing of the stages (the landing areas lie past the stages),
+    // so the load queue and the LDS work side by side; the address tables
+    // are computed while the loads are in flight.  Positions the staging
+    // never writes (the border) stay zero for the whole kernel.
     sload(0);
+    constexpr int kZeroIters = (kStages * kStage / 16 + 255) / 256;
 #pragma unroll
-    for (int s0 = 0; s0 < AD; ++s0) {
-        fa[s0][0] = aload(0, s0, 0);
-        fa[s0][1] = aload(0, s0, 1);
+    for (int it = 0; it < kZeroIters; ++it) {
+        const int i = tid + 256 * it;
+        if (i < kStages * kStage / 16) ((v4u *)smem)[i] = v4u{0u, 0u, 0u, 0u};
+        if (it < AD) {
+            fa[it][0] = aload(0, it, 0);
+            fa[it][1] = aload(0, it, 1);
+        }
     }
-    // Zero the stages: positions the staging never writes (the border) stay
-    // zero for the whole kernel.
-    for (int i = tid; i < kStages * kStage / 16; i += 256) ((v4u *)smem)[i] = v4u{0u, 0u, 0u, 0u};
+    static_assert(kZeroIters >= AD, "every set-up fragment issued");
+    __builtin_amdgcn_sched_barrier(0);
+    // LDS byte address, in each stage, of each pixel of quad `lane`; pixels
+    // outside the halo (only with padding beyond kH-1) or past the plane go
+    // to the lane's own slot past the landing areas, so the transposition
+    // writes every quad without a branch.  (Pixel index p < 256 and oW <= 256:
+    // the reciprocal multiply is the exact row.)
+    const bool qv = lane < A.nq;
+    const int dummy = kStages * kStage + 4 * kLand + lane * 16;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int p = 4 * lane + k;
+        const int oh = (int)(((uint32_t)p * A.rcp_ow) >> 16), ow = p - oh * A.oW;
+        const int hr = oh + A.oy, hc = ow + A.ox;
+        const bool v = qv && hr >= 0 && hr < A.HR && hc >= 0 && hc < A.HC;
+#pragma unroll
+        for (int st = 0; st < kStages; ++st)
+            wdst[st][k] = v ? st * kStage + wave * PS + (hr * HP + hc) * 16 : dummy;
+    }
+    // This lane's pixel in each block: LDS byte offset of its halo position
+    // in plane g of a stage.  Slots past the image read position j16 (their
+    // column is never stored; distinct positions keep the read conflict-free).
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        const int p = b * 16 + j16;   // < 256, and W <= 256: exact row by reciprocal
+        const int ih = (int)(((uint32_t)p * A.rcp_w) >> 16), iw = p - ih * A.W;
+        bbase[b] = g * PS + (p < HW ? ih * HP + iw : j16) * 16;
+    }
 
     v4f acc[2][NB];
 #pragma unroll
