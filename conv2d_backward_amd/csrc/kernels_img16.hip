@@ -8,12 +8,12 @@
 //   * A (the weight read as [Ci, K]) comes from a fragment image that a
 //     prologue writes in the exact lane order of the MFMA A fragments;
 //   * B (the im2col of grad_out) is read from the caller's NCHW tensor and
-//     turned channel-minor on its way into LDS: each thread loads 8 channels
-//     x 4 consecutive pixels (eight 8-byte loads), transposes the 8 x 4 block
-//     of 16-bit values in registers (v_perm_b32) and writes 4 positions of 8
-//     channels (16 bytes each).  Positions outside the grad_out plane stay
-//     zero: that border is the transposed padding kH-1-pad of the shader's
-//     header comment.
+//     turned channel-minor on its way into LDS: each wave copies 8 channel
+//     planes into a landing area with direct loads, reads them back with
+//     gfx950's transposing LDS read (4 channels of one pixel per lane) and
+//     writes 16-byte positions of 8 channels.  Positions outside the grad_out
+//     plane stay zero: that border is the transposed padding kH-1-pad of the
+//     shader's header comment.
 //
 // Work-group: 256 threads (4 waves) own one image and 128 input channels.
 // Wave w owns input-channel blocks 2w, 2w+1 (16 channels each) and all NB
@@ -65,13 +65,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint3
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (long)bytes, kRsrcWord3);
 }
 
-// Low (sel = kLo) or high (kHi) 16-bit halves of a and b packed as
-// half(a) | half(b) << 16.
-constexpr unsigned kLo = 0x05040100u, kHi = 0x07060302u;
-__device__ __forceinline__ unsigned pack2(unsigned a, unsigned b, unsigned sel) {
-    return __builtin_amdgcn_perm(b, a, sel);
-}
-
 // F16: fp16 inputs (V_MFMA_F32_16X16X32_F16), else bf16.  NB pixel blocks of
 // 16 per wave (the image's pixels, H*W <= 16*NB), T taps, KW the kernel
 // width, HPT the halo pitch and HRT the most halo rows (all fixed at compile
@@ -101,11 +94,16 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // Within a chunk's taps: the next chunk's landed planes are read into
     // registers in tap kReadTap, transposed into its stage during tap
     // kStageTap and made visible by the barrier of tap kBarTap; the last tap
-    // reads the next chunk's first B fragments.
-    constexpr int kStageTap = T > 2 ? 2 : 0;
-    constexpr int kReadTap = kStageTap > 0 ? kStageTap - 1 : 0;
-    constexpr int kBarTap = T > 4 ? 4 : T - 1;
-    static_assert(kStageTap <= kBarTap && kBarTap < T, "tap schedule");
+    // reads the next chunk's first B fragments.  The copy of the chunk after
+    // next goes out one quarter per tap over the last four taps: a quarter
+    // of the chip's copy traffic at a time, and every A prefetch issued
+    // after a quarter (whose wait, in issue order, includes it) is waited
+    // for eight taps later.
+    constexpr int kReadTap = T / 3;
+    constexpr int kStageTap = kReadTap + 1;
+    constexpr int kBarTap = kStageTap + 2;
+    constexpr int kLoadTap = T - 4;
+    static_assert(kReadTap >= 1 && kStageTap < kLoadTap && kBarTap < T - 1, "tap schedule");
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -125,13 +123,13 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // Staging.  Wave w stages channels 8w .. 8w+7 of every chunk: four
     // 16-byte direct loads per lane copy those 8 channel planes of grad_out
     // (contiguous in NCHW) into the wave's own 4 KB landing area a chunk
-    // ahead, and lane q later transposes pixel quad q of them (8 channels x
-    // 4 pixels: eight 8-byte LDS reads and 16 v_perm_b32) into 4 positions
-    // of the chunk's stage.  A wave transposes only what it loaded itself, so
-    // its own load counter is the only wait.  The copy starts at the 16-byte
-    // boundary at or below the planes, which then sit `shift` bytes into the
-    // landing area (0 or 8: whole 4-pixel quads keep every plane 8-byte
-    // aligned).
+    // ahead; gfx950's transposing LDS read then turns them channel-minor on
+    // the way into registers, and lane l writes pixel 64s + l of the chunk's
+    // stage in write s (8 channels, 16 bytes).  A wave transposes only what
+    // it loaded itself, so its own load counter is the only wait.  The copy
+    // starts at the 16-byte boundary at or below the planes, which then sit
+    // `shift` bytes into the landing area (0 or 8: whole 4-pixel quads keep
+    // every plane 8-byte aligned).
     const int oHW = A.oH * A.oW;
     const int plane_bytes = oHW * 2;
     const int chunk_bytes = 32 * plane_bytes;
@@ -142,46 +140,67 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // Every wave issues all four loads per chunk (past the tensor they read
     // zeros, past the chunk's channels data the transposition ignores), so
     // the number of loads in flight is known at compile time.
+    auto sload_one = [&](int c, int k) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(grs, (lds_ptr_t)(land + 1024 * k), 16,
+                                                 loff + 1024 * k, c * chunk_bytes, 0, 0);
+    };
     auto sload = [&](int c) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(grs, (lds_ptr_t)(land + 1024 * k), 16,
-                                                     loff + 1024 * k, c * chunk_bytes, 0, 0);
+        for (int k = 0; k < 4; ++k) sload_one(c, k);
     };
     // Filled after the stages are zeroed (below): the LDS byte address, in
-    // each stage, of each pixel of quad `lane`, and this lane's pixel in each
-    // block.
+    // each stage, of pixel 64s + lane (write s), and this lane's pixel in
+    // each block.
     int wdst[kStages][4];
     const int HW = A.H * A.W;
     int bbase[NB];
-    // Transpose quad `lane` of the landed planes of chunk c (channels past
-    // Co read as 0) into stage `buf` (a compile-time index), in two parts a
-    // tap apart: sread takes the quad into registers, swrite turns it round
-    // and writes it, so the writes never wait on the reads' LDS round trip.
-    v2u v[8];
+    // ds_read_b64_tr_b16 (lane layout measured on the GPU): within each 16
+    // lanes, lanes 4r .. 4r+3 each load 4 consecutive 16-bit values, which
+    // together form row r (16 values); lane i receives element i of rows
+    // 0 .. 3.  Read (s, h): row r of the lanes 16g + 4r + j is channel
+    // 4h + r, pixels 64s + 16g + 4j .. +3, so lane l = 16g + i receives
+    // channels 4h .. 4h+3 of pixel 64s + l, packed two per dword in channel
+    // order: reads (s, 0) and (s, 1) are the 16 bytes of write s.  Pixels
+    // past the plane (up to 255) stay inside the landing area (8 planes of
+    // at most 255 pixels after at most 8 bytes); their writes go to a
+    // per-lane slot.  In two parts a tap apart: sread_one takes a piece into
+    // registers, swrite_one writes a position, so the writes never wait on
+    // the reads' LDS round trip.
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4s *lds_v4s_t;
+    const int rb = shift + ((lane >> 2) & 3) * plane_bytes + (16 * (lane >> 4) + 4 * (lane & 3)) * 2;
+    const int rb4 = rb + 4 * plane_bytes;
+    v2u tv[4][2];
+    auto sread_one = [&](int i) {   // piece (s, h) = (i / 2, i % 2)
+        const int s = i >> 1, h = i & 1;
+        tv[s][h] = __builtin_bit_cast(
+            v2u, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t)(land + (h ? rb4 : rb) + 128 * s)));
+    };
     auto sread = [&]() {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = *(const v2u *)(land + shift + i * plane_bytes + 8 * lane);
+        for (int i = 0; i < 8; ++i) sread_one(i);
     };
-    auto swrite = [&](int c, int buf) {
+    auto smask = [&](int c) {
         const int room = A.Co - 32 * c - 8 * wave;   // channels of the wave's 8 that exist
         if (room < 8) {   // (uniform: only the last chunk of a ragged Co)
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                if (i >= room) v[i] = v2u{0u, 0u};
-        }
+            for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const unsigned sel = (k & 1) ? kHi : kLo;
-            v4u o;
+                for (int d = 0; d < 2; ++d) {
+                    const int ch = 4 * h + 2 * d;   // channels ch (low half), ch + 1 (high)
+                    const unsigned keep = (ch < room ? 0xffffu : 0u) | (ch + 1 < room ? 0xffff0000u : 0u);
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const unsigned a = (k < 2) ? v[2 * m].x : v[2 * m].y;
-                const unsigned b = (k < 2) ? v[2 * m + 1].x : v[2 * m + 1].y;
-                o[m] = pack2(a, b, sel);
-            }
-            *(v4u *)(smem + wdst[buf][k]) = o;
+                    for (int t = 0; t < 4; ++t) tv[t][h][d] &= keep;
+                }
         }
+    };
+    auto swrite_one = [&](int t, int buf) {
+        *(v4u *)(smem + wdst[buf][t]) = v4u{tv[t][0].x, tv[t][0].y, tv[t][1].x, tv[t][1].y};
+    };
+    auto swrite = [&](int c, int buf) {
+        smask(c);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) swrite_one(t, buf);
     };
 
     // A fragments: wave w's ci blocks 2w, 2w+1 of the 128-channel tile are
@@ -204,10 +223,16 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     static_assert(AD >= 1, "prefetch distance");
     v8bf fa[T][2];
     v8bf fb[NB];
-    // Loads issued after a chunk's landing loads until the next chunk's
-    // landed planes are read: the two A prefetches of every tap from tap
-    // kStageTap + 1 of one chunk to tap kReadTap of the next.
-    constexpr int kAfterLanding = 2 * (T - kStageTap + kReadTap);
+    // Within a tap: the second A prefetch goes with block kA1Block's MFMAs,
+    // a quarter of the copy with the last block's.
+    static_assert(NB >= 9, "a tap carries eight landing reads");
+    constexpr int kA1Block = NB / 2;
+    // Loads issued after the copy's last quarter (the last tap's last block)
+    // until the next chunk's landed planes are read: the two A prefetches of
+    // each of its taps before kReadTap and the first of tap kReadTap.  In
+    // chunk 0 the copy went out in the set-up, after every set-up fragment:
+    // the same count.
+    constexpr int kAfterLanding = 2 * kReadTap + 1;
 
     // Chunk 0's copy goes out first, then the first A fragments interleaved
     // with the zeroing of the stages (the landing areas lie past the stages),
@@ -227,22 +252,21 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     }
     static_assert(kZeroIters >= AD, "every set-up fragment issued");
     __builtin_amdgcn_sched_barrier(0);
-    // LDS byte address, in each stage, of each pixel of quad `lane`; pixels
-    // outside the halo (only with padding beyond kH-1) or past the plane go
-    // to the lane's own slot past the landing areas, so the transposition
-    // writes every quad without a branch.  (Pixel index p < 256 and oW <= 256:
-    // the reciprocal multiply is the exact row.)
-    const bool qv = lane < A.nq;
+    // LDS byte address, in each stage, of pixel 64s + lane; pixels outside
+    // the halo (only with padding beyond kH-1) or past the plane go to the
+    // lane's own slot past the landing areas, so the staging writes every
+    // position without a branch.  (Pixel index p < 256 and oW <= 256: the
+    // reciprocal multiply is the exact row.)
     const int dummy = kStages * kStage + 4 * kLand + lane * 16;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int p = 4 * lane + k;
+    for (int t = 0; t < 4; ++t) {
+        const int p = 64 * t + lane;
         const int oh = (int)(((uint32_t)p * A.rcp_ow) >> 16), ow = p - oh * A.oW;
         const int hr = oh + A.oy, hc = ow + A.ox;
-        const bool v = qv && hr >= 0 && hr < A.HR && hc >= 0 && hc < A.HC;
+        const bool v = p < oHW && hr >= 0 && hr < A.HR && hc >= 0 && hc < A.HC;
 #pragma unroll
         for (int st = 0; st < kStages; ++st)
-            wdst[st][k] = v ? st * kStage + wave * PS + (hr * HP + hc) * 16 : dummy;
+            wdst[st][t] = v ? st * kStage + wave * PS + (hr * HP + hc) * 16 : dummy;
     }
     // This lane's pixel in each block: LDS byte offset of its halo position
     // in plane g of a stage.  Slots past the image read position j16 (their
@@ -269,7 +293,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 
     // Set-up: chunk 0 staged into stage 0, chunk 1's copy in flight, the
     // first A fragments in flight, chunk 0's first B fragments read.
-    __syncthreads();   // the zeroing is done before any position is staged
+    lds_barrier();   // the zeroing is done before any position is staged
     // (Chunk 0's copy and the first A fragments went out before the zeroing,
     // into the landing areas and registers, so their latencies overlap it
     // and each other; the copy is complete once at most the 2 AD fragment
@@ -278,7 +302,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     sread();
     swrite(0, 0);
     sload(1);
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int b = 0; b < NB; ++b) fb[b] = *(const v8bf *)(smem + bbase[b] + tap_offset(0, 0));
 
@@ -288,7 +312,10 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // read after block b + 1's MFMAs of this tap are issued, so the read
     // never waits for the MFMAs that still read the register (in the last
     // tap: the next chunk's first tap, from its stage, staged and made
-    // visible earlier in this chunk).
+    // visible earlier in this chunk).  With one wave per SIMD, every other
+    // instruction has to issue in the shadow of the MFMAs: each block's pair
+    // of MFMAs carries at most one piece of the remaining work (an A
+    // prefetch, a landing read, a quad write, a direct load).
     auto run_chunk = [&](const int chunk, auto st_c) {
         constexpr int ST = decltype(st_c)::value;
         constexpr int NX = (ST + 1) % kStages;   // stage of the next chunk
@@ -303,15 +330,13 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                 else if (more)
                     fb[b] = *(const v8bf *)(smem + bbase[b] + tap_offset(NX, 0));
             };
-            {
-                const int t2 = tp + AD;
-                const int c2 = t2 < T ? chunk : chunk + 1;
-                const int t2m = t2 < T ? t2 : t2 - T;
-                fa[t2m][0] = aload(c2, t2m, 0);
-                fa[t2m][1] = aload(c2, t2m, 1);
-            }
+            const int t2 = tp + AD;
+            const int c2 = t2 < T ? chunk : chunk + 1;
+            const int t2m = t2 < T ? t2 : t2 - T;
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
+                if (b == 0) fa[t2m][0] = aload(c2, t2m, 0);
+                if (b == kA1Block) fa[t2m][1] = aload(c2, t2m, 1);
 #pragma unroll
                 for (int cb = 0; cb < 2; ++cb)
                     if constexpr (F16)
@@ -322,55 +347,107 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                         acc[cb][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                             fb[b], fa[tp][cb], acc[cb][b], 0, 0, 0);
                 if (b >= 1) next_b(b - 1);
+                if (tp == kReadTap && more) {
+                    if (b == 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kAfterLanding) : "memory");
+                    if (b < 8) sread_one(b);
+                }
+                if (tp == kStageTap && more) {
+                    // The stage was last read two chunks ago, before the
+                    // last barrier.
+                    if (b == 0) smask(chunk + 1);
+                    if (b >= 1 && b <= 4) swrite_one(b - 1, NX);
+                }
+                // The landing area is refilled only after every landed value
+                // is in registers (the stage writes used them).
+                if (tp >= kLoadTap && b == NB - 1 && more) sload_one(chunk + 2, tp - kLoadTap);
                 __builtin_amdgcn_sched_barrier(0);
             }
             next_b(NB - 1);
-            if (tp == kReadTap && more) {
-                // The next chunk's copy was issued a chunk ago; only A
-                // prefetches were issued after it: the previous chunk's
-                // from tap kStageTap + 1 on and this chunk's up to here, or
-                // in chunk 0 (whose set-up fragments went out before the
-                // copy) this chunk's alone.
-                if (chunk == 0)
-                    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (kReadTap + 1)) : "memory");
-                else
-                    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kAfterLanding) : "memory");
-                sread();
-            }
-            if (tp == kStageTap && more) {
-                // The stage was last read two chunks ago, before the last
-                // barrier.
-                swrite(chunk + 1, NX);
-                sload(chunk + 2);
-            }
-            if (tp == kBarTap) __syncthreads();
+            if (tp == kBarTap) lds_barrier();
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    for (int chunk = 0; chunk < A.nchunks; chunk += kStages) {
-        run_chunk(chunk, std::integral_constant<int, 0>{});
-        if (chunk + 1 < A.nchunks) run_chunk(chunk + 1, std::integral_constant<int, 1>{});
-        if (chunk + 2 < A.nchunks) run_chunk(chunk + 2, std::integral_constant<int, 2>{});
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-
-    // Epilogue.  grad_out is the MFMA's A operand and the weight its B
+    // Output stores.  grad_out is the MFMA's A operand and the weight its B
     // operand, so lane (j16, g) holds D[4g + r][j16] of each block: pixels
     // 16b + 4g .. 16b + 4g + 3 (consecutive in the NCHW plane, and 16-byte
     // aligned as H*W is a multiple of 4, checked at launch) of input channel
     // j16 of the wave's channel block cb.  One 16-byte store each, every
     // 4 lanes of a channel a full 64-byte run; slots past the image are not
     // stored.
+    auto store_block = [&](int b) {
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-        const int ci = ci_tile * 128 + wave * 32 + cb * 16 + j16;
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
+        for (int cb = 0; cb < 2; ++cb) {
+            const int ci = ci_tile * 128 + wave * 32 + cb * 16 + j16;
             const int p = 16 * b + 4 * g;
             const int off = (p < HW && ci < A.Ci) ? ((n * A.Ci + ci) * HW + p) * 4 : kOOB;
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, acc[cb][b]), drs, off,
                                                    0, 0);
         }
+    };
+    // The last chunk runs block by block, all taps of a group of blocks at a
+    // time, and stores each group as soon as its sums are complete: the
+    // 25 MB of a deep stage's fp32 output then leaves while the chunk still
+    // computes, instead of in one burst at the end.  Every fragment of the
+    // chunk is in registers by then (the ring holds taps 0 .. T-2, tap T-1
+    // is loaded here) and every block's tap-0 B fragment was read in the
+    // previous chunk's last tap (or in the set-up).  Groups are pairs of
+    // blocks (a triple last when NB is odd), so each accumulator's MFMAs
+    // are at least four apart.
+    auto run_last = [&](const int chunk, auto st_c) {
+        constexpr int ST = decltype(st_c)::value;
+        fa[T - 1][0] = aload(chunk, T - 1, 0);
+        fa[T - 1][1] = aload(chunk, T - 1, 1);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        constexpr int NG = NB / 2;
+#pragma unroll
+        for (int gr = 0; gr < NG; ++gr) {
+            const int b0 = 2 * gr;
+            const int nbk = gr == NG - 1 ? NB - b0 : 2;
+            v8bf x[2][3];
+#pragma unroll
+            for (int k = 0; k < 3; ++k)
+                if (k < nbk) x[0][k] = fb[b0 + k];
+#pragma unroll
+            for (int tp = 0; tp < T; ++tp) {
+                if (tp + 1 < T) {
+#pragma unroll
+                    for (int k = 0; k < 3; ++k)
+                        if (k < nbk)
+                            x[(tp + 1) & 1][k] =
+                                *(const v8bf *)(smem + bbase[b0 + k] + tap_offset(ST, tp + 1));
+                }
+#pragma unroll
+                for (int k = 0; k < 3; ++k)
+#pragma unroll
+                    for (int cb = 0; cb < 2; ++cb)
+                        if (k < nbk) {
+                            if constexpr (F16)
+                                acc[cb][b0 + k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                    __builtin_bit_cast(v8h, x[tp & 1][k]),
+                                    __builtin_bit_cast(v8h, fa[tp][cb]), acc[cb][b0 + k], 0, 0, 0);
+                            else
+                                acc[cb][b0 + k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                    x[tp & 1][k], fa[tp][cb], acc[cb][b0 + k], 0, 0, 0);
+                        }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int k = 0; k < 3; ++k)
+                if (k < nbk) store_block(b0 + k);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    auto step = [&](const int chunk, auto st_c) {
+        if (chunk + 1 < A.nchunks)
+            run_chunk(chunk, st_c);
+        else
+            run_last(chunk, st_c);
+    };
+    for (int chunk = 0; chunk < A.nchunks; chunk += kStages) {
+        step(chunk, std::integral_constant<int, 0>{});
+        if (chunk + 1 < A.nchunks) step(chunk + 1, std::integral_constant<int, 1>{});
+        if (chunk + 2 < A.nchunks) step(chunk + 2, std::integral_constant<int, 2>{});
     }
 }
 
