@@ -32,18 +32,6 @@ __host__ __device__ inline int xcd_order(int L, int G) {
     return x * q + (x < r ? x : r) + k;
 }
 
-#ifdef __HIP__
-// Work-group barrier for hand-offs through LDS: waits for this wave's own
-// LDS instructions, then for every wave.  __syncthreads() also fences global
-// memory, and the compiler implements that fence by waiting for every
-// outstanding direct (buffer -> LDS) load, which drains the prefetches a
-// pipeline keeps in flight across the barrier.  A kernel that hands off data
-// landed by direct loads waits for them itself (s_waitcnt vmcnt) before this.
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-#endif
-
 constexpr int kMaxPhasesPerLaunch = 16;
 
 struct Phase {

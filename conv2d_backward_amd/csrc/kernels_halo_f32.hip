@@ -38,6 +38,7 @@
 #include <algorithm>
 
 #include "gi_common.h"
+#include "lds_barrier.h"
 #include "gi_launch.h"
 
 namespace gi {
@@ -240,7 +241,7 @@ __device__ __forceinline__ void run_phase(const HaloArgs &A, const HaloPhase &P,
     } else {
         wait_dma<0>();
     }
-    __syncthreads();
+    lds_barrier();
     for (int i = 0; i < h; ++i) {
         const int stg = s0 + i;
         const int cur = i % A.stages;
@@ -287,7 +288,7 @@ __device__ __forceinline__ void run_phase(const HaloArgs &A, const HaloPhase &P,
             wait_dma<NDMA>();
         else
             wait_dma<0>();
-        __syncthreads();
+        lds_barrier();
     }
 }
 
@@ -422,7 +423,7 @@ __device__ __forceinline__ void run_fused(const HaloArgs &A, v2f *smem2, const i
     } else {
         wait_dma<0>();
     }
-    __syncthreads();
+    lds_barrier();
     for (int chunk = 0; chunk < A.nchunks; ++chunk) {
         const int cur = chunk % A.stages;
         const bool ahead = chunk + D < A.nchunks;
@@ -448,7 +449,7 @@ __device__ __forceinline__ void run_fused(const HaloArgs &A, v2f *smem2, const i
             wait_dma<NDMA>();
         else
             wait_dma<0>();
-        __syncthreads();
+        lds_barrier();
     }
 }
 

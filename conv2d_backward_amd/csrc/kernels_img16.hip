@@ -45,6 +45,7 @@
 #include <type_traits>
 
 #include "gi_common.h"
+#include "lds_barrier.h"
 #include "gi_launch.h"
 
 namespace gi {

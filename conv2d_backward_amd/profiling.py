@@ -42,13 +42,13 @@ PROFILES = os.path.join(ROOT, "profiles")
 # Sources that define each main kernel (its launch parameters come from the
 # planner, whose result is matched separately through the plan description).
 KERNEL_SOURCES = {
-    ("halo", "f32"): ["kernels_halo_f32.hip"],
+    ("halo", "f32"): ["kernels_halo_f32.hip", "lds_barrier.h"],
     ("halo", "bf16"): ["kernels_halo_bf16.hip", "half_launch.h"],
     ("halo", "f16"): ["kernels_halo_bf16.hip", "half_launch.h"],
     ("stem", "f32"): ["kernels_stem_f32.hip"],
     ("col2im", "f32"): ["kernels_col2im_f32.hip"],
-    ("img16", "bf16"): ["kernels_img16.hip", "half_launch.h"],
-    ("img16", "f16"): ["kernels_img16.hip", "half_launch.h"],
+    ("img16", "bf16"): ["kernels_img16.hip", "half_launch.h", "lds_barrier.h"],
+    ("img16", "f16"): ["kernels_img16.hip", "half_launch.h", "lds_barrier.h"],
     ("gw", "f32"): ["kernels_gw_f32.hip", "gw_common.h"],
     ("gwd", "f32"): ["kernels_gw_f32.hip", "gw_common.h"],
     ("fwd", "f32"): ["kernels_fwd_f32.hip", "fwd_common.h"],
