@@ -45,6 +45,7 @@ namespace gi {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v2f __attribute__((ext_vector_type(2)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 namespace {
 
@@ -525,6 +526,60 @@ __global__ __launch_bounds__(256 * KS, OCC) __attribute__((amdgpu_waves_per_eu(O
             for (int blk = 0; blk < NB; ++blk) acc[k][blk] = v4f{0.f, 0.f, 0.f, 0.f};
         run_fused<NB, HG, MP, KS, PITCH>(A, smem_all, pbase, myph, acc,
                                          a0, b0, n_img, ci_tile, grs, wrs);
+        // Stride 2, four phases: a phase's pixels are every other float of
+        // an input row, so storing each phase by itself writes every cache
+        // line in two halves at different moments (twice the output bytes
+        // reach HBM).  Instead the four phases' sums meet in LDS, 16 input
+        // channels at a time (both groups' wave w), and all threads store
+        // whole rows of the 2TR x 2TC input tile, 16 bytes per lane.  (The
+        // stages are free: run_fused ends on a barrier after its last reads.)
+        const int TT = A.TR * A.TC;
+        const size_t lds_bytes = ((size_t)A.stages * (A.Tall * 4 * 64 + 4 * A.HPc) + 128) * 8;
+        if (A.stride == 2 && A.nphases == 4 && NPH == 4 && !A.fold && (A.W & 3) == 0 &&
+            (A.TC & 1) == 0 && (size_t)256 * TT <= lds_bytes) {
+            float *const X = (float *)smem_all;   // [phase][16 channels][TT]
+            int pidx[2][2] = {{0, 0}, {0, 0}};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) pidx[A.ph[q].rho_h & 1][A.ph[q].rho_w & 1] = q;
+            const int qpr = A.TC / 2;                 // 16-byte quads per input row of the tile
+            const int nquad = 16 * 2 * A.TR * qpr;
+            for (int w = 0; w < 4; ++w) {
+                if (wave == w) {
+#pragma unroll
+                    for (int k = 0; k < MP; ++k) {
+                        if (myph[k] < 0) continue;
+#pragma unroll
+                        for (int blk = 0; blk < NB; ++blk) {
+                            const int px = blk * 16 + l16;
+                            if (px < TT)
+#pragma unroll
+                                for (int r = 0; r < 4; ++r) {
+                                    const float v = acc[k][blk][r];
+                                    X[(myph[k] * 16 + 4 * g4 + r) * TT + px] = v;
+                                }
+                        }
+                    }
+                }
+                __syncthreads();
+                for (int q = (int)threadIdx.x; q < nquad; q += 256 * KS) {
+                    const int cl = q / (2 * A.TR * qpr), rem = q - cl * (2 * A.TR * qpr);
+                    const int row = rem / qpr, qc = rem - (rem / qpr) * qpr;
+                    const int rh = row & 1, a = row >> 1;
+                    const int ih = 2 * a0 + row, iw = 2 * b0 + 4 * qc;
+                    const int ci = ci0 + w * 16 + cl;
+                    const float *x0 = X + (pidx[rh][0] * 16 + cl) * TT + a * A.TC + 2 * qc;
+                    const float *x1 = X + (pidx[rh][1] * 16 + cl) * TT + a * A.TC + 2 * qc;
+                    const v4u v = v4u{__float_as_uint(x0[0]), __float_as_uint(x1[0]),
+                                      __float_as_uint(x0[1]), __float_as_uint(x1[1])};
+                    const int off = (ih < A.H && iw < A.W && ci < A.Ci)
+                                        ? (((n_img * A.Ci + ci) * A.H + ih) * A.W + iw) * 4
+                                        : kOOB;
+                    __builtin_amdgcn_raw_buffer_store_b128(v, drs, off, 0, 0);
+                }
+                __syncthreads();
+            }
+            return;
+        }
 #pragma unroll
         for (int k = 0; k < MP; ++k) {
             if (myph[k] < 0) continue;

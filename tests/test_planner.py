@@ -66,6 +66,12 @@ FIXED_INSTANCES = [
      ["cfg=12 fused", "HP=15", "tile=7x14"]),
     (S(2, 70, 27, 29, 20, 3, 3, 2, 1, 1), False, gi.VARIANT_HALO, (13, 7, 15, 0, 2),
      ["cfg=13 fused"]),
+    # Fused stride 2 with whole-row stores: odd H (one phase's grid a row
+    # shorter, the last row tile ragged) and ragged column and row tiles.
+    (S(2, 70, 27, 28, 20, 3, 3, 2, 1, 1), False, gi.VARIANT_HALO, (13, 7, 14, 0, 2),
+     ["cfg=11 fused", "tile=7x14", "wgs=4x2"]),
+    (S(3, 50, 30, 36, 24, 3, 3, 2, 1, 1), False, gi.VARIANT_HALO, (8, 7, 14, 0, 2),
+     ["cfg=12 fused", "tile=7x14", "wgs=18x1"]),
     (S(1, 40, 21, 22, 12, 3, 2, 2, 1, 0), False, gi.VARIANT_HALO, (13, 11, 11, 0, 2),
      ["cfg=13 fused"]),
     (S(4, 30, 17, 17, 36, 1, 7, 1, 0, 3), False, gi.VARIANT_HALO, (8, 7, 17, 1, 0),
