@@ -111,6 +111,92 @@ def test_image_kernel_b_reads_conflict_free():
 
 
 # ----------------------------------------------------------------------------
+# The same kernel's staging: wave w direct-loads the 8 channel planes 8w..8w+7
+# of a chunk (contiguous in NCHW, `shift` bytes into its 4 KB landing area)
+# and reads them back with ds_read_b64_tr_b16.  Lane layout of that read
+# (measured on the GPU): within each 16 lanes, lanes 4r..4r+3 each load 4
+# consecutive 16-bit values which together form row r (16 values), and lane
+# i receives element i of rows 0..3.  Read (s, h) must hand lane l channels
+# 4h..4h+3 of pixel 64s + l, and reads (s, 0), (s, 1) together the 8
+# channels of that pixel in order (the 16 bytes of the stage write).
+# ----------------------------------------------------------------------------
+
+LAND = 4096
+
+
+def tr16_read(mem, addr):
+    """Model of one ds_read_b64_tr_b16: mem maps a 16-bit element's byte
+    address to its value; addr holds the 64 lanes' byte addresses."""
+    out = []
+    for g in range(4):
+        rows = []
+        for r in range(4):
+            row = []
+            for j in range(4):
+                a = addr[16 * g + 4 * r + j]
+                assert a % 8 == 0 and 0 <= a and a + 8 <= LAND, (g, r, j, a)
+                row += [mem.get(a + 2 * k) for k in range(4)]
+            rows.append(row)
+        out += [[rows[r][i] for r in range(4)] for i in range(16)]
+    return out
+
+
+def staging_read_addrs(shift, plane_bytes, s, h):
+    """Per-lane byte address of staging read (s, h), as the kernel forms it."""
+    out = []
+    for lane in range(64):
+        rb = shift + ((lane >> 2) & 3) * plane_bytes + (16 * (lane >> 4) + 4 * (lane & 3)) * 2
+        out.append(rb + (4 * plane_bytes if h else 0) + 128 * s)
+    return out
+
+
+def landed(shift, ohw):
+    """The landing area after the copy: element (channel c, pixel p)."""
+    return {shift + c * 2 * ohw + 2 * p: (c, p) for c in range(8) for p in range(ohw)}
+
+
+@pytest.mark.parametrize("ohw,shift", [(196, 0), (196, 8), (4, 8), (100, 0), (144, 8),
+                                       (252, 8), (252, 0)])
+def test_image_staging_transpose(ohw, shift):
+    """Every pixel of the image reaches its own lane and write with its 8
+    channels in order; pixels past the plane stay inside the landing area."""
+    mem = landed(shift, ohw)
+    for s in range(4):
+        got = [tr16_read(mem, staging_read_addrs(shift, 2 * ohw, s, h)) for h in (0, 1)]
+        for lane in range(64):
+            p = 64 * s + lane
+            if p < ohw:
+                assert got[0][lane] + got[1][lane] == [(c, p) for c in range(8)], (s, lane)
+
+
+def test_image_staging_plan_limits():
+    """The launch admits only images whose 8 planes (after at most 8 bytes of
+    shift) fit the landing area, in whole 4-pixel quads; every such shift
+    keeps the reads 8-byte aligned and in bounds (tr16_read asserts both)."""
+    for ohw in range(4, 256, 4):
+        assert 8 + 16 * ohw <= LAND
+        for plane0 in range(0, 64):   # (n * Co + 8w) for any n, Co, w
+            shift = (plane0 * 2 * ohw) % 16
+            assert shift in (0, 8)
+            for s in range(4):
+                for h in (0, 1):
+                    tr16_read({}, staging_read_addrs(shift, 2 * ohw, s, h))
+
+
+def test_image_staging_model_sees_a_planted_mistake():
+    """Swapping the roles of lane bits 0-1 and 2-3 in the read address (a
+    plausible mix-up of row and column in the transposition) delivers the
+    wrong channel to some lane."""
+    ohw, shift = 196, 0
+    mem = landed(shift, ohw)
+    addr = []
+    for lane in range(64):
+        addr.append(shift + (lane & 3) * 2 * ohw + (16 * (lane >> 4) + 4 * ((lane >> 2) & 3)) * 2)
+    got = tr16_read(mem, addr)
+    assert any(got[lane] != [(c, lane) for c in range(4)] for lane in range(64))
+
+
+# ----------------------------------------------------------------------------
 # The 16-bit halo-tile kernel (kernels_halo_bf16.hip): wave (wm, wn) reads
 # pixel p = (wn*NBW + b)*16 + lane%16 of a TR x TC tile, position
 # (p / TC)*HP + p % TC in plane lane/16 (PS bytes apart), shifted by the tap.
