@@ -1151,7 +1151,9 @@ bool plan_gwd(const conv2d_gi_params &p, GwdPlan &out, bool bias = false) {
     a.co_blocks = (p.Co + 63) / 64;
     int cfg;
     if (flat) {
-        cfg = p.kW == 3 ? 0 : 1;
+        // 3 x 3 on rows of at least 18 pixels: the instance whose K blocks
+        // inside a row skip the column masks.
+        cfg = p.kW == 3 ? (p.W >= 18 ? 6 : 0) : 1;
         a.colmap = 0;
         a.khg = p.kW == 3 ? 3 : 1;
     } else if (p.kW == 3 && (p.stride == 1 || p.stride == 2) && p.Ci >= 16) {

@@ -310,11 +310,13 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void *dst, int v
 }
 
 // NB column blocks of 16 per wave; KW kernel columns (tap-major map, 0 for
-// the flattened map); S stride (0: read from A); FLAT pixel layout.
-template <int NB, int KW, int S, bool FLAT>
+// the flattened map); S stride (0: read from A); FLAT pixel layout; PLAIN
+// (flat only): K blocks that no kernel column's mask touches skip the masks.
+template <int NB, int KW, int S, bool FLAT, bool PLAIN = false>
 __global__ __launch_bounds__(kGwdThreads) void gi_gwd_f32(const GwdArgs A) {
     extern __shared__ __attribute__((aligned(16))) float sm[];
     static_assert(!FLAT || (KW > 0 && S == 1), "flat layout: tap-major map, stride 1");
+    static_assert(!PLAIN || FLAT, "the mask bypass is for the flat layout");
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int i = lane & 15, g = lane >> 4;
@@ -446,18 +448,41 @@ __global__ __launch_bounds__(kGwdThreads) void gi_gwd_f32(const GwdArgs A) {
         if (FLAT) {
             constexpr int NKW = KW > 0 ? KW : 1;
             float am[NKW][4];
+            // Column masks of the K block: a pixel's value is kept for the
+            // kernel columns whose input column stays in its row.
+            auto masks = [&](bool with_bias) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                // Column of the pixel (W >= 2 here), moved out of every
-                // kernel column's range past the group's end.
-                const int f = f0 + g + 4 * j;
-                const int ow = f < kv ? f - (int)__umulhi((uint32_t)f, A.m_w) * A.W : 1 << 24;
+                for (int j = 0; j < 4; ++j) {
+                    // Column of the pixel (W >= 2 here), moved out of every
+                    // kernel column's range past the group's end.
+                    const int f = f0 + g + 4 * j;
+                    const int ow = f < kv ? f - (int)__umulhi((uint32_t)f, A.m_w) * A.W : 1 << 24;
 #pragma unroll
-                for (int kw = 0; kw < NKW; ++kw)
-                    am[kw][j] = (uint32_t)(ow + kw - A.pad_w) < (uint32_t)A.W ? F.a[j] : 0.f;
-                // The centre column (kw == pad_w, as oW == W) masks only the
-                // pixels past the group's end.
-                bsum += am[(NKW - 1) / 2][j];
+                    for (int kw = 0; kw < NKW; ++kw)
+                        am[kw][j] = (uint32_t)(ow + kw - A.pad_w) < (uint32_t)A.W ? F.a[j] : 0.f;
+                    // The centre column (kw == pad_w, as oW == W) masks only
+                    // the pixels past the group's end.
+                    if (with_bias) bsum += am[(NKW - 1) / 2][j];
+                }
+            };
+            if constexpr (PLAIN) {
+                // A block whose 16 pixels lie in one row, at least the
+                // kernel's reach from both of its ends, and before the
+                // group's end needs no masks (a uniform test: f0 and kv are
+                // the same for the wave).
+                const int c0 = f0 - (int)__umulhi((uint32_t)f0, A.m_w) * A.W;
+                if (f0 + 16 <= kv && c0 >= A.pad_w && c0 + 15 + (NKW - 1 - A.pad_w) < A.W) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+#pragma unroll
+                        for (int kw = 0; kw < NKW; ++kw) am[kw][j] = F.a[j];
+                } else {
+                    masks(false);
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) bsum += am[(NKW - 1) / 2][j];
+            } else {
+                masks(true);
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j)
@@ -663,19 +688,20 @@ hipError_t launch_gw_f32(const GwArgs &a, hipStream_t s, const KernelEvents &ev)
 //   3: row-padded, tap-major, 3 x 3, stride 2
 //   4: row-padded, flattened map, 10 blocks, stride 2
 //   5: row-padded, flattened map, 8 blocks, any stride
+//   6: as 0, with the mask bypass (rows of at least 18 pixels)
 int gwd_f32_blocks(int cfg) {
-    static const int nb[] = {9, 7, 9, 9, 10, 8};
-    return cfg >= 0 && cfg < 6 ? nb[cfg] : 0;
+    static const int nb[] = {9, 7, 9, 9, 10, 8, 9};
+    return cfg >= 0 && cfg < 7 ? nb[cfg] : 0;
 }
 
 // Work-groups per compute unit that the registers allow: one wave of each
 // work-group per SIMD, 512 registers per lane per SIMD shared by VGPRs and
 // AGPRs; the counts are those of the gfx950 build of each instantiation
-// (cfg 0: 180 + 36, cfg 1: 128 + 28, cfg 2: 128 + 36, cfg 3: 128 + 36,
-// cfg 4: 164 + 40, cfg 5: 136 + 32).
+// (cfg 0: 180 + 36, cfg 1: 132 + 28, cfg 2: 128 + 36, cfg 3: 128 + 36,
+// cfg 4: 164 + 40, cfg 5: 136 + 32, cfg 6: 184 + 36).
 int gwd_f32_max_wgs(int cfg) {
-    static const int occ[] = {2, 3, 3, 3, 2, 3};
-    return cfg >= 0 && cfg < 6 ? occ[cfg] : 1;
+    static const int occ[] = {2, 3, 3, 3, 2, 3, 2};
+    return cfg >= 0 && cfg < 7 ? occ[cfg] : 1;
 }
 
 size_t gwd_f32_lds_bytes(const GwdArgs &a) {
@@ -683,7 +709,7 @@ size_t gwd_f32_lds_bytes(const GwdArgs &a) {
 }
 
 hipError_t launch_gwd_f32(const GwdArgs &a, int cfg, hipStream_t s, const KernelEvents &ev) {
-    if (cfg < 0 || cfg > 5 || a.LA % 8 != 4 || a.LX % 8 != 4 || a.stages < 1 || a.stages > 2 ||
+    if (cfg < 0 || cfg > 6 || a.LA % 8 != 4 || a.LX % 8 != 4 || a.stages < 1 || a.stages > 2 ||
         a.stage_floats % 256 != 0 || a.nslots != 16 * a.LA + a.XC * (a.LX / 4) ||
         4 * a.nslots > a.stage_floats || (!a.flat && (a.OWP % 16 != 0 || a.XW % 4 != 0 ||
                                                         a.XO % 4 != 0)))
@@ -708,7 +734,8 @@ hipError_t launch_gwd_f32(const GwdArgs &a, int cfg, hipStream_t s, const Kernel
         case 2: e = go(gi_gwd_f32<9, 3, 1, false>); break;
         case 3: e = go(gi_gwd_f32<9, 3, 2, false>); break;
         case 4: e = go(gi_gwd_f32<10, 0, 2, false>); break;
-        default: e = go(gi_gwd_f32<8, 0, 0, false>); break;
+        case 5: e = go(gi_gwd_f32<8, 0, 0, false>); break;
+        default: e = go(gi_gwd_f32<9, 3, 1, true, true>); break;
     }
     if (e != hipSuccess) return e;
     const int total = a.Co * a.Ci * a.kH * a.kW;

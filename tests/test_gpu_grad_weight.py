@@ -111,6 +111,9 @@ GWD_SHAPES = [
     S(1, 5, 16, 16, 20, 5, 5, 1, 2, 2),      # flattened map, any stride (1)
     S(1, 4, 12, 12, 8, 2, 3, 3, 1, 1),       # flattened map, stride 3
     S(2, 24, 8, 8, 130, 3, 3, 1, 1, 1),      # three Co blocks, last one ragged
+    S(2, 20, 21, 36, 70, 3, 3, 1, 1, 1),     # flat, 36-pixel rows: unmasked K blocks
+    S(1, 16, 18, 18, 64, 3, 3, 1, 1, 1),     # flat, 18-pixel rows: one unmasked column
+    S(2, 16, 9, 24, 64, 1, 3, 1, 0, 1),      # flat 1x3 on 24-pixel rows
 ]
 
 

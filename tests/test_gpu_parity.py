@@ -266,6 +266,10 @@ COL2IM_SHAPES = [
     workloads.Shape(2, 1, 30, 31, 64, 1, 1, 1, 0, 0),      # 1 x 1: one column
     workloads.Shape(1, 6, 19, 21, 64, 5, 5, 2, 2, 2),      # 150 columns: last block partial
     workloads.Shape(1, 3, 224, 224, 64, 7, 7, 2, 3, 3),    # one stem image at full size
+    workloads.Shape(2, 1, 33, 29, 64, 7, 7, 2, 3, 3),      # 49 columns: a 1-column tail
+    workloads.Shape(1, 2, 26, 31, 52, 7, 7, 2, 3, 3),      # 98 columns: a 2-column tail, Co % 4 = 0
+    workloads.Shape(1, 4, 21, 18, 61, 5, 5, 2, 2, 2),      # 100 columns: a 4-column tail, ragged Co
+    workloads.Shape(2, 4, 13, 15, 64, 3, 3, 1, 1, 1),      # 36 columns: tail at stride 1
 ]
 
 
