@@ -1114,6 +1114,17 @@ uint32_t div_magic(int d) {
     return d <= 1 ? 0u : (uint32_t)((1ULL << 32) / (uint64_t)d + 1);
 }
 
+// (m, k) of q = (s * m) >> k = floor(s / d) for 0 <= s < 2^14: 2^k >= 2^14 d,
+// m = ceil(2^k / d) < 2^15, so s * m < 2^29 (one 24-bit multiply) and the
+// error s * (m d - 2^k) / 2^k stays below s d / 2^k <= 1 (exact).
+uint32_t div24(int d) {
+    if (d < 1) return 0u;
+    int k = 14;
+    while ((1LL << k) < 16384LL * d) ++k;
+    const uint64_t m = ((1ULL << k) + (uint64_t)d - 1) / (uint64_t)d;
+    return (uint32_t)k << 24 | (uint32_t)m;
+}
+
 int odd_quads(int64_t n) {   // smallest multiple of 4 >= n whose quarter is odd
     int64_t v = (n + 3) / 4 * 4;
     if ((v / 4) % 2 == 0) v += 4;
@@ -1123,6 +1134,8 @@ int odd_quads(int64_t n) {   // smallest multiple of 4 >= n whose quarter is odd
 bool plan_gwd(const conv2d_gi_params &p, GwdPlan &out, bool bias = false) {
     const int64_t lim = 0x7fff0000LL;
     if ((int64_t)p.N * p.Co * p.oH * p.oW * 4 > lim) return false;
+    // Planes within the kernel's 24-bit multiplies.
+    if ((int64_t)p.oH * p.oW >= (1 << 24) || (int64_t)p.H * p.W >= (1 << 24)) return false;
     if ((int64_t)p.N * p.Ci * p.H * p.W * 4 > lim) return false;
     const int64_t total = (int64_t)p.Co * p.Ci * p.kH * p.kW;
     if (total * 4 > lim) return false;
@@ -1252,11 +1265,11 @@ bool plan_gwd(const conv2d_gi_params &p, GwdPlan &out, bool bias = false) {
     }
     if (!found) return false;
     if (flat) a.XR = 0;
-    a.m_la4 = div_magic(a.LA / 4);
-    a.m_owp4 = div_magic(a.OWP / 4);
-    a.m_lx4 = div_magic(a.LX / 4);
-    a.m_xw4 = div_magic(a.XW / 4);
     a.m_w = div_magic(p.W);
+    a.d24_la4 = div24(a.LA / 4);
+    a.d24_owp4 = div24(a.OWP / 4);
+    a.d24_lx4 = div24(a.LX / 4);
+    a.d24_xw4 = div24(a.XW / 4);
     out.args = a;
     out.cfg = cfg;
     out.args.bias = bias ? 1 : 0;

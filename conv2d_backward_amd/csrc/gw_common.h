@@ -82,9 +82,13 @@ struct GwdArgs {
     int32_t nslots;          // 16-byte pieces per stage: 16*LA + XC*LX/4
     int32_t stage_floats;    // LDS floats per stage (a multiple of 256)
     int32_t stages;          // 1 or 2
-    // Division by a constant d >= 1: q = d == 1 ? s : umulhi(s, m) with
-    // m = floor(2^32 / d) + 1, exact for s * d < 2^32.
-    uint32_t m_la4, m_owp4, m_lx4, m_xw4, m_w;
+    // Division by W >= 1: q = W == 1 ? s : umulhi(s, m_w) with
+    // m_w = floor(2^32 / W) + 1, exact for s * W < 2^32.
+    uint32_t m_w;
+    // Divisions by LA/4, OWP/4, LX/4 and XW/4 on 24-bit multiplies (full
+    // rate): q = (s * m) >> k with m in the low 24 bits and k in the high 8,
+    // exact for 0 <= s < 2^14.
+    uint32_t d24_la4, d24_owp4, d24_lx4, d24_xw4;
 };
 
 // grad_weight fp32 (kernels_gw_f32.hip): most taps per work-group, most

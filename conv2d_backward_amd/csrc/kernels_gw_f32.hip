@@ -299,9 +299,12 @@ __global__ __launch_bounds__(256) void gw_channel_sum_f32(const float *__restric
 // tap reaches such a row (one kernel row, no row padding).
 constexpr int kGwdThreads = 256;
 
-__device__ __forceinline__ int udiv(int s, int d, uint32_t m) {
-    return d == 1 ? s : (int)__umulhi((uint32_t)s, m);
+// floor(s / d) for 0 <= s < 2^14 from the packed (m, k) of GwdArgs::d24_*:
+// one full-rate 24-bit multiply and a shift.
+__device__ __forceinline__ int div24(int s, uint32_t v) {
+    return (int)(__umul24((uint32_t)s, v & 0xffffffu) >> (v >> 24));
 }
+__device__ __forceinline__ int mul24(int a, int b) { return (int)__umul24((uint32_t)a, (uint32_t)b); }
 
 // Direct global -> LDS load of 16 bytes per lane: lane i writes dst + 16i;
 // an out-of-range offset writes zeros.  dst is the same for the whole wave.
@@ -383,37 +386,41 @@ __global__ __launch_bounds__(kGwdThreads) void gi_gwd_f32(const GwdArgs A) {
         // Row-padded: first input row; flat: first needed float of a plane.
         const int ih0 = oh0 * st - A.pad_h + kh0;
         const int fbase = (oh0 - A.pad_h + kh0) * A.W - A.pad_w;
+        // Branch-free per piece, on 24-bit multiplies (operands below 2^24:
+        // channel and row counts, planes of fewer than 2^24 pixels); an
+        // invalid piece's offset is computed and then replaced by kOOB.
+        const int gfirst = oh0 * A.oW;   // flat: the group's first pixel in a plane
         for (int k = wave; k < nins; k += 4) {
             const int s = 64 * k + lane;
-            int off = -1;
             if (k < LA4) {   // grad_out pieces (16*LA of them: whole instructions)
-                const int co = udiv(s, LA4, A.m_la4), q = s - co * LA4;
-                if (co0 + co < A.Co) {
-                    const int plane = gplane0 + co * oHW;
-                    if (FLAT) {
-                        off = ((plane + oh0 * A.oW) & ~3) + 4 * q;
-                    } else {
-                        const int r = udiv(q, OWP4, A.m_owp4), cc = q - r * OWP4;
-                        if (r < rows_v && 4 * cc < A.oW) off = plane + (oh0 + r) * A.oW + 4 * cc;
-                    }
+                const int co = div24(s, A.d24_la4), q = s - mul24(co, LA4);
+                const int plane = gplane0 + mul24(co, oHW);
+                bool ok = co0 + co < A.Co;
+                int off;
+                if (FLAT) {
+                    off = ((plane + gfirst) & ~3) + 4 * q;
+                } else {
+                    const int r = div24(q, A.d24_owp4), cc = q - mul24(r, OWP4);
+                    ok = ok & (r < rows_v) & (4 * cc < A.oW);
+                    off = plane + mul24(oh0 + r, A.oW) + 4 * cc;
                 }
-                dma16(grs, stp + 256 * k, off >= 0 ? off * 4 : kOOB);
+                dma16(grs, stp + 256 * k, ok ? off * 4 : kOOB);
             } else {         // input pieces
                 const int s2 = s - 16 * A.LA;
-                const int seg = udiv(s2, LX4, A.m_lx4), q = s2 - seg * LX4;
-                if (s2 < A.XC * LX4 && ci_lo + seg < A.Ci) {
-                    const int plane = xplane0 + seg * HW;
-                    if (FLAT) {
-                        const int o = ((plane + fbase) & ~3) + 4 * q;
-                        if (o >= 0 && (!A.plane_zero || (o >= plane && o < plane + HW))) off = o;
-                    } else {
-                        const int xr = udiv(q, XW4, A.m_xw4), cc = q - xr * XW4;
-                        const int ih = ih0 + xr, iw = 4 * cc - A.XO;
-                        if (xr < A.XR && ih >= 0 && ih < A.H && iw >= 0 && iw < A.W)
-                            off = plane + ih * A.W + iw;
-                    }
+                const int seg = div24(s2, A.d24_lx4), q = s2 - mul24(seg, LX4);
+                const int plane = xplane0 + mul24(seg, HW);
+                bool ok = (s2 < A.XC * LX4) & (ci_lo + seg < A.Ci);
+                int off;
+                if (FLAT) {
+                    off = ((plane + fbase) & ~3) + 4 * q;
+                    ok = ok & (off >= 0) & ((A.plane_zero == 0) | ((off >= plane) & (off < plane + HW)));
+                } else {
+                    const int xr = div24(q, A.d24_xw4), cc = q - mul24(xr, XW4);
+                    const int ih = ih0 + xr, iw = 4 * cc - A.XO;
+                    ok = ok & (xr < A.XR) & (ih >= 0) & (ih < A.H) & (iw >= 0) & (iw < A.W);
+                    off = plane + mul24(ih, A.W) + iw;
                 }
-                dma16(xrs, stp + 256 * k, off >= 0 ? off * 4 : kOOB);
+                dma16(xrs, stp + 256 * k, ok ? off * 4 : kOOB);
             }
         }
     };
@@ -709,6 +716,11 @@ size_t gwd_f32_lds_bytes(const GwdArgs &a) {
 }
 
 hipError_t launch_gwd_f32(const GwdArgs &a, int cfg, hipStream_t s, const KernelEvents &ev) {
+    // (Piece indices below 2^14 and planes below 2^24 pixels: the 24-bit
+    // divisions and multiplies of the direct loads.)
+    if (a.nslots > 16384 - 64 || (int64_t)a.H * a.W >= (1 << 24) ||
+        (int64_t)a.oH * a.oW >= (1 << 24))
+        return hipErrorInvalidValue;
     if (cfg < 0 || cfg > 6 || a.LA % 8 != 4 || a.LX % 8 != 4 || a.stages < 1 || a.stages > 2 ||
         a.stage_floats % 256 != 0 || a.nslots != 16 * a.LA + a.XC * (a.LX / 4) ||
         4 * a.nslots > a.stage_floats || (!a.flat && (a.OWP % 16 != 0 || a.XW % 4 != 0 ||

@@ -292,3 +292,18 @@ def test_col2im_bank_layout():
         assert (lp - s.kW) % 32 == 0 and (plane - s.kH * s.kW) % 32 == 0, txt
         assert ws >= 16 * ((ncols + 15) // 16) and ws % 32 == (8 if s.stride == 2 else 16), txt
     assert seen >= 10
+
+
+def test_div24_exact():
+    """The grad_weight kernel's piece divisions: q = (s * m) >> k with
+    2^k >= 2^14 d and m = ceil(2^k / d) equals s // d for every s < 2^14, and
+    s * m stays below 2^29 (one 24-bit multiply)."""
+    for d in list(range(1, 600)) + [1021, 4093, 16383]:
+        k = 14
+        while (1 << k) < 16384 * d:
+            k += 1
+        m = ((1 << k) + d - 1) // d
+        assert m < (1 << 15)
+        for s in range(0, 16384, 1 if d < 64 else 7):
+            assert (s * m) >> k == s // d, (d, s)
+            assert s * m < (1 << 29)
