@@ -1237,10 +1237,14 @@ bool plan_gwd(const conv2d_gi_params &p, GwdPlan &out, bool bias = false) {
             const int64_t per_cu = (wgs + kCUs - 1) / kCUs;
             // One wave per SIMD leaves LDS and load latency exposed
             // (measured: about 0.7 of the MFMA rate); a single stage waits
-            // for each group's loads, which a second work-group hides.
+            // for each group's loads, which a second work-group hides.  Two
+            // stages carry the next group's loads through the K blocks
+            // (registers and issue slots): with a second work-group they
+            // measured no faster than one stage (strided downsample: 198.9
+            // against 187.4 us with one stage and twice the rows).
             const double mfma = (double)nkb * 4 * NB * 32;         // cycles per group
             const double eff = occ >= 2 ? 1.0 : 0.7;
-            const double sync = stages == 2 ? 400.0 : (occ >= 2 ? 800.0 : 3000.0);
+            const double sync = stages == 2 ? 900.0 : (occ >= 2 ? 800.0 : 3000.0);
             const double t_main = (double)per_cu * gs * mfma / eff +
                                   (double)gs * sync * (double)((per_cu + occ - 1) / occ);
             const double t_red = (double)slices * total * 8 * 2.4e9 / 4.0e12;
